@@ -1,0 +1,229 @@
+/*
+ * fp64 CPU oracle for the Mamba-2 mixer core (depthwise causal conv + SiLU,
+ * the selective state-space recurrence, grouped gated RMSNorm, single-token
+ * decode).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do. It shares no code, header or constant with the
+ * HIP kernels.
+ *
+ * Every operation is fp64 on fp64 copies of the caller's inputs (which are
+ * exact copies of the fp32 / bf16 values the GPU sees). Loops are plain and
+ * sequential per (batch, head); the only parallelism is an OpenMP loop over
+ * independent (batch, head) or (batch, token) units, which does not change
+ * any result.
+ *
+ * Sources (the web pages this method is described on):
+ *  - "feat(model): Nemotron-H hybrid ... on the CPU" (gllm PR #86), section
+ *    "2. feat(model): Nemotron-H on the CPU": the mixer is in_proj, then
+ *    CausalConv1D, SSMScan and GatedRMSNorm, then out_proj; state is kept
+ *    per sequence. Section "Validation": the scan that serves as truth is a
+ *    plain sequential recurrence (not a chunked form).
+ *  - "feat(model): add Nemotron-3 Nano hybrid ..." (Modalities PR #459),
+ *    section "Testing" and the attribution commit message: packed
+ *    [z, x, B, C, dt] projection layout, conv1d shapes, GatedRMSNorm
+ *    semantics.
+ *  - "NemotronH-0.3B-A0.3B" model card, section "Notes": n_groups divides
+ *    the mixer intermediate size heads * head_dim.
+ *  The recurrence itself is h_t = exp(dt_t*A) h_{t-1} + dt_t B_t (x) x_t,
+ *  y_t = C_t . h_t + D x_t, as stated for this workload.
+ *
+ * Readings where the pages are silent (each is also listed in the design
+ * notes): conv taps are a cross-correlation with w[c][W-1] on the current
+ * token, left-padded by the conv state (oldest row first); SiLU applies to
+ * every xBC channel; head h uses B/C group h / (H/G); the gated norm gates
+ * first, norm(y * silu(z)) * w, over G contiguous channel groups.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double silu(double u) { return u / (1.0 + exp(-u)); }
+
+/*
+ * Depthwise causal conv over the channels of xBC followed by SiLU.
+ * xbc [B, L, C]; w [C, W]; bias [C] or NULL; conv_in [B, W-1, C] or NULL
+ * (zeros); out [B, L, C]; conv_out [B, W-1, C] or NULL.
+ * ext[b] = conv_in[b] ++ xbc[b] (W-1 + L rows);
+ * out[b,t,c] = silu(bias[c] + sum_k w[c,k] * ext[b, t+k, c]);
+ * conv_out[b] = the last W-1 rows of ext[b].
+ */
+void oracle_conv1d_silu(int64_t Bn, int64_t L, int64_t C, int64_t W,
+                        const double* xbc, const double* w, const double* bias,
+                        const double* conv_in, double* out, double* conv_out) {
+  const int64_t R = W - 1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < Bn; ++b) {
+    for (int64_t c = 0; c < C; ++c) {
+      for (int64_t t = 0; t < L; ++t) {
+        double acc = bias ? bias[c] : 0.0;
+        for (int64_t k = 0; k < W; ++k) {
+          int64_t e = t + k; /* row of ext */
+          double v;
+          if (e < R)
+            v = conv_in ? conv_in[(b * R + e) * C + c] : 0.0;
+          else
+            v = xbc[(b * L + (e - R)) * C + c];
+          acc += w[c * W + k] * v;
+        }
+        out[(b * L + t) * C + c] = silu(acc);
+      }
+      if (conv_out) {
+        for (int64_t r = 0; r < R; ++r) {
+          int64_t e = L + r;
+          double v;
+          if (e < R)
+            v = conv_in ? conv_in[(b * R + e) * C + c] : 0.0;
+          else
+            v = xbc[(b * L + (e - R)) * C + c];
+          conv_out[(b * R + r) * C + c] = v;
+        }
+      }
+    }
+  }
+}
+
+/*
+ * Sequential selective-state-space recurrence, one token at a time.
+ * x [B,L,H,P]; dt [B,L,H]; A [H]; Bm, Cm [B,L,G,N]; D [H] or NULL;
+ * s_in [B,H,P,N] or NULL (zeros); y [B,L,H,P]; s_out [B,H,P,N] or NULL.
+ * Per (b, h) with g = h / (H/G):
+ *   S = s_in[b,h]
+ *   for t: a = exp(dt*A[h]); S = a*S + dt * x_t (outer) B_t;
+ *          y_t[p] = sum_n S[p,n] C_t[n] + D[h] x_t[p]
+ */
+void oracle_ssm_scan(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t G,
+                     int64_t N, const double* x, const double* dt,
+                     const double* A, const double* Bm, const double* Cm,
+                     const double* D, const double* s_in, double* y,
+                     double* s_out) {
+  const int64_t hpg = H / G;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < Bn; ++b) {
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / hpg;
+      double* S = (double*)malloc((size_t)(P * N) * sizeof(double));
+      for (int64_t i = 0; i < P * N; ++i)
+        S[i] = s_in ? s_in[((b * H + h) * P) * N + i] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const double d = dt[(b * L + t) * H + h];
+        const double a = exp(d * A[h]);
+        const double* xt = x + ((b * L + t) * H + h) * P;
+        const double* Bt = Bm + ((b * L + t) * G + g) * N;
+        const double* Ct = Cm + ((b * L + t) * G + g) * N;
+        double* yt = y + ((b * L + t) * H + h) * P;
+        for (int64_t p = 0; p < P; ++p) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            double s = a * S[p * N + n] + d * xt[p] * Bt[n];
+            S[p * N + n] = s;
+            acc += s * Ct[n];
+          }
+          yt[p] = acc + (D ? D[h] * xt[p] : 0.0);
+        }
+      }
+      if (s_out)
+        for (int64_t i = 0; i < P * N; ++i) s_out[((b * H + h) * P) * N + i] = S[i];
+      free(S);
+    }
+  }
+}
+
+/*
+ * Grouped gated RMSNorm. y, z [rows, HP]; w [HP]; out [rows, HP].
+ * For each row and group j of S = HP/G contiguous channels:
+ *   q_c = y_c * silu(z_c); out_c = q_c * w_c / sqrt(mean_j(q^2) + eps).
+ */
+void oracle_gated_rmsnorm(int64_t rows, int64_t HP, int64_t G, const double* y,
+                          const double* z, const double* w, double eps,
+                          double* out) {
+  const int64_t S = HP / G;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t j = 0; j < G; ++j) {
+      const int64_t c0 = r * HP + j * S;
+      double ss = 0.0;
+      for (int64_t c = 0; c < S; ++c) {
+        double q = y[c0 + c] * silu(z[c0 + c]);
+        ss += q * q;
+      }
+      const double inv = 1.0 / sqrt(ss / (double)S + eps);
+      for (int64_t c = 0; c < S; ++c) {
+        double q = y[c0 + c] * silu(z[c0 + c]);
+        out[c0 + c] = q * w[j * S + c] * inv;
+      }
+    }
+  }
+}
+
+/*
+ * Whole mixer core on a prefill of L tokens:
+ * conv+SiLU over xbc [B,L,Cch] (Cch = H*P + 2*G*N, channel order x | B | C),
+ * split, recurrence, then the gated norm with z [B,L,H*P] when z != NULL
+ * (else out = y). y_pre [B,L,H*P] (optional) receives the pre-norm y.
+ */
+void oracle_mixer_prefill(int64_t Bn, int64_t L, int64_t H, int64_t P,
+                          int64_t G, int64_t N, int64_t W, const double* xbc,
+                          const double* z, const double* dt, const double* A,
+                          const double* D, const double* conv_w,
+                          const double* conv_b, const double* norm_w,
+                          double eps, const double* conv_in, double* conv_out,
+                          const double* s_in, double* s_out, double* out,
+                          double* y_pre) {
+  const int64_t HP = H * P, GN = G * N, C = HP + 2 * GN;
+  const int64_t T = Bn * L;
+  double* v = (double*)malloc((size_t)(T * C) * sizeof(double));
+  double* x = (double*)malloc((size_t)(T * HP) * sizeof(double));
+  double* Bm = (double*)malloc((size_t)(T * GN) * sizeof(double));
+  double* Cm = (double*)malloc((size_t)(T * GN) * sizeof(double));
+  double* y = (double*)malloc((size_t)(T * HP) * sizeof(double));
+  oracle_conv1d_silu(Bn, L, C, W, xbc, conv_w, conv_b, conv_in, v, conv_out);
+  for (int64_t i = 0; i < T; ++i) {
+    memcpy(x + i * HP, v + i * C, (size_t)HP * sizeof(double));
+    memcpy(Bm + i * GN, v + i * C + HP, (size_t)GN * sizeof(double));
+    memcpy(Cm + i * GN, v + i * C + HP + GN, (size_t)GN * sizeof(double));
+  }
+  oracle_ssm_scan(Bn, L, H, P, G, N, x, dt, A, Bm, Cm, D, s_in, y, s_out);
+  if (y_pre) memcpy(y_pre, y, (size_t)(T * HP) * sizeof(double));
+  if (z)
+    oracle_gated_rmsnorm(T, HP, G, y, z, norm_w, eps, out);
+  else
+    memcpy(out, y, (size_t)(T * HP) * sizeof(double));
+  free(v); free(x); free(Bm); free(Cm); free(y);
+}
+
+/*
+ * One decode token per sequence, states updated in place:
+ * xbc_t [B,Cch], z_t [B,HP] or NULL, dt_t [B,H], conv_state [B,W-1,Cch],
+ * ssm_state [B,H,P,N]; out [B,HP]. The new conv state is the last W-1 rows
+ * of [old state ; token].
+ */
+void oracle_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t G,
+                        int64_t N, int64_t W, const double* xbc_t,
+                        const double* z_t, const double* dt_t, const double* A,
+                        const double* D, const double* conv_w,
+                        const double* conv_b, const double* norm_w, double eps,
+                        double* conv_state, double* ssm_state, double* out) {
+  const int64_t HP = H * P, C = HP + 2 * G * N, R = W - 1;
+  double* cs_new = (double*)malloc((size_t)(Bn * R * C + 1) * sizeof(double));
+  double* s_new = (double*)malloc((size_t)(Bn * H * P * N) * sizeof(double));
+  oracle_mixer_prefill(Bn, 1, H, P, G, N, W, xbc_t, z_t, dt_t, A, D, conv_w,
+                       conv_b, norm_w, eps, conv_state, cs_new, ssm_state,
+                       s_new, out, NULL);
+  memcpy(conv_state, cs_new, (size_t)(Bn * R * C) * sizeof(double));
+  memcpy(ssm_state, s_new, (size_t)(Bn * H * P * N) * sizeof(double));
+  free(cs_new); free(s_new);
+}
+
+/* Threads the OpenMP runtime will use (reported beside CPU timings). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
