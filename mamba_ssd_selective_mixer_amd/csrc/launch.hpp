@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family). The
+// C-ABI layer validates every argument before it calls any of these.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct ScanShape {
+  int B, L, H, P, G, N, Q, nc;
+};
+
+// Depthwise causal conv + SiLU; io_bf16 selects bf16 (else fp32) elements.
+hipError_t launch_conv1d(bool io_bf16, int B, int L, int C, int W, const void* xbc,
+                         int64_t xs, const void* w, const void* bias, const void* cin,
+                         void* out, int64_t os, hipStream_t st);
+// conv_out[b] = last W-1 rows of [cin[b] ; xbc[b]] (safe when cout == cin).
+hipError_t launch_conv_state(bool io_bf16, int B, int L, int C, int W, const void* xbc,
+                             int64_t xs, const void* cin, void* cout, hipStream_t st);
+// Grouped gated RMSNorm; y_f32 says y is fp32 (else io dtype).
+hipError_t launch_gated_norm(bool io_bf16, bool y_f32, int rows, int HP, int G,
+                             const void* y, const void* z, const void* w, float eps,
+                             void* out, hipStream_t st);
+// One decode token per sequence.
+hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
+                         const void* xbc, const void* z, const void* dt, const float* A,
+                         const float* D, const void* cw, const void* cb, const void* nw,
+                         float eps, void* conv_state, float* ssm_state, void* y,
+                         hipStream_t st);
+// Chunked scan, three phases: chunk states, state passing, chunk outputs.
+hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
+                              const void* dt, const float* A, const void* Bm, int64_t bs,
+                              float* states, float* lam_end, hipStream_t st);
+hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
+                             const float* s_in, float* s_out, hipStream_t st);
+hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
+                            const void* dt, const float* A, const float* D, const void* Bm,
+                            const void* Cm, int64_t bs, const float* states, void* y,
+                            bool y_f32, hipStream_t st);
+
+}  // namespace ssd

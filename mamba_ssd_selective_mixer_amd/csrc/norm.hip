@@ -1,0 +1,68 @@
+// Grouped gated RMSNorm ("feat(model): Nemotron-H hybrid ... on the CPU",
+// section "2. feat(model)": GatedRMSNorm after the scan; "feat(model): add
+// Nemotron-3 Nano hybrid ..." attribution commit: GatedRMSNorm semantics).
+//
+// For each row and each of G groups of S = HP/G contiguous channels:
+//   q = y * silu(z);  out = q * w / sqrt(mean(q^2) + eps).
+// One workgroup per row; each wave reduces whole groups with 8-channel
+// vector accesses and a wave64 butterfly sum, then re-reads its group (from
+// L1/L2) to scale and store.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+
+template <class T, class TY>
+__global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
+                                                    const T* __restrict__ z,
+                                                    const T* __restrict__ w, float eps,
+                                                    T* out, int HP, int G) {
+  const int64_t row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int S = HP / G, S8 = S / 8;
+  for (int j = wave; j < G; j += 4) {
+    const int64_t base = row * HP + (int64_t)j * S;
+    float ss = 0.f;
+    for (int v = lane; v < S8; v += 64) {
+      float yv[8], zv[8];
+      load8(y + base + v * 8, yv);
+      load8(z + base + v * 8, zv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = yv[i] * silu(zv[i]);
+        ss += q * q;
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = __builtin_amdgcn_rsqf(ss / (float)S + eps);
+    for (int v = lane; v < S8; v += 64) {
+      float yv[8], zv[8], wv[8], o[8];
+      load8(y + base + v * 8, yv);
+      load8(z + base + v * 8, zv);
+      load8(w + (int64_t)j * S + v * 8, wv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = yv[i] * silu(zv[i]) * wv[i] * inv;
+      store8(out + base + v * 8, o);
+    }
+  }
+}
+
+hipError_t launch_gated_norm(bool io_bf16, bool y_f32, int rows, int HP, int G, const void* y,
+                             const void* z, const void* w, float eps, void* out,
+                             hipStream_t st) {
+  dim3 grid(rows), block(256);
+  if (io_bf16) {
+    if (y_f32)
+      hipLaunchKernelGGL((k_gated_norm<bf16, float>), grid, block, 0, st, (const float*)y,
+                         (const bf16*)z, (const bf16*)w, eps, (bf16*)out, HP, G);
+    else
+      hipLaunchKernelGGL((k_gated_norm<bf16, bf16>), grid, block, 0, st, (const bf16*)y,
+                         (const bf16*)z, (const bf16*)w, eps, (bf16*)out, HP, G);
+  } else {
+    hipLaunchKernelGGL((k_gated_norm<float, float>), grid, block, 0, st, (const float*)y,
+                       (const float*)z, (const float*)w, eps, (float*)out, HP, G);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssd

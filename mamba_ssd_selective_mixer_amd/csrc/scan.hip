@@ -1,0 +1,347 @@
+// Chunked state-space-duality (SSD) scan on gfx950: the block decomposition
+// of the selective recurrence ("feat(model): add Nemotron-3 Nano hybrid ..."
+// attribution commit: the chunk-parallel SSD block decomposition,
+// ssd_minimal_discrete / segsum).
+//
+// For chunk k = [t0, t0 + Q) of head h (group g = h / (H/G)), with
+// a_t = dt_t A_h and the inclusive segment sum Lam_t = sum_{r=t0..t} a_r:
+//   chunk state   dS_k[p,n] = sum_s exp(Lam_end - Lam_s) dt_s x_s[p] B_s[n]
+//   state passing S_in(0) = S_init, S_in(k+1) = exp(Lam_end,k) S_in(k) + dS_k
+//   chunk output  y_t[p] = sum_{s<=t} (C_t . B_s) exp(Lam_t - Lam_s) dt_s x_s[p]
+//                          + exp(Lam_t) (S_in(k) C_t)[p] + D_h x_t[p]
+// The three dense contractions (B^T (w x), C B^T, and the masked (C B^T) X
+// together with C S_in^T) run on 16x16 MFMA tiles: bf16 operands with fp32
+// accumulation for bf16 I/O, fp32 operands for fp32 I/O. Decays are always
+// formed as exp(Lam_t - Lam_s) of a masked difference, never as a ratio of
+// exponentials, so they stay finite for any chunk length.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+
+constexpr int kScanThreads = 256;  // 4 waves
+constexpr int kStateSB = 64;       // tokens staged per block in the chunk-state kernel
+
+template <class T> struct Pad { static constexpr int v = 8; };     // bf16: 16 bytes per LDS row
+template <> struct Pad<float> { static constexpr int v = 4; };
+
+// Inclusive cumulative sum of a_s = dt_s * A over the chunk (s < len; zero
+// beyond) into lam[], and dt_s into dts[]. Q <= 256 = blockDim.
+template <class T>
+__device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, int64_t row0, int H, int h,
+                                             float Ah, int len, float* lam, float* dts,
+                                             float* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float d = 0.f;
+  if (tid < len) d = to_f(dt[(row0 + tid) * H + h]);
+  float v = d * Ah;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  float add = 0.f;
+  for (int w = 0; w < wave; ++w) add += wsum[w];
+  lam[tid] = v + add;
+  dts[tid] = d;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1: chunk states dS_k = (w x)^T B per (chunk, head, batch).
+template <class T>
+__global__ __launch_bounds__(kScanThreads) void k_chunk_state(
+    const T* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, int64_t bs, float* __restrict__ states,
+    float* __restrict__ lam_end, int L, int H, int G, int P, int N, int Q, int nc) {
+  using M = Mfma<T>;
+  constexpr int KP = kStateSB + Pad<T>::v;
+  extern __shared__ __align__(16) unsigned char smraw[];
+  T* XwT = reinterpret_cast<T*>(smraw);  // [P][KP]  x_s[p] * w_s, k = s contiguous
+  T* BT = XwT + P * KP;                  // [N][KP]  B_s[n]
+  __shared__ float lam[kScanThreads], dts[kScanThreads], wgt[kScanThreads], wsum[4];
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const int t0 = c * Q, len = min(Q, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  chunk_cumsum<T>(dt, row0, H, h, A[h], len, lam, dts, wsum);
+  const float lamE = lam[len - 1];
+  wgt[tid] = tid < len ? fexp(lamE - lam[tid]) * dts[tid] : 0.f;
+  __syncthreads();
+
+  const int ntn = N / 16, tiles = (P / 16) * ntn;
+  constexpr int kMaxTPW = 16;  // (128/16)*(128/16)/4
+  f32x4 acc[kMaxTPW];
+#pragma unroll
+  for (int i = 0; i < kMaxTPW; ++i) acc[i] = zero4();
+
+  const int P8 = P / 8, N8 = N / 8;
+  for (int s0 = 0; s0 < len; s0 += kStateSB) {
+    for (int v = tid; v < kStateSB * P8; v += kScanThreads) {
+      const int s = v / P8, p0 = (v % P8) * 8;
+      float xv[8];
+      if (s0 + s < len) {
+        load8(x + (row0 + s0 + s) * xs + (int64_t)h * P + p0, xv);
+        const float ww = wgt[s0 + s];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] *= ww;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<T>(xv[j]);
+    }
+    for (int v = tid; v < kStateSB * N8; v += kScanThreads) {
+      const int s = v / N8, n0 = (v % N8) * 8;
+      float bv[8];
+      if (s0 + s < len) {
+        load8(Bm + (row0 + s0 + s) * bs + (int64_t)g * N + n0, bv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<T>(bv[j]);
+    }
+    __syncthreads();
+    const int kk = M::KPL * (lane >> 4), rr = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kMaxTPW; ++i) {
+      const int tile = wave + 4 * i;
+      if (tile < tiles) {
+        const int tp = tile / ntn, tn = tile % ntn;
+        const T* ap = XwT + (tp * 16 + rr) * KP + kk;
+        const T* bp = BT + (tn * 16 + rr) * KP + kk;
+#pragma unroll
+        for (int k = 0; k < kStateSB; k += M::KSTEP)
+          acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
+      }
+    }
+    __syncthreads();
+  }
+
+  float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+#pragma unroll
+  for (int i = 0; i < kMaxTPW; ++i) {
+    const int tile = wave + 4 * i;
+    if (tile < tiles) {
+      const int tp = tile / ntn, tn = tile % ntn;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = tp * 16 + 4 * (lane >> 4) + r, n = tn * 16 + (lane & 15);
+        out[(int64_t)p * N + n] = acc[i][r];
+      }
+    }
+  }
+  if (tid == 0) lam_end[((int64_t)b * H + h) * nc + c] = lamE;
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2: state passing along the chunks, in place: states[k] := S_in(k).
+__global__ __launch_bounds__(kScanThreads) void k_state_pass(float* states,
+                                                             const float* __restrict__ lam_end,
+                                                             const float* s_in, float* s_out,
+                                                             int H, int PN, int nc) {
+  const int e = (blockIdx.x * kScanThreads + threadIdx.x) * 4;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (e >= PN) return;
+  const int64_t bh = (int64_t)b * H + h;
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (s_in) S = *reinterpret_cast<const float4*>(s_in + bh * PN + e);
+  for (int c = 0; c < nc; ++c) {
+    float* p = states + (((int64_t)b * nc + c) * H + h) * PN + e;
+    const float4 d = *reinterpret_cast<const float4*>(p);
+    *reinterpret_cast<float4*>(p) = S;
+    const float al = fexp(lam_end[bh * nc + c]);
+    S.x = al * S.x + d.x;
+    S.y = al * S.y + d.y;
+    S.z = al * S.z + d.z;
+    S.w = al * S.w + d.w;
+  }
+  if (s_out) *reinterpret_cast<float4*>(s_out + bh * PN + e) = S;
+}
+
+// ---------------------------------------------------------------------------
+// Phase 3: chunk outputs. Each wave owns 16-row tiles of the chunk: it forms
+// the causal tiles of M = (C B^T) o exp(Lam_t - Lam_s) in its LDS slab, then
+// y = M (dt x) + exp(Lam_t) C S_in^T + D x for every 16-column tile of P.
+template <class T, bool YF32>
+__global__ __launch_bounds__(kScanThreads) void k_chunk_out(
+    const T* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, const T* __restrict__ Bm, const T* __restrict__ Cm, int64_t bs,
+    const float* __restrict__ states, void* __restrict__ yout, int L, int H, int G, int P,
+    int N, int Q, int nc) {
+  using M = Mfma<T>;
+  const int QK = Q + Pad<T>::v;
+  extern __shared__ __align__(16) unsigned char smraw[];
+  T* XdtT = reinterpret_cast<T*>(smraw);  // [P][QK]  dt_s x_s[p], k = s contiguous
+  T* Mall = XdtT + P * QK;                // [4 waves][16][QK]
+  __shared__ float lam[kScanThreads], dts[kScanThreads], wsum[4];
+
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / G);
+  const int t0 = c * Q, len = min(Q, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kk = M::KPL * (lane >> 4), rr = lane & 15;
+
+  chunk_cumsum<T>(dt, row0, H, h, A[h], len, lam, dts, wsum);
+
+  const int P8 = P / 8;
+  for (int v = tid; v < Q * P8; v += kScanThreads) {
+    const int s = v / P8, p0 = (v % P8) * 8;
+    float xv[8];
+    if (s < len) {
+      load8(x + (row0 + s) * xs + (int64_t)h * P + p0, xv);
+      const float d = dts[s];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] *= d;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) XdtT[(p0 + j) * QK + s] = from_f<T>(xv[j]);
+  }
+  __syncthreads();
+
+  const float* Sin = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  const float Dh = D ? D[h] : 0.f;
+  T* Mw = Mall + wave * 16 * QK;
+  const T* Cg = Cm + (int64_t)g * N;
+  const T* Bg = Bm + (int64_t)g * N;
+  const int nrt = (len + 15) / 16;
+  for (int rt0 = 0; rt0 < nrt; rt0 += 4) {
+    const int rt = rt0 + wave;
+    const bool active = rt < nrt;
+    const int ns = (rt + 1) * 16;
+    const int nsr = (ns + M::KSTEP - 1) / M::KSTEP * M::KSTEP;
+    const int trow = rt * 16 + rr;  // A-operand row of this lane
+    const bool trow_ok = active && trow < len;
+    if (active) {
+      for (int st = 0; st <= rt; ++st) {
+        const int scol = st * 16 + rr;
+        const bool scol_ok = scol < len;
+        f32x4 gacc = zero4();
+        for (int k = 0; k < N; k += M::KSTEP) {
+          typename M::frag fa, fb;
+          if (trow_ok) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          else fa = typename M::frag{};
+          if (scol_ok) fb = M::ld(Bg + (row0 + scol) * bs + k + kk);
+          else fb = typename M::frag{};
+          gacc = M::mma(fa, fb, gacc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
+          float m = 0.f;
+          if (s <= t && t < len) m = gacc[r] * fexp(lam[t] - lam[s]);
+          Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<T>(m);
+        }
+      }
+      for (int s = ns + (lane & 15); s < nsr; s += 16)
+        for (int r = 0; r < 4; ++r) Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<T>(0.f);
+    }
+    __syncthreads();
+    if (active) {
+      for (int pt = 0; pt < P / 16; ++pt) {
+        f32x4 acc = zero4(), acc2 = zero4();
+        const T* mp = Mw + rr * QK + kk;
+        const T* xp = XdtT + (pt * 16 + rr) * QK + kk;
+        for (int k = 0; k < nsr; k += M::KSTEP) acc = M::mma(M::ld(mp + k), M::ld(xp + k), acc);
+        const float* sp = Sin + (int64_t)(pt * 16 + rr) * N + kk;
+        for (int k = 0; k < N; k += M::KSTEP) {
+          typename M::frag fa;
+          if (trow_ok) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          else fa = typename M::frag{};
+          acc2 = M::mma(fa, M::cvt(sp + k), acc2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt * 16 + 4 * (lane >> 4) + r, p = pt * 16 + (lane & 15);
+          if (t < len) {
+            const float xv = to_f(x[(row0 + t) * xs + (int64_t)h * P + p]);
+            const float yv = acc[r] + fexp(lam[t]) * acc2[r] + Dh * xv;
+            const int64_t o = (row0 + t) * (int64_t)H * P + (int64_t)h * P + p;
+            if (YF32) reinterpret_cast<float*>(yout)[o] = yv;
+            else reinterpret_cast<T*>(yout)[o] = from_f<T>(yv);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+static size_t state_lds(bool bf, int P, int N) {
+  const int KP = kStateSB + (bf ? 8 : 4);
+  return (size_t)(P + N) * KP * (bf ? 2 : 4);
+}
+static size_t out_lds(bool bf, int P, int Q) {
+  const int QK = Q + (bf ? 8 : 4);
+  return (size_t)(P + 4 * 16) * QK * (bf ? 2 : 4);
+}
+
+hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
+                              const void* dt, const float* A, const void* Bm, int64_t bs,
+                              float* states, float* lam_end, hipStream_t st) {
+  dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
+  const size_t lds = state_lds(io_bf16, s.P, s.N);
+  if (io_bf16) {
+    hipLaunchKernelGGL(k_chunk_state<bf16>, grid, block, lds, st, (const bf16*)x, xs,
+                       (const bf16*)dt, A, (const bf16*)Bm, bs, states, lam_end, s.L, s.H, s.G,
+                       s.P, s.N, s.Q, s.nc);
+  } else {
+    hipLaunchKernelGGL(k_chunk_state<float>, grid, block, lds, st, (const float*)x, xs,
+                       (const float*)dt, A, (const float*)Bm, bs, states, lam_end, s.L, s.H,
+                       s.G, s.P, s.N, s.Q, s.nc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
+                             const float* s_in, float* s_out, hipStream_t st) {
+  const int PN = s.P * s.N;
+  dim3 grid((PN / 4 + kScanThreads - 1) / kScanThreads, s.H, s.B), block(kScanThreads);
+  hipLaunchKernelGGL(k_state_pass, grid, block, 0, st, states, lam_end, s_in, s_out, s.H, PN,
+                     s.nc);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
+                            const void* dt, const float* A, const float* D, const void* Bm,
+                            const void* Cm, int64_t bs, const float* states, void* y, bool y_f32,
+                            hipStream_t st) {
+  dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
+  const size_t lds = out_lds(io_bf16, s.P, s.Q);
+#define SSD_OUT(TT, YF)                                                                          \
+  do {                                                                                           \
+    hipLaunchKernelGGL((k_chunk_out<TT, YF>), grid, block, lds, st, (const TT*)x, xs,            \
+                       (const TT*)dt, A, D, (const TT*)Bm, (const TT*)Cm, bs, states, y, s.L,    \
+                       s.H, s.G, s.P, s.N, s.Q, s.nc);                                           \
+  } while (0)
+  if (io_bf16) {
+    if (y_f32) SSD_OUT(bf16, true);
+    else SSD_OUT(bf16, false);
+  } else {
+    SSD_OUT(float, true);
+  }
+#undef SSD_OUT
+  return hipGetLastError();
+}
+
+// LDS bytes the two MFMA kernels need for a shape (the host checks these
+// against the 160 KiB of one CU before launching).
+size_t scan_lds_bytes(bool io_bf16, int P, int N, int Q) {
+  const size_t a = state_lds(io_bf16, P, N), b = out_lds(io_bf16, P, Q);
+  return a > b ? a : b;
+}
+
+}  // namespace ssd
