@@ -79,14 +79,22 @@ int check_dims(int entry, const ssd_dims* d) {
 int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
 struct ScanWs {
+  bool fast;
   float* states;
   float* lam_end;
   float* y32;
   unsigned char* conv;
+  void* fastws;
   size_t total;
 };
 
-ScanWs carve(const ssd_dims* d, void* base, bool with_conv) {
+bool use_fast(const ssd_dims* d, bool conv) {
+  return ssd::fast_path_ok(d->io_dtype == SSD_BF16, d->headdim, d->dstate, d->nheads, d->ngroups,
+                           d->chunk, d->conv_width, conv);
+}
+
+// Workspace layout for the scan (conv = the scan consumes raw xBC rows).
+ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   ScanWs w{};
   const size_t B = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
   const size_t nc = nchunks(d);
@@ -96,17 +104,29 @@ ScanWs carve(const ssd_dims* d, void* base, bool with_conv) {
     off += round_up(bytes, kWsAlign);
     return o;
   };
-  const size_t o_states = take(B * nc * H * P * N * 4);
-  const size_t o_lam = take(B * H * nc * 4);
-  const size_t o_y = take(B * L * H * P * 4);
-  const size_t o_conv = with_conv ? take(B * L * (size_t)channels(d) * esize(d)) : 0;
+  w.fast = use_fast(d, conv);
+  size_t o_states = 0, o_lam = 0, o_y = 0, o_conv = 0, o_fast = 0;
+  if (w.fast) {
+    o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads));
+    if (d->nheads / d->ngroups != 4) o_y = take(B * L * H * P * 4);
+  } else {
+    o_states = take(B * nc * H * P * N * 4);
+    o_lam = take(B * H * nc * 4);
+    o_y = take(B * L * H * P * 4);
+    if (conv) o_conv = take(B * L * (size_t)channels(d) * esize(d));
+  }
   w.total = off;
   if (base) {
     unsigned char* p = (unsigned char*)base;
-    w.states = (float*)(p + o_states);
-    w.lam_end = (float*)(p + o_lam);
-    w.y32 = (float*)(p + o_y);
-    w.conv = with_conv ? p + o_conv : nullptr;
+    if (w.fast) {
+      w.fastws = p + o_fast;
+      w.y32 = o_y ? (float*)(p + o_y) : nullptr;
+    } else {
+      w.states = (float*)(p + o_states);
+      w.lam_end = (float*)(p + o_lam);
+      w.y32 = (float*)(p + o_y);
+      w.conv = conv ? p + o_conv : nullptr;
+    }
   }
   return w;
 }
@@ -133,6 +153,39 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
                                            d->nheads * d->headdim, d->ngroups, ws.y32, z,
                                            norm_w, eps, y, st));
   return rc;
+}
+
+int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const void* Cm,
+             int64_t xs, int64_t bs, const void* dt, const float* A, const float* D,
+             const void* conv_w, const void* conv_b, const void* conv_in, const void* z,
+             const void* norm_w, float eps, const float* s_in, float* s_out, void* y,
+             const ScanWs& ws, hipStream_t st) {
+  ssd::FastScanArgs a{};
+  a.B = d->batch;
+  a.L = d->seqlen;
+  a.H = d->nheads;
+  a.G = d->ngroups;
+  a.x = x;
+  a.Bm = Bm;
+  a.Cm = Cm;
+  a.xs = xs;
+  a.bs = bs;
+  a.dt = dt;
+  a.A = A;
+  a.D = D;
+  a.conv = conv;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.conv_in = conv_in;
+  a.z = z;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.s_in = s_in;
+  a.s_out = s_out;
+  a.y = y;
+  a.y32 = ws.y32;
+  a.ws = ws.fastws;
+  return hip_status(ssd::launch_fast_scan(a, st));
 }
 
 }  // namespace
@@ -234,6 +287,10 @@ int ssd_chunk_scan(const ssd_dims* d, const void* x, int64_t x_tok_stride, const
       any_overlap(workspace, need.total, y, ny) || any_overlap(workspace, need.total, x, nx))
     return SSD_ERR_ALIAS;
   const ScanWs ws = carve(d, workspace, false);
+  if (ws.fast)
+    return run_fast(d, false, x, Bm, Cm, x_tok_stride, bc_tok_stride, dt, A, D, nullptr, nullptr,
+                    nullptr, z, norm_w, eps, ssm_state_in, ssm_state_out, y, ws,
+                    (hipStream_t)stream);
   return run_scan(d, x, x_tok_stride, dt, A, D, Bm, Cm, bc_tok_stride, z, norm_w, eps,
                   ssm_state_in, ssm_state_out, y, ws, (hipStream_t)stream);
 }
@@ -315,6 +372,17 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
   const ScanWs ws = carve(d, workspace, true);
   hipStream_t st = (hipStream_t)stream;
   const bool bf = d->io_dtype == SSD_BF16;
+  const int64_t GN = (int64_t)d->ngroups * d->dstate;
+  if (ws.fast) {
+    // conv recomputed inside the scan kernels; the new conv state is taken
+    // after them because they read conv_state_in (which it may overwrite).
+    const unsigned char* xb = (const unsigned char*)xbc;
+    rc = run_fast(d, true, xbc, xb + HP * e, xb + (HP + GN) * e, C, C, dt, A, D, conv_w, conv_b,
+                  conv_state_in, z, norm_w, eps, ssm_state_in, ssm_state_out, out, ws, st);
+    if (rc || !conv_state_out) return rc;
+    return hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
+                                             C, conv_state_in, conv_state_out, st));
+  }
   rc = hip_status(ssd::launch_conv1d(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc, C,
                                      conv_w, conv_b, conv_state_in, ws.conv, C, st));
   if (rc) return rc;
@@ -324,7 +392,6 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
     if (rc) return rc;
   }
   const unsigned char* v = ws.conv;
-  const int64_t GN = (int64_t)d->ngroups * d->dstate;
   return run_scan(d, v, C, dt, A, D, v + HP * e, v + (HP + GN) * e, C, z, norm_w, eps,
                   ssm_state_in, ssm_state_out, out, ws, st);
 }

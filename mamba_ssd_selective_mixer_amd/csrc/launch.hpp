@@ -39,3 +39,34 @@ hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int
                             bool y_f32, hipStream_t st);
 
 }  // namespace ssd
+
+namespace ssd {
+
+// Fast path (head_dim 64, d_state 128, bf16, heads per group a multiple of 4).
+struct FastScanArgs {
+  int B, L, H, G;
+  const void* x;      // x rows (conv mode: the raw xBC rows)
+  const void* Bm;     // B rows (conv mode: xBC + H*P)
+  const void* Cm;     // C rows (conv mode: xBC + H*P + G*N)
+  int64_t xs, bs;     // token strides (elements)
+  const void* dt;
+  const float* A;
+  const float* D;
+  bool conv;          // recompute conv + SiLU from raw xBC rows
+  const void* conv_w;
+  const void* conv_b;
+  const void* conv_in;
+  const void* z;      // null: y is the scan output
+  const void* norm_w;
+  float eps;
+  const float* s_in;
+  float* s_out;
+  void* y;            // [B, L, H*P] bf16
+  float* y32;         // [B, L, H*P] fp32 scratch (norm groups wider than 4 heads)
+  void* ws;           // fast_ws_bytes(B, L, H) bytes, 256-byte aligned
+};
+bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
+size_t fast_ws_bytes(int B, int L, int H);
+hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st);
+
+}  // namespace ssd

@@ -6,7 +6,7 @@ Conv states are exact copies and must match bit for bit."""
 import numpy as np
 import pytest
 
-from gpu_util import TOL, check, dev, host, torch_dtype
+from gpu_util import TOL, check, check_head_scaled, dev, host, torch_dtype
 from mamba_ssd_selective_mixer_amd import synth
 from oracle import oracle
 
@@ -142,9 +142,11 @@ def test_chunk_scan_bf16(ops, kw):
 
 
 @pytest.mark.parametrize("Q", [32, 64, 128, 256])
-def test_chunk_scan_chunk_invariance(ops, Q):
-    """Every chunk length gives the oracle's answer (the SSD identity on the GPU)."""
-    scan_case(ops, small("c1", batch=1, seqlen=520), True, False, Q=Q)
+@pytest.mark.parametrize("dstate", [128, 64])
+def test_chunk_scan_chunk_invariance(ops, Q, dstate):
+    """Every chunk length gives the oracle's answer (the SSD identity on the GPU);
+    d_state 64 runs the generic kernels at the requested chunk length."""
+    scan_case(ops, small("c1", batch=1, seqlen=520, dstate=dstate), True, False, Q=Q)
 
 
 @pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=1, seqlen=700))])
@@ -222,7 +224,8 @@ def test_decode_bf16(ops, kw):
 
 
 # -------------------------------------------------------------- full prefill
-def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False, inplace=False):
+def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False, inplace=False,
+                 with_norm=True):
     """Whole path (conv -> scan -> norm) with state in/out; optional chaining
     over `pieces` (token boundaries) each resuming from the previous state."""
     import torch
@@ -230,7 +233,8 @@ def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False,
     prm = synth.layer_params(cfg, slow_decay=slow, with_bias=with_bias)
     inp = synth.prefill_inputs(cfg)
     st = synth.initial_states(cfg) if with_state else {"conv_state": None, "ssm_state": None}
-    ref = oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"],
+    zz = inp["z"] if with_norm else None
+    ref = oracle.mixer_prefill(inp["xbc"], zz, inp["dt"], prm["A"], prm["D"],
                                prm["conv_w"], prm["conv_b"], prm["norm_w"], prm["eps"],
                                cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
                                conv_in=st["conv_state"], s_in=st["ssm_state"])
@@ -244,14 +248,18 @@ def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False,
         d = make_dims(ops, cfg, seqlen=b - a)
         cs2 = cs if inplace else torch.empty_like(cs)
         ss2 = ss if inplace else torch.empty_like(ss)
-        out = ops.ssd_mixer_prefill(d, dev(inp["xbc"][:, a:b], td), dev(inp["z"][:, a:b], td),
+        out = ops.ssd_mixer_prefill(d, dev(inp["xbc"][:, a:b], td),
+                                    dev(zz[:, a:b], td) if with_norm else None,
                                     dev(inp["dt"][:, a:b], td), dev(prm["A"]), dev(prm["D"]),
                                     dev(prm["conv_w"], td), dev(prm["conv_b"], td),
                                     dev(prm["norm_w"], td), prm["eps"], cs, cs2, ss, ss2)
         outs.append(host(out))
         cs, ss = cs2, ss2
     tol = TOL[cfg.dtype]
-    check("prefill out", np.concatenate(outs, axis=1), ref["out"], tol)
+    if with_bias and not with_norm and cfg.dtype == "bf16":
+        check_head_scaled("prefill y", np.concatenate(outs, axis=1), ref["out"], tol, cfg.headdim)
+    else:
+        check("prefill out", np.concatenate(outs, axis=1), ref["out"], tol)
     check("prefill final state", host(ss), ref["s_out"], tol)
     assert np.array_equal(host(cs), ref["conv_out"])
 
@@ -266,6 +274,31 @@ def test_prefill_fp32_tiny_state_bias(ops):
 
 def test_prefill_bf16(ops):
     prefill_case(ops, small("c1", batch=2, seqlen=400), with_state=True)
+
+
+@pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333),   # 8 heads per group
+                                dict(batch=3, seqlen=129),
+                                dict(batch=1, seqlen=5, nheads=16, ngroups=4)])
+def test_prefill_bf16_shapes(ops, kw):
+    prefill_case(ops, small("c1", **kw), with_state=True)
+
+
+@pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333), dict(batch=3, seqlen=129)])
+def test_prefill_bf16_conv_bias(ops, kw):
+    """With a conv bias the whole prefill is checked before the norm (z = None),
+    with the tolerance scaled by the head's largest |y| at that token. bf16 B
+    and C carrying a shared bias offset make C.B^T sums whose operand rounding
+    no longer averages out and y reaches |16|; the error is then bounded by
+    the size of the summed terms, and after normalising by a small group RMS
+    it exceeds 2e-2 in rare elements for any bf16-operand kernel (shown by
+    emulating the rounding points on the CPU). Bias with the norm is checked
+    elementwise at fp32 I/O in test_prefill_fp32_tiny_state_bias."""
+    prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=False)
+
+
+def test_prefill_generic_shapes(ops):
+    """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
+    prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
 
 
 def test_prefill_pieces_uneven(ops):
