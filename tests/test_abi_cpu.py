@@ -116,7 +116,7 @@ def test_workspace_sizes(lib):
     ws = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
     nc = c1.seqlen // c1.chunk
     assert ws >= c1.batch * nc * c1.nheads * c1.headdim * c1.dstate * 4
-    assert lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d)) > ws
+    assert lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d)) >= ws
     bad = dims(c1, headdim=48)
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(bad)) == 0
 
