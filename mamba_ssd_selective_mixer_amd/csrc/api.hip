@@ -108,7 +108,6 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   size_t o_states = 0, o_lam = 0, o_y = 0, o_conv = 0, o_fast = 0;
   if (w.fast) {
     o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads));
-    if (d->nheads / d->ngroups != 4) o_y = take(B * L * H * P * 4);
   } else {
     o_states = take(B * nc * H * P * N * 4);
     o_lam = take(B * H * nc * 4);
@@ -120,7 +119,6 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
     unsigned char* p = (unsigned char*)base;
     if (w.fast) {
       w.fastws = p + o_fast;
-      w.y32 = o_y ? (float*)(p + o_y) : nullptr;
     } else {
       w.states = (float*)(p + o_states);
       w.lam_end = (float*)(p + o_lam);
@@ -183,7 +181,6 @@ int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const 
   a.s_in = s_in;
   a.s_out = s_out;
   a.y = y;
-  a.y32 = ws.y32;
   a.ws = ws.fastws;
   return hip_status(ssd::launch_fast_scan(a, st));
 }

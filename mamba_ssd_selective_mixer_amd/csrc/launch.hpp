@@ -61,8 +61,8 @@ struct FastScanArgs {
   float eps;
   const float* s_in;
   float* s_out;
-  void* y;            // [B, L, H*P] bf16
-  float* y32;         // [B, L, H*P] fp32 scratch (norm groups wider than 4 heads)
+  void* y;            // [B, L, H*P] bf16 (norm groups wider than 4 heads: y, then
+                      // normalised in place)
   void* ws;           // fast_ws_bytes(B, L, H) bytes, 256-byte aligned
 };
 bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
