@@ -28,7 +28,58 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA, TFLOP/s
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 / fp16 MFMA, TFLOP/s
+
+KERNEL_NAMES = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
+                "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
+                "fused_chunk_out_norm")
+DOMINANT = "fused_chunk_out_norm"
+# HBM bytes per launch of a kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counters, with the hash of the kernel sources they were taken on.
+TRAFFIC_FILES = {"fused_chunk_out_norm": "fused_chunk_out_norm.tiny_layer_prefill.traffic.txt"}
+KERNEL_SOURCES = ("mamba_ssd_selective_mixer_amd/csrc/scan_fast.hip",
+                  "mamba_ssd_selective_mixer_amd/csrc/common.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """Counter-measured HBM bytes per launch, or None when no measurement
+    exists or the kernel sources changed since it was taken."""
+    name = TRAFFIC_FILES.get(kernel)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of 512 MiB, run 5 times, so HBM counters
+    can be scaled by what they read for a known number of bytes."""
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
 def parse():
@@ -39,6 +90,10 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without the per-kernel HIP events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (for the HBM counter scale)")
     return ap.parse_args()
 
 
@@ -93,7 +148,10 @@ def to_dev(torch, a, dt):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda", dt)
 
 
-def run_prefill(torch, ops, synth, cfg, steps, warmup, nsets, with_states):
+def run_prefill(torch, ops, synth, cfg, steps, warmup, nsets, with_states, kernel_events=False):
+    """Mean ms per prefill call over `steps` timed calls; with kernel_events,
+    also {kernel: (launches, mean ms)} from the library's per-kernel HIP
+    events recorded over the same timed calls."""
     bf = torch.bfloat16
     prm = synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
@@ -124,9 +182,25 @@ def run_prefill(torch, ops, synth, cfg, steps, warmup, nsets, with_states):
     tm.start()
     for i in range(steps):
         step(i)
-    ms = tm.stop_ms()
+    ms = tm.stop_ms() / steps
     torch.cuda.synchronize()
-    return ms / steps
+    kern = {}
+    if kernel_events:
+        # The same timed steps again, each kernel launch bracketed by a pair of
+        # HIP events on its stream. The events add gaps between launches (not
+        # to the kernels), so the step time above comes from the first pass.
+        ops.profile_start(8 * steps)
+        tm.start()
+        for i in range(steps):
+            step(i)
+        kern["_step_ms"] = tm.stop_ms() / steps
+        torch.cuda.synchronize()
+        ops.profile_stop()
+        for name in KERNEL_NAMES:
+            n, t = ops.profile_read(name)
+            if n:
+                kern[name] = (n, t / n)
+    return ms, kern
 
 
 def run_chain(torch, ops, synth, cfg, reps, nsets_unused=None):
@@ -194,21 +268,25 @@ def run_decode(torch, ops, synth, cfg, reps):
     return ms / reps  # per 64-step loop
 
 
-def cpu_baseline(synth, cfg):
-    """The fp64 oracle on one full step of the headline workload, host cores."""
+def cpu_baseline(synth, cfg, budget_s=10.0):
+    """The fp64 oracle on full steps of the headline workload on the host
+    cores, repeated until about `budget_s` seconds of wall time are spent."""
     from oracle import oracle
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)
-    t = time.perf_counter()
-    oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"], prm["conv_w"],
-                         None, prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim, cfg.ngroups,
-                         cfg.dstate)
-    sec = time.perf_counter() - t
-    tokens = cfg.batch * cfg.seqlen
+    reps, sec = 0, 0.0
+    while sec < budget_s and reps < 100:
+        t = time.perf_counter()
+        oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"], prm["conv_w"],
+                             None, prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim,
+                             cfg.ngroups, cfg.dstate)
+        sec += time.perf_counter() - t
+        reps += 1
+    tokens = cfg.batch * cfg.seqlen * reps
     return {"value": tokens / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"one full step ({cfg.batch}x{cfg.seqlen} tokens), fp64 sequential "
-                      f"recurrence + conv + gated norm, {sec:.2f} s wall"}
+            "sample": f"{reps} full step(s) of {cfg.batch}x{cfg.seqlen} tokens (fp64 sequential "
+                      f"recurrence + conv + gated norm), {sec:.1f} s wall"}
 
 
 def main():
@@ -223,11 +301,33 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     cfg = synth.CONFIGS["c1"]
-    ms = run_prefill(torch, ops, synth, cfg, args.steps, args.warmup, args.sets, False)
+    ms, kern = run_prefill(torch, ops, synth, cfg, args.steps, args.warmup, args.sets, False,
+                           kernel_events=not args.no_kernel_events)
     tokens = cfg.batch * cfg.seqlen
     nbytes = prefill_bytes(cfg, cfg.seqlen, False)
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    # the dominant kernel: chunk output + fused gated norm. It reads every
+    # input of the step (xBC, z, dt) and writes the output, so its
+    # algorithmic bytes per launch are the step's.
+    if DOMINANT in kern:
+        k_ms = kern[DOMINANT][1]
+        roof = {"bound": "hbm", "kernel": DOMINANT, "achieved": nbytes / (k_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": nbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "traffic": measured_traffic(DOMINANT), "algorithmic_bytes": nbytes,
+                "kernel_us": k_ms * 1e3,
+                "kernels_us": {k: v[1] * 1e3 for k, v in kern.items() if k != "_step_ms"},
+                "events_pass_ms_per_step": kern["_step_ms"],
+                "step_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "step_mfma_tflops": prefill_flops(cfg, cfg.seqlen) / (ms * 1e-3) / 1e12}
+    else:
+        roof = {"bound": "hbm", "kernel": "whole prefill step", "achieved":
+                nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes": nbytes}
     rec = {
         "metric": "Mamba-2 mixer tokens/sec (prefill, decode) on 1 MI355X; % HBM/MFMA roofline",
         "value": tokens / (ms * 1e-3),
@@ -238,16 +338,12 @@ def main():
         "config": {"workload": "tiny-model layer prefill: batch 4 x 2048 tokens, 32 heads x 64, "
                                "8 groups, state 128, conv width 4, chunk 128",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "whole prefill step (ssd_mixer_prefill)",
-                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes": nbytes,
-                     "mfma_tflops": prefill_flops(cfg, cfg.seqlen) / (ms * 1e-3) / 1e12},
+        "roofline": roof,
     }
     if not args.quick:
         wl = {}
         c2 = synth.CONFIGS["c2"]
-        ms2 = run_prefill(torch, ops, synth, c2, max(3, args.steps // 5), 2, 2, True)
+        ms2, _ = run_prefill(torch, ops, synth, c2, max(3, args.steps // 5), 2, 2, True)
         b2 = prefill_bytes(c2, c2.seqlen, True)
         wl["large_prefill"] = {"tokens_per_s": c2.seqlen / (ms2 * 1e-3), "ms": ms2,
                                "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -193,6 +193,38 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z,
                       float* ssm_state_out, void* out, void* workspace,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Per-kernel timing of the library's own launches, a measurement aid (the
+ * timing is read on the stream each kernel runs on, so it needs no access
+ * to the caller's streams). ssd_profile_start(capacity) creates `capacity`
+ * pairs of HIP events and switches timing on: from then on every kernel
+ * launch of this library takes the next pair and records one event right
+ * before and one right after the kernel on its stream. Launches beyond
+ * `capacity` are not timed and ssd_profile_stop() then returns
+ * SSD_ERR_WORKSPACE. ssd_profile_read() waits for the recorded events of one
+ * kernel and returns how many launches were timed and their summed duration
+ * in milliseconds; it can be called any number of times until the next
+ * start, which drops the previous pool. The state is process-wide (calls are
+ * serialised by a lock); do not switch timing on while a stream is captured
+ * into a graph. Kernel identifiers: */
+typedef enum {
+  SSD_K_CONV1D = 0,          /* conv + SiLU over xBC, standalone      */
+  SSD_K_CONV_STATE = 1,      /* conv state out (last W-1 rows)        */
+  SSD_K_GATED_NORM = 2,      /* grouped gated RMSNorm, standalone     */
+  SSD_K_DECODE = 3,          /* one decode token                      */
+  SSD_K_CHUNK_STATE = 4,     /* generic path: chunk states            */
+  SSD_K_STATE_PASS = 5,      /* generic path: state passing           */
+  SSD_K_CHUNK_OUT = 6,       /* generic path: chunk output            */
+  SSD_K_FAST_STATE = 7,      /* fast path: conv + chunk states        */
+  SSD_K_FAST_PASS = 8,       /* fast path: state passing              */
+  SSD_K_FAST_OUT = 9,        /* fast path: conv + chunk output + norm */
+  SSD_K_COUNT = 10
+} ssd_kernel_id;
+int ssd_profile_start(int capacity);
+int ssd_profile_stop(void);
+int ssd_profile_read(int kernel, int64_t* launches, double* total_ms);
+const char* ssd_kernel_name(int kernel);
+
 #ifdef __cplusplus
 }
 #endif

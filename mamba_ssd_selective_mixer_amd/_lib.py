@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssd_mi355x.so")
 
 SSD_F32, SSD_BF16 = 0, 1
+KERNELS = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
+           "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
+           "fused_chunk_out_norm")
 ENTRY = {"conv1d": 0, "chunk_scan": 1, "gated_rmsnorm": 2, "decode_step": 3, "mixer_prefill": 4}
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_DTYPE", -5: "SSD_ERR_ALIAS", -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_HIP",
@@ -21,7 +24,8 @@ STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNS
 EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "ssd_validate",
            "ssd_status_str", "ssd_conv1d", "ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan",
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_mixer_prefill_workspace_bytes",
-           "ssd_mixer_prefill")
+           "ssd_mixer_prefill", "ssd_profile_start", "ssd_profile_stop", "ssd_profile_read",
+           "ssd_kernel_name")
 
 
 class Dims(ctypes.Structure):
@@ -58,6 +62,10 @@ def load():
         "ssd_mixer_prefill_workspace_bytes": (sz, [P]),
         "ssd_mixer_prefill": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
                                     vp, sz, vp]),
+        "ssd_profile_start": (i32, [i32]),
+        "ssd_profile_stop": (i32, []),
+        "ssd_profile_read": (i32, [i32, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]),
+        "ssd_kernel_name": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -112,6 +112,7 @@ static hipError_t conv_dispatch(int B, int L, int C, int W, const void* xbc, int
 hipError_t launch_conv1d(bool io_bf16, int B, int L, int C, int W, const void* xbc, int64_t xs,
                          const void* w, const void* bias, const void* cin, void* out, int64_t os,
                          hipStream_t st) {
+  ProfScope ps(st, KID_CONV1D);
   return io_bf16 ? conv_dispatch<bf16>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st)
                  : conv_dispatch<float>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st);
 }
@@ -133,6 +134,7 @@ static hipError_t conv_state_dispatch(int B, int L, int C, int W, const void* xb
 
 hipError_t launch_conv_state(bool io_bf16, int B, int L, int C, int W, const void* xbc,
                              int64_t xs, const void* cin, void* cout, hipStream_t st) {
+  ProfScope ps(st, KID_CONV_STATE);
   return io_bf16 ? conv_state_dispatch<bf16>(B, L, C, W, xbc, xs, cin, cout, st)
                  : conv_state_dispatch<float>(B, L, C, W, xbc, xs, cin, cout, st);
 }

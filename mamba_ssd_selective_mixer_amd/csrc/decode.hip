@@ -166,6 +166,7 @@ hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
                          const float* D, const void* cw, const void* cb, const void* nw,
                          float eps, void* conv_state, float* ssm_state, void* y,
                          hipStream_t st) {
+  ProfScope ps(st, KID_DECODE);
   return io_bf16 ? decode_dispatch<bf16>(B, H, P, G, N, W, xbc, z, dt, A, D, cw, cb, nw, eps,
                                          conv_state, ssm_state, y, st)
                  : decode_dispatch<float>(B, H, P, G, N, W, xbc, z, dt, A, D, cw, cb, nw, eps,

@@ -2,6 +2,8 @@
 // C-ABI layer validates every argument before it calls any of these.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "prof.hpp"
 #include <stdint.h>
 
 namespace ssd {

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
 hipError_t launch_gated_norm(bool io_bf16, bool y_f32, int rows, int HP, int G, const void* y,
                              const void* z, const void* w, float eps, void* out,
                              hipStream_t st) {
+  ProfScope ps(st, KID_GATED_NORM);
   dim3 grid(rows), block(256);
   if (io_bf16) {
     if (y_f32)

@@ -292,6 +292,7 @@ static size_t out_lds(bool bf, int P, int Q) {
 hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
                               const void* dt, const float* A, const void* Bm, int64_t bs,
                               float* states, float* lam_end, hipStream_t st) {
+  ProfScope ps(st, KID_CHUNK_STATE);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
   const size_t lds = state_lds(io_bf16, s.P, s.N);
   if (io_bf16) {
@@ -308,6 +309,7 @@ hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, i
 
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
                              const float* s_in, float* s_out, hipStream_t st) {
+  ProfScope ps(st, KID_STATE_PASS);
   const int PN = s.P * s.N;
   dim3 grid((PN / 4 + kScanThreads - 1) / kScanThreads, s.H, s.B), block(kScanThreads);
   hipLaunchKernelGGL(k_state_pass, grid, block, 0, st, states, lam_end, s_in, s_out, s.H, PN,
@@ -319,6 +321,7 @@ hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int
                             const void* dt, const float* A, const float* D, const void* Bm,
                             const void* Cm, int64_t bs, const float* states, void* y, bool y_f32,
                             hipStream_t st) {
+  ProfScope ps(st, KID_CHUNK_OUT);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
   const size_t lds = out_lds(io_bf16, s.P, s.Q);
 #define SSD_OUT(TT, YF)                                                                          \

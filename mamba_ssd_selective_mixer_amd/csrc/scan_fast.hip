@@ -714,16 +714,22 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   s.GN = a.G * N;
 
   dim3 g1(nc, a.B * (a.H / HB));
+  {
+  ProfScope ps(st, KID_FAST_STATE);
   if (a.conv)
     hipLaunchKernelGGL(k_fstate<true>, g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
                        lam_end, a.L, a.H, a.G, nc);
   else
     hipLaunchKernelGGL(k_fstate<false>, g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
                        lam_end, a.L, a.H, a.G, nc);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  {
+  ProfScope ps(st, KID_FAST_PASS);
   hipLaunchKernelGGL(k_fpass, dim3(PN / 1024, a.H, a.B), dim3(256), 0, st, dS, lam_end, a.s_in,
                      a.s_out, sinb, a.H, nc);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // fused norm when a norm group is exactly the 4-head block; otherwise y
@@ -733,12 +739,15 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_fout<CV, NM>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D,      \
                      sinb, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps, (bf16*)a.y, a.L, a.H, \
                      a.G, nc)
+  {
+  ProfScope ps(st, KID_FAST_OUT);
   if (a.conv) {
     if (fused) SSD_FOUT(true, true);
     else SSD_FOUT(true, false);
   } else {
     if (fused) SSD_FOUT(false, true);
     else SSD_FOUT(false, false);
+  }
   }
 #undef SSD_FOUT
   e = hipGetLastError();

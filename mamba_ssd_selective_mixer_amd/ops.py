@@ -194,3 +194,22 @@ def ssd_mixer_prefill(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps=
                                        _stream(stream))
     _check(rc, "ssd_mixer_prefill")
     return out
+
+
+def profile_start(capacity: int) -> None:
+    """Time every kernel launch of the library with a pair of HIP events on
+    the launch stream, for the next `capacity` launches."""
+    _check(_lib.load().ssd_profile_start(int(capacity)), "ssd_profile_start")
+
+
+def profile_stop() -> None:
+    _check(_lib.load().ssd_profile_stop(), "ssd_profile_stop")
+
+
+def profile_read(kernel: str) -> tuple[int, float]:
+    """(timed launches, summed milliseconds) of one kernel since profile_start."""
+    n = ctypes.c_int64(0)
+    ms = ctypes.c_double(0.0)
+    _check(_lib.load().ssd_profile_read(_lib.KERNELS.index(kernel), ctypes.byref(n),
+                                        ctypes.byref(ms)), "ssd_profile_read")
+    return int(n.value), float(ms.value)

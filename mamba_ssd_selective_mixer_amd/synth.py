@@ -77,11 +77,17 @@ def rng(cfg_index: int, stream: int) -> np.random.Generator:
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
-    """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
+    """Round finite fp32 values to the nearest bf16 (ties to even); returns
+    fp32. Works on the bit patterns in uint32 (no finite value carries out
+    of 32 bits)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    r += u
+    r &= 0xFFFF0000
+    return r.view(np.float32).reshape(a.shape)
 
 
 def to_io(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -131,3 +131,16 @@ def test_state_slot_size_matches_page_figure(lib):
     mib = g["mamba_layers"] * per_layer / 2 ** 20
     assert round(mib, 1) == g["mib_per_slot"]
     assert lib.ssd_conv_channels(ctypes.byref(d)) == 64 * 64 + 2 * 8 * 128
+
+
+def test_kernel_names_and_profile_arguments(lib):
+    """Kernel identifiers of the timing aid match the binding's table, and
+    reading checks its arguments before touching any event."""
+    for i, name in enumerate(_lib.KERNELS):
+        assert lib.ssd_kernel_name(i).decode() == name
+    assert lib.ssd_kernel_name(len(_lib.KERNELS)) == b"unknown"
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0)
+    assert lib.ssd_profile_read(len(_lib.KERNELS), ctypes.byref(n), ctypes.byref(ms)) == -2
+    assert lib.ssd_profile_read(0, None, ctypes.byref(ms)) == -1
+    assert lib.ssd_profile_read(0, ctypes.byref(n), ctypes.byref(ms)) == 0 and n.value == 0
+    assert lib.ssd_profile_start(0) == -2
