@@ -46,7 +46,8 @@
  * element size must be multiples of 16 bytes.
  *
  * Ownership. The caller owns every buffer and the stream; the library
- * allocates no device memory and keeps no mutable global state. Scratch
+ * allocates no device memory and keeps no mutable global state apart from
+ * the opt-in timing aid declared at the end of this header. Scratch
  * space comes from a caller-provided workspace of at least the size the
  * matching *_workspace_bytes() call returns (256-byte aligned).
  *
@@ -62,6 +63,19 @@
  * may be short), nheads % ngroups == 0, headdim in {16, 32, 64, 128},
  * dstate in {16, 32, 64, 128}, conv_width in {2, 3, 4},
  * chunk in {32, 64, 128, 256}.
+ *
+ * Precision. State, decay exponents, sums and the norm are fp32. The dense
+ * contractions of the chunked scan run on MFMA with fp32 accumulation: with
+ * fp32 operands for fp32 I/O; with bf16 operands for bf16 I/O outside the
+ * fast path; in the fast path (bf16 I/O,
+ * headdim 64, dstate 128, heads per group a multiple of 4, dims->chunk >= 64,
+ * conv width 4 when the call includes the conv; the norm is fused when a norm
+ * group is exactly 4 heads) with fp16 operands (B, C, x, the decay-masked
+ * C B^T, chunk states and carried-in states), with D x taken from x at fp16 hi + lo precision. Such operands must stay within
+ * fp16 range (|v| < 65504): activations after SiLU, dt-weighted states of
+ * magnitude beyond that are outside the fast path's envelope. In the fast
+ * path the chunk length is an internal choice (128 tokens); the result does
+ * not depend on dims->chunk beyond rounding.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
