@@ -47,6 +47,9 @@ struct Src {
 // states all stay far inside its range for normalised activations.
 typedef _Float16 f16;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+// Native 4 x 32-bit vector: arrays of it stay in registers (arrays of the
+// HIP uint4 struct can end up in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 SSD_DEV uint32_t pk(float a, float b) {
   const f16 lo = (f16)a, hi = (f16)b;
@@ -63,12 +66,15 @@ SSD_DEV void load8h(const f16* p, float (&v)[8]) {
     v[2 * i + 1] = h2f_hi(w[i]);
   }
 }
+// An empty asm that takes the values in registers: the computation of x
+// cannot be sunk past this point.
+SSD_DEV void pin(uint32_t (&x)[2]) { asm volatile("" : "+v"(x[0]), "+v"(x[1])); }
 SSD_DEV f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Unpack 8 bf16 (one 16-byte row segment) to fp32.
-SSD_DEV void unpack8(const uint4 u, float (&v)[8]) {
+SSD_DEV void unpack8(const u32x4 u, float (&v)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -93,18 +99,18 @@ SSD_DEV void conv_stage(const bf16* __restrict__ src, int64_t ts, int tseq, int 
                         const Src& s, int ch, const bf16* cin_b, const float* scale, f16* dst,
                         int ld, f16* lo = nullptr, int ldlo = 0) {
   constexpr int R = CONV ? W - 1 : 0;
-  uint4 raw[8 + R];
+  u32x4 raw[8 + R];
 #pragma unroll
   for (int i = 0; i < 8 + R; ++i) {
     const int t = tseq - R + i;
     const bf16* p = (CONV && t < 0 && cin_b) ? cin_b + (int64_t)(W - 1 + t) * s.C + ch
                                              : src + (int64_t)min(max(t, 0), Lm1) * ts;
-    raw[i] = *reinterpret_cast<const uint4*>(p);
+    raw[i] = *reinterpret_cast<const u32x4*>(p);
   }
-  uint4 wraw[4];  // 8 channels x 4 taps, bf16, element (j, k) at j*W + k
+  u32x4 wraw[4];  // 8 channels x 4 taps, bf16, element (j, k) at j*W + k
   float bi[8];
   if (CONV) {
-    const uint4* wp = reinterpret_cast<const uint4*>(s.cw + (int64_t)ch * W);
+    const u32x4* wp = reinterpret_cast<const u32x4*>(s.cw + (int64_t)ch * W);
 #pragma unroll
     for (int q = 0; q < 4; ++q) wraw[q] = wp[q];
     if (s.cbias) {
@@ -136,7 +142,7 @@ SSD_DEV void conv_stage(const bf16* __restrict__ src, int64_t ts, int tseq, int 
 #pragma unroll
         for (int k = 0; k < W; ++k) {
           const int e = j * W + k;  // bf16 element of the 32-element weight block
-          const uint32_t wd = (&wraw[e >> 3].x)[(e >> 1) & 3];
+          const uint32_t wd = wraw[e >> 3][(e >> 1) & 3];
           u += __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16)) * win[k][j];
         }
         u = silu(u);
@@ -173,85 +179,6 @@ SSD_DEV void conv_stage(const bf16* __restrict__ src, int64_t ts, int tseq, int 
     for (int j = 0; j < 8; ++j)
       *reinterpret_cast<uint4*>(dst + j * ld) = make_uint4(pk8[j][0], pk8[j][1], pk8[j][2], pk8[j][3]);
   }
-}
-
-// 4 tokens x 8 channels of conv+SiLU output (or of the plain input), for
-// the transposed x staging of the output kernel: fp16(x) goes to
-// dst + j*ld (4 tokens contiguous, 8 bytes per channel row) and x - fp16(x)
-// to lo + i*ldlo (8 channels contiguous per token row). Same load pattern as
-// conv_stage with half the rows in flight.
-template <bool CONV>
-SSD_DEV void conv_stage4(const bf16* __restrict__ src, int64_t ts, int tseq, int nvalid, int Lm1,
-                         const Src& s, int ch, const bf16* cin_b, f16* dst, int ld, f16* lo,
-                         int ldlo) {
-  constexpr int R = CONV ? W - 1 : 0;
-  uint4 raw[4 + R];
-#pragma unroll
-  for (int i = 0; i < 4 + R; ++i) {
-    const int t = tseq - R + i;
-    const bf16* p = (CONV && t < 0 && cin_b) ? cin_b + (int64_t)(W - 1 + t) * s.C + ch
-                                             : src + (int64_t)min(max(t, 0), Lm1) * ts;
-    raw[i] = *reinterpret_cast<const uint4*>(p);
-  }
-  uint4 wraw[4];
-  float bi[8];
-  if (CONV) {
-    const uint4* wp = reinterpret_cast<const uint4*>(s.cw + (int64_t)ch * W);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wraw[q] = wp[q];
-    if (s.cbias) {
-      load8(s.cbias + ch, bi);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bi[j] = 0.f;
-    }
-  }
-  float win[R + 1][8];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    unpack8(raw[i], win[i]);
-    if (tseq - R + i < 0 && !cin_b) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) win[i][j] = 0.f;
-    }
-  }
-  uint32_t pk4[8][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    unpack8(raw[i + R], win[R]);
-    float v[8], rem[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float u;
-      if (CONV) {
-        u = bi[j];
-#pragma unroll
-        for (int k = 0; k < W; ++k) {
-          const int e = j * W + k;
-          const uint32_t wd = (&wraw[e >> 3].x)[(e >> 1) & 3];
-          u += __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16)) * win[k][j];
-        }
-        u = silu(u);
-      } else {
-        u = win[R][j];
-      }
-      v[j] = i < nvalid ? u : 0.f;
-      const f16 hv = (f16)v[j];
-      rem[j] = v[j] - (float)hv;
-      const uint32_t hbits = (uint32_t)__builtin_bit_cast(uint16_t, hv);
-      if (i & 1) pk4[j][i >> 1] |= hbits << 16;
-      else pk4[j][i >> 1] = hbits;
-    }
-    *reinterpret_cast<uint4*>(lo + i * ldlo) =
-        make_uint4(pk(rem[0], rem[1]), pk(rem[2], rem[3]), pk(rem[4], rem[5]), pk(rem[6], rem[7]));
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) win[r][j] = win[r + 1][j];
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<uint2*>(dst + j * ld) = make_uint2(pk4[j][0], pk4[j][1]);
 }
 
 // Inclusive cumsum of dt*A over the chunk for the HB = 4 heads of the
@@ -423,21 +350,121 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 }
 
 // ---------------------------------------------------------------- phase 3
+// Raw rows of one x staging item: 4 tokens (+ W-1 halo when CONV) of one
+// 8-channel vector, loaded ahead of their use (addresses clamped into the
+// sequence; rows outside are masked when converted).
+template <bool CONV>
+struct XRaw {
+  static constexpr int R = CONV ? W - 1 : 0;
+  u32x4 v[4 + R];
+};
+
+template <bool CONV>
+SSD_DEV void x_load(XRaw<CONV>& r, const bf16* __restrict__ src, int64_t ts, int tseq, int Lm1,
+                    const Src& s, int ch, const bf16* cin_b) {
+  constexpr int R = XRaw<CONV>::R;
+#pragma unroll
+  for (int i = 0; i < 4 + R; ++i) {
+    const int t = tseq - R + i;
+    const bf16* p = (CONV && t < 0 && cin_b) ? cin_b + (int64_t)(W - 1 + t) * s.C + ch
+                                             : src + (int64_t)min(max(t, 0), Lm1) * ts;
+    r.v[i] = *reinterpret_cast<const u32x4*>(p);
+  }
+}
+
+// conv + SiLU (or the plain input) of a loaded item; fp16(x) goes to
+// hi + j*ld and x - fp16(x) to lo + j*ld (channel row j, the 4 tokens
+// contiguous: the MFMA A-operand layout [p][s]).
+template <bool CONV>
+SSD_DEV void x_store(const XRaw<CONV>& r, int tseq, int nvalid, const Src& s, int ch,
+                     const bf16* cin_b, f16* hi, f16* lo, int ld) {
+  constexpr int R = XRaw<CONV>::R;
+  u32x4 wraw[4];
+  float bi[8];
+  if (CONV) {
+    const u32x4* wp = reinterpret_cast<const u32x4*>(s.cw + (int64_t)ch * W);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wraw[q] = wp[q];
+    if (s.cbias) {
+      load8(s.cbias + ch, bi);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bi[j] = 0.f;
+    }
+  }
+  float win[R + 1][8];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    unpack8(r.v[i], win[i]);
+    if (tseq - R + i < 0 && !cin_b) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) win[i][j] = 0.f;
+    }
+  }
+  uint32_t ph[8][2], pl[8][2];  // channel j, tokens (0,1) | (2,3)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unpack8(r.v[i + R], win[R]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float u;
+      if (CONV) {
+        u = bi[j];
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const int e = j * W + k;
+          const uint32_t wd = wraw[e >> 3][(e >> 1) & 3];
+          u += __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16)) * win[k][j];
+        }
+        u = silu(u);
+      } else {
+        u = win[R][j];
+      }
+      const float v = i < nvalid ? u : 0.f;
+      const f16 hv = (f16)v;
+      const f16 lv = (f16)(v - (float)hv);
+      const uint32_t hb = (uint32_t)__builtin_bit_cast(uint16_t, hv);
+      const uint32_t lb = (uint32_t)__builtin_bit_cast(uint16_t, lv);
+      if (i & 1) {
+        ph[j][i >> 1] |= hb << 16;
+        pl[j][i >> 1] |= lb << 16;
+      } else {
+        ph[j][i >> 1] = hb;
+        pl[j][i >> 1] = lb;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) win[rr][j] = win[rr + 1][j];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    *reinterpret_cast<uint2*>(hi + j * ld) = make_uint2(ph[j][0], ph[j][1]);
+    *reinterpret_cast<uint2*>(lo + j * ld) = make_uint2(pl[j][0], pl[j][1]);
+  }
+}
+
 // NORM: fuse the gated RMSNorm (the 4 heads are one norm group); else the
 // scan output y is written (bf16).
 //
-// Wave w owns row tiles w and 7-w of the chunk (equal causal work) for all 4
-// heads. It keeps in registers the C.B^T tiles of its rows (computed as
-// (B C^T) tiles, whose MFMA output layout is exactly the A-operand layout of
-// the next product once that product's 32 k-slots are mapped to the
-// sequence positions 4q..4q+3 and 16+4q..16+4q+3 of its two 16-column
-// tiles) and its C fragments, so after the first phase the LDS only holds
-// x: fp16(x) transposed for the MFMA, plus the part fp16 drops (XL) so D x
-// is taken at ~22-bit mantissa precision. Heads go in two passes of 2; the
-// wave's y values stay in registers (fp16) until both passes are done, then
-// go through an LDS tile to a coalesced epilogue that gates with z,
-// normalises each row over its 256 channels and stores 16-byte vectors.
-constexpr int XLS = 2 * P + 8;  // padded row of the [t][2 heads x P] low part
+// Every product is computed transposed, y^T[p, t], so a lane's accumulator
+// holds 4 consecutive channels p of one token t (the row t = lane % 16 of
+// the wave's row tile): y^T = X^T M'^T + S_in (exp(Lam_t) C_t)^T + D x^T.
+// Wave w owns row tiles w and 7-w of the chunk (equal causal work) for all
+// 4 heads. The C.B^T tiles of its rows stay in registers (computed as
+// (B C^T) tiles, whose MFMA output layout is the B-operand layout of the
+// next product once its 32 k-slots are mapped to the sequence positions
+// 4q..4q+3 and 16+4q..16+4q+3 of two 16-column tiles). D x runs on the MFMA
+// as [x_hi | x_lo] against [D_hi I ; D_hi I] and [D_lo I ; D_lo I], so the
+// largest term of y keeps ~22 mantissa bits (the norm divides by rms(q)).
+// Phases: B, C staged (conv) -> G tiles and C fragments in registers while
+// the carried-in states of the 4 heads are fetched -> states through LDS ->
+// the inter-chunk term for all heads (y kept as fp16 pairs) -> x of one head
+// at a time through two LDS buffers, the next head's rows loaded while the
+// current head is computed -> y through an LDS tile to a coalesced epilogue
+// that gates with z (prefetched), normalises each row over its 256 channels
+// and stores 16-byte vectors.
 template <bool CONV, bool NORM>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
@@ -447,15 +474,15 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 const bf16* __restrict__ nw, float eps,
                                                 bf16* __restrict__ out, int L, int H, int G,
                                                 int nc) {
-  static_assert(2 * P * RS == QI * NS && QI * XLS == QI * NS, "x hi/lo reuse the B/C space");
+  static_assert(4 * P * RS == 2 * QI * NS, "two x buffers fill the B/C space");
+  static_assert(HB * P * NS == 2 * QI * NS, "the 4 heads' states fill the B/C space");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
-  __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then XT | XL per head pair, then Ot
-  __shared__ float lam[HB][QI], dts[HB][QI];
+  __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then states, then x buffers, then Ot
+  __shared__ float lam[HB][QI], dts[HB][QI], csd[HB][QI];
   f16* Bs = U;
   f16* Cs = U + QI * NS;
-  f16* XT = U;                // [head of pair][p][s]: fp16(x)
-  f16* XL = U + 2 * P * RS;   // [t][head of pair x p]: x - fp16(x)
-  f16* Ot = U;                // [t][4 heads x p]: y
+  f16* Sl = U;  // [head][p][NS]: S_in
+  f16* Ot = U;  // [t][4 heads x p]: y
 
   const int c = blockIdx.x, hpb = H / HB;
   const int b = blockIdx.y / hpb, h0 = (blockIdx.y % hpb) * HB, g = h0 / (H / G);
@@ -465,30 +492,63 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
   const int HP = s.HP;
 
-  heads_cumsum(dt, row0, H, h0, len, A, lam, dts);
+  // dt of head `wave`, positions 2 lane and 2 lane + 1, fetched before B/C
+  const int tc = 2 * lane;
+  const float dr0 = to_f(dt[(row0 + min(tc, len - 1)) * H + h0 + wave]);
+  const float dr1 = to_f(dt[(row0 + min(tc + 1, len - 1)) * H + h0 + wave]);
 
   const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
   // B and C, natural layout [t][n]: 16 channel vectors x 16 token blocks each.
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int i = tid, cv = i & 15, tbi = i >> 4, n0 = cv * 8;
+    const int cv = tid & 15, tbi = tid >> 4, n0 = cv * 8;
     const bf16* base = (half ? s.c : s.b) + (int64_t)b * L * s.bs + g * N + n0;
     const int ch = s.HP + (half ? s.GN : 0) + g * N + n0;
     conv_stage<CONV, false>(base, s.bs, t0 + tbi * 8, min(8, max(0, len - tbi * 8)), L - 1, s, ch,
                             cin_b, nullptr, (half ? Cs : Bs) + (tbi * 8) * NS + n0, NS);
   }
+  // Lam (inclusive cumsum of dt A), dt, and csd[s] = exp(Lam_ref - Lam_s) dt_s
+  // with Lam_ref the value at the end of s's 32-position block (<= Lam_s).
+  {
+    const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
+    const float Ah = A[h0 + wave];
+    const float a0 = d0 * Ah, a1 = d1 * Ah;
+    float v = a0 + a1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float n = __shfl_up(v, o, 64);
+      if (lane >= o) v += n;
+    }
+    const float l0 = v - a1, l1 = v;
+    const float lref = __shfl(l1, lane | 15, 64);
+    lam[wave][tc] = l0;
+    lam[wave][tc + 1] = l1;
+    dts[wave][tc] = d0;
+    dts[wave][tc + 1] = d1;
+    csd[wave][tc] = fexp(lref - l0) * d0;
+    csd[wave][tc + 1] = fexp(lref - l1) * d1;
+  }
   __syncthreads();
 
   const int rta = wave, rtb = 7 - wave;
-  // (B C^T) tiles j <= rt of the wave's two row tiles: lane holds C_t.B_s for
-  // t = 16 rt + rr and s = 16 j + 4 q4 + r (fp16, the MFMA operand precision).
-  uint2 Ga[4], Gb[8];
+  // C fragments of the wave's rows (B operand: column t, k = n)
   f16x8 Cfa[4], Cfb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     Cfa[ks] = *reinterpret_cast<const f16x8*>(Cs + (rta * 16 + rr) * NS + ks * 32 + kk);
     Cfb[ks] = *reinterpret_cast<const f16x8*>(Cs + (rtb * 16 + rr) * NS + ks * 32 + kk);
   }
+  // carried-in states of the 4 heads (contiguous [head][p][n]), in flight
+  // while the G tiles are computed
+  f16x8 sreg[16];
+  {
+    const f16* sp = sin_h + (((int64_t)b * nc + c) * H + h0) * (int64_t)(P * N);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sreg[i] = *reinterpret_cast<const f16x8*>(sp + (tid + NT * i) * 8);
+  }
+  // (B C^T) tiles j <= rt of the wave's two row tiles: lane holds C_t.B_s for
+  // t = 16 rt + rr and s = 16 j + 4 q4 + r (fp16, the MFMA operand precision).
+  uint2 Ga[4], Gb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     f32x4 ga = zero4(), gb = zero4();
@@ -502,136 +562,174 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     if (j < 4) Ga[j] = make_uint2(pk(ga[0], ga[1]), pk(ga[2], ga[3]));
     Gb[j] = make_uint2(pk(gb[0], gb[1]), pk(gb[2], gb[3]));
   }
-  // y starts as the inter-chunk term exp(Lam_t) C_t S_in^T for all 4 heads,
-  // kept as fp16 pairs: [row tile][head][p tile][rows r4+0,1 | r4+2,3].
+  __syncthreads();  // B and C no longer read from LDS
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = tid + NT * i, row = idx >> 4, v = idx & 15;  // row = head * P + p
+    *reinterpret_cast<f16x8*>(Sl + row * NS + v * 8) = sreg[i];
+  }
+  __syncthreads();
+
+  // y^T starts as the inter-chunk term S_in (exp(Lam_t) C_t)^T, kept as fp16
+  // pairs: [row tile][head][p tile][p = r4 + 0,1 | r4 + 2,3] at t = 16 rt + rr.
   uint32_t yk[2][4][4][2];
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    const f16* sp = sin_h + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
-    f32x4 acc2a[4], acc2b[4];
+    const float ea = fexp(lam[hh][rta * 16 + rr]), eb = fexp(lam[hh][rtb * 16 + rr]);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) { acc2a[pt] = zero4(); acc2b[pt] = zero4(); }
+    for (int pt = 0; pt < 4; ++pt) {
+      f32x4 acc_a = zero4(), acc_b = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const f16x8 sf = *reinterpret_cast<const f16x8*>(sp + (pt * 16 + rr) * N + ks * 32 + kk);
-        acc2a[pt] = mma16(Cfa[ks], sf, acc2a[pt]);
-        acc2b[pt] = mma16(Cfb[ks], sf, acc2b[pt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 sf =
+            *reinterpret_cast<const f16x8*>(Sl + (hh * P + pt * 16 + rr) * NS + ks * 32 + kk);
+        acc_a = mma16(sf, Cfa[ks], acc_a);
+        acc_b = mma16(sf, Cfb[ks], acc_b);
       }
+      yk[0][hh][pt][0] = pk(ea * acc_a[0], ea * acc_a[1]);
+      yk[0][hh][pt][1] = pk(ea * acc_a[2], ea * acc_a[3]);
+      yk[1][hh][pt][0] = pk(eb * acc_b[0], eb * acc_b[1]);
+      yk[1][hh][pt][1] = pk(eb * acc_b[2], eb * acc_b[3]);
+      // materialise the packed values here (not next to their later uses),
+      // so the fp32 accumulators die at once
+      pin(yk[0][hh][pt]);
+      pin(yk[1][hh][pt]);
+    }
+  }
+  __syncthreads();  // states no longer read: the x buffers follow
+
+  // x staging item of this thread (one head): 8 channel vectors x 32 blocks
+  // of 4 tokens; within 64 lanes, 2 vectors x 32 blocks.
+  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
+  const bf16* xb = s.x + (int64_t)b * L * s.xs;
+  const int xnv = min(4, max(0, len - xtb * 4));
+  XRaw<CONV> xr;
+  {
+    const int ch = h0 * P + xp0;
+    x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+    x_store<CONV>(xr, t0 + xtb * 4, xnv, s, ch, cin_b, U + xp0 * RS + xtb * 4,
+                  U + P * RS + xp0 * RS + xtb * 4, RS);
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int hh = 0; hh < HB; ++hh) {
+    const f16* XT = U + (hh & 1) * (2 * P * RS);  // [p][s]: fp16(x)
+    const f16* XL = XT + P * RS;                  // [p][s]: x - fp16(x)
+    if (hh + 1 < HB) {
+      const int ch = (h0 + hh + 1) * P + xp0;
+      x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+    }
+    const float Dh = D ? D[h0 + hh] : 0.f;
+    const f16 dhi = (f16)Dh, dlo = (f16)(Dh - (float)dhi);
+    // B operands [D I ; D I]: k-slot 8 q4 + j of column rr is D when
+    // (8 q4 + j) mod 16 == rr
+    f16x8 dfh, dfl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool on = ((8 * (q4 & 1) + j) == rr);
+      dfh[j] = on ? dhi : (f16)0.f;
+      dfl[j] = on ? dlo : (f16)0.f;
     }
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
       const int rt = ui == 0 ? rta : rtb;
-      float el[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) el[r] = fexp(lam[hh][rt * 16 + r4 + r]);
+      const int trow = rt * 16 + rr;  // this lane's token (B-operand column)
+      const float lt = lam[hh][trow];
+      f32x4 acc[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const f32x4 a2 = ui == 0 ? acc2a[pt] : acc2b[pt];
-        yk[ui][hh][pt][0] = pk(el[0] * a2[0], el[1] * a2[1]);
-        yk[ui][hh][pt][1] = pk(el[2] * a2[2], el[3] * a2[3]);
+        const uint32_t* w2 = yk[ui][hh][pt];
+        acc[pt][0] = h2f_lo(w2[0]);
+        acc[pt][1] = h2f_hi(w2[0]);
+        acc[pt][2] = h2f_lo(w2[1]);
+        acc[pt][3] = h2f_hi(w2[1]);
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // one head's S_in fragments in flight at a time
-  }
-  __syncthreads();  // B and C no longer read from LDS
-
-  const bf16* xb = s.x + (int64_t)b * L * s.xs;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    // x of heads 2*pass, 2*pass+1: 16 channel vectors x 32 blocks of 4 tokens;
-    // within 32 lanes, 2 vectors x 16 blocks hit distinct LDS banks.
-#pragma unroll 1
-    for (int i = tid; i < 512; i += NT) {
-      const int tb = (i >> 1) & 31, cv = (i & 1) | ((i >> 6) << 1);
-      const int hs = cv >> 3, p0 = (cv & 7) * 8;
-      const int ch = (h0 + 2 * pass + hs) * P + p0;
-      conv_stage4<CONV>(xb + ch, s.xs, t0 + tb * 4, min(4, max(0, len - tb * 4)), L - 1, s, ch,
-                        cin_b, XT + (hs * P + p0) * RS + tb * 4, RS,
-                        XL + (tb * 4) * XLS + hs * P + p0, XLS);
-    }
-    __syncthreads();
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int hh = 2 * pass + hi;
-      const float Dh = D ? D[h0 + hh] : 0.f;
+      for (int ks = 0; ks < 4; ++ks) {
+        if (2 * ks <= rt) {
+          // k-slots 8 q4 + r <-> s = 32 ks + 4 q4 + r, 8 q4 + 4 + r <-> s + 16
+          const int s0 = ks * 32 + r4;
+          uint2 g0, g1;
+          if (ui == 0) {
+            g0 = Ga[(2 * ks) & 3];
+            g1 = (2 * ks + 1 <= rt) ? Ga[(2 * ks + 1) & 3] : make_uint2(0u, 0u);
+          } else {
+            g0 = Gb[2 * ks];
+            g1 = (2 * ks + 1 <= rt) ? Gb[2 * ks + 1] : make_uint2(0u, 0u);
+          }
+          const float gv[8] = {h2f_lo(g0.x), h2f_hi(g0.x), h2f_lo(g0.y), h2f_hi(g0.y),
+                               h2f_lo(g1.x), h2f_hi(g1.x), h2f_lo(g1.y), h2f_hi(g1.y)};
+          f16x8 af;
+          if (2 * ks + 2 <= rt) {
+            // whole block before the row tile: exp(Lam_t - Lam_s) dt_s =
+            // exp(Lam_t - Lam_ref) csd_s, both factors <= 1
+            const float rf = fexp(lt - lam[hh][ks * 32 + 31]);
+            const float4 c0 = *reinterpret_cast<const float4*>(&csd[hh][s0]);
+            const float4 c1 = *reinterpret_cast<const float4*>(&csd[hh][s0 + 16]);
+            const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-      for (int ui = 0; ui < 2; ++ui) {
-        const int rt = ui == 0 ? rta : rtb;
-        const int trow = rt * 16 + rr;  // A-operand row
-        const float lt = lam[hh][trow];
-        f32x4 acc[4];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = zero4();
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (2 * ks <= rt) {
-            // k-slots 8 q4 + r <-> s = 32 ks + 4 q4 + r, 8 q4 + 4 + r <-> s + 16
-            const int s0 = ks * 32 + r4;
+            for (int j = 0; j < 8; ++j) af[j] = (f16)(gv[j] * rf * cs[j]);
+          } else {
             const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
             const float4 l1 = *reinterpret_cast<const float4*>(&lam[hh][s0 + 16]);
             const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][s0]);
             const float4 d1 = *reinterpret_cast<const float4*>(&dts[hh][s0 + 16]);
             const float ls[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
             const float ds[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-            uint2 g0, g1;
-            if (ui == 0) {
-              g0 = Ga[(2 * ks) & 3];
-              g1 = (2 * ks + 1 <= rt) ? Ga[(2 * ks + 1) & 3] : make_uint2(0u, 0u);
-            } else {
-              g0 = Gb[2 * ks];
-              g1 = (2 * ks + 1 <= rt) ? Gb[2 * ks + 1] : make_uint2(0u, 0u);
-            }
-            const float gv[8] = {h2f_lo(g0.x), h2f_hi(g0.x), h2f_lo(g0.y), h2f_hi(g0.y),
-                                 h2f_lo(g1.x), h2f_hi(g1.x), h2f_lo(g1.y), h2f_hi(g1.y)};
-            f16x8 af;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int sj = s0 + (j & 3) + (j >> 2) * 16;
               const float m = gv[j] * fexp(fminf(lt - ls[j], 0.f)) * ds[j];
               af[j] = (f16)(sj <= trow ? m : 0.f);
             }
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-              const f16* xr = XT + (hi * P + pt * 16 + rr) * RS + s0;
-              const uint2 lo = *reinterpret_cast<const uint2*>(xr);
-              const uint2 hi2 = *reinterpret_cast<const uint2*>(xr + 16);
-              const uint4 u = make_uint4(lo.x, lo.y, hi2.x, hi2.y);
-              acc[pt] = mma16(af, __builtin_bit_cast(f16x8, u), acc[pt]);
-            }
           }
-        }
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          float yv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = rt * 16 + r4 + r;
-            const int p = pt * 16 + rr;
-            const float xv = (float)XT[(hi * P + p) * RS + t] + (float)XL[t * XLS + hi * P + p];
-            yv[r] = acc[pt][r] + Dh * xv;
-          }
-          // add to the inter-chunk term; register indices stay static under
-          // the runtime pass loop
-          uint32_t* w2 = pass == 0 ? yk[ui][hi][pt] : yk[ui][2 + hi][pt];
-          const float o0 = h2f_lo(w2[0]), o1 = h2f_hi(w2[0]);
-          const float o2 = h2f_lo(w2[1]), o3 = h2f_hi(w2[1]);
-          const uint32_t p01 = pk(yv[0] + o0, yv[1] + o1), p23 = pk(yv[2] + o2, yv[3] + o3);
-          if (pass == 0) {
-            yk[ui][hi][pt][0] = p01;
-            yk[ui][hi][pt][1] = p23;
-          } else {
-            yk[ui][2 + hi][pt][0] = p01;
-            yk[ui][2 + hi][pt][1] = p23;
+          for (int pt = 0; pt < 4; ++pt) {
+            const f16* xr0 = XT + (pt * 16 + rr) * RS + s0;
+            const uint2 lo = *reinterpret_cast<const uint2*>(xr0);
+            const uint2 hi2 = *reinterpret_cast<const uint2*>(xr0 + 16);
+            const uint4 u = make_uint4(lo.x, lo.y, hi2.x, hi2.y);
+            acc[pt] = mma16(__builtin_bit_cast(f16x8, u), af, acc[pt]);
           }
         }
       }
+      // D x: A = [x_hi | x_lo] over the row tile's 16 positions
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const f16x8 xa = *reinterpret_cast<const f16x8*>((q4 < 2 ? XT : XL) + (pt * 16 + rr) * RS +
+                                                         rt * 16 + 8 * (q4 & 1));
+        acc[pt] = mma16(xa, dfh, acc[pt]);
+        acc[pt] = mma16(xa, dfl, acc[pt]);
+        yk[ui][hh][pt][0] = pk(acc[pt][0], acc[pt][1]);
+        yk[ui][hh][pt][1] = pk(acc[pt][2], acc[pt][3]);
+        pin(yk[ui][hh][pt]);
+      }
     }
-    __syncthreads();  // XT/XL of this pair no longer read (and Ot may follow)
+    if (hh + 1 < HB) {
+      f16* nx = U + ((hh + 1) & 1) * (2 * P * RS);
+      const int ch = (h0 + hh + 1) * P + xp0;
+      x_store<CONV>(xr, t0 + xtb * 4, xnv, s, ch, cin_b, nx + xp0 * RS + xtb * 4,
+                    nx + P * RS + xp0 * RS + xtb * 4, RS);
+    }
+    __syncthreads();
   }
 
-  // y -> Ot [t][4 heads x P]
+  // Epilogue: 32 consecutive threads take one row (8 channels each); thread
+  // rows t = tid / 32 + 8 e. z is fetched before y goes through LDS.
+  const int ev8 = tid & 31, et0 = tid >> 5;
+  constexpr int EPI = QI * (HB * P / 8) / NT;  // 16 rows per thread
+  u32x4 zr[NORM ? EPI : 1];
+  float wv8[8];
+  if (NORM) {
+#pragma unroll
+    for (int e = 0; e < EPI; ++e) {
+      const int t = et0 + 8 * e;
+      zr[e] = *reinterpret_cast<const u32x4*>(z + (row0 + min(t, len - 1)) * HP + h0 * P + ev8 * 8);
+    }
+    load8(nw + h0 * P + ev8 * 8, wv8);
+  }
+  // y -> Ot [t][4 heads x P]: a lane's 4 channels of one token are 8 bytes
 #pragma unroll
   for (int ui = 0; ui < 2; ++ui) {
     const int rt = ui == 0 ? rta : rtb;
@@ -639,26 +737,19 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t w2 = yk[ui][hh][pt][r >> 1];
-          const uint16_t bits = (r & 1) ? (uint16_t)(w2 >> 16) : (uint16_t)(w2 & 0xffffu);
-          Ot[(rt * 16 + r4 + r) * OS + hh * P + pt * 16 + rr] = __builtin_bit_cast(f16, bits);
-        }
+        *reinterpret_cast<uint2*>(Ot + (rt * 16 + rr) * OS + hh * P + pt * 16 + r4) =
+            make_uint2(yk[ui][hh][pt][0], yk[ui][hh][pt][1]);
   }
   __syncthreads();
 
-  // Epilogue: 32 consecutive threads take one row (8 channels each).
-  for (int i = tid; i < QI * (HB * P / 8); i += NT) {
-    const int t = i >> 5, v8 = i & 31;
-    const bool ok = t < len;
-    const int64_t go = (row0 + min(t, len - 1)) * HP + h0 * P + v8 * 8;
+#pragma unroll
+  for (int e = 0; e < EPI; ++e) {
+    const int t = et0 + 8 * e;
     float yv[8];
-    load8h(Ot + t * OS + v8 * 8, yv);
+    load8h(Ot + t * OS + ev8 * 8, yv);
     if (NORM) {
-      float zv[8], wv8[8];
-      load8(z + go, zv);
-      load8(nw + h0 * P + v8 * 8, wv8);
+      float zv[8];
+      unpack8(zr[e], zv);
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -671,7 +762,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 8; ++j) yv[j] *= wv8[j] * inv;
     }
-    if (ok) store8(out + go, yv);
+    if (t < len) store8(out + (row0 + t) * HP + h0 * P + ev8 * 8, yv);
   }
 }
 
