@@ -21,6 +21,8 @@ template <> SSD_DEV bf16 from_f<bf16>(float v) { return (bf16)v; }  // round to 
 
 // exp(x) through the hardware base-2 exponential.
 SSD_DEV float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+SSD_DEV float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = 1.4426950408889634f;
 SSD_DEV float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 SSD_DEV float silu(float u) { return u * frcp(1.0f + fexp(-u)); }
 

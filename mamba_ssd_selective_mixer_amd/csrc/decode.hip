@@ -18,6 +18,7 @@ namespace ssd {
 constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 8;  // state float4 loads kept in flight per lane
 
+
 template <class T, int N, int W>
 __global__ __launch_bounds__(kDecThreads) void k_decode(
     const T* __restrict__ xbc, const T* __restrict__ z, const T* __restrict__ dt,
@@ -66,42 +67,90 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   }
   __syncthreads();
 
-  // 2. state update and output, head by head.
+  // 2. state update and output, head by head. The state of the next head is
+  // loaded before the current head is updated; state loads and stores are
+  // non-temporal (each element is touched once per step).
   constexpr int LPR = N / 4;                 // lanes per state row
   const int PN = P * N;
   const int n0 = (4 * tid) % N;
   const float4 Bv = *reinterpret_cast<const float4*>(Bs + n0);
   const float4 Cv = *reinterpret_cast<const float4*>(Cs + n0);
   const int iters = (PN + 4 * kDecThreads - 1) / (4 * kDecThreads);
-  for (int hl = 0; hl < hpg; ++hl) {
-    const int h = g * hpg + hl;
-    const float dtv = to_f(dt[(int64_t)b * H + h]);
-    const float al = fexp(dtv * A[h]);
-    const float Dh = D ? D[h] : 0.f;
-    float* st = ssm + ((int64_t)b * H + h) * PN;
-    for (int i0 = 0; i0 < iters; i0 += kDecUnroll) {
-      float4 s[kDecUnroll];
+  float* sb = ssm + ((int64_t)b * H + (int64_t)g * hpg) * PN;  // the group's heads
+  if (iters <= kDecUnroll) {
+    f32x4 cur[kDecUnroll];
+    auto load_head = [&](int hl, f32x4 (&dst)[kDecUnroll]) {
+      const float* st = sb + (int64_t)hl * PN;
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
-        const int e = 4 * tid + (i0 + u) * 4 * kDecThreads;
-        if (i0 + u < iters && e < PN) s[u] = *reinterpret_cast<const float4*>(st + e);
+        const int e = 4 * tid + u * 4 * kDecThreads;
+        if (u < iters && e < PN) {
+          dst[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
+        }
       }
+    };
+    load_head(0, cur);
+    for (int hl = 0; hl < hpg; ++hl) {
+      f32x4 nxt[kDecUnroll];
+      if (hl + 1 < hpg) load_head(hl + 1, nxt);
+      const int h = g * hpg + hl;
+      const float dtv = to_f(dt[(int64_t)b * H + h]);
+      const float al = fexp(dtv * A[h]);
+      const float Dh = D ? D[h] : 0.f;
+      float* st = sb + (int64_t)hl * PN;
 #pragma unroll
       for (int u = 0; u < kDecUnroll; ++u) {
-        const int e = 4 * tid + (i0 + u) * 4 * kDecThreads;
-        if (i0 + u < iters && e < PN) {
+        const int e = 4 * tid + u * 4 * kDecThreads;
+        if (u < iters && e < PN) {
           const int p = e / N;
           const float xp = xs[hl * P + p];
           const float dx = dtv * xp;
-          float4 v = s[u];
-          v.x = al * v.x + dx * Bv.x;
-          v.y = al * v.y + dx * Bv.y;
-          v.z = al * v.z + dx * Bv.z;
-          v.w = al * v.w + dx * Bv.w;
-          *reinterpret_cast<float4*>(st + e) = v;
-          float part = v.x * Cv.x + v.y * Cv.y + v.z * Cv.z + v.w * Cv.w;
+          f32x4 v = cur[u];
+          v[0] = al * v[0] + dx * Bv.x;
+          v[1] = al * v[1] + dx * Bv.y;
+          v[2] = al * v[2] + dx * Bv.z;
+          v[3] = al * v[3] + dx * Bv.w;
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(st + e));
+          float part = v[0] * Cv.x + v[1] * Cv.y + v[2] * Cv.z + v[3] * Cv.w;
           part = group_sum(part, LPR);
           if ((tid % LPR) == 0) ys[hl * P + p] = part + Dh * xp;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kDecUnroll; ++u) cur[u] = nxt[u];
+    }
+  } else {
+    for (int hl = 0; hl < hpg; ++hl) {
+      const int h = g * hpg + hl;
+      const float dtv = to_f(dt[(int64_t)b * H + h]);
+      const float al = fexp(dtv * A[h]);
+      const float Dh = D ? D[h] : 0.f;
+      float* st = ssm + ((int64_t)b * H + h) * PN;
+      for (int i0 = 0; i0 < iters; i0 += kDecUnroll) {
+        f32x4 s[kDecUnroll];
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+          const int e = 4 * tid + (i0 + u) * 4 * kDecThreads;
+          if (i0 + u < iters && e < PN)
+            s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
+        }
+#pragma unroll
+        for (int u = 0; u < kDecUnroll; ++u) {
+          const int e = 4 * tid + (i0 + u) * 4 * kDecThreads;
+          if (i0 + u < iters && e < PN) {
+            const int p = e / N;
+            const float xp = xs[hl * P + p];
+            const float dx = dtv * xp;
+            f32x4 v = s[u];
+            v[0] = al * v[0] + dx * Bv.x;
+            v[1] = al * v[1] + dx * Bv.y;
+            v[2] = al * v[2] + dx * Bv.z;
+            v[3] = al * v[3] + dx * Bv.w;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(st + e));
+            float part = v[0] * Cv.x + v[1] * Cv.y + v[2] * Cv.z + v[3] * Cv.w;
+            part = group_sum(part, LPR);
+            if ((tid % LPR) == 0) ys[hl * P + p] = part + Dh * xp;
+          }
         }
       }
     }
