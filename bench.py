@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events")
+    ap.add_argument("--only", choices=("large", "chain", "decode"),
+                    help="time only one of the secondary workloads (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for the HBM counter scale)")
     return ap.parse_args()
@@ -289,6 +291,35 @@ def cpu_baseline(synth, cfg, budget_s=10.0):
                       f"recurrence + conv + gated norm), {sec:.1f} s wall"}
 
 
+def secondary(torch, ops, synth, args, which):
+    """The large-layer prefill, the long-context chain and the decode loop."""
+    wl = {}
+    if "large" in which:
+        c2 = synth.CONFIGS["c2"]
+        ms2, _ = run_prefill(torch, ops, synth, c2, max(3, args.steps // 5), 2, 2, True)
+        b2 = prefill_bytes(c2, c2.seqlen, True)
+        wl["large_prefill"] = {"tokens_per_s": c2.seqlen / (ms2 * 1e-3), "ms": ms2,
+                               "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "mfma_frac": prefill_flops(c2, c2.seqlen) / (ms2 * 1e-3) / 1e12
+                               / MFMA_BF16_PEAK_TFS}
+    if "chain" in which:
+        c3 = synth.CONFIGS["c3"]
+        ms3 = run_chain(torch, ops, synth, c3, 3)
+        b3 = prefill_bytes(c3, c3.seqlen, True) * c3.pieces
+        wl["long_context_chain"] = {"tokens_per_s": c3.seqlen * c3.pieces / (ms3 * 1e-3),
+                                    "ms_per_chain": ms3,
+                                    "hbm_frac": b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if "decode" in which:
+        c4 = synth.CONFIGS["c4"]
+        ms4 = run_decode(torch, ops, synth, c4, 3)
+        b4 = decode_bytes(c4) * c4.steps
+        wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms4 * 1e-3),
+                        "us_per_step": ms4 * 1e3 / c4.steps,
+                        "hbm_gbs": b4 / (ms4 * 1e-3) / 1e9,
+                        "hbm_frac": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return wl
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -303,6 +334,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.only:
+        print(json.dumps(secondary(torch, ops, synth, args, (args.only,))))
         return
     cfg = synth.CONFIGS["c1"]
     ms, kern = run_prefill(torch, ops, synth, cfg, args.steps, args.warmup, args.sets, False,
@@ -341,28 +375,7 @@ def main():
         "roofline": roof,
     }
     if not args.quick:
-        wl = {}
-        c2 = synth.CONFIGS["c2"]
-        ms2, _ = run_prefill(torch, ops, synth, c2, max(3, args.steps // 5), 2, 2, True)
-        b2 = prefill_bytes(c2, c2.seqlen, True)
-        wl["large_prefill"] = {"tokens_per_s": c2.seqlen / (ms2 * 1e-3), "ms": ms2,
-                               "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "mfma_frac": prefill_flops(c2, c2.seqlen) / (ms2 * 1e-3) / 1e12
-                               / MFMA_BF16_PEAK_TFS}
-        c3 = synth.CONFIGS["c3"]
-        ms3 = run_chain(torch, ops, synth, c3, 3)
-        b3 = prefill_bytes(c3, c3.seqlen, True) * c3.pieces
-        wl["long_context_chain"] = {"tokens_per_s": c3.seqlen * c3.pieces / (ms3 * 1e-3),
-                                    "ms_per_chain": ms3,
-                                    "hbm_frac": b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        c4 = synth.CONFIGS["c4"]
-        ms4 = run_decode(torch, ops, synth, c4, 3)
-        b4 = decode_bytes(c4) * c4.steps
-        wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms4 * 1e-3),
-                        "us_per_step": ms4 * 1e3 / c4.steps,
-                        "hbm_gbs": b4 / (ms4 * 1e-3) / 1e9,
-                        "hbm_frac": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        rec["workloads"] = wl
+        rec["workloads"] = secondary(torch, ops, synth, args, ("large", "chain", "decode"))
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(synth, cfg)
     print(json.dumps(rec))

@@ -51,10 +51,11 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 // HIP uint4 struct can end up in scratch memory).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-SSD_DEV uint32_t pk(float a, float b) {
-  const f16 lo = (f16)a, hi = (f16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-}
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> one word of two fp16 (round to nearest even; a in the low half)
+SSD_DEV f16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, f16x2); }
+SSD_DEV uint32_t pk(float a, float b) { return __builtin_bit_cast(uint32_t, cvt2(a, b)); }
 SSD_DEV float h2f_lo(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu)); }
 SSD_DEV float h2f_hi(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16)); }
 SSD_DEV void load8h(const f16* p, float (&v)[8]) {
@@ -158,9 +159,11 @@ SSD_DEV void rows_load(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const bf16* __restr
 template <bool CONV, int T>
 SSD_DEV void rows_mask_head(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], int tseq, const bf16* cin_b) {
   if constexpr (CONV) {
+    if (tseq < W - 1 && !cin_b) {  // only the first rows of a sequence
 #pragma unroll
-    for (int i = 0; i < W - 1; ++i)
-      if (tseq - (W - 1) + i < 0 && !cin_b) raw[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < W - 1; ++i)
+        if (tseq - (W - 1) + i < 0) raw[i] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
@@ -179,10 +182,12 @@ SSD_DEV void conv_store(Rows8<CONV>& raw, int tseq, int nvalid, const Src& s, in
   rows_mask_head<CONV, 8>(raw, tseq, cin_b);
   float v[8][8];
   conv_tile<CONV, 8>(raw, s, ch, v);
+  if (nvalid < 8) {  // only the tail of a sequence
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : 0.f;
+      for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : 0.f;
+  }
   if (TRANS) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -235,19 +240,27 @@ SSD_DEV void x_store(XRaw<CONV>& r, int tseq, int nvalid, const Src& s, int ch,
   rows_mask_head<CONV, 4>(r.v, tseq, cin_b);
   float v[4][8];
   conv_tile<CONV, 4>(r.v, s, ch, v);
+  if (scale) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] *= scale[i];
+  }
+  if (nvalid < 4) {  // only the tail of a sequence
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float u = v[i][j];
-      if (scale) u *= scale[i];
-      u = i < nvalid ? u : 0.f;
-      h[i] = (float)(f16)u;
-      l[i] = u - h[i];
-    }
-    *reinterpret_cast<uint2*>(hi + j * ld) = make_uint2(pk(h[0], h[1]), pk(h[2], h[3]));
-    if (LO) *reinterpret_cast<uint2*>(lo + j * ld) = make_uint2(pk(l[0], l[1]), pk(l[2], l[3]));
+    const f16x2 h01 = cvt2(v[0][j], v[1][j]), h23 = cvt2(v[2][j], v[3][j]);
+    *reinterpret_cast<uint2*>(hi + j * ld) =
+        make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+    if (LO)
+      *reinterpret_cast<uint2*>(lo + j * ld) =
+          make_uint2(pk(v[0][j] - (float)h01[0], v[1][j] - (float)h01[1]),
+                     pk(v[2][j] - (float)h23[0], v[3][j] - (float)h23[1]));
   }
 }
 
@@ -283,17 +296,21 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const bf16* xb = s.x + (int64_t)b * L * s.xs;
   const bf16* bb = s.b + (int64_t)b * L * s.bs;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
-  // of 4 tokens. The rows of head 0 are loaded together with those of B.
+  // of 4 tokens. The rows of heads 0 and 1 are loaded together with those of
+  // B; later heads are loaded two heads ahead.
   const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
   const int xnv = min(4, max(0, len - xtb * 4));
-  XRaw<CONV> xr;
+  XRaw<CONV> xr[2];
   {
     int cv, tbi;
     tmap(tid, cv, tbi);  // 16 channel vectors x 16 token blocks, one per thread
     const int n0 = cv * 8, tseq = t0 + tbi * 8, ch = s.HP + g * N + n0;
     Rows8<CONV> rb;
     rows_load<CONV, 8>(rb, bb + g * N + n0, s.bs, tseq, L - 1, s, ch, cin_b);
-    x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      x_load<CONV>(xr[k], xb + (h0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
+                   (h0 + k) * P + xp0, cin_b);
     conv_store<CONV, true>(rb, tseq, min(8, max(0, len - tbi * 8)), s, ch, cin_b,
                            BT + n0 * RS + tbi * 8, RS);
   }
@@ -326,16 +343,16 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
       bfr[i][ks] = *reinterpret_cast<const f16x8*>(BT + ((2 * wave + i) * 16 + rr) * RS +
                                                   ks * 32 + kk);
 
-  x_store<CONV, false>(xr, t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, &wv[0][xtb * 4],
+  x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, &wv[0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
   __syncthreads();
 
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const f16* XT = XB + (hh & 1) * (P * RS);
-    if (hh + 1 < HB) {
-      const int ch = (h0 + hh + 1) * P + xp0;
-      x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+    if (hh + 2 < HB) {
+      const int ch = (h0 + hh + 2) * P + xp0;
+      x_load<CONV>(xr[hh & 1], xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
     }
     f32x4 acc[2][4];
 #pragma unroll
@@ -361,8 +378,8 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     if (hh + 1 < HB) {
       f16* nx = XB + ((hh + 1) & 1) * (P * RS);
       const int ch = (h0 + hh + 1) * P + xp0;
-      x_store<CONV, false>(xr, t0 + xtb * 4, xnv, s, ch, cin_b, &wv[hh + 1][xtb * 4],
-                           nx + xp0 * RS + xtb * 4, nullptr, RS);
+      x_store<CONV, false>(xr[(hh + 1) & 1], t0 + xtb * 4, xnv, s, ch, cin_b,
+                           &wv[hh + 1][xtb * 4], nx + xp0 * RS + xtb * 4, nullptr, RS);
     }
     __syncthreads();
   }
@@ -473,6 +490,13 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const float dr1 = to_f(dt[(row0 + min(tc + 1, len - 1)) * H + h0 + wave]);
 
   const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
+  // x staging item of this thread (one head): 8 channel vectors x 32 blocks
+  // of 4 tokens; within 64 lanes, 2 vectors x 32 blocks. The rows of head 0
+  // are loaded with those of B and C.
+  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
+  const bf16* xb = s.x + (int64_t)b * L * s.xs;
+  const int xnv = min(4, max(0, len - xtb * 4));
+  XRaw<CONV> xr;
   // B and C, natural layout [t][n]: 16 channel vectors x 16 token blocks
   // each; the rows of both are loaded before either is converted.
   {
@@ -483,6 +507,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     Rows8<CONV> rb, rc;
     rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
     rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
+    x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
     conv_store<CONV, false>(rb, tseq, nv, s, chb, cin_b, Bs + (tbi * 8) * NS + n0, NS);
     conv_store<CONV, false>(rc, tseq, nv, s, chc, cin_b, Cs + (tbi * 8) * NS + n0, NS);
   }
@@ -577,19 +602,15 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
   __syncthreads();  // states no longer read: the x buffers follow
 
-  // x staging item of this thread (one head): 8 channel vectors x 32 blocks
-  // of 4 tokens; within 64 lanes, 2 vectors x 32 blocks.
-  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
-  const bf16* xb = s.x + (int64_t)b * L * s.xs;
-  const int xnv = min(4, max(0, len - xtb * 4));
-  XRaw<CONV> xr;
-  {
-    const int ch = h0 * P + xp0;
-    x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
-    x_store<CONV, true>(xr, t0 + xtb * 4, xnv, s, ch, cin_b, nullptr, U + xp0 * RS + xtb * 4,
-                        U + P * RS + xp0 * RS + xtb * 4, RS);
-  }
+  x_store<CONV, true>(xr, t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, nullptr,
+                      U + xp0 * RS + xtb * 4, U + P * RS + xp0 * RS + xtb * 4, RS);
   __syncthreads();
+
+  // epilogue mapping: 32 consecutive threads take one row (8 channels each),
+  // thread rows t = tid / 32 + 8 e; z is fetched during the last head
+  const int ev8 = tid & 31, et0 = tid >> 5;
+  constexpr int EPI = QI * (HB * P / 8) / NT;  // 16 rows per thread
+  u32x4 zr[NORM ? EPI : 1];
 
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
@@ -598,6 +619,13 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     if (hh + 1 < HB) {
       const int ch = (h0 + hh + 1) * P + xp0;
       x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+    } else if (NORM) {
+#pragma unroll
+      for (int e = 0; e < EPI; ++e) {
+        const int t = et0 + 8 * e;
+        zr[e] = *reinterpret_cast<const u32x4*>(z + (row0 + min(t, len - 1)) * HP + h0 * P +
+                                                ev8 * 8);
+      }
     }
     const float Dh = D ? D[h0 + hh] : 0.f;
     const f16 dhi = (f16)Dh, dlo = (f16)(Dh - (float)dhi);
@@ -696,20 +724,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     __syncthreads();
   }
 
-  // Epilogue: 32 consecutive threads take one row (8 channels each); thread
-  // rows t = tid / 32 + 8 e. z is fetched before y goes through LDS.
-  const int ev8 = tid & 31, et0 = tid >> 5;
-  constexpr int EPI = QI * (HB * P / 8) / NT;  // 16 rows per thread
-  u32x4 zr[NORM ? EPI : 1];
+  // Epilogue
   float wv8[8];
-  if (NORM) {
-#pragma unroll
-    for (int e = 0; e < EPI; ++e) {
-      const int t = et0 + 8 * e;
-      zr[e] = *reinterpret_cast<const u32x4*>(z + (row0 + min(t, len - 1)) * HP + h0 * P + ev8 * 8);
-    }
-    load8(nw + h0 * P + ev8 * 8, wv8);
-  }
+  if (NORM) load8(nw + h0 * P + ev8 * 8, wv8);
   // y -> Ot [t][4 heads x P]: a lane's 4 channels of one token are 8 bytes
 #pragma unroll
   for (int ui = 0; ui < 2; ++ui) {
