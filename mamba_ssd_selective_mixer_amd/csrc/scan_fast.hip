@@ -26,9 +26,16 @@ namespace fast {
 
 constexpr int P = 64, N = 128, QI = 128, HB = 4, W = 4;
 constexpr int NT = 256;       // threads per workgroup (4 waves): two workgroups fit a CU
-constexpr int RS = QI + 8;    // padded 16-bit row of [.][QI] tiles (16 B skew per row)
-constexpr int NS = N + 8;     // padded 16-bit row of [.][N] tiles
-constexpr int OS = HB * P + 8;
+// LDS row pitches in 16-bit elements. [.][QI] tiles (x, B^T) are read 8
+// bytes per lane by 16 consecutive rows: a pitch of 2 mod 32 banks keeps those
+// reads (and the 8-byte transposed writes) free of bank conflicts, at the
+// price of 8-byte (not 16-byte) row alignment, so every access to them is at
+// most 8 bytes wide. [.][N] tiles are read 16 bytes per lane by 8 rows:
+// a pitch of 4 mod 32 banks, 16-byte aligned. The output tile [t][4 heads x
+// P] is written 8 bytes per lane by 16 rows: 2 mod 32 banks.
+constexpr int RS = QI + 4;
+constexpr int NS = N + 8;
+constexpr int OS = HB * P + 4;
 
 // Where the x / B / C rows of one batch come from.
 struct Src {
@@ -58,9 +65,20 @@ SSD_DEV f16x2 cvt2(float a, float b) { return __builtin_convertvector(f32x2{a, b
 SSD_DEV uint32_t pk(float a, float b) { return __builtin_bit_cast(uint32_t, cvt2(a, b)); }
 SSD_DEV float h2f_lo(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu)); }
 SSD_DEV float h2f_hi(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16)); }
+// 16 bytes from an 8-byte aligned LDS address, as two 8-byte accesses
+SSD_DEV f16x8 lds16(const f16* p) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 4);
+  return __builtin_bit_cast(f16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
+SSD_DEV void sts16(f16* p, const u32x4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(v[0], v[1]);
+  *reinterpret_cast<uint2*>(p + 4) = make_uint2(v[2], v[3]);
+}
 SSD_DEV void load8h(const f16* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 4);
+  const uint32_t w[4] = {a.x, a.y, b.x, b.y};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = h2f_lo(w[i]);
@@ -191,8 +209,8 @@ SSD_DEV void conv_store(Rows8<CONV>& raw, int tseq, int nvalid, const Src& s, in
   if (TRANS) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4*>(dst + j * ld) = u32x4{pk(v[0][j], v[1][j]), pk(v[2][j], v[3][j]),
-                                                      pk(v[4][j], v[5][j]), pk(v[6][j], v[7][j])};
+      sts16(dst + j * ld, u32x4{pk(v[0][j], v[1][j]), pk(v[2][j], v[3][j]), pk(v[4][j], v[5][j]),
+                                pk(v[6][j], v[7][j])});
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -340,8 +358,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      bfr[i][ks] = *reinterpret_cast<const f16x8*>(BT + ((2 * wave + i) * 16 + rr) * RS +
-                                                  ks * 32 + kk);
+      bfr[i][ks] = lds16(BT + ((2 * wave + i) * 16 + rr) * RS + ks * 32 + kk);
 
   x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, &wv[0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
@@ -363,7 +380,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const f16x8 xf = *reinterpret_cast<const f16x8*>(XT + (pt * 16 + rr) * RS + ks * 32 + kk);
+        const f16x8 xf = lds16(XT + (pt * 16 + rr) * RS + ks * 32 + kk);
         acc[0][pt] = mma16(bfr[0][ks], xf, acc[0][pt]);
         acc[1][pt] = mma16(bfr[1][ks], xf, acc[1][pt]);
       }
@@ -466,7 +483,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 const bf16* __restrict__ nw, float eps,
                                                 bf16* __restrict__ out, int L, int H, int G,
                                                 int nc) {
-  static_assert(4 * P * RS == 2 * QI * NS, "two x buffers fill the B/C space");
+  static_assert(4 * P * RS <= 2 * QI * NS, "two x buffers fit the B/C space");
   static_assert(HB * P * NS == 2 * QI * NS, "the 4 heads' states fill the B/C space");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
   __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then states, then x buffers, then Ot
@@ -665,9 +682,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
             g0 = Gb[2 * ks];
             g1 = (2 * ks + 1 <= rt) ? Gb[2 * ks + 1] : make_uint2(0u, 0u);
           }
-          const float gv[8] = {h2f_lo(g0.x), h2f_hi(g0.x), h2f_lo(g0.y), h2f_hi(g0.y),
-                               h2f_lo(g1.x), h2f_hi(g1.x), h2f_lo(g1.y), h2f_hi(g1.y)};
-          f16x8 af;
+          // decay factors (fp32) -> fp16 pairs, times the fp16 C.B^T pairs
+          float dj[8];
           if (2 * ks + 2 <= rt) {
             // whole block before the row tile: exp(Lam_t - Lam_s) dt_s =
             // exp(Lam_t - Lam_ref) csd_s, both factors <= 1
@@ -676,7 +692,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
             const float4 c1 = *reinterpret_cast<const float4*>(&csd[hh][s0 + 16]);
             const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) af[j] = (f16)(gv[j] * rf * cs[j]);
+            for (int j = 0; j < 8; ++j) dj[j] = rf * cs[j];
           } else {
             const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
             const float4 l1 = *reinterpret_cast<const float4*>(&lam[hh][s0 + 16]);
@@ -689,10 +705,17 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
               const int sj = s0 + (j & 3) + (j >> 2) * 16;
               // s > t gives exp2 of a positive argument (possibly inf);
               // the select drops it
-              const float m = gv[j] * fexp2(lt - ls[j]) * ds[j];
-              af[j] = (f16)(sj <= trow ? m : 0.f);
+              const float m = fexp2(lt - ls[j]) * ds[j];
+              dj[j] = sj <= trow ? m : 0.f;
             }
           }
+          const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y};
+          u32x4 aw;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            aw[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, gw[q]) *
+                                                     cvt2(dj[2 * q], dj[2 * q + 1]));
+          const f16x8 af = __builtin_bit_cast(f16x8, aw);
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) {
             const f16* xr0 = XT + (pt * 16 + rr) * RS + s0;
@@ -706,7 +729,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       // D x: A = [x_hi | x_lo] over the row tile's 16 positions
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const f16x8 xa = *reinterpret_cast<const f16x8*>((q4 < 2 ? XT : XL) + (pt * 16 + rr) * RS +
+        const f16x8 xa = lds16((q4 < 2 ? XT : XL) + (pt * 16 + rr) * RS +
                                                          rt * 16 + 8 * (q4 & 1));
         acc[pt] = mma16(xa, dfh, acc[pt]);
         acc[pt] = mma16(xa, dfl, acc[pt]);
