@@ -4,13 +4,16 @@
 //
 // For each row and each of G groups of S = HP/G contiguous channels:
 //   q = y * silu(z);  out = q * w / sqrt(mean(q^2) + eps).
-// One workgroup per row; each wave reduces whole groups with 8-channel
-// vector accesses and a wave64 butterfly sum, then re-reads its group (from
-// L1/L2) to scale and store.
+// One workgroup per row; each wave takes whole groups. When a group fits in
+// kNormVec 8-channel vectors per lane (S <= 64 * 8 * kNormVec), q stays in
+// registers between the sum of squares and the scaled store, so y, z and
+// the SiLU are touched once; larger groups re-read y and z (from L1/L2).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ssd {
+
+constexpr int kNormVec = 4;
 
 template <class T, class TY>
 __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
@@ -20,6 +23,42 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
   const int64_t row = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int S = HP / G, S8 = S / 8;
+  const float inv_S = 1.0f / (float)S;
+  if (S8 <= 64 * kNormVec) {
+    for (int j = wave; j < G; j += 4) {
+      const int64_t base = row * HP + (int64_t)j * S;
+      float q[kNormVec][8];
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < kNormVec; ++k) {
+        const int v = lane + 64 * k;
+        if (v < S8) {
+          float yv[8], zv[8];
+          load8(y + base + v * 8, yv);
+          load8(z + base + v * 8, zv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            q[k][i] = yv[i] * silu(zv[i]);
+            ss += q[k][i] * q[k][i];
+          }
+        }
+      }
+      ss = wave_sum(ss);
+      const float inv = __builtin_amdgcn_rsqf(ss * inv_S + eps);
+#pragma unroll
+      for (int k = 0; k < kNormVec; ++k) {
+        const int v = lane + 64 * k;
+        if (v < S8) {
+          float wv[8], o[8];
+          load8(w + (int64_t)j * S + v * 8, wv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = q[k][i] * wv[i] * inv;
+          store8(out + base + v * 8, o);
+        }
+      }
+    }
+    return;
+  }
   for (int j = wave; j < G; j += 4) {
     const int64_t base = row * HP + (int64_t)j * S;
     float ss = 0.f;
@@ -34,7 +73,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
       }
     }
     ss = wave_sum(ss);
-    const float inv = __builtin_amdgcn_rsqf(ss / (float)S + eps);
+    const float inv = __builtin_amdgcn_rsqf(ss * inv_S + eps);
     for (int v = lane; v < S8; v += 64) {
       float yv[8], zv[8], wv[8], o[8];
       load8(y + base + v * 8, yv);

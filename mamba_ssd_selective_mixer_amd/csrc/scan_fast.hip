@@ -297,44 +297,19 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
                                                int nc) {
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
-  __shared__ float wv[HB][QI];
-  const int c = blockIdx.x, hpb = H / HB;
-  const int b = blockIdx.y / hpb, h0 = (blockIdx.y % hpb) * HB, g = h0 / (H / G);
+  __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
+  const int c = blockIdx.x, hpg = H / G;
+  const int b = blockIdx.y / G, g = blockIdx.y % G, hg0 = g * hpg;
   const int t0 = c * QI, len = min(QI, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
-
-  // dt of head `wave`, positions 2 lane and 2 lane + 1, fetched before B
   const int tc = 2 * lane;
-  const float dr0 = to_f(dt[(row0 + min(tc, len - 1)) * H + h0 + wave]);
-  const float dr1 = to_f(dt[(row0 + min(tc + 1, len - 1)) * H + h0 + wave]);
 
-  const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
-  const bf16* xb = s.x + (int64_t)b * L * s.xs;
-  const bf16* bb = s.b + (int64_t)b * L * s.bs;
-  // x staging item of this thread (one head): 8 channel vectors x 32 blocks
-  // of 4 tokens. The rows of heads 0 and 1 are loaded together with those of
-  // B; later heads are loaded two heads ahead.
-  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
-  const int xnv = min(4, max(0, len - xtb * 4));
-  XRaw<CONV> xr[2];
-  {
-    int cv, tbi;
-    tmap(tid, cv, tbi);  // 16 channel vectors x 16 token blocks, one per thread
-    const int n0 = cv * 8, tseq = t0 + tbi * 8, ch = s.HP + g * N + n0;
-    Rows8<CONV> rb;
-    rows_load<CONV, 8>(rb, bb + g * N + n0, s.bs, tseq, L - 1, s, ch, cin_b);
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      x_load<CONV>(xr[k], xb + (h0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
-                   (h0 + k) * P + xp0, cin_b);
-    conv_store<CONV, true>(rb, tseq, min(8, max(0, len - tbi * 8)), s, ch, cin_b,
-                           BT + n0 * RS + tbi * 8, RS);
-  }
-  {
-    // Lam = inclusive cumsum of dt A (flat past len, where dt counts as 0),
-    // kept in log2 units (Lam log2 e) so every decay is one exp2
+  // Lam = inclusive cumsum of dt A over the chunk for head h0 + wave (flat
+  // past len, where dt counts as 0), kept in log2 units so every decay is
+  // one exp2; w_s = exp(Lam_end - Lam_s) dt_s goes to dst[wave][s].
+  auto cumsum = [&](int h0, float dr0, float dr1, float (*dst)[QI]) {
     const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
     const float Ah = A[h0 + wave] * kLog2e;
     const float a0 = d0 * Ah, a1 = d1 * Ah;
@@ -346,10 +321,38 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     }
     const float l0 = v - a1, l1 = v;
     const float lamE = __shfl(l1, 63, 64);
-    wv[wave][tc] = fexp2(lamE - l0) * d0;
-    wv[wave][tc + 1] = fexp2(lamE - l1) * d1;
+    dst[wave][tc] = fexp2(lamE - l0) * d0;
+    dst[wave][tc + 1] = fexp2(lamE - l1) * d1;
     if (lane == 0) lam_end[((int64_t)b * H + h0 + wave) * nc + c] = lamE;
+  };
+  auto dt_at = [&](int h, int t) { return to_f(dt[(row0 + min(t, len - 1)) * H + h]); };
+
+  // dt of the first head block, fetched before B
+  const float dr0 = dt_at(hg0 + wave, tc), dr1 = dt_at(hg0 + wave, tc + 1);
+
+  const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
+  const bf16* xb = s.x + (int64_t)b * L * s.xs;
+  const bf16* bb = s.b + (int64_t)b * L * s.bs;
+  // x staging item of this thread (one head): 8 channel vectors x 32 blocks
+  // of 4 tokens. The rows of the group's heads 0 and 1 are loaded together
+  // with those of B; later heads are loaded two heads ahead.
+  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
+  const int xnv = min(4, max(0, len - xtb * 4));
+  XRaw<CONV> xr[2];
+  {
+    int cv, tbi;
+    tmap(tid, cv, tbi);  // 16 channel vectors x 16 token blocks, one per thread
+    const int n0 = cv * 8, tseq = t0 + tbi * 8, ch = s.HP + g * N + n0;
+    Rows8<CONV> rb;
+    rows_load<CONV, 8>(rb, bb + g * N + n0, s.bs, tseq, L - 1, s, ch, cin_b);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      x_load<CONV>(xr[k], xb + (hg0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
+                   (hg0 + k) * P + xp0, cin_b);
+    conv_store<CONV, true>(rb, tseq, min(8, max(0, len - tbi * 8)), s, ch, cin_b,
+                           BT + n0 * RS + tbi * 8, RS);
   }
+  cumsum(hg0, dr0, dr1, wv[0]);
   __syncthreads();
 
   // B^T fragments of n-tiles 2 wave, 2 wave + 1 (A operand: row n, k = s)
@@ -360,45 +363,58 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     for (int ks = 0; ks < 4; ++ks)
       bfr[i][ks] = lds16(BT + ((2 * wave + i) * 16 + rr) * RS + ks * 32 + kk);
 
-  x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, &wv[0][xtb * 4],
+  x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, hg0 * P + xp0, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
   __syncthreads();
 
+  // heads of the group in blocks of HB; head k = j HB + hh (even HB keeps
+  // the buffer parity of head k equal to the parity of hh)
+  for (int j = 0; j * HB < hpg; ++j) {
+    float(*wcur)[QI] = wv[j & 1];
+    float(*wnext)[QI] = wv[(j + 1) & 1];
+    const int h0 = hg0 + j * HB;
+    const bool more = (j + 1) * HB < hpg;
 #pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    const f16* XT = XB + (hh & 1) * (P * RS);
-    if (hh + 2 < HB) {
-      const int ch = (h0 + hh + 2) * P + xp0;
-      x_load<CONV>(xr[hh & 1], xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
-    }
-    f32x4 acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[i][pt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const f16x8 xf = lds16(XT + (pt * 16 + rr) * RS + ks * 32 + kk);
-        acc[0][pt] = mma16(bfr[0][ks], xf, acc[0][pt]);
-        acc[1][pt] = mma16(bfr[1][ks], xf, acc[1][pt]);
+    for (int hh = 0; hh < HB; ++hh) {
+      const int k = j * HB + hh;
+      const f16* XT = XB + (hh & 1) * (P * RS);
+      if (k + 2 < hpg) {
+        const int ch = (hg0 + k + 2) * P + xp0;
+        x_load<CONV>(xr[hh & 1], xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
       }
-    // lane: n = (2 wave + i) * 16 + r4 + r, p = pt * 16 + rr
-    f16* o = states + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
+      // next block's decay weights, published by this iteration's barrier
+      if (hh == HB - 2 && more) cumsum(h0 + HB, dt_at(h0 + HB + wave, tc),
+                                       dt_at(h0 + HB + wave, tc + 1), wnext);
+      f32x4 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        *reinterpret_cast<uint2*>(o + (pt * 16 + rr) * N + (2 * wave + i) * 16 + r4) =
-            make_uint2(pk(acc[i][pt][0], acc[i][pt][1]), pk(acc[i][pt][2], acc[i][pt][3]));
-    if (hh + 1 < HB) {
-      f16* nx = XB + ((hh + 1) & 1) * (P * RS);
-      const int ch = (h0 + hh + 1) * P + xp0;
-      x_store<CONV, false>(xr[(hh + 1) & 1], t0 + xtb * 4, xnv, s, ch, cin_b,
-                           &wv[hh + 1][xtb * 4], nx + xp0 * RS + xtb * 4, nullptr, RS);
+        for (int pt = 0; pt < 4; ++pt) acc[i][pt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const f16x8 xf = lds16(XT + (pt * 16 + rr) * RS + ks * 32 + kk);
+          acc[0][pt] = mma16(bfr[0][ks], xf, acc[0][pt]);
+          acc[1][pt] = mma16(bfr[1][ks], xf, acc[1][pt]);
+        }
+      // lane: n = (2 wave + i) * 16 + r4 + r, p = pt * 16 + rr
+      f16* o = states + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          *reinterpret_cast<uint2*>(o + (pt * 16 + rr) * N + (2 * wave + i) * 16 + r4) =
+              make_uint2(pk(acc[i][pt][0], acc[i][pt][1]), pk(acc[i][pt][2], acc[i][pt][3]));
+      if (k + 1 < hpg) {
+        f16* nx = XB + ((hh + 1) & 1) * (P * RS);
+        const int ch = (hg0 + k + 1) * P + xp0;
+        const float* sc = hh + 1 < HB ? &wcur[hh + 1][xtb * 4] : &wnext[0][xtb * 4];
+        x_store<CONV, false>(xr[(hh + 1) & 1], t0 + xtb * 4, xnv, s, ch, cin_b, sc,
+                             nx + xp0 * RS + xtb * 4, nullptr, RS);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -827,12 +843,14 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
 
   dim3 g1(nc, a.B * (a.H / HB));
   {
+  // one workgroup per (chunk, batch, group): B staged once for the group
   ProfScope ps(st, KID_FAST_STATE);
+  const dim3 g0(nc, a.B * a.G);
   if (a.conv)
-    hipLaunchKernelGGL(k_fstate<true>, g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
+    hipLaunchKernelGGL(k_fstate<true>, g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
                        lam_end, a.L, a.H, a.G, nc);
   else
-    hipLaunchKernelGGL(k_fstate<false>, g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
+    hipLaunchKernelGGL(k_fstate<false>, g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
                        lam_end, a.L, a.H, a.G, nc);
   }
   hipError_t e = hipGetLastError();

@@ -296,6 +296,13 @@ def test_prefill_bf16_conv_bias(ops, kw):
     prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=False)
 
 
+@pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333), dict(batch=3, seqlen=129)])
+def test_prefill_bf16_conv_bias_normed(ops, kw):
+    """Conv bias with the gated norm, every output element within 2e-2 (the
+    fp16 MFMA operands keep the shared-offset C.B^T sums precise enough)."""
+    prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=True)
+
+
 def test_prefill_generic_shapes(ops):
     """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
     prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
