@@ -225,12 +225,15 @@ def test_decode_bf16(ops, kw):
 
 # -------------------------------------------------------------- full prefill
 def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False, inplace=False,
-                 with_norm=True):
+                 with_norm=True, A=None):
     """Whole path (conv -> scan -> norm) with state in/out; optional chaining
-    over `pieces` (token boundaries) each resuming from the previous state."""
+    over `pieces` (token boundaries) each resuming from the previous state.
+    A, when given, replaces the drawn per-head decay rates."""
     import torch
     td = torch_dtype(cfg.dtype)
     prm = synth.layer_params(cfg, slow_decay=slow, with_bias=with_bias)
+    if A is not None:
+        prm["A"] = np.full(cfg.nheads, A, dtype=np.float32)
     inp = synth.prefill_inputs(cfg)
     st = synth.initial_states(cfg) if with_state else {"conv_state": None, "ssm_state": None}
     zz = inp["z"] if with_norm else None
@@ -301,6 +304,26 @@ def test_prefill_bf16_conv_bias_normed(ops, kw):
     """Conv bias with the gated norm, every output element within 2e-2 (the
     fp16 MFMA operands keep the shared-offset C.B^T sums precise enough)."""
     prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=True)
+
+
+@pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=2, seqlen=300))])
+def test_prefill_no_decay(ops, name, kw):
+    """A = 0: no forgetting, the scan is a running sum over the whole
+    sequence (states carried across every chunk and the initial state)."""
+    prefill_case(ops, small(name, **kw), with_state=True, A=0.0)
+
+
+@pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=2, seqlen=300))])
+def test_prefill_memoryless(ops, name, kw):
+    """A = -1e4: every decay underflows to 0, y_t = dt_t (C_t . B_t) x_t + D x_t."""
+    prefill_case(ops, small(name, **kw), with_state=True, A=-1e4)
+
+
+@pytest.mark.parametrize("name,L", [("c0", 1), ("c1", 1), ("c1", 2), ("c1", 129)])
+def test_prefill_short(ops, name, L):
+    """One- and two-token calls (shorter than the conv window) and a chunk
+    plus one token, resuming from nonzero conv and SSM states."""
+    prefill_case(ops, small(name, batch=2, seqlen=L), with_state=True)
 
 
 def test_prefill_generic_shapes(ops):
