@@ -284,11 +284,11 @@ SSD_DEV void x_store(XRaw<CONV>& r, int tseq, int nvalid, const Src& s, int ch,
 
 // ---------------------------------------------------------------- phase 1
 // dS_h [P x N] = sum_s x_s w_s (outer) B_s, w_s = exp(Lam_end - Lam_s) dt_s,
-// for the 4 heads of the workgroup, computed transposed (dS_h^T = B^T X'),
-// so each lane holds 4 consecutive n of one p and writes them as 8 bytes.
-// B^T is staged once (conv) and each wave keeps the fragments of its two
-// n-tiles in registers; x of one head at a time goes through two LDS
-// buffers, the next head's rows loaded while the current head is computed.
+// for every head of the group, computed transposed (dS_h^T = B^T X'), so
+// each lane holds 4 consecutive n of one p and stores them as 8 bytes (a
+// wave's four stores per row cover one whole 128-byte line). B^T is staged
+// once (conv) for the group; x of one head at a time goes through two LDS
+// buffers, the rows of later heads loaded two heads ahead.
 template <bool CONV>
 __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict__ dt,
                                                const float* __restrict__ A,
@@ -355,13 +355,10 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   cumsum(hg0, dr0, dr1, wv[0]);
   __syncthreads();
 
-  // B^T fragments of n-tiles 2 wave, 2 wave + 1 (A operand: row n, k = s)
-  f16x8 bfr[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      bfr[i][ks] = lds16(BT + ((2 * wave + i) * 16 + rr) * RS + ks * 32 + kk);
+  // wave w: n-tiles 4 (w & 1) .. + 3 (one 128-byte half row of dS^T) and
+  // p-tiles 2 (w >> 1), + 1, so each row segment a wave stores is a whole
+  // cache line
+  const int nt0 = 4 * (wave & 1), pt0 = 2 * (wave >> 1);
 
   x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, hg0 * P + xp0, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
@@ -385,27 +382,33 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
       // next block's decay weights, published by this iteration's barrier
       if (hh == HB - 2 && more) cumsum(h0 + HB, dt_at(h0 + HB + wave, tc),
                                        dt_at(h0 + HB + wave, tc + 1), wnext);
-      f32x4 acc[2][4];
+      f32x4 acc[4][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[i][pt] = zero4();
+        for (int pi = 0; pi < 2; ++pi) acc[j][pi] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks) {
+        f16x8 xf[2];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const f16x8 xf = lds16(XT + (pt * 16 + rr) * RS + ks * 32 + kk);
-          acc[0][pt] = mma16(bfr[0][ks], xf, acc[0][pt]);
-          acc[1][pt] = mma16(bfr[1][ks], xf, acc[1][pt]);
+        for (int pi = 0; pi < 2; ++pi)
+          xf[pi] = lds16(XT + ((pt0 + pi) * 16 + rr) * RS + ks * 32 + kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // B^T fragment (A operand: row n, k = s)
+          const f16x8 bf = lds16(BT + ((nt0 + j) * 16 + rr) * RS + ks * 32 + kk);
+#pragma unroll
+          for (int pi = 0; pi < 2; ++pi) acc[j][pi] = mma16(bf, xf[pi], acc[j][pi]);
         }
-      // lane: n = (2 wave + i) * 16 + r4 + r, p = pt * 16 + rr
+      }
+      // lane: n = (nt0 + j) * 16 + r4 + r, p = (pt0 + pi) * 16 + rr
       f16* o = states + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          *reinterpret_cast<uint2*>(o + (pt * 16 + rr) * N + (2 * wave + i) * 16 + r4) =
-              make_uint2(pk(acc[i][pt][0], acc[i][pt][1]), pk(acc[i][pt][2], acc[i][pt][3]));
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(o + ((pt0 + pi) * 16 + rr) * N + (nt0 + j) * 16 + r4) =
+              make_uint2(pk(acc[j][pi][0], acc[j][pi][1]), pk(acc[j][pi][2], acc[j][pi][3]));
       if (k + 1 < hpg) {
         f16* nx = XB + ((hh + 1) & 1) * (P * RS);
         const int ch = (hg0 + k + 1) * P + xp0;
