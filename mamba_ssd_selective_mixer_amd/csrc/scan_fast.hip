@@ -659,8 +659,11 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
       for (int e = 0; e < EPI; ++e) {
         const int t = et0 + 8 * e;
-        zr[e] = *reinterpret_cast<const u32x4*>(z + (row0 + min(t, len - 1)) * HP + h0 * P +
-                                                ev8 * 8);
+        // z is read once, here: a streaming load does not displace the x, B
+        // and C lines (also read by the chunk-state kernel) or the chunk
+        // states held in the last-level cache
+        zr[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            z + (row0 + min(t, len - 1)) * HP + h0 * P + ev8 * 8));
       }
     }
     const float Dh = D ? D[h0 + hh] : 0.f;
@@ -802,7 +805,17 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 8; ++j) yv[j] *= wv8[j] * inv;
     }
-    if (t < len) store8(out + (row0 + t) * HP + h0 * P + ev8 * 8, yv);
+    if (t < len) {
+      bf16* yp = out + (row0 + t) * HP + h0 * P + ev8 * 8;
+      if constexpr (NORM) {
+        // streaming store: the normalised output is final
+        const u32x4 w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
+                         pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(yp));
+      } else {
+        store8(yp, yv);  // the separate gated norm reads it back
+      }
+    }
   }
 }
 
