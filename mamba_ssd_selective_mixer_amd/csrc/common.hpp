@@ -46,9 +46,12 @@ SSD_DEV void store8(float* p, const float (&v)[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+// two fp32 -> one word of two bf16 (round to nearest even; a in the low
+// half), one packed conversion
 SSD_DEV uint32_t pack_bf16x2(float a, float b) {
-  bf16 lo = (bf16)a, hi = (bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2));
 }
 SSD_DEV void store8(bf16* p, const float (&v)[8]) {
   uint4 a;
@@ -59,17 +62,48 @@ SSD_DEV void store8(bf16* p, const float (&v)[8]) {
   *reinterpret_cast<uint4*>(p) = a;
 }
 
-// ---- wave64 reductions ----------------------------------------------------
-SSD_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---- cross-lane sums, scans and broadcasts -------------------------------
+// Built on DPP row operations (a row is 16 lanes): each step is one VALU
+// instruction reading another lane's register, with no LDS round trip.
+// dpp_src<CTRL, ROWS>(v): the value of the lane CTRL selects, 0 where it
+// selects no lane (bound_ctrl) or where the row is not in the ROWS mask.
+template <int CTRL, int ROWS = 0xF>
+SSD_DEV float dpp_src(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, true));
+}
+// Sum over aligned groups of W lanes (W a power of two <= 64). For W <= 16
+// every lane of the group holds the sum; for W = 32 and 64 the group's last
+// lane does.
+template <int W>
+SSD_DEV float group_sum_last(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v += dpp_src<0xB1>(v);        // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_src<0x4E>(v);        // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_src<0x141>(v);       // row_half_mirror
+  if constexpr (W >= 16) v += dpp_src<0x140>(v);      // row_mirror
+  if constexpr (W >= 32) v += dpp_src<0x142, 0xA>(v); // row_bcast:15 into rows 1, 3
+  if constexpr (W >= 64) v += dpp_src<0x143, 0xC>(v); // row_bcast:31 into rows 2, 3
   return v;
 }
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
-SSD_DEV float group_sum(float v, int width) {
-  for (int o = width >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// value of lane l (uniform)
+SSD_DEV float lane_value(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// sum over the 64 lanes (uniform)
+SSD_DEV float wave_sum(float v) { return lane_value(group_sum_last<64>(v), 63); }
+// inclusive prefix sum over the 64 lanes
+SSD_DEV float wave_incl_scan(float v) {
+  v += dpp_src<0x111>(v);       // row_shr:1
+  v += dpp_src<0x112>(v);       // row_shr:2
+  v += dpp_src<0x114>(v);       // row_shr:4
+  v += dpp_src<0x118>(v);       // row_shr:8
+  v += dpp_src<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_src<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
+// value of the last lane of this lane's row
+SSD_DEV float row_last(float v) { return dpp_src<0x15F>(v); }  // row_newbcast:15
 
 // ---- MFMA fragments ---------------------------------------------------------
 // 16x16 output tile, fp32 accumulate. For one MFMA of depth KSTEP, lane l

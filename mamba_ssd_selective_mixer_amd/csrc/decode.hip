@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
           v[3] = al * v[3] + dx * Bv.w;
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(st + e));
           float part = v[0] * Cv.x + v[1] * Cv.y + v[2] * Cv.z + v[3] * Cv.w;
-          part = group_sum(part, LPR);
-          if ((tid % LPR) == 0) ys[hl * P + p] = part + Dh * xp;
+          part = group_sum_last<LPR>(part);
+          if ((tid % LPR) == LPR - 1) ys[hl * P + p] = part + Dh * xp;
         }
       }
 #pragma unroll
@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
             v[3] = al * v[3] + dx * Bv.w;
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(st + e));
             float part = v[0] * Cv.x + v[1] * Cv.y + v[2] * Cv.z + v[3] * Cv.w;
-            part = group_sum(part, LPR);
-            if ((tid % LPR) == 0) ys[hl * P + p] = part + Dh * xp;
+            part = group_sum_last<LPR>(part);
+            if ((tid % LPR) == LPR - 1) ys[hl * P + p] = part + Dh * xp;
           }
         }
       }

@@ -34,12 +34,7 @@ __device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, int64_t r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float d = 0.f;
   if (tid < len) d = to_f(dt[(row0 + tid) * H + h]);
-  float v = d * Ah;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  const float v = wave_incl_scan(d * Ah);
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
   float add = 0.f;

@@ -302,7 +302,8 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const int b = blockIdx.y / G, g = blockIdx.y % G, hg0 = g * hpg;
   const int t0 = c * QI, len = min(QI, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: read it into a scalar register
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
   const int tc = 2 * lane;
 
@@ -313,14 +314,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
     const float Ah = A[h0 + wave] * kLog2e;
     const float a0 = d0 * Ah, a1 = d1 * Ah;
-    float v = a0 + a1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float n = __shfl_up(v, o, 64);
-      if (lane >= o) v += n;
-    }
+    const float v = wave_incl_scan(a0 + a1);
     const float l0 = v - a1, l1 = v;
-    const float lamE = __shfl(l1, 63, 64);
+    const float lamE = lane_value(l1, 63);
     dst[wave][tc] = fexp2(lamE - l0) * d0;
     dst[wave][tc + 1] = fexp2(lamE - l1) * d1;
     if (lane == 0) lam_end[((int64_t)b * H + h0 + wave) * nc + c] = lamE;
@@ -516,7 +512,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const int b = blockIdx.y / hpb, h0 = (blockIdx.y % hpb) * HB, g = h0 / (H / G);
   const int t0 = c * QI, len = min(QI, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: read it into a scalar register
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
   const int HP = s.HP;
 
@@ -553,14 +550,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
     const float Ah = A[h0 + wave] * kLog2e;  // Lam in log2 units
     const float a0 = d0 * Ah, a1 = d1 * Ah;
-    float v = a0 + a1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float n = __shfl_up(v, o, 64);
-      if (lane >= o) v += n;
-    }
+    const float v = wave_incl_scan(a0 + a1);
     const float l0 = v - a1, l1 = v;
-    const float lref = __shfl(l1, lane | 15, 64);
+    const float lref = row_last(l1);  // lane 16 k + 15 ends the block of 32
     lam[wave][tc] = l0;
     lam[wave][tc + 1] = l1;
     dts[wave][tc] = d0;
@@ -644,10 +636,16 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 
   // epilogue mapping: 32 consecutive threads take one row (8 channels each),
   // thread rows t = tid / 32 + 8 e; z is fetched during the last head
-  const int ev8 = tid & 31, et0 = tid >> 5;
-  constexpr int EPI = QI * (HB * P / 8) / NT;  // 16 rows per thread
-  u32x4 zr[NORM ? EPI : 1];
+  static_assert(HB * P == 256 && NT == 256, "epilogue mapping");
+  const int ev8 = tid & 15, et0 = tid >> 4;
+  constexpr int EPI = QI / (NT / 16);  // 8 rows per thread
+  u32x4 zr[NORM ? 2 * EPI : 1];
 
+  // causal mask of the diagonal 16 x 16 tiles, position r of this lane's
+  // k-slot quadruple: s = 16 rt + r4 + r against t = 16 rt + rr
+  bool dmask[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dmask[r] = r4 + r <= rr;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
     const f16* XT = U + (hh & 1) * (2 * P * RS);  // [p][s]: fp16(x)
@@ -658,12 +656,14 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     } else if (NORM) {
 #pragma unroll
       for (int e = 0; e < EPI; ++e) {
-        const int t = et0 + 8 * e;
+        const int t = et0 + 16 * e;
         // z is read once, here: a streaming load does not displace the x, B
         // and C lines (also read by the chunk-state kernel) or the chunk
         // states held in the last-level cache
-        zr[e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            z + (row0 + min(t, len - 1)) * HP + h0 * P + ev8 * 8));
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          zr[2 * e + hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              z + (row0 + min(t, len - 1)) * HP + h0 * P + hf * 128 + ev8 * 8));
       }
     }
     const float Dh = D ? D[h0 + hh] : 0.f;
@@ -716,19 +716,39 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
             for (int j = 0; j < 8; ++j) dj[j] = rf * cs[j];
           } else {
-            const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
-            const float4 l1 = *reinterpret_cast<const float4*>(&lam[hh][s0 + 16]);
-            const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][s0]);
-            const float4 d1 = *reinterpret_cast<const float4*>(&dts[hh][s0 + 16]);
-            const float ls[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-            const float ds[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            // the block holding the diagonal 16 x 16 tile: for odd rt its
+            // first 16 positions all precede the row tile (no mask) and the
+            // tile is its second half; for even rt the tile is its first
+            // half and the second half lies after every t (zero). In the
+            // tile, s <= t is r4 + r <= rr. Masked positions give exp2 of a
+            // positive argument (possibly inf); the select drops it.
+            const int sd = (rt & 1) ? s0 + 16 : s0;
+            const float4 ld = *reinterpret_cast<const float4*>(&lam[hh][sd]);
+            const float4 dd = *reinterpret_cast<const float4*>(&dts[hh][sd]);
+            const float lsd[4] = {ld.x, ld.y, ld.z, ld.w};
+            const float dsd[4] = {dd.x, dd.y, dd.z, dd.w};
+            float md[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int sj = s0 + (j & 3) + (j >> 2) * 16;
-              // s > t gives exp2 of a positive argument (possibly inf);
-              // the select drops it
-              const float m = fexp2(lt - ls[j]) * ds[j];
-              dj[j] = sj <= trow ? m : 0.f;
+            for (int r = 0; r < 4; ++r) {
+              const float m = fexp2(lt - lsd[r]) * dsd[r];
+              md[r] = dmask[r] ? m : 0.f;
+            }
+            if (rt & 1) {
+              const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
+              const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][s0]);
+              const float ls[4] = {l0.x, l0.y, l0.z, l0.w};
+              const float ds[4] = {d0.x, d0.y, d0.z, d0.w};
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                dj[r] = fexp2(lt - ls[r]) * ds[r];
+                dj[4 + r] = md[r];
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                dj[r] = md[r];
+                dj[4 + r] = 0.f;
+              }
             }
           }
           const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y};
@@ -769,9 +789,13 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     __syncthreads();
   }
 
-  // Epilogue
-  float wv8[8];
-  if (NORM) load8(nw + h0 * P + ev8 * 8, wv8);
+  // Epilogue: 16 consecutive threads (one DPP row) take one token row, 8
+  // channels from each 128-channel half, rows t = tid / 16 + 16 e
+  float wv8[2][8];
+  if (NORM) {
+    load8(nw + h0 * P + ev8 * 8, wv8[0]);
+    load8(nw + h0 * P + 128 + ev8 * 8, wv8[1]);
+  }
   // y -> Ot [t][4 heads x P]: a lane's 4 channels of one token are 8 bytes
 #pragma unroll
   for (int ui = 0; ui < 2; ++ui) {
@@ -787,33 +811,41 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 
 #pragma unroll
   for (int e = 0; e < EPI; ++e) {
-    const int t = et0 + 8 * e;
-    float yv[8];
-    load8h(Ot + t * OS + ev8 * 8, yv);
+    const int t = et0 + 16 * e;
+    float yv[2][8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) load8h(Ot + t * OS + hf * 128 + ev8 * 8, yv[hf]);
     if (NORM) {
-      float zv[8];
-      unpack8(zr[e], zv);
       float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        yv[j] *= silu(zv[j]);
-        ss += yv[j] * yv[j];
-      }
+      for (int hf = 0; hf < 2; ++hf) {
+        float zv[8];
+        unpack8(zr[2 * e + hf], zv);
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, 64);
+        for (int j = 0; j < 8; ++j) {
+          yv[hf][j] *= silu(zv[j]);
+          ss += yv[hf][j] * yv[hf][j];
+        }
+      }
+      ss = group_sum_last<16>(ss);
       const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / (HB * P)) + eps);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) yv[j] *= wv8[j] * inv;
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) yv[hf][j] *= wv8[hf][j] * inv;
     }
     if (t < len) {
-      bf16* yp = out + (row0 + t) * HP + h0 * P + ev8 * 8;
-      if constexpr (NORM) {
-        // streaming store: the normalised output is final
-        const u32x4 w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
-                         pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(yp));
-      } else {
-        store8(yp, yv);  // the separate gated norm reads it back
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16* yp = out + (row0 + t) * HP + h0 * P + hf * 128 + ev8 * 8;
+        if constexpr (NORM) {
+          // streaming store: the normalised output is final
+          const u32x4 w = {pack_bf16x2(yv[hf][0], yv[hf][1]), pack_bf16x2(yv[hf][2], yv[hf][3]),
+                           pack_bf16x2(yv[hf][4], yv[hf][5]), pack_bf16x2(yv[hf][6], yv[hf][7])};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(yp));
+        } else {
+          store8(yp, yv[hf]);  // the separate gated norm reads it back
+        }
       }
     }
   }
