@@ -639,7 +639,18 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   static_assert(HB * P == 256 && NT == 256, "epilogue mapping");
   const int ev8 = tid & 15, et0 = tid >> 4;
   constexpr int EPI = QI / (NT / 16);  // 8 rows per thread
+  constexpr int ZPF = EPI / 2;         // rows whose z is fetched during the last head
   u32x4 zr[NORM ? 2 * EPI : 1];
+  auto z_fetch = [&](int e) {
+    const int t = et0 + 16 * e;
+    // z is read once, here: a streaming load does not displace the x, B
+    // and C lines (also read by the chunk-state kernel) or the chunk
+    // states held in the last-level cache
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      zr[2 * e + hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          z + (row0 + min(t, len - 1)) * HP + h0 * P + hf * 128 + ev8 * 8));
+  };
 
   // causal mask of the diagonal 16 x 16 tiles, position r of this lane's
   // k-slot quadruple: s = 16 rt + r4 + r against t = 16 rt + rr
@@ -655,16 +666,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
     } else if (NORM) {
 #pragma unroll
-      for (int e = 0; e < EPI; ++e) {
-        const int t = et0 + 16 * e;
-        // z is read once, here: a streaming load does not displace the x, B
-        // and C lines (also read by the chunk-state kernel) or the chunk
-        // states held in the last-level cache
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          zr[2 * e + hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              z + (row0 + min(t, len - 1)) * HP + h0 * P + hf * 128 + ev8 * 8));
-      }
+      for (int e = 0; e < ZPF; ++e) z_fetch(e);
     }
     const float Dh = D ? D[h0 + hh] : 0.f;
     const f16 dhi = (f16)Dh, dlo = (f16)(Dh - (float)dhi);
@@ -758,14 +760,16 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
             aw[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, gw[q]) *
                                                      cvt2(dj[2 * q], dj[2 * q + 1]));
           const f16x8 af = __builtin_bit_cast(f16x8, aw);
+          f16x8 xa[4];
 #pragma unroll
           for (int pt = 0; pt < 4; ++pt) {
             const f16* xr0 = XT + (pt * 16 + rr) * RS + s0;
             const uint2 lo = *reinterpret_cast<const uint2*>(xr0);
             const uint2 hi2 = *reinterpret_cast<const uint2*>(xr0 + 16);
-            const uint4 u = make_uint4(lo.x, lo.y, hi2.x, hi2.y);
-            acc[pt] = mma16(__builtin_bit_cast(f16x8, u), af, acc[pt]);
+            xa[pt] = __builtin_bit_cast(f16x8, make_uint4(lo.x, lo.y, hi2.x, hi2.y));
           }
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) acc[pt] = mma16(xa[pt], af, acc[pt]);
         }
       }
       // D x: A = [x_hi | x_lo] over the row tile's 16 positions
@@ -790,7 +794,12 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
 
   // Epilogue: 16 consecutive threads (one DPP row) take one token row, 8
-  // channels from each 128-channel half, rows t = tid / 16 + 16 e
+  // channels from each 128-channel half, rows t = tid / 16 + 16 e; the z of
+  // the later rows is fetched now, behind the first rows' work
+  if constexpr (NORM) {
+#pragma unroll
+    for (int e = ZPF; e < EPI; ++e) z_fetch(e);
+  }
   float wv8[2][8];
   if (NORM) {
     load8(nw + h0 * P + ev8 * 8, wv8[0]);
