@@ -128,22 +128,34 @@ SSD_DEV void conv_chan(const u32x4 (&raw)[T + W - 1], const u32x4 (&wraw)[4], fl
 #pragma unroll
   for (int i = 0; i < T; ++i) v[i][J] = silu(dot2bf(pr[i], w01, dot2bf(pr[i + 2], w23, bias)));
 }
-template <bool CONV, int T>
-SSD_DEV void conv_tile(const u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const Src& s, int ch,
-                       float (&v)[T][8]) {
+// Conv weights (8 channels x 4 taps, bf16, element (j, k) at j*W + k) and
+// bias (8 bf16, zero without one) of one 8-channel vector. Loaded by the
+// caller ahead of the rows they are applied to, so that waiting for those
+// rows also covers them and never drains later loads or stores.
+template <bool CONV>
+struct ConvW {
+  u32x4 w[4];
+  u32x4 b;
+};
+template <>
+struct ConvW<false> {};
+template <bool CONV>
+SSD_DEV void convw_load(ConvW<CONV>& cw, const Src& s, int ch) {
   if constexpr (CONV) {
     static_assert(W == 4, "two bf16 pairs per window");
-    u32x4 wraw[4];  // 8 channels x 4 taps, bf16, element (j, k) at j*W + k
     const u32x4* wp = reinterpret_cast<const u32x4*>(s.cw + (int64_t)ch * W);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wraw[q] = wp[q];
+    for (int q = 0; q < 4; ++q) cw.w[q] = wp[q];
+    cw.b = s.cbias ? *reinterpret_cast<const u32x4*>(s.cbias + ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+template <bool CONV, int T>
+SSD_DEV void conv_tile(const u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const ConvW<CONV>& cw,
+                       float (&v)[T][8]) {
+  if constexpr (CONV) {
+    const u32x4(&wraw)[4] = cw.w;
     float bi[8];
-    if (s.cbias) {
-      load8(s.cbias + ch, bi);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bi[j] = 0.f;
-    }
+    unpack8(cw.b, bi);
     conv_chan<0, T>(raw, wraw, bi[0], v);
     conv_chan<1, T>(raw, wraw, bi[1], v);
     conv_chan<2, T>(raw, wraw, bi[2], v);
@@ -195,11 +207,11 @@ SSD_DEV void rows_mask_head(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], int tseq, cons
 template <bool CONV>
 using Rows8 = u32x4[8 + (CONV ? W - 1 : 0)];
 template <bool CONV, bool TRANS>
-SSD_DEV void conv_store(Rows8<CONV>& raw, int tseq, int nvalid, const Src& s, int ch,
+SSD_DEV void conv_store(Rows8<CONV>& raw, const ConvW<CONV>& cw, int tseq, int nvalid,
                         const bf16* cin_b, f16* dst, int ld) {
   rows_mask_head<CONV, 8>(raw, tseq, cin_b);
   float v[8][8];
-  conv_tile<CONV, 8>(raw, s, ch, v);
+  conv_tile<CONV, 8>(raw, cw, v);
   if (nvalid < 8) {  // only the tail of a sequence
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -218,14 +230,6 @@ SSD_DEV void conv_store(Rows8<CONV>& raw, int tseq, int nvalid, const Src& s, in
                                                       pk(v[i][4], v[i][5]), pk(v[i][6], v[i][7])};
   }
 }
-template <bool CONV, bool TRANS>
-SSD_DEV void conv_stage(const bf16* __restrict__ src, int64_t ts, int tseq, int nvalid, int Lm1,
-                        const Src& s, int ch, const bf16* cin_b, f16* dst, int ld) {
-  Rows8<CONV> raw;
-  rows_load<CONV, 8>(raw, src, ts, tseq, Lm1, s, ch, cin_b);
-  conv_store<CONV, TRANS>(raw, tseq, nvalid, s, ch, cin_b, dst, ld);
-}
-
 // x-channel block mapping for transposed staging: within 16 lanes, 2 channel
 // vectors x 8 token blocks, so the 16-byte LDS writes of a phase hit 16
 // distinct bank groups. Returns (cv, tbi) for block index i of a tile with
@@ -253,11 +257,11 @@ SSD_DEV void x_load(XRaw<CONV>& r, const bf16* __restrict__ src, int64_t ts, int
 // x - fp16(x) to lo + j*ld (channel row j, the 4 tokens contiguous: the
 // MFMA operand layout [p][s]). Rows past nvalid are zero.
 template <bool CONV, bool LO>
-SSD_DEV void x_store(XRaw<CONV>& r, int tseq, int nvalid, const Src& s, int ch,
+SSD_DEV void x_store(XRaw<CONV>& r, const ConvW<CONV>& cw, int tseq, int nvalid,
                      const bf16* cin_b, const float* scale, f16* hi, f16* lo, int ld) {
   rows_mask_head<CONV, 4>(r.v, tseq, cin_b);
   float v[4][8];
-  conv_tile<CONV, 4>(r.v, s, ch, v);
+  conv_tile<CONV, 4>(r.v, cw, v);
   if (scale) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -335,17 +339,22 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr[2];
+  ConvW<CONV> cwx;  // weights of the next x item to be staged
   {
     int cv, tbi;
     tmap(tid, cv, tbi);  // 16 channel vectors x 16 token blocks, one per thread
     const int n0 = cv * 8, tseq = t0 + tbi * 8, ch = s.HP + g * N + n0;
+    // weights before rows (see ConvW)
+    ConvW<CONV> cwb;
+    convw_load<CONV>(cwb, s, ch);
+    convw_load<CONV>(cwx, s, hg0 * P + xp0);
     Rows8<CONV> rb;
     rows_load<CONV, 8>(rb, bb + g * N + n0, s.bs, tseq, L - 1, s, ch, cin_b);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       x_load<CONV>(xr[k], xb + (hg0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
                    (hg0 + k) * P + xp0, cin_b);
-    conv_store<CONV, true>(rb, tseq, min(8, max(0, len - tbi * 8)), s, ch, cin_b,
+    conv_store<CONV, true>(rb, cwb, tseq, min(8, max(0, len - tbi * 8)), cin_b,
                            BT + n0 * RS + tbi * 8, RS);
   }
   cumsum(hg0, dr0, dr1, wv[0]);
@@ -356,7 +365,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   // cache line
   const int nt0 = 4 * (wave & 1), pt0 = 2 * (wave >> 1);
 
-  x_store<CONV, false>(xr[0], t0 + xtb * 4, xnv, s, hg0 * P + xp0, cin_b, &wv[0][0][xtb * 4],
+  x_store<CONV, false>(xr[0], cwx, t0 + xtb * 4, xnv, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
   __syncthreads();
 
@@ -367,17 +376,26 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     float(*wnext)[QI] = wv[(j + 1) & 1];
     const int h0 = hg0 + j * HB;
     const bool more = (j + 1) * HB < hpg;
+    // dt of the next block, fetched a block ahead of its cumsum (a load
+    // waited on right away would also wait for this block's stores)
+    bf16 dn0 = {}, dn1 = {};
+    if (more) {
+      dn0 = dt[(row0 + min(tc, len - 1)) * H + h0 + HB + wave];
+      dn1 = dt[(row0 + min(tc + 1, len - 1)) * H + h0 + HB + wave];
+    }
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
       const int k = j * HB + hh;
       const f16* XT = XB + (hh & 1) * (P * RS);
+      // weights of head k + 1 (staged at the end of this head), issued
+      // before the rows of head k + 2
+      if (k + 1 < hpg) convw_load<CONV>(cwx, s, (hg0 + k + 1) * P + xp0);
       if (k + 2 < hpg) {
         const int ch = (hg0 + k + 2) * P + xp0;
         x_load<CONV>(xr[hh & 1], xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
       }
       // next block's decay weights, published by this iteration's barrier
-      if (hh == HB - 2 && more) cumsum(h0 + HB, dt_at(h0 + HB + wave, tc),
-                                       dt_at(h0 + HB + wave, tc + 1), wnext);
+      if (hh == HB - 2 && more) cumsum(h0 + HB, to_f(dn0), to_f(dn1), wnext);
       f32x4 acc[4][2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -407,9 +425,8 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
               make_uint2(pk(acc[j][pi][0], acc[j][pi][1]), pk(acc[j][pi][2], acc[j][pi][3]));
       if (k + 1 < hpg) {
         f16* nx = XB + ((hh + 1) & 1) * (P * RS);
-        const int ch = (hg0 + k + 1) * P + xp0;
         const float* sc = hh + 1 < HB ? &wcur[hh + 1][xtb * 4] : &wnext[0][xtb * 4];
-        x_store<CONV, false>(xr[(hh + 1) & 1], t0 + xtb * 4, xnv, s, ch, cin_b, sc,
+        x_store<CONV, false>(xr[(hh + 1) & 1], cwx, t0 + xtb * 4, xnv, cin_b, sc,
                              nx + xp0 * RS + xtb * 4, nullptr, RS);
       }
       __syncthreads();
@@ -503,6 +520,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
   __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then states, then x buffers, then Ot
   __shared__ float lam[HB][QI], dts[HB][QI], csd[HB][QI];
+  // conv weights ([channel][tap]) and bias of the block's HB * P x channels
+  constexpr int kXW = CONV ? HB * P * W / 8 : 1, kXB = CONV ? HB * P / 8 : 1;
+  __shared__ __align__(16) u32x4 XWl[kXW], XBl[kXB];
   f16* Bs = U;
   f16* Cs = U + QI * NS;
   f16* Sl = U;  // [head][p][NS]: S_in
@@ -530,6 +550,22 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const bf16* xb = s.x + (int64_t)b * L * s.xs;
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr;
+  // this thread's piece of the block's x conv weights / bias, for XWl / XBl
+  u32x4 xwp = {0u, 0u, 0u, 0u};
+  if constexpr (CONV) {
+    if (tid < kXW)
+      xwp = reinterpret_cast<const u32x4*>(s.cw + (int64_t)h0 * P * W)[tid];
+    else if (tid < kXW + kXB && s.cbias)
+      xwp = reinterpret_cast<const u32x4*>(s.cbias + h0 * P)[tid - kXW];
+  }
+  // conv weights of an x item (local channel lch) from LDS
+  auto xw_get = [&](ConvW<CONV>& cw, int lch) {
+    if constexpr (CONV) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cw.w[q] = XWl[lch * W / 8 + q];
+      cw.b = XBl[lch / 8];
+    }
+  };
   // B and C, natural layout [t][n]: 16 channel vectors x 16 token blocks
   // each; the rows of both are loaded before either is converted.
   {
@@ -537,12 +573,20 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     const int tseq = t0 + tbi * 8, nv = min(8, max(0, len - tbi * 8));
     const int64_t boff = (int64_t)b * L * s.bs + g * N + n0;
     const int chb = s.HP + g * N + n0, chc = chb + s.GN;
+    // weights before rows (see ConvW)
+    ConvW<CONV> cwb, cwc;
+    convw_load<CONV>(cwb, s, chb);
+    convw_load<CONV>(cwc, s, chc);
     Rows8<CONV> rb, rc;
     rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
     rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
     x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
-    conv_store<CONV, false>(rb, tseq, nv, s, chb, cin_b, Bs + (tbi * 8) * NS + n0, NS);
-    conv_store<CONV, false>(rc, tseq, nv, s, chc, cin_b, Cs + (tbi * 8) * NS + n0, NS);
+    conv_store<CONV, false>(rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS);
+    conv_store<CONV, false>(rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS);
+    if constexpr (CONV) {
+      if (tid < kXW) XWl[tid] = xwp;
+      else if (tid < kXW + kXB) XBl[tid - kXW] = xwp;
+    }
   }
   // Lam (inclusive cumsum of dt A), dt, and csd[s] = exp(Lam_ref - Lam_s) dt_s
   // with Lam_ref the value at the end of s's 32-position block (<= Lam_s).
@@ -630,8 +674,12 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
   __syncthreads();  // states no longer read: the x buffers follow
 
-  x_store<CONV, true>(xr, t0 + xtb * 4, xnv, s, h0 * P + xp0, cin_b, nullptr,
-                      U + xp0 * RS + xtb * 4, U + P * RS + xp0 * RS + xtb * 4, RS);
+  {
+    ConvW<CONV> cwx;
+    xw_get(cwx, xp0);
+    x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, U + xp0 * RS + xtb * 4,
+                        U + P * RS + xp0 * RS + xtb * 4, RS);
+  }
   __syncthreads();
 
   // epilogue mapping: 32 consecutive threads take one row (8 channels each),
@@ -786,8 +834,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     }
     if (hh + 1 < HB) {
       f16* nx = U + ((hh + 1) & 1) * (2 * P * RS);
-      const int ch = (h0 + hh + 1) * P + xp0;
-      x_store<CONV, true>(xr, t0 + xtb * 4, xnv, s, ch, cin_b, nullptr, nx + xp0 * RS + xtb * 4,
+      ConvW<CONV> cwx;
+      xw_get(cwx, (hh + 1) * P + xp0);
+      x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, nx + xp0 * RS + xtb * 4,
                           nx + P * RS + xp0 * RS + xtb * 4, RS);
     }
     __syncthreads();
