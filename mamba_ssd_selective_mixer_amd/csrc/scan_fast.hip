@@ -767,38 +767,24 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
             for (int j = 0; j < 8; ++j) dj[j] = rf * cs[j];
           } else {
             // the block holding the diagonal 16 x 16 tile: for odd rt its
-            // first 16 positions all precede the row tile (no mask) and the
-            // tile is its second half; for even rt the tile is its first
-            // half and the second half lies after every t (zero). In the
-            // tile, s <= t is r4 + r <= rr. Masked positions give exp2 of a
-            // positive argument (possibly inf); the select drops it.
-            const int sd = (rt & 1) ? s0 + 16 : s0;
-            const float4 ld = *reinterpret_cast<const float4*>(&lam[hh][sd]);
-            const float4 dd = *reinterpret_cast<const float4*>(&dts[hh][sd]);
-            const float lsd[4] = {ld.x, ld.y, ld.z, ld.w};
-            const float dsd[4] = {dd.x, dd.y, dd.z, dd.w};
-            float md[4];
+            // first 16 positions all precede the row tile and the tile is its
+            // second half; for even rt the tile is its first half and the
+            // second half lies after every t. In the tile, s <= t is
+            // r4 + r <= rr. Positions with s > t get exponent -inf (exactly
+            // 0, no select after a possibly infinite exp2).
+            const bool odd = rt & 1;
+            const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
+            const float4 l1 = *reinterpret_cast<const float4*>(&lam[hh][s0 + 16]);
+            const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][s0]);
+            const float4 d1 = *reinterpret_cast<const float4*>(&dts[hh][s0 + 16]);
+            const float ls[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            const float ds[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            constexpr float kNegInf = -__builtin_huge_valf();
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float m = fexp2(lt - lsd[r]) * dsd[r];
-              md[r] = dmask[r] ? m : 0.f;
-            }
-            if (rt & 1) {
-              const float4 l0 = *reinterpret_cast<const float4*>(&lam[hh][s0]);
-              const float4 d0 = *reinterpret_cast<const float4*>(&dts[hh][s0]);
-              const float ls[4] = {l0.x, l0.y, l0.z, l0.w};
-              const float ds[4] = {d0.x, d0.y, d0.z, d0.w};
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                dj[r] = fexp2(lt - ls[r]) * ds[r];
-                dj[4 + r] = md[r];
-              }
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                dj[r] = md[r];
-                dj[4 + r] = 0.f;
-              }
+              const bool on0 = odd || dmask[r], on1 = odd && dmask[r];
+              dj[r] = fexp2(on0 ? lt - ls[r] : kNegInf) * ds[r];
+              dj[4 + r] = fexp2(on1 ? lt - ls[4 + r] : kNegInf) * ds[4 + r];
             }
           }
           const uint32_t gw[4] = {g0.x, g0.y, g1.x, g1.y};
