@@ -289,8 +289,9 @@ SSD_DEV void x_store(XRaw<CONV>& r, const ConvW<CONV>& cw, int tseq, int nvalid,
 // ---------------------------------------------------------------- phase 1
 // dS_h [P x N] = sum_s x_s w_s (outer) B_s, w_s = exp(Lam_end - Lam_s) dt_s,
 // for every head of the group, computed transposed (dS_h^T = B^T X'), so
-// each lane holds 4 consecutive n of one p and stores them as 8 bytes (a
-// wave's four stores per row cover one whole 128-byte line). B^T is staged
+// each lane holds 4 consecutive n of one p; pairs of lanes trade halves
+// and store 16 bytes each (a wave's stores per row cover one whole 128-byte
+// line). B^T is staged
 // once (conv) for the group; x of one head at a time goes through two LDS
 // buffers, the rows of later heads loaded two heads ahead.
 template <bool CONV>
@@ -417,12 +418,26 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
       }
       // lane: n = (nt0 + j) * 16 + r4 + r, p = (pt0 + pi) * 16 + rr
       f16* o = states + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
+      // lanes q4 = 2m, 2m + 1 (16 apart) trade halves (an LDS-crossbar lane
+      // swap, lane ^ 16) so each stores 16 bytes: the even one n-tile 2 jp,
+      // the odd one n-tile 2 jp + 1. A store instruction then writes 64-byte
+      // pieces of 16 rows instead of 32-byte ones.
+      const bool evq = (q4 & 1) == 0;
 #pragma unroll
       for (int pi = 0; pi < 2; ++pi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint2*>(o + ((pt0 + pi) * 16 + rr) * N + (nt0 + j) * 16 + r4) =
-              make_uint2(pk(acc[j][pi][0], acc[j][pi][1]), pk(acc[j][pi][2], acc[j][pi][3]));
+        for (int jp = 0; jp < 2; ++jp) {
+          const int ja = 2 * jp, jb = ja + 1;
+          const uint32_t a0 = pk(acc[ja][pi][0], acc[ja][pi][1]);
+          const uint32_t a1 = pk(acc[ja][pi][2], acc[ja][pi][3]);
+          const uint32_t b0 = pk(acc[jb][pi][0], acc[jb][pi][1]);
+          const uint32_t b1 = pk(acc[jb][pi][2], acc[jb][pi][3]);
+          const uint32_t r0 = __builtin_amdgcn_ds_swizzle(evq ? b0 : a0, 0x401F);
+          const uint32_t r1 = __builtin_amdgcn_ds_swizzle(evq ? b1 : a1, 0x401F);
+          const u32x4 w = evq ? u32x4{a0, a1, r0, r1} : u32x4{r0, r1, b0, b1};
+          const int n0 = evq ? (nt0 + ja) * 16 + r4 : (nt0 + jb) * 16 + r4 - 4;
+          *reinterpret_cast<u32x4*>(o + ((pt0 + pi) * 16 + rr) * N + n0) = w;
+        }
       if (k + 1 < hpg) {
         f16* nx = XB + ((hh + 1) & 1) * (P * RS);
         const float* sc = hh + 1 < HB ? &wcur[hh + 1][xtb * 4] : &wnext[0][xtb * 4];
