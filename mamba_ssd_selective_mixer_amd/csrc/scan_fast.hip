@@ -335,9 +335,11 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const bf16* xb = s.x + (int64_t)b * L * s.xs;
   const bf16* bb = s.b + (int64_t)b * L * s.bs;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
-  // of 4 tokens. The rows of the group's heads 0 and 1 are loaded together
-  // with those of B; later heads are loaded two heads ahead.
-  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
+  // of 4 tokens, 8 consecutive lanes on the 8 vectors of one block, so each
+  // row load instruction reads whole 128-byte lines of 8 rows. The rows of
+  // the group's heads 0 and 1 are loaded together with those of B; later
+  // heads are loaded two heads ahead.
+  const int xtb = tid >> 3, xcv = tid & 7, xp0 = xcv * 8;
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr[2];
   ConvW<CONV> cwx;  // weights of the next x item to be staged
@@ -559,9 +561,10 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 
   const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
-  // of 4 tokens; within 64 lanes, 2 vectors x 32 blocks. The rows of head 0
-  // are loaded with those of B and C.
-  const int xtb = (tid >> 1) & 31, xcv = (tid & 1) | ((tid >> 6) << 1), xp0 = xcv * 8;
+  // of 4 tokens, 8 consecutive lanes on the 8 vectors of one block (whole
+  // 128-byte lines per row load). The rows of head 0 are loaded with those
+  // of B and C.
+  const int xtb = tid >> 3, xcv = tid & 7, xp0 = xcv * 8;
   const bf16* xb = s.x + (int64_t)b * L * s.xs;
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr;
