@@ -107,7 +107,7 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   w.fast = use_fast(d, conv);
   size_t o_states = 0, o_lam = 0, o_y = 0, o_conv = 0, o_fast = 0;
   if (w.fast) {
-    o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads));
+    o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads, d->ngroups, conv));
   } else {
     o_states = take(B * nc * H * P * N * 4);
     o_lam = take(B * H * nc * 4);

@@ -65,10 +65,10 @@ struct FastScanArgs {
   float* s_out;
   void* y;            // [B, L, H*P] bf16 (norm groups wider than 4 heads: y, then
                       // normalised in place)
-  void* ws;           // fast_ws_bytes(B, L, H) bytes, 256-byte aligned
+  void* ws;           // fast_ws_bytes(B, L, H, G, conv) bytes, 256-byte aligned
 };
 bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
-size_t fast_ws_bytes(int B, int L, int H);
+size_t fast_ws_bytes(int B, int L, int H, int G, bool conv);
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st);
 
 }  // namespace ssd

@@ -200,7 +200,9 @@ SSD_DEV void rows_mask_head(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], int tseq, cons
 // Stage 8 tokens x 8 channels of conv+SiLU output (or of the plain input
 // when !CONV) into LDS as fp16: TRANS=false writes row i (token) at
 // dst + i*ld as one 16-byte vector; TRANS=true writes row j (channel) at
-// dst + j*ld with the 8 tokens contiguous. Rows past nvalid are zero.
+// dst + j*ld with the 8 tokens contiguous. Rows past nvalid are zero. With
+// gdst, rows i < nvalid also go to global memory at gdst + i*gld (16 bytes
+// each); without dst, only there.
 // src: the channel vector's element at token 0 of this batch; tseq: sequence
 // position of the first token; Lm1: last token of the sequence; ch: absolute
 // xBC channel (conv weights); cin_b: conv state of this batch or null.
@@ -208,7 +210,8 @@ template <bool CONV>
 using Rows8 = u32x4[8 + (CONV ? W - 1 : 0)];
 template <bool CONV, bool TRANS>
 SSD_DEV void conv_store(Rows8<CONV>& raw, const ConvW<CONV>& cw, int tseq, int nvalid,
-                        const bf16* cin_b, f16* dst, int ld) {
+                        const bf16* cin_b, f16* dst, int ld, f16* gdst = nullptr,
+                        int64_t gld = 0) {
   rows_mask_head<CONV, 8>(raw, tseq, cin_b);
   float v[8][8];
   conv_tile<CONV, 8>(raw, cw, v);
@@ -218,6 +221,14 @@ SSD_DEV void conv_store(Rows8<CONV>& raw, const ConvW<CONV>& cw, int tseq, int n
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : 0.f;
   }
+  if (gdst) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nvalid)
+        *reinterpret_cast<u32x4*>(gdst + i * gld) = u32x4{
+            pk(v[i][0], v[i][1]), pk(v[i][2], v[i][3]), pk(v[i][4], v[i][5]), pk(v[i][6], v[i][7])};
+  }
+  if (!dst) return;
   if (TRANS) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -230,15 +241,6 @@ SSD_DEV void conv_store(Rows8<CONV>& raw, const ConvW<CONV>& cw, int tseq, int n
                                                       pk(v[i][4], v[i][5]), pk(v[i][6], v[i][7])};
   }
 }
-// x-channel block mapping for transposed staging: within 16 lanes, 2 channel
-// vectors x 8 token blocks, so the 16-byte LDS writes of a phase hit 16
-// distinct bank groups. Returns (cv, tbi) for block index i of a tile with
-// ncv channel vectors and QI/8 = 16 token blocks.
-SSD_DEV void tmap(int i, int& cv, int& tbi) {
-  tbi = (i >> 1) & 15;
-  cv = (i & 1) | ((i >> 5) << 1);
-}
-
 // Raw rows of one x staging item: 4 tokens (+ W-1 halo when CONV) of one
 // 8-channel vector, loaded ahead of their use.
 template <bool CONV>
@@ -286,6 +288,15 @@ SSD_DEV void x_store(XRaw<CONV>& r, const ConvW<CONV>& cw, int tseq, int nvalid,
   }
 }
 
+// B-channel block mapping for transposed staging: within 16 lanes, 2 channel
+// vectors x 8 token blocks, so the 16-byte LDS writes of a phase hit 16
+// distinct bank groups. Returns (cv, tbi) for block index i of a tile with
+// 16 channel vectors and QI/8 = 16 token blocks.
+SSD_DEV void tmap(int i, int& cv, int& tbi) {
+  tbi = (i >> 1) & 15;
+  cv = (i & 1) | ((i >> 5) << 1);
+}
+
 // ---------------------------------------------------------------- phase 1
 // dS_h [P x N] = sum_s x_s w_s (outer) B_s, w_s = exp(Lam_end - Lam_s) dt_s,
 // for every head of the group, computed transposed (dS_h^T = B^T X'), so
@@ -294,12 +305,13 @@ SSD_DEV void x_store(XRaw<CONV>& r, const ConvW<CONV>& cw, int tseq, int nvalid,
 // line). B^T is staged
 // once (conv) for the group; x of one head at a time goes through two LDS
 // buffers, the rows of later heads loaded two heads ahead.
-template <bool CONV>
+template <bool CONV, bool PRE>
 __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict__ dt,
                                                const float* __restrict__ A,
                                                f16* __restrict__ states,
-                                               float* __restrict__ lam_end, int L, int H, int G,
-                                               int nc) {
+                                               float* __restrict__ lam_end,
+                                               f16* __restrict__ bcv, f16* __restrict__ ccv,
+                                               int L, int H, int G, int nc) {
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
@@ -343,10 +355,22 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr[2];
   ConvW<CONV> cwx;  // weights of the next x item to be staged
+  // B item of this thread (16 channel vectors x 16 blocks of 8 tokens): with
+  // PRE, 16 lanes on the 16 vectors of a row, so the rows kept for the
+  // output kernel are stored as whole 256-byte pieces; otherwise the mapping
+  // whose transposed LDS writes are conflict-free
+  int cv, tbi;
+  if constexpr (PRE) {
+    cv = tid & 15;
+    tbi = tid >> 4;
+  } else {
+    tmap(tid, cv, tbi);
+  }
+  const int n0 = cv * 8, tseq = t0 + tbi * 8;
+  const int nvb = min(8, max(0, len - tbi * 8));
+  const int64_t grow = (row0 + tbi * 8) * s.GN + g * N + n0;  // its row in bcv / ccv
   {
-    int cv, tbi;
-    tmap(tid, cv, tbi);  // 16 channel vectors x 16 token blocks, one per thread
-    const int n0 = cv * 8, tseq = t0 + tbi * 8, ch = s.HP + g * N + n0;
+    const int ch = s.HP + g * N + n0;
     // weights before rows (see ConvW)
     ConvW<CONV> cwb;
     convw_load<CONV>(cwb, s, ch);
@@ -357,8 +381,20 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     for (int k = 0; k < 2; ++k)
       x_load<CONV>(xr[k], xb + (hg0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
                    (hg0 + k) * P + xp0, cin_b);
-    conv_store<CONV, true>(rb, cwb, tseq, min(8, max(0, len - tbi * 8)), cin_b,
-                           BT + n0 * RS + tbi * 8, RS);
+    // with PRE, conv'd B also kept (natural layout) for the output kernel
+    conv_store<CONV, true>(rb, cwb, tseq, nvb, cin_b, BT + n0 * RS + tbi * 8, RS,
+                           PRE ? bcv + grow : nullptr, s.GN);
+  }
+  // with PRE, conv'd C too for the output kernel (a group spans several of
+  // its 4-head blocks, each of which would otherwise redo the B and C conv):
+  // rows fetched now, converted after head 0 is staged
+  Rows8<CONV> rc;
+  ConvW<CONV> cwc;
+  if constexpr (PRE) {
+    const int ch = s.HP + s.GN + g * N + n0;
+    convw_load<CONV>(cwc, s, ch);
+    rows_load<CONV, 8>(rc, s.c + (int64_t)b * L * s.bs + g * N + n0, s.bs, tseq, L - 1, s, ch,
+                       cin_b);
   }
   cumsum(hg0, dr0, dr1, wv[0]);
   __syncthreads();
@@ -370,6 +406,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 
   x_store<CONV, false>(xr[0], cwx, t0 + xtb * 4, xnv, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
+  if constexpr (PRE) conv_store<CONV, false>(rc, cwc, tseq, nvb, cin_b, nullptr, 0, ccv + grow, s.GN);
   __syncthreads();
 
   // heads of the group in blocks of HB; head k = j HB + hh (even HB keeps
@@ -523,11 +560,13 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 // current head is computed -> y through an LDS tile to a coalesced epilogue
 // that gates with z (prefetched), normalises each row over its 256 channels
 // and stores 16-byte vectors.
-template <bool CONV, bool NORM>
+template <bool CONV, bool NORM, bool PREC>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
                                                 const float* __restrict__ D,
                                                 const f16* __restrict__ sin_h,
+                                                const f16* __restrict__ bcv,
+                                                const f16* __restrict__ ccv,
                                                 const bf16* __restrict__ z,
                                                 const bf16* __restrict__ nw, float eps,
                                                 bf16* __restrict__ out, int L, int H, int G,
@@ -585,22 +624,44 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     }
   };
   // B and C, natural layout [t][n]: 16 channel vectors x 16 token blocks
-  // each; the rows of both are loaded before either is converted.
+  // each; the rows of both are loaded before either is converted. With PREC
+  // both come already convolved, in fp16, from the chunk-state kernel.
   {
     const int cv = tid & 15, tbi = tid >> 4, n0 = cv * 8;
     const int tseq = t0 + tbi * 8, nv = min(8, max(0, len - tbi * 8));
     const int64_t boff = (int64_t)b * L * s.bs + g * N + n0;
     const int chb = s.HP + g * N + n0, chc = chb + s.GN;
-    // weights before rows (see ConvW)
-    ConvW<CONV> cwb, cwc;
-    convw_load<CONV>(cwb, s, chb);
-    convw_load<CONV>(cwc, s, chc);
-    Rows8<CONV> rb, rc;
-    rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
-    rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
-    x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
-    conv_store<CONV, false>(rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS);
-    conv_store<CONV, false>(rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS);
+    // rows of the precomputed buffers, clamped into the sequence
+    auto pre_rows = [&](const f16* src, u32x4 (&v)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const u32x4*>(
+            src + ((int64_t)b * L + min(tseq + i, L - 1)) * s.GN + g * N + n0);
+    };
+    auto pre_put = [&](const u32x4 (&v)[8], f16* dst) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(dst + i * NS) = i < nv ? v[i] : u32x4{0u, 0u, 0u, 0u};
+    };
+    if constexpr (PREC) {
+      u32x4 vb[8], vc[8];
+      pre_rows(bcv, vb);
+      pre_rows(ccv, vc);
+      x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
+      pre_put(vb, Bs + (tbi * 8) * NS + n0);
+      pre_put(vc, Cs + (tbi * 8) * NS + n0);
+    } else {
+      // weights before rows (see ConvW)
+      ConvW<CONV> cwb, cwc;
+      convw_load<CONV>(cwb, s, chb);
+      convw_load<CONV>(cwc, s, chc);
+      Rows8<CONV> rb, rc;
+      rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
+      rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
+      x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
+      conv_store<CONV, false>(rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS);
+      conv_store<CONV, false>(rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS);
+    }
     if constexpr (CONV) {
       if (tid < kXW) XWl[tid] = xwp;
       else if (tid < kXW + kXB) XBl[tid - kXW] = xwp;
@@ -921,10 +982,19 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
          (!conv || W == fast::W);
 }
 
-size_t fast_ws_bytes(int B, int L, int H) {
+// Workspace: chunk-state increments and carried-in states (fp16), Lam_end,
+// and, with the conv when a group spans several 4-head blocks, the
+// convolved B and C rows in fp16 for the output kernel.
+namespace {
+size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
+bool pre_c(int H, int G, bool conv) { return conv && H / G > fast::HB; }
+}  // namespace
+size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
   const size_t nc = (L + fast::QI - 1) / fast::QI;
   const size_t PN = fast::P * fast::N;
-  return (size_t)B * nc * H * PN * (2 + 2) + (size_t)B * H * nc * 4 + 3 * 256;
+  const size_t rows = (size_t)B * L * G * fast::N * 2;
+  return 2 * ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4) +
+         (pre_c(H, G, conv) ? 2 * ws_round(rows) : 0);
 }
 
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
@@ -933,10 +1003,15 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   const size_t PN = P * N;
   unsigned char* w = (unsigned char*)a.ws;
   fast::f16* dS = (fast::f16*)w;
-  w += ((size_t)a.B * nc * a.H * PN * 2 + 255) / 256 * 256;
+  w += ws_round((size_t)a.B * nc * a.H * PN * 2);
   fast::f16* sinb = (fast::f16*)w;
-  w += ((size_t)a.B * nc * a.H * PN * 2 + 255) / 256 * 256;
+  w += ws_round((size_t)a.B * nc * a.H * PN * 2);
   float* lam_end = (float*)w;
+  w += ws_round((size_t)a.B * a.H * nc * 4);
+  const size_t rows = (size_t)a.B * a.L * a.G * N * 2;
+  const bool prec = pre_c(a.H, a.G, a.conv);
+  fast::f16* bcv = prec ? (fast::f16*)w : nullptr;
+  fast::f16* ccv = prec ? (fast::f16*)(w + ws_round(rows)) : nullptr;
 
   Src s;
   s.x = (const bf16*)a.x;
@@ -956,12 +1031,15 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   // one workgroup per (chunk, batch, group): B staged once for the group
   ProfScope ps(st, KID_FAST_STATE);
   const dim3 g0(nc, a.B * a.G);
-  if (a.conv)
-    hipLaunchKernelGGL(k_fstate<true>, g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
-                       lam_end, a.L, a.H, a.G, nc);
+  if (prec)
+    hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
+                       dS, lam_end, bcv, ccv, a.L, a.H, a.G, nc);
+  else if (a.conv)
+    hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
+                       dS, lam_end, nullptr, nullptr, a.L, a.H, a.G, nc);
   else
-    hipLaunchKernelGGL(k_fstate<false>, g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, dS,
-                       lam_end, a.L, a.H, a.G, nc);
+    hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
+                       dS, lam_end, nullptr, nullptr, a.L, a.H, a.G, nc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -976,18 +1054,20 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   // fused norm when a norm group is exactly the 4-head block; otherwise y
   // (bf16) goes to the output and the grouped norm runs on it in place.
   const bool fused = a.z && (a.H / a.G) == HB;
-#define SSD_FOUT(CV, NM)                                                                         \
-  hipLaunchKernelGGL((k_fout<CV, NM>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D,      \
-                     sinb, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps, (bf16*)a.y, a.L, a.H, \
-                     a.G, nc)
+#define SSD_FOUT(CV, NM, PC)                                                                  \
+  hipLaunchKernelGGL((k_fout<CV, NM, PC>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D, \
+                     sinb, bcv, ccv, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps,            \
+                     (bf16*)a.y, a.L, a.H, a.G, nc)
   {
   ProfScope ps(st, KID_FAST_OUT);
+  // a fused norm group is one 4-head block, so it never needs precomputed C
   if (a.conv) {
-    if (fused) SSD_FOUT(true, true);
-    else SSD_FOUT(true, false);
+    if (fused) SSD_FOUT(true, true, false);
+    else if (prec) SSD_FOUT(true, false, true);
+    else SSD_FOUT(true, false, false);
   } else {
-    if (fused) SSD_FOUT(false, true);
-    else SSD_FOUT(false, false);
+    if (fused) SSD_FOUT(false, true, false);
+    else SSD_FOUT(false, false, false);
   }
   }
 #undef SSD_FOUT
