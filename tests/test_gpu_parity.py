@@ -326,6 +326,17 @@ def test_prefill_short(ops, name, L):
     prefill_case(ops, small(name, batch=2, seqlen=L), with_state=True)
 
 
+@pytest.mark.parametrize("kw,pieces", [(dict(batch=3, seqlen=200), None),
+                                       (dict(batch=2, seqlen=2), None),
+                                       (dict(batch=2, seqlen=300), [2, 150])])
+def test_prefill_grouped_heads(ops, kw, pieces):
+    """8 heads per group, so the chunk-state kernel writes the convolved B and
+    C rows once for the output kernel's two 4-head blocks: several sequences
+    (per-sequence row indexing), calls shorter than the conv window (conv
+    state rows feed the stored C), and pieces chained through both states."""
+    prefill_case(ops, small("c1", nheads=64, **kw), with_state=True, pieces=pieces)
+
+
 def test_prefill_generic_shapes(ops):
     """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
     prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
