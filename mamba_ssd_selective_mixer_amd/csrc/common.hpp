@@ -62,6 +62,25 @@ SSD_DEV void store8(bf16* p, const float (&v)[8]) {
   *reinterpret_cast<uint4*>(p) = a;
 }
 
+// Streaming (non-temporal) 8-element loads and stores, for data read once or
+// not read back: they do not displace cached lines other kernels reuse.
+typedef unsigned u32x4s __attribute__((ext_vector_type(4)));
+SSD_DEV void load8_stream(const bf16* p, float (&v)[8]) {
+  const u32x4s u = __builtin_nontemporal_load(reinterpret_cast<const u32x4s*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+SSD_DEV void load8_stream(const float* p, float (&v)[8]) { load8(p, v); }
+SSD_DEV void store8_stream(bf16* p, const float (&v)[8]) {
+  const u32x4s u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4s*>(p));
+}
+SSD_DEV void store8_stream(float* p, const float (&v)[8]) { store8(p, v); }
+
 // ---- cross-lane sums, scans and broadcasts -------------------------------
 // Built on DPP row operations (a row is 16 lanes): each step is one VALU
 // instruction reading another lane's register, with no LDS round trip.

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
         if (v < S8) {
           float yv[8], zv[8];
           load8(y + base + v * 8, yv);
-          load8(z + base + v * 8, zv);
+          load8_stream(z + base + v * 8, zv);  // z is read once
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             q[k][i] = yv[i] * silu(zv[i]);
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
           load8(w + (int64_t)j * S + v * 8, wv);
 #pragma unroll
           for (int i = 0; i < 8; ++i) o[i] = q[k][i] * wv[i] * inv;
-          store8(out + base + v * 8, o);
+          store8_stream(out + base + v * 8, o);  // final output, not read back
         }
       }
     }

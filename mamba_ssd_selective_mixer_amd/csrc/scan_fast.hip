@@ -515,7 +515,9 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
       const int c = min(c0 + u, nc - 1);
-      d[u] = *reinterpret_cast<const u32x4*>(dS + (((int64_t)b * nc + c) * H + h) * PN + e);
+      // each increment is read once: a streaming load
+      d[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(dS + (((int64_t)b * nc + c) * H + h) * PN + e));
       al[u] = fexp2(lam_end[bh * nc + c]);  // Lam_end in log2 units
     }
 #pragma unroll
