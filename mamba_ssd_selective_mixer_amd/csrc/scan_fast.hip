@@ -174,7 +174,8 @@ SSD_DEV void conv_tile(const u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const ConvW<C
 // before any is used; addresses are clamped into the sequence (the conv
 // state supplies rows before token 0 when present, else they are zeroed by
 // rows_mask_head), so the loads are not serialised behind per-lane branches.
-template <bool CONV, int T>
+// NTL: streaming loads, for rows no later kernel reads again
+template <bool CONV, int T, bool NTL = false>
 SSD_DEV void rows_load(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const bf16* __restrict__ src,
                        int64_t ts, int tseq, int Lm1, const Src& s, int ch, const bf16* cin_b) {
   constexpr int R = CONV ? W - 1 : 0;
@@ -183,7 +184,10 @@ SSD_DEV void rows_load(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const bf16* __restr
     const int t = tseq - R + i;
     const bf16* p = (CONV && t < 0 && cin_b) ? cin_b + (int64_t)(W - 1 + t) * s.C + ch
                                              : src + (int64_t)min(max(t, 0), Lm1) * ts;
-    raw[i] = *reinterpret_cast<const u32x4*>(p);
+    if constexpr (NTL)
+      raw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else
+      raw[i] = *reinterpret_cast<const u32x4*>(p);
   }
 }
 template <bool CONV, int T>
@@ -248,10 +252,10 @@ struct XRaw {
   u32x4 v[4 + (CONV ? W - 1 : 0)];
 };
 
-template <bool CONV>
+template <bool CONV, bool NTL = false>
 SSD_DEV void x_load(XRaw<CONV>& r, const bf16* __restrict__ src, int64_t ts, int tseq, int Lm1,
                     const Src& s, int ch, const bf16* cin_b) {
-  rows_load<CONV, 4>(r.v, src, ts, tseq, Lm1, s, ch, cin_b);
+  rows_load<CONV, 4, NTL>(r.v, src, ts, tseq, Lm1, s, ch, cin_b);
 }
 
 // conv + SiLU (or the plain input) of a loaded item, times scale[i] for
@@ -604,7 +608,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
   // of 4 tokens, 8 consecutive lanes on the 8 vectors of one block (whole
   // 128-byte lines per row load). The rows of head 0 are loaded with those
-  // of B and C.
+  // of B and C. With PREC the x rows (also read by the chunk-state kernel
+  // before) are streamed: nothing reads them after this kernel.
   const int xtb = tid >> 3, xcv = tid & 7, xp0 = xcv * 8;
   const bf16* xb = s.x + (int64_t)b * L * s.xs;
   const int xnv = min(4, max(0, len - xtb * 4));
@@ -649,7 +654,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       u32x4 vb[8], vc[8];
       pre_rows(bcv, vb);
       pre_rows(ccv, vc);
-      x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
+      x_load<CONV, PREC>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
       pre_put(vb, Bs + (tbi * 8) * NS + n0);
       pre_put(vc, Cs + (tbi * 8) * NS + n0);
     } else {
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       Rows8<CONV> rb, rc;
       rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
       rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
-      x_load<CONV>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
+      x_load<CONV, PREC>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
       conv_store<CONV, false>(rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS);
       conv_store<CONV, false>(rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS);
     }
@@ -701,7 +706,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   {
     const f16* sp = sin_h + (((int64_t)b * nc + c) * H + h0) * (int64_t)(P * N);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sreg[i] = *reinterpret_cast<const f16x8*>(sp + (tid + NT * i) * 8);
+    for (int i = 0; i < 16; ++i)  // read once: streaming loads
+      sreg[i] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(sp + (tid + NT * i) * 8));
   }
   // (B C^T) tiles j <= rt of the wave's two row tiles: lane holds C_t.B_s for
   // t = 16 rt + rr and s = 16 j + 4 q4 + r (fp16, the MFMA operand precision).
@@ -792,7 +798,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     const f16* XL = XT + P * RS;                  // [p][s]: x - fp16(x)
     if (hh + 1 < HB) {
       const int ch = (h0 + hh + 1) * P + xp0;
-      x_load<CONV>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+      x_load<CONV, PREC>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
     } else if (NORM) {
 #pragma unroll
       for (int e = 0; e < ZPF; ++e) z_fetch(e);
