@@ -7,17 +7,21 @@
 // Same block decomposition as the generic kernels ("feat(model): add
 // Nemotron-3 Nano hybrid ..." attribution commit: ssd_minimal_discrete /
 // segsum), blocked in 128-token chunks. Three launches:
-//   1. k_fstate  (chunk, batch x head-block): conv+SiLU of x and B for the
-//      chunk, dS_h = (x w_h)^T B for 4 heads on fp16 MFMA, written fp16.
+//   1. k_fstate  (chunk, batch x group): conv+SiLU of B once and of x per
+//      head, dS_h = (x w_h)^T B for every head of the group on fp16 MFMA,
+//      written fp16; when a group spans several 4-head blocks it also
+//      writes the convolved B and C rows (fp16) for step 3.
 //   2. k_fpass   state passing along chunks in fp32; S_in(k) written as fp16
 //      (the precision the MFMA consumes), final state fp32.
-//   3. k_fout    (chunk, batch x head-block): conv+SiLU of x, B, C; the causal
-//      C B^T computed once and shared by the 4 heads; per head
+//   3. k_fout    (chunk, batch x 4-head block): conv+SiLU of x, B, C (B and
+//      C read convolved when step 1 wrote them); the causal C B^T computed
+//      once and shared by the 4 heads; per head
 //      y = M' x + exp(Lam_t) C S_in^T + D x with M'[t,s] = (C_t.B_s)
 //      exp(Lam_t - Lam_s) dt_s on fp16 MFMA and D x from x kept as an fp16
 //      hi + lo pair (the norm that follows divides by rms(q), so this
 //      largest term of y must not carry operand rounding); then the gated
-//      RMSNorm over the 4 heads (one norm group) and a coalesced store.
+//      RMSNorm when the 4 heads are one norm group, else y for the separate
+//      grouped norm; coalesced stores.
 #include "common.hpp"
 #include "launch.hpp"
 
