@@ -773,8 +773,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
   __syncthreads();
 
-  // epilogue mapping: 32 consecutive threads take one row (8 channels each),
-  // thread rows t = tid / 32 + 8 e; z is fetched during the last head
+  // epilogue mapping: 16 consecutive threads take one row (8 channels from
+  // each 128-channel half), thread rows t = tid / 16 + 16 e; the z of the
+  // first ZPF rows is fetched during the last head
   static_assert(HB * P == 256 && NT == 256, "epilogue mapping");
   const int ev8 = tid & 15, et0 = tid >> 4;
   constexpr int EPI = QI / (NT / 16);  // 8 rows per thread
@@ -1040,26 +1041,26 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
 
   dim3 g1(nc, a.B * (a.H / HB));
   {
-  // one workgroup per (chunk, batch, group): B staged once for the group
-  ProfScope ps(st, KID_FAST_STATE);
-  const dim3 g0(nc, a.B * a.G);
-  if (prec)
-    hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
-                       dS, lam_end, bcv, ccv, a.L, a.H, a.G, nc);
-  else if (a.conv)
-    hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
-                       dS, lam_end, nullptr, nullptr, a.L, a.H, a.G, nc);
-  else
-    hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A,
-                       dS, lam_end, nullptr, nullptr, a.L, a.H, a.G, nc);
+    // one workgroup per (chunk, batch, group): B staged once for the group
+    ProfScope ps(st, KID_FAST_STATE);
+    const dim3 g0(nc, a.B * a.G);
+    const bf16* dt = (const bf16*)a.dt;
+    if (prec)
+      hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
+                         bcv, ccv, a.L, a.H, a.G, nc);
+    else if (a.conv)
+      hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
+                         nullptr, nullptr, a.L, a.H, a.G, nc);
+    else
+      hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
+                         nullptr, nullptr, a.L, a.H, a.G, nc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-  ProfScope ps(st, KID_FAST_PASS);
-  hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
-                     lam_end, a.s_in,
-                     a.s_out, sinb, a.H, nc);
+    ProfScope ps(st, KID_FAST_PASS);
+    hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
+                       lam_end, a.s_in, a.s_out, sinb, a.H, nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1071,16 +1072,16 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
                      sinb, bcv, ccv, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps,            \
                      (bf16*)a.y, a.L, a.H, a.G, nc)
   {
-  ProfScope ps(st, KID_FAST_OUT);
-  // a fused norm group is one 4-head block, so it never needs precomputed C
-  if (a.conv) {
-    if (fused) SSD_FOUT(true, true, false);
-    else if (prec) SSD_FOUT(true, false, true);
-    else SSD_FOUT(true, false, false);
-  } else {
-    if (fused) SSD_FOUT(false, true, false);
-    else SSD_FOUT(false, false, false);
-  }
+    ProfScope ps(st, KID_FAST_OUT);
+    // a fused norm group is one 4-head block, so it never needs precomputed C
+    if (a.conv) {
+      if (fused) SSD_FOUT(true, true, false);
+      else if (prec) SSD_FOUT(true, false, true);
+      else SSD_FOUT(true, false, false);
+    } else {
+      if (fused) SSD_FOUT(false, true, false);
+      else SSD_FOUT(false, false, false);
+    }
   }
 #undef SSD_FOUT
   e = hipGetLastError();
