@@ -67,15 +67,18 @@
  * Precision. State, decay exponents, sums and the norm are fp32. The dense
  * contractions of the chunked scan run on MFMA with fp32 accumulation: with
  * fp32 operands for fp32 I/O; with bf16 operands for bf16 I/O outside the
- * fast path; in the fast path (bf16 I/O,
- * headdim 64, dstate 128, heads per group a multiple of 4, dims->chunk >= 64,
- * conv width 4 when the call includes the conv; the norm is fused when a norm
- * group is exactly 4 heads) with fp16 operands (B, C, x, the decay-masked
- * C B^T, chunk states and carried-in states), with D x taken from x at fp16 hi + lo precision. Such operands must stay within
- * fp16 range (|v| < 65504): activations after SiLU, dt-weighted states of
- * magnitude beyond that are outside the fast path's envelope. In the fast
- * path the chunk length is an internal choice (128 tokens); the result does
- * not depend on dims->chunk beyond rounding.
+ * fast path; in the fast path (bf16 I/O, headdim 64, dstate 128, heads per
+ * group a multiple of 4, dims->chunk >= 64, conv width 4 when the call
+ * includes the conv) with fp16 operands (B, C, x, the decay-masked C B^T,
+ * chunk states and carried-in states), with D x taken from x at fp16 hi + lo
+ * precision. Such operands must stay within fp16 range (|v| < 65504):
+ * activations after SiLU, dt-weighted states of magnitude beyond that are
+ * outside the fast path's envelope. In the fast path the chunk length is an
+ * internal choice (128 tokens); the result does not depend on dims->chunk
+ * beyond rounding. The fast path fuses the gated norm into its chunk-output
+ * kernel, also when a norm group spans several of that kernel's 4-head
+ * blocks: their per-token sums of squares are exchanged through the
+ * workspace.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H

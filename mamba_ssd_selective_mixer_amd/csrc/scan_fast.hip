@@ -20,8 +20,9 @@
 //      exp(Lam_t - Lam_s) dt_s on fp16 MFMA and D x from x kept as an fp16
 //      hi + lo pair (the norm that follows divides by rms(q), so this
 //      largest term of y must not carry operand rounding); then the gated
-//      RMSNorm when the 4 heads are one norm group, else y for the separate
-//      grouped norm; coalesced stores.
+//      RMSNorm, within the block when the 4 heads are one norm group, else
+//      across the group's blocks (per-token sums of q^2 exchanged through
+//      device memory); coalesced stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -414,7 +415,8 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 
   x_store<CONV, false>(xr[0], cwx, t0 + xtb * 4, xnv, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
-  if constexpr (PRE) conv_store<CONV, false>(rc, cwc, tseq, nvb, cin_b, nullptr, 0, ccv + grow, s.GN);
+  if constexpr (PRE)
+    conv_store<CONV, false>(rc, cwc, tseq, nvb, cin_b, nullptr, 0, ccv + grow, s.GN);
   __syncthreads();
 
   // heads of the group in blocks of HB; head k = j HB + hh (even HB keeps
@@ -499,17 +501,29 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 // ---------------------------------------------------------------- phase 2
 // S_in(0) = initial state (or 0); S_in(k+1) = exp(Lam_end,k) S_in(k) + dS_k.
 // One thread carries 8 consecutive (p, n) elements of one (batch, head) in
-// fp32 through all chunks, reading dS_k 8 chunks ahead.
+// fp32 through all chunks, reading dS_k 8 chunks ahead. It also resets the
+// state of the output kernel's cross-block norm (this launch always precedes
+// that one on the stream): the kParts ticket counters to 0 and the npart
+// per-row partial-sum slots to kUnset.
+constexpr int kParts = 8;          // ticket partitions: block index mod 8, one per XCD
+constexpr float kUnset = -1.0f;    // an unwritten slot: never a sum of squares (nor NaN)
 constexpr int kPassDepth = 8;
 constexpr int kPassVec = 8;
 __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
-                                               f16* __restrict__ sin_h, int H, int nc) {
+                                               f16* __restrict__ sin_h, int* sync, float* part,
+                                               int64_t npart, int H, int nc) {
   constexpr int PN = P * N;
   const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * H + h;
+  {
+    const int64_t gt = ((int64_t)(b * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nt = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+    if (sync && gt < kParts) sync[gt] = 0;
+    for (int64_t i = gt; i < npart; i += nt) part[i] = kUnset;
+  }
   float S[kPassVec];
   if (s_in) {
     load8(s_in + bh * PN + e, S);
@@ -550,8 +564,11 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 }
 
 // ---------------------------------------------------------------- phase 3
-// NORM: fuse the gated RMSNorm (the 4 heads are one norm group); else the
-// scan output y is written (bf16).
+// NM selects the epilogue: 0 writes the scan output y (bf16); 1 fuses the
+// gated RMSNorm when the 4 heads are one norm group; 2 fuses it when a norm
+// group spans nb = H/G/4 blocks: each block publishes its per-token sums of
+// q^2 over its 256 channels, gathers its partners' sums, and scales its own
+// rows (no y round trip through HBM).
 //
 // Every product is computed transposed, y^T[p, t], so a lane's accumulator
 // holds 4 consecutive channels p of one token t (the row t = lane % 16 of
@@ -570,7 +587,8 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 // current head is computed -> y through an LDS tile to a coalesced epilogue
 // that gates with z (prefetched), normalises each row over its 256 channels
 // and stores 16-byte vectors.
-template <bool CONV, bool NORM, bool PREC>
+constexpr int kSpinMax = 1 << 20;  // bound on the polls of the partners' sums
+template <bool CONV, int NM, bool PREC>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
                                                 const float* __restrict__ D,
@@ -579,8 +597,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 const f16* __restrict__ ccv,
                                                 const bf16* __restrict__ z,
                                                 const bf16* __restrict__ nw, float eps,
-                                                bf16* __restrict__ out, int L, int H, int G,
-                                                int nc) {
+                                                bf16* __restrict__ out, float* part, int* sync,
+                                                int L, int H, int G, int nc) {
   static_assert(4 * P * RS <= 2 * QI * NS, "two x buffers fit the B/C space");
   static_assert(HB * P * NS == 2 * QI * NS, "the 4 heads' states fill the B/C space");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
@@ -594,8 +612,35 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   f16* Sl = U;  // [head][p][NS]: S_in
   f16* Ot = U;  // [t][4 heads x p]: y
 
-  const int c = blockIdx.x, hpb = H / HB;
-  const int b = blockIdx.y / hpb, h0 = (blockIdx.y % hpb) * HB, g = h0 / (H / G);
+  const int hpb = H / HB;
+  int c, b, h0, tk = 0;
+  if constexpr (NM == 2) {
+    // the tile comes from a ticket taken in arrival order. Blocks whose index
+    // is v mod kParts (those one XCD receives) take tickets from counter v
+    // and serve the norm groups that are v mod kParts, so the blocks of a
+    // group share that XCD's L2 (and their B and C rows); a group's blocks
+    // hold consecutive tickets of their partition, so a workgroup only waits
+    // for partners that have already started, whatever the dispatch order.
+    // When the group count is not a multiple of kParts: one partition.
+    __shared__ int tk_s;
+    const int nb = H / G / HB, nbat = gridDim.y / hpb;
+    const int ngrp = gridDim.x * nbat * G, nparts = ngrp % kParts == 0 ? kParts : 1;
+    const int part_id = (blockIdx.y * gridDim.x + blockIdx.x) % nparts;
+    if (threadIdx.x == 0)
+      tk_s = __hip_atomic_fetch_add(sync + part_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int kloc = __builtin_amdgcn_readfirstlane(tk_s);
+    const int grp = (kloc / nb) * nparts + part_id;
+    tk = grp * nb + kloc % nb;
+    h0 = ((grp % G) * nb + tk % nb) * HB;
+    b = (grp / G) % nbat;
+    c = grp / G / nbat;
+  } else {
+    c = blockIdx.x;
+    b = blockIdx.y / hpb;
+    h0 = (blockIdx.y % hpb) * HB;
+  }
+  const int g = h0 / (H / G);
   const int t0 = c * QI, len = min(QI, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   // the wave index is uniform: read it into a scalar register
@@ -780,7 +825,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const int ev8 = tid & 15, et0 = tid >> 4;
   constexpr int EPI = QI / (NT / 16);  // 8 rows per thread
   constexpr int ZPF = EPI / 2;         // rows whose z is fetched during the last head
-  u32x4 zr[NORM ? 2 * EPI : 1];
+  u32x4 zr[NM ? 2 * EPI : 1];
   auto z_fetch = [&](int e) {
     const int t = et0 + 16 * e;
     // z is read once, here: a streaming load does not displace the x, B
@@ -804,7 +849,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     if (hh + 1 < HB) {
       const int ch = (h0 + hh + 1) * P + xp0;
       x_load<CONV, PREC>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
-    } else if (NORM) {
+    } else if (NM) {
 #pragma unroll
       for (int e = 0; e < ZPF; ++e) z_fetch(e);
     }
@@ -923,12 +968,12 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   // Epilogue: 16 consecutive threads (one DPP row) take one token row, 8
   // channels from each 128-channel half, rows t = tid / 16 + 16 e; the z of
   // the later rows is fetched now, behind the first rows' work
-  if constexpr (NORM) {
+  if constexpr (NM != 0) {
 #pragma unroll
     for (int e = ZPF; e < EPI; ++e) z_fetch(e);
   }
   float wv8[2][8];
-  if (NORM) {
+  if (NM) {
     load8(nw + h0 * P + ev8 * 8, wv8[0]);
     load8(nw + h0 * P + 128 + ev8 * 8, wv8[1]);
   }
@@ -945,13 +990,89 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
   __syncthreads();
 
+  if constexpr (NM == 2) {
+    // q = y silu(z) goes back into Ot (fp16) and each row's sum of q^2 over
+    // this block's 256 channels is published at device scope
+    const int nb = H / G / HB, grp = tk / nb;
+    float* inv_s = &csd[0][0];  // per-row sums, then 1 / rms (csd is free by now)
+#pragma unroll
+    for (int e = 0; e < EPI; ++e) {
+      const int t = et0 + 16 * e;
+      float ss = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f16* op = Ot + t * OS + hf * 128 + ev8 * 8;
+        float yv[8], zv[8];
+        load8h(op, yv);
+        unpack8(zr[2 * e + hf], zv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          yv[j] *= silu(zv[j]);
+          ss += yv[j] * yv[j];
+        }
+        sts16(op, u32x4{pk(yv[0], yv[1]), pk(yv[2], yv[3]), pk(yv[4], yv[5]), pk(yv[6], yv[7])});
+      }
+      ss = group_sum_last<16>(ss);
+      if (ev8 == 0) inv_s[t] = ss;
+    }
+    __syncthreads();
+    // one thread per row publishes this block's sum and gathers the group's:
+    // a slot still holding kUnset (never a sum of squares, not even NaN) has
+    // not been written yet; a wait that runs out poisons the row
+    if (tid < QI) {
+      const int j = tk % nb;
+      const float own = inv_s[tid];
+      __hip_atomic_store(part + (int64_t)tk * QI + tid, own, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      const float* gp = part + (int64_t)grp * nb * QI + tid;
+      float sq = 0.f;
+      bool ok = false;
+      for (int it = 0; it < kSpinMax && !ok; ++it) {
+        sq = 0.f;
+        ok = true;
+#pragma unroll 8
+        for (int k = 0; k < nb; ++k) {
+          const float v = k == j ? own
+                                 : __hip_atomic_load(gp + (int64_t)k * QI, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+          ok = ok && v != kUnset;
+          sq += v;
+        }
+        if (!ok) __builtin_amdgcn_s_sleep(2);
+      }
+      inv_s[tid] = ok ? __builtin_amdgcn_rsqf(sq * (1.0f / (nb * HB * P)) + eps)
+                      : __builtin_nanf("");
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPI; ++e) {
+      const int t = et0 + 16 * e;
+      const float inv = inv_s[t];
+      if (t < len) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          float yv[8];
+          load8h(Ot + t * OS + hf * 128 + ev8 * 8, yv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yv[j] *= wv8[hf][j] * inv;
+          // streaming store: the normalised output is final
+          const u32x4 w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]),
+                           pack_bf16x2(yv[4], yv[5]), pack_bf16x2(yv[6], yv[7])};
+          __builtin_nontemporal_store(
+              w, reinterpret_cast<u32x4*>(out + (row0 + t) * HP + h0 * P + hf * 128 + ev8 * 8));
+        }
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int e = 0; e < EPI; ++e) {
     const int t = et0 + 16 * e;
     float yv[2][8];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) load8h(Ot + t * OS + hf * 128 + ev8 * 8, yv[hf]);
-    if (NORM) {
+    if (NM) {
       float ss = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -973,15 +1094,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     if (t < len) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        bf16* yp = out + (row0 + t) * HP + h0 * P + hf * 128 + ev8 * 8;
-        if constexpr (NORM) {
-          // streaming store: the normalised output is final
-          const u32x4 w = {pack_bf16x2(yv[hf][0], yv[hf][1]), pack_bf16x2(yv[hf][2], yv[hf][3]),
-                           pack_bf16x2(yv[hf][4], yv[hf][5]), pack_bf16x2(yv[hf][6], yv[hf][7])};
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(yp));
-        } else {
-          store8(yp, yv[hf]);  // the separate gated norm reads it back
-        }
+        // streaming store: the (normalised or plain) output is final
+        store8_stream(out + (row0 + t) * HP + h0 * P + hf * 128 + ev8 * 8, yv[hf]);
       }
     }
   }
@@ -995,19 +1109,24 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
          (!conv || W == fast::W);
 }
 
-// Workspace: chunk-state increments and carried-in states (fp16), Lam_end,
-// and, with the conv when a group spans several 4-head blocks, the
+// Workspace: chunk-state increments and carried-in states (fp16), Lam_end;
+// when a group spans several 4-head blocks, the per-row partial sums and
+// the ticket counters of the cross-block norm and, with the conv, the
 // convolved B and C rows in fp16 for the output kernel.
 namespace {
 size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
-bool pre_c(int H, int G, bool conv) { return conv && H / G > fast::HB; }
+bool wide(int H, int G) { return H / G > fast::HB; }
+bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 }  // namespace
 size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
   const size_t nc = (L + fast::QI - 1) / fast::QI;
   const size_t PN = fast::P * fast::N;
   const size_t rows = (size_t)B * L * G * fast::N * 2;
-  return 2 * ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4) +
-         (pre_c(H, G, conv) ? 2 * ws_round(rows) : 0);
+  size_t n = 2 * ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4);
+  if (wide(H, G))
+    n += ws_round(nc * B * (H / fast::HB) * fast::QI * 4) + ws_round(fast::kParts * 4);
+  if (pre_c(H, G, conv)) n += 2 * ws_round(rows);
+  return n;
 }
 
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
@@ -1021,6 +1140,15 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   w += ws_round((size_t)a.B * nc * a.H * PN * 2);
   float* lam_end = (float*)w;
   w += ws_round((size_t)a.B * a.H * nc * 4);
+  float* part = nullptr;
+  int* sync = nullptr;
+  const int64_t npart = (int64_t)nc * a.B * (a.H / HB) * QI;
+  if (wide(a.H, a.G)) {
+    part = (float*)w;
+    w += ws_round(npart * 4);
+    sync = (int*)w;
+    w += ws_round(kParts * 4);
+  }
   const size_t rows = (size_t)a.B * a.L * a.G * N * 2;
   const bool prec = pre_c(a.H, a.G, a.conv);
   fast::f16* bcv = prec ? (fast::f16*)w : nullptr;
@@ -1060,34 +1188,36 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   {
     ProfScope ps(st, KID_FAST_PASS);
     hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
-                       lam_end, a.s_in, a.s_out, sinb, a.H, nc);
+                       lam_end, a.s_in, a.s_out, sinb, sync, part, part ? npart : 0, a.H,
+                       nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // fused norm when a norm group is exactly the 4-head block; otherwise y
-  // (bf16) goes to the output and the grouped norm runs on it in place.
-  const bool fused = a.z && (a.H / a.G) == HB;
+  // gated norm: within the block when a norm group is exactly the 4-head
+  // block, across the group's blocks when it spans several; without z the
+  // scan output y is written
 #define SSD_FOUT(CV, NM, PC)                                                                  \
   hipLaunchKernelGGL((k_fout<CV, NM, PC>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D, \
                      sinb, bcv, ccv, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps,            \
-                     (bf16*)a.y, a.L, a.H, a.G, nc)
+                     (bf16*)a.y, part, sync, a.L, a.H, a.G, nc)
   {
     ProfScope ps(st, KID_FAST_OUT);
-    // a fused norm group is one 4-head block, so it never needs precomputed C
+    const int nm = !a.z ? 0 : wide(a.H, a.G) ? 2 : 1;
+    // precomputed B and C exist exactly when the conv is on and a group spans
+    // several blocks
     if (a.conv) {
-      if (fused) SSD_FOUT(true, true, false);
-      else if (prec) SSD_FOUT(true, false, true);
-      else SSD_FOUT(true, false, false);
+      if (nm == 1) SSD_FOUT(true, 1, false);
+      else if (nm == 2) SSD_FOUT(true, 2, true);
+      else if (prec) SSD_FOUT(true, 0, true);
+      else SSD_FOUT(true, 0, false);
     } else {
-      if (fused) SSD_FOUT(false, true, false);
-      else SSD_FOUT(false, false, false);
+      if (nm == 1) SSD_FOUT(false, 1, false);
+      else if (nm == 2) SSD_FOUT(false, 2, false);
+      else SSD_FOUT(false, 0, false);
     }
   }
 #undef SSD_FOUT
-  e = hipGetLastError();
-  if (e != hipSuccess || !a.z || fused) return e;
-  return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.norm_w, a.eps, a.y,
-                           st);
+  return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -337,6 +337,23 @@ def test_prefill_grouped_heads(ops, kw, pieces):
     prefill_case(ops, small("c1", nheads=64, **kw), with_state=True, pieces=pieces)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(nheads=32, ngroups=1, batch=1, seqlen=300),  # 8 blocks per group; 3 groups: one partition
+    dict(nheads=24, ngroups=2, batch=2, seqlen=200),  # 3 blocks per group; 8 groups: 8 partitions
+    dict(nheads=16, ngroups=2, batch=1, seqlen=260),  # 2 blocks per group; 6 groups, ragged tail
+])
+def test_prefill_norm_across_blocks(ops, kw):
+    """Norm groups wider than the output kernel's 4-head block: each block
+    publishes its per-token sums of squares and gathers its partners', with
+    the tickets split over 8 partitions (group count a multiple of 8) or not."""
+    prefill_case(ops, small("c1", **kw), with_state=True)
+
+
+def test_chunk_scan_norm_across_blocks(ops):
+    """The same exchange in the chunk-scan entry point (no conv), one partition."""
+    scan_case(ops, small("c1", nheads=32, ngroups=1, batch=1, seqlen=300), True, True)
+
+
 def test_prefill_generic_shapes(ops):
     """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
     prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
