@@ -78,7 +78,10 @@
  * beyond rounding. The fast path fuses the gated norm into its chunk-output
  * kernel, also when a norm group spans several of that kernel's 4-head
  * blocks: their per-token sums of squares are exchanged through the
- * workspace.
+ * workspace, which needs the group's blocks to run concurrently (at least
+ * 8 * (H/G/4 - 1) + 1 resident workgroups of 256 threads; a stream with the
+ * whole GPU has 512). A wait that cannot complete writes NaN rows after a
+ * bounded time instead of hanging.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H

@@ -1149,6 +1149,9 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     sync = (int*)w;
     w += ws_round(kParts * 4);
   }
+  // output kernel epilogue: 0 = y, 1 = norm within the block, 2 = norm
+  // across the group's blocks (its state is reset by the pass kernel)
+  const int nm = !a.z ? 0 : wide(a.H, a.G) ? 2 : 1;
   const size_t rows = (size_t)a.B * a.L * a.G * N * 2;
   const bool prec = pre_c(a.H, a.G, a.conv);
   fast::f16* bcv = prec ? (fast::f16*)w : nullptr;
@@ -1188,8 +1191,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   {
     ProfScope ps(st, KID_FAST_PASS);
     hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
-                       lam_end, a.s_in, a.s_out, sinb, sync, part, part ? npart : 0, a.H,
-                       nc);
+                       lam_end, a.s_in, a.s_out, sinb, nm == 2 ? sync : nullptr, part,
+                       nm == 2 ? npart : 0, a.H, nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1202,7 +1205,6 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
                      (bf16*)a.y, part, sync, a.L, a.H, a.G, nc)
   {
     ProfScope ps(st, KID_FAST_OUT);
-    const int nm = !a.z ? 0 : wide(a.H, a.G) ? 2 : 1;
     // precomputed B and C exist exactly when the conv is on and a group spans
     // several blocks
     if (a.conv) {
