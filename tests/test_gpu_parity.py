@@ -389,19 +389,24 @@ def test_causality_gpu(ops):
         assert not np.array_equal(out[:, t], base[:, t])
 
 
-def test_determinism(ops):
-    """Two runs on the same inputs give bit-identical outputs and states."""
+@pytest.mark.parametrize("kw", [dict(batch=2, seqlen=300),
+                                dict(nheads=64, ngroups=2, batch=2, seqlen=300)])
+def test_determinism(ops, kw):
+    """Repeated runs on the same inputs give bit-identical outputs and states;
+    the second shape normalises across 8 blocks per group, whose tickets (and
+    so the order in which partners finish) change from run to run."""
     import torch
-    cfg = small("c1", batch=2, seqlen=300)
+    cfg = small("c1", **kw)
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)
     res = []
-    for _ in range(2):
+    for _ in range(3):
         so = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
         out = ops.ssd_mixer_prefill(d, dev(inp["xbc"], td), dev(inp["z"], td), dev(inp["dt"], td),
                                     dev(prm["A"]), dev(prm["D"]), dev(prm["conv_w"], td), None,
                                     dev(prm["norm_w"], td), prm["eps"], ssm_state_out=so)
         res.append((host(out), host(so)))
-    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    for r in res[1:]:
+        assert np.array_equal(res[0][0], r[0]) and np.array_equal(res[0][1], r[1])
