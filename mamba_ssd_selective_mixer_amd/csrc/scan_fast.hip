@@ -325,7 +325,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
   const int c = blockIdx.x, hpg = H / G;
-  const int b = blockIdx.y / G, g = blockIdx.y % G, hg0 = g * hpg;
+  const int b = blockIdx.z, g = blockIdx.y, hg0 = g * hpg;
   const int t0 = c * QI, len = min(QI, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   // the wave index is uniform: read it into a scalar register
@@ -612,7 +612,6 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   f16* Sl = U;  // [head][p][NS]: S_in
   f16* Ot = U;  // [t][4 heads x p]: y
 
-  const int hpb = H / HB;
   int c, b, h0, tk = 0;
   if constexpr (NM == 2) {
     // the tile comes from a ticket taken in arrival order. Blocks whose index
@@ -623,9 +622,9 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     // for partners that have already started, whatever the dispatch order.
     // When the group count is not a multiple of kParts: one partition.
     __shared__ int tk_s;
-    const int nb = H / G / HB, nbat = gridDim.y / hpb;
+    const int nb = H / G / HB, nbat = gridDim.z;
     const int ngrp = gridDim.x * nbat * G, nparts = ngrp % kParts == 0 ? kParts : 1;
-    const int part_id = (blockIdx.y * gridDim.x + blockIdx.x) % nparts;
+    const int part_id = ((blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) % nparts;
     if (threadIdx.x == 0)
       tk_s = __hip_atomic_fetch_add(sync + part_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -637,8 +636,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     c = grp / G / nbat;
   } else {
     c = blockIdx.x;
-    b = blockIdx.y / hpb;
-    h0 = (blockIdx.y % hpb) * HB;
+    b = blockIdx.z;
+    h0 = blockIdx.y * HB;
   }
   const int g = h0 / (H / G);
   const int t0 = c * QI, len = min(QI, L - t0);
@@ -1170,11 +1169,12 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   s.HP = a.H * P;
   s.GN = a.G * N;
 
-  dim3 g1(nc, a.B * (a.H / HB));
+  // (chunk, 4-head block, batch): the chunk varies fastest in dispatch order
+  const dim3 g1(nc, a.H / HB, a.B);
   {
-    // one workgroup per (chunk, batch, group): B staged once for the group
+    // one workgroup per (chunk, group, batch): B staged once for the group
     ProfScope ps(st, KID_FAST_STATE);
-    const dim3 g0(nc, a.B * a.G);
+    const dim3 g0(nc, a.G, a.B);
     const bf16* dt = (const bf16*)a.dt;
     if (prec)
       hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,

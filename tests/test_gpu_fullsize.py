@@ -155,3 +155,28 @@ def test_decode_loop_full(env):
             check(f"c4 out step {k}", host(y[seqs]), ro, TOLB)
     check("c4 final SSM state", host(ss[seqs]), rss, TOLB)
     assert np.array_equal(host(cs[seqs]), rcs)
+
+
+def test_prefill_many_sequences(env):
+    """Maximum-size edge: the large-layer shape with 1024 short sequences, so
+    batch x 4-head blocks (65 536) exceeds one grid dimension's limit (the
+    kernels put the batch in its own dimension), with the norm spanning 8
+    blocks per group in 8 ticket partitions. Sampled sequences, outputs and
+    final states, against the fp64 oracle on those sequences alone."""
+    torch, ops = env
+    cfg = synth.replace(synth.CONFIGS["c2"], batch=1024, seqlen=5)
+    assert cfg.batch * cfg.nheads // 4 > 65535
+    prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
+    bf = torch.bfloat16
+    so = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
+    out = ops.ssd_mixer_prefill(dims(ops, torch, cfg), dev(inp["xbc"], bf), dev(inp["z"], bf),
+                                dev(inp["dt"], bf), dev(prm["A"]), dev(prm["D"]),
+                                dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"],
+                                ssm_state_out=so)
+    for b in (0, 517, cfg.batch - 1):
+        sl = slice(b, b + 1)
+        ref = oracle.mixer_prefill(inp["xbc"][sl], inp["z"][sl], inp["dt"][sl], prm["A"],
+                                   prm["D"], prm["conv_w"], None, prm["norm_w"], prm["eps"],
+                                   cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate)
+        check(f"out, sequence {b}", host(out[sl]), ref["out"], TOLB)
+        check(f"final state, sequence {b}", host(so[sl]), ref["s_out"], TOLB)
