@@ -63,8 +63,7 @@ struct FastScanArgs {
   float eps;
   const float* s_in;
   float* s_out;
-  void* y;            // [B, L, H*P] bf16 (norm groups wider than 4 heads: y, then
-                      // normalised in place)
+  void* y;            // [B, L, H*P] bf16: the normalised output (z given) or y
   void* ws;           // fast_ws_bytes(B, L, H, G, conv) bytes, 256-byte aligned
 };
 bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
