@@ -76,12 +76,13 @@
  * outside the fast path's envelope. In the fast path the chunk length is an
  * internal choice (128 tokens); the result does not depend on dims->chunk
  * beyond rounding. The fast path fuses the gated norm into its chunk-output
- * kernel, also when a norm group spans several of that kernel's 4-head
- * blocks: their per-token sums of squares are exchanged through the
- * workspace, which needs the group's blocks to run concurrently (at least
- * 8 * (H/G/4 - 1) + 1 resident workgroups of 256 threads; a stream with the
- * whole GPU has 512). A wait that cannot complete writes NaN rows after a
- * bounded time instead of hanging.
+ * kernel, also when a norm group spans several (up to 32) of that kernel's
+ * 4-head blocks: their per-token sums of squares are exchanged through the
+ * workspace, which needs the group's blocks to run concurrently (a stream
+ * with the whole GPU qualifies: 512 resident workgroups, 64 per XCD, against
+ * at most 31 waiting per XCD). A wait that cannot complete writes NaN rows
+ * after a bounded time instead of hanging. Wider norm groups are normalised
+ * by a separate pass over the scan output.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H

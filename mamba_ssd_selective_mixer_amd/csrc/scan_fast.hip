@@ -1093,7 +1093,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     if (t < len) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        // streaming store: the (normalised or plain) output is final
+        // streaming store: the output is final (for norm groups of more than
+        // kMaxNormBlocks blocks the grouped norm streams y back once)
         store8_stream(out + (row0 + t) * HP + h0 * P + hf * 128 + ev8 * 8, yv[hf]);
       }
     }
@@ -1115,6 +1116,11 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
 namespace {
 size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
 bool wide(int H, int G) { return H / G > fast::HB; }
+// Most 4-head blocks per norm group normalised across blocks: a waiting
+// block holds its slot, and up to (blocks - 1) blocks of one group per ticket
+// partition may wait for the rest, so the group must fit well inside one
+// XCD's 64 resident workgroups. Wider groups take y and the grouped norm.
+constexpr int kMaxNormBlocks = 32;
 bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 }  // namespace
 size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
@@ -1149,8 +1155,10 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     w += ws_round(kParts * 4);
   }
   // output kernel epilogue: 0 = y, 1 = norm within the block, 2 = norm
-  // across the group's blocks (its state is reset by the pass kernel)
-  const int nm = !a.z ? 0 : wide(a.H, a.G) ? 2 : 1;
+  // across the group's blocks (its state is reset by the pass kernel); with
+  // more than kMaxNormBlocks blocks per group, y and then the grouped norm
+  const bool norm_after = a.z && a.H / a.G > kMaxNormBlocks * HB;
+  const int nm = !a.z || norm_after ? 0 : wide(a.H, a.G) ? 2 : 1;
   const size_t rows = (size_t)a.B * a.L * a.G * N * 2;
   const bool prec = pre_c(a.H, a.G, a.conv);
   fast::f16* bcv = prec ? (fast::f16*)w : nullptr;
@@ -1219,7 +1227,10 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     }
   }
 #undef SSD_FOUT
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !norm_after) return e;
+  return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.norm_w, a.eps, a.y,
+                           st);
 }
 
 }  // namespace ssd

@@ -341,11 +341,13 @@ def test_prefill_grouped_heads(ops, kw, pieces):
     dict(nheads=32, ngroups=1, batch=1, seqlen=300),  # 8 blocks per group; 3 groups: one partition
     dict(nheads=24, ngroups=2, batch=2, seqlen=200),  # 3 blocks per group; 8 groups: 8 partitions
     dict(nheads=16, ngroups=2, batch=1, seqlen=260),  # 2 blocks per group; 6 groups, ragged tail
+    dict(nheads=144, ngroups=1, batch=1, seqlen=130),  # 36 blocks: y, then the grouped norm
 ])
 def test_prefill_norm_across_blocks(ops, kw):
     """Norm groups wider than the output kernel's 4-head block: each block
     publishes its per-token sums of squares and gathers its partners', with
-    the tickets split over 8 partitions (group count a multiple of 8) or not."""
+    the tickets split over 8 partitions (group count a multiple of 8) or not;
+    beyond 32 blocks per group the norm runs after the scan instead."""
     prefill_case(ops, small("c1", **kw), with_state=True)
 
 
