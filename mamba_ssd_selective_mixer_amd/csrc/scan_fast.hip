@@ -629,6 +629,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       tk_s = __hip_atomic_fetch_add(sync + part_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int kloc = __builtin_amdgcn_readfirstlane(tk_s);
+    // norm group grp = (chunk * batches + batch) * G + group; its j-th block
+    // (heads of block j of the group) holds slot tk = grp * nb + j
     const int grp = (kloc / nb) * nparts + part_id;
     tk = grp * nb + kloc % nb;
     h0 = ((grp % G) * nb + tk % nb) * HB;
