@@ -121,6 +121,20 @@ def test_workspace_sizes(lib):
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(bad)) == 0
 
 
+def test_workspace_covers_wide_norm_groups(lib):
+    """Large-layer shape (32 heads per norm group): the prefill workspace holds
+    the fp16 chunk increments and carried-in states, the convolved B and C
+    rows the output kernel reads, and the per-row sums its blocks exchange."""
+    c2 = synth.CONFIGS["c2"]
+    d = dims(c2)
+    ws = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
+    nc = -(-c2.seqlen // 128)
+    states = 2 * c2.batch * nc * c2.nheads * c2.headdim * c2.dstate * 2
+    rows = 2 * c2.batch * c2.seqlen * c2.ngroups * c2.dstate * 2
+    sums = nc * c2.batch * (c2.nheads // 4) * 128 * 4
+    assert ws >= states + rows + sums
+
+
 def test_state_slot_size_matches_page_figure(lib):
     """A sequence slot of Nemotron 3 Nano (23 Mamba-2 layers of 64 x 64 heads)
     holds 47.6 MiB of fp32 recurrent state (tests/golden/nano_recurrent_state.json)."""
