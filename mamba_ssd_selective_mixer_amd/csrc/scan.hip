@@ -225,10 +225,12 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
         const bool scol_ok = scol < len;
         f32x4 gacc = zero4();
         for (int k = 0; k < N; k += M::KSTEP) {
+          // a lane's k-slice past N (N = 16 under a 32-deep bf16 MFMA) is zero
+          const bool kin = k + kk < N;
           typename M::frag fa, fb;
-          if (trow_ok) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          if (trow_ok && kin) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
           else fa = typename M::frag{};
-          if (scol_ok) fb = M::ld(Bg + (row0 + scol) * bs + k + kk);
+          if (scol_ok && kin) fb = M::ld(Bg + (row0 + scol) * bs + k + kk);
           else fb = typename M::frag{};
           gacc = M::mma(fa, fb, gacc);
         }
@@ -252,10 +254,13 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
         for (int k = 0; k < nsr; k += M::KSTEP) acc = M::mma(M::ld(mp + k), M::ld(xp + k), acc);
         const float* sp = Sin + (int64_t)(pt * 16 + rr) * N + kk;
         for (int k = 0; k < N; k += M::KSTEP) {
-          typename M::frag fa;
-          if (trow_ok) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          const bool kin = k + kk < N;
+          typename M::frag fa, fs;
+          if (trow_ok && kin) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
           else fa = typename M::frag{};
-          acc2 = M::mma(fa, M::cvt(sp + k), acc2);
+          if (kin) fs = M::cvt(sp + k);
+          else fs = typename M::frag{};
+          acc2 = M::mma(fa, fs, acc2);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

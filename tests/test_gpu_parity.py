@@ -160,6 +160,20 @@ def test_chunk_scan_large_heads_group(ops):
     scan_case(ops, small("c2", seqlen=300), True, True)
 
 
+@pytest.mark.parametrize("Q,with_norm", [(64, True), (32, False), (128, True)])
+def test_chunk_scan_bf16_small_state(ops, Q, with_norm):
+    """d_state 16 with bf16 operands (generic kernels): the C.B^T and C.S_in
+    contractions run 32 deep, so the k-slices past d_state must read nothing
+    and count as zero."""
+    scan_case(ops, small("c1", nheads=2, ngroups=1, headdim=32, dstate=16, batch=1, seqlen=100),
+              True, with_norm, Q=Q)
+
+
+def test_prefill_bf16_small_state(ops):
+    prefill_case(ops, small("c1", nheads=4, ngroups=1, headdim=32, dstate=16, batch=2,
+                            seqlen=100), with_state=True)
+
+
 def test_chunk_scan_fp32_shapes(ops):
     scan_case(ops, small("c0", nheads=8, headdim=32, ngroups=2, dstate=64, seqlen=130,
                          batch=2), True, True)
