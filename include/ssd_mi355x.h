@@ -66,12 +66,12 @@
  *
  * Precision. State, decay exponents, sums and the norm are fp32. The dense
  * contractions of the chunked scan run on MFMA with fp32 accumulation: with
- * fp32 operands for fp32 I/O; with bf16 operands for bf16 I/O outside the
- * fast path; in the fast path (bf16 I/O, headdim 64, dstate 128, heads per
- * group a multiple of 4, dims->chunk >= 64, conv width 4 when the call
- * includes the conv) with fp16 operands (B, C, x, the decay-masked C B^T,
- * chunk states and carried-in states), with D x taken from x at fp16 hi + lo
- * precision. Such operands must stay within fp16 range (|v| < 65504):
+ * fp32 operands for fp32 I/O and fp16 operands for bf16 I/O (B, C, x scaled
+ * by dt or the decay weights, the decay-masked C B^T and the carried-in
+ * states; in the fast path, used for bf16 I/O with headdim 64, dstate 128,
+ * heads per group a multiple of 4, dims->chunk >= 64 and conv width 4 when
+ * the call includes the conv, also the chunk states, and D x taken from x at
+ * fp16 hi + lo precision). Such operands must stay within fp16 range (|v| < 65504):
  * activations after SiLU, dt-weighted states of magnitude beyond that are
  * outside the fast path's envelope. In the fast path the chunk length is an
  * internal choice (128 tokens); the result does not depend on dims->chunk

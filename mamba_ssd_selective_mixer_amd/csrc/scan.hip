@@ -10,8 +10,10 @@
 //   chunk output  y_t[p] = sum_{s<=t} (C_t . B_s) exp(Lam_t - Lam_s) dt_s x_s[p]
 //                          + exp(Lam_t) (S_in(k) C_t)[p] + D_h x_t[p]
 // The three dense contractions (B^T (w x), C B^T, and the masked (C B^T) X
-// together with C S_in^T) run on 16x16 MFMA tiles: bf16 operands with fp32
-// accumulation for bf16 I/O, fp32 operands for fp32 I/O. Decays are always
+// together with C S_in^T) run on 16x16 MFMA tiles with fp32 accumulation:
+// fp16 operands for bf16 I/O (inputs converted as they are staged; the norm
+// that may follow amplifies operand rounding, and fp16's mantissa is 8x
+// finer than bf16's), fp32 operands for fp32 I/O. Decays are always
 // formed as exp(Lam_t - Lam_s) of a masked difference, never as a ratio of
 // exponentials, so they stay finite for any chunk length.
 #include "common.hpp"
@@ -51,11 +53,12 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
     const T* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, int64_t bs, float* __restrict__ states,
     float* __restrict__ lam_end, int L, int H, int G, int P, int N, int Q, int nc) {
-  using M = Mfma<T>;
-  constexpr int KP = kStateSB + Pad<T>::v;
+  typedef typename OpOf<T>::type O;  // MFMA operand type
+  using M = Mfma<O>;
+  constexpr int KP = kStateSB + Pad<O>::v;
   extern __shared__ __align__(16) unsigned char smraw[];
-  T* XwT = reinterpret_cast<T*>(smraw);  // [P][KP]  x_s[p] * w_s, k = s contiguous
-  T* BT = XwT + P * KP;                  // [N][KP]  B_s[n]
+  O* XwT = reinterpret_cast<O*>(smraw);  // [P][KP]  x_s[p] * w_s, k = s contiguous
+  O* BT = XwT + P * KP;                  // [N][KP]  B_s[n]
   __shared__ float lam[kScanThreads], dts[kScanThreads], wgt[kScanThreads], wsum[4];
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
         for (int j = 0; j < 8; ++j) xv[j] = 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<T>(xv[j]);
+      for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<O>(xv[j]);
     }
     for (int v = tid; v < kStateSB * N8; v += kScanThreads) {
       const int s = v / N8, n0 = (v % N8) * 8;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
         for (int j = 0; j < 8; ++j) bv[j] = 0.f;
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<T>(bv[j]);
+      for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<O>(bv[j]);
     }
     __syncthreads();
     const int kk = M::KPL * (lane >> 4), rr = lane & 15;
@@ -111,8 +114,8 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
       const int tile = wave + 4 * i;
       if (tile < tiles) {
         const int tp = tile / ntn, tn = tile % ntn;
-        const T* ap = XwT + (tp * 16 + rr) * KP + kk;
-        const T* bp = BT + (tn * 16 + rr) * KP + kk;
+        const O* ap = XwT + (tp * 16 + rr) * KP + kk;
+        const O* bp = BT + (tn * 16 + rr) * KP + kk;
 #pragma unroll
         for (int k = 0; k < kStateSB; k += M::KSTEP)
           acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
@@ -172,11 +175,12 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
     const float* __restrict__ D, const T* __restrict__ Bm, const T* __restrict__ Cm, int64_t bs,
     const float* __restrict__ states, void* __restrict__ yout, int L, int H, int G, int P,
     int N, int Q, int nc) {
-  using M = Mfma<T>;
-  const int QK = Q + Pad<T>::v;
+  typedef typename OpOf<T>::type O;  // MFMA operand type
+  using M = Mfma<O>;
+  const int QK = Q + Pad<O>::v;
   extern __shared__ __align__(16) unsigned char smraw[];
-  T* XdtT = reinterpret_cast<T*>(smraw);  // [P][QK]  dt_s x_s[p], k = s contiguous
-  T* Mall = XdtT + P * QK;                // [4 waves][16][QK]
+  O* XdtT = reinterpret_cast<O*>(smraw);  // [P][QK]  dt_s x_s[p], k = s contiguous
+  O* Mall = XdtT + P * QK;                // [4 waves][16][QK]
   __shared__ float lam[kScanThreads], dts[kScanThreads], wsum[4];
 
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -202,13 +206,13 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
       for (int j = 0; j < 8; ++j) xv[j] = 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) XdtT[(p0 + j) * QK + s] = from_f<T>(xv[j]);
+    for (int j = 0; j < 8; ++j) XdtT[(p0 + j) * QK + s] = from_f<O>(xv[j]);
   }
   __syncthreads();
 
   const float* Sin = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   const float Dh = D ? D[h] : 0.f;
-  T* Mw = Mall + wave * 16 * QK;
+  O* Mw = Mall + wave * 16 * QK;
   const T* Cg = Cm + (int64_t)g * N;
   const T* Bg = Bm + (int64_t)g * N;
   const int nrt = (len + 15) / 16;
@@ -225,12 +229,12 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
         const bool scol_ok = scol < len;
         f32x4 gacc = zero4();
         for (int k = 0; k < N; k += M::KSTEP) {
-          // a lane's k-slice past N (N = 16 under a 32-deep bf16 MFMA) is zero
+          // a lane's k-slice past N (N = 16 under a 32-deep fp16 MFMA) is zero
           const bool kin = k + kk < N;
           typename M::frag fa, fb;
-          if (trow_ok && kin) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          if (trow_ok && kin) fa = M::ldg(Cg + (row0 + trow) * bs + k + kk);
           else fa = typename M::frag{};
-          if (scol_ok && kin) fb = M::ld(Bg + (row0 + scol) * bs + k + kk);
+          if (scol_ok && kin) fb = M::ldg(Bg + (row0 + scol) * bs + k + kk);
           else fb = typename M::frag{};
           gacc = M::mma(fa, fb, gacc);
         }
@@ -239,24 +243,24 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
           const int t = rt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
           float m = 0.f;
           if (s <= t && t < len) m = gacc[r] * fexp(lam[t] - lam[s]);
-          Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<T>(m);
+          Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<O>(m);
         }
       }
       for (int s = ns + (lane & 15); s < nsr; s += 16)
-        for (int r = 0; r < 4; ++r) Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<T>(0.f);
+        for (int r = 0; r < 4; ++r) Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<O>(0.f);
     }
     __syncthreads();
     if (active) {
       for (int pt = 0; pt < P / 16; ++pt) {
         f32x4 acc = zero4(), acc2 = zero4();
-        const T* mp = Mw + rr * QK + kk;
-        const T* xp = XdtT + (pt * 16 + rr) * QK + kk;
+        const O* mp = Mw + rr * QK + kk;
+        const O* xp = XdtT + (pt * 16 + rr) * QK + kk;
         for (int k = 0; k < nsr; k += M::KSTEP) acc = M::mma(M::ld(mp + k), M::ld(xp + k), acc);
         const float* sp = Sin + (int64_t)(pt * 16 + rr) * N + kk;
         for (int k = 0; k < N; k += M::KSTEP) {
           const bool kin = k + kk < N;
           typename M::frag fa, fs;
-          if (trow_ok && kin) fa = M::ld(Cg + (row0 + trow) * bs + k + kk);
+          if (trow_ok && kin) fa = M::ldg(Cg + (row0 + trow) * bs + k + kk);
           else fa = typename M::frag{};
           if (kin) fs = M::cvt(sp + k);
           else fs = typename M::frag{};
