@@ -112,7 +112,7 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
     o_states = take(B * nc * H * P * N * 4);
     o_lam = take(B * H * nc * 4);
     o_y = take(B * L * H * P * 4);
-    if (conv) o_conv = take(B * L * (size_t)channels(d) * esize(d));
+    if (conv) o_conv = take(B * L * (size_t)channels(d) * 4);  // fp32 conv output
   }
   w.total = off;
   if (base) {
@@ -129,21 +129,22 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   return w;
 }
 
+// x_f32: x, B and C are fp32 (the conv's internal copy), else the I/O type.
 int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const float* A,
-             const float* D, const void* Bm, const void* Cm, int64_t bs, const void* z,
+             const float* D, const void* Bm, const void* Cm, int64_t bs, bool x_f32, const void* z,
              const void* norm_w, float eps, const float* s_in, float* s_out, void* y,
              const ScanWs& ws, hipStream_t st) {
   const bool bf = d->io_dtype == SSD_BF16;
   ssd::ScanShape s{d->batch, d->seqlen, d->nheads, d->headdim, d->ngroups,
                    d->dstate, d->chunk, (int)nchunks(d)};
   int rc = hip_status(
-      ssd::launch_chunk_state(bf, s, x, xs, dt, A, Bm, bs, ws.states, ws.lam_end, st));
+      ssd::launch_chunk_state(bf, x_f32, s, x, xs, dt, A, Bm, bs, ws.states, ws.lam_end, st));
   if (rc) return rc;
   rc = hip_status(ssd::launch_state_pass(s, ws.states, ws.lam_end, s_in, s_out, st));
   if (rc) return rc;
   const bool fused_norm = z != nullptr;
   void* ydst = fused_norm ? (void*)ws.y32 : y;
-  rc = hip_status(ssd::launch_chunk_out(bf, s, x, xs, dt, A, D, Bm, Cm, bs, ws.states, ydst,
+  rc = hip_status(ssd::launch_chunk_out(bf, x_f32, s, x, xs, dt, A, D, Bm, Cm, bs, ws.states, ydst,
                                         fused_norm || !bf, st));
   if (rc) return rc;
   if (fused_norm)
@@ -243,7 +244,7 @@ int ssd_conv1d(const ssd_dims* d, const void* xbc, int64_t xbc_tok_stride, const
   const bool bf = d->io_dtype == SSD_BF16;
   rc = hip_status(ssd::launch_conv1d(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
                                      xbc_tok_stride, w, bias, conv_state_in, out, out_tok_stride,
-                                     st));
+                                     false, st));
   if (rc || !conv_state_out) return rc;
   return hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
                                            xbc_tok_stride, conv_state_in, conv_state_out, st));
@@ -288,7 +289,7 @@ int ssd_chunk_scan(const ssd_dims* d, const void* x, int64_t x_tok_stride, const
     return run_fast(d, false, x, Bm, Cm, x_tok_stride, bc_tok_stride, dt, A, D, nullptr, nullptr,
                     nullptr, z, norm_w, eps, ssm_state_in, ssm_state_out, y, ws,
                     (hipStream_t)stream);
-  return run_scan(d, x, x_tok_stride, dt, A, D, Bm, Cm, bc_tok_stride, z, norm_w, eps,
+  return run_scan(d, x, x_tok_stride, dt, A, D, Bm, Cm, bc_tok_stride, false, z, norm_w, eps,
                   ssm_state_in, ssm_state_out, y, ws, (hipStream_t)stream);
 }
 
@@ -380,8 +381,10 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
     return hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
                                              C, conv_state_in, conv_state_out, st));
   }
+  // the conv output stays fp32 for the scan: with a conv bias, B and C carry
+  // a shared offset whose C.B products cancel, so their rounding matters
   rc = hip_status(ssd::launch_conv1d(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc, C,
-                                     conv_w, conv_b, conv_state_in, ws.conv, C, st));
+                                     conv_w, conv_b, conv_state_in, ws.conv, C, true, st));
   if (rc) return rc;
   if (conv_state_out) {
     rc = hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
@@ -389,7 +392,7 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
     if (rc) return rc;
   }
   const unsigned char* v = ws.conv;
-  return run_scan(d, v, C, dt, A, D, v + HP * e, v + (HP + GN) * e, C, z, norm_w, eps,
+  return run_scan(d, v, C, dt, A, D, v + HP * 4, v + (HP + GN) * 4, C, true, z, norm_w, eps,
                   ssm_state_in, ssm_state_out, out, ws, st);
 }
 

@@ -163,6 +163,7 @@ template <> struct Mfma<h16> {
     f[4] = (h16)b.x; f[5] = (h16)b.y; f[6] = (h16)b.z; f[7] = (h16)b.w;
     return f;
   }
+  static SSD_DEV frag ldg(const float* p) { return cvt(p); }
 };
 template <> struct Mfma<float> {
   static constexpr int KPL = 1, KSTEP = 4;

@@ -16,10 +16,11 @@ namespace ssd {
 constexpr int kConvTT = 32;   // tokens per thread
 constexpr int kConvThreads = 256;
 
-template <class T, int W>
+// TO: output element type (the I/O type, or fp32 for the scan's internal copy)
+template <class T, class TO, int W>
 __global__ __launch_bounds__(kConvThreads) void k_conv1d(
     const T* __restrict__ xbc, int64_t xs, const T* __restrict__ w,
-    const T* __restrict__ bias, const T* __restrict__ cin, T* __restrict__ out,
+    const T* __restrict__ bias, const T* __restrict__ cin, TO* __restrict__ out,
     int64_t os, int L, int C) {
   const int cv = blockIdx.x * kConvThreads + threadIdx.x;
   if (cv * 8 >= C) return;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_state(
   }
 }
 
-template <class T>
+template <class T, class TO>
 static hipError_t conv_dispatch(int B, int L, int C, int W, const void* xbc, int64_t xs,
                                 const void* w, const void* bias, const void* cin, void* out,
                                 int64_t os, hipStream_t st) {
@@ -100,21 +101,23 @@ static hipError_t conv_dispatch(int B, int L, int C, int W, const void* xbc, int
   const T* Wt = (const T*)w;
   const T* Bi = (const T*)bias;
   const T* Ci = (const T*)cin;
-  T* O = (T*)out;
+  TO* O = (TO*)out;
+  const dim3 blk(kConvThreads);
   switch (W) {
-    case 2: hipLaunchKernelGGL((k_conv1d<T, 2>), grid, dim3(kConvThreads), 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
-    case 3: hipLaunchKernelGGL((k_conv1d<T, 3>), grid, dim3(kConvThreads), 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
-    default: hipLaunchKernelGGL((k_conv1d<T, 4>), grid, dim3(kConvThreads), 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
+    case 2: hipLaunchKernelGGL((k_conv1d<T, TO, 2>), grid, blk, 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
+    case 3: hipLaunchKernelGGL((k_conv1d<T, TO, 3>), grid, blk, 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
+    default: hipLaunchKernelGGL((k_conv1d<T, TO, 4>), grid, blk, 0, st, X, xs, Wt, Bi, Ci, O, os, L, C); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_conv1d(bool io_bf16, int B, int L, int C, int W, const void* xbc, int64_t xs,
                          const void* w, const void* bias, const void* cin, void* out, int64_t os,
-                         hipStream_t st) {
+                         bool out_f32, hipStream_t st) {
   ProfScope ps(st, KID_CONV1D);
-  return io_bf16 ? conv_dispatch<bf16>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st)
-                 : conv_dispatch<float>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st);
+  if (!io_bf16) return conv_dispatch<float, float>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st);
+  return out_f32 ? conv_dispatch<bf16, float>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st)
+                 : conv_dispatch<bf16, bf16>(B, L, C, W, xbc, xs, w, bias, cin, out, os, st);
 }
 
 template <class T>

@@ -12,10 +12,11 @@ struct ScanShape {
   int B, L, H, P, G, N, Q, nc;
 };
 
-// Depthwise causal conv + SiLU; io_bf16 selects bf16 (else fp32) elements.
+// Depthwise causal conv + SiLU; io_bf16 selects bf16 (else fp32) elements;
+// out_f32 writes the output in fp32 whatever the I/O type.
 hipError_t launch_conv1d(bool io_bf16, int B, int L, int C, int W, const void* xbc,
                          int64_t xs, const void* w, const void* bias, const void* cin,
-                         void* out, int64_t os, hipStream_t st);
+                         void* out, int64_t os, bool out_f32, hipStream_t st);
 // conv_out[b] = last W-1 rows of [cin[b] ; xbc[b]] (safe when cout == cin).
 hipError_t launch_conv_state(bool io_bf16, int B, int L, int C, int W, const void* xbc,
                              int64_t xs, const void* cin, void* cout, hipStream_t st);
@@ -30,15 +31,16 @@ hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
                          float eps, void* conv_state, float* ssm_state, void* y,
                          hipStream_t st);
 // Chunked scan, three phases: chunk states, state passing, chunk outputs.
-hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
-                              const void* dt, const float* A, const void* Bm, int64_t bs,
-                              float* states, float* lam_end, hipStream_t st);
+// x_f32: x, B and C are fp32 (else the I/O type); dt and y are the I/O type.
+hipError_t launch_chunk_state(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
+                              int64_t xs, const void* dt, const float* A, const void* Bm,
+                              int64_t bs, float* states, float* lam_end, hipStream_t st);
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
                              const float* s_in, float* s_out, hipStream_t st);
-hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
-                            const void* dt, const float* A, const float* D, const void* Bm,
-                            const void* Cm, int64_t bs, const float* states, void* y,
-                            bool y_f32, hipStream_t st);
+hipError_t launch_chunk_out(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
+                            int64_t xs, const void* dt, const float* A, const float* D,
+                            const void* Bm, const void* Cm, int64_t bs, const float* states,
+                            void* y, bool y_f32, hipStream_t st);
 
 }  // namespace ssd
 

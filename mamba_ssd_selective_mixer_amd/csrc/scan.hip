@@ -48,10 +48,12 @@ __device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, int64_t r
 
 // ---------------------------------------------------------------------------
 // Phase 1: chunk states dS_k = (w x)^T B per (chunk, head, batch).
-template <class T>
+// T: I/O type (dt); TX: element type of x and B (T, or fp32 when they come
+// from the conv's internal fp32 copy).
+template <class T, class TX>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
-    const T* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
-    const T* __restrict__ Bm, int64_t bs, float* __restrict__ states,
+    const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
+    const TX* __restrict__ Bm, int64_t bs, float* __restrict__ states,
     float* __restrict__ lam_end, int L, int H, int G, int P, int N, int Q, int nc) {
   typedef typename OpOf<T>::type O;  // MFMA operand type
   using M = Mfma<O>;
@@ -169,10 +171,10 @@ __global__ __launch_bounds__(kScanThreads) void k_state_pass(float* states,
 // Phase 3: chunk outputs. Each wave owns 16-row tiles of the chunk: it forms
 // the causal tiles of M = (C B^T) o exp(Lam_t - Lam_s) in its LDS slab, then
 // y = M (dt x) + exp(Lam_t) C S_in^T + D x for every 16-column tile of P.
-template <class T, bool YF32>
+template <class T, class TX, bool YF32>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
-    const T* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, const T* __restrict__ Bm, const T* __restrict__ Cm, int64_t bs,
+    const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, const TX* __restrict__ Bm, const TX* __restrict__ Cm, int64_t bs,
     const float* __restrict__ states, void* __restrict__ yout, int L, int H, int G, int P,
     int N, int Q, int nc) {
   typedef typename OpOf<T>::type O;  // MFMA operand type
@@ -213,8 +215,8 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
   const float* Sin = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   const float Dh = D ? D[h] : 0.f;
   O* Mw = Mall + wave * 16 * QK;
-  const T* Cg = Cm + (int64_t)g * N;
-  const T* Bg = Bm + (int64_t)g * N;
+  const TX* Cg = Cm + (int64_t)g * N;
+  const TX* Bg = Bm + (int64_t)g * N;
   const int nrt = (len + 15) / 16;
   for (int rt0 = 0; rt0 < nrt; rt0 += 4) {
     const int rt = rt0 + wave;
@@ -293,21 +295,20 @@ static size_t out_lds(bool bf, int P, int Q) {
   return (size_t)(P + 4 * 16) * QK * (bf ? 2 : 4);
 }
 
-hipError_t launch_chunk_state(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
-                              const void* dt, const float* A, const void* Bm, int64_t bs,
-                              float* states, float* lam_end, hipStream_t st) {
+hipError_t launch_chunk_state(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
+                              int64_t xs, const void* dt, const float* A, const void* Bm,
+                              int64_t bs, float* states, float* lam_end, hipStream_t st) {
   ProfScope ps(st, KID_CHUNK_STATE);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
   const size_t lds = state_lds(io_bf16, s.P, s.N);
-  if (io_bf16) {
-    hipLaunchKernelGGL(k_chunk_state<bf16>, grid, block, lds, st, (const bf16*)x, xs,
-                       (const bf16*)dt, A, (const bf16*)Bm, bs, states, lam_end, s.L, s.H, s.G,
-                       s.P, s.N, s.Q, s.nc);
-  } else {
-    hipLaunchKernelGGL(k_chunk_state<float>, grid, block, lds, st, (const float*)x, xs,
-                       (const float*)dt, A, (const float*)Bm, bs, states, lam_end, s.L, s.H,
-                       s.G, s.P, s.N, s.Q, s.nc);
-  }
+#define SSD_STATE(TT, TX)                                                                      \
+  hipLaunchKernelGGL((k_chunk_state<TT, TX>), grid, block, lds, st, (const TX*)x, xs,           \
+                     (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, s.L, s.H, s.G, s.P,  \
+                     s.N, s.Q, s.nc)
+  if (!io_bf16) SSD_STATE(float, float);
+  else if (x_f32) SSD_STATE(bf16, float);
+  else SSD_STATE(bf16, bf16);
+#undef SSD_STATE
   return hipGetLastError();
 }
 
@@ -321,24 +322,24 @@ hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_out(bool io_bf16, const ScanShape& s, const void* x, int64_t xs,
-                            const void* dt, const float* A, const float* D, const void* Bm,
-                            const void* Cm, int64_t bs, const float* states, void* y, bool y_f32,
-                            hipStream_t st) {
+hipError_t launch_chunk_out(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
+                            int64_t xs, const void* dt, const float* A, const float* D,
+                            const void* Bm, const void* Cm, int64_t bs, const float* states,
+                            void* y, bool y_f32, hipStream_t st) {
   ProfScope ps(st, KID_CHUNK_OUT);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
   const size_t lds = out_lds(io_bf16, s.P, s.Q);
-#define SSD_OUT(TT, YF)                                                                          \
-  do {                                                                                           \
-    hipLaunchKernelGGL((k_chunk_out<TT, YF>), grid, block, lds, st, (const TT*)x, xs,            \
-                       (const TT*)dt, A, D, (const TT*)Bm, (const TT*)Cm, bs, states, y, s.L,    \
-                       s.H, s.G, s.P, s.N, s.Q, s.nc);                                           \
-  } while (0)
-  if (io_bf16) {
-    if (y_f32) SSD_OUT(bf16, true);
-    else SSD_OUT(bf16, false);
+#define SSD_OUT(TT, TX, YF)                                                                     \
+  hipLaunchKernelGGL((k_chunk_out<TT, TX, YF>), grid, block, lds, st, (const TX*)x, xs,         \
+                     (const TT*)dt, A, D, (const TX*)Bm, (const TX*)Cm, bs, states, y, s.L, s.H, \
+                     s.G, s.P, s.N, s.Q, s.nc)
+  if (!io_bf16) SSD_OUT(float, float, true);
+  else if (x_f32) {
+    if (y_f32) SSD_OUT(bf16, float, true);
+    else SSD_OUT(bf16, float, false);
   } else {
-    SSD_OUT(float, true);
+    if (y_f32) SSD_OUT(bf16, bf16, true);
+    else SSD_OUT(bf16, bf16, false);
   }
 #undef SSD_OUT
   return hipGetLastError();

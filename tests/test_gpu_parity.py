@@ -178,6 +178,16 @@ def test_chunk_scan_bf16_generic_norm(ops):
               True, True, Q=128)
 
 
+@pytest.mark.parametrize("P,N,W", [(128, 16, 2), (64, 64, 4)])
+def test_prefill_generic_bias_normed(ops, P, N, W):
+    """Generic kernels with a conv bias and the gated norm (bf16 I/O): the
+    bias shifts B and C by a shared offset whose C.B products cancel, and the
+    norm amplifies what remains, so the conv output must not be rounded to
+    bf16 between the conv and the scan (it reached 1.1-2.5x the tolerance)."""
+    prefill_case(ops, small("c1", nheads=64, ngroups=8, headdim=P, dstate=N, conv_width=W,
+                            batch=1, seqlen=129), with_state=False, with_bias=True)
+
+
 def test_prefill_bf16_small_state(ops):
     prefill_case(ops, small("c1", nheads=4, ngroups=1, headdim=32, dstate=16, batch=2,
                             seqlen=100), with_state=True)
