@@ -193,6 +193,34 @@ def test_prefill_bf16_small_state(ops):
                             seqlen=100), with_state=True)
 
 
+@pytest.mark.parametrize("kw", [dict(batch=2, seqlen=200),                      # fast path
+                                dict(batch=2, seqlen=128, headdim=32, dstate=64)])  # generic
+def test_chunk_scan_strided_views(ops, kw):
+    """x, B and C passed as strided views into one padded xBC tensor (token
+    stride > row width), the way a caller hands over slices of a projection."""
+    import torch
+    cfg = small("c1", **kw)
+    td = torch_dtype(cfg.dtype)
+    d = make_dims(ops, cfg)
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg)
+    x, Bm, Cm = synth.split_channels(cfg, inp["xbc"])
+    HP, GN, C = cfg.hp, cfg.gn, cfg.channels
+    big = torch.zeros(cfg.batch, cfg.seqlen, C + 64, dtype=td, device="cuda")
+    big[..., :C] = dev(inp["xbc"], td)
+    s0 = synth.initial_states(cfg)["ssm_state"]
+    so = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
+    y = ops.ssd_chunk_scan(d, big[..., :HP], dev(inp["dt"], td), dev(prm["A"]), dev(prm["D"]),
+                           big[..., HP:HP + GN], big[..., HP + GN:C], z=dev(inp["z"], td),
+                           norm_w=dev(prm["norm_w"], td), eps=prm["eps"], ssm_state_in=dev(s0),
+                           ssm_state_out=so)
+    ry, rs = oracle.ssm_scan(x, inp["dt"], prm["A"], Bm, Cm, prm["D"], s0)
+    ry = oracle.gated_rmsnorm(ry.reshape(cfg.batch, cfg.seqlen, HP), inp["z"], prm["norm_w"],
+                              cfg.ngroups, prm["eps"])
+    check("scan y (strided)", host(y), ry, TOL[cfg.dtype])
+    check("final state (strided)", host(so), rs, TOL[cfg.dtype])
+
+
 def test_chunk_scan_fp32_shapes(ops):
     scan_case(ops, small("c0", nheads=8, headdim=32, ngroups=2, dstate=64, seqlen=130,
                          batch=2), True, True)
