@@ -24,7 +24,7 @@ namespace ssd {
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kStateSB = 64;       // tokens staged per block in the chunk-state kernel
 
-template <class T> struct Pad { static constexpr int v = 8; };     // bf16: 16 bytes per LDS row
+template <class T> struct Pad { static constexpr int v = 8; };     // fp16 operands: 16 bytes per LDS row
 template <> struct Pad<float> { static constexpr int v = 4; };
 
 // Inclusive cumulative sum of a_s = dt_s * A over the chunk (s < len; zero
