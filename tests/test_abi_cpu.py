@@ -110,6 +110,59 @@ def test_null_and_alignment_checks_return_before_launch(lib):
                               V((1 << 43) + S // 2), V(1 << 40), V(1 << 41), need, None) == -5
 
 
+def test_prefill_decode_norm_refuse_before_launch(lib):
+    """The mixer prefill, decode step and standalone norm refuse NULLs,
+    misalignment, a short workspace, a wrong shape and aliasing with their
+    documented codes, before any launch (addresses are never dereferenced)."""
+    V = ctypes.c_void_p
+    NULL, SHAPE, ALIAS, WORKSPACE, ALIGN = -1, -2, -5, -6, -8
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    xbc, z, dt, A, D, cw, nw = (V(k << 36) for k in (1, 2, 3, 4, 5, 6, 7))
+    cs_in, cs_out, ss_in, ss_out, out, ws = (V(k << 36) for k in (8, 9, 10, 11, 12, 13))
+
+    def prefill(**kw):
+        a = dict(xbc=xbc, z=z, dt=dt, A=A, D=D, cw=cw, cb=None, nw=nw, cs_in=cs_in,
+                 cs_out=cs_out, ss_in=ss_in, ss_out=ss_out, out=out, ws=ws, n=need)
+        a.update(kw)
+        return lib.ssd_mixer_prefill(ctypes.byref(d), a["xbc"], a["z"], a["dt"], a["A"], a["D"],
+                                     a["cw"], a["cb"], a["nw"], 1e-5, a["cs_in"], a["cs_out"],
+                                     a["ss_in"], a["ss_out"], a["out"], a["ws"], a["n"], None)
+
+    assert prefill(xbc=None) == NULL
+    assert prefill(nw=None) == NULL                      # z given without a norm weight
+    assert prefill(out=V((12 << 36) + 8)) == ALIGN
+    assert prefill(n=need - 1) == WORKSPACE
+    assert prefill(ws=None) == WORKSPACE
+    assert prefill(cs_out=V((1 << 36) + 4096)) == ALIAS  # new conv state inside xBC
+    assert prefill(cs_out=V((8 << 36) + 16)) == ALIAS    # conv states partly overlapping
+    assert prefill(ss_out=V((10 << 36) + 64)) == ALIAS   # SSM states partly overlapping
+    assert prefill(ws=V((12 << 36) + 256)) == ALIAS      # workspace over the output
+
+    dd = dims(synth.CONFIGS["c4"], seqlen=1)
+    st, y = V(14 << 36), V(15 << 36)
+
+    def decode(d_=dd, **kw):
+        a = dict(x=xbc, z=z, dt=dt, cs=cs_in, ss=st, y=y, nw=nw)
+        a.update(kw)
+        return lib.ssd_decode_step(ctypes.byref(d_), a["x"], a["z"], a["dt"], A, D, cw, None,
+                                   a["nw"], 1e-5, a["cs"], a["ss"], a["y"], None)
+
+    assert decode(d_=dims(synth.CONFIGS["c4"], seqlen=2)) == SHAPE
+    assert decode(ss=None) == NULL
+    assert decode(nw=None) == NULL
+    assert decode(y=V((15 << 36) + 4)) == ALIGN
+    assert decode(cs=V((14 << 36) + 4096)) == ALIAS      # conv state inside the SSM state
+
+    n = 4 * 2048 * 32 * 64 * 2
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), None, z, nw, 1e-5, out, None) == NULL
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), y, z, nw, 1e-5, V((12 << 36) + 2), None) == ALIGN
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), y, z, nw, 1e-5, V((15 << 36) + n // 2),
+                                 None) == ALIAS          # out partly over y
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), y, z, nw, 1e-5, z, None) == ALIAS
+
+
 def test_workspace_sizes(lib):
     c1 = synth.CONFIGS["c1"]
     d = dims(c1)
