@@ -284,6 +284,17 @@ def test_decode_bf16(ops, kw):
     decode_case(ops, synth.replace(synth.CONFIGS["c4"], **kw), steps=3)
 
 
+# Decode shapes across the envelope (head_dim, d_state, conv width, heads per
+# group, I/O type, gate on or off), each stepped three times.
+@pytest.mark.parametrize("base,kw,norm", [
+    ("c4", dict(batch=3, nheads=8, ngroups=1, headdim=128, dstate=128, conv_width=2), True),
+    ("c4", dict(batch=5, nheads=4, ngroups=4, headdim=16, dstate=32, conv_width=3), True),
+    ("c0", dict(batch=2, nheads=8, ngroups=2, headdim=64, dstate=16), True),
+    ("c4", dict(batch=2, nheads=16, ngroups=8, headdim=32, dstate=64, conv_width=2), False)])
+def test_decode_envelope(ops, base, kw, norm):
+    decode_case(ops, synth.replace(synth.CONFIGS[base], **kw), steps=3, with_norm=norm)
+
+
 # -------------------------------------------------------------- full prefill
 def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False, inplace=False,
                  with_norm=True, A=None):
