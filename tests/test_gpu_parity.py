@@ -458,6 +458,38 @@ def test_prefill_pieces_in_place(ops):
     prefill_case(ops, small("c3", seqlen=300), with_state=True, pieces=[2, 128], inplace=True)
 
 
+def test_concurrent_streams(ops):
+    """Two prefill calls in flight at once on two streams, each with its own
+    workspace (one of them normalising across blocks, whose tickets live in
+    the workspace), give bit-identical results to the same calls run one
+    after the other: the library keeps no state between calls."""
+    import torch
+    bf = torch.bfloat16
+    cases = []
+    for cfg in (small("c1", batch=2, seqlen=300), small("c1", nheads=64, ngroups=2, batch=2,
+                                                         seqlen=300)):
+        d = make_dims(ops, cfg)
+        prm = synth.layer_params(cfg)
+        inp = synth.prefill_inputs(cfg)
+        args = (dev(inp["xbc"], bf), dev(inp["z"], bf), dev(inp["dt"], bf), dev(prm["A"]),
+                dev(prm["D"]), dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"])
+        cases.append((d, args))
+    ref = [host(ops.ssd_mixer_prefill(d, *a)) for d, a in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = []
+    for (d, a), st in zip(cases, streams):
+        ws = ops.workspace(ops.ssd_mixer_prefill_workspace_bytes(d))
+        outs.append((torch.empty(d.batch, d.seqlen, d.hp, dtype=bf, device="cuda"), ws))
+    for _ in range(3):
+        for (d, a), st, (o, ws) in zip(cases, streams, outs):
+            st.wait_stream(torch.cuda.current_stream())
+            ops.ssd_mixer_prefill(d, *a, out=o, ws=ws, stream=st)
+        torch.cuda.synchronize()
+        for r, (o, _) in zip(ref, outs):
+            assert np.array_equal(host(o), r)
+
+
 def test_causality_gpu(ops):
     """Perturbing token t leaves every earlier output of the GPU path unchanged."""
     cfg = small("c1", batch=1, seqlen=256)
