@@ -490,6 +490,41 @@ def test_concurrent_streams(ops):
             assert np.array_equal(host(o), r)
 
 
+@pytest.mark.parametrize("kw", [dict(batch=2, seqlen=300),                 # norm in the block
+                                dict(nheads=64, ngroups=2, batch=2, seqlen=300)])  # across blocks
+def test_graph_replay(ops, kw):
+    """The fused prefill captured into a HIP graph and replayed several times,
+    with eager work and synchronisation between replays, matches the eager
+    call on every replay (its only per-call state, the cross-block norm's
+    tickets and slots, is reset by a kernel, not a memset)."""
+    import torch
+    bf = torch.bfloat16
+    cfg = small("c1", **kw)
+    d = make_dims(ops, cfg)
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg)
+    args = (dev(inp["xbc"], bf), dev(inp["z"], bf), dev(inp["dt"], bf), dev(prm["A"]),
+            dev(prm["D"]), dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"])
+    ref = host(ops.ssd_mixer_prefill(d, *args))
+    ws = ops.workspace(ops.ssd_mixer_prefill_workspace_bytes(d))
+    out = torch.empty(cfg.batch, cfg.seqlen, cfg.hp, dtype=bf, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.ssd_mixer_prefill(d, *args, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.ssd_mixer_prefill(d, *args, out=out, ws=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(7)                      # scribble over the workspace between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref), f"replay {i}"
+
+
 def test_causality_gpu(ops):
     """Perturbing token t leaves every earlier output of the GPU path unchanged."""
     cfg = small("c1", batch=1, seqlen=256)
