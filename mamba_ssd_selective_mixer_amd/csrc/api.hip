@@ -30,16 +30,38 @@ int64_t channels(const ssd_dims* d) {
 }
 int64_t nchunks(const ssd_dims* d) { return (d->seqlen + d->chunk - 1) / d->chunk; }
 
-// Byte ranges: NULL or identical pointers are fine, any other overlap is not.
-bool partial_overlap(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b || a == b) return false;
+bool any_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + nb && y < x + na;
 }
-bool any_overlap(const void* a, size_t na, const void* b, size_t nb) {
-  if (!a || !b) return false;
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
+
+// One buffer of a call: its byte range, whether the call writes it, and the
+// slot of the one buffer it may coincide with exactly (an in-place pair such
+// as ssm_state_in / ssm_state_out), or -1.
+struct Range {
+  const void* p;
+  size_t n;
+  bool written;
+  int twin;
+};
+// Every buffer the call writes must be disjoint from every other buffer it
+// touches, except its documented in-place twin at exactly the same address
+// and size. Buffers that are only read may overlap each other (x, B and C
+// may be views of one tensor).
+bool aliased(std::initializer_list<Range> list) {
+  const Range* r = list.begin();
+  const int n = (int)list.size();
+  for (int i = 0; i < n; ++i) {
+    if (!r[i].written) continue;
+    for (int j = 0; j < n; ++j) {
+      if (j == i || (r[j].written && j < i)) continue;
+      if (!any_overlap(r[i].p, r[i].n, r[j].p, r[j].n)) continue;
+      const bool twins = (r[i].twin == j || r[j].twin == i) && r[i].p == r[j].p && r[i].n == r[j].n;
+      if (!twins) return true;
+    }
+  }
+  return false;
 }
 
 int check_dims(int entry, const ssd_dims* d) {
@@ -236,9 +258,12 @@ int ssd_conv1d(const ssd_dims* d, const void* xbc, int64_t xbc_tok_stride, const
   const size_t nx = ((B * L - 1) * xbc_tok_stride + C) * e;
   const size_t no = ((B * L - 1) * out_tok_stride + C) * e;
   const size_t ns = B * R * C * e;
-  if (any_overlap(out, no, xbc, nx) || any_overlap(out, no, conv_state_in, ns) ||
-      any_overlap(out, no, conv_state_out, ns) || partial_overlap(conv_state_in, ns, conv_state_out, ns) ||
-      any_overlap(conv_state_out, ns, xbc, nx))
+  if (aliased({{xbc, nx, false, -1},
+               {w, C * d->conv_width * e, false, -1},
+               {bias, C * e, false, -1},
+               {conv_state_in, ns, false, 4},
+               {conv_state_out, ns, true, 3},
+               {out, no, true, -1}}))
     return SSD_ERR_ALIAS;
   hipStream_t st = (hipStream_t)stream;
   const bool bf = d->io_dtype == SSD_BF16;
@@ -278,11 +303,18 @@ int ssd_chunk_scan(const ssd_dims* d, const void* x, int64_t x_tok_stride, const
   const size_t T = (size_t)d->batch * d->seqlen;
   const size_t ny = T * HP * e, nst = (size_t)d->batch * HP * d->dstate * 4;
   const size_t nx = ((T - 1) * x_tok_stride + HP) * e, nb = ((T - 1) * bc_tok_stride + GN) * e;
-  if (any_overlap(y, ny, x, nx) || any_overlap(y, ny, Bm, nb) || any_overlap(y, ny, Cm, nb) ||
-      any_overlap(y, ny, dt, T * d->nheads * e) || any_overlap(y, ny, z, ny) ||
-      any_overlap(y, ny, ssm_state_in, nst) || any_overlap(y, ny, ssm_state_out, nst) ||
-      partial_overlap(ssm_state_in, nst, ssm_state_out, nst) ||
-      any_overlap(workspace, need.total, y, ny) || any_overlap(workspace, need.total, x, nx))
+  if (aliased({{x, nx, false, -1},
+               {dt, T * d->nheads * e, false, -1},
+               {A, (size_t)d->nheads * 4, false, -1},
+               {D, (size_t)d->nheads * 4, false, -1},
+               {Bm, nb, false, -1},
+               {Cm, nb, false, -1},
+               {z, ny, false, -1},
+               {norm_w, (size_t)HP * e, false, -1},
+               {ssm_state_in, nst, false, 9},
+               {ssm_state_out, nst, true, 8},
+               {y, ny, true, -1},
+               {workspace, need.total, true, -1}}))
     return SSD_ERR_ALIAS;
   const ScanWs ws = carve(d, workspace, false);
   if (ws.fast)
@@ -300,7 +332,11 @@ int ssd_gated_rmsnorm(const ssd_dims* d, const void* y, const void* z, const voi
   if (!y || !z || !w || !out) return SSD_ERR_NULL;
   if (!aligned16(y) || !aligned16(z) || !aligned16(w) || !aligned16(out)) return SSD_ERR_ALIGN;
   const size_t n = (size_t)d->batch * d->seqlen * d->nheads * d->headdim * esize(d);
-  if (partial_overlap(out, n, y, n) || any_overlap(out, n, z, n)) return SSD_ERR_ALIAS;
+  if (aliased({{y, n, false, 3},
+               {z, n, false, -1},
+               {w, (size_t)d->nheads * d->headdim * esize(d), false, -1},
+               {out, n, true, 0}}))
+    return SSD_ERR_ALIAS;
   return hip_status(ssd::launch_gated_norm(d->io_dtype == SSD_BF16, false,
                                            d->batch * d->seqlen, d->nheads * d->headdim,
                                            d->ngroups, y, z, w, eps, out, (hipStream_t)stream));
@@ -322,9 +358,17 @@ int ssd_decode_step(const ssd_dims* d, const void* xbc_t, const void* z_t, const
   const size_t HP = (size_t)d->nheads * d->headdim;
   const size_t ny = B * HP * e, ncs = B * (d->conv_width - 1) * C * e,
                nss = B * HP * d->dstate * 4;
-  if (any_overlap(y_t, ny, xbc_t, B * C * e) || any_overlap(y_t, ny, z_t, ny) ||
-      any_overlap(y_t, ny, conv_state, ncs) || any_overlap(y_t, ny, ssm_state, nss) ||
-      any_overlap(conv_state, ncs, ssm_state, nss) || any_overlap(conv_state, ncs, xbc_t, B * C * e))
+  if (aliased({{xbc_t, B * C * e, false, -1},
+               {z_t, ny, false, -1},
+               {dt_t, B * d->nheads * e, false, -1},
+               {A, (size_t)d->nheads * 4, false, -1},
+               {D, (size_t)d->nheads * 4, false, -1},
+               {conv_w, C * d->conv_width * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {conv_state, ncs, true, -1},
+               {ssm_state, nss, true, -1},
+               {y_t, ny, true, -1}}))
     return SSD_ERR_ALIAS;
   return hip_status(ssd::launch_decode(d->io_dtype == SSD_BF16, d->batch, d->nheads,
                                        d->headdim, d->ngroups, d->dstate, d->conv_width, xbc_t,
@@ -358,14 +402,20 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
   const size_t HP = (size_t)d->nheads * d->headdim;
   const size_t nx = T * C * e, no = T * HP * e, ncs = (size_t)d->batch * (d->conv_width - 1) * C * e,
                nss = (size_t)d->batch * HP * d->dstate * 4;
-  if (any_overlap(out, no, xbc, nx) || any_overlap(out, no, z, no) ||
-      any_overlap(out, no, dt, T * d->nheads * e) || any_overlap(out, no, conv_state_in, ncs) ||
-      any_overlap(out, no, conv_state_out, ncs) || any_overlap(out, no, ssm_state_in, nss) ||
-      any_overlap(out, no, ssm_state_out, nss) ||
-      partial_overlap(conv_state_in, ncs, conv_state_out, ncs) ||
-      partial_overlap(ssm_state_in, nss, ssm_state_out, nss) ||
-      any_overlap(conv_state_out, ncs, xbc, nx) || any_overlap(workspace, need.total, out, no) ||
-      any_overlap(workspace, need.total, xbc, nx))
+  if (aliased({{xbc, nx, false, -1},
+               {z, no, false, -1},
+               {dt, T * d->nheads * e, false, -1},
+               {A, (size_t)d->nheads * 4, false, -1},
+               {D, (size_t)d->nheads * 4, false, -1},
+               {conv_w, C * d->conv_width * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {conv_state_in, ncs, false, 9},
+               {conv_state_out, ncs, true, 8},
+               {ssm_state_in, nss, false, 11},
+               {ssm_state_out, nss, true, 10},
+               {out, no, true, -1},
+               {workspace, need.total, true, -1}}))
     return SSD_ERR_ALIAS;
   const ScanWs ws = carve(d, workspace, true);
   hipStream_t st = (hipStream_t)stream;

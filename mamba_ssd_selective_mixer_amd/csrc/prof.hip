@@ -13,7 +13,7 @@
 
 namespace ssd {
 
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 
 namespace {
 
@@ -48,7 +48,7 @@ void release() {
 
 void prof_record(hipStream_t st, int kid, bool begin) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_prof_on || kid < 0 || kid >= KID_COUNT) return;
+  if (!g_prof_on.load(std::memory_order_relaxed) || kid < 0 || kid >= KID_COUNT) return;
   if (begin) {
     if (g_used >= g_slots.size()) {
       g_overflow = true;
@@ -92,13 +92,13 @@ int ssd_profile_start(int capacity) {
   }
   for (int k = 0; k < KID_COUNT; ++k) g_open[k] = -1;
   g_overflow = false;
-  g_prof_on = true;
+  g_prof_on.store(true, std::memory_order_release);
   return SSD_OK;
 }
 
 int ssd_profile_stop(void) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_prof_on = false;
+  g_prof_on.store(false, std::memory_order_release);
   return g_overflow ? SSD_ERR_WORKSPACE : SSD_OK;
 }
 

@@ -5,6 +5,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 namespace ssd {
 
 // Kernel identifiers; the order matches ssd_kernel_id in the public header.
@@ -22,7 +24,8 @@ enum KernelId {
   KID_COUNT
 };
 
-extern bool g_prof_on;
+// switched by ssd_profile_start / _stop, possibly from another thread
+extern std::atomic<bool> g_prof_on;
 void prof_record(hipStream_t st, int kid, bool begin);
 
 // Brackets the launches in its scope with a pair of events when timing is on.
@@ -30,10 +33,10 @@ struct ProfScope {
   hipStream_t st;
   int kid;
   ProfScope(hipStream_t s, int k) : st(s), kid(k) {
-    if (g_prof_on) prof_record(st, kid, true);
+    if (g_prof_on.load(std::memory_order_acquire)) prof_record(st, kid, true);
   }
   ~ProfScope() {
-    if (g_prof_on) prof_record(st, kid, false);
+    if (g_prof_on.load(std::memory_order_acquire)) prof_record(st, kid, false);
   }
 };
 

@@ -90,9 +90,62 @@ def _tok_stride(t, inner: int, name: str) -> int:
 
 
 def _need_cuda(*ts):
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("all tensors must be device (HIP) tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
+
+
+def _want(t, name: str, dtype, numel: int, contiguous: bool = True, optional: bool = False):
+    """Check a tensor argument: dtype, element count and (by default) dense
+    layout; the C ABI reads exactly numel elements from the base pointer."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _want_rows(t, name: str, dtype, B: int, L: int, width: int) -> int:
+    """A [B, L, ...] token view whose trailing `width` elements are dense;
+    returns its token stride."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.dim() < 3 or t.shape[0] != B or t.shape[1] != L:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected [{B}, {L}, ...]")
+    n = 1
+    for k in t.shape[2:]:
+        n *= k
+    if n != width:
+        raise ValueError(f"{name}: rows of {n} elements, expected {width}")
+    return _tok_stride(t, width, name)
+
+
+def _want_ws(ws, need: int):
+    if ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace of {ws.numel()} bytes, {need} needed")
+
+
+def _alloc(stream, fn):
+    """Allocate on the stream the call runs on, so the caching allocator
+    never hands the memory to other work while the call's kernels run."""
+    if stream is None:
+        return fn()
+    with torch.cuda.stream(stream):
+        return fn()
 
 
 # ---------------------------------------------------------------- host logic
@@ -125,29 +178,49 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def ssd_conv1d(d: SSDDims, xbc, w, bias=None, conv_state_in=None, conv_state_out=None,
                out=None, stream=None):
-    _need_cuda(xbc, w, bias, conv_state_in, conv_state_out, out)
-    C = d.channels
+    C, io = d.channels, d.io_dtype
+    xs = _want_rows(xbc, "xbc", io, d.batch, d.seqlen, C)
+    _want(w, "w", io, C * d.conv_width)
+    _want(bias, "bias", io, C, optional=True)
+    ns = d.batch * (d.conv_width - 1) * C
+    _want(conv_state_in, "conv_state_in", io, ns, optional=True)
+    _want(conv_state_out, "conv_state_out", io, ns, optional=True)
     if out is None:
-        out = torch.empty(d.batch, d.seqlen, C, dtype=d.io_dtype, device=xbc.device)
-    rc = _lib.load().ssd_conv1d(ctypes.byref(d.c()), _p(xbc), _tok_stride(xbc, C, "xbc"), _p(w),
-                                _p(bias), _p(conv_state_in), _p(conv_state_out), _p(out),
-                                _tok_stride(out, C, "out"), _stream(stream))
+        out = _alloc(stream, lambda: torch.empty(d.batch, d.seqlen, C, dtype=io,
+                                                 device=xbc.device))
+    os_ = _want_rows(out, "out", io, d.batch, d.seqlen, C)
+    _need_cuda(xbc, w, bias, conv_state_in, conv_state_out, out)
+    rc = _lib.load().ssd_conv1d(ctypes.byref(d.c()), _p(xbc), xs, _p(w), _p(bias),
+                                _p(conv_state_in), _p(conv_state_out), _p(out), os_,
+                                _stream(stream))
     _check(rc, "ssd_conv1d")
     return out
 
 
 def ssd_chunk_scan(d: SSDDims, x, dt, A, D, Bm, Cm, z=None, norm_w=None, eps=1e-5,
                    ssm_state_in=None, ssm_state_out=None, y=None, ws=None, stream=None):
-    _need_cuda(x, dt, A, D, Bm, Cm, z, norm_w, ssm_state_in, ssm_state_out, y, ws)
-    xs = _tok_stride(x, d.hp, "x")
-    bs = _tok_stride(Bm, d.ngroups * d.dstate, "Bm")
-    if _tok_stride(Cm, d.ngroups * d.dstate, "Cm") != bs:
+    io, f32 = d.io_dtype, torch.float32
+    B, L, H = d.batch, d.seqlen, d.nheads
+    xs = _want_rows(x, "x", io, B, L, d.hp)
+    bs = _want_rows(Bm, "Bm", io, B, L, d.ngroups * d.dstate)
+    if _want_rows(Cm, "Cm", io, B, L, d.ngroups * d.dstate) != bs:
         raise ValueError("Bm and Cm must share one token stride")
+    _want(dt, "dt", io, B * L * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(z, "z", io, B * L * d.hp, optional=True)
+    _want(norm_w, "norm_w", io, d.hp, optional=z is None)
+    ns = B * H * d.headdim * d.dstate
+    _want(ssm_state_in, "ssm_state_in", f32, ns, optional=True)
+    _want(ssm_state_out, "ssm_state_out", f32, ns, optional=True)
     if y is None:
-        y = torch.empty(d.batch, d.seqlen, d.hp, dtype=d.io_dtype, device=x.device)
+        y = _alloc(stream, lambda: torch.empty(B, L, d.hp, dtype=io, device=x.device))
+    _want(y, "y", io, B * L * d.hp)
     need = ssd_chunk_scan_workspace_bytes(d)
     if ws is None:
-        ws = workspace(need, x.device)
+        ws = _alloc(stream, lambda: workspace(need, x.device))
+    _want_ws(ws, need)
+    _need_cuda(x, dt, A, D, Bm, Cm, z, norm_w, ssm_state_in, ssm_state_out, y, ws)
     rc = _lib.load().ssd_chunk_scan(ctypes.byref(d.c()), _p(x), xs, _p(dt), _p(A), _p(D), _p(Bm),
                                     _p(Cm), bs, _p(z), _p(norm_w), float(eps), _p(ssm_state_in),
                                     _p(ssm_state_out), _p(y), _p(ws), ws.numel(), _stream(stream))
@@ -156,9 +229,14 @@ def ssd_chunk_scan(d: SSDDims, x, dt, A, D, Bm, Cm, z=None, norm_w=None, eps=1e-
 
 
 def ssd_gated_rmsnorm(d: SSDDims, y, z, w, eps=1e-5, out=None, stream=None):
-    _need_cuda(y, z, w, out)
+    io, n = d.io_dtype, d.batch * d.seqlen * d.hp
+    _want(y, "y", io, n)
+    _want(z, "z", io, n)
+    _want(w, "w", io, d.hp)
     if out is None:
-        out = torch.empty_like(y)
+        out = _alloc(stream, lambda: torch.empty_like(y))
+    _want(out, "out", io, n)
+    _need_cuda(y, z, w, out)
     rc = _lib.load().ssd_gated_rmsnorm(ctypes.byref(d.c()), _p(y), _p(z), _p(w), float(eps),
                                        _p(out), _stream(stream))
     _check(rc, "ssd_gated_rmsnorm")
@@ -167,9 +245,22 @@ def ssd_gated_rmsnorm(d: SSDDims, y, z, w, eps=1e-5, out=None, stream=None):
 
 def ssd_decode_step(d: SSDDims, xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, eps,
                     conv_state, ssm_state, y_t=None, stream=None):
-    _need_cuda(xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state, y_t)
+    io, f32 = d.io_dtype, torch.float32
+    B, H, C = d.batch, d.nheads, d.channels
+    _want(xbc_t, "xbc_t", io, B * C)
+    _want(z_t, "z_t", io, B * d.hp, optional=True)
+    _want(dt_t, "dt_t", io, B * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp, optional=z_t is None)
+    _want(conv_state, "conv_state", io, B * (d.conv_width - 1) * C)
+    _want(ssm_state, "ssm_state", f32, B * H * d.headdim * d.dstate)
     if y_t is None:
-        y_t = torch.empty(d.batch, d.hp, dtype=d.io_dtype, device=xbc_t.device)
+        y_t = _alloc(stream, lambda: torch.empty(B, d.hp, dtype=io, device=xbc_t.device))
+    _want(y_t, "y_t", io, B * d.hp)
+    _need_cuda(xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, conv_state, ssm_state, y_t)
     rc = _lib.load().ssd_decode_step(ctypes.byref(d.c()), _p(xbc_t), _p(z_t), _p(dt_t), _p(A),
                                      _p(D), _p(conv_w), _p(conv_b), _p(norm_w), float(eps),
                                      _p(conv_state), _p(ssm_state), _p(y_t), _stream(stream))
@@ -180,13 +271,30 @@ def ssd_decode_step(d: SSDDims, xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, 
 def ssd_mixer_prefill(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps=1e-5,
                       conv_state_in=None, conv_state_out=None, ssm_state_in=None,
                       ssm_state_out=None, out=None, ws=None, stream=None):
-    _need_cuda(xbc, z, dt, A, D, conv_w, conv_b, norm_w, conv_state_in, conv_state_out,
-               ssm_state_in, ssm_state_out, out, ws)
+    io, f32 = d.io_dtype, torch.float32
+    B, L, H, C = d.batch, d.seqlen, d.nheads, d.channels
+    _want(xbc, "xbc", io, B * L * C)
+    _want(z, "z", io, B * L * d.hp, optional=True)
+    _want(dt, "dt", io, B * L * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp, optional=z is None)
+    ncs, nss = B * (d.conv_width - 1) * C, B * H * d.headdim * d.dstate
+    _want(conv_state_in, "conv_state_in", io, ncs, optional=True)
+    _want(conv_state_out, "conv_state_out", io, ncs, optional=True)
+    _want(ssm_state_in, "ssm_state_in", f32, nss, optional=True)
+    _want(ssm_state_out, "ssm_state_out", f32, nss, optional=True)
     if out is None:
-        out = torch.empty(d.batch, d.seqlen, d.hp, dtype=d.io_dtype, device=xbc.device)
+        out = _alloc(stream, lambda: torch.empty(B, L, d.hp, dtype=io, device=xbc.device))
+    _want(out, "out", io, B * L * d.hp)
     need = ssd_mixer_prefill_workspace_bytes(d)
     if ws is None:
-        ws = workspace(need, xbc.device)
+        ws = _alloc(stream, lambda: workspace(need, xbc.device))
+    _want_ws(ws, need)
+    _need_cuda(xbc, z, dt, A, D, conv_w, conv_b, norm_w, conv_state_in, conv_state_out,
+               ssm_state_in, ssm_state_out, out, ws)
     rc = _lib.load().ssd_mixer_prefill(ctypes.byref(d.c()), _p(xbc), _p(z), _p(dt), _p(A), _p(D),
                                        _p(conv_w), _p(conv_b), _p(norm_w), float(eps),
                                        _p(conv_state_in), _p(conv_state_out), _p(ssm_state_in),

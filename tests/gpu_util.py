@@ -38,20 +38,3 @@ def check(name: str, got, ref, tol: float):
         f"{name}: |gpu-ref| beyond {tol} at flat index {i}: gpu {got.flat[i]:.6g} ref "
         f"{ref.flat[i]:.6g} (max abs {max_abs:.3e}, max rel {max_rel:.3e})")
     return max_abs, max_rel
-
-
-def check_head_scaled(name: str, got, ref, tol: float, P: int):
-    """|gpu - ref| <= tol * (1 + max |ref| over the element's head at that
-    token). Used where the outputs reach magnitudes well above 1 and bf16
-    operands bound the error by the size of the summed terms, not of their
-    (possibly cancelling) sum."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape
-    lead = ref.shape[:-1]
-    scale = np.abs(ref.reshape(*lead, -1, P)).max(-1, keepdims=True)
-    scale = np.broadcast_to(scale, (*lead, ref.shape[-1] // P, P)).reshape(ref.shape)
-    excess = np.abs(got - ref) - tol * (1.0 + scale)
-    i = int(np.argmax(excess))
-    assert excess.flat[i] <= 0, (f"{name}: beyond {tol} x head scale at {i}: gpu {got.flat[i]:.6g} "
-                                 f"ref {ref.flat[i]:.6g} scale {scale.flat[i]:.3g}")

@@ -211,3 +211,97 @@ def test_kernel_names_and_profile_arguments(lib):
     assert lib.ssd_profile_read(0, None, ctypes.byref(ms)) == -1
     assert lib.ssd_profile_read(0, ctypes.byref(n), ctypes.byref(ms)) == 0 and n.value == 0
     assert lib.ssd_profile_start(0) == -2
+
+
+# Every buffer a call writes against every other buffer it touches: placed
+# at the same address (or, for its in-place twin, 256 bytes into it) the
+# call must return SSD_ERR_ALIAS before any launch. Addresses are fake and
+# never dereferenced.
+_ALIAS = -5
+
+
+def _alias_cases(buffers, written, twins):
+    cases = []
+    for w in written:
+        for o in buffers:
+            if o == w:
+                continue
+            cases.append((w, o, 256 if twins.get(w) == o else 0))
+    return cases
+
+
+_PREFILL_BUFS = ("xbc", "z", "dt", "A", "D", "cw", "cb", "nw", "cs_in", "cs_out", "ss_in",
+                 "ss_out", "out", "ws")
+_PREFILL_W = ("cs_out", "ss_out", "out", "ws")
+_PREFILL_TWINS = {"cs_out": "cs_in", "ss_out": "ss_in"}
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_PREFILL_BUFS, _PREFILL_W, _PREFILL_TWINS))
+def test_prefill_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
+    a = {k: (i + 1) << 36 for i, k in enumerate(_PREFILL_BUFS)}
+    a[w] = a[o] + off
+    rc = lib.ssd_mixer_prefill(ctypes.byref(d), *(V(a[k]) for k in _PREFILL_BUFS[:8]), 1e-5,
+                               *(V(a[k]) for k in _PREFILL_BUFS[8:]), need, None)
+    assert rc == _ALIAS
+
+
+_SCAN_BUFS = ("x", "dt", "A", "D", "Bm", "Cm", "z", "nw", "ss_in", "ss_out", "y", "ws")
+_SCAN_W = ("ss_out", "y", "ws")
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_SCAN_BUFS, _SCAN_W, {"ss_out": "ss_in"}))
+def test_chunk_scan_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
+    a = {k: (i + 1) << 36 for i, k in enumerate(_SCAN_BUFS)}
+    a[w] = a[o] + off
+    rc = lib.ssd_chunk_scan(ctypes.byref(d), V(a["x"]), 4096, V(a["dt"]), V(a["A"]), V(a["D"]),
+                            V(a["Bm"]), V(a["Cm"]), 4096, V(a["z"]), V(a["nw"]), 1e-5,
+                            V(a["ss_in"]), V(a["ss_out"]), V(a["y"]), V(a["ws"]), need, None)
+    assert rc == _ALIAS
+
+
+_DEC_BUFS = ("x", "z", "dt", "A", "D", "cw", "cb", "nw", "cs", "ss", "y")
+_DEC_W = ("cs", "ss", "y")
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_DEC_BUFS, _DEC_W, {}))
+def test_decode_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c4"], seqlen=1)
+    a = {k: (i + 1) << 36 for i, k in enumerate(_DEC_BUFS)}
+    a[w] = a[o] + off
+    rc = lib.ssd_decode_step(ctypes.byref(d), *(V(a[k]) for k in _DEC_BUFS[:8]), 1e-5,
+                             *(V(a[k]) for k in _DEC_BUFS[8:]), None)
+    assert rc == _ALIAS
+
+
+_CONV_BUFS = ("xbc", "w", "bias", "cs_in", "cs_out", "out")
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_CONV_BUFS, ("cs_out", "out"),
+                                                 {"cs_out": "cs_in"}))
+def test_conv1d_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    a = {k: (i + 1) << 36 for i, k in enumerate(_CONV_BUFS)}
+    a[w] = a[o] + off
+    rc = lib.ssd_conv1d(ctypes.byref(d), V(a["xbc"]), 4096, V(a["w"]), V(a["bias"]),
+                        V(a["cs_in"]), V(a["cs_out"]), V(a["out"]), 4096, None)
+    assert rc == _ALIAS
+
+
+@pytest.mark.parametrize("o", ["z", "w"])
+def test_gated_rmsnorm_alias_every_pair(lib, o):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    a = {"y": 1 << 36, "z": 2 << 36, "w": 3 << 36}
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), V(a["y"]), V(a["z"]), V(a["w"]), 1e-5,
+                                 V(a[o]), None) == _ALIAS
+    # out may equal y (in place) but not sit partly over it
+    assert lib.ssd_gated_rmsnorm(ctypes.byref(d), V(a["y"]), V(a["z"]), V(a["w"]), 1e-5,
+                                 V(a["y"] + 256), None) == _ALIAS

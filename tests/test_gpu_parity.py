@@ -6,7 +6,7 @@ Conv states are exact copies and must match bit for bit."""
 import numpy as np
 import pytest
 
-from gpu_util import TOL, check, check_head_scaled, dev, host, torch_dtype
+from gpu_util import TOL, check, dev, host, torch_dtype
 from mamba_ssd_selective_mixer_amd import synth
 from oracle import oracle
 
@@ -142,11 +142,14 @@ def test_chunk_scan_bf16(ops, kw):
 
 
 @pytest.mark.parametrize("Q", [32, 64, 128, 256])
-@pytest.mark.parametrize("dstate", [128, 64])
-def test_chunk_scan_chunk_invariance(ops, Q, dstate):
-    """Every chunk length gives the oracle's answer (the SSD identity on the GPU);
-    d_state 64 runs the generic kernels at the requested chunk length."""
-    scan_case(ops, small("c1", batch=1, seqlen=520, dstate=dstate), True, False, Q=Q)
+@pytest.mark.parametrize("dstate,dtype", [(64, "bf16"), (128, "f32"), (16, "f32")])
+def test_chunk_scan_chunk_invariance(ops, Q, dstate, dtype):
+    """Every chunk length gives the oracle's answer (the SSD identity on the
+    GPU), each run by the generic kernels at the requested chunk length: bf16
+    I/O with d_state 64, and fp32 I/O (1e-4) with the layer's d_state 128 and
+    with 16. (bf16 I/O at head_dim 64 / d_state 128 takes the fused path,
+    whose chunk length is fixed at 128 tokens.)"""
+    scan_case(ops, small("c1", batch=1, seqlen=520, dstate=dstate, dtype=dtype), True, False, Q=Q)
 
 
 @pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=1, seqlen=700))])
@@ -243,10 +246,10 @@ def test_chunk_scan_state_in_place(ops):
 
 
 # ------------------------------------------------------------------- decode
-def decode_case(ops, cfg, steps, with_norm=True):
+def decode_case(ops, cfg, steps, with_norm=True, with_bias=False):
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg, seqlen=1)
-    prm = synth.layer_params(cfg)
+    prm = synth.layer_params(cfg, with_bias=with_bias)
     st = synth.initial_states(cfg)
     cs, ss = dev(st["conv_state"], td), dev(st["ssm_state"])
     rcs, rss = st["conv_state"].astype(np.float64), st["ssm_state"].astype(np.float64)
@@ -256,10 +259,11 @@ def decode_case(ops, cfg, steps, with_norm=True):
         y = ops.ssd_decode_step(d, dev(inp["xbc_t"], td),
                                 dev(inp["z_t"], td) if with_norm else None,
                                 dev(inp["dt_t"], td), dev(prm["A"]), dev(prm["D"]),
-                                dev(prm["conv_w"], td), None, dev(prm["norm_w"], td), prm["eps"],
-                                cs, ss)
+                                dev(prm["conv_w"], td), dev(prm["conv_b"], td),
+                                dev(prm["norm_w"], td), prm["eps"], cs, ss)
         ro, rcs, rss = oracle.decode_step(inp["xbc_t"], inp["z_t"] if with_norm else None,
-                                          inp["dt_t"], prm["A"], prm["D"], prm["conv_w"], None,
+                                          inp["dt_t"], prm["A"], prm["D"], prm["conv_w"],
+                                          prm["conv_b"],
                                           prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim,
                                           cfg.ngroups, cfg.dstate, rcs, rss)
         check(f"decode out step {k}", host(y), ro, tol)
@@ -275,6 +279,19 @@ def test_decode_fp32_tiny(ops):
 
 def test_decode_fp32_no_norm(ops):
     decode_case(ops, synth.replace(synth.CONFIGS["c0"], batch=2), steps=2, with_norm=False)
+
+
+# Decode with a conv bias: fp32 tiny shapes and bf16 shapes of the decode
+# loop's layer (256 heads in 8 groups, state 128), gate on and off.
+@pytest.mark.parametrize("base,kw,norm", [
+    ("c0", dict(batch=3), True),
+    ("c0", dict(batch=2, nheads=8, ngroups=2, headdim=32, dstate=64, conv_width=3), False),
+    ("c4", dict(batch=4), True),
+    ("c4", dict(batch=3), False),
+    ("c4", dict(batch=2, nheads=32, dstate=64, conv_width=2), True)])
+def test_decode_conv_bias(ops, base, kw, norm):
+    decode_case(ops, synth.replace(synth.CONFIGS[base], **kw), steps=4, with_norm=norm,
+                with_bias=True)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=4), dict(batch=2, nheads=32, dstate=64),
@@ -331,10 +348,7 @@ def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False,
         outs.append(host(out))
         cs, ss = cs2, ss2
     tol = TOL[cfg.dtype]
-    if with_bias and not with_norm and cfg.dtype == "bf16":
-        check_head_scaled("prefill y", np.concatenate(outs, axis=1), ref["out"], tol, cfg.headdim)
-    else:
-        check("prefill out", np.concatenate(outs, axis=1), ref["out"], tol)
+    check("prefill out", np.concatenate(outs, axis=1), ref["out"], tol)
     check("prefill final state", host(ss), ref["s_out"], tol)
     assert np.array_equal(host(cs), ref["conv_out"])
 
@@ -360,14 +374,10 @@ def test_prefill_bf16_shapes(ops, kw):
 
 @pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333), dict(batch=3, seqlen=129)])
 def test_prefill_bf16_conv_bias(ops, kw):
-    """With a conv bias the whole prefill is checked before the norm (z = None),
-    with the tolerance scaled by the head's largest |y| at that token. bf16 B
-    and C carrying a shared bias offset make C.B^T sums whose operand rounding
-    no longer averages out and y reaches |16|; the error is then bounded by
-    the size of the summed terms, and after normalising by a small group RMS
-    it exceeds 2e-2 in rare elements for any bf16-operand kernel (shown by
-    emulating the rounding points on the CPU). Bias with the norm is checked
-    elementwise at fp32 I/O in test_prefill_fp32_tiny_state_bias."""
+    """With a conv bias the whole prefill is checked before the norm (z = None):
+    every element of y within 2e-2 + 2e-2 |ref|. The bias shifts B and C by a
+    shared offset, so C.B^T sums of O(16) partly cancel; the fp16 operands and
+    the fp32 conv intermediate keep that within the tolerance."""
     prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=False)
 
 
