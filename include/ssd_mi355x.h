@@ -61,7 +61,7 @@
  *
  * Supported envelope: batch >= 1, seqlen >= 1 (any length; the last chunk
  * may be short), nheads % ngroups == 0, headdim in {16, 32, 64, 128},
- * dstate in {16, 32, 64, 128}, conv_width in {2, 3, 4},
+ * dstate in {16, 32, 64, 128, 256}, conv_width in {2, 3, 4},
  * chunk in {32, 64, 128, 256}.
  *
  * Precision. State, decay exponents, sums and the norm are fp32. The dense
@@ -71,9 +71,12 @@
  * states; in the fast path, used for bf16 I/O with headdim 64, dstate 128,
  * heads per group a multiple of 4, dims->chunk >= 64 and conv width 4 when
  * the call includes the conv, also the chunk states, and D x taken from x at
- * fp16 hi + lo precision). Such operands must stay within fp16 range (|v| < 65504):
- * activations after SiLU, dt-weighted states of magnitude beyond that are
- * outside the fast path's envelope. In the fast path the chunk length is an
+ * fp16 hi + lo precision). Those fp16 intermediates (activations after SiLU,
+ * C B^T, chunk states, carried-in states, the scan output before the norm)
+ * must stay within fp16 range (|v| < 65504); a value beyond it becomes
+ * infinite, so the output or final state is not finite and
+ * ssd_workspace_status() reports SSD_ERR_NONFINITE for the call. With
+ * SSD_FLAG_FP32_OPERANDS every intermediate is fp32 (no such limit). In the fast path the chunk length is an
  * internal choice (128 tokens); the result does not depend on dims->chunk
  * beyond rounding. The fast path fuses the gated norm into its chunk-output
  * kernel, also when a norm group spans several (up to 32) of that kernel's
@@ -81,7 +84,8 @@
  * workspace, which needs the group's blocks to run concurrently (a stream
  * with the whole GPU qualifies: 512 resident workgroups, 64 per XCD, against
  * at most 31 waiting per XCD). A wait that cannot complete writes NaN rows
- * after a bounded time instead of hanging. Wider norm groups are normalised
+ * after a bounded time instead of hanging and records SSD_ERR_TIMEOUT for
+ * ssd_workspace_status(). Wider norm groups are normalised
  * by a separate pass over the scan output.
  */
 #ifndef SSD_MI355X_H
@@ -103,10 +107,20 @@ typedef enum {
   SSD_ERR_ALIAS = -5,       /* input/output buffers partially overlap        */
   SSD_ERR_WORKSPACE = -6,   /* workspace NULL, misaligned or too small       */
   SSD_ERR_HIP = -7,         /* the HIP runtime refused a launch              */
-  SSD_ERR_ALIGN = -8        /* pointer or stride breaks the 16-byte rule     */
+  SSD_ERR_ALIGN = -8,       /* pointer or stride breaks the 16-byte rule     */
+  SSD_ERR_TIMEOUT = -9,     /* (ssd_workspace_status) a cross-workgroup norm
+                               exchange gave up waiting; its rows are NaN    */
+  SSD_ERR_NONFINITE = -10   /* (ssd_workspace_status) an output or the final
+                               SSM state is infinite or NaN                  */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* ssd_dims.flags. SSD_FLAG_FP32_OPERANDS: run the chunked scan's dense
+ * contractions on fp32 MFMA operands for bf16 I/O as well (every
+ * intermediate keeps fp32 range; the general kernels are used, not the fused
+ * ones). Unknown bits are refused (SSD_ERR_UNSUPPORTED). */
+enum { SSD_FLAG_FP32_OPERANDS = 1 };
 
 typedef struct {
   int32_t batch;      /* B: sequences                                        */
@@ -118,6 +132,7 @@ typedef struct {
   int32_t conv_width; /* W                                                   */
   int32_t chunk;      /* Q: chunk length of the block decomposition          */
   int32_t io_dtype;   /* ssd_dtype                                           */
+  int32_t flags;      /* SSD_FLAG_* bits, 0 by default                       */
 } ssd_dims;
 
 /* Conv channels Cch = H*P + 2*G*N. */
@@ -213,6 +228,30 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z,
                       void* conv_state_out, const float* ssm_state_in,
                       float* ssm_state_out, void* out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/*
+ * Status of the chunk-scan or mixer-prefill call that last used `workspace`
+ * (a device pointer, the workspace passed to that call). Conditions that
+ * depend on the data, and so cannot be checked before the launch, are
+ * recorded by the kernels in the first word of the workspace; this call
+ * copies that word to the host on `stream` and waits for the stream, so it
+ * sees the call once it has completed. Returns SSD_OK, SSD_ERR_TIMEOUT (a
+ * cross-workgroup norm exchange gave up; the affected rows are NaN; see the
+ * fast path under "Precision" above) or SSD_ERR_NONFINITE (an output row or
+ * the final SSM state is infinite or NaN: a non-finite input, or, in the
+ * fused path, an fp16 intermediate beyond its range -- repeat the call with
+ * SSD_FLAG_FP32_OPERANDS). SSD_ERR_HIP if the copy fails.
+ */
+int ssd_workspace_status(const void* workspace, void* stream);
+
+/*
+ * Diagnostic: set the bound on the polls of the fused path's cross-workgroup
+ * norm exchange (default 2^20) for launches made after the call, process
+ * wide. 0 makes every such wait give up at once (every kernel still exits
+ * normally, the rows are NaN and the status is SSD_ERR_TIMEOUT). Returns the
+ * previous bound, or SSD_ERR_SHAPE for a negative one.
+ */
+int ssd_set_exchange_spin_limit(int polls);
 
 /*
  * Per-kernel timing of the library's own launches, a measurement aid (the

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ssd_mi355x.h"
 #include "launch.hpp"
 
@@ -17,6 +19,9 @@ constexpr size_t kLdsPerCU = 160 * 1024;
 constexpr size_t kWsAlign = 256;
 
 size_t esize(const ssd_dims* d) { return d->io_dtype == SSD_BF16 ? 2 : 4; }
+bool f32op(const ssd_dims* d) { return (d->flags & SSD_FLAG_FP32_OPERANDS) != 0; }
+// bound on the polls of the fast path's cross-block norm exchange
+std::atomic<int> g_spin_limit{1 << 20};
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool is_one_of(int v, std::initializer_list<int> set) {
   for (int s : set)
@@ -67,12 +72,13 @@ bool aliased(std::initializer_list<Range> list) {
 int check_dims(int entry, const ssd_dims* d) {
   if (!d) return SSD_ERR_NULL;
   if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+  if (d->flags & ~SSD_FLAG_FP32_OPERANDS) return SSD_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->ngroups < 1 ||
       d->dstate < 1)
     return SSD_ERR_SHAPE;
   if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
   if (!is_one_of(d->headdim, {16, 32, 64, 128})) return SSD_ERR_UNSUPPORTED;
-  if (!is_one_of(d->dstate, {16, 32, 64, 128})) return SSD_ERR_UNSUPPORTED;
+  if (!is_one_of(d->dstate, {16, 32, 64, 128, 256})) return SSD_ERR_UNSUPPORTED;
   if (d->batch > 65535 || d->nheads > 65535) return SSD_ERR_UNSUPPORTED;
   const bool conv = entry == SSD_ENTRY_CONV1D || entry == SSD_ENTRY_DECODE_STEP ||
                     entry == SSD_ENTRY_MIXER_PREFILL;
@@ -85,7 +91,8 @@ int check_dims(int entry, const ssd_dims* d) {
   if (scan) {
     if (d->chunk < 1) return SSD_ERR_SHAPE;
     if (!is_one_of(d->chunk, {32, 64, 128, 256})) return SSD_ERR_UNSUPPORTED;
-    if (ssd::scan_lds_bytes(d->io_dtype == SSD_BF16, d->headdim, d->dstate, d->chunk) >
+    if (ssd::scan_lds_bytes(d->io_dtype == SSD_BF16 && !f32op(d), d->headdim, d->dstate,
+                            d->chunk) >
         kLdsPerCU - 8192)
       return SSD_ERR_UNSUPPORTED;
   }
@@ -102,6 +109,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
 struct ScanWs {
   bool fast;
+  int* status;
   float* states;
   float* lam_end;
   float* y32;
@@ -111,8 +119,8 @@ struct ScanWs {
 };
 
 bool use_fast(const ssd_dims* d, bool conv) {
-  return ssd::fast_path_ok(d->io_dtype == SSD_BF16, d->headdim, d->dstate, d->nheads, d->ngroups,
-                           d->chunk, d->conv_width, conv);
+  return !f32op(d) && ssd::fast_path_ok(d->io_dtype == SSD_BF16, d->headdim, d->dstate,
+                                        d->nheads, d->ngroups, d->chunk, d->conv_width, conv);
 }
 
 // Workspace layout for the scan (conv = the scan consumes raw xBC rows).
@@ -127,6 +135,7 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
     return o;
   };
   w.fast = use_fast(d, conv);
+  const size_t o_status = take(4);  // the call's status word (ssd_workspace_status)
   size_t o_states = 0, o_lam = 0, o_y = 0, o_conv = 0, o_fast = 0;
   if (w.fast) {
     o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads, d->ngroups, conv));
@@ -139,6 +148,7 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   w.total = off;
   if (base) {
     unsigned char* p = (unsigned char*)base;
+    w.status = (int*)(p + o_status);
     if (w.fast) {
       w.fastws = p + o_fast;
     } else {
@@ -159,15 +169,16 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
   const bool bf = d->io_dtype == SSD_BF16;
   ssd::ScanShape s{d->batch, d->seqlen, d->nheads, d->headdim, d->ngroups,
                    d->dstate, d->chunk, (int)nchunks(d)};
-  int rc = hip_status(
-      ssd::launch_chunk_state(bf, x_f32, s, x, xs, dt, A, Bm, bs, ws.states, ws.lam_end, st));
+  const bool fo = f32op(d);
+  int rc = hip_status(ssd::launch_chunk_state(bf, x_f32, fo, s, x, xs, dt, A, Bm, bs, ws.states,
+                                              ws.lam_end, ws.status, st));
   if (rc) return rc;
-  rc = hip_status(ssd::launch_state_pass(s, ws.states, ws.lam_end, s_in, s_out, st));
+  rc = hip_status(ssd::launch_state_pass(s, ws.states, ws.lam_end, s_in, s_out, ws.status, st));
   if (rc) return rc;
   const bool fused_norm = z != nullptr;
   void* ydst = fused_norm ? (void*)ws.y32 : y;
-  rc = hip_status(ssd::launch_chunk_out(bf, x_f32, s, x, xs, dt, A, D, Bm, Cm, bs, ws.states, ydst,
-                                        fused_norm || !bf, st));
+  rc = hip_status(ssd::launch_chunk_out(bf, x_f32, fo, s, x, xs, dt, A, D, Bm, Cm, bs, ws.states,
+                                        ydst, fused_norm || !bf, ws.status, st));
   if (rc) return rc;
   if (fused_norm)
     rc = hip_status(ssd::launch_gated_norm(bf, true, d->batch * d->seqlen,
@@ -205,6 +216,8 @@ int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const 
   a.s_out = s_out;
   a.y = y;
   a.ws = ws.fastws;
+  a.status = ws.status;
+  a.spin_max = g_spin_limit.load(std::memory_order_relaxed);
   return hip_status(ssd::launch_fast_scan(a, st));
 }
 
@@ -238,6 +251,8 @@ const char* ssd_status_str(int status) {
     case SSD_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case SSD_ERR_HIP: return "HIP runtime error at launch";
     case SSD_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case SSD_ERR_TIMEOUT: return "a cross-workgroup norm exchange gave up waiting";
+    case SSD_ERR_NONFINITE: return "an output or the final state is not finite";
     default: return "unknown status";
   }
 }
@@ -444,6 +459,24 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
   const unsigned char* v = ws.conv;
   return run_scan(d, v, C, dt, A, D, v + HP * 4, v + (HP + GN) * 4, C, true, z, norm_w, eps,
                   ssm_state_in, ssm_state_out, out, ws, st);
+}
+
+int ssd_workspace_status(const void* workspace, void* stream) {
+  if (!workspace) return SSD_ERR_NULL;
+  if ((uintptr_t)workspace % kWsAlign) return SSD_ERR_WORKSPACE;
+  int word = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return SSD_ERR_HIP;
+  if (word & 1) return SSD_ERR_TIMEOUT;
+  if (word & 2) return SSD_ERR_NONFINITE;
+  return SSD_OK;
+}
+
+int ssd_set_exchange_spin_limit(int polls) {
+  if (polls < 0) return SSD_ERR_SHAPE;
+  return g_spin_limit.exchange(polls);
 }
 
 }  // extern "C"

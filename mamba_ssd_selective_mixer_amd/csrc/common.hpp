@@ -173,6 +173,7 @@ template <> struct Mfma<float> {
   }
   static SSD_DEV frag ld(const float* p) { return *p; }
   static SSD_DEV frag ldg(const float* p) { return *p; }
+  static SSD_DEV frag ldg(const bf16* p) { return (float)*p; }
   static SSD_DEV frag cvt(const float* p) { return *p; }
 };
 

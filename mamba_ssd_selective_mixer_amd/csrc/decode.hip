@@ -203,7 +203,8 @@ static hipError_t decode_dispatch(int B, int H, int P, int G, int N, int W, cons
     case 16: SSD_DEC_W(16); break;
     case 32: SSD_DEC_W(32); break;
     case 64: SSD_DEC_W(64); break;
-    default: SSD_DEC_W(128); break;
+    case 128: SSD_DEC_W(128); break;
+    default: SSD_DEC_W(256); break;
   }
 #undef SSD_DEC_W
 #undef SSD_DEC

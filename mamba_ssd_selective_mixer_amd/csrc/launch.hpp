@@ -32,15 +32,19 @@ hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
                          hipStream_t st);
 // Chunked scan, three phases: chunk states, state passing, chunk outputs.
 // x_f32: x, B and C are fp32 (else the I/O type); dt and y are the I/O type.
-hipError_t launch_chunk_state(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
-                              int64_t xs, const void* dt, const float* A, const void* Bm,
-                              int64_t bs, float* states, float* lam_end, hipStream_t st);
+// f32op: fp32 MFMA operands for bf16 I/O too (else fp16). status: the call's
+// status word, cleared by the chunk-state kernel; the others set bits in it.
+hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
+                              const void* x, int64_t xs, const void* dt, const float* A,
+                              const void* Bm, int64_t bs, float* states, float* lam_end,
+                              int* status, hipStream_t st);
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
-                             const float* s_in, float* s_out, hipStream_t st);
-hipError_t launch_chunk_out(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
-                            int64_t xs, const void* dt, const float* A, const float* D,
-                            const void* Bm, const void* Cm, int64_t bs, const float* states,
-                            void* y, bool y_f32, hipStream_t st);
+                             const float* s_in, float* s_out, int* status, hipStream_t st);
+hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
+                            const void* x, int64_t xs, const void* dt, const float* A,
+                            const float* D, const void* Bm, const void* Cm, int64_t bs,
+                            const float* states, void* y, bool y_f32, int* status,
+                            hipStream_t st);
 
 }  // namespace ssd
 
@@ -67,6 +71,8 @@ struct FastScanArgs {
   float* s_out;
   void* y;            // [B, L, H*P] bf16: the normalised output (z given) or y
   void* ws;           // fast_ws_bytes(B, L, H, G, conv) bytes, 256-byte aligned
+  int* status;        // the call's status word (cleared by the first kernel)
+  int spin_max;       // bound on the cross-block norm's polls
 };
 bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
 size_t fast_ws_bytes(int B, int L, int H, int G, bool conv);

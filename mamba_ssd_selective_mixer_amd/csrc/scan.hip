@@ -16,6 +16,8 @@
 // finer than bf16's), fp32 operands for fp32 I/O. Decays are always
 // formed as exp(Lam_t - Lam_s) of a masked difference, never as a ratio of
 // exponentials, so they stay finite for any chunk length.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -26,6 +28,11 @@ constexpr int kStateSB = 64;       // tokens staged per block in the chunk-state
 
 template <class T> struct Pad { static constexpr int v = 8; };     // fp16 operands: 16 bytes per LDS row
 template <> struct Pad<float> { static constexpr int v = 4; };
+// MFMA operand type: fp16 for bf16 I/O unless F32OP asks for fp32 operands
+// (fp32 range for every intermediate), fp32 for fp32 I/O.
+template <class T, bool F32OP>
+using OpT = typename std::conditional<F32OP, float, typename OpOf<T>::type>::type;
+constexpr int kStatusNonFinite = 2;  // status bit: an output or the final state is not finite
 
 // Inclusive cumulative sum of a_s = dt_s * A over the chunk (s < len; zero
 // beyond) into lam[], and dt_s into dts[]. Q <= 256 = blockDim.
@@ -49,13 +56,14 @@ __device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, int64_t r
 // ---------------------------------------------------------------------------
 // Phase 1: chunk states dS_k = (w x)^T B per (chunk, head, batch).
 // T: I/O type (dt); TX: element type of x and B (T, or fp32 when they come
-// from the conv's internal fp32 copy).
-template <class T, class TX>
+// from the conv's internal fp32 copy). MAXT: most 16x16 output tiles per wave
+// (P N / 1024 rounded up to 16 or 32; d_state 256 with head_dim 128 needs 32).
+template <class T, class TX, bool F32OP, int MAXT>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
     const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const TX* __restrict__ Bm, int64_t bs, float* __restrict__ states,
-    float* __restrict__ lam_end, int L, int H, int G, int P, int N, int Q, int nc) {
-  typedef typename OpOf<T>::type O;  // MFMA operand type
+    float* __restrict__ lam_end, int* status, int L, int H, int G, int P, int N, int Q, int nc) {
+  typedef OpT<T, F32OP> O;  // MFMA operand type
   using M = Mfma<O>;
   constexpr int KP = kStateSB + Pad<O>::v;
   extern __shared__ __align__(16) unsigned char smraw[];
@@ -68,6 +76,8 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
   const int t0 = c * Q, len = min(Q, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // this call's status word starts clear (later kernels only set bits)
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
 
   chunk_cumsum<T>(dt, row0, H, h, A[h], len, lam, dts, wsum);
   const float lamE = lam[len - 1];
@@ -75,7 +85,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
   __syncthreads();
 
   const int ntn = N / 16, tiles = (P / 16) * ntn;
-  constexpr int kMaxTPW = 16;  // (128/16)*(128/16)/4
+  constexpr int kMaxTPW = MAXT;
   f32x4 acc[kMaxTPW];
 #pragma unroll
   for (int i = 0; i < kMaxTPW; ++i) acc[i] = zero4();
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
 __global__ __launch_bounds__(kScanThreads) void k_state_pass(float* states,
                                                              const float* __restrict__ lam_end,
                                                              const float* s_in, float* s_out,
-                                                             int H, int PN, int nc) {
+                                                             int* status, int H, int PN, int nc) {
   const int e = (blockIdx.x * kScanThreads + threadIdx.x) * 4;
   const int h = blockIdx.y, b = blockIdx.z;
   if (e >= PN) return;
@@ -164,20 +174,23 @@ __global__ __launch_bounds__(kScanThreads) void k_state_pass(float* states,
     S.z = al * S.z + d.z;
     S.w = al * S.w + d.w;
   }
-  if (s_out) *reinterpret_cast<float4*>(s_out + bh * PN + e) = S;
+  if (s_out) {
+    *reinterpret_cast<float4*>(s_out + bh * PN + e) = S;
+    if (S.x * 0.f + S.y * 0.f + S.z * 0.f + S.w * 0.f != 0.f) atomicOr(status, kStatusNonFinite);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Phase 3: chunk outputs. Each wave owns 16-row tiles of the chunk: it forms
 // the causal tiles of M = (C B^T) o exp(Lam_t - Lam_s) in its LDS slab, then
 // y = M (dt x) + exp(Lam_t) C S_in^T + D x for every 16-column tile of P.
-template <class T, class TX, bool YF32>
+template <class T, class TX, bool YF32, bool F32OP>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
     const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ D, const TX* __restrict__ Bm, const TX* __restrict__ Cm, int64_t bs,
-    const float* __restrict__ states, void* __restrict__ yout, int L, int H, int G, int P,
-    int N, int Q, int nc) {
-  typedef typename OpOf<T>::type O;  // MFMA operand type
+    const float* __restrict__ states, void* __restrict__ yout, int* status, int L, int H, int G,
+    int P, int N, int Q, int nc) {
+  typedef OpT<T, F32OP> O;  // MFMA operand type
   using M = Mfma<O>;
   const int QK = Q + Pad<O>::v;
   extern __shared__ __align__(16) unsigned char smraw[];
@@ -218,6 +231,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
   const TX* Cg = Cm + (int64_t)g * N;
   const TX* Bg = Bm + (int64_t)g * N;
   const int nrt = (len + 15) / 16;
+  float chk = 0.f;  // NaN once any output is infinite or NaN
   for (int rt0 = 0; rt0 < nrt; rt0 += 4) {
     const int rt = rt0 + wave;
     const bool active = rt < nrt;
@@ -274,6 +288,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
           if (t < len) {
             const float xv = to_f(x[(row0 + t) * xs + (int64_t)h * P + p]);
             const float yv = acc[r] + fexp(lam[t]) * acc2[r] + Dh * xv;
+            chk += yv * 0.f;
             const int64_t o = (row0 + t) * (int64_t)H * P + (int64_t)h * P + p;
             if (YF32) reinterpret_cast<float*>(yout)[o] = yv;
             else reinterpret_cast<T*>(yout)[o] = from_f<T>(yv);
@@ -283,72 +298,89 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
     }
     __syncthreads();
   }
+  if (chk != 0.f) atomicOr(status, kStatusNonFinite);
 }
 
 // ---------------------------------------------------------------------------
-static size_t state_lds(bool bf, int P, int N) {
-  const int KP = kStateSB + (bf ? 8 : 4);
-  return (size_t)(P + N) * KP * (bf ? 2 : 4);
+// op16: the MFMA operands are fp16 (else fp32)
+static size_t state_lds(bool op16, int P, int N) {
+  const int KP = kStateSB + (op16 ? 8 : 4);
+  return (size_t)(P + N) * KP * (op16 ? 2 : 4);
 }
-static size_t out_lds(bool bf, int P, int Q) {
-  const int QK = Q + (bf ? 8 : 4);
-  return (size_t)(P + 4 * 16) * QK * (bf ? 2 : 4);
+static size_t out_lds(bool op16, int P, int Q) {
+  const int QK = Q + (op16 ? 8 : 4);
+  return (size_t)(P + 4 * 16) * QK * (op16 ? 2 : 4);
 }
 
-hipError_t launch_chunk_state(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
-                              int64_t xs, const void* dt, const float* A, const void* Bm,
-                              int64_t bs, float* states, float* lam_end, hipStream_t st) {
+hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
+                              const void* x, int64_t xs, const void* dt, const float* A,
+                              const void* Bm, int64_t bs, float* states, float* lam_end,
+                              int* status, hipStream_t st) {
   ProfScope ps(st, KID_CHUNK_STATE);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
-  const size_t lds = state_lds(io_bf16, s.P, s.N);
-#define SSD_STATE(TT, TX)                                                                      \
-  hipLaunchKernelGGL((k_chunk_state<TT, TX>), grid, block, lds, st, (const TX*)x, xs,           \
-                     (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, s.L, s.H, s.G, s.P,  \
-                     s.N, s.Q, s.nc)
-  if (!io_bf16) SSD_STATE(float, float);
-  else if (x_f32) SSD_STATE(bf16, float);
-  else SSD_STATE(bf16, bf16);
+  const size_t lds = state_lds(io_bf16 && !f32op, s.P, s.N);
+  const bool t32 = s.P * s.N > 16 * 1024;  // tiles per wave beyond 16
+#define SSD_STATE_T(TT, TX, F, T)                                                              \
+  hipLaunchKernelGGL((k_chunk_state<TT, TX, F, T>), grid, block, lds, st, (const TX*)x, xs,     \
+                     (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, status, s.L, s.H,    \
+                     s.G, s.P, s.N, s.Q, s.nc)
+#define SSD_STATE(TT, TX, F) \
+  if (t32) SSD_STATE_T(TT, TX, F, 32); else SSD_STATE_T(TT, TX, F, 16)
+  if (!io_bf16) {
+    SSD_STATE(float, float, true);
+  } else if (x_f32) {
+    if (f32op) { SSD_STATE(bf16, float, true); }
+    else { SSD_STATE(bf16, float, false); }
+  } else {
+    if (f32op) { SSD_STATE(bf16, bf16, true); }
+    else { SSD_STATE(bf16, bf16, false); }
+  }
 #undef SSD_STATE
+#undef SSD_STATE_T
   return hipGetLastError();
 }
 
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
-                             const float* s_in, float* s_out, hipStream_t st) {
+                             const float* s_in, float* s_out, int* status, hipStream_t st) {
   ProfScope ps(st, KID_STATE_PASS);
   const int PN = s.P * s.N;
   dim3 grid((PN / 4 + kScanThreads - 1) / kScanThreads, s.H, s.B), block(kScanThreads);
-  hipLaunchKernelGGL(k_state_pass, grid, block, 0, st, states, lam_end, s_in, s_out, s.H, PN,
-                     s.nc);
+  hipLaunchKernelGGL(k_state_pass, grid, block, 0, st, states, lam_end, s_in, s_out, status, s.H,
+                     PN, s.nc);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_out(bool io_bf16, bool x_f32, const ScanShape& s, const void* x,
-                            int64_t xs, const void* dt, const float* A, const float* D,
-                            const void* Bm, const void* Cm, int64_t bs, const float* states,
-                            void* y, bool y_f32, hipStream_t st) {
+hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
+                            const void* x, int64_t xs, const void* dt, const float* A,
+                            const float* D, const void* Bm, const void* Cm, int64_t bs,
+                            const float* states, void* y, bool y_f32, int* status,
+                            hipStream_t st) {
   ProfScope ps(st, KID_CHUNK_OUT);
   dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
-  const size_t lds = out_lds(io_bf16, s.P, s.Q);
-#define SSD_OUT(TT, TX, YF)                                                                     \
-  hipLaunchKernelGGL((k_chunk_out<TT, TX, YF>), grid, block, lds, st, (const TX*)x, xs,         \
-                     (const TT*)dt, A, D, (const TX*)Bm, (const TX*)Cm, bs, states, y, s.L, s.H, \
-                     s.G, s.P, s.N, s.Q, s.nc)
-  if (!io_bf16) SSD_OUT(float, float, true);
+  const size_t lds = out_lds(io_bf16 && !f32op, s.P, s.Q);
+#define SSD_OUT(TT, TX, YF, F)                                                                  \
+  hipLaunchKernelGGL((k_chunk_out<TT, TX, YF, F>), grid, block, lds, st, (const TX*)x, xs,      \
+                     (const TT*)dt, A, D, (const TX*)Bm, (const TX*)Cm, bs, states, y, status,  \
+                     s.L, s.H, s.G, s.P, s.N, s.Q, s.nc)
+#define SSD_OUT_F(TT, TX, YF) \
+  if (f32op) SSD_OUT(TT, TX, YF, true); else SSD_OUT(TT, TX, YF, false)
+  if (!io_bf16) SSD_OUT(float, float, true, true);
   else if (x_f32) {
-    if (y_f32) SSD_OUT(bf16, float, true);
-    else SSD_OUT(bf16, float, false);
+    if (y_f32) { SSD_OUT_F(bf16, float, true); }
+    else { SSD_OUT_F(bf16, float, false); }
   } else {
-    if (y_f32) SSD_OUT(bf16, bf16, true);
-    else SSD_OUT(bf16, bf16, false);
+    if (y_f32) { SSD_OUT_F(bf16, bf16, true); }
+    else { SSD_OUT_F(bf16, bf16, false); }
   }
+#undef SSD_OUT_F
 #undef SSD_OUT
   return hipGetLastError();
 }
 
 // LDS bytes the two MFMA kernels need for a shape (the host checks these
 // against the 160 KiB of one CU before launching).
-size_t scan_lds_bytes(bool io_bf16, int P, int N, int Q) {
-  const size_t a = state_lds(io_bf16, P, N), b = out_lds(io_bf16, P, Q);
+size_t scan_lds_bytes(bool op16, int P, int N, int Q) {
+  const size_t a = state_lds(op16, P, N), b = out_lds(op16, P, Q);
   return a > b ? a : b;
 }
 

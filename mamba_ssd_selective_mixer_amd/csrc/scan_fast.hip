@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
                                                f16* __restrict__ states,
                                                float* __restrict__ lam_end,
                                                f16* __restrict__ bcv, f16* __restrict__ ccv,
-                                               int L, int H, int G, int nc) {
+                                               int* status, int L, int H, int G, int nc) {
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
@@ -332,6 +332,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
   const int tc = 2 * lane;
+  // this call's status word starts clear (the later kernels of the call only
+  // set bits in it)
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
 
   // Lam = inclusive cumsum of dt A over the chunk for head h0 + wave (flat
   // past len, where dt counts as 0), kept in log2 units so every decay is
@@ -508,12 +511,15 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 constexpr int kParts = 8;          // ticket partitions: block index mod 8, one per XCD
 constexpr float kUnset = -1.0f;    // an unwritten slot: never a sum of squares (nor NaN)
 constexpr int kPassDepth = 8;
+// bits of the call's status word (first word of the workspace)
+constexpr int kStatusTimeout = 1;    // a cross-block norm wait gave up
+constexpr int kStatusNonFinite = 2;  // an output or the final state is not finite
 constexpr int kPassVec = 8;
 __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
                                                f16* __restrict__ sin_h, int* sync, float* part,
-                                               int64_t npart, int H, int nc) {
+                                               int64_t npart, int* status, int H, int nc) {
   constexpr int PN = P * N;
   const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -560,7 +566,13 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
       }
     }
   }
-  if (s_out) store8(s_out + bh * PN + e, S);
+  if (s_out) {
+    store8(s_out + bh * PN + e, S);
+    float chk = 0.f;  // NaN when any element is infinite or NaN
+#pragma unroll
+    for (int j = 0; j < kPassVec; ++j) chk += S[j] * 0.f;
+    if (chk != 0.f) atomicOr(status, kStatusNonFinite);
+  }
 }
 
 // ---------------------------------------------------------------- phase 3
@@ -587,7 +599,6 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
 // current head is computed -> y through an LDS tile to a coalesced epilogue
 // that gates with z (prefetched), normalises each row over its 256 channels
 // and stores 16-byte vectors.
-constexpr int kSpinMax = 1 << 20;  // bound on the polls of the partners' sums
 template <bool CONV, int NM, bool PREC>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
@@ -598,7 +609,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 const bf16* __restrict__ z,
                                                 const bf16* __restrict__ nw, float eps,
                                                 bf16* __restrict__ out, float* part, int* sync,
-                                                int L, int H, int G, int nc) {
+                                                int* status, int spin_max, int L, int H, int G,
+                                                int nc) {
   static_assert(4 * P * RS <= 2 * QI * NS, "two x buffers fit the B/C space");
   static_assert(HB * P * NS == 2 * QI * NS, "the 4 heads' states fill the B/C space");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
@@ -1028,7 +1040,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       const float* gp = part + (int64_t)grp * nb * QI + tid;
       float sq = 0.f;
       bool ok = false;
-      for (int it = 0; it < kSpinMax && !ok; ++it) {
+      for (int it = 0; it < spin_max && !ok; ++it) {
         sq = 0.f;
         ok = true;
 #pragma unroll 8
@@ -1043,6 +1055,10 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       }
       inv_s[tid] = ok ? __builtin_amdgcn_rsqf(sq * (1.0f / (nb * HB * P)) + eps)
                       : __builtin_nanf("");
+      // report a wait that gave up, and rows whose sum of squares is not
+      // finite (an input or an intermediate out of range), in the status word
+      if (!ok) atomicOr(status, kStatusTimeout);
+      else if (tid < len && !(sq < __builtin_huge_valf())) atomicOr(status, kStatusNonFinite);
     }
     __syncthreads();
 #pragma unroll
@@ -1086,6 +1102,8 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
         }
       }
       ss = group_sum_last<16>(ss);
+      if (ev8 == 0 && t < len && !(ss < __builtin_huge_valf()))
+        atomicOr(status, kStatusNonFinite);
       const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / (HB * P)) + eps);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
@@ -1093,6 +1111,14 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
         for (int j = 0; j < 8; ++j) yv[hf][j] *= wv8[hf][j] * inv;
     }
     if (t < len) {
+      if (!NM) {
+        float chk = 0.f;  // NaN when any value is infinite or NaN
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) chk += yv[hf][j] * 0.f;
+        if (chk != 0.f) atomicOr(status, kStatusNonFinite);
+      }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         // streaming store: the output is final (for norm groups of more than
@@ -1188,13 +1214,13 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     const bf16* dt = (const bf16*)a.dt;
     if (prec)
       hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         bcv, ccv, a.L, a.H, a.G, nc);
+                         bcv, ccv, a.status, a.L, a.H, a.G, nc);
     else if (a.conv)
       hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
     else
       hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1202,7 +1228,7 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     ProfScope ps(st, KID_FAST_PASS);
     hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
                        lam_end, a.s_in, a.s_out, sinb, nm == 2 ? sync : nullptr, part,
-                       nm == 2 ? npart : 0, a.H, nc);
+                       nm == 2 ? npart : 0, a.status, a.H, nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1212,7 +1238,7 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
 #define SSD_FOUT(CV, NM, PC)                                                                  \
   hipLaunchKernelGGL((k_fout<CV, NM, PC>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D, \
                      sinb, bcv, ccv, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps,            \
-                     (bf16*)a.y, part, sync, a.L, a.H, a.G, nc)
+                     (bf16*)a.y, part, sync, a.status, a.spin_max, a.L, a.H, a.G, nc)
   {
     ProfScope ps(st, KID_FAST_OUT);
     // precomputed B and C exist exactly when the conv is on and a group spans

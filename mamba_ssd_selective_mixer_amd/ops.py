@@ -27,6 +27,7 @@ class SSDDims:
     conv_width: int = 4
     chunk: int = 128
     io_dtype: torch.dtype = torch.bfloat16
+    flags: int = 0      # SSD_FLAG_* bits (1: fp32 MFMA operands for bf16 I/O)
 
     @property
     def hp(self):
@@ -39,7 +40,7 @@ class SSDDims:
     def c(self) -> _lib.Dims:
         code = {torch.float32: _lib.SSD_F32, torch.bfloat16: _lib.SSD_BF16}.get(self.io_dtype, 99)
         return _lib.Dims(self.batch, self.seqlen, self.nheads, self.headdim, self.ngroups,
-                         self.dstate, self.conv_width, self.chunk, code)
+                         self.dstate, self.conv_width, self.chunk, code, self.flags)
 
     def replace(self, **kw) -> "SSDDims":
         return dataclasses.replace(self, **kw)
@@ -302,6 +303,22 @@ def ssd_mixer_prefill(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps=
                                        _stream(stream))
     _check(rc, "ssd_mixer_prefill")
     return out
+
+
+def ssd_workspace_status(ws, stream=None) -> int:
+    """Status code of the scan / prefill call that last used workspace `ws`
+    (waits for `stream`): 0, SSD_ERR_TIMEOUT (-9) or SSD_ERR_NONFINITE (-10)."""
+    _need_cuda(ws)
+    return int(_lib.load().ssd_workspace_status(_p(ws), _stream(stream)))
+
+
+def ssd_set_exchange_spin_limit(polls: int) -> int:
+    """Diagnostic: bound on the fused path's cross-block norm polls; returns
+    the previous bound."""
+    rc = int(_lib.load().ssd_set_exchange_spin_limit(int(polls)))
+    if rc < 0:
+        raise SSDError(rc, "ssd_set_exchange_spin_limit")
+    return rc
 
 
 def profile_start(capacity: int) -> None:

@@ -51,7 +51,10 @@ def test_validate_configs(lib):
 @pytest.mark.parametrize("kw,entry,rc", [
     (dict(nheads=30), 1, -2),          # n_groups must divide the heads
     (dict(headdim=48), 1, -3),
-    (dict(dstate=256), 1, -3),
+    (dict(dstate=512), 1, -3),
+    (dict(dstate=256), 1, 0),
+    (dict(dstate=256, seqlen=1), 3, 0),
+    (dict(flags=2), 1, -3),            # unknown flag bits
     (dict(io_dtype=7), 1, -4),
     (dict(seqlen=0), 1, -2),
     (dict(batch=0), 0, -2),

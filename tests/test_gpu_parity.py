@@ -453,6 +453,27 @@ def test_prefill_fast_path_shapes(ops, H, G, B, L, st, bias):
                  with_bias=bias)
 
 
+# d_state 256 (the top of the envelope): the general kernels with 32 output
+# tiles per wave in the chunk-state kernel at head_dim 128, and the decode
+# kernel with one wave per state row.
+@pytest.mark.parametrize("P,io", [(64, "bf16"), (128, "bf16"), (32, "f32")])
+def test_prefill_dstate256(ops, P, io):
+    prefill_case(ops, small("c1", nheads=8, ngroups=2, headdim=P, dstate=256, batch=2,
+                            seqlen=200, dtype=io), with_state=True)
+
+
+def test_chunk_scan_dstate256_fp32(ops):
+    scan_case(ops, small("c0", nheads=4, headdim=64, ngroups=1, dstate=256, seqlen=150,
+                         batch=2), True, True)
+
+
+@pytest.mark.parametrize("kw", [dict(batch=3, nheads=8, ngroups=2, headdim=64, dstate=256),
+                                dict(batch=2, nheads=4, ngroups=1, headdim=128, dstate=256,
+                                     conv_width=2)])
+def test_decode_dstate256(ops, kw):
+    decode_case(ops, synth.replace(synth.CONFIGS["c4"], **kw), steps=3)
+
+
 def test_prefill_generic_shapes(ops):
     """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
     prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
