@@ -515,10 +515,12 @@ constexpr int kPassDepth = 8;
 constexpr int kStatusTimeout = 1;    // a cross-block norm wait gave up
 constexpr int kStatusNonFinite = 2;  // an output or the final state is not finite
 constexpr int kPassVec = 8;
-__global__ __launch_bounds__(256) void k_fpass(const f16* __restrict__ dS,
+// dS and sin_h are one buffer: S_in(k) overwrites dS_k, which this thread
+// has loaded before (its own elements only), so neither pointer is restrict.
+__global__ __launch_bounds__(256) void k_fpass(const f16* dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
-                                               f16* __restrict__ sin_h, int* sync, float* part,
+                                               f16* sin_h, int* sync, float* part,
                                                int64_t npart, int* status, int H, int nc) {
   constexpr int PN = P * N;
   const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
@@ -1137,7 +1139,8 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
          (!conv || W == fast::W);
 }
 
-// Workspace: chunk-state increments and carried-in states (fp16), Lam_end;
+// Workspace: chunk-state increments, overwritten in place by the carried-in
+// states (fp16), Lam_end;
 // when a group spans several 4-head blocks, the per-row partial sums and
 // the ticket counters of the cross-block norm and, with the conv, the
 // convolved B and C rows in fp16 for the output kernel.
@@ -1155,7 +1158,7 @@ size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
   const size_t nc = (L + fast::QI - 1) / fast::QI;
   const size_t PN = fast::P * fast::N;
   const size_t rows = (size_t)B * L * G * fast::N * 2;
-  size_t n = 2 * ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4);
+  size_t n = ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4);
   if (wide(H, G))
     n += ws_round(nc * B * (H / fast::HB) * fast::QI * 4) + ws_round(fast::kParts * 4);
   if (pre_c(H, G, conv)) n += 2 * ws_round(rows);
@@ -1167,9 +1170,9 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   const int nc = (a.L + QI - 1) / QI;
   const size_t PN = P * N;
   unsigned char* w = (unsigned char*)a.ws;
+  // chunk increments, overwritten in place by the carried-in states
   fast::f16* dS = (fast::f16*)w;
-  w += ws_round((size_t)a.B * nc * a.H * PN * 2);
-  fast::f16* sinb = (fast::f16*)w;
+  fast::f16* sinb = dS;
   w += ws_round((size_t)a.B * nc * a.H * PN * 2);
   float* lam_end = (float*)w;
   w += ws_round((size_t)a.B * a.H * nc * 4);
