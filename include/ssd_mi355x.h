@@ -110,8 +110,10 @@ typedef enum {
   SSD_ERR_ALIGN = -8,       /* pointer or stride breaks the 16-byte rule     */
   SSD_ERR_TIMEOUT = -9,     /* (ssd_workspace_status) a cross-workgroup norm
                                exchange gave up waiting; its rows are NaN    */
-  SSD_ERR_NONFINITE = -10   /* (ssd_workspace_status) an output or the final
+  SSD_ERR_NONFINITE = -10,  /* (ssd_workspace_status) an output or the final
                                SSM state is infinite or NaN                  */
+  SSD_ERR_SCRATCH = -11     /* (ssd_mixer_prefill_noalloc) the call needs more
+                               scratch than the library's fixed buffer holds */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -228,6 +230,28 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z,
                       void* conv_state_out, const float* ssm_state_in,
                       float* ssm_state_out, void* out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/*
+ * ssd_mixer_prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The call allocates nothing. Its scratch
+ * is a fixed 64 MiB device array inside this library, one copy per GPU,
+ * held until the process ends; a call whose
+ * ssd_mixer_prefill_workspace_bytes(d) exceeds 64 MiB returns
+ * SSD_ERR_SCRATCH before any launch (the tiny-model layer, 4 x 2048 tokens
+ * at 32 heads, needs 32 MiB). Every call on one GPU shares that array and
+ * leaves its contents behind: calls on one stream run in order, calls that
+ * overlap in time on one GPU (several streams or threads) race. The kernels
+ * clear what must start at zero themselves. Runs on the current device;
+ * arguments, layouts, aliasing rules and results are those of
+ * ssd_mixer_prefill.
+ */
+int ssd_mixer_prefill_noalloc(const ssd_dims* d, const void* xbc, const void* z,
+                              const void* dt, const float* A, const float* D,
+                              const void* conv_w, const void* conv_b, const void* norm_w,
+                              float eps, const void* conv_state_in, void* conv_state_out,
+                              const float* ssm_state_in, float* ssm_state_out, void* out,
+                              void* stream);
 
 /*
  * Status of the chunk-scan or mixer-prefill call that last used `workspace`

@@ -253,6 +253,7 @@ const char* ssd_status_str(int status) {
     case SSD_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case SSD_ERR_TIMEOUT: return "a cross-workgroup norm exchange gave up waiting";
     case SSD_ERR_NONFINITE: return "an output or the final state is not finite";
+    case SSD_ERR_SCRATCH: return "the call needs more scratch than the fixed buffer holds";
     default: return "unknown status";
   }
 }

@@ -305,6 +305,37 @@ def ssd_mixer_prefill(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps=
     return out
 
 
+def ssd_mixer_prefill_noalloc(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, out,
+                              eps=1e-5, conv_state_in=None, conv_state_out=None,
+                              ssm_state_in=None, ssm_state_out=None, stream=None):
+    """ssd_mixer_prefill with the library's fixed per-GPU scratch buffer
+    instead of a workspace; `out` is required, so nothing is allocated."""
+    io, f32 = d.io_dtype, torch.float32
+    B, L, H, C = d.batch, d.seqlen, d.nheads, d.channels
+    _want(xbc, "xbc", io, B * L * C)
+    _want(z, "z", io, B * L * d.hp, optional=True)
+    _want(dt, "dt", io, B * L * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp, optional=z is None)
+    ncs, nss = B * (d.conv_width - 1) * C, B * H * d.headdim * d.dstate
+    _want(conv_state_in, "conv_state_in", io, ncs, optional=True)
+    _want(conv_state_out, "conv_state_out", io, ncs, optional=True)
+    _want(ssm_state_in, "ssm_state_in", f32, nss, optional=True)
+    _want(ssm_state_out, "ssm_state_out", f32, nss, optional=True)
+    _want(out, "out", io, B * L * d.hp)
+    _need_cuda(xbc, z, dt, A, D, conv_w, conv_b, norm_w, conv_state_in, conv_state_out,
+               ssm_state_in, ssm_state_out, out)
+    rc = _lib.load().ssd_mixer_prefill_noalloc(
+        ctypes.byref(d.c()), _p(xbc), _p(z), _p(dt), _p(A), _p(D), _p(conv_w), _p(conv_b),
+        _p(norm_w), float(eps), _p(conv_state_in), _p(conv_state_out), _p(ssm_state_in),
+        _p(ssm_state_out), _p(out), _stream(stream))
+    _check(rc, "ssd_mixer_prefill_noalloc")
+    return out
+
+
 def ssd_workspace_status(ws, stream=None) -> int:
     """Status code of the scan / prefill call that last used workspace `ws`
     (waits for `stream`): 0, SSD_ERR_TIMEOUT (-9) or SSD_ERR_NONFINITE (-10)."""
