@@ -1,22 +1,29 @@
 """Benchmark of the Mamba-2 mixer core on one MI355X.
 
 A step is one pass of the whole prefill hot path (conv + SiLU over xBC, the
-chunked SSD scan, the gated RMSNorm) over one batch of synthetic input of
-the tiny-model layer shape (4 x 2048 tokens, 32 heads x 64, 8 groups,
-state 128, conv width 4, chunk 128, bf16 I/O), inputs already resident in
-HBM. Four input/output buffer sets rotate across steps so no step reads
-inputs the previous one left in the 256 MB Infinity Cache.
+chunked SSD scan, the gated RMSNorm, the final conv and SSM states written
+out) over one batch of synthetic input of the large-model layer shape:
+1 x 8192 tokens, 256 heads x 64, 8 groups, state 128, conv width 4, chunk
+256, bf16 I/O, zero initial state, inputs already resident in HBM. Two
+input/output buffer sets alternate across steps (each set, 0.85 GB, is
+larger than the 256 MB Infinity Cache).
 
-Also measured (reported under "workloads"): the large-model layer prefill
-(1 x 8192 tokens, 256 heads), the long-context chained prefill (16 pieces
-of 8192 tokens, each resuming from the previous piece's states) and the
-decode loop (256 sequences x 64 single-token steps, 256 heads).
+Also measured (reported under "workloads"): the tiny-model layer prefill
+(4 x 2048 tokens, 32 heads), the long-context chained prefill (16 pieces of
+8192 tokens, each resuming from the previous piece's states, per piece and
+per chain), the decode loop (256 sequences x 64 single-token steps, 256
+heads), the tiny fp32 layer and a bf16 shape outside the fused kernels'
+envelope (both on the general kernels); under "ceilings": a streaming copy
+and an MFMA-only loop on this GPU; under "cpu_baseline": the fp64 oracle on
+the host cores.
 
 Prints one JSON line. Only one GPU is used: --gpus above 1 exits.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -27,22 +34,23 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 / fp16 MFMA, TFLOP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2500.0   # dense fp16 / bf16 MFMA, TFLOP/s
 
 KERNEL_NAMES = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
                 "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
                 "fused_chunk_out_norm")
 DOMINANT = "fused_chunk_out_norm"
-# HBM bytes per launch of a kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# counters, with the hash of the kernel sources they were taken on.
-TRAFFIC_FILES = {"fused_chunk_out_norm": "fused_chunk_out_norm.tiny_layer_prefill.traffic.txt"}
+FUSED = ("fused_chunk_state", "fused_state_pass", "fused_chunk_out_norm")
+# Counter-measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# scaled by a copy of known size), kept with the hash of the kernel sources
+# they were taken on.
+TRAFFIC_FILE = "{kernel}.large_layer_prefill.traffic.txt"
 KERNEL_SOURCES = ("mamba_ssd_selective_mixer_amd/csrc/scan_fast.hip",
                   "mamba_ssd_selective_mixer_amd/csrc/common.hpp")
 
 
 def kernel_source_hash() -> str:
-    import hashlib
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -51,11 +59,11 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str):
-    """Counter-measured HBM bytes per launch, or None when no measurement
-    exists or the kernel sources changed since it was taken."""
-    name = TRAFFIC_FILES.get(kernel)
-    path = os.path.join(ROOT, "profiles", name) if name else None
-    if not path or not os.path.exists(path):
+    """HBM bytes per launch of `kernel` on the large-model layer from the
+    counter summary under profiles/, or None when there is none or the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILE.format(kernel=kernel))
+    if not os.path.exists(path):
         return None
     fields = {}
     for line in open(path):
@@ -70,54 +78,49 @@ def measured_traffic(kernel: str):
         return None
 
 
-def copy_calibration(torch):
-    """A plain device-to-device copy of 512 MiB, run 5 times, so HBM counters
-    can be scaled by what they read for a known number of bytes."""
-    n = 512 << 20
-    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(5):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
-
-
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--sets", type=int, default=4, help="rotating input/output buffer sets")
+    ap.add_argument("--sets", type=int, default=2, help="alternating input/output buffer sets")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events")
-    ap.add_argument("--only", choices=("large", "chain", "decode"),
+    ap.add_argument("--only", choices=("tiny", "chain", "decode", "general"),
                     help="time only one of the secondary workloads (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for the HBM counter scale)")
     return ap.parse_args()
 
 
-def prefill_bytes(cfg, L, with_states):
-    """Algorithmic HBM bytes of one prefill call: xBC, z, dt read once, out
-    written once, plus the requested state I/O."""
+# ------------------------------------------------------------ byte / flop counts
+def token_bytes(cfg):
+    """Algorithmic bytes per token of a prefill call: xBC, z, dt read once and
+    the output written once."""
     e = 2 if cfg.dtype == "bf16" else 4
-    tok = cfg.batch * L
-    b = e * tok * (cfg.channels + 2 * cfg.hp + cfg.nheads)
-    if with_states:
-        ssm = cfg.batch * cfg.hp * cfg.dstate * 4
-        conv = cfg.batch * (cfg.conv_width - 1) * cfg.channels * e
-        b += 2 * (ssm + conv)
-    return b
+    return e * (cfg.channels + 2 * cfg.hp + cfg.nheads)
 
 
-def prefill_flops(cfg, L):
-    """Dense contractions of the chunked scan (causal half of the Q x Q
-    products): C B^T per group, (C B^T o decay) X, C S_in^T and B^T X per head."""
+def state_bytes(cfg):
+    """One sequence's SSM state (fp32) and conv state (I/O dtype)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    return cfg.hp * cfg.dstate * 4 + (cfg.conv_width - 1) * cfg.channels * e
+
+
+def prefill_bytes(cfg, states_in, states_out):
+    b = token_bytes(cfg) * cfg.batch * cfg.seqlen
+    return b + cfg.batch * state_bytes(cfg) * (int(states_in) + int(states_out))
+
+
+def prefill_flops(cfg):
+    """Dense contractions of the chunked scan at the configuration's chunk
+    length (causal half of the Q x Q products): C B^T per group, the masked
+    (C B^T) X, C S_in^T and B^T X per head."""
     Q = cfg.chunk
-    tok = cfg.batch * L
-    per_tok_group = Q * cfg.dstate          # causal half of 2*Q*N
+    tok = cfg.batch * cfg.seqlen
+    per_tok_group = Q * cfg.dstate
     per_tok_head = Q * cfg.headdim + 2 * cfg.headdim * cfg.dstate * 2
     return tok * (cfg.ngroups * per_tok_group + cfg.nheads * per_tok_head)
 
@@ -129,8 +132,10 @@ def decode_bytes(cfg):
             + e * B * (cfg.channels + 2 * cfg.hp + cfg.nheads))
 
 
+# ------------------------------------------------------------------ timing
 class Timer:
-    """HIP events on the stream the library launches on."""
+    """HIP events on the stream the library launches on (torch's current
+    stream, which the binding passes to every call)."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -150,32 +155,55 @@ def to_dev(torch, a, dt):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda", dt)
 
 
-def run_prefill(torch, ops, synth, cfg, steps, warmup, nsets, with_states, kernel_events=False):
-    """Mean ms per prefill call over `steps` timed calls; with kernel_events,
-    also {kernel: (launches, mean ms)} from the library's per-kernel HIP
-    events recorded over the same timed calls."""
-    bf = torch.bfloat16
+def kernel_times(ops, run, steps, launches_per_step=8):
+    """{kernel: mean ms per launch} from the library's per-kernel HIP events
+    (recorded on the stream each kernel runs on) over `steps` calls of run()."""
+    ops.profile_start(launches_per_step * steps)
+    for i in range(steps):
+        run(i)
+    ops.profile_stop()
+    out = {}
+    for name in KERNEL_NAMES:
+        n, t = ops.profile_read(name)
+        if n:
+            out[name] = t / n
+    return out
+
+
+def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, states_out,
+                     kernel_events=True):
+    """Mean ms per prefill call over `steps` timed calls (HIP events around the
+    whole timed region), and per-kernel mean ms from a second, event-bracketed
+    pass over the same calls (the per-kernel events add gaps between
+    launches, so the step time comes from the first pass)."""
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     prm = synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
-                    cfg.conv_width, cfg.chunk, bf)
+                    cfg.conv_width, cfg.chunk, td)
     A, D = to_dev(torch, prm["A"], torch.float32), to_dev(torch, prm["D"], torch.float32)
-    cw, nw = to_dev(torch, prm["conv_w"], bf), to_dev(torch, prm["norm_w"], bf)
+    cw, nw = to_dev(torch, prm["conv_w"], td), to_dev(torch, prm["norm_w"], td)
     base = synth.prefill_inputs(cfg)
+    st0 = synth.initial_states(cfg) if states_in else None
     sets = []
-    for i in range(nsets):
-        # distinct buffers per set; contents of set 0 are the seeded inputs
-        s = {k: to_dev(torch, v, bf) for k, v in base.items()}
-        s["out"] = torch.empty(cfg.batch, cfg.seqlen, cfg.hp, dtype=bf, device="cuda")
-        if with_states:
-            s["cs"] = torch.zeros(cfg.batch, cfg.conv_width - 1, cfg.channels, dtype=bf, device="cuda")
-            s["ss"] = torch.zeros(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
+    for _ in range(nsets):
+        s = {k: to_dev(torch, v, td) for k, v in base.items()}
+        s["out"] = torch.empty(cfg.batch, cfg.seqlen, cfg.hp, dtype=td, device="cuda")
+        if states_in:
+            s["cs_in"] = to_dev(torch, st0["conv_state"], td)
+            s["ss_in"] = to_dev(torch, st0["ssm_state"], torch.float32)
+        if states_out:
+            s["cs_out"] = torch.empty(cfg.batch, cfg.conv_width - 1, cfg.channels, dtype=td,
+                                      device="cuda")
+            s["ss_out"] = torch.empty(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate,
+                                      device="cuda")
         sets.append(s)
     ws = ops.workspace(ops.ssd_mixer_prefill_workspace_bytes(d))
 
     def step(i):
         s = sets[i % nsets]
         ops.ssd_mixer_prefill(d, s["xbc"], s["z"], s["dt"], A, D, cw, None, nw, prm["eps"],
-                              s.get("cs"), s.get("cs"), s.get("ss"), s.get("ss"), s["out"], ws)
+                              s.get("cs_in"), s.get("cs_out"), s.get("ss_in"), s.get("ss_out"),
+                              s["out"], ws)
 
     for i in range(warmup):
         step(i)
@@ -186,27 +214,32 @@ def run_prefill(torch, ops, synth, cfg, steps, warmup, nsets, with_states, kerne
         step(i)
     ms = tm.stop_ms() / steps
     torch.cuda.synchronize()
-    kern = {}
-    if kernel_events:
-        # The same timed steps again, each kernel launch bracketed by a pair of
-        # HIP events on its stream. The events add gaps between launches (not
-        # to the kernels), so the step time above comes from the first pass.
-        ops.profile_start(8 * steps)
-        tm.start()
-        for i in range(steps):
-            step(i)
-        kern["_step_ms"] = tm.stop_ms() / steps
-        torch.cuda.synchronize()
-        ops.profile_stop()
-        for name in KERNEL_NAMES:
-            n, t = ops.profile_read(name)
-            if n:
-                kern[name] = (n, t / n)
-    return ms, kern
+    kern = kernel_times(ops, step, steps) if kernel_events else {}
+    status = ops.ssd_workspace_status(ws)
+    del sets, ws
+    torch.cuda.empty_cache()
+    return ms, kern, status
 
 
-def run_chain(torch, ops, synth, cfg, reps, nsets_unused=None):
-    """Long-context prefill: cfg.pieces pieces chained through conv/SSM state."""
+def summarize_prefill(cfg, ms, kern, states_in, states_out):
+    tokens = cfg.batch * cfg.seqlen
+    nb = prefill_bytes(cfg, states_in, states_out)
+    kb = token_bytes(cfg) * tokens
+    r = {"tokens_per_s": tokens / (ms * 1e-3), "us_per_call": ms * 1e3,
+         "algorithmic_bytes": nb, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+         "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFS,
+         "kernels_us": {k: v * 1e3 for k, v in kern.items()}}
+    out_k = DOMINANT if DOMINANT in kern else ("chunk_out" if "chunk_out" in kern else None)
+    if out_k:
+        r["dominant_kernel"] = out_k
+        r["dominant_kernel_bytes"] = kb
+        r["dominant_kernel_hbm_frac"] = kb / (kern[out_k] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return r
+
+
+def run_chain(torch, ops, synth, cfg, reps, kernel_events=True):
+    """Long-context prefill: cfg.pieces pieces chained through conv/SSM state
+    (each call reads the previous piece's states and writes its own)."""
     bf = torch.bfloat16
     prm = synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
@@ -222,12 +255,16 @@ def run_chain(torch, ops, synth, cfg, reps, nsets_unused=None):
     ss = torch.zeros(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
     ws = ops.workspace(ops.ssd_mixer_prefill_workspace_bytes(d))
 
+    def piece(i):
+        p = pieces[i % cfg.pieces]
+        ops.ssd_mixer_prefill(d, p["xbc"], p["z"], p["dt"], A, D, cw, None, nw, prm["eps"],
+                              cs, cs, ss, ss, out, ws)
+
     def chain():
         cs.zero_()
         ss.zero_()
-        for p in pieces:
-            ops.ssd_mixer_prefill(d, p["xbc"], p["z"], p["dt"], A, D, cw, None, nw, prm["eps"],
-                                  cs, cs, ss, ss, out, ws)
+        for i in range(cfg.pieces):
+            piece(i)
 
     chain()
     torch.cuda.synchronize()
@@ -235,11 +272,12 @@ def run_chain(torch, ops, synth, cfg, reps, nsets_unused=None):
     tm.start()
     for _ in range(reps):
         chain()
-    ms = tm.stop_ms()
-    return ms / reps
+    ms = tm.stop_ms() / reps
+    kern = kernel_times(ops, piece, cfg.pieces) if kernel_events else {}
+    return ms, kern
 
 
-def run_decode(torch, ops, synth, cfg, reps):
+def run_decode(torch, ops, synth, cfg, reps, kernel_events=True):
     bf = torch.bfloat16
     prm = synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, 1, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
@@ -255,10 +293,14 @@ def run_decode(torch, ops, synth, cfg, reps):
         steps.append({kk: to_dev(torch, v, bf) for kk, v in t.items()})
     y = torch.empty(cfg.batch, cfg.hp, dtype=bf, device="cuda")
 
+    def one(i):
+        t = steps[i % cfg.steps]
+        ops.ssd_decode_step(d, t["xbc_t"], t["z_t"], t["dt_t"], A, D, cw, None, nw, prm["eps"],
+                            cs, ss, y)
+
     def loop():
-        for t in steps:
-            ops.ssd_decode_step(d, t["xbc_t"], t["z_t"], t["dt_t"], A, D, cw, None, nw,
-                                prm["eps"], cs, ss, y)
+        for i in range(cfg.steps):
+            one(i)
 
     loop()
     torch.cuda.synchronize()
@@ -266,57 +308,144 @@ def run_decode(torch, ops, synth, cfg, reps):
     tm.start()
     for _ in range(reps):
         loop()
-    ms = tm.stop_ms()
-    return ms / reps  # per 64-step loop
+    ms = tm.stop_ms() / reps  # per 64-step loop
+    kern = kernel_times(ops, one, cfg.steps, 2) if kernel_events else {}
+    return ms, kern
 
 
-def cpu_baseline(synth, cfg, budget_s=10.0):
-    """The fp64 oracle on full steps of the headline workload on the host
-    cores, repeated until about `budget_s` seconds of wall time are spent."""
+def ceilings(torch):
+    """A streaming 2 GiB device copy and an MFMA-only loop on this GPU."""
+    from mamba_ssd_selective_mixer_amd import build as hb
+    lib = ctypes.CDLL(hb.CEIL_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ceil_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.ceil_mfma.argtypes = [vp, i32, i32, vp]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    blocks = 256 * 8
+    tm = Timer(torch)
+    for _ in range(2):
+        assert lib.ceil_copy(vp(src.data_ptr()), vp(dst.data_ptr()), n, blocks, st) == 0
+    tm.start()
+    reps = 5
+    for _ in range(reps):
+        assert lib.ceil_copy(vp(src.data_ptr()), vp(dst.data_ptr()), n, blocks, st) == 0
+    copy_ms = tm.stop_ms() / reps
+    del src, dst
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    iters = 2000
+    assert lib.ceil_mfma(vp(out.data_ptr()), 2048, 50, st) == 0
+    tm.start()
+    assert lib.ceil_mfma(vp(out.data_ptr()), 2048, iters, st) == 0
+    mfma_ms = tm.stop_ms()
+    flops = 2048 * 4 * iters * 8 * 2 * 16 * 16 * 32
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 2 * n / (copy_ms * 1e-3) / 1e9,
+            "copy_desc": "2 GiB device-to-device copy, 16-byte non-temporal loads and stores, "
+                         "2048 workgroups of 256 threads (GB/s counts bytes read + written)",
+            "mfma_f16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "mfma_desc": "fp16 16x16x32 MFMA only, 8 independent chains per wave, "
+                         "2048 workgroups of 256 threads"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(synth, cfg, budget_s=12.0, one_thread_tokens=1024):
+    """The fp64 oracle on the headline workload on the host cores: full
+    steps (all 8192 tokens, all heads) repeated until about budget_s of wall
+    time on all threads, then one thread on the first one_thread_tokens
+    tokens of the same step."""
     from oracle import oracle
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)
+
+    def one(x, z, dt):
+        oracle.mixer_prefill(x, z, dt, prm["A"], prm["D"], prm["conv_w"], None, prm["norm_w"],
+                             prm["eps"], cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate)
+
+    threads = oracle.num_threads()
     reps, sec = 0, 0.0
-    while sec < budget_s and reps < 100:
+    while sec < budget_s and reps < 50:
         t = time.perf_counter()
-        oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"], prm["conv_w"],
-                             None, prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim,
-                             cfg.ngroups, cfg.dstate)
+        one(inp["xbc"], inp["z"], inp["dt"])
         sec += time.perf_counter() - t
         reps += 1
     tokens = cfg.batch * cfg.seqlen * reps
-    return {"value": tokens / sec, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} full step(s) of {cfg.batch}x{cfg.seqlen} tokens (fp64 sequential "
-                      f"recurrence + conv + gated norm), {sec:.1f} s wall"}
+    n1 = one_thread_tokens
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        one(inp["xbc"][:, :n1], inp["z"][:, :n1], inp["dt"][:, :n1])
+        sec1 = time.perf_counter() - t
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": tokens / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{reps} full step(s) of {cfg.batch} x {cfg.seqlen} tokens of the "
+                      f"large-model layer (fp64 sequential recurrence, explicit conv and gated "
+                      f"norm), {sec:.1f} s wall on {threads} threads",
+            "one_thread": {"value": cfg.batch * n1 / sec1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"the first {n1} tokens of the same step, {sec1:.1f} s"}}
 
 
 def secondary(torch, ops, synth, args, which):
-    """The large-layer prefill, the long-context chain and the decode loop."""
     wl = {}
-    if "large" in which:
-        c2 = synth.CONFIGS["c2"]
-        ms2, _ = run_prefill(torch, ops, synth, c2, max(3, args.steps // 5), 2, 2, True)
-        b2 = prefill_bytes(c2, c2.seqlen, True)
-        wl["large_prefill"] = {"tokens_per_s": c2.seqlen / (ms2 * 1e-3), "ms": ms2,
-                               "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                               "mfma_frac": prefill_flops(c2, c2.seqlen) / (ms2 * 1e-3) / 1e12
-                               / MFMA_BF16_PEAK_TFS}
+    ke = not args.no_kernel_events
+    if "tiny" in which:
+        c1 = synth.CONFIGS["c1"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, c1, max(10, args.steps), 3, 4, False,
+                                        False, ke)
+        wl["tiny_layer_prefill"] = dict(summarize_prefill(c1, ms, kern, False, False), status=rc,
+                                        config="4 x 2048 tokens, 32 heads x 64, 8 groups, state "
+                                               "128, chunk 128, bf16, no states")
     if "chain" in which:
         c3 = synth.CONFIGS["c3"]
-        ms3 = run_chain(torch, ops, synth, c3, 3)
-        b3 = prefill_bytes(c3, c3.seqlen, True) * c3.pieces
-        wl["long_context_chain"] = {"tokens_per_s": c3.seqlen * c3.pieces / (ms3 * 1e-3),
-                                    "ms_per_chain": ms3,
-                                    "hbm_frac": b3 / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        ms, kern = run_chain(torch, ops, synth, c3, 3, ke)
+        tokens = c3.seqlen * c3.pieces
+        nb = prefill_bytes(c3, True, True) * c3.pieces
+        wl["long_context_chain"] = {
+            "tokens_per_s": tokens / (ms * 1e-3), "ms_per_chain": ms,
+            "us_per_piece": ms * 1e3 / c3.pieces,
+            "algorithmic_bytes_per_piece": nb // c3.pieces,
+            "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernels_us": {k: v * 1e3 for k, v in kern.items()},
+            "config": "16 pieces of 1 x 8192 tokens, 32 heads x 64, 8 groups, state 128, "
+                      "each resuming from the previous piece's conv and SSM state"}
     if "decode" in which:
         c4 = synth.CONFIGS["c4"]
-        ms4 = run_decode(torch, ops, synth, c4, 3)
+        ms, kern = run_decode(torch, ops, synth, c4, 3, ke)
         b4 = decode_bytes(c4) * c4.steps
-        wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms4 * 1e-3),
-                        "us_per_step": ms4 * 1e3 / c4.steps,
-                        "hbm_gbs": b4 / (ms4 * 1e-3) / 1e9,
-                        "hbm_frac": b4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms * 1e-3),
+                        "us_per_step": ms * 1e3 / c4.steps,
+                        "algorithmic_bytes_per_step": decode_bytes(c4),
+                        "hbm_gbs": b4 / (ms * 1e-3) / 1e9,
+                        "hbm_frac": b4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "kernels_us": {k: v * 1e3 for k, v in kern.items()},
+                        "config": "256 sequences x 64 steps, 256 heads x 64, 8 groups, "
+                                  "state 128, states ~ N(0, 0.1) updated in place"}
+    if "general" in which:
+        c0 = synth.CONFIGS["c0"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, c0, 50, 5, 1, False, False, ke)
+        wl["tiny_fp32_layer"] = dict(summarize_prefill(c0, ms, kern, False, False), status=rc,
+                                     config="1 x 256 tokens, 4 heads x 16, 1 group, state 16, "
+                                            "chunk 64, fp32 (general kernels)")
+        cg = synth.replace(synth.CONFIGS["c1"], dstate=64)
+        ms, kern, rc = prefill_workload(torch, ops, synth, cg, 10, 3, 2, False, False, ke)
+        wl["general_bf16_prefill"] = dict(summarize_prefill(cg, ms, kern, False, False),
+                                          status=rc,
+                                          config="4 x 2048 tokens, 32 heads x 64, 8 groups, "
+                                                 "state 64, chunk 128, bf16 (general kernels)")
     return wl
 
 
@@ -333,35 +462,45 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     if args.copy_calibration:
-        copy_calibration(torch)
+        n = 512 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
     if args.only:
-        print(json.dumps(secondary(torch, ops, synth, args, (args.only,))))
+        print(json.dumps(secondary(torch, ops, synth, args, (args.only,))), flush=True)
         return
-    cfg = synth.CONFIGS["c1"]
-    ms, kern = run_prefill(torch, ops, synth, cfg, args.steps, args.warmup, args.sets, False,
-                           kernel_events=not args.no_kernel_events)
+    cfg = synth.CONFIGS["c2"]
+    ms, kern, rc = prefill_workload(torch, ops, synth, cfg, args.steps, args.warmup, args.sets,
+                                    False, True, not args.no_kernel_events)
+    if rc != 0:
+        print(f"prefill reported status {rc}", file=sys.stderr)
+        sys.exit(1)
+    head = summarize_prefill(cfg, ms, kern, False, True)
     tokens = cfg.batch * cfg.seqlen
-    nbytes = prefill_bytes(cfg, cfg.seqlen, False)
-    # the dominant kernel: chunk output + fused gated norm. It reads every
-    # input of the step (xBC, z, dt) and writes the output, so its
-    # algorithmic bytes per launch are the step's.
+    nbytes = head["algorithmic_bytes"]
     if DOMINANT in kern:
-        k_ms = kern[DOMINANT][1]
-        roof = {"bound": "hbm", "kernel": DOMINANT, "achieved": nbytes / (k_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": nbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "traffic": measured_traffic(DOMINANT), "algorithmic_bytes": nbytes,
-                "kernel_us": k_ms * 1e3,
-                "kernels_us": {k: v[1] * 1e3 for k, v in kern.items() if k != "_step_ms"},
-                "events_pass_ms_per_step": kern["_step_ms"],
+        # the output kernel reads every input of the step (xBC, z, dt) and
+        # writes its output: its algorithmic bytes per launch are the step's
+        # token bytes (the final states are written by the other kernels)
+        kb, k_ms = head["dominant_kernel_bytes"], kern[DOMINANT]
+        traffic = {k: measured_traffic(k) for k in FUSED}
+        roof = {"bound": "hbm", "kernel": DOMINANT, "achieved": kb / (k_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 /
+                HBM_PEAK_GBS, "traffic": traffic[DOMINANT],
+                "algorithmic_bytes_per_launch": kb, "kernel_us": k_ms * 1e3,
+                "traffic_per_launch": traffic,
+                "step_traffic_over_algorithmic": (sum(traffic.values()) / nbytes
+                                                  if all(traffic.values()) else None),
                 "step_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "step_mfma_tflops": prefill_flops(cfg, cfg.seqlen) / (ms * 1e-3) / 1e12}
+                "step_mfma_frac": head["mfma_frac"]}
     else:
-        roof = {"bound": "hbm", "kernel": "whole prefill step", "achieved":
-                nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
-                "algorithmic_bytes": nbytes}
+        roof = {"bound": "hbm", "kernel": "whole prefill step",
+                "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": None}
     rec = {
         "metric": "Mamba-2 mixer tokens/sec (prefill, decode) on 1 MI355X; % HBM/MFMA roofline",
         "value": tokens / (ms * 1e-3),
@@ -369,16 +508,20 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "tiny-model layer prefill: batch 4 x 2048 tokens, 32 heads x 64, "
-                               "8 groups, state 128, conv width 4, chunk 128",
+        "config": {"workload": "large-model layer prefill: batch 1 x 8192 tokens, 256 heads x "
+                               "64, 8 groups, state 128, conv width 4, chunk 256, bf16 I/O, "
+                               "zero initial state, final conv and SSM states written",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
         "roofline": roof,
+        "headline": head,
     }
     if not args.quick:
-        rec["workloads"] = secondary(torch, ops, synth, args, ("large", "chain", "decode"))
+        rec["workloads"] = secondary(torch, ops, synth, args, ("tiny", "chain", "decode",
+                                                               "general"))
+        rec["ceilings"] = ceilings(torch)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(synth, cfg)
-    print(json.dumps(rec))
+    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

@@ -56,6 +56,7 @@ def _bind(path: str):
     lib.oracle_mixer_prefill.argtypes = [i64] * 7 + [dp] * 8 + [ctypes.c_double] + [dp] * 6
     lib.oracle_decode_step.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_double] + [dp] * 3
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return lib
 
 
@@ -83,6 +84,9 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self._lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self._lib.oracle_set_num_threads(int(n))
 
 
     def conv1d_silu(self, xbc, w, bias=None, conv_in=None):
@@ -175,6 +179,10 @@ def default() -> Oracle:
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
 
 
 def conv1d_silu(*args, **kw):

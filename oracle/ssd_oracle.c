@@ -227,3 +227,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set the threads of later parallel loops (a 1-thread timing, for one). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
