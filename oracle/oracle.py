@@ -55,6 +55,9 @@ def _bind(path: str):
     lib.oracle_gated_rmsnorm.argtypes = [i64] * 3 + [dp] * 3 + [ctypes.c_double, dp]
     lib.oracle_mixer_prefill.argtypes = [i64] * 7 + [dp] * 8 + [ctypes.c_double] + [dp] * 6
     lib.oracle_decode_step.argtypes = [i64] * 6 + [dp] * 8 + [ctypes.c_double] + [dp] * 3
+    lib.oracle_dt_a.argtypes = [i64] * 2 + [dp] * 5
+    lib.oracle_mixer_prefill_packed.argtypes = [i64] * 8 + [dp] * 7 + [ctypes.c_double] + [dp] * 5
+    lib.oracle_decode_step_packed.argtypes = [i64] * 7 + [dp] * 7 + [ctypes.c_double] + [dp] * 3
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return lib
@@ -147,6 +150,55 @@ class Oracle:
         return {"out": out, "y": y, "conv_out": cs, "s_out": so}
 
 
+    def dt_a(self, dt_raw, dt_bias, A_log):
+        """The step before the path: dt = softplus(dt_raw + dt_bias),
+        A = -exp(A_log) (Modalities PR #459 attribution commit: A_log and
+        dt_bias are the mixer's parameters). dt_raw [..., H] -> (dt, A)."""
+        dt_raw, dt_bias, A_log = map(_f64, (dt_raw, dt_bias, A_log))
+        H = dt_raw.shape[-1]
+        dt = np.empty_like(dt_raw)
+        A = np.empty(H)
+        self._lib.oracle_dt_a(dt_raw.size // H, H, _p(dt_raw), _p(dt_bias), _p(A_log), _p(dt),
+                              _p(A))
+        return dt, A
+
+    def mixer_prefill_packed(self, zxbcdt, dt_bias, A_log, D, conv_w, conv_b, norm_w, eps, H, P,
+                             G, N, conv_in=None, s_in=None):
+        """Prefill on packed projection rows [z | xBC | dt_raw] (gllm PR #86,
+        "Supporting changes": in_proj emits [z | xBC | dt] in one row);
+        zxbcdt [B, L, row] with row >= 2HP + 2GN + H. Returns dict(out,
+        conv_out, s_out)."""
+        zxbcdt, dt_bias, A_log, D, conv_w, conv_b, norm_w, conv_in, s_in = map(
+            _f64, (zxbcdt, dt_bias, A_log, D, conv_w, conv_b, norm_w, conv_in, s_in))
+        Bn, L, R = zxbcdt.shape
+        W = conv_w.shape[1]
+        C = H * P + 2 * G * N
+        assert R >= H * P + C + H
+        out = np.empty((Bn, L, H * P))
+        cs = np.empty((Bn, W - 1, C))
+        so = np.empty((Bn, H, P, N))
+        self._lib.oracle_mixer_prefill_packed(Bn, L, H, P, G, N, W, R, _p(zxbcdt), _p(dt_bias),
+                                              _p(A_log), _p(D), _p(conv_w), _p(conv_b),
+                                              _p(norm_w), float(eps), _p(conv_in), _p(cs),
+                                              _p(s_in), _p(so), _p(out))
+        return {"out": out, "conv_out": cs, "s_out": so}
+
+    def decode_step_packed(self, zxbcdt_t, dt_bias, A_log, D, conv_w, conv_b, norm_w, eps, H, P,
+                           G, N, conv_state, ssm_state):
+        """One token per sequence from packed rows [B, row]; returns
+        (out [B,HP], conv_state', ssm_state') without touching the arguments."""
+        zxbcdt_t, dt_bias, A_log, D, conv_w, conv_b, norm_w = map(
+            _f64, (zxbcdt_t, dt_bias, A_log, D, conv_w, conv_b, norm_w))
+        cs = np.array(conv_state, dtype=np.float64, copy=True, order="C")
+        ss = np.array(ssm_state, dtype=np.float64, copy=True, order="C")
+        Bn, R = zxbcdt_t.shape
+        W = conv_w.shape[1]
+        out = np.empty((Bn, H * P))
+        self._lib.oracle_decode_step_packed(Bn, H, P, G, N, W, R, _p(zxbcdt_t), _p(dt_bias),
+                                            _p(A_log), _p(D), _p(conv_w), _p(conv_b),
+                                            _p(norm_w), float(eps), _p(cs), _p(ss), _p(out))
+        return out, cs, ss
+
     def decode_step(self, xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, eps, H, P, G, N,
                     conv_state, ssm_state):
         """One token per sequence; returns (out [B,HP], conv_state', ssm_state')
@@ -203,6 +255,18 @@ def mixer_prefill(*args, **kw):
 
 def decode_step(*args, **kw):
     return default().decode_step(*args, **kw)
+
+
+def dt_a(*args, **kw):
+    return default().dt_a(*args, **kw)
+
+
+def mixer_prefill_packed(*args, **kw):
+    return default().mixer_prefill_packed(*args, **kw)
+
+
+def decode_step_packed(*args, **kw):
+    return default().decode_step_packed(*args, **kw)
 
 def split_xbc(v, H, P, G, N):
     """Channel order of the conv output: x (H*P) | B (G*N) | C (G*N)

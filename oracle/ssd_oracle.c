@@ -218,6 +218,87 @@ void oracle_decode_step(int64_t Bn, int64_t H, int64_t P, int64_t G,
   free(cs_new); free(s_new);
 }
 
+/*
+ * The step just before the path: the projection emits dt_raw per head, and
+ * the layer's parameters dt_bias and A_log give the positive step size and
+ * the negative decay rate the recurrence uses ("feat(model): add Nemotron-3
+ * Nano hybrid ..." attribution commit names conv1d / A_log / D / dt_bias as
+ * the mixer's state-space parameters; the pages give no formula, so this is
+ * the plain reading that the workloads' input recipe also follows, dt being
+ * softplus of a shifted normal and A minus the exponential of a uniform):
+ *   dt[t,h] = softplus(dt_raw[t,h] + dt_bias[h]) = log(1 + exp(v)),
+ *   A[h]    = -exp(A_log[h]).
+ * No clamp of dt. dt_raw [T, H]; dt_bias, A_log [H]; dt [T, H]; A [H].
+ */
+static double softplus(double v) { return v > 0.0 ? v + log1p(exp(-v)) : log1p(exp(v)); }
+
+void oracle_dt_a(int64_t T, int64_t H, const double* dt_raw, const double* dt_bias,
+                 const double* A_log, double* dt, double* A) {
+  for (int64_t i = 0; i < T; ++i)
+    for (int64_t h = 0; h < H; ++h) dt[i * H + h] = softplus(dt_raw[i * H + h] + dt_bias[h]);
+  for (int64_t h = 0; h < H; ++h) A[h] = -exp(A_log[h]);
+}
+
+/*
+ * Split the packed projection rows [z (H*P) | xBC (Cch) | dt_raw (H)] of T
+ * tokens (row_stride >= 2*H*P + 2*G*N + H elements between tokens; "feat(model):
+ * Nemotron-H hybrid ... on the CPU", "Supporting changes": in_proj emits
+ * [z | xBC | dt] in one row) into dense z [T, HP], xbc [T, Cch], dt_raw [T, H].
+ */
+static void split_packed(int64_t T, int64_t HP, int64_t C, int64_t H, int64_t row_stride,
+                         const double* row, double* z, double* xbc, double* dt_raw) {
+  for (int64_t i = 0; i < T; ++i) {
+    const double* r = row + i * row_stride;
+    memcpy(z + i * HP, r, (size_t)HP * sizeof(double));
+    memcpy(xbc + i * C, r + HP, (size_t)C * sizeof(double));
+    memcpy(dt_raw + i * H, r + HP + C, (size_t)H * sizeof(double));
+  }
+}
+
+/* The whole mixer prefill on packed rows: split, dt / A from the raw values
+ * and the layer's parameters, then oracle_mixer_prefill (gate always on). */
+void oracle_mixer_prefill_packed(int64_t Bn, int64_t L, int64_t H, int64_t P, int64_t G,
+                                 int64_t N, int64_t W, int64_t row_stride,
+                                 const double* zxbcdt, const double* dt_bias,
+                                 const double* A_log, const double* D,
+                                 const double* conv_w, const double* conv_b,
+                                 const double* norm_w, double eps, const double* conv_in,
+                                 double* conv_out, const double* s_in, double* s_out,
+                                 double* out) {
+  const int64_t HP = H * P, C = HP + 2 * G * N, T = Bn * L;
+  double* z = (double*)malloc((size_t)(T * HP) * sizeof(double));
+  double* xbc = (double*)malloc((size_t)(T * C) * sizeof(double));
+  double* raw = (double*)malloc((size_t)(T * H) * sizeof(double));
+  double* dt = (double*)malloc((size_t)(T * H) * sizeof(double));
+  double* A = (double*)malloc((size_t)H * sizeof(double));
+  split_packed(T, HP, C, H, row_stride, zxbcdt, z, xbc, raw);
+  oracle_dt_a(T, H, raw, dt_bias, A_log, dt, A);
+  oracle_mixer_prefill(Bn, L, H, P, G, N, W, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps,
+                       conv_in, conv_out, s_in, s_out, out, NULL);
+  free(z); free(xbc); free(raw); free(dt); free(A);
+}
+
+/* One decode token per sequence from packed rows [B, row_stride], states in
+ * place (as oracle_decode_step). */
+void oracle_decode_step_packed(int64_t Bn, int64_t H, int64_t P, int64_t G, int64_t N,
+                               int64_t W, int64_t row_stride, const double* zxbcdt_t,
+                               const double* dt_bias, const double* A_log, const double* D,
+                               const double* conv_w, const double* conv_b,
+                               const double* norm_w, double eps, double* conv_state,
+                               double* ssm_state, double* out) {
+  const int64_t HP = H * P, C = HP + 2 * G * N;
+  double* z = (double*)malloc((size_t)(Bn * HP) * sizeof(double));
+  double* xbc = (double*)malloc((size_t)(Bn * C) * sizeof(double));
+  double* raw = (double*)malloc((size_t)(Bn * H) * sizeof(double));
+  double* dt = (double*)malloc((size_t)(Bn * H) * sizeof(double));
+  double* A = (double*)malloc((size_t)H * sizeof(double));
+  split_packed(Bn, HP, C, H, row_stride, zxbcdt_t, z, xbc, raw);
+  oracle_dt_a(Bn, H, raw, dt_bias, A_log, dt, A);
+  oracle_decode_step(Bn, H, P, G, N, W, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps,
+                     conv_state, ssm_state, out);
+  free(z); free(xbc); free(raw); free(dt); free(A);
+}
+
 /* Threads the OpenMP runtime will use (reported beside CPU timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

@@ -306,6 +306,80 @@ def pin_worked_example(orc):
     return max(_rel(y.ravel(), ref_y), _rel(s.ravel(), [ref_s]))
 
 
+# The step before the path: dt = softplus(dt_raw + dt_bias) against numpy's
+# logaddexp and torch's softplus (fp64, across the range where exp overflows
+# or underflows), A = -exp(A_log) on exact values, and the hand-worked values
+# of tests/golden/dt_a_worked_example.json.
+def pin_dt_a(orc):
+    import torch
+    errs = []
+    v = np.concatenate([np.linspace(-40, 40, 161), [-700.0, -30.5, 30.5, 700.0, 745.0]])
+    H = v.size
+    dt, A = orc.dt_a(v[None, :] - 0.25, np.full(H, 0.25), np.log(np.arange(1, H + 1, dtype=float)))
+    ref = np.logaddexp(0.0, v)
+    errs.append(float(np.max(np.abs(dt[0] - ref) / np.maximum(ref, 1e-300))))
+    ref_t = torch.nn.functional.softplus(torch.from_numpy(v), threshold=700.0).numpy()
+    errs.append(float(np.max(np.abs(dt[0] - ref_t) / np.maximum(ref_t, 1e-300))))
+    errs.append(_rel(A, -np.arange(1, H + 1, dtype=float)))
+    with open(os.path.join(GOLDEN, "dt_a_worked_example.json")) as f:
+        g = json.load(f)
+    n = len(g["dt_raw"])
+    dt, _ = orc.dt_a(np.array(g["dt_raw"])[None, :], np.array(g["dt_bias"]), np.zeros(n))
+    errs.append(_rel(dt[0], [math.log(a / b) for a, b in g["dt_as_ln_of"]]))
+    _, A = orc.dt_a(np.zeros((1, len(g["A_log"]))), np.zeros(len(g["A_log"])),
+                    np.array(g["A_log"]))
+    errs.append(_rel(A, g["A"]))
+    return max(errs)
+
+
+def rand_packed(seed, pad=5, **kw):
+    """Random packed rows [z | xBC | dt_raw | pad] and the layer's dt_bias,
+    A_log; the split below is written out here, independently of the
+    oracle's."""
+    k = rand_mixer(seed, **kw)
+    r = np.random.default_rng(seed + 1000)
+    Bn, L = k["xbc"].shape[:2]
+    H = k["H"]
+    raw = r.standard_normal((Bn, L, H))
+    row = np.concatenate([k["z"], k["xbc"], raw, r.standard_normal((Bn, L, pad))], -1)
+    k.update(row=row, raw=raw, dt_bias=r.uniform(-3.0, 1.0, H),
+             A_log=r.uniform(math.log(0.05), math.log(2.0), H))
+    k["dt"] = np.logaddexp(0.0, raw + k["dt_bias"])
+    k["A"] = -np.exp(k["A_log"])
+    return k
+
+
+# The packed-row entry points equal the unpacked ones on z, xBC and dt taken
+# from the row's three column ranges, with dt = logaddexp(0, raw + bias) and
+# A = -exp(A_log) computed here (prefill in two pieces, and decode steps).
+def pin_packed(orc):
+    k = rand_packed(17, L=19)
+    errs = []
+    cs, ss = k["conv_in"], k["s_in"]
+    full = orc.mixer_prefill(k["xbc"], k["z"], k["dt"], k["A"], k["D"], k["conv_w"], k["conv_b"],
+                             k["norm_w"], k["eps"], k["H"], k["P"], k["G"], k["N"],
+                             conv_in=cs, s_in=ss)
+    outs = []
+    for a, b in ((0, 7), (7, 19)):
+        r = orc.mixer_prefill_packed(k["row"][:, a:b], k["dt_bias"], k["A_log"], k["D"],
+                                     k["conv_w"], k["conv_b"], k["norm_w"], k["eps"], k["H"],
+                                     k["P"], k["G"], k["N"], conv_in=cs, s_in=ss)
+        cs, ss = r["conv_out"], r["s_out"]
+        outs.append(r["out"])
+    errs += [_rel(np.concatenate(outs, 1), full["out"]), _rel(cs, full["conv_out"]),
+             _rel(ss, full["s_out"])]
+    cs, ss, cs2, ss2 = k["conv_in"], k["s_in"], k["conv_in"], k["s_in"]
+    for t in range(4):
+        o1, cs, ss = orc.decode_step(k["xbc"][:, t], k["z"][:, t], k["dt"][:, t], k["A"], k["D"],
+                                     k["conv_w"], k["conv_b"], k["norm_w"], k["eps"], k["H"],
+                                     k["P"], k["G"], k["N"], cs, ss)
+        o2, cs2, ss2 = orc.decode_step_packed(k["row"][:, t], k["dt_bias"], k["A_log"], k["D"],
+                                              k["conv_w"], k["conv_b"], k["norm_w"], k["eps"],
+                                              k["H"], k["P"], k["G"], k["N"], cs2, ss2)
+        errs += [_rel(o2, o1), _rel(cs2, cs), _rel(ss2, ss)]
+    return max(errs)
+
+
 PINS = {
     "unrolled": pin_unrolled,
     "chunked": pin_chunked,
@@ -320,6 +394,8 @@ PINS = {
     "linearity": pin_linearity,
     "composition": pin_composition,
     "worked_example": pin_worked_example,
+    "dt_a": pin_dt_a,
+    "packed": pin_packed,
 }
 
 LIMITS = {name: 1e-11 for name in PINS}

@@ -33,6 +33,18 @@ MUTATIONS = {
         ("memcpy(Cm + i * GN, v + i * C + HP + GN, ", "memcpy(Cm + i * GN, v + i * C + HP, ")],
     "decode_conv_state_not_kept": [
         ("memcpy(conv_state, cs_new, (size_t)(Bn * R * C) * sizeof(double));", "(void)cs_new;")],
+    "softplus_dropped": [("dt[i * H + h] = softplus(dt_raw[i * H + h] + dt_bias[h]);",
+                          "dt[i * H + h] = dt_raw[i * H + h] + dt_bias[h];")],
+    "dt_bias_dropped": [("softplus(dt_raw[i * H + h] + dt_bias[h])", "softplus(dt_raw[i * H + h])")],
+    "softplus_large_branch": [("v + log1p(exp(-v))", "v + log1p(exp(v))")],
+    "A_log_sign": [("A[h] = -exp(A_log[h]);", "A[h] = exp(A_log[h]);")],
+    "A_log_not_exponentiated": [("A[h] = -exp(A_log[h]);", "A[h] = -A_log[h];")],
+    "packed_z_xbc_swapped": [
+        ("memcpy(z + i * HP, r, (size_t)HP * sizeof(double));",
+         "memcpy(z + i * HP, r + C, (size_t)HP * sizeof(double));"),
+        ("memcpy(xbc + i * C, r + HP, (size_t)C * sizeof(double));",
+         "memcpy(xbc + i * C, r, (size_t)C * sizeof(double));")],
+    "packed_dt_offset": [("memcpy(dt_raw + i * H, r + HP + C, ", "memcpy(dt_raw + i * H, r + C, ")],
 }
 
 
