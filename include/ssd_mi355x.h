@@ -216,7 +216,10 @@ int ssd_decode_step(const ssd_dims* d, const void* xbc_t, const void* z_t,
 /*
  * The whole prefill path in one call: conv + SiLU over xbc, the chunked scan
  * and the gated norm, with state in and out (the composition of the three
- * calls above, fused where the kernels allow).
+ * calls above, fused where the kernels allow). ("feat(model): Nemotron-H
+ * hybrid ... on the CPU", section "2. feat(model)": CausalConv1D, SSMScan and
+ * GatedRMSNorm in that order; section "Validation": prefill in uneven pieces,
+ * the second resuming from state, must match one-shot prefill.)
  *   xbc [B, L, Cch] contiguous; z [B, L, H*P] or NULL; dt [B, L, H];
  *   conv_state_in / conv_state_out [B, W-1, Cch] or NULL (may be equal);
  *   ssm_state_in / ssm_state_out [B, H, P, N] fp32 or NULL (may be equal);
@@ -230,6 +233,39 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z,
                       void* conv_state_out, const float* ssm_state_in,
                       float* ssm_state_out, void* out, void* workspace,
                       size_t ws_bytes, void* stream);
+
+/*
+ * The step just before the path, fused: the prefill and decode entries
+ * below take the input projection's packed rows and the layer's raw
+ * state-space parameters instead of dt and A ("feat(model): Nemotron-H
+ * hybrid ... on the CPU", "Supporting changes": in_proj emits [z | xBC | dt]
+ * in one row; "feat(model): add Nemotron-3 Nano hybrid ..." attribution
+ * commit: packed [z, x, B, C, dt] projection, conv1d / A_log / D / dt_bias
+ * parameters). Per token the row holds z (H*P), then xBC (Cch, order
+ * x | B | C), then dt_raw (H), in io_dtype; row_stride >= 2*H*P + 2*G*N + H
+ * elements separates tokens (row_stride * element size a multiple of 16
+ * bytes). The kernels form dt = softplus(dt_raw + dt_bias[h]) =
+ * log(1 + exp(dt_raw + dt_bias[h])) and A = -exp(A_log[h]) (no clamp of dt;
+ * the pages name the parameters but give no formula: this is the plain
+ * reading) and otherwise compute exactly what ssd_mixer_prefill /
+ * ssd_decode_step compute with that dt and A and the row's z and xBC.
+ *   dt_bias, A_log [H] fp32, required; norm_w required (the row carries z).
+ *   ssd_mixer_prefill_packed: zxbcdt [B, L, row_stride]; the workspace is
+ *   ssd_mixer_prefill_workspace_bytes(d); states, out and aliasing rules as
+ *   ssd_mixer_prefill (the row range is an input).
+ *   ssd_decode_step_packed: zxbcdt_t [B, row_stride]; states and y_t as
+ *   ssd_decode_step.
+ */
+int ssd_mixer_prefill_packed(const ssd_dims* d, const void* zxbcdt, int64_t row_stride,
+                             const float* dt_bias, const float* A_log, const float* D,
+                             const void* conv_w, const void* conv_b, const void* norm_w,
+                             float eps, const void* conv_state_in, void* conv_state_out,
+                             const float* ssm_state_in, float* ssm_state_out, void* out,
+                             void* workspace, size_t ws_bytes, void* stream);
+int ssd_decode_step_packed(const ssd_dims* d, const void* zxbcdt_t, int64_t row_stride,
+                           const float* dt_bias, const float* A_log, const float* D,
+                           const void* conv_w, const void* conv_b, const void* norm_w, float eps,
+                           void* conv_state, float* ssm_state, void* y_t, void* stream);
 
 /*
  * ssd_mixer_prefill without a workspace argument, for callers that cannot

@@ -26,7 +26,8 @@ SSD_FLAG_FP32_OPERANDS = 1
 EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "ssd_validate",
            "ssd_status_str", "ssd_conv1d", "ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan",
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_mixer_prefill_workspace_bytes",
-           "ssd_mixer_prefill", "ssd_mixer_prefill_noalloc", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
+           "ssd_mixer_prefill", "ssd_mixer_prefill_packed", "ssd_decode_step_packed",
+           "ssd_mixer_prefill_noalloc", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
            "ssd_profile_start", "ssd_profile_stop", "ssd_profile_read", "ssd_kernel_name")
 
 
@@ -64,6 +65,10 @@ def load():
         "ssd_mixer_prefill_workspace_bytes": (sz, [P]),
         "ssd_mixer_prefill": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
                                     vp, sz, vp]),
+        "ssd_mixer_prefill_packed": (i32, [P, vp, i64, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                           vp, vp, vp, sz, vp]),
+        "ssd_decode_step_packed": (i32, [P, vp, i64, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                         vp]),
         "ssd_mixer_prefill_noalloc": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                             vp, vp, vp]),
         "ssd_workspace_status": (i32, [vp, vp]),

@@ -162,13 +162,15 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
 }
 
 // x_f32: x, B and C are fp32 (the conv's internal copy), else the I/O type.
-int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const float* A,
-             const float* D, const void* Bm, const void* Cm, int64_t bs, bool x_f32, const void* z,
-             const void* norm_w, float eps, const float* s_in, float* s_out, void* y,
-             const ScanWs& ws, hipStream_t st) {
+// dta: dt's token stride and preprocessing (A holds A_log when dta.bias is
+// set); zs: z's token stride.
+int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const DtA& dta,
+             const float* A, const float* D, const void* Bm, const void* Cm, int64_t bs,
+             bool x_f32, const void* z, int64_t zs, const void* norm_w, float eps,
+             const float* s_in, float* s_out, void* y, const ScanWs& ws, hipStream_t st) {
   const bool bf = d->io_dtype == SSD_BF16;
   ssd::ScanShape s{d->batch, d->seqlen, d->nheads, d->headdim, d->ngroups,
-                   d->dstate, d->chunk, (int)nchunks(d)};
+                   d->dstate, d->chunk, (int)nchunks(d), dta};
   const bool fo = f32op(d);
   int rc = hip_status(ssd::launch_chunk_state(bf, x_f32, fo, s, x, xs, dt, A, Bm, bs, ws.states,
                                               ws.lam_end, ws.status, st));
@@ -182,16 +184,16 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
   if (rc) return rc;
   if (fused_norm)
     rc = hip_status(ssd::launch_gated_norm(bf, true, d->batch * d->seqlen,
-                                           d->nheads * d->headdim, d->ngroups, ws.y32, z,
+                                           d->nheads * d->headdim, d->ngroups, ws.y32, z, zs,
                                            norm_w, eps, y, st));
   return rc;
 }
 
 int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const void* Cm,
-             int64_t xs, int64_t bs, const void* dt, const float* A, const float* D,
-             const void* conv_w, const void* conv_b, const void* conv_in, const void* z,
-             const void* norm_w, float eps, const float* s_in, float* s_out, void* y,
-             const ScanWs& ws, hipStream_t st) {
+             int64_t xs, int64_t bs, const void* dt, const DtA& dta, const float* A,
+             const float* D, const void* conv_w, const void* conv_b, const void* conv_in,
+             const void* z, int64_t zs, const void* norm_w, float eps, const float* s_in,
+             float* s_out, void* y, const ScanWs& ws, hipStream_t st) {
   ssd::FastScanArgs a{};
   a.B = d->batch;
   a.L = d->seqlen;
@@ -205,6 +207,9 @@ int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const 
   a.dt = dt;
   a.A = A;
   a.D = D;
+  a.dts = dta.dts;
+  a.zs = zs;
+  a.dt_bias = dta.bias;
   a.conv = conv;
   a.conv_w = conv_w;
   a.conv_b = conv_b;
@@ -219,6 +224,44 @@ int run_fast(const ssd_dims* d, bool conv, const void* x, const void* Bm, const 
   a.status = ws.status;
   a.spin_max = g_spin_limit.load(std::memory_order_relaxed);
   return hip_status(ssd::launch_fast_scan(a, st));
+}
+
+// The launches of a whole prefill (arguments already checked): xbc rows with
+// token stride xs, z with token stride zs (or null), dt per dta.
+int run_prefill(const ssd_dims* d, const void* xbc, int64_t xs, const void* z, int64_t zs,
+                const void* dt, const DtA& dta, const float* A, const float* D,
+                const void* conv_w, const void* conv_b, const void* norm_w, float eps,
+                const void* conv_state_in, void* conv_state_out, const float* ssm_state_in,
+                float* ssm_state_out, void* out, void* workspace, hipStream_t st) {
+  const ScanWs ws = carve(d, workspace, true);
+  const bool bf = d->io_dtype == SSD_BF16;
+  const size_t e = esize(d), C = channels(d), HP = (size_t)d->nheads * d->headdim;
+  const int64_t GN = (int64_t)d->ngroups * d->dstate;
+  int rc;
+  if (ws.fast) {
+    // conv recomputed inside the scan kernels; the new conv state is taken
+    // after them because they read conv_state_in (which it may overwrite).
+    const unsigned char* xb = (const unsigned char*)xbc;
+    rc = run_fast(d, true, xbc, xb + HP * e, xb + (HP + GN) * e, xs, xs, dt, dta, A, D, conv_w,
+                  conv_b, conv_state_in, z, zs, norm_w, eps, ssm_state_in, ssm_state_out, out,
+                  ws, st);
+    if (rc || !conv_state_out) return rc;
+    return hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
+                                             xs, conv_state_in, conv_state_out, st));
+  }
+  // the conv output stays fp32 for the scan: with a conv bias, B and C carry
+  // a shared offset whose C.B products cancel, so their rounding matters
+  rc = hip_status(ssd::launch_conv1d(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc, xs,
+                                     conv_w, conv_b, conv_state_in, ws.conv, C, true, st));
+  if (rc) return rc;
+  if (conv_state_out) {
+    rc = hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
+                                           xs, conv_state_in, conv_state_out, st));
+    if (rc) return rc;
+  }
+  const unsigned char* v = ws.conv;
+  return run_scan(d, v, C, dt, dta, A, D, v + HP * 4, v + (HP + GN) * 4, C, true, z, zs, norm_w,
+                  eps, ssm_state_in, ssm_state_out, out, ws, st);
 }
 
 }  // namespace
@@ -333,12 +376,13 @@ int ssd_chunk_scan(const ssd_dims* d, const void* x, int64_t x_tok_stride, const
                {workspace, need.total, true, -1}}))
     return SSD_ERR_ALIAS;
   const ScanWs ws = carve(d, workspace, false);
+  const DtA plain{d->nheads, nullptr};
   if (ws.fast)
-    return run_fast(d, false, x, Bm, Cm, x_tok_stride, bc_tok_stride, dt, A, D, nullptr, nullptr,
-                    nullptr, z, norm_w, eps, ssm_state_in, ssm_state_out, y, ws,
+    return run_fast(d, false, x, Bm, Cm, x_tok_stride, bc_tok_stride, dt, plain, A, D, nullptr,
+                    nullptr, nullptr, z, HP, norm_w, eps, ssm_state_in, ssm_state_out, y, ws,
                     (hipStream_t)stream);
-  return run_scan(d, x, x_tok_stride, dt, A, D, Bm, Cm, bc_tok_stride, false, z, norm_w, eps,
-                  ssm_state_in, ssm_state_out, y, ws, (hipStream_t)stream);
+  return run_scan(d, x, x_tok_stride, dt, plain, A, D, Bm, Cm, bc_tok_stride, false, z, HP,
+                  norm_w, eps, ssm_state_in, ssm_state_out, y, ws, (hipStream_t)stream);
 }
 
 int ssd_gated_rmsnorm(const ssd_dims* d, const void* y, const void* z, const void* w, float eps,
@@ -355,7 +399,8 @@ int ssd_gated_rmsnorm(const ssd_dims* d, const void* y, const void* z, const voi
     return SSD_ERR_ALIAS;
   return hip_status(ssd::launch_gated_norm(d->io_dtype == SSD_BF16, false,
                                            d->batch * d->seqlen, d->nheads * d->headdim,
-                                           d->ngroups, y, z, w, eps, out, (hipStream_t)stream));
+                                           d->ngroups, y, z, (int64_t)d->nheads * d->headdim, w,
+                                           eps, out, (hipStream_t)stream));
 }
 
 int ssd_decode_step(const ssd_dims* d, const void* xbc_t, const void* z_t, const void* dt_t,
@@ -388,8 +433,9 @@ int ssd_decode_step(const ssd_dims* d, const void* xbc_t, const void* z_t, const
     return SSD_ERR_ALIAS;
   return hip_status(ssd::launch_decode(d->io_dtype == SSD_BF16, d->batch, d->nheads,
                                        d->headdim, d->ngroups, d->dstate, d->conv_width, xbc_t,
-                                       z_t, dt_t, A, D, conv_w, conv_b, norm_w, eps, conv_state,
-                                       ssm_state, y_t, (hipStream_t)stream));
+                                       (int64_t)C, z_t, (int64_t)HP, dt_t,
+                                       DtA{d->nheads, nullptr}, A, D, conv_w, conv_b, norm_w, eps,
+                                       conv_state, ssm_state, y_t, (hipStream_t)stream));
 }
 
 size_t ssd_mixer_prefill_workspace_bytes(const ssd_dims* d) {
@@ -433,33 +479,91 @@ int ssd_mixer_prefill(const ssd_dims* d, const void* xbc, const void* z, const v
                {out, no, true, -1},
                {workspace, need.total, true, -1}}))
     return SSD_ERR_ALIAS;
-  const ScanWs ws = carve(d, workspace, true);
-  hipStream_t st = (hipStream_t)stream;
-  const bool bf = d->io_dtype == SSD_BF16;
-  const int64_t GN = (int64_t)d->ngroups * d->dstate;
-  if (ws.fast) {
-    // conv recomputed inside the scan kernels; the new conv state is taken
-    // after them because they read conv_state_in (which it may overwrite).
-    const unsigned char* xb = (const unsigned char*)xbc;
-    rc = run_fast(d, true, xbc, xb + HP * e, xb + (HP + GN) * e, C, C, dt, A, D, conv_w, conv_b,
-                  conv_state_in, z, norm_w, eps, ssm_state_in, ssm_state_out, out, ws, st);
-    if (rc || !conv_state_out) return rc;
-    return hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
-                                             C, conv_state_in, conv_state_out, st));
-  }
-  // the conv output stays fp32 for the scan: with a conv bias, B and C carry
-  // a shared offset whose C.B products cancel, so their rounding matters
-  rc = hip_status(ssd::launch_conv1d(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc, C,
-                                     conv_w, conv_b, conv_state_in, ws.conv, C, true, st));
+  return run_prefill(d, xbc, (int64_t)C, z, (int64_t)HP, dt, DtA{d->nheads, nullptr}, A, D,
+                     conv_w, conv_b, norm_w, eps, conv_state_in, conv_state_out, ssm_state_in,
+                     ssm_state_out, out, workspace, (hipStream_t)stream);
+}
+
+int ssd_mixer_prefill_packed(const ssd_dims* d, const void* zxbcdt, int64_t row_stride,
+                             const float* dt_bias, const float* A_log, const float* D,
+                             const void* conv_w, const void* conv_b, const void* norm_w,
+                             float eps, const void* conv_state_in, void* conv_state_out,
+                             const float* ssm_state_in, float* ssm_state_out, void* out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_dims(SSD_ENTRY_MIXER_PREFILL, d);
   if (rc) return rc;
-  if (conv_state_out) {
-    rc = hip_status(ssd::launch_conv_state(bf, d->batch, d->seqlen, (int)C, d->conv_width, xbc,
-                                           C, conv_state_in, conv_state_out, st));
-    if (rc) return rc;
-  }
-  const unsigned char* v = ws.conv;
-  return run_scan(d, v, C, dt, A, D, v + HP * 4, v + (HP + GN) * 4, C, true, z, norm_w, eps,
-                  ssm_state_in, ssm_state_out, out, ws, st);
+  if (!zxbcdt || !dt_bias || !A_log || !conv_w || !norm_w || !out) return SSD_ERR_NULL;
+  const size_t e = esize(d), T = (size_t)d->batch * d->seqlen, C = channels(d);
+  const size_t HP = (size_t)d->nheads * d->headdim, width = HP + C + d->nheads;
+  if (row_stride < (int64_t)width) return SSD_ERR_SHAPE;
+  if (!aligned16(zxbcdt) || (row_stride * e) % 16 || !aligned16(dt_bias) || !aligned16(A_log) ||
+      !aligned16(D) || !aligned16(conv_w) || !aligned16(conv_b) || !aligned16(norm_w) ||
+      !aligned16(conv_state_in) || !aligned16(conv_state_out) || !aligned16(ssm_state_in) ||
+      !aligned16(ssm_state_out) || !aligned16(out))
+    return SSD_ERR_ALIGN;
+  const ScanWs need = carve(d, nullptr, true);
+  if (!workspace || ws_bytes < need.total || ((uintptr_t)workspace % kWsAlign))
+    return SSD_ERR_WORKSPACE;
+  const size_t nrow = ((T - 1) * row_stride + width) * e, no = T * HP * e,
+               ncs = (size_t)d->batch * (d->conv_width - 1) * C * e,
+               nss = (size_t)d->batch * HP * d->dstate * 4, nh = (size_t)d->nheads * 4;
+  if (aliased({{zxbcdt, nrow, false, -1},
+               {dt_bias, nh, false, -1},
+               {A_log, nh, false, -1},
+               {D, nh, false, -1},
+               {conv_w, C * d->conv_width * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {conv_state_in, ncs, false, 8},
+               {conv_state_out, ncs, true, 7},
+               {ssm_state_in, nss, false, 10},
+               {ssm_state_out, nss, true, 9},
+               {out, no, true, -1},
+               {workspace, need.total, true, -1}}))
+    return SSD_ERR_ALIAS;
+  const unsigned char* row = (const unsigned char*)zxbcdt;
+  return run_prefill(d, row + HP * e, row_stride, zxbcdt, row_stride, row + (HP + C) * e,
+                     DtA{row_stride, dt_bias}, A_log, D, conv_w, conv_b, norm_w, eps,
+                     conv_state_in, conv_state_out, ssm_state_in, ssm_state_out, out, workspace,
+                     (hipStream_t)stream);
+}
+
+int ssd_decode_step_packed(const ssd_dims* d, const void* zxbcdt_t, int64_t row_stride,
+                           const float* dt_bias, const float* A_log, const float* D,
+                           const void* conv_w, const void* conv_b, const void* norm_w, float eps,
+                           void* conv_state, float* ssm_state, void* y_t, void* stream) {
+  int rc = check_dims(SSD_ENTRY_DECODE_STEP, d);
+  if (rc) return rc;
+  if (!zxbcdt_t || !dt_bias || !A_log || !conv_w || !norm_w || !conv_state || !ssm_state || !y_t)
+    return SSD_ERR_NULL;
+  const size_t e = esize(d), B = d->batch, C = channels(d);
+  const size_t HP = (size_t)d->nheads * d->headdim, width = HP + C + d->nheads;
+  if (row_stride < (int64_t)width) return SSD_ERR_SHAPE;
+  if (!aligned16(zxbcdt_t) || (row_stride * e) % 16 || !aligned16(dt_bias) ||
+      !aligned16(A_log) || !aligned16(D) || !aligned16(conv_w) || !aligned16(conv_b) ||
+      !aligned16(norm_w) || !aligned16(conv_state) || !aligned16(ssm_state) || !aligned16(y_t))
+    return SSD_ERR_ALIGN;
+  const size_t nrow = ((B - 1) * row_stride + width) * e, ny = B * HP * e,
+               ncs = B * (d->conv_width - 1) * C * e, nss = B * HP * d->dstate * 4,
+               nh = (size_t)d->nheads * 4;
+  if (aliased({{zxbcdt_t, nrow, false, -1},
+               {dt_bias, nh, false, -1},
+               {A_log, nh, false, -1},
+               {D, nh, false, -1},
+               {conv_w, C * d->conv_width * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {conv_state, ncs, true, -1},
+               {ssm_state, nss, true, -1},
+               {y_t, ny, true, -1}}))
+    return SSD_ERR_ALIAS;
+  const unsigned char* row = (const unsigned char*)zxbcdt_t;
+  return hip_status(ssd::launch_decode(d->io_dtype == SSD_BF16, d->batch, d->nheads,
+                                       d->headdim, d->ngroups, d->dstate, d->conv_width,
+                                       row + HP * e, row_stride, zxbcdt_t, row_stride,
+                                       row + (HP + C) * e, DtA{row_stride, dt_bias}, A_log, D,
+                                       conv_w, conv_b, norm_w, eps, conv_state, ssm_state, y_t,
+                                       (hipStream_t)stream));
 }
 
 int ssd_workspace_status(const void* workspace, void* stream) {

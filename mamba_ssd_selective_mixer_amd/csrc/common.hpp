@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dta.hpp"
+
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -33,6 +35,20 @@ SSD_DEV float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr float kLog2e = 1.4426950408889634f;
 SSD_DEV float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 SSD_DEV float silu(float u) { return u * frcp(1.0f + fexp(-u)); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|), with log1p(e)
+// taken as log(u) e / (u - 1), u = 1 + e (exact when u rounds to 1).
+SSD_DEV float softplus(float v) {
+  const float e = fexp(-__builtin_fabsf(v));
+  const float u = 1.0f + e;
+  const float l = u == 1.0f ? e : __builtin_amdgcn_logf(u) * 0.6931471805599453f * e * frcp(u - 1.0f);
+  return __builtin_fmaxf(v, 0.0f) + l;
+}
+
+SSD_DEV float dt_of(float raw, const DtA& p, int h) {
+  return p.bias ? softplus(raw + p.bias[h]) : raw;
+}
+SSD_DEV float a_of(const float* A, const DtA& p, int h) { return p.bias ? -fexp(A[h]) : A[h]; }
 
 // ---- 8-element vector I/O (16 bytes for bf16, 32 bytes for fp32) ---------
 SSD_DEV void load8(const float* p, float (&v)[8]) {

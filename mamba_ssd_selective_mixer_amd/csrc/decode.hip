@@ -24,7 +24,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     const T* __restrict__ xbc, const T* __restrict__ z, const T* __restrict__ dt,
     const float* __restrict__ A, const float* __restrict__ D, const T* __restrict__ cw,
     const T* __restrict__ cb, const T* __restrict__ nw, float eps, T* __restrict__ conv_state,
-    float* __restrict__ ssm, T* __restrict__ y, int H, int P, int G, float inv_S) {
+    float* __restrict__ ssm, T* __restrict__ y, int64_t xrs, int64_t zrs, DtA dta, int H, int P,
+    int G, float inv_S) {
   extern __shared__ __align__(16) float sm[];
   const int g = blockIdx.x, b = blockIdx.y;
   const int hpg = H / G, S = hpg * P;
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     T* cs = conv_state + (int64_t)b * (W - 1) * C + c0;
 #pragma unroll
     for (int r = 0; r < W - 1; ++r) load8(cs + (int64_t)r * C, win[r]);
-    load8(xbc + (int64_t)b * C + c0, win[W - 1]);
+    load8(xbc + (int64_t)b * xrs + c0, win[W - 1]);
 #pragma unroll
     for (int r = 0; r < W - 1; ++r) store8(cs + (int64_t)r * C, win[r + 1]);
     float wv[W][8];
@@ -94,8 +95,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
       f32x4 nxt[kDecUnroll];
       if (hl + 1 < hpg) load_head(hl + 1, nxt);
       const int h = g * hpg + hl;
-      const float dtv = to_f(dt[(int64_t)b * H + h]);
-      const float al = fexp(dtv * A[h]);
+      const float dtv = dt_of(to_f(dt[(int64_t)b * dta.dts + h]), dta, h);
+      const float al = fexp(dtv * a_of(A, dta, h));
       const float Dh = D ? D[h] : 0.f;
       float* st = sb + (int64_t)hl * PN;
 #pragma unroll
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   } else {
     for (int hl = 0; hl < hpg; ++hl) {
       const int h = g * hpg + hl;
-      const float dtv = to_f(dt[(int64_t)b * H + h]);
-      const float al = fexp(dtv * A[h]);
+      const float dtv = dt_of(to_f(dt[(int64_t)b * dta.dts + h]), dta, h);
+      const float al = fexp(dtv * a_of(A, dta, h));
       const float Dh = D ? D[h] : 0.f;
       float* st = ssm + ((int64_t)b * H + h) * PN;
       for (int i0 = 0; i0 < iters; i0 += kDecUnroll) {
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   // 3. gated RMSNorm over the group's S channels (or the plain output).
   T* yo = y + (int64_t)b * HP + (int64_t)g * S;
   if (z) {
-    const T* zz = z + (int64_t)b * HP + (int64_t)g * S;
+    const T* zz = z + (int64_t)b * zrs + (int64_t)g * S;
     float ss = 0.f;
     for (int i = tid; i < S; i += kDecThreads) {
       const float q = ys[i] * silu(to_f(zz[i]));
@@ -182,9 +183,10 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
 
 template <class T>
 static hipError_t decode_dispatch(int B, int H, int P, int G, int N, int W, const void* xbc,
-                                  const void* z, const void* dt, const float* A, const float* D,
-                                  const void* cw, const void* cb, const void* nw, float eps,
-                                  void* conv_state, float* ssm, void* y, hipStream_t st) {
+                                  int64_t xrs, const void* z, int64_t zrs, const void* dt,
+                                  const DtA& dta, const float* A, const float* D, const void* cw,
+                                  const void* cb, const void* nw, float eps, void* conv_state,
+                                  float* ssm, void* y, hipStream_t st) {
   const int S = H / G * P;
   const size_t lds = (size_t)(2 * S + 2 * N) * sizeof(float);
   dim3 grid(G, B), block(kDecThreads);
@@ -192,7 +194,7 @@ static hipError_t decode_dispatch(int B, int H, int P, int G, int N, int W, cons
 #define SSD_DEC(NN, WW)                                                                          \
   hipLaunchKernelGGL((k_decode<T, NN, WW>), grid, block, lds, st, (const T*)xbc, (const T*)z,    \
                      (const T*)dt, A, D, (const T*)cw, (const T*)cb, (const T*)nw, eps,          \
-                     (T*)conv_state, ssm, (T*)y, H, P, G, inv_S)
+                     (T*)conv_state, ssm, (T*)y, xrs, zrs, dta, H, P, G, inv_S)
 #define SSD_DEC_W(NN)                     \
   switch (W) {                            \
     case 2: SSD_DEC(NN, 2); break;        \
@@ -212,15 +214,15 @@ static hipError_t decode_dispatch(int B, int H, int P, int G, int N, int W, cons
 }
 
 hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
-                         const void* xbc, const void* z, const void* dt, const float* A,
-                         const float* D, const void* cw, const void* cb, const void* nw,
-                         float eps, void* conv_state, float* ssm_state, void* y,
-                         hipStream_t st) {
+                         const void* xbc, int64_t xrs, const void* z, int64_t zrs,
+                         const void* dt, const DtA& dta, const float* A, const float* D,
+                         const void* cw, const void* cb, const void* nw, float eps,
+                         void* conv_state, float* ssm_state, void* y, hipStream_t st) {
   ProfScope ps(st, KID_DECODE);
-  return io_bf16 ? decode_dispatch<bf16>(B, H, P, G, N, W, xbc, z, dt, A, D, cw, cb, nw, eps,
-                                         conv_state, ssm_state, y, st)
-                 : decode_dispatch<float>(B, H, P, G, N, W, xbc, z, dt, A, D, cw, cb, nw, eps,
-                                          conv_state, ssm_state, y, st);
+  return io_bf16 ? decode_dispatch<bf16>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A, D, cw,
+                                         cb, nw, eps, conv_state, ssm_state, y, st)
+                 : decode_dispatch<float>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A, D, cw,
+                                          cb, nw, eps, conv_state, ssm_state, y, st);
 }
 
 }  // namespace ssd

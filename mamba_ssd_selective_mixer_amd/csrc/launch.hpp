@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "dta.hpp"
 #include "prof.hpp"
 #include <stdint.h>
 
@@ -10,6 +11,7 @@ namespace ssd {
 
 struct ScanShape {
   int B, L, H, P, G, N, Q, nc;
+  DtA dta;  // dt's token stride, and raw dt + bias / A_log or dt / A as given
 };
 
 // Depthwise causal conv + SiLU; io_bf16 selects bf16 (else fp32) elements;
@@ -20,16 +22,18 @@ hipError_t launch_conv1d(bool io_bf16, int B, int L, int C, int W, const void* x
 // conv_out[b] = last W-1 rows of [cin[b] ; xbc[b]] (safe when cout == cin).
 hipError_t launch_conv_state(bool io_bf16, int B, int L, int C, int W, const void* xbc,
                              int64_t xs, const void* cin, void* cout, hipStream_t st);
-// Grouped gated RMSNorm; y_f32 says y is fp32 (else io dtype).
+// Grouped gated RMSNorm; y_f32 says y is fp32 (else io dtype); zs: token
+// stride of z (elements; y and out are dense).
 hipError_t launch_gated_norm(bool io_bf16, bool y_f32, int rows, int HP, int G,
-                             const void* y, const void* z, const void* w, float eps,
+                             const void* y, const void* z, int64_t zs, const void* w, float eps,
                              void* out, hipStream_t st);
-// One decode token per sequence.
+// One decode token per sequence; xrs, zrs: row strides (elements) of the
+// token's xBC and z; dta: dt's row stride and preprocessing.
 hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
-                         const void* xbc, const void* z, const void* dt, const float* A,
-                         const float* D, const void* cw, const void* cb, const void* nw,
-                         float eps, void* conv_state, float* ssm_state, void* y,
-                         hipStream_t st);
+                         const void* xbc, int64_t xrs, const void* z, int64_t zrs,
+                         const void* dt, const DtA& dta, const float* A, const float* D,
+                         const void* cw, const void* cb, const void* nw, float eps,
+                         void* conv_state, float* ssm_state, void* y, hipStream_t st);
 // Chunked scan, three phases: chunk states, state passing, chunk outputs.
 // x_f32: x, B and C are fp32 (else the I/O type); dt and y are the I/O type.
 // f32op: fp32 MFMA operands for bf16 I/O too (else fp16). status: the call's
@@ -58,8 +62,10 @@ struct FastScanArgs {
   const void* Cm;     // C rows (conv mode: xBC + H*P + G*N)
   int64_t xs, bs;     // token strides (elements)
   const void* dt;
-  const float* A;
+  const float* A;     // A, or A_log when dt_bias is set
   const float* D;
+  int64_t dts, zs;    // token strides of dt and z (elements)
+  const float* dt_bias;  // null: dt and A as given; else dt = softplus(dt + bias), A = -exp(A)
   bool conv;          // recompute conv + SiLU from raw xBC rows
   const void* conv_w;
   const void* conv_b;

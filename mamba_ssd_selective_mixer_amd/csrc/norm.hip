@@ -17,7 +17,7 @@ constexpr int kNormVec = 4;
 
 template <class T, class TY>
 __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
-                                                    const T* __restrict__ z,
+                                                    const T* __restrict__ z, int64_t zs,
                                                     const T* __restrict__ w, float eps,
                                                     T* out, int HP, int G) {
   const int64_t row = blockIdx.x;
@@ -27,6 +27,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
   if (S8 <= 64 * kNormVec) {
     for (int j = wave; j < G; j += 4) {
       const int64_t base = row * HP + (int64_t)j * S;
+      const int64_t zbase = row * zs + (int64_t)j * S;
       float q[kNormVec][8];
       float ss = 0.f;
 #pragma unroll
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
         if (v < S8) {
           float yv[8], zv[8];
           load8(y + base + v * 8, yv);
-          load8_stream(z + base + v * 8, zv);  // z is read once
+          load8_stream(z + zbase + v * 8, zv);  // z is read once
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             q[k][i] = yv[i] * silu(zv[i]);
@@ -61,11 +62,12 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
   }
   for (int j = wave; j < G; j += 4) {
     const int64_t base = row * HP + (int64_t)j * S;
+    const int64_t zbase = row * zs + (int64_t)j * S;
     float ss = 0.f;
     for (int v = lane; v < S8; v += 64) {
       float yv[8], zv[8];
       load8(y + base + v * 8, yv);
-      load8(z + base + v * 8, zv);
+      load8(z + zbase + v * 8, zv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q = yv[i] * silu(zv[i]);
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
     for (int v = lane; v < S8; v += 64) {
       float yv[8], zv[8], wv[8], o[8];
       load8(y + base + v * 8, yv);
-      load8(z + base + v * 8, zv);
+      load8(z + zbase + v * 8, zv);
       load8(w + (int64_t)j * S + v * 8, wv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] = yv[i] * silu(zv[i]) * wv[i] * inv;
@@ -87,20 +89,20 @@ __global__ __launch_bounds__(256) void k_gated_norm(const TY* y,
 }
 
 hipError_t launch_gated_norm(bool io_bf16, bool y_f32, int rows, int HP, int G, const void* y,
-                             const void* z, const void* w, float eps, void* out,
+                             const void* z, int64_t zs, const void* w, float eps, void* out,
                              hipStream_t st) {
   ProfScope ps(st, KID_GATED_NORM);
   dim3 grid(rows), block(256);
   if (io_bf16) {
     if (y_f32)
       hipLaunchKernelGGL((k_gated_norm<bf16, float>), grid, block, 0, st, (const float*)y,
-                         (const bf16*)z, (const bf16*)w, eps, (bf16*)out, HP, G);
+                         (const bf16*)z, zs, (const bf16*)w, eps, (bf16*)out, HP, G);
     else
       hipLaunchKernelGGL((k_gated_norm<bf16, bf16>), grid, block, 0, st, (const bf16*)y,
-                         (const bf16*)z, (const bf16*)w, eps, (bf16*)out, HP, G);
+                         (const bf16*)z, zs, (const bf16*)w, eps, (bf16*)out, HP, G);
   } else {
     hipLaunchKernelGGL((k_gated_norm<float, float>), grid, block, 0, st, (const float*)y,
-                       (const float*)z, (const float*)w, eps, (float*)out, HP, G);
+                       (const float*)z, zs, (const float*)w, eps, (float*)out, HP, G);
   }
   return hipGetLastError();
 }

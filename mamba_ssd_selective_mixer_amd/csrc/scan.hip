@@ -37,12 +37,12 @@ constexpr int kStatusNonFinite = 2;  // status bit: an output or the final state
 // Inclusive cumulative sum of a_s = dt_s * A over the chunk (s < len; zero
 // beyond) into lam[], and dt_s into dts[]. Q <= 256 = blockDim.
 template <class T>
-__device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, int64_t row0, int H, int h,
-                                             float Ah, int len, float* lam, float* dts,
-                                             float* wsum) {
+__device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, const DtA& dta,
+                                             int64_t row0, int h, float Ah, int len, float* lam,
+                                             float* dts, float* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float d = 0.f;
-  if (tid < len) d = to_f(dt[(row0 + tid) * H + h]);
+  if (tid < len) d = dt_of(to_f(dt[(row0 + tid) * dta.dts + h]), dta, h);
   const float v = wave_incl_scan(d * Ah);
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
@@ -62,7 +62,8 @@ template <class T, class TX, bool F32OP, int MAXT>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
     const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const TX* __restrict__ Bm, int64_t bs, float* __restrict__ states,
-    float* __restrict__ lam_end, int* status, int L, int H, int G, int P, int N, int Q, int nc) {
+    float* __restrict__ lam_end, int* status, DtA dta, int L, int H, int G, int P, int N, int Q,
+    int nc) {
   typedef OpT<T, F32OP> O;  // MFMA operand type
   using M = Mfma<O>;
   constexpr int KP = kStateSB + Pad<O>::v;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
   // this call's status word starts clear (later kernels only set bits)
   if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
 
-  chunk_cumsum<T>(dt, row0, H, h, A[h], len, lam, dts, wsum);
+  chunk_cumsum<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, wsum);
   const float lamE = lam[len - 1];
   wgt[tid] = tid < len ? fexp(lamE - lam[tid]) * dts[tid] : 0.f;
   __syncthreads();
@@ -188,8 +189,8 @@ template <class T, class TX, bool YF32, bool F32OP>
 __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
     const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const float* __restrict__ D, const TX* __restrict__ Bm, const TX* __restrict__ Cm, int64_t bs,
-    const float* __restrict__ states, void* __restrict__ yout, int* status, int L, int H, int G,
-    int P, int N, int Q, int nc) {
+    const float* __restrict__ states, void* __restrict__ yout, int* status, DtA dta, int L, int H,
+    int G, int P, int N, int Q, int nc) {
   typedef OpT<T, F32OP> O;  // MFMA operand type
   using M = Mfma<O>;
   const int QK = Q + Pad<O>::v;
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_out(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kk = M::KPL * (lane >> 4), rr = lane & 15;
 
-  chunk_cumsum<T>(dt, row0, H, h, A[h], len, lam, dts, wsum);
+  chunk_cumsum<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, wsum);
 
   const int P8 = P / 8;
   for (int v = tid; v < Q * P8; v += kScanThreads) {
@@ -322,8 +323,8 @@ hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanSh
   const bool t32 = s.P * s.N > 16 * 1024;  // tiles per wave beyond 16
 #define SSD_STATE_T(TT, TX, F, T)                                                              \
   hipLaunchKernelGGL((k_chunk_state<TT, TX, F, T>), grid, block, lds, st, (const TX*)x, xs,     \
-                     (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, status, s.L, s.H,    \
-                     s.G, s.P, s.N, s.Q, s.nc)
+                     (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, status, s.dta, s.L,  \
+                     s.H, s.G, s.P, s.N, s.Q, s.nc)
 #define SSD_STATE(TT, TX, F) \
   if (t32) SSD_STATE_T(TT, TX, F, 32); else SSD_STATE_T(TT, TX, F, 16)
   if (!io_bf16) {
@@ -361,7 +362,7 @@ hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShap
 #define SSD_OUT(TT, TX, YF, F)                                                                  \
   hipLaunchKernelGGL((k_chunk_out<TT, TX, YF, F>), grid, block, lds, st, (const TX*)x, xs,      \
                      (const TT*)dt, A, D, (const TX*)Bm, (const TX*)Cm, bs, states, y, status,  \
-                     s.L, s.H, s.G, s.P, s.N, s.Q, s.nc)
+                     s.dta, s.L, s.H, s.G, s.P, s.N, s.Q, s.nc)
 #define SSD_OUT_F(TT, TX, YF) \
   if (f32op) SSD_OUT(TT, TX, YF, true); else SSD_OUT(TT, TX, YF, false)
   if (!io_bf16) SSD_OUT(float, float, true, true);

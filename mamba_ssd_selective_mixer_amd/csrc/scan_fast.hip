@@ -52,6 +52,8 @@ struct Src {
   const bf16* cbias;  // conv bias [Cch] or null
   const bf16* cin;    // conv state in [B][W-1][Cch] or null
   int C, HP, GN;      // conv channels, H*P, G*N
+  int64_t zs;         // token stride of z (elements)
+  DtA dta;            // dt's token stride; raw dt + bias and A_log, or dt and A as given
 };
 
 // Internal MFMA operands are fp16 (11-bit mantissa, 8x finer than bf16):
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   // one exp2; w_s = exp(Lam_end - Lam_s) dt_s goes to dst[wave][s].
   auto cumsum = [&](int h0, float dr0, float dr1, float (*dst)[QI]) {
     const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
-    const float Ah = A[h0 + wave] * kLog2e;
+    const float Ah = a_of(A, s.dta, h0 + wave) * kLog2e;
     const float a0 = d0 * Ah, a1 = d1 * Ah;
     const float v = wave_incl_scan(a0 + a1);
     const float l0 = v - a1, l1 = v;
@@ -350,7 +352,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     dst[wave][tc + 1] = fexp2(lamE - l1) * d1;
     if (lane == 0) lam_end[((int64_t)b * H + h0 + wave) * nc + c] = lamE;
   };
-  auto dt_at = [&](int h, int t) { return to_f(dt[(row0 + min(t, len - 1)) * H + h]); };
+  auto dt_at = [&](int h, int t) {
+    return dt_of(to_f(dt[(row0 + min(t, len - 1)) * s.dta.dts + h]), s.dta, h);
+  };
 
   // dt of the first head block, fetched before B
   const float dr0 = dt_at(hg0 + wave, tc), dr1 = dt_at(hg0 + wave, tc + 1);
@@ -433,8 +437,8 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     // waited on right away would also wait for this block's stores)
     bf16 dn0 = {}, dn1 = {};
     if (more) {
-      dn0 = dt[(row0 + min(tc, len - 1)) * H + h0 + HB + wave];
-      dn1 = dt[(row0 + min(tc + 1, len - 1)) * H + h0 + HB + wave];
+      dn0 = dt[(row0 + min(tc, len - 1)) * s.dta.dts + h0 + HB + wave];
+      dn1 = dt[(row0 + min(tc + 1, len - 1)) * s.dta.dts + h0 + HB + wave];
     }
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
@@ -448,7 +452,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
         x_load<CONV>(xr[hh & 1], xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
       }
       // next block's decay weights, published by this iteration's barrier
-      if (hh == HB - 2 && more) cumsum(h0 + HB, to_f(dn0), to_f(dn1), wnext);
+      if (hh == HB - 2 && more)
+        cumsum(h0 + HB, dt_of(to_f(dn0), s.dta, h0 + HB + wave),
+               dt_of(to_f(dn1), s.dta, h0 + HB + wave), wnext);
       f32x4 acc[4][2];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -665,8 +671,10 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 
   // dt of head `wave`, positions 2 lane and 2 lane + 1, fetched before B/C
   const int tc = 2 * lane;
-  const float dr0 = to_f(dt[(row0 + min(tc, len - 1)) * H + h0 + wave]);
-  const float dr1 = to_f(dt[(row0 + min(tc + 1, len - 1)) * H + h0 + wave]);
+  const float dr0 =
+      dt_of(to_f(dt[(row0 + min(tc, len - 1)) * s.dta.dts + h0 + wave]), s.dta, h0 + wave);
+  const float dr1 =
+      dt_of(to_f(dt[(row0 + min(tc + 1, len - 1)) * s.dta.dts + h0 + wave]), s.dta, h0 + wave);
 
   const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
@@ -742,7 +750,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   // with Lam_ref the value at the end of s's 32-position block (<= Lam_s).
   {
     const float d0 = tc < len ? dr0 : 0.f, d1 = tc + 1 < len ? dr1 : 0.f;
-    const float Ah = A[h0 + wave] * kLog2e;  // Lam in log2 units
+    const float Ah = a_of(A, s.dta, h0 + wave) * kLog2e;  // Lam in log2 units
     const float a0 = d0 * Ah, a1 = d1 * Ah;
     const float v = wave_incl_scan(a0 + a1);
     const float l0 = v - a1, l1 = v;
@@ -849,7 +857,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
       zr[2 * e + hf] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          z + (row0 + min(t, len - 1)) * HP + h0 * P + hf * 128 + ev8 * 8));
+          z + (row0 + min(t, len - 1)) * s.zs + h0 * P + hf * 128 + ev8 * 8));
   };
 
   // causal mask of the diagonal 16 x 16 tiles, position r of this lane's
@@ -1207,6 +1215,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   s.C = a.H * P + 2 * a.G * N;
   s.HP = a.H * P;
   s.GN = a.G * N;
+  s.zs = a.zs;
+  s.dta = DtA{a.dts, a.dt_bias};
 
   // (chunk, 4-head block, batch): the chunk varies fastest in dispatch order
   const dim3 g1(nc, a.H / HB, a.B);
@@ -1260,8 +1270,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
 #undef SSD_FOUT
   e = hipGetLastError();
   if (e != hipSuccess || !norm_after) return e;
-  return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.norm_w, a.eps, a.y,
-                           st);
+  return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.zs, a.norm_w, a.eps,
+                           a.y, st);
 }
 
 }  // namespace ssd

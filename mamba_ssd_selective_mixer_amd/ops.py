@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -303,6 +304,87 @@ def ssd_mixer_prefill(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, eps=
                                        _stream(stream))
     _check(rc, "ssd_mixer_prefill")
     return out
+
+
+def _want_packed(t, name: str, d: SSDDims, lead: tuple) -> int:
+    """Packed projection rows [..., row] with row >= 2HP + 2GN + H, the row
+    dense; returns the row stride (elements between tokens)."""
+    width = 2 * d.hp + 2 * d.ngroups * d.dstate + d.nheads
+    if t.dtype != d.io_dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {d.io_dtype}")
+    if tuple(t.shape[:-1]) != lead or t.shape[-1] < width:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {list(lead)} + [>= {width}]")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: rows must be dense")
+    rs = t.stride(-2)
+    for i in range(len(lead) - 1):   # outer dims stack rows evenly
+        if lead[i] > 1 and t.stride(i) != rs * int(np.prod(lead[i + 1:])):
+            raise ValueError(f"{name}: outer strides must be multiples of the row stride")
+    return rs
+
+
+def ssd_mixer_prefill_packed(d: SSDDims, zxbcdt, dt_bias, A_log, D, conv_w, conv_b, norm_w,
+                             eps=1e-5, conv_state_in=None, conv_state_out=None,
+                             ssm_state_in=None, ssm_state_out=None, out=None, ws=None,
+                             stream=None):
+    """Prefill on the projection's packed rows [z | xBC | dt_raw] ([B, L, row]),
+    with dt = softplus(dt_raw + dt_bias) and A = -exp(A_log) formed in the
+    kernels."""
+    io, f32 = d.io_dtype, torch.float32
+    B, L, H, C = d.batch, d.seqlen, d.nheads, d.channels
+    rs = _want_packed(zxbcdt, "zxbcdt", d, (B, L))
+    _want(dt_bias, "dt_bias", f32, H)
+    _want(A_log, "A_log", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp)
+    ncs, nss = B * (d.conv_width - 1) * C, B * H * d.headdim * d.dstate
+    _want(conv_state_in, "conv_state_in", io, ncs, optional=True)
+    _want(conv_state_out, "conv_state_out", io, ncs, optional=True)
+    _want(ssm_state_in, "ssm_state_in", f32, nss, optional=True)
+    _want(ssm_state_out, "ssm_state_out", f32, nss, optional=True)
+    if out is None:
+        out = _alloc(stream, lambda: torch.empty(B, L, d.hp, dtype=io, device=zxbcdt.device))
+    _want(out, "out", io, B * L * d.hp)
+    need = ssd_mixer_prefill_workspace_bytes(d)
+    if ws is None:
+        ws = _alloc(stream, lambda: workspace(need, zxbcdt.device))
+    _want_ws(ws, need)
+    _need_cuda(zxbcdt, dt_bias, A_log, D, conv_w, conv_b, norm_w, conv_state_in, conv_state_out,
+               ssm_state_in, ssm_state_out, out, ws)
+    rc = _lib.load().ssd_mixer_prefill_packed(
+        ctypes.byref(d.c()), _p(zxbcdt), rs, _p(dt_bias), _p(A_log), _p(D), _p(conv_w),
+        _p(conv_b), _p(norm_w), float(eps), _p(conv_state_in), _p(conv_state_out),
+        _p(ssm_state_in), _p(ssm_state_out), _p(out), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "ssd_mixer_prefill_packed")
+    return out
+
+
+def ssd_decode_step_packed(d: SSDDims, zxbcdt_t, dt_bias, A_log, D, conv_w, conv_b, norm_w, eps,
+                           conv_state, ssm_state, y_t=None, stream=None):
+    """One decode token per sequence from packed rows [B, row]."""
+    io, f32 = d.io_dtype, torch.float32
+    B, H, C = d.batch, d.nheads, d.channels
+    rs = _want_packed(zxbcdt_t, "zxbcdt_t", d, (B,))
+    _want(dt_bias, "dt_bias", f32, H)
+    _want(A_log, "A_log", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp)
+    _want(conv_state, "conv_state", io, B * (d.conv_width - 1) * C)
+    _want(ssm_state, "ssm_state", f32, B * H * d.headdim * d.dstate)
+    if y_t is None:
+        y_t = _alloc(stream, lambda: torch.empty(B, d.hp, dtype=io, device=zxbcdt_t.device))
+    _want(y_t, "y_t", io, B * d.hp)
+    _need_cuda(zxbcdt_t, dt_bias, A_log, D, conv_w, conv_b, norm_w, conv_state, ssm_state, y_t)
+    rc = _lib.load().ssd_decode_step_packed(
+        ctypes.byref(d.c()), _p(zxbcdt_t), rs, _p(dt_bias), _p(A_log), _p(D), _p(conv_w),
+        _p(conv_b), _p(norm_w), float(eps), _p(conv_state), _p(ssm_state), _p(y_t),
+        _stream(stream))
+    _check(rc, "ssd_decode_step_packed")
+    return y_t
 
 
 def ssd_mixer_prefill_noalloc(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, out,

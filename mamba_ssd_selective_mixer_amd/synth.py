@@ -165,6 +165,65 @@ def initial_states(cfg: Cfg, batch: int | None = None, dtype: str | None = None)
     return {"conv_state": to_io(conv, dtype), "ssm_state": np.ascontiguousarray(ssm)}
 
 
+# ---------------------------------------------------------------- packed rows
+# The same draws in the projection's raw form: the per-token row is
+# [z | x | B | C | dt_raw] with dt_raw ~ N(0,1) (the normal that the recipe
+# above shifts by -2 and passes through softplus), and the layer carries
+# dt_bias = -2 and A_log ~ U(log 1, log 16) (the uniform whose exponential
+# the recipe above negates). `pad` extra columns per row (filled with 30000,
+# never read) make the row stride wider than the row.
+PAD_VALUE = 30000.0
+
+
+def packed_params(cfg: Cfg, slow_decay: bool = False, with_bias: bool = False,
+                  dtype: str | None = None) -> dict:
+    """A_log, dt_bias, D (fp32), conv weight (+ bias), norm weight, eps."""
+    dtype = dtype or cfg.dtype
+    r = rng(cfg.index, 0)
+    H, C, W = cfg.nheads, cfg.channels, cfg.conv_width
+    lo, hi = (math.log(0.005), math.log(0.05)) if slow_decay else (math.log(1.0), math.log(16.0))
+    A_log = r.uniform(lo, hi, H)
+    D = r.standard_normal(H)
+    conv_w = r.standard_normal((C, W), dtype=np.float32) * np.float32(0.5)
+    conv_b = r.standard_normal(C, dtype=np.float32) * np.float32(0.5) if with_bias else None
+    return {
+        "A_log": A_log.astype(np.float32),
+        "dt_bias": np.full(H, -2.0, dtype=np.float32),
+        "D": D.astype(np.float32),
+        "conv_w": to_io(conv_w, dtype),
+        "conv_b": None if conv_b is None else to_io(conv_b, dtype),
+        "norm_w": to_io(np.ones(cfg.hp, dtype=np.float32), dtype),
+        "eps": 1e-5,
+    }
+
+
+def packed_rows(cfg: Cfg, batch: int, seqlen: int, stream: int, pad: int = 0,
+                dtype: str | None = None) -> np.ndarray:
+    """[B, L, 2HP + 2GN + H + pad] rows [z | x | B | C | dt_raw | pad]."""
+    dtype = dtype or cfg.dtype
+    r = rng(cfg.index, stream)
+    Bn, L, H, P, G, N = batch, seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate
+    sn = np.float32(1.0 / math.sqrt(N))
+    x = r.standard_normal((Bn, L, H * P), dtype=np.float32)
+    Bm = r.standard_normal((Bn, L, G * N), dtype=np.float32) * sn
+    Cm = r.standard_normal((Bn, L, G * N), dtype=np.float32) * sn
+    z = r.standard_normal((Bn, L, H * P), dtype=np.float32)
+    raw = r.standard_normal((Bn, L, H)).astype(np.float32)
+    fill = np.full((Bn, L, pad), PAD_VALUE, dtype=np.float32)
+    return to_io(np.concatenate([z, x, Bm, Cm, raw, fill], axis=-1), dtype)
+
+
+def packed_prefill_inputs(cfg: Cfg, piece: int = 0, pad: int = 0, batch: int | None = None,
+                          seqlen: int | None = None, dtype: str | None = None) -> np.ndarray:
+    return packed_rows(cfg, batch or cfg.batch, seqlen or cfg.seqlen, 1 + piece, pad, dtype)
+
+
+def packed_decode_inputs(cfg: Cfg, step: int, pad: int = 0, batch: int | None = None,
+                         dtype: str | None = None) -> np.ndarray:
+    """One token per sequence: [B, row]."""
+    return packed_rows(cfg, batch or cfg.batch, 1, 1 + step, pad, dtype)[:, 0]
+
+
 def split_channels(cfg: Cfg, xbc: np.ndarray):
     """Views x [.., H, P], B [.., G, N], C [.., G, N] of a [.., Cch] array."""
     HP, GN = cfg.hp, cfg.gn

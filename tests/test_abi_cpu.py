@@ -309,3 +309,55 @@ def test_gated_rmsnorm_alias_every_pair(lib, o):
     # out may equal y (in place) but not sit partly over it
     assert lib.ssd_gated_rmsnorm(ctypes.byref(d), V(a["y"]), V(a["z"]), V(a["w"]), 1e-5,
                                  V(a["y"] + 256), None) == _ALIAS
+
+
+_PK_BUFS = ("row", "dtb", "alog", "D", "cw", "cb", "nw", "cs_in", "cs_out", "ss_in", "ss_out",
+            "out", "ws")
+_PK_W = ("cs_out", "ss_out", "out", "ws")
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_PK_BUFS, _PK_W,
+                                                 {"cs_out": "cs_in", "ss_out": "ss_in"}))
+def test_prefill_packed_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
+    a = {k: (i + 1) << 36 for i, k in enumerate(_PK_BUFS)}
+    a[w] = a[o] + off
+    rs = 2 * 2048 + 2 * 1024 + 32
+    rc = lib.ssd_mixer_prefill_packed(ctypes.byref(d), V(a["row"]), rs,
+                                      *(V(a[k]) for k in _PK_BUFS[1:7]), 1e-5,
+                                      *(V(a[k]) for k in _PK_BUFS[7:]), need, None)
+    assert rc == _ALIAS
+
+
+def test_packed_entries_refuse_before_launch(lib):
+    """Row stride narrower than [z | xBC | dt] or breaking the 16-byte rule,
+    missing dt_bias / A_log / norm weight: refused before any launch."""
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
+    width = 2 * 2048 + 2 * 1024 + 32
+    a = [V(k << 36) for k in range(1, 14)]
+
+    def pre(rs=width + 8, **kw):
+        args = list(a)
+        for i, v in kw.items():
+            args[int(i[1:])] = v
+        return lib.ssd_mixer_prefill_packed(ctypes.byref(d), args[0], rs, *args[1:7], 1e-5,
+                                            *args[7:], need, None)
+
+    assert pre(rs=width - 1) == -2
+    assert pre(rs=width + 1) == -8                 # (width + 1) * 2 bytes is not 16-aligned
+    assert pre(a1=None) == -1                      # dt_bias
+    assert pre(a2=None) == -1                      # A_log
+    assert pre(a6=None) == -1                      # norm weight
+    dd = dims(synth.CONFIGS["c4"], seqlen=1)
+    wdec = 2 * 16384 + 2 * 1024 + 256
+    assert lib.ssd_decode_step_packed(ctypes.byref(dd), a[0], wdec - 8, *a[1:7], 1e-5, *a[7:10],
+                                      None) == -2
+    assert lib.ssd_decode_step_packed(ctypes.byref(dd), a[0], wdec, None, *a[2:7], 1e-5,
+                                      *a[7:10], None) == -1
+    # y_t over the packed rows
+    assert lib.ssd_decode_step_packed(ctypes.byref(dd), a[0], wdec, *a[1:7], 1e-5, a[7], a[8],
+                                      V((1 << 36) + 4096), None) == -5
