@@ -71,7 +71,12 @@
  * states; in the fast path, used for bf16 I/O with headdim 64, dstate 128,
  * heads per group a multiple of 4, dims->chunk >= 64 and conv width 4 when
  * the call includes the conv, also the chunk states, and D x taken from x at
- * fp16 hi + lo precision). Those fp16 intermediates (activations after SiLU,
+ * fp16 hi + lo precision). The fp16 rounding of the carried-in states and of
+ * C bounds the error of the inter-chunk term by about 2^-11 times the sum of
+ * |C_n S_n| over the state, not |y|: inputs for which that sum is much larger
+ * than y (a conv bias with slowly decaying heads, A of order -0.01, measured
+ * at up to 8x the 2e-2 bf16 tolerance after the norm) need
+ * SSD_FLAG_FP32_OPERANDS. Those fp16 intermediates (activations after SiLU,
  * C B^T, chunk states, carried-in states, the scan output before the norm)
  * must stay within fp16 range (|v| < 65504); a value beyond it becomes
  * infinite, so the output or final state is not finite and
@@ -120,8 +125,14 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 /* ssd_dims.flags. SSD_FLAG_FP32_OPERANDS: run the chunked scan's dense
  * contractions on fp32 MFMA operands for bf16 I/O as well (every
- * intermediate keeps fp32 range; the general kernels are used, not the fused
- * ones). Unknown bits are refused (SSD_ERR_UNSUPPORTED). */
+ * intermediate keeps fp32 range and precision; the general kernels are used,
+ * not the fused ones). Needed when the inter-chunk term C . S_in is badly
+ * conditioned: B and C sharing a large offset (a conv bias does this) over
+ * slowly decaying heads make the state grow along that offset, and in some
+ * rows C . S_in is a sum of large terms that nearly cancel; fp16 operands
+ * resolve each term to 2^-11 of itself, and the norm divides by that row's
+ * small RMS (see "Precision" above). Unknown bits are refused
+ * (SSD_ERR_UNSUPPORTED). The workspace query takes the flag into account. */
 enum { SSD_FLAG_FP32_OPERANDS = 1 };
 
 typedef struct {

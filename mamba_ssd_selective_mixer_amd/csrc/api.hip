@@ -20,6 +20,7 @@ constexpr size_t kWsAlign = 256;
 
 size_t esize(const ssd_dims* d) { return d->io_dtype == SSD_BF16 ? 2 : 4; }
 bool f32op(const ssd_dims* d) { return (d->flags & SSD_FLAG_FP32_OPERANDS) != 0; }
+
 // bound on the polls of the fast path's cross-block norm exchange
 std::atomic<int> g_spin_limit{1 << 20};
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

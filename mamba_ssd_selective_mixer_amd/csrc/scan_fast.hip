@@ -601,12 +601,14 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
 // as [x_hi | x_lo] against [D_hi I ; D_hi I] and [D_lo I ; D_lo I], so the
 // largest term of y keeps ~22 mantissa bits (the norm divides by rms(q)).
 // Phases: B, C staged (conv) -> G tiles and C fragments in registers while
-// the carried-in states of the 4 heads are fetched -> states through LDS ->
-// the inter-chunk term for all heads (y kept as fp16 pairs) -> x of one head
-// at a time through two LDS buffers, the next head's rows loaded while the
-// current head is computed -> y through an LDS tile to a coalesced epilogue
-// that gates with z (prefetched), normalises each row over its 256 channels
-// and stores 16-byte vectors.
+// the first head's carried-in states are fetched -> per head: its x tile and
+// its carried-in states staged in LDS (the next head's rows and states
+// loaded meanwhile), the inter-chunk term, the intra-chunk term and D x
+// accumulated in the same fp32 registers (the first two can be large and of
+// opposite sign, so no rounding between them), y kept as fp16 pairs -> y
+// through an LDS tile to a coalesced epilogue that gates with z
+// (prefetched), normalises each row over its 256 channels and stores
+// 16-byte vectors.
 template <bool CONV, int NM, bool PREC>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
@@ -619,18 +621,19 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 bf16* __restrict__ out, float* part, int* sync,
                                                 int* status, int spin_max, int L, int H, int G,
                                                 int nc) {
-  static_assert(4 * P * RS <= 2 * QI * NS, "two x buffers fit the B/C space");
-  static_assert(HB * P * NS == 2 * QI * NS, "the 4 heads' states fill the B/C space");
+  static_assert(2 * P * RS + P * NS <= 2 * QI * NS, "x tile and one head's states fit");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
-  __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then states, then x buffers, then Ot
+  __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then x tile + states, then Ot
   __shared__ float lam[HB][QI], dts[HB][QI], csd[HB][QI];
   // conv weights ([channel][tap]) and bias of the block's HB * P x channels
   constexpr int kXW = CONV ? HB * P * W / 8 : 1, kXB = CONV ? HB * P / 8 : 1;
   __shared__ __align__(16) u32x4 XWl[kXW], XBl[kXB];
   f16* Bs = U;
   f16* Cs = U + QI * NS;
-  f16* Sl = U;  // [head][p][NS]: S_in
-  f16* Ot = U;  // [t][4 heads x p]: y
+  f16* XT = U;                // [p][RS]: fp16(x) of the current head
+  f16* XL = U + P * RS;       // [p][RS]: x - fp16(x)
+  f16* Sl = U + 2 * P * RS;   // [p][NS]: S_in of the current head
+  f16* Ot = U;                // [t][4 heads x p]: y
 
   int c, b, h0, tk = 0;
   if constexpr (NM == 2) {
@@ -772,15 +775,24 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     Cfa[ks] = *reinterpret_cast<const f16x8*>(Cs + (rta * 16 + rr) * NS + ks * 32 + kk);
     Cfb[ks] = *reinterpret_cast<const f16x8*>(Cs + (rtb * 16 + rr) * NS + ks * 32 + kk);
   }
-  // carried-in states of the 4 heads (contiguous [head][p][n]), in flight
-  // while the G tiles are computed
-  f16x8 sreg[16];
-  {
-    const f16* sp = sin_h + (((int64_t)b * nc + c) * H + h0) * (int64_t)(P * N);
+  // carried-in states of one head (contiguous [p][n], 16 KB): 4 x 16 bytes
+  // per thread, loaded a head ahead and staged into LDS with that head's x
+  const f16* sbase = sin_h + (((int64_t)b * nc + c) * H + h0) * (int64_t)(P * N);
+  u32x4 sreg[4];
+  auto s_load = [&](int hh) {
+    const f16* sp = sbase + (int64_t)hh * (P * N);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)  // read once: streaming loads
-      sreg[i] = __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(sp + (tid + NT * i) * 8));
-  }
+    for (int i = 0; i < 4; ++i)  // read once: streaming loads
+      sreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + (tid + NT * i) * 8));
+  };
+  auto s_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, v = idx & 15;  // row = p
+      *reinterpret_cast<u32x4*>(Sl + row * NS + v * 8) = sreg[i];
+    }
+  };
+  s_load(0);  // in flight while the G tiles are computed
   // (B C^T) tiles j <= rt of the wave's two row tiles: lane holds C_t.B_s for
   // t = 16 rt + rr and s = 16 j + 4 q4 + r (fp16, the MFMA operand precision).
   uint2 Ga[4], Gb[8];
@@ -798,48 +810,18 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     Gb[j] = make_uint2(pk(gb[0], gb[1]), pk(gb[2], gb[3]));
   }
   __syncthreads();  // B and C no longer read from LDS
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int idx = tid + NT * i, row = idx >> 4, v = idx & 15;  // row = head * P + p
-    *reinterpret_cast<f16x8*>(Sl + row * NS + v * 8) = sreg[i];
-  }
-  __syncthreads();
-
-  // y^T starts as the inter-chunk term S_in (exp(Lam_t) C_t)^T, kept as fp16
-  // pairs: [row tile][head][p tile][p = r4 + 0,1 | r4 + 2,3] at t = 16 rt + rr.
-  uint32_t yk[2][4][4][2];
-#pragma unroll
-  for (int hh = 0; hh < HB; ++hh) {
-    const float ea = fexp2(lam[hh][rta * 16 + rr]), eb = fexp2(lam[hh][rtb * 16 + rr]);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      f32x4 acc_a = zero4(), acc_b = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f16x8 sf =
-            *reinterpret_cast<const f16x8*>(Sl + (hh * P + pt * 16 + rr) * NS + ks * 32 + kk);
-        acc_a = mma16(sf, Cfa[ks], acc_a);
-        acc_b = mma16(sf, Cfb[ks], acc_b);
-      }
-      yk[0][hh][pt][0] = pk(ea * acc_a[0], ea * acc_a[1]);
-      yk[0][hh][pt][1] = pk(ea * acc_a[2], ea * acc_a[3]);
-      yk[1][hh][pt][0] = pk(eb * acc_b[0], eb * acc_b[1]);
-      yk[1][hh][pt][1] = pk(eb * acc_b[2], eb * acc_b[3]);
-      // materialise the packed values here (not next to their later uses),
-      // so the fp32 accumulators die at once
-      pin(yk[0][hh][pt]);
-      pin(yk[1][hh][pt]);
-    }
-  }
-  __syncthreads();  // states no longer read: the x buffers follow
-
   {
     ConvW<CONV> cwx;
     xw_get(cwx, xp0);
-    x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, U + xp0 * RS + xtb * 4,
-                        U + P * RS + xp0 * RS + xtb * 4, RS);
+    x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, XT + xp0 * RS + xtb * 4,
+                        XL + xp0 * RS + xtb * 4, RS);
+    s_store();
   }
   __syncthreads();
+
+  // y^T of the block: fp16 pairs [row tile][head][p tile][p = r4 + 0,1 |
+  // r4 + 2,3] at t = 16 rt + rr.
+  uint32_t yk[2][4][4][2];
 
   // epilogue mapping: 16 consecutive threads take one row (8 channels from
   // each 128-channel half), thread rows t = tid / 16 + 16 e; the z of the
@@ -867,11 +849,10 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   for (int r = 0; r < 4; ++r) dmask[r] = r4 + r <= rr;
 #pragma unroll
   for (int hh = 0; hh < HB; ++hh) {
-    const f16* XT = U + (hh & 1) * (2 * P * RS);  // [p][s]: fp16(x)
-    const f16* XL = XT + P * RS;                  // [p][s]: x - fp16(x)
     if (hh + 1 < HB) {
       const int ch = (h0 + hh + 1) * P + xp0;
       x_load<CONV, PREC>(xr, xb + ch, s.xs, t0 + xtb * 4, L - 1, s, ch, cin_b);
+      s_load(hh + 1);
     } else if (NM) {
 #pragma unroll
       for (int e = 0; e < ZPF; ++e) z_fetch(e);
@@ -892,14 +873,25 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       const int rt = ui == 0 ? rta : rtb;
       const int trow = rt * 16 + rr;  // this lane's token (B-operand column)
       const float lt = lam[hh][trow];
+      // inter-chunk term S_in (exp(Lam_t) C_t)^T first, in the accumulators
+      // the intra-chunk term is added to
       f32x4 acc[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const uint32_t* w2 = yk[ui][hh][pt];
-        acc[pt][0] = h2f_lo(w2[0]);
-        acc[pt][1] = h2f_hi(w2[0]);
-        acc[pt][2] = h2f_lo(w2[1]);
-        acc[pt][3] = h2f_hi(w2[1]);
+        acc[pt] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f16x8 sf =
+              *reinterpret_cast<const f16x8*>(Sl + (pt * 16 + rr) * NS + ks * 32 + kk);
+          acc[pt] = mma16(sf, ui == 0 ? Cfa[ks] : Cfb[ks], acc[pt]);
+        }
+      }
+      {
+        const float et = fexp2(lt);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[pt][r] *= et;
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -978,14 +970,15 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
         pin(yk[ui][hh][pt]);
       }
     }
+    __syncthreads();  // this head's x tile and states no longer read
     if (hh + 1 < HB) {
-      f16* nx = U + ((hh + 1) & 1) * (2 * P * RS);
       ConvW<CONV> cwx;
       xw_get(cwx, (hh + 1) * P + xp0);
-      x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, nx + xp0 * RS + xtb * 4,
-                          nx + P * RS + xp0 * RS + xtb * 4, RS);
+      x_store<CONV, true>(xr, cwx, t0 + xtb * 4, xnv, cin_b, nullptr, XT + xp0 * RS + xtb * 4,
+                          XL + xp0 * RS + xtb * 4, RS);
+      s_store();
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // Epilogue: 16 consecutive threads (one DPP row) take one token row, 8

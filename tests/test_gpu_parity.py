@@ -314,7 +314,7 @@ def test_decode_envelope(ops, base, kw, norm):
 
 # -------------------------------------------------------------- full prefill
 def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False, inplace=False,
-                 with_norm=True, A=None):
+                 with_norm=True, A=None, flags=0):
     """Whole path (conv -> scan -> norm) with state in/out; optional chaining
     over `pieces` (token boundaries) each resuming from the previous state.
     A, when given, replaces the drawn per-head decay rates."""
@@ -337,7 +337,7 @@ def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False,
         cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
     outs = []
     for a, b in zip(bounds[:-1], bounds[1:]):
-        d = make_dims(ops, cfg, seqlen=b - a)
+        d = make_dims(ops, cfg, seqlen=b - a, flags=flags)
         cs2 = cs if inplace else torch.empty_like(cs)
         ss2 = ss if inplace else torch.empty_like(ss)
         out = ops.ssd_mixer_prefill(d, dev(inp["xbc"][:, a:b], td),
@@ -386,6 +386,27 @@ def test_prefill_bf16_conv_bias_normed(ops, kw):
     """Conv bias with the gated norm, every output element within 2e-2 (the
     fp16 MFMA operands keep the shared-offset C.B^T sums precise enough)."""
     prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=True)
+
+
+FP16_ILL_CONDITIONED = pytest.mark.xfail(strict=True, reason=(
+    "fp16 MFMA operands: with a conv bias and slow decay C . S_in is a sum of large terms "
+    "that nearly cancel in some rows; rounding S_in and C to fp16 puts the normalised "
+    "output at 2-8x the tolerance there (SSD_FLAG_FP32_OPERANDS is the documented remedy)"))
+
+
+@pytest.mark.parametrize("flags", [1, pytest.param(0, marks=FP16_ILL_CONDITIONED)])
+@pytest.mark.parametrize("kw,pieces", [(dict(batch=1, seqlen=600), [2, 130, 257]),
+                                       (dict(nheads=64, batch=2, seqlen=300), None),
+                                       (dict(batch=2, seqlen=400, dstate=64), None)])
+def test_prefill_bias_slow_decay(ops, kw, pieces, flags):
+    """Conv bias with slow decay: B and C share an offset and the state grows
+    over hundreds of tokens, so some rows of y are small sums of large terms;
+    with fp32 operands (SSD_FLAG_FP32_OPERANDS) every element is within 2e-2.
+    The fp16-operand kernels (fused and general) are expected to miss the
+    tolerance on these inputs (a documented limit, checked so that a change in
+    either direction is seen)."""
+    prefill_case(ops, small("c1", **kw), with_state=True, pieces=pieces, slow=True,
+                 with_bias=True, flags=flags)
 
 
 @pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=2, seqlen=300))])
