@@ -58,6 +58,8 @@ def _bind(path: str):
     lib.oracle_dt_a.argtypes = [i64] * 2 + [dp] * 5
     lib.oracle_mixer_prefill_packed.argtypes = [i64] * 8 + [dp] * 7 + [ctypes.c_double] + [dp] * 5
     lib.oracle_decode_step_packed.argtypes = [i64] * 7 + [dp] * 7 + [ctypes.c_double] + [dp] * 3
+    lib.oracle_mixer_varlen.argtypes = ([i64] + [dp] * 3 + [i64] * 5 + [dp] * 8 + [ctypes.c_double]
+                                        + [dp] * 3)
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     return lib
@@ -199,6 +201,28 @@ class Oracle:
                                             _p(norm_w), float(eps), _p(cs), _p(ss), _p(out))
         return out, cs, ss
 
+    def mixer_varlen(self, cu_seqlens, slots, has_state, xbc, z, dt, A, D, conv_w, conv_b,
+                     norm_w, eps, H, P, G, N, conv_pool, ssm_pool):
+        """Sequences packed back to back (tokens [cu[i], cu[i+1]) of xbc [T, C],
+        z [T, HP], dt [T, H]), each resuming from its state slot (gllm PR #86,
+        "Validation": two sequences in one batch on separate slots, one
+        prefilling while the other decodes). Returns (out [T, HP], conv_pool',
+        ssm_pool') without touching the arguments."""
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        sl = np.ascontiguousarray(slots, dtype=np.int32)
+        hs = None if has_state is None else np.ascontiguousarray(has_state, dtype=np.uint8)
+        xbc, z, dt, A, D, conv_w, conv_b, norm_w = map(
+            _f64, (xbc, z, dt, A, D, conv_w, conv_b, norm_w))
+        cp = np.array(conv_pool, dtype=np.float64, copy=True, order="C")
+        sp = np.array(ssm_pool, dtype=np.float64, copy=True, order="C")
+        T = xbc.shape[0]
+        W = conv_w.shape[1]
+        out = np.zeros((T, H * P))
+        self._lib.oracle_mixer_varlen(len(sl), _p(cu), _p(sl), _p(hs), H, P, G, N, W, _p(xbc),
+                                      _p(z), _p(dt), _p(A), _p(D), _p(conv_w), _p(conv_b),
+                                      _p(norm_w), float(eps), _p(cp), _p(sp), _p(out))
+        return out, cp, sp
+
     def decode_step(self, xbc_t, z_t, dt_t, A, D, conv_w, conv_b, norm_w, eps, H, P, G, N,
                     conv_state, ssm_state):
         """One token per sequence; returns (out [B,HP], conv_state', ssm_state')
@@ -255,6 +279,10 @@ def mixer_prefill(*args, **kw):
 
 def decode_step(*args, **kw):
     return default().decode_step(*args, **kw)
+
+
+def mixer_varlen(*args, **kw):
+    return default().mixer_varlen(*args, **kw)
 
 
 def dt_a(*args, **kw):

@@ -299,6 +299,45 @@ void oracle_decode_step_packed(int64_t Bn, int64_t H, int64_t P, int64_t G, int6
   free(z); free(xbc); free(raw); free(dt); free(A);
 }
 
+/*
+ * Continuous batching over a state pool ("feat(model): Nemotron-H hybrid ...
+ * on the CPU", section "2. feat(model)": the state lives in the engine's
+ * slots; section "Validation": two sequences in one batch on separate slots,
+ * one prefilling while the other decodes). nseq sequences packed back to
+ * back: sequence i owns tokens [cu[i], cu[i+1]) of xbc [T, Cch], z [T, HP]
+ * (or NULL) and dt [T, H], and the state slot slots[i] of conv_pool
+ * [S, W-1, Cch] and ssm_pool [S, H, P, N]. It resumes from that slot when
+ * has_state[i] is nonzero (has_state NULL: always), else from zeros, runs
+ * the mixer prefill over its tokens (one token is a decode step), writes its
+ * outputs to out [T, HP] and its final states back into the same slot.
+ * Sequences with no tokens leave their slot as it is. Each sequence is
+ * computed by itself: the pool slots of a call are distinct.
+ */
+void oracle_mixer_varlen(int64_t nseq, const int32_t* cu, const int32_t* slots,
+                         const uint8_t* has_state, int64_t H, int64_t P, int64_t G, int64_t N,
+                         int64_t W, const double* xbc, const double* z, const double* dt,
+                         const double* A, const double* D, const double* conv_w,
+                         const double* conv_b, const double* norm_w, double eps,
+                         double* conv_pool, double* ssm_pool, double* out) {
+  const int64_t HP = H * P, C = HP + 2 * G * N, R = W - 1, SN = HP * N;
+  double* cs = (double*)malloc((size_t)(R * C + 1) * sizeof(double));
+  double* ss = (double*)malloc((size_t)SN * sizeof(double));
+  for (int64_t i = 0; i < nseq; ++i) {
+    const int64_t t0 = cu[i], L = cu[i + 1] - cu[i];
+    if (L <= 0) continue;
+    double* cslot = conv_pool + (int64_t)slots[i] * R * C;
+    double* sslot = ssm_pool + (int64_t)slots[i] * SN;
+    const int resume = has_state ? has_state[i] != 0 : 1;
+    oracle_mixer_prefill(1, L, H, P, G, N, W, xbc + t0 * C, z ? z + t0 * HP : NULL,
+                         dt + t0 * H, A, D, conv_w, conv_b, norm_w, eps,
+                         resume ? cslot : NULL, cs, resume ? sslot : NULL, ss, out + t0 * HP,
+                         NULL);
+    memcpy(cslot, cs, (size_t)(R * C) * sizeof(double));
+    memcpy(sslot, ss, (size_t)SN * sizeof(double));
+  }
+  free(cs); free(ss);
+}
+
 /* Threads the OpenMP runtime will use (reported beside CPU timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

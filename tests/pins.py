@@ -380,6 +380,53 @@ def pin_packed(orc):
     return max(errs)
 
 
+# Continuous batching over a state pool: ragged sequences packed back to back
+# (lengths 5, 1, 13, 0, 2, 1: prefills, decode steps, an empty sequence),
+# each on its own slot (out of order, unused slots in between, one fresh
+# sequence starting from zeros), equal the per-sequence prefill and decode
+# entries called one by one, with unused slots untouched.
+def pin_varlen(orc):
+    k = rand_mixer(18, Bn=1, L=22)
+    r = np.random.default_rng(19)
+    H, P, G, N, W = k["H"], k["P"], k["G"], k["N"], k["conv_w"].shape[1]
+    C, HP = H * P + 2 * G * N, H * P
+    lens = [5, 1, 13, 0, 2, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = np.array([4, 0, 7, 2, 5, 1], dtype=np.int32)
+    has = np.array([1, 1, 0, 1, 1, 1], dtype=np.uint8)
+    S = 8
+    cpool = 0.3 * r.standard_normal((S, W - 1, C))
+    spool = 0.3 * r.standard_normal((S, H, P, N))
+    xbc, z, dt = k["xbc"][0], k["z"][0], k["dt"][0]
+    out, cp, sp = orc.mixer_varlen(cu, slots, has, xbc, z, dt, k["A"], k["D"], k["conv_w"],
+                                   k["conv_b"], k["norm_w"], k["eps"], H, P, G, N, cpool, spool)
+    errs = []
+    cp_ref, sp_ref = cpool.copy(), spool.copy()
+    for i, L in enumerate(lens):
+        if L == 0:
+            continue
+        a, s_ = cu[i], slots[i]
+        cin = cpool[s_][None] if has[i] else np.zeros((1, W - 1, C))
+        sin = spool[s_][None] if has[i] else np.zeros((1, H, P, N))
+        if L == 1:
+            o, cs, ss = orc.decode_step(xbc[a:a + 1], z[a:a + 1], dt[a:a + 1], k["A"], k["D"],
+                                        k["conv_w"], k["conv_b"], k["norm_w"], k["eps"], H, P,
+                                        G, N, cin, sin)
+            errs.append(_rel(out[a], o[0]))
+        else:
+            res = orc.mixer_prefill(xbc[None, a:a + L], z[None, a:a + L], dt[None, a:a + L],
+                                    k["A"], k["D"], k["conv_w"], k["conv_b"], k["norm_w"],
+                                    k["eps"], H, P, G, N, conv_in=cin, s_in=sin)
+            errs.append(_rel(out[a:a + L], res["out"][0]))
+            cs, ss = res["conv_out"], res["s_out"]
+        cp_ref[s_], sp_ref[s_] = cs[0], ss[0]
+    errs += [_rel(cp, cp_ref), _rel(sp, sp_ref)]
+    untouched = [3, 6]  # slots no sequence uses, and slot 2 (empty sequence)
+    errs.append(float(np.max(np.abs(cp[untouched + [2]] - cpool[untouched + [2]]))))
+    errs.append(float(np.max(np.abs(sp[untouched + [2]] - spool[untouched + [2]]))))
+    return max(errs)
+
+
 PINS = {
     "unrolled": pin_unrolled,
     "chunked": pin_chunked,
@@ -396,6 +443,7 @@ PINS = {
     "worked_example": pin_worked_example,
     "dt_a": pin_dt_a,
     "packed": pin_packed,
+    "varlen": pin_varlen,
 }
 
 LIMITS = {name: 1e-11 for name in PINS}

@@ -45,6 +45,14 @@ MUTATIONS = {
         ("memcpy(xbc + i * C, r + HP, (size_t)C * sizeof(double));",
          "memcpy(xbc + i * C, r, (size_t)C * sizeof(double));")],
     "packed_dt_offset": [("memcpy(dt_raw + i * H, r + HP + C, ", "memcpy(dt_raw + i * H, r + C, ")],
+    "varlen_slot_ignored": [("double* sslot = ssm_pool + (int64_t)slots[i] * SN;",
+                             "double* sslot = ssm_pool + i * SN;")],
+    "varlen_fresh_not_zero": [("const int resume = has_state ? has_state[i] != 0 : 1;",
+                               "const int resume = 1;")],
+    "varlen_state_not_written": [("memcpy(sslot, ss, (size_t)SN * sizeof(double));",
+                                  "(void)ss;")],
+    "varlen_token_offset": [("oracle_mixer_prefill(1, L, H, P, G, N, W, xbc + t0 * C,",
+                             "oracle_mixer_prefill(1, L, H, P, G, N, W, xbc + i * C,")],
 }
 
 
