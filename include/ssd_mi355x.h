@@ -117,8 +117,11 @@ typedef enum {
                                exchange gave up waiting; its rows are NaN    */
   SSD_ERR_NONFINITE = -10,  /* (ssd_workspace_status) an output or the final
                                SSM state is infinite or NaN                  */
-  SSD_ERR_SCRATCH = -11     /* (ssd_mixer_prefill_noalloc) the call needs more
+  SSD_ERR_SCRATCH = -11,    /* (ssd_mixer_prefill_noalloc) the call needs more
                                scratch than the library's fixed buffer holds */
+  SSD_ERR_VARLEN = -12      /* (ssd_workspace_status) a ragged batch's offsets
+                               or slots failed the device checks; nothing of
+                               the call was written                          */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -277,6 +280,44 @@ int ssd_decode_step_packed(const ssd_dims* d, const void* zxbcdt_t, int64_t row_
                            const float* dt_bias, const float* A_log, const float* D,
                            const void* conv_w, const void* conv_b, const void* norm_w, float eps,
                            void* conv_state, float* ssm_state, void* y_t, void* stream);
+
+/*
+ * Continuous batching over a state pool: ragged sequences, prefilling and
+ * decoding, in one call ("feat(model): Nemotron-H hybrid ... on the CPU",
+ * section "2. feat(model)": the state lives in the engine's slots; section
+ * "Validation": two sequences in one batch on separate slots, one
+ * prefilling while the other decodes).
+ *   d->batch = number of sequences, d->seqlen = T, their total tokens.
+ *   cu_seqlens [batch + 1] int32 (device): sequence i owns tokens
+ *     [cu_seqlens[i], cu_seqlens[i+1]) of xbc [T, Cch], z [T, H*P] (or NULL)
+ *     and dt [T, H], all contiguous; a one-token sequence is a decode step.
+ *   slots [batch] int32 (device): the state slot of each sequence in
+ *     conv_pool [num_slots, W-1, Cch] (io_dtype) and ssm_pool
+ *     [num_slots, H, P, N] (fp32).
+ *   has_state [batch] uint8 (device) or NULL: sequence i resumes from its
+ *     slot when has_state[i] != 0 (NULL: every sequence), else starts from
+ *     zero states.
+ *   Each sequence's output rows go to out [T, H*P] and its final conv and
+ *   SSM states are written back into its slot; a sequence with no tokens
+ *   leaves its slot as it is. The kernels check on the device that
+ *   cu_seqlens starts at 0, ends at T and never decreases, and that every
+ *   slot of a sequence with tokens lies in [0, num_slots) and is used once;
+ *   a call that fails computes and writes nothing and
+ *   ssd_workspace_status() reports SSD_ERR_VARLEN.
+ *   Workspace: ssd_mixer_varlen_workspace_bytes(d, num_slots) (0 means the
+ *   shape is outside this entry's envelope). Envelope: the fused kernels'
+ *   (bf16 I/O, headdim 64, dstate 128, conv width 4, heads per group a
+ *   multiple of 4 and at most 128, no flags); otherwise
+ *   SSD_ERR_UNSUPPORTED. The pools are read and written in place; every
+ *   other buffer must not overlap them, out or the workspace.
+ */
+size_t ssd_mixer_varlen_workspace_bytes(const ssd_dims* d, int32_t num_slots);
+int ssd_mixer_varlen(const ssd_dims* d, const int32_t* cu_seqlens, const int32_t* slots,
+                     const uint8_t* has_state, int32_t num_slots, const void* xbc, const void* z,
+                     const void* dt, const float* A, const float* D, const void* conv_w,
+                     const void* conv_b, const void* norm_w, float eps, void* conv_pool,
+                     float* ssm_pool, void* out, void* workspace, size_t ws_bytes,
+                     void* stream);
 
 /*
  * ssd_mixer_prefill without a workspace argument, for callers that cannot

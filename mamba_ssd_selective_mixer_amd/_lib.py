@@ -19,7 +19,7 @@ ENTRY = {"conv1d": 0, "chunk_scan": 1, "gated_rmsnorm": 2, "decode_step": 3, "mi
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_DTYPE", -5: "SSD_ERR_ALIAS", -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_HIP",
           -8: "SSD_ERR_ALIGN", -9: "SSD_ERR_TIMEOUT", -10: "SSD_ERR_NONFINITE",
-          -11: "SSD_ERR_SCRATCH"}
+          -11: "SSD_ERR_SCRATCH", -12: "SSD_ERR_VARLEN"}
 SSD_FLAG_FP32_OPERANDS = 1
 
 # every symbol the header declares
@@ -27,6 +27,7 @@ EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "
            "ssd_status_str", "ssd_conv1d", "ssd_chunk_scan_workspace_bytes", "ssd_chunk_scan",
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_mixer_prefill_workspace_bytes",
            "ssd_mixer_prefill", "ssd_mixer_prefill_packed", "ssd_decode_step_packed",
+           "ssd_mixer_varlen_workspace_bytes", "ssd_mixer_varlen",
            "ssd_mixer_prefill_noalloc", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
            "ssd_profile_start", "ssd_profile_stop", "ssd_profile_read", "ssd_kernel_name")
 
@@ -69,6 +70,9 @@ def load():
                                            vp, vp, vp, sz, vp]),
         "ssd_decode_step_packed": (i32, [P, vp, i64, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                          vp]),
+        "ssd_mixer_varlen_workspace_bytes": (sz, [P, i32]),
+        "ssd_mixer_varlen": (i32, [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp,
+                                   vp, vp, sz, vp]),
         "ssd_mixer_prefill_noalloc": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                             vp, vp, vp]),
         "ssd_workspace_status": (i32, [vp, vp]),

@@ -298,6 +298,7 @@ const char* ssd_status_str(int status) {
     case SSD_ERR_TIMEOUT: return "a cross-workgroup norm exchange gave up waiting";
     case SSD_ERR_NONFINITE: return "an output or the final state is not finite";
     case SSD_ERR_SCRATCH: return "the call needs more scratch than the fixed buffer holds";
+    case SSD_ERR_VARLEN: return "ragged-batch offsets or slots are invalid (nothing was computed)";
     default: return "unknown status";
   }
 }
@@ -567,6 +568,96 @@ int ssd_decode_step_packed(const ssd_dims* d, const void* zxbcdt_t, int64_t row_
                                        (hipStream_t)stream));
 }
 
+size_t ssd_mixer_varlen_workspace_bytes(const ssd_dims* d, int32_t num_slots) {
+  if (check_dims(SSD_ENTRY_MIXER_PREFILL, d) || num_slots < 1) return 0;
+  if (!use_fast(d, true) || d->nheads / d->ngroups > ssd::fast_max_norm_heads()) return 0;
+  return round_up(4, kWsAlign) +
+         ssd::fast_varlen_ws_bytes(d->batch, d->seqlen, d->nheads, d->ngroups, num_slots);
+}
+
+int ssd_mixer_varlen(const ssd_dims* d, const int32_t* cu_seqlens, const int32_t* slots,
+                     const uint8_t* has_state, int32_t num_slots, const void* xbc, const void* z,
+                     const void* dt, const float* A, const float* D, const void* conv_w,
+                     const void* conv_b, const void* norm_w, float eps, void* conv_pool,
+                     float* ssm_pool, void* out, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  int rc = check_dims(SSD_ENTRY_MIXER_PREFILL, d);
+  if (rc) return rc;
+  if (num_slots < 1) return SSD_ERR_SHAPE;
+  if (!use_fast(d, true) || d->nheads / d->ngroups > ssd::fast_max_norm_heads())
+    return SSD_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !slots || !xbc || !dt || !A || !conv_w || !conv_pool || !ssm_pool || !out)
+    return SSD_ERR_NULL;
+  if (z && !norm_w) return SSD_ERR_NULL;
+  if (!aligned16(xbc) || !aligned16(z) || !aligned16(dt) || !aligned16(A) || !aligned16(D) ||
+      !aligned16(conv_w) || !aligned16(conv_b) || !aligned16(norm_w) || !aligned16(conv_pool) ||
+      !aligned16(ssm_pool) || !aligned16(out) || ((uintptr_t)cu_seqlens & 3) ||
+      ((uintptr_t)slots & 3))
+    return SSD_ERR_ALIGN;
+  const size_t need = ssd_mixer_varlen_workspace_bytes(d, num_slots);
+  if (!workspace || ws_bytes < need || ((uintptr_t)workspace % kWsAlign))
+    return SSD_ERR_WORKSPACE;
+  const size_t e = esize(d), T = (size_t)d->seqlen, C = channels(d), nseq = d->batch;
+  const size_t HP = (size_t)d->nheads * d->headdim, nh = (size_t)d->nheads * 4;
+  const size_t ncp = (size_t)num_slots * (d->conv_width - 1) * C * e,
+               nsp = (size_t)num_slots * HP * d->dstate * 4;
+  if (aliased({{xbc, T * C * e, false, -1},
+               {z, T * HP * e, false, -1},
+               {dt, T * d->nheads * e, false, -1},
+               {A, nh, false, -1},
+               {D, nh, false, -1},
+               {conv_w, C * d->conv_width * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {cu_seqlens, (nseq + 1) * 4, false, -1},
+               {slots, nseq * 4, false, -1},
+               {has_state, nseq, false, -1},
+               {conv_pool, ncp, true, -1},
+               {ssm_pool, nsp, true, -1},
+               {out, T * HP * e, true, -1},
+               {workspace, need, true, -1}}))
+    return SSD_ERR_ALIAS;
+  unsigned char* ws = (unsigned char*)workspace;
+  const int64_t GN = (int64_t)d->ngroups * d->dstate;
+  const unsigned char* xb = (const unsigned char*)xbc;
+  ssd::FastScanArgs a{};
+  a.B = d->batch;
+  a.L = d->seqlen;
+  a.H = d->nheads;
+  a.G = d->ngroups;
+  a.x = xbc;
+  a.Bm = xb + HP * e;
+  a.Cm = xb + (HP + GN) * e;
+  a.xs = (int64_t)C;
+  a.bs = (int64_t)C;
+  a.dt = dt;
+  a.A = A;
+  a.D = D;
+  a.dts = d->nheads;
+  a.zs = (int64_t)HP;
+  a.dt_bias = nullptr;
+  a.conv = true;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.conv_in = nullptr;
+  a.z = z;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.s_in = nullptr;
+  a.s_out = nullptr;
+  a.y = out;
+  a.status = (int*)ws;
+  a.ws = ws + round_up(4, kWsAlign);
+  a.spin_max = g_spin_limit.load(std::memory_order_relaxed);
+  a.q.cu = cu_seqlens;
+  a.q.slots = slots;
+  a.q.has_state = has_state;
+  a.q.conv_pool = conv_pool;
+  a.q.ssm_pool = ssm_pool;
+  a.num_slots = num_slots;
+  return hip_status(ssd::launch_fast_scan(a, (hipStream_t)stream));
+}
+
 int ssd_workspace_status(const void* workspace, void* stream) {
   if (!workspace) return SSD_ERR_NULL;
   if ((uintptr_t)workspace % kWsAlign) return SSD_ERR_WORKSPACE;
@@ -575,6 +666,7 @@ int ssd_workspace_status(const void* workspace, void* stream) {
   if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
     return SSD_ERR_HIP;
+  if (word & 4) return SSD_ERR_VARLEN;
   if (word & 1) return SSD_ERR_TIMEOUT;
   if (word & 2) return SSD_ERR_NONFINITE;
   return SSD_OK;

@@ -54,6 +54,20 @@ hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShap
 
 namespace ssd {
 
+// Ragged sequences over a state pool (continuous batching), or a dense batch
+// when cu is null. The chunk table (chunk_seq, chunk_first, valid) is built
+// on the device at the start of the call.
+struct Seqs {
+  const int32_t* cu;           // [nseq + 1] token offsets; null: dense batch
+  const int32_t* chunk_seq;    // [chunks] sequence owning each global chunk, -1 none
+  const int32_t* chunk_first;  // [nseq + 1] first global chunk of each sequence
+  const int32_t* slots;        // [nseq] state slot of each sequence
+  const uint8_t* has_state;    // [nseq] resume from the slot (else zeros), or null: all
+  const int* valid;            // 1 when the call's metadata passed the device checks
+  void* conv_pool;             // [slots, W-1, Cch] io dtype
+  float* ssm_pool;             // [slots, H, P, N] fp32
+};
+
 // Fast path (head_dim 64, d_state 128, bf16, heads per group a multiple of 4).
 struct FastScanArgs {
   int B, L, H, G;
@@ -79,9 +93,17 @@ struct FastScanArgs {
   void* ws;           // fast_ws_bytes(B, L, H, G, conv) bytes, 256-byte aligned
   int* status;        // the call's status word (cleared by the first kernel)
   int spin_max;       // bound on the cross-block norm's polls
+  // ragged batch (q.cu set): B sequences packed back to back (L = total
+  // tokens); states in pool slots; the table lives in the workspace
+  Seqs q;
+  int num_slots;
 };
 bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool conv);
 size_t fast_ws_bytes(int B, int L, int H, int G, bool conv);
+// ragged batch of nseq sequences, T tokens in all, over a pool of num_slots
+size_t fast_varlen_ws_bytes(int nseq, int T, int H, int G, int num_slots);
+// most 4-head blocks per norm group the fused exchange handles
+int fast_max_norm_heads();
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st);
 
 }  // namespace ssd

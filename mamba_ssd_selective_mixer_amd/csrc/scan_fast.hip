@@ -54,7 +54,42 @@ struct Src {
   int C, HP, GN;      // conv channels, H*P, G*N
   int64_t zs;         // token stride of z (elements)
   DtA dta;            // dt's token stride; raw dt + bias and A_log, or dt and A as given
+  Seqs q;             // ragged sequences over a state pool, or a dense batch (q.cu null)
 };
+
+// Where one chunk of one sequence lies. Dense batch: chunk c of sequence b,
+// all of length L. Ragged: global chunk c of the call's chunk table, whose
+// sequence, length and state slot come from the table. False for a chunk
+// no sequence owns (the table is padded) or when the table is invalid.
+struct ChunkGeo {
+  int64_t tok0;     // global token row of the sequence's token 0
+  int64_t kg;       // global chunk index: storage of dS / S_in / Lam_end
+  int L, t0, len;   // sequence length, chunk start within it, tokens in the chunk
+  const bf16* cin;  // the sequence's conv state rows, or null (zeros)
+};
+SSD_DEV bool chunk_geo(const Src& s, int c, int b, int L, int nc, ChunkGeo& g) {
+  if (!s.q.cu) {
+    g.tok0 = (int64_t)b * L;
+    g.kg = (int64_t)b * nc + c;
+    g.L = L;
+    g.t0 = c * QI;
+    g.len = min(QI, L - g.t0);
+    g.cin = s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
+    return true;
+  }
+  if (__builtin_amdgcn_readfirstlane(*s.q.valid) != 1) return false;
+  const int seq = __builtin_amdgcn_readfirstlane(s.q.chunk_seq[c]);
+  if (seq < 0) return false;
+  const int a = s.q.cu[seq];
+  g.tok0 = a;
+  g.kg = c;
+  g.L = s.q.cu[seq + 1] - a;
+  g.t0 = (c - s.q.chunk_first[seq]) * QI;
+  g.len = min(QI, g.L - g.t0);
+  const bool resume = !s.q.has_state || s.q.has_state[seq];
+  g.cin = resume ? (const bf16*)s.q.conv_pool + (int64_t)s.q.slots[seq] * (W - 1) * s.C : nullptr;
+  return true;
+}
 
 // Internal MFMA operands are fp16 (11-bit mantissa, 8x finer than bf16):
 // conv outputs, C.B^T, the masked decay matrix, chunk states and passed
@@ -326,17 +361,19 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
-  const int c = blockIdx.x, hpg = H / G;
-  const int b = blockIdx.z, g = blockIdx.y, hg0 = g * hpg;
-  const int t0 = c * QI, len = min(QI, L - t0);
-  const int64_t row0 = (int64_t)b * L + t0;
+  const int hpg = H / G, g = blockIdx.y, hg0 = g * hpg;
+  ChunkGeo cg;
+  if (!chunk_geo(s, blockIdx.x, blockIdx.z, L, nc, cg)) return;
+  L = cg.L;
+  const int t0 = cg.t0, len = cg.len;
+  const int64_t row0 = cg.tok0 + t0;
   // the wave index is uniform: read it into a scalar register
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
   const int tc = 2 * lane;
   // this call's status word starts clear (the later kernels of the call only
-  // set bits in it)
-  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
+  // set bits in it); with a ragged batch the table kernel cleared it
+  if (!s.q.cu && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
 
   // Lam = inclusive cumsum of dt A over the chunk for head h0 + wave (flat
   // past len, where dt counts as 0), kept in log2 units so every decay is
@@ -350,7 +387,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     const float lamE = lane_value(l1, 63);
     dst[wave][tc] = fexp2(lamE - l0) * d0;
     dst[wave][tc + 1] = fexp2(lamE - l1) * d1;
-    if (lane == 0) lam_end[((int64_t)b * H + h0 + wave) * nc + c] = lamE;
+    if (lane == 0) lam_end[cg.kg * H + h0 + wave] = lamE;
   };
   auto dt_at = [&](int h, int t) {
     return dt_of(to_f(dt[(row0 + min(t, len - 1)) * s.dta.dts + h]), s.dta, h);
@@ -359,9 +396,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   // dt of the first head block, fetched before B
   const float dr0 = dt_at(hg0 + wave, tc), dr1 = dt_at(hg0 + wave, tc + 1);
 
-  const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
-  const bf16* xb = s.x + (int64_t)b * L * s.xs;
-  const bf16* bb = s.b + (int64_t)b * L * s.bs;
+  const bf16* cin_b = CONV ? cg.cin : nullptr;
+  const bf16* xb = s.x + cg.tok0 * s.xs;
+  const bf16* bb = s.b + cg.tok0 * s.bs;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
   // of 4 tokens, 8 consecutive lanes on the 8 vectors of one block, so each
   // row load instruction reads whole 128-byte lines of 8 rows. The rows of
@@ -409,7 +446,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   if constexpr (PRE) {
     const int ch = s.HP + s.GN + g * N + n0;
     convw_load<CONV>(cwc, s, ch);
-    rows_load<CONV, 8>(rc, s.c + (int64_t)b * L * s.bs + g * N + n0, s.bs, tseq, L - 1, s, ch,
+    rows_load<CONV, 8>(rc, s.c + cg.tok0 * s.bs + g * N + n0, s.bs, tseq, L - 1, s, ch,
                        cin_b);
   }
   cumsum(hg0, dr0, dr1, wv[0]);
@@ -475,7 +512,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
         }
       }
       // lane: n = (nt0 + j) * 16 + r4 + r, p = (pt0 + pi) * 16 + rr
-      f16* o = states + (((int64_t)b * nc + c) * H + h0 + hh) * (int64_t)(P * N);
+      f16* o = states + (cg.kg * H + h0 + hh) * (int64_t)(P * N);
       // lanes q4 = 2m, 2m + 1 (16 apart) trade halves (an LDS-crossbar lane
       // swap, lane ^ 16) so each stores 16 bytes: the even one n-tile 2 jp,
       // the odd one n-tile 2 jp + 1. A store instruction then writes 64-byte
@@ -527,20 +564,39 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
                                                f16* sin_h, int* sync, float* part,
-                                               int64_t npart, int* status, int H, int nc) {
+                                               int64_t npart, int* status, Seqs q, int H,
+                                               int nc) {
   constexpr int PN = P * N;
   const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
   const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = (int64_t)b * H + h;
   {
     const int64_t gt = ((int64_t)(b * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
     const int64_t nt = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
     if (sync && gt < kParts) sync[gt] = 0;
     for (int64_t i = gt; i < npart; i += nt) part[i] = kUnset;
   }
+  // the chunks of sequence b (global chunk k0 onwards) and where its state
+  // comes from and goes to
+  int64_t k0;
+  const float* sin_p;
+  float* sout_p;
+  if (!q.cu) {
+    const int64_t bh = (int64_t)b * H + h;
+    k0 = (int64_t)b * nc;
+    sin_p = s_in ? s_in + bh * PN : nullptr;
+    sout_p = s_out ? s_out + bh * PN : nullptr;
+  } else {
+    if (__builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
+    if (q.cu[b + 1] - q.cu[b] <= 0) return;  // no tokens: the slot is left as it is
+    k0 = q.chunk_first[b];
+    nc = q.chunk_first[b + 1] - q.chunk_first[b];
+    float* slot = q.ssm_pool + ((int64_t)q.slots[b] * H + h) * PN;
+    sin_p = !q.has_state || q.has_state[b] ? slot : nullptr;
+    sout_p = slot;
+  }
   float S[kPassVec];
-  if (s_in) {
-    load8(s_in + bh * PN + e, S);
+  if (sin_p) {
+    load8(sin_p + e, S);
   } else {
 #pragma unroll
     for (int j = 0; j < kPassVec; ++j) S[j] = 0.f;
@@ -553,8 +609,8 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
       const int c = min(c0 + u, nc - 1);
       // each increment is read once: a streaming load
       d[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(dS + (((int64_t)b * nc + c) * H + h) * PN + e));
-      al[u] = fexp2(lam_end[bh * nc + c]);  // Lam_end in log2 units
+          reinterpret_cast<const u32x4*>(dS + ((k0 + c) * H + h) * PN + e));
+      al[u] = fexp2(lam_end[(k0 + c) * H + h]);  // Lam_end in log2 units
     }
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
@@ -565,7 +621,7 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
         o.y = pk(S[2], S[3]);
         o.z = pk(S[4], S[5]);
         o.w = pk(S[6], S[7]);
-        *reinterpret_cast<u32x4*>(sin_h + (((int64_t)b * nc + c) * H + h) * PN + e) = o;
+        *reinterpret_cast<u32x4*>(sin_h + ((k0 + c) * H + h) * PN + e) = o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           S[2 * j] = al[u] * S[2 * j] + h2f_lo(d[u][j]);
@@ -574,8 +630,8 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
       }
     }
   }
-  if (s_out) {
-    store8(s_out + bh * PN + e, S);
+  if (sout_p) {
+    store8(sout_p + e, S);
     float chk = 0.f;  // NaN when any element is infinite or NaN
 #pragma unroll
     for (int j = 0; j < kPassVec; ++j) chk += S[j] * 0.f;
@@ -665,8 +721,13 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     h0 = blockIdx.y * HB;
   }
   const int g = h0 / (H / G);
-  const int t0 = c * QI, len = min(QI, L - t0);
-  const int64_t row0 = (int64_t)b * L + t0;
+  // with a ragged batch, every block of a chunk no sequence owns returns
+  // here, before any exchange: its norm-group partners share the chunk
+  ChunkGeo cg;
+  if (!chunk_geo(s, c, b, L, nc, cg)) return;
+  L = cg.L;
+  const int t0 = cg.t0, len = cg.len;
+  const int64_t row0 = cg.tok0 + t0;
   // the wave index is uniform: read it into a scalar register
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rr = lane & 15, q4 = lane >> 4, kk = 8 * q4, r4 = 4 * q4;
@@ -679,14 +740,14 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   const float dr1 =
       dt_of(to_f(dt[(row0 + min(tc + 1, len - 1)) * s.dta.dts + h0 + wave]), s.dta, h0 + wave);
 
-  const bf16* cin_b = CONV && s.cin ? s.cin + (int64_t)b * (W - 1) * s.C : nullptr;
+  const bf16* cin_b = CONV ? cg.cin : nullptr;
   // x staging item of this thread (one head): 8 channel vectors x 32 blocks
   // of 4 tokens, 8 consecutive lanes on the 8 vectors of one block (whole
   // 128-byte lines per row load). The rows of head 0 are loaded with those
   // of B and C. With PREC the x rows (also read by the chunk-state kernel
   // before) are streamed: nothing reads them after this kernel.
   const int xtb = tid >> 3, xcv = tid & 7, xp0 = xcv * 8;
-  const bf16* xb = s.x + (int64_t)b * L * s.xs;
+  const bf16* xb = s.x + cg.tok0 * s.xs;
   const int xnv = min(4, max(0, len - xtb * 4));
   XRaw<CONV> xr;
   // this thread's piece of the block's x conv weights / bias, for XWl / XBl
@@ -711,14 +772,14 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   {
     const int cv = tid & 15, tbi = tid >> 4, n0 = cv * 8;
     const int tseq = t0 + tbi * 8, nv = min(8, max(0, len - tbi * 8));
-    const int64_t boff = (int64_t)b * L * s.bs + g * N + n0;
+    const int64_t boff = cg.tok0 * s.bs + g * N + n0;
     const int chb = s.HP + g * N + n0, chc = chb + s.GN;
     // rows of the precomputed buffers, clamped into the sequence
     auto pre_rows = [&](const f16* src, u32x4 (&v)[8]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         v[i] = *reinterpret_cast<const u32x4*>(
-            src + ((int64_t)b * L + min(tseq + i, L - 1)) * s.GN + g * N + n0);
+            src + (cg.tok0 + min(tseq + i, L - 1)) * s.GN + g * N + n0);
     };
     auto pre_put = [&](const u32x4 (&v)[8], f16* dst) {
 #pragma unroll
@@ -777,7 +838,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   }
   // carried-in states of one head (contiguous [p][n], 16 KB): 4 x 16 bytes
   // per thread, loaded a head ahead and staged into LDS with that head's x
-  const f16* sbase = sin_h + (((int64_t)b * nc + c) * H + h0) * (int64_t)(P * N);
+  const f16* sbase = sin_h + (cg.kg * H + h0) * (int64_t)(P * N);
   u32x4 sreg[4];
   auto s_load = [&](int hh) {
     const f16* sp = sbase + (int64_t)hh * (P * N);
@@ -1155,46 +1216,196 @@ bool wide(int H, int G) { return H / G > fast::HB; }
 constexpr int kMaxNormBlocks = 32;
 bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 }  // namespace
-size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
-  const size_t nc = (L + fast::QI - 1) / fast::QI;
-  const size_t PN = fast::P * fast::N;
-  const size_t rows = (size_t)B * L * G * fast::N * 2;
-  size_t n = ws_round((size_t)B * nc * H * PN * 2) + ws_round((size_t)B * H * nc * 4);
-  if (wide(H, G))
-    n += ws_round(nc * B * (H / fast::HB) * fast::QI * 4) + ws_round(fast::kParts * 4);
-  if (pre_c(H, G, conv)) n += 2 * ws_round(rows);
-  return n;
+// Byte offsets of the workspace pieces. Dense batch: B sequences of L
+// tokens, B * ceil(L / QI) chunks. Ragged batch (varlen): B sequences, L
+// tokens in all, at most ceil(L / QI) + B chunks (a padded table), plus the
+// chunk table and a bitmap of the pool's slots.
+struct FastLayout {
+  int64_t chunks, npart;
+  size_t dS, lam, part, sync, bcv, ccv, valid, first, cseq, bitmap, total;
+};
+FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int num_slots) {
+  using namespace fast;
+  FastLayout f{};
+  const size_t PN = P * N;
+  f.chunks = varlen ? (int64_t)(L + QI - 1) / QI + B : (int64_t)B * ((L + QI - 1) / QI);
+  f.npart = f.chunks * (H / HB) * QI;
+  const size_t rows = (size_t)(varlen ? L : (int64_t)B * L) * G * N * 2;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += ws_round(n);
+    return o;
+  };
+  f.dS = take((size_t)f.chunks * H * PN * 2);
+  f.lam = take((size_t)f.chunks * H * 4);
+  if (wide(H, G)) {
+    f.part = take((size_t)f.npart * 4);
+    f.sync = take(kParts * 4);
+  }
+  if (pre_c(H, G, conv)) {
+    f.bcv = take(rows);
+    f.ccv = take(rows);
+  }
+  if (varlen) {
+    f.valid = take(4);
+    f.first = take(((size_t)B + 1) * 4);
+    f.cseq = take((size_t)f.chunks * 4);
+    f.bitmap = take(((size_t)num_slots + 31) / 32 * 4);
+  }
+  f.total = off;
+  return f;
 }
+
+size_t fast_ws_bytes(int B, int L, int H, int G, bool conv) {
+  return fast_layout(B, L, H, G, conv, false, 0).total;
+}
+size_t fast_varlen_ws_bytes(int nseq, int T, int H, int G, int num_slots) {
+  return fast_layout(nseq, T, H, G, true, true, num_slots).total;
+}
+int fast_max_norm_heads() { return kMaxNormBlocks * fast::HB; }
+
+namespace fast {
+// The chunk table of a ragged batch, built by one workgroup at the start of
+// the call: sequence i owns tokens [cu[i], cu[i+1]) and ceil(len_i / QI)
+// consecutive global chunks from chunk_first[i]; chunk_seq maps each chunk
+// back (-1 past the last). Checks on the device what the host cannot see:
+// cu[0] == 0, cu[nseq] == T, no negative length, every slot of a sequence
+// with tokens inside the pool and used once (a bitmap). Any failure leaves
+// valid = 0 (every later kernel of the call then does nothing: no output,
+// no state is written) and sets the call's status bit.
+constexpr int kTableThreads = 1024;
+constexpr int kStatusVarlen = 4;  // status bit: the ragged batch's metadata is invalid
+__global__ __launch_bounds__(kTableThreads) void k_varlen_table(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int nseq, int T,
+    int num_slots, int32_t* chunk_first, int32_t* chunk_seq, int64_t max_chunks,
+    uint32_t* bitmap, int* valid, int* status) {
+  __shared__ int bad;
+  __shared__ int csum[kTableThreads];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    bad = 0;
+    *status = 0;  // this call's status word starts clear
+    *valid = 0;
+  }
+  const int nw = (num_slots + 31) / 32;
+  for (int i = tid; i < nw; i += kTableThreads) bitmap[i] = 0u;
+  __syncthreads();
+  // thread tid takes sequences [i0, i1)
+  const int per = (nseq + kTableThreads - 1) / kTableThreads;
+  const int i0 = min(nseq, tid * per), i1 = min(nseq, i0 + per);
+  int cnt = 0, err = 0;
+  if (tid == 0 && (cu[0] != 0 || cu[nseq] != T)) err = 1;
+  for (int i = i0; i < i1; ++i) {
+    const int len = cu[i + 1] - cu[i];
+    if (len < 0) {
+      err = 1;
+      continue;
+    }
+    if (len == 0) continue;
+    const int sl = slots[i];
+    if (sl < 0 || sl >= num_slots) {
+      err = 1;
+      continue;
+    }
+    const uint32_t bit = 1u << (sl & 31);
+    if (atomicOr(bitmap + (sl >> 5), bit) & bit) err = 1;  // slot used twice
+    cnt += (len + QI - 1) / QI;
+  }
+  if (err) atomicOr(&bad, 1);
+  // exclusive scan of the per-thread chunk counts
+  csum[tid] = cnt;
+  __syncthreads();
+  for (int d = 1; d < kTableThreads; d <<= 1) {
+    const int v = tid >= d ? csum[tid - d] : 0;
+    __syncthreads();
+    csum[tid] += v;
+    __syncthreads();
+  }
+  int base = csum[tid] - cnt;
+  const int total = csum[kTableThreads - 1];
+  for (int i = i0; i < i1; ++i) {
+    chunk_first[i] = base;
+    const int len = cu[i + 1] - cu[i];
+    const int n = len > 0 ? (len + QI - 1) / QI : 0;
+    for (int j = 0; j < n; ++j)  // bounded: garbage offsets only make the call invalid
+      if (base + j >= 0 && base + j < max_chunks) chunk_seq[base + j] = i;
+    base += n;
+  }
+  if (tid == 0) chunk_first[nseq] = total;
+  for (int64_t k = max(total, 0) + tid; k < max_chunks; k += kTableThreads) chunk_seq[k] = -1;
+  __syncthreads();
+  if (tid == 0) {
+    if (bad || total > max_chunks) {
+      atomicOr(status, kStatusVarlen);
+    } else {
+      // the table's global writes are ordered before the flag's
+      __threadfence();
+      *valid = 1;
+    }
+  }
+}
+
+// The new conv state of each sequence of a ragged batch: the last W-1 rows
+// of [its slot's rows (or zeros) ; its tokens], written back into the slot
+// (in place: a row is read before any row it could overwrite).
+__global__ __launch_bounds__(256) void k_varlen_conv_state(const bf16* __restrict__ xbc,
+                                                           int64_t xs, Seqs q, int C) {
+  const int cv = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (cv * 8 >= C || __builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
+  const int a = q.cu[b], L = q.cu[b + 1] - a;
+  if (L <= 0) return;
+  bf16* slot = (bf16*)q.conv_pool + (int64_t)q.slots[b] * (W - 1) * C + cv * 8;
+  const bool resume = !q.has_state || q.has_state[b];
+#pragma unroll
+  for (int r = 0; r < W - 1; ++r) {
+    const int e = L + r;  // row of [state ; tokens]
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (e >= W - 1)
+      v = *reinterpret_cast<const u32x4*>(xbc + (a + e - (W - 1)) * xs + cv * 8);
+    else if (resume)
+      v = *reinterpret_cast<const u32x4*>(slot + (int64_t)e * C);
+    *reinterpret_cast<u32x4*>(slot + (int64_t)r * C) = v;
+  }
+}
+}  // namespace fast
 
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   using namespace fast;
-  const int nc = (a.L + QI - 1) / QI;
+  const bool varlen = a.q.cu != nullptr;
+  const FastLayout f = fast_layout(a.B, a.L, a.H, a.G, a.conv, varlen, a.num_slots);
+  // dense: (chunk, ., batch) grids; ragged: (global chunk, ., 1)
+  const int nc = varlen ? (int)f.chunks : (a.L + QI - 1) / QI;
+  const int gz = varlen ? 1 : a.B;
   const size_t PN = P * N;
   unsigned char* w = (unsigned char*)a.ws;
   // chunk increments, overwritten in place by the carried-in states
-  fast::f16* dS = (fast::f16*)w;
+  fast::f16* dS = (fast::f16*)(w + f.dS);
   fast::f16* sinb = dS;
-  w += ws_round((size_t)a.B * nc * a.H * PN * 2);
-  float* lam_end = (float*)w;
-  w += ws_round((size_t)a.B * a.H * nc * 4);
-  float* part = nullptr;
-  int* sync = nullptr;
-  const int64_t npart = (int64_t)nc * a.B * (a.H / HB) * QI;
-  if (wide(a.H, a.G)) {
-    part = (float*)w;
-    w += ws_round(npart * 4);
-    sync = (int*)w;
-    w += ws_round(kParts * 4);
-  }
+  float* lam_end = (float*)(w + f.lam);
+  float* part = wide(a.H, a.G) ? (float*)(w + f.part) : nullptr;
+  int* sync = wide(a.H, a.G) ? (int*)(w + f.sync) : nullptr;
+  const int64_t npart = f.npart;
   // output kernel epilogue: 0 = y, 1 = norm within the block, 2 = norm
   // across the group's blocks (its state is reset by the pass kernel); with
   // more than kMaxNormBlocks blocks per group, y and then the grouped norm
   const bool norm_after = a.z && a.H / a.G > kMaxNormBlocks * HB;
   const int nm = !a.z || norm_after ? 0 : wide(a.H, a.G) ? 2 : 1;
-  const size_t rows = (size_t)a.B * a.L * a.G * N * 2;
   const bool prec = pre_c(a.H, a.G, a.conv);
-  fast::f16* bcv = prec ? (fast::f16*)w : nullptr;
-  fast::f16* ccv = prec ? (fast::f16*)(w + ws_round(rows)) : nullptr;
+  fast::f16* bcv = prec ? (fast::f16*)(w + f.bcv) : nullptr;
+  fast::f16* ccv = prec ? (fast::f16*)(w + f.ccv) : nullptr;
+  Seqs q = a.q;
+  if (varlen) {
+    q.valid = (const int*)(w + f.valid);
+    q.chunk_first = (const int32_t*)(w + f.first);
+    q.chunk_seq = (const int32_t*)(w + f.cseq);
+    hipLaunchKernelGGL(k_varlen_table, dim3(1), dim3(kTableThreads), 0, st, a.q.cu, a.q.slots,
+                       a.B, a.L, a.num_slots, (int32_t*)(w + f.first), (int32_t*)(w + f.cseq),
+                       f.chunks, (uint32_t*)(w + f.bitmap), (int*)(w + f.valid), a.status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   Src s;
   s.x = (const bf16*)a.x;
@@ -1210,13 +1421,14 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   s.GN = a.G * N;
   s.zs = a.zs;
   s.dta = DtA{a.dts, a.dt_bias};
+  s.q = q;
 
   // (chunk, 4-head block, batch): the chunk varies fastest in dispatch order
-  const dim3 g1(nc, a.H / HB, a.B);
+  const dim3 g1(nc, a.H / HB, gz);
   {
     // one workgroup per (chunk, group, batch): B staged once for the group
     ProfScope ps(st, KID_FAST_STATE);
-    const dim3 g0(nc, a.G, a.B);
+    const dim3 g0(nc, a.G, gz);
     const bf16* dt = (const bf16*)a.dt;
     if (prec)
       hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
@@ -1234,7 +1446,7 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     ProfScope ps(st, KID_FAST_PASS);
     hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
                        lam_end, a.s_in, a.s_out, sinb, nm == 2 ? sync : nullptr, part,
-                       nm == 2 ? npart : 0, a.status, a.H, nc);
+                       nm == 2 ? npart : 0, a.status, q, a.H, nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1262,7 +1474,15 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   }
 #undef SSD_FOUT
   e = hipGetLastError();
-  if (e != hipSuccess || !norm_after) return e;
+  if (e != hipSuccess) return e;
+  if (varlen) {
+    // new conv states last: the scan kernels read the slots' old rows
+    const int C = a.H * P + 2 * a.G * N;
+    hipLaunchKernelGGL(k_varlen_conv_state, dim3((C / 8 + 255) / 256, a.B), dim3(256), 0, st,
+                       (const bf16*)a.x, a.xs, q, C);
+    return hipGetLastError();
+  }
+  if (!norm_after) return e;
   return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.zs, a.norm_w, a.eps,
                            a.y, st);
 }

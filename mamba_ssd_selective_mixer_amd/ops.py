@@ -387,6 +387,55 @@ def ssd_decode_step_packed(d: SSDDims, zxbcdt_t, dt_bias, A_log, D, conv_w, conv
     return y_t
 
 
+def ssd_mixer_varlen_workspace_bytes(d: SSDDims, num_slots: int) -> int:
+    return int(_lib.load().ssd_mixer_varlen_workspace_bytes(ctypes.byref(d.c()), int(num_slots)))
+
+
+def ssd_mixer_varlen(d: SSDDims, cu_seqlens, slots, xbc, z, dt, A, D, conv_w, conv_b, norm_w,
+                     conv_pool, ssm_pool, eps=1e-5, has_state=None, out=None, ws=None,
+                     stream=None):
+    """Ragged sequences (d.batch of them, d.seqlen tokens in all) packed back
+    to back, each resuming from and writing back its state slot in the
+    pools; cu_seqlens [batch+1] and slots [batch] int32 device tensors,
+    has_state [batch] uint8 or None. Check the call's validity with
+    ssd_workspace_status(ws) (SSD_ERR_VARLEN when offsets or slots are bad)."""
+    io, f32 = d.io_dtype, torch.float32
+    B, T, H, C = d.batch, d.seqlen, d.nheads, d.channels
+    _want(cu_seqlens, "cu_seqlens", torch.int32, B + 1)
+    _want(slots, "slots", torch.int32, B)
+    _want(has_state, "has_state", torch.uint8, B, optional=True)
+    _want(xbc, "xbc", io, T * C)
+    _want(z, "z", io, T * d.hp, optional=True)
+    _want(dt, "dt", io, T * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * d.conv_width)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp, optional=z is None)
+    if conv_pool.dtype != io or not conv_pool.is_contiguous() or conv_pool.dim() != 3 or \
+            tuple(conv_pool.shape[1:]) != (d.conv_width - 1, C):
+        raise ValueError(f"conv_pool: expected contiguous [slots, {d.conv_width - 1}, {C}] {io}")
+    S = conv_pool.shape[0]
+    _want(ssm_pool, "ssm_pool", f32, S * H * d.headdim * d.dstate)
+    if out is None:
+        out = _alloc(stream, lambda: torch.empty(T, d.hp, dtype=io, device=xbc.device))
+    _want(out, "out", io, T * d.hp)
+    need = ssd_mixer_varlen_workspace_bytes(d, S)
+    if need == 0:
+        raise SSDError(-3, "ssd_mixer_varlen_workspace_bytes")
+    if ws is None:
+        ws = _alloc(stream, lambda: workspace(need, xbc.device))
+    _want_ws(ws, need)
+    _need_cuda(cu_seqlens, slots, has_state, xbc, z, dt, A, D, conv_w, conv_b, norm_w,
+               conv_pool, ssm_pool, out, ws)
+    rc = _lib.load().ssd_mixer_varlen(
+        ctypes.byref(d.c()), _p(cu_seqlens), _p(slots), _p(has_state), S, _p(xbc), _p(z),
+        _p(dt), _p(A), _p(D), _p(conv_w), _p(conv_b), _p(norm_w), float(eps), _p(conv_pool),
+        _p(ssm_pool), _p(out), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "ssd_mixer_varlen")
+    return out
+
+
 def ssd_mixer_prefill_noalloc(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, out,
                               eps=1e-5, conv_state_in=None, conv_state_out=None,
                               ssm_state_in=None, ssm_state_out=None, stream=None):

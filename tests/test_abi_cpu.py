@@ -361,3 +361,48 @@ def test_packed_entries_refuse_before_launch(lib):
     # y_t over the packed rows
     assert lib.ssd_decode_step_packed(ctypes.byref(dd), a[0], wdec, *a[1:7], 1e-5, a[7], a[8],
                                       V((1 << 36) + 4096), None) == -5
+
+
+_VL_BUFS = ("xbc", "z", "dt", "A", "D", "cw", "cb", "nw", "cu", "slots", "has", "cpool",
+            "spool", "out", "ws")
+_VL_W = ("cpool", "spool", "out", "ws")
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_VL_BUFS, _VL_W, {}))
+def test_varlen_alias_every_pair(lib, w, o, off):
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"], batch=3, seqlen=500)
+    need = lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 8)
+    a = {k: (i + 1) << 36 for i, k in enumerate(_VL_BUFS)}
+    a[w] = a[o] + off
+    rc = lib.ssd_mixer_varlen(ctypes.byref(d), V(a["cu"]), V(a["slots"]), V(a["has"]), 8,
+                              *(V(a[k]) for k in _VL_BUFS[:8]), 1e-5, V(a["cpool"]),
+                              V(a["spool"]), V(a["out"]), V(a["ws"]), need, None)
+    assert rc == _ALIAS
+
+
+def test_varlen_envelope_and_refusals(lib):
+    """The batched entry runs on the fused kernels only: other shapes, flags
+    or a missing pool are refused before any launch."""
+    V = ctypes.c_void_p
+    d = dims(synth.CONFIGS["c1"], batch=3, seqlen=500)
+    assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 8) > 0
+    assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
+    for bad in (dict(dstate=64), dict(io_dtype=_lib.SSD_F32), dict(flags=1),
+                dict(nheads=288, ngroups=1)):  # 288 heads per norm group: beyond the fused norm
+        dd = dims(synth.CONFIGS["c1"], batch=3, seqlen=500, **bad)
+        assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(dd), 8) == 0, bad
+        a = [V(k << 36) for k in range(1, 16)]
+        rc = lib.ssd_mixer_varlen(ctypes.byref(dd), a[0], a[1], None, 8, *a[2:10], 1e-5, *a[10:14],
+                                  1 << 30, None)
+        assert rc == -3, bad
+    a = [V(k << 36) for k in range(1, 16)]
+    need = lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 8)
+    assert lib.ssd_mixer_varlen(ctypes.byref(d), None, a[1], None, 8, *a[2:10], 1e-5,
+                                *a[10:14], need, None) == -1
+    assert lib.ssd_mixer_varlen(ctypes.byref(d), a[0], a[1], None, 8, *a[2:10], 1e-5, None,
+                                *a[11:14], need, None) == -1
+    assert lib.ssd_mixer_varlen(ctypes.byref(d), a[0], a[1], None, 0, *a[2:10], 1e-5,
+                                *a[10:14], need, None) == -2
+    assert lib.ssd_mixer_varlen(ctypes.byref(d), a[0], a[1], None, 8, *a[2:10], 1e-5,
+                                *a[10:14], need - 1, None) == -6
