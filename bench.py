@@ -1,14 +1,17 @@
 """Benchmark of the Mamba-2 mixer core on one MI355X.
 
-A step is one pass of the whole prefill hot path (conv + SiLU over xBC, the
-chunked SSD scan, the gated RMSNorm, the final conv and SSM states written
-out) over one batch of synthetic input of the large-model layer shape:
-1 x 8192 tokens, 256 heads x 64, 8 groups, state 128, conv width 4, chunk
-256, bf16 I/O, zero initial state, inputs already resident in HBM. Two
-input/output buffer sets alternate across steps (each set, 0.85 GB, is
-larger than the 256 MB Infinity Cache).
+A step is one pass of the whole prefill hot path (dt = softplus(dt_raw +
+dt_bias) and A = -exp(A_log), conv + SiLU over xBC, the chunked SSD scan,
+the gated RMSNorm, the final conv and SSM states written out) over one batch
+of synthetic input of the large-model layer shape: 1 x 8192 tokens, 256
+heads x 64, 8 groups, state 128, conv width 4, chunk 256, bf16 I/O, zero
+initial state, the input projection's packed rows [z | xBC | dt_raw]
+already resident in HBM. Two input/output buffer sets alternate across
+steps (each set, 0.85 GB, is larger than the 256 MB Infinity Cache).
 
-Also measured (reported under "workloads"): the tiny-model layer prefill
+Also measured (reported under "workloads"): the same layer from separate
+x | B | C, z, dt tensors, a serving-style mixed batch (ragged prefills and
+decode steps over a state pool in one call), the tiny-model layer prefill
 (4 x 2048 tokens, 32 heads), the long-context chained prefill (16 pieces of
 8192 tokens, each resuming from the previous piece's states, per piece and
 per chain), the decode loop (256 sequences x 64 single-token steps, 256
@@ -88,7 +91,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="alternating input/output buffer sets")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events")
-    ap.add_argument("--only", choices=("tiny", "chain", "decode", "general"),
+    ap.add_argument("--only", choices=("tiny", "chain", "decode", "general", "serving",
+                                       "unpacked"),
                     help="time only one of the secondary workloads (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for the HBM counter scale)")
@@ -171,18 +175,25 @@ def kernel_times(ops, run, steps, launches_per_step=8):
 
 
 def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, states_out,
-                     kernel_events=True):
+                     kernel_events=True, packed=False):
     """Mean ms per prefill call over `steps` timed calls (HIP events around the
     whole timed region), and per-kernel mean ms from a second, event-bracketed
     pass over the same calls (the per-kernel events add gaps between
-    launches, so the step time comes from the first pass)."""
+    launches, so the step time comes from the first pass). packed: the call
+    takes the input projection's rows [z | xBC | dt_raw] with dt_bias and
+    A_log (dt and A formed in the kernels)."""
     td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    prm = synth.layer_params(cfg)
+    prm = synth.packed_params(cfg) if packed else synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
                     cfg.conv_width, cfg.chunk, td)
-    A, D = to_dev(torch, prm["A"], torch.float32), to_dev(torch, prm["D"], torch.float32)
+    D = to_dev(torch, prm["D"], torch.float32)
+    if packed:
+        dtb = to_dev(torch, prm["dt_bias"], torch.float32)
+        alog = to_dev(torch, prm["A_log"], torch.float32)
+    else:
+        A = to_dev(torch, prm["A"], torch.float32)
     cw, nw = to_dev(torch, prm["conv_w"], td), to_dev(torch, prm["norm_w"], td)
-    base = synth.prefill_inputs(cfg)
+    base = {"row": synth.packed_prefill_inputs(cfg)} if packed else synth.prefill_inputs(cfg)
     st0 = synth.initial_states(cfg) if states_in else None
     sets = []
     for _ in range(nsets):
@@ -201,9 +212,14 @@ def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, st
 
     def step(i):
         s = sets[i % nsets]
-        ops.ssd_mixer_prefill(d, s["xbc"], s["z"], s["dt"], A, D, cw, None, nw, prm["eps"],
-                              s.get("cs_in"), s.get("cs_out"), s.get("ss_in"), s.get("ss_out"),
-                              s["out"], ws)
+        if packed:
+            ops.ssd_mixer_prefill_packed(d, s["row"], dtb, alog, D, cw, None, nw, prm["eps"],
+                                         s.get("cs_in"), s.get("cs_out"), s.get("ss_in"),
+                                         s.get("ss_out"), s["out"], ws)
+        else:
+            ops.ssd_mixer_prefill(d, s["xbc"], s["z"], s["dt"], A, D, cw, None, nw, prm["eps"],
+                                  s.get("cs_in"), s.get("cs_out"), s.get("ss_in"),
+                                  s.get("ss_out"), s["out"], ws)
 
     for i in range(warmup):
         step(i)
@@ -311,6 +327,59 @@ def run_decode(torch, ops, synth, cfg, reps, kernel_events=True):
     ms = tm.stop_ms() / reps  # per 64-step loop
     kern = kernel_times(ops, one, cfg.steps, 2) if kernel_events else {}
     return ms, kern
+
+
+def run_serving(torch, ops, synth, reps, kernel_events=True):
+    """Continuous batching on the large-model layer (256 heads x 64, 8 groups,
+    state 128) over a pool of 512 state slots: one call takes 16 fresh
+    prefills (lengths drawn from 64..1024 tokens) and 240 decode steps (one
+    token each, resuming from their slots), every sequence on its own slot."""
+    bf = torch.bfloat16
+    cfg = synth.replace(synth.CONFIGS["c2"], chunk=128)
+    r = np.random.default_rng(2024)
+    lens = np.concatenate([r.integers(64, 1025, 16), np.ones(240, dtype=np.int64)])
+    T, nseq, S = int(lens.sum()), len(lens), 512
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = r.permutation(S)[:nseq].astype(np.int32)
+    has = np.concatenate([np.zeros(16), np.ones(240)]).astype(np.uint8)
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg, batch=1, seqlen=T)
+    d = ops.SSDDims(nseq, T, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 128, bf)
+    cpool = torch.zeros(S, 3, cfg.channels, dtype=bf, device="cuda")
+    spool = torch.zeros(S, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
+    spool.normal_(0.0, 0.1 ** 0.5)
+    args = (torch.tensor(cu, device="cuda"), torch.tensor(slots, device="cuda"),
+            to_dev(torch, inp["xbc"][0], bf), to_dev(torch, inp["z"][0], bf),
+            to_dev(torch, inp["dt"][0], bf), to_dev(torch, prm["A"], torch.float32),
+            to_dev(torch, prm["D"], torch.float32), to_dev(torch, prm["conv_w"], bf), None,
+            to_dev(torch, prm["norm_w"], bf), cpool, spool)
+    hs = torch.tensor(has, device="cuda")
+    out = torch.empty(T, cfg.hp, dtype=bf, device="cuda")
+    ws = ops.workspace(ops.ssd_mixer_varlen_workspace_bytes(d, S))
+
+    def one(_i=0):
+        ops.ssd_mixer_varlen(d, *args, eps=prm["eps"], has_state=hs, out=out, ws=ws)
+
+    one()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(reps):
+        one()
+    ms = tm.stop_ms() / reps
+    kern = kernel_times(ops, one, reps) if kernel_events else {}
+    status = ops.ssd_workspace_status(ws)
+    # algorithmic bytes: every token's inputs and output, each sequence's
+    # final states written, the decode steps' states read
+    nb = token_bytes(cfg) * T + state_bytes(cfg) * (nseq + int(has.sum()))
+    del cpool, spool, ws
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": T / (ms * 1e-3), "us_per_call": ms * 1e3,
+            "algorithmic_bytes": nb, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernels_us": {k: v * 1e3 for k, v in kern.items()}, "status": status,
+            "config": f"one call: 16 prefills ({int(lens[:16].sum())} tokens, 64-1024 each, "
+                      f"fresh) + 240 decode steps on a 512-slot pool, 256 heads x 64, 8 groups, "
+                      f"state 128, bf16"}
 
 
 def ceilings(torch):
@@ -434,6 +503,16 @@ def secondary(torch, ops, synth, args, which):
                         "kernels_us": {k: v * 1e3 for k, v in kern.items()},
                         "config": "256 sequences x 64 steps, 256 heads x 64, 8 groups, "
                                   "state 128, states ~ N(0, 0.1) updated in place"}
+    if "serving" in which:
+        wl["serving_mixed_batch"] = run_serving(torch, ops, synth, 5, ke)
+    if "unpacked" in which:
+        c2 = synth.CONFIGS["c2"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
+                                        True, ke)
+        wl["large_layer_prefill_unpacked"] = dict(
+            summarize_prefill(c2, ms, kern, False, True), status=rc,
+            config="the headline layer and inputs with x | B | C, z and dt (already softplus-ed) "
+                   "as separate tensors and A given")
     if "general" in which:
         c0 = synth.CONFIGS["c0"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c0, 50, 5, 1, False, False, ke)
@@ -475,7 +554,7 @@ def main():
         return
     cfg = synth.CONFIGS["c2"]
     ms, kern, rc = prefill_workload(torch, ops, synth, cfg, args.steps, args.warmup, args.sets,
-                                    False, True, not args.no_kernel_events)
+                                    False, True, not args.no_kernel_events, packed=True)
     if rc != 0:
         print(f"prefill reported status {rc}", file=sys.stderr)
         sys.exit(1)
@@ -510,14 +589,16 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "large-model layer prefill: batch 1 x 8192 tokens, 256 heads x "
                                "64, 8 groups, state 128, conv width 4, chunk 256, bf16 I/O, "
-                               "zero initial state, final conv and SSM states written",
+                               "zero initial state, final conv and SSM states written; inputs "
+                               "as the projection's packed rows [z | xBC | dt_raw] with "
+                               "dt_bias = -2 and A_log ~ U(log 1, log 16)",
                    "global_batch": cfg.batch, "seq_len": cfg.seqlen, "parallelism": "none"},
         "roofline": roof,
         "headline": head,
     }
     if not args.quick:
-        rec["workloads"] = secondary(torch, ops, synth, args, ("tiny", "chain", "decode",
-                                                               "general"))
+        rec["workloads"] = secondary(torch, ops, synth, args, ("unpacked", "tiny", "chain",
+                                                               "decode", "serving", "general"))
         rec["ceilings"] = ceilings(torch)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(synth, cfg)
