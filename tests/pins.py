@@ -427,6 +427,48 @@ def pin_varlen(orc):
     return max(errs)
 
 
+# Backward pass (oracle/backward.py: autograd of a plain torch fp64
+# forward). Its forward equals the C oracle's; its gradients equal central
+# finite differences of the C oracle's forward, element by element, for every
+# input and parameter (the C oracle is a different implementation, so a
+# mistake in either shows).
+def pin_backward(orc):
+    from oracle import backward as bwd
+    errs = []
+    for seed, kw in [(21, dict(L=11)), (22, dict(Bn=1, L=6, H=4, G=1, P=3, N=2, W=2))]:
+        k = rand_mixer(seed, **kw)
+        args = (k["xbc"], k["z"], k["dt"], k["A"], k["D"], k["conv_w"], k["conv_b"],
+                k["norm_w"], k["eps"], k["H"], k["P"], k["G"], k["N"])
+        o, s_ = bwd.mixer_forward(*args, conv_in=k["conv_in"], s_in=k["s_in"])
+        r = orc.mixer_prefill(*args, conv_in=k["conv_in"], s_in=k["s_in"])
+        errs += [_rel(o, r["out"]), _rel(s_, r["s_out"])]
+    k = rand_mixer(23, Bn=1, L=7, H=2, P=2, G=1, N=3, W=3)
+    rng = np.random.default_rng(24)
+    d_out = rng.standard_normal((1, 7, 4))
+    d_s = rng.standard_normal((1, 2, 2, 3))
+    names = ["xbc", "z", "dt", "A", "D", "conv_w", "conv_b", "norm_w", "conv_in", "s_in"]
+    g = bwd.mixer_backward(*(k[n] for n in names[:8]), k["eps"], k["H"], k["P"], k["G"], k["N"],
+                           d_out, conv_in=k["conv_in"], s_in=k["s_in"], d_s_out=d_s)
+
+    def loss(kk):
+        r = orc.mixer_prefill(kk["xbc"], kk["z"], kk["dt"], kk["A"], kk["D"], kk["conv_w"],
+                              kk["conv_b"], kk["norm_w"], kk["eps"], kk["H"], kk["P"], kk["G"],
+                              kk["N"], conv_in=kk["conv_in"], s_in=kk["s_in"])
+        return float((r["out"] * d_out).sum() + (r["s_out"] * d_s).sum())
+
+    h = 1e-6
+    for n in names:
+        fd = np.zeros_like(k[n])
+        for i in range(k[n].size):
+            kp = {**k, n: k[n].copy()}
+            km = {**k, n: k[n].copy()}
+            kp[n].flat[i] += h
+            km[n].flat[i] -= h
+            fd.flat[i] = (loss(kp) - loss(km)) / (2 * h)
+        errs.append(float(np.max(np.abs(fd - g[n])) / (1.0 + np.max(np.abs(fd)))))
+    return max(errs)
+
+
 PINS = {
     "unrolled": pin_unrolled,
     "chunked": pin_chunked,
@@ -444,7 +486,9 @@ PINS = {
     "dt_a": pin_dt_a,
     "packed": pin_packed,
     "varlen": pin_varlen,
+    "backward": pin_backward,
 }
 
 LIMITS = {name: 1e-11 for name in PINS}
+LIMITS["backward"] = 1e-7   # central differences with h = 1e-6 (truncation ~h^2, rounding ~1e-10)
 LIMITS["causality"] = 0.0
