@@ -342,6 +342,45 @@ int ssd_mixer_prefill_noalloc(const ssd_dims* d, const void* xbc, const void* z,
                               void* stream);
 
 /*
+ * Backward pass of ssd_mixer_prefill with the gated norm, for training
+ * ("feat(model): add Nemotron-3 Nano hybrid ...", section "Testing":
+ * gradient flow through the mixer; section "Caveats": the pure-PyTorch
+ * backend's activation memory). Given the forward's inputs and d_out (and,
+ * optionally, the gradient of the final SSM state), returns the gradients of
+ * sum(out * d_out) + sum(ssm_state_out * d_ssm_state_out) with respect to
+ * every input and parameter. Nothing from the forward is kept: the call
+ * recomputes the conv output, the carried-in state of every 64-token chunk
+ * and the scan output before the norm, in fp32.
+ *   Inputs as ssd_mixer_prefill: xbc [B, L, Cch], z [B, L, H*P] (required),
+ *   dt [B, L, H] (after softplus), A [H], D [H] or NULL (zero),
+ *   conv_w [Cch, W], conv_b [Cch] or NULL, norm_w [H*P] (required),
+ *   conv_state_in [B, W-1, Cch] or NULL (zeros), ssm_state_in [B, H, P, N]
+ *   fp32 or NULL (zeros); d_out [B, L, H*P]; d_ssm_state_out [B, H, P, N]
+ *   fp32 or NULL (zero).
+ *   Outputs (overwritten, never accumulated into): d_xbc, d_z, d_dt in
+ *   io_dtype with the shapes of xbc, z, dt; fp32 d_A [H], d_D [H] (NULL: not
+ *   computed), d_conv_w [Cch, W], d_conv_b [Cch] (NULL: not computed),
+ *   d_norm_w [H*P], d_conv_state_in [B, W-1, Cch] and d_ssm_state_in
+ *   [B, H, P, N] (NULL: not computed).
+ *   d->chunk and the FP32_OPERANDS flag are checked as for the forward but
+ *   do not change the result. Envelope: the forward's, with H*P <= 16384
+ *   and ngroups <= 256 (else ssd_mixer_backward_workspace_bytes returns 0
+ *   and the call SSD_ERR_UNSUPPORTED). Every output must be disjoint from
+ *   every other buffer. Workspace: ssd_mixer_backward_workspace_bytes(d);
+ *   its status word (ssd_workspace_status) reports a non-finite recomputed
+ *   scan output.
+ */
+size_t ssd_mixer_backward_workspace_bytes(const ssd_dims* d);
+int ssd_mixer_backward(const ssd_dims* d, const void* xbc, const void* z, const void* dt,
+                       const float* A, const float* D, const void* conv_w, const void* conv_b,
+                       const void* norm_w, float eps, const void* conv_state_in,
+                       const float* ssm_state_in, const void* d_out,
+                       const float* d_ssm_state_out, void* d_xbc, void* d_z, void* d_dt,
+                       float* d_A, float* d_D, float* d_conv_w, float* d_conv_b,
+                       float* d_norm_w, float* d_conv_state_in, float* d_ssm_state_in,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Status of the chunk-scan or mixer-prefill call that last used `workspace`
  * (a device pointer, the workspace passed to that call). Conditions that
  * depend on the data, and so cannot be checked before the launch, are
@@ -390,7 +429,14 @@ typedef enum {
   SSD_K_FAST_STATE = 7,      /* fast path: conv + chunk states        */
   SSD_K_FAST_PASS = 8,       /* fast path: state passing              */
   SSD_K_FAST_OUT = 9,        /* fast path: conv + chunk output + norm */
-  SSD_K_COUNT = 10
+  SSD_K_BWD_NORM = 10,       /* backward: gated norm                  */
+  SSD_K_BWD_CHUNK_Z = 11,    /* backward: chunk state-gradient terms  */
+  SSD_K_BWD_REV_PASS = 12,   /* backward: reverse state passing       */
+  SSD_K_BWD_CHUNK = 13,      /* backward: per-chunk gradients         */
+  SSD_K_BWD_GROUP_SUM = 14,  /* backward: B / C gradients per group   */
+  SSD_K_BWD_CONV_DU = 15,    /* backward: SiLU + conv weight gradient */
+  SSD_K_BWD_CONV_DX = 16,    /* backward: conv input gradient         */
+  SSD_K_COUNT = 17
 } ssd_kernel_id;
 int ssd_profile_start(int capacity);
 int ssd_profile_stop(void);

@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(HERE, "libssd_mi355x.so")
 SSD_F32, SSD_BF16 = 0, 1
 KERNELS = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
            "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
-           "fused_chunk_out_norm")
+           "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z", "bwd_rev_pass", "bwd_chunk",
+           "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx")
 ENTRY = {"conv1d": 0, "chunk_scan": 1, "gated_rmsnorm": 2, "decode_step": 3, "mixer_prefill": 4}
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_DTYPE", -5: "SSD_ERR_ALIAS", -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_HIP",
@@ -28,7 +29,8 @@ EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "
            "ssd_gated_rmsnorm", "ssd_decode_step", "ssd_mixer_prefill_workspace_bytes",
            "ssd_mixer_prefill", "ssd_mixer_prefill_packed", "ssd_decode_step_packed",
            "ssd_mixer_varlen_workspace_bytes", "ssd_mixer_varlen",
-           "ssd_mixer_prefill_noalloc", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
+           "ssd_mixer_prefill_noalloc", "ssd_mixer_backward_workspace_bytes",
+           "ssd_mixer_backward", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
            "ssd_profile_start", "ssd_profile_stop", "ssd_profile_read", "ssd_kernel_name")
 
 
@@ -75,6 +77,9 @@ def load():
                                    vp, vp, sz, vp]),
         "ssd_mixer_prefill_noalloc": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
                                             vp, vp, vp]),
+        "ssd_mixer_backward_workspace_bytes": (sz, [P]),
+        "ssd_mixer_backward": (i32, [P, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ssd_workspace_status": (i32, [vp, vp]),
         "ssd_set_exchange_spin_limit": (i32, [i32]),
         "ssd_profile_start": (i32, [i32]),

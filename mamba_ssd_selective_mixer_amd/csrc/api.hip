@@ -658,6 +658,112 @@ int ssd_mixer_varlen(const ssd_dims* d, const int32_t* cu_seqlens, const int32_t
   return hip_status(ssd::launch_fast_scan(a, (hipStream_t)stream));
 }
 
+// The backward kernels' own limits: a norm row spreads over the 256 threads
+// of a workgroup at most 64 channels each; norm groups fit a 256-entry table.
+constexpr int kBwdMaxHP = 256 * 64, kBwdMaxGroups = 256;
+
+size_t ssd_mixer_backward_workspace_bytes(const ssd_dims* d) {
+  if (check_dims(SSD_ENTRY_MIXER_PREFILL, d)) return 0;
+  if ((int64_t)d->nheads * d->headdim > kBwdMaxHP || d->ngroups > kBwdMaxGroups) return 0;
+  return round_up(4, kWsAlign) + ssd::backward_ws_bytes(d->batch, d->seqlen, d->nheads,
+                                                        d->headdim, d->ngroups, d->dstate);
+}
+
+int ssd_mixer_backward(const ssd_dims* d, const void* xbc, const void* z, const void* dt,
+                       const float* A, const float* D, const void* conv_w, const void* conv_b,
+                       const void* norm_w, float eps, const void* conv_state_in,
+                       const float* ssm_state_in, const void* d_out,
+                       const float* d_ssm_state_out, void* d_xbc, void* d_z, void* d_dt,
+                       float* d_A, float* d_D, float* d_conv_w, float* d_conv_b,
+                       float* d_norm_w, float* d_conv_state_in, float* d_ssm_state_in,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_dims(SSD_ENTRY_MIXER_PREFILL, d);
+  if (rc) return rc;
+  if ((int64_t)d->nheads * d->headdim > kBwdMaxHP || d->ngroups > kBwdMaxGroups)
+    return SSD_ERR_UNSUPPORTED;
+  // the recomputed forward runs the generic kernels with fp32 operands
+  ssd_dims inner = *d;
+  inner.flags |= SSD_FLAG_FP32_OPERANDS;
+  inner.chunk = 64;
+  if ((rc = check_dims(SSD_ENTRY_MIXER_PREFILL, &inner))) return rc;
+  if (!xbc || !z || !dt || !A || !conv_w || !norm_w || !d_out || !d_xbc || !d_z || !d_dt ||
+      !d_A || !d_conv_w || !d_norm_w)
+    return SSD_ERR_NULL;
+  if (!aligned16(xbc) || !aligned16(z) || !aligned16(dt) || !aligned16(A) || !aligned16(D) ||
+      !aligned16(conv_w) || !aligned16(conv_b) || !aligned16(norm_w) ||
+      !aligned16(conv_state_in) || !aligned16(ssm_state_in) || !aligned16(d_out) ||
+      !aligned16(d_ssm_state_out) || !aligned16(d_xbc) || !aligned16(d_z) || !aligned16(d_dt) ||
+      !aligned16(d_A) || !aligned16(d_D) || !aligned16(d_conv_w) || !aligned16(d_conv_b) ||
+      !aligned16(d_norm_w) || !aligned16(d_conv_state_in) || !aligned16(d_ssm_state_in))
+    return SSD_ERR_ALIGN;
+  const size_t need = ssd_mixer_backward_workspace_bytes(d);
+  if (!workspace || ws_bytes < need || ((uintptr_t)workspace % kWsAlign))
+    return SSD_ERR_WORKSPACE;
+  const size_t e = esize(d), T = (size_t)d->batch * d->seqlen, C = channels(d);
+  const size_t HP = (size_t)d->nheads * d->headdim, nh = (size_t)d->nheads * 4;
+  const size_t ncs = (size_t)d->batch * (d->conv_width - 1) * C,
+               nss = (size_t)d->batch * HP * d->dstate * 4, W = d->conv_width;
+  if (aliased({{xbc, T * C * e, false, -1},
+               {z, T * HP * e, false, -1},
+               {dt, T * d->nheads * e, false, -1},
+               {A, nh, false, -1},
+               {D, nh, false, -1},
+               {conv_w, C * W * e, false, -1},
+               {conv_b, C * e, false, -1},
+               {norm_w, HP * e, false, -1},
+               {conv_state_in, ncs * e, false, -1},
+               {ssm_state_in, nss, false, -1},
+               {d_out, T * HP * e, false, -1},
+               {d_ssm_state_out, nss, false, -1},
+               {d_xbc, T * C * e, true, -1},
+               {d_z, T * HP * e, true, -1},
+               {d_dt, T * d->nheads * e, true, -1},
+               {d_A, nh, true, -1},
+               {d_D, nh, true, -1},
+               {d_conv_w, C * W * 4, true, -1},
+               {d_conv_b, C * 4, true, -1},
+               {d_norm_w, HP * 4, true, -1},
+               {d_conv_state_in, ncs * 4, true, -1},
+               {d_ssm_state_in, nss, true, -1},
+               {workspace, need, true, -1}}))
+    return SSD_ERR_ALIAS;
+  ssd::BackwardArgs a{};
+  a.io_bf16 = d->io_dtype == SSD_BF16;
+  a.B = d->batch;
+  a.L = d->seqlen;
+  a.H = d->nheads;
+  a.P = d->headdim;
+  a.G = d->ngroups;
+  a.N = d->dstate;
+  a.W = d->conv_width;
+  a.xbc = xbc;
+  a.z = z;
+  a.dt = dt;
+  a.A = A;
+  a.D = D;
+  a.conv_w = conv_w;
+  a.conv_b = conv_b;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.conv_in = conv_state_in;
+  a.s_in = ssm_state_in;
+  a.d_out = d_out;
+  a.d_s_out = d_ssm_state_out;
+  a.d_xbc = d_xbc;
+  a.d_z = d_z;
+  a.d_dt = d_dt;
+  a.d_A = d_A;
+  a.d_D = d_D;
+  a.d_conv_w = d_conv_w;
+  a.d_conv_b = d_conv_b;
+  a.d_norm_w = d_norm_w;
+  a.d_conv_in = d_conv_state_in;
+  a.d_s_in = d_ssm_state_in;
+  a.status = (int*)workspace;
+  a.ws = (unsigned char*)workspace + round_up(4, kWsAlign);
+  return hip_status(ssd::launch_backward(a, (hipStream_t)stream));
+}
+
 int ssd_workspace_status(const void* workspace, void* stream) {
   if (!workspace) return SSD_ERR_NULL;
   if ((uintptr_t)workspace % kWsAlign) return SSD_ERR_WORKSPACE;

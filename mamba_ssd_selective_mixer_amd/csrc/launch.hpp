@@ -107,3 +107,41 @@ int fast_max_norm_heads();
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st);
 
 }  // namespace ssd
+
+namespace ssd {
+
+// Backward pass of the mixer prefill (conv + SiLU, chunked scan, gated norm).
+// Activation gradients in the I/O type, parameter and state gradients fp32.
+struct BackwardArgs {
+  bool io_bf16;
+  int B, L, H, P, G, N, W;
+  const void* xbc;      // [B, L, Cch]
+  const void* z;        // [B, L, H*P]
+  const void* dt;       // [B, L, H] (after softplus)
+  const float* A;       // [H] (negative)
+  const float* D;       // [H] or null (zero)
+  const void* conv_w;   // [Cch, W]
+  const void* conv_b;   // [Cch] or null
+  const void* norm_w;   // [H*P]
+  float eps;
+  const void* conv_in;  // [B, W-1, Cch] or null (zeros)
+  const float* s_in;    // [B, H, P, N] or null (zeros)
+  const void* d_out;    // [B, L, H*P]
+  const float* d_s_out; // [B, H, P, N] or null (zero)
+  void* d_xbc;          // [B, L, Cch]
+  void* d_z;            // [B, L, H*P]
+  void* d_dt;           // [B, L, H]
+  float* d_A;           // [H]
+  float* d_D;           // [H] or null
+  float* d_conv_w;      // [Cch, W]
+  float* d_conv_b;      // [Cch] or null
+  float* d_norm_w;      // [H*P]
+  float* d_conv_in;     // [B, W-1, Cch] or null
+  float* d_s_in;        // [B, H, P, N] or null
+  void* ws;             // backward_ws_bytes(...) bytes, 256-byte aligned
+  int* status;          // the call's status word
+};
+size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);
+
+}  // namespace ssd

@@ -32,7 +32,9 @@ bool g_overflow = false;
 const char* kNames[KID_COUNT] = {
     "conv1d_silu",      "conv_state",       "gated_rmsnorm", "decode_step",
     "chunk_state",      "state_pass",       "chunk_out",     "fused_chunk_state",
-    "fused_state_pass", "fused_chunk_out_norm",
+    "fused_state_pass", "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z",
+    "bwd_rev_pass",     "bwd_chunk",        "bwd_group_sum", "bwd_conv_du",
+    "bwd_conv_dx",
 };
 
 void release() {

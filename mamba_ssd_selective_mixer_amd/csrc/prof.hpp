@@ -21,6 +21,13 @@ enum KernelId {
   KID_FAST_STATE,
   KID_FAST_PASS,
   KID_FAST_OUT,
+  KID_BWD_NORM,
+  KID_BWD_CHUNK_Z,
+  KID_BWD_REV_PASS,
+  KID_BWD_CHUNK,
+  KID_BWD_GROUP_SUM,
+  KID_BWD_CONV_DU,
+  KID_BWD_CONV_DX,
   KID_COUNT
 };
 

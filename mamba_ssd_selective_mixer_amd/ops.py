@@ -467,6 +467,76 @@ def ssd_mixer_prefill_noalloc(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm
     return out
 
 
+def ssd_mixer_backward_workspace_bytes(d: SSDDims) -> int:
+    return int(_lib.load().ssd_mixer_backward_workspace_bytes(ctypes.byref(d.c())))
+
+
+BACKWARD_GRADS = ("xbc", "z", "dt", "A", "D", "conv_w", "conv_b", "norm_w", "conv_state_in",
+                  "ssm_state_in")
+
+
+def ssd_mixer_backward(d: SSDDims, xbc, z, dt, A, D, conv_w, conv_b, norm_w, d_out, eps=1e-5,
+                       conv_state_in=None, ssm_state_in=None, d_ssm_state_out=None,
+                       grads=None, ws=None, stream=None):
+    """Gradients of the mixer prefill (conv + SiLU, chunked scan, gated
+    norm) for upstream gradient d_out (and d_ssm_state_out of the final
+    state). Returns a dict keyed by BACKWARD_GRADS: xbc, z, dt in the I/O
+    dtype; A, D, conv_w, conv_b, norm_w and the two initial states in fp32
+    (D, conv_b and the states only when the forward had them). `grads` may
+    supply any of these output tensors."""
+    io, f32 = d.io_dtype, torch.float32
+    B, L, H, C, W = d.batch, d.seqlen, d.nheads, d.channels, d.conv_width
+    _want(xbc, "xbc", io, B * L * C)
+    _want(z, "z", io, B * L * d.hp)
+    _want(dt, "dt", io, B * L * H)
+    _want(A, "A", f32, H)
+    _want(D, "D", f32, H, optional=True)
+    _want(conv_w, "conv_w", io, C * W)
+    _want(conv_b, "conv_b", io, C, optional=True)
+    _want(norm_w, "norm_w", io, d.hp)
+    _want(d_out, "d_out", io, B * L * d.hp)
+    ncs, nss = B * (W - 1) * C, B * H * d.headdim * d.dstate
+    _want(conv_state_in, "conv_state_in", io, ncs, optional=True)
+    _want(ssm_state_in, "ssm_state_in", f32, nss, optional=True)
+    _want(d_ssm_state_out, "d_ssm_state_out", f32, nss, optional=True)
+    dev = xbc.device
+    spec = {"xbc": ((B, L, C), io), "z": ((B, L, d.hp), io), "dt": ((B, L, H), io),
+            "A": ((H,), f32), "D": ((H,), f32), "conv_w": ((C, W), f32), "conv_b": ((C,), f32),
+            "norm_w": ((d.hp,), f32), "conv_state_in": ((B, W - 1, C), f32),
+            "ssm_state_in": ((B, H, d.headdim, d.dstate), f32)}
+    present = {"D": D is not None, "conv_b": conv_b is not None,
+               "conv_state_in": conv_state_in is not None,
+               "ssm_state_in": ssm_state_in is not None}
+    g = dict(grads or {})
+    for k in BACKWARD_GRADS:
+        if not present.get(k, True):
+            g.pop(k, None)
+            continue
+        shape, dtype = spec[k]
+        if g.get(k) is None:
+            g[k] = _alloc(stream, lambda: torch.empty(shape, dtype=dtype, device=dev))
+        n = 1
+        for s in shape:
+            n *= s
+        _want(g[k], "grad " + k, dtype, n)
+    need = ssd_mixer_backward_workspace_bytes(d)
+    if need == 0:
+        raise SSDError(-3, "ssd_mixer_backward_workspace_bytes")
+    if ws is None:
+        ws = _alloc(stream, lambda: workspace(need, dev))
+    _want_ws(ws, need)
+    _need_cuda(xbc, z, dt, A, D, conv_w, conv_b, norm_w, d_out, conv_state_in, ssm_state_in,
+               d_ssm_state_out, ws, *g.values())
+    rc = _lib.load().ssd_mixer_backward(
+        ctypes.byref(d.c()), _p(xbc), _p(z), _p(dt), _p(A), _p(D), _p(conv_w), _p(conv_b),
+        _p(norm_w), float(eps), _p(conv_state_in), _p(ssm_state_in), _p(d_out),
+        _p(d_ssm_state_out), _p(g["xbc"]), _p(g["z"]), _p(g["dt"]), _p(g["A"]), _p(g.get("D")),
+        _p(g["conv_w"]), _p(g.get("conv_b")), _p(g["norm_w"]), _p(g.get("conv_state_in")),
+        _p(g.get("ssm_state_in")), _p(ws), ws.numel(), _stream(stream))
+    _check(rc, "ssd_mixer_backward")
+    return g
+
+
 def ssd_workspace_status(ws, stream=None) -> int:
     """Status code of the scan / prefill call that last used workspace `ws`
     (waits for `stream`): 0, SSD_ERR_TIMEOUT (-9) or SSD_ERR_NONFINITE (-10)."""

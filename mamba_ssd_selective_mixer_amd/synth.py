@@ -165,6 +165,24 @@ def initial_states(cfg: Cfg, batch: int | None = None, dtype: str | None = None)
     return {"conv_state": to_io(conv, dtype), "ssm_state": np.ascontiguousarray(ssm)}
 
 
+# ---------------------------------------------------------------- backward
+def backward_seeds(cfg: Cfg, batch: int | None = None, seqlen: int | None = None,
+                   dtype: str | None = None) -> dict:
+    """Upstream gradients for the backward pass and a non-trivial norm
+    weight (stream 200): d_out [B,L,H*P] ~ N(0,1) (I/O dtype), d_ssm_state_out
+    [B,H,P,N] ~ N(0, variance 0.1) fp32, norm_w [H*P] = 1 + N(0,1)/4 (I/O
+    dtype)."""
+    dtype = dtype or cfg.dtype
+    Bn, L = batch or cfg.batch, seqlen or cfg.seqlen
+    r = rng(cfg.index, 200)
+    d_out = r.standard_normal((Bn, L, cfg.hp), dtype=np.float32)
+    sd = np.float32(math.sqrt(0.1))
+    d_s = r.standard_normal((Bn, cfg.nheads, cfg.headdim, cfg.dstate), dtype=np.float32) * sd
+    nw = np.float32(1.0) + r.standard_normal(cfg.hp, dtype=np.float32) * np.float32(0.25)
+    return {"d_out": to_io(d_out, dtype), "d_ssm_state_out": np.ascontiguousarray(d_s),
+            "norm_w": to_io(nw, dtype)}
+
+
 # ---------------------------------------------------------------- packed rows
 # The same draws in the projection's raw form: the per-token row is
 # [z | x | B | C | dt_raw] with dt_raw ~ N(0,1) (the normal that the recipe

@@ -406,3 +406,66 @@ def test_varlen_envelope_and_refusals(lib):
                                 *a[10:14], need, None) == -2
     assert lib.ssd_mixer_varlen(ctypes.byref(d), a[0], a[1], None, 8, *a[2:10], 1e-5,
                                 *a[10:14], need - 1, None) == -6
+
+
+def test_argtypes_match_header_arity(lib):
+    """Every prototype in the header has as many parameters as the binding
+    passes (a missing or extra argument would shift every later one)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text)
+    assert len(protos) == len(_lib.EXPORTS)
+    for name, params in protos:
+        params = params.strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
+_BWD_BUFS = ("xbc", "z", "dt", "A", "D", "cw", "cb", "nw", "cs_in", "ss_in", "d_out", "d_ss_out",
+             "g_xbc", "g_z", "g_dt", "g_A", "g_D", "g_cw", "g_cb", "g_nw", "g_cs_in", "g_ss_in",
+             "ws")
+_BWD_W = ("g_xbc", "g_z", "g_dt", "g_A", "g_D", "g_cw", "g_cb", "g_nw", "g_cs_in", "g_ss_in",
+          "ws")
+
+
+def _bwd_call(lib, d, a, need):
+    V = ctypes.c_void_p
+    return lib.ssd_mixer_backward(ctypes.byref(d), *(V(a[k]) for k in _BWD_BUFS[:8]), 1e-5,
+                                  *(V(a[k]) for k in _BWD_BUFS[8:]), need, None)
+
+
+@pytest.mark.parametrize("w,o,off", _alias_cases(_BWD_BUFS, _BWD_W, {}))
+def test_backward_alias_every_pair(lib, w, o, off):
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
+    a = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
+    a[w] = a[o] + off
+    assert _bwd_call(lib, d, a, need) == _ALIAS
+
+
+def test_backward_refuses_before_launch(lib):
+    d = dims(synth.CONFIGS["c1"])
+    need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
+    # workspace: the status word, fp32 conv output / its gradient, y, chunk
+    # states and their gradients (64-token chunks), per-head dB / dC
+    cfg = synth.CONFIGS["c1"]
+    T, C, HP = cfg.batch * cfg.seqlen, cfg.channels, cfg.hp
+    nc = -(-cfg.seqlen // 64)
+    st = cfg.batch * nc * HP * cfg.dstate * 4
+    r = lambda b: -(-b // 256) * 256
+    assert need == (256 + 2 * r(T * C * 4) + r(T * HP * 4) + 2 * r(st)
+                    + r(cfg.batch * cfg.nheads * nc * 4) + 2 * r(T * cfg.nheads * cfg.dstate * 4))
+    base = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
+    for k in ("xbc", "z", "dt", "A", "cw", "nw", "d_out", "g_xbc", "g_z", "g_dt", "g_A", "g_cw",
+              "g_nw", "ws"):
+        a = dict(base)
+        a[k] = 0
+        assert _bwd_call(lib, d, a, need) == (-6 if k == "ws" else -1), k
+    for k in ("D", "cb", "cs_in", "ss_in", "d_ss_out", "g_D", "g_cb", "g_cs_in", "g_ss_in"):
+        a = dict(base)
+        a[k] += 4
+        assert _bwd_call(lib, d, a, need) == -8, k
+    assert _bwd_call(lib, d, base, need - 1) == -6
+    wide = dims(cfg, nheads=512)  # H*P = 32768 channels in a norm row
+    assert lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(wide)) == 0
+    assert _bwd_call(lib, wide, base, need) == -3
+    assert _bwd_call(lib, dims(cfg, flags=4), base, need) == -3
