@@ -436,7 +436,8 @@ typedef enum {
   SSD_K_BWD_GROUP_SUM = 14,  /* backward: B / C gradients per group   */
   SSD_K_BWD_CONV_DU = 15,    /* backward: SiLU + conv weight gradient */
   SSD_K_BWD_CONV_DX = 16,    /* backward: conv input gradient         */
-  SSD_K_COUNT = 17
+  SSD_K_BWD_Y = 17,          /* backward: scan output recomputed      */
+  SSD_K_COUNT = 18
 } ssd_kernel_id;
 int ssd_profile_start(int capacity);
 int ssd_profile_stop(void);

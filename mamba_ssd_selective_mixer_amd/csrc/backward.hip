@@ -3,20 +3,21 @@
 // state), the gradients with respect to xBC, z, dt, A, D, the conv weight
 // and bias, the norm weight and the initial states ("feat(model): add
 // Nemotron-3 Nano hybrid ..." section "Testing": gradient flow through the
-// mixer; "Caveats": the native backend is activation-memory hungry).
+// mixer; "Caveats": the native backend is activation-memory hungry, so
+// nothing of the forward is kept: it is recomputed here).
 //
-// The forward is recomputed first on the general kernels with fp32 MFMA
-// operands (conv output v, the carried-in state of every chunk, pre-norm y);
-// then, per chunk k of head h with Lam the inclusive cumsum of dt A inside
-// the chunk, E[t,s] = exp(Lam_t - Lam_s) (s <= t), G = C B^T, K = dY X^T:
-//   dX[s]   = sum_{t>=s} G E dt_s dY[t] + D dY[s] + w_s (dS_out B_s),  w_s = exp(Lam_end - Lam_s) dt_s
-//   dC[t]   = sum_{s<=t} K E dt_s B[s] + exp(Lam_t) dY[t] S_in
-//   dB[s]   = sum_{t>=s} K E dt_s C[t] + w_s X[s] dS_out
+// Per chunk of Q = 64 tokens of head h, with Lam the inclusive cumsum of
+// dt A inside the chunk, E[t,s] = exp(Lam_t - Lam_s) (s <= t), G = C B^T,
+// K = dY X^T, M = G o E dt_s, dG = K o E dt_s, w_s = exp(Lam_end - Lam_s) dt_s:
+//   y       = M X + exp(Lam_t) C S_in^T + D X                (recomputed)
+//   dX[s]   = sum_{t>=s} M[t,s] dY[t] + D dY[s] + w_s (B_s dS_out^T)
+//   dC[t]   = sum_{s<=t} dG[t,s] B[s] + exp(Lam_t) dY[t] S_in
+//   dB[s]   = sum_{t>=s} dG[t,s] C[t] + w_s X[s] dS_out
 //   dS_in   = exp(Lam_end) dS_out + sum_t exp(Lam_t) dY[t] (outer) C[t]
 // with dS_out of chunk k the dS_in of chunk k+1 (a reverse pass over the
-// chunks), and dt, A through dLam (reverse cumsum within the chunk). The
-// gated norm and the conv are differentiated directly. Everything is fp32;
-// dense products are plain loops over L2-resident operands.
+// chunks), and dt, A through dLam. The dense products run on fp32 MFMA
+// (16x16x4, fp32 accumulation) with operand slices staged in LDS; the gated
+// norm and the conv are differentiated elementwise.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,9 +25,18 @@ namespace ssd {
 namespace bwd {
 
 constexpr int kThreads = 256;
-constexpr int kNormRows = 8;      // rows per norm-backward workgroup
-constexpr int kMaxNormVec = 64;   // H*P / 256 channels per thread at most
+constexpr int kQ = 64;           // chunk length
+constexpr int kQP = kQ + 4;      // pitch of the Q x Q tiles (floats)
+constexpr int kKS = 32;          // width of a staged operand slice
+constexpr int kSP = kKS + 4;     // pitch of a staged slice
+constexpr int kNormBlocks = 512; // most norm-backward workgroups (one dw part each)
 constexpr int kMaxGroups = 256;
+
+// MFMA 16x16x4 fp32. Lane l supplies A[row l%16][k l/16] and B[k l/16][col
+// l%16]; acc[r] is C[row 4 (l/16) + r][col l%16].
+SSD_DEV f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 // zero n floats
 __global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
@@ -35,66 +45,39 @@ __global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
-// ---------------------------------------------------------------- gated norm
-// q = y silu(z), r = (mean_group(q^2) + eps)^-1/2, out = q r w. For each row:
-//   dq = w r g - q r^3 mean_group(w g q);  dy = dq silu(z);
-//   dz = dq y silu'(z);  dw += g q r  (summed over rows).
-// dy overwrites y (each thread reads its channels before writing them).
-template <class T>
-__global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __restrict__ z,
-                                                       const T* __restrict__ w,
-                                                       const T* __restrict__ g, float eps,
-                                                       T* __restrict__ dz, float* dw,
-                                                       int64_t rows, int HP, int G) {
-  __shared__ float sq[kMaxGroups], sg[kMaxGroups];
-  const int tid = threadIdx.x;
-  const int S = HP / G;
-  float dwp[kMaxNormVec];
-#pragma unroll
-  for (int i = 0; i < kMaxNormVec; ++i) dwp[i] = 0.f;
-  const int nv = (HP + kThreads - 1) / kThreads;
-  for (int rr = 0; rr < kNormRows; ++rr) {
-    const int64_t row = (int64_t)blockIdx.x * kNormRows + rr;
-    if (row >= rows) break;
-    for (int j = tid; j < G; j += kThreads) sq[j] = sg[j] = 0.f;
-    __syncthreads();
-    for (int i = 0; i < nv; ++i) {
-      const int c = tid + i * kThreads;
-      if (c < HP) {
-        const int64_t o = row * HP + c;
-        const float zz = to_f(z[o]), q = y[o] * zz / (1.f + __expf(-zz));
-        atomicAdd(&sq[c / S], q * q);
-        atomicAdd(&sg[c / S], to_f(w[c]) * to_f(g[o]) * q);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kMaxNormVec; ++i) {
-      const int c = tid + i * kThreads;
-      if (i < nv && c < HP) {
-        const int64_t o = row * HP + c;
-        const int j = c / S;
-        const float r = rsqrtf(sq[j] / S + eps), k3 = r * r * r * sg[j] / S;
-        const float zz = to_f(z[o]), sig = 1.f / (1.f + __expf(-zz)), s = zz * sig;
-        const float yy = y[o], q = yy * s, gg = to_f(g[o]);
-        const float dq = to_f(w[c]) * r * gg - q * k3;
-        y[o] = dq * s;
-        dz[o] = from_f<T>(dq * yy * (sig + s * (1.f - sig)));
-        dwp[i] += gg * q * r;
-      }
-    }
-    __syncthreads();
+// Rows [0, rows) x columns [0, kKS) of a row-major fp32 matrix (row stride
+// rs, elements) into dst [rows][kSP]; rows >= nrows and columns >= ncols
+// (a multiple of 4) are zero.
+SSD_DEV void stage(float* dst, const float* src, int64_t rs, int rows, int nrows, int ncols) {
+  for (int i = threadIdx.x; i < rows * (kKS / 4); i += kThreads) {
+    const int r = i / (kKS / 4), c4 = (i % (kKS / 4)) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nrows && c4 < ncols) v = *reinterpret_cast<const float4*>(src + r * rs + c4);
+    *reinterpret_cast<float4*>(dst + r * kSP + c4) = v;
   }
-#pragma unroll
-  for (int i = 0; i < kMaxNormVec; ++i) {
-    const int c = tid + i * kThreads;
-    if (i < nv && c < HP) atomicAdd(dw + c, dwp[i]);
+}
+
+// The ten causal 16x16 tiles (rt, st), st <= rt, of a 64 x 64 block spread
+// over the four waves (at most three each): whether slot i of wave w holds one.
+SSD_DEV bool causal_tile(int w, int i, int& rt, int& st) {
+  if (w == 3) {
+    rt = 3;
+    st = 3;
+    return i == 0;
   }
+  if (w == 0) {
+    rt = i == 0 ? 0 : 1;
+    st = i == 0 ? 0 : i - 1;
+    return true;
+  }
+  rt = w + 1;
+  st = i;
+  return true;
 }
 
 // ---------------------------------------------------------------- chunk Lam
 // Lam (inclusive cumsum of dt A over the chunk, natural log units), dt and
-// exp(Lam) of the first len positions into lam / dts / ex (Q <= 64: wave 0).
+// exp(Lam) of the first len positions into lam / dts / ex (wave 0).
 template <class T>
 __device__ __forceinline__ void chunk_lam(const T* __restrict__ dt, const DtA& dta, int64_t row0,
                                           int h, float Ah, int len, float* lam, float* dts,
@@ -110,28 +93,211 @@ __device__ __forceinline__ void chunk_lam(const T* __restrict__ dt, const DtA& d
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- y recompute
+// y = M X + exp(Lam_t) C S_in^T + D X of one (chunk, head) in fp32, with
+// S_in the chunk's carried-in state (fp32). Wave w owns rows 16 w .. 16 w + 15.
+template <class T, int P>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_y(const float* __restrict__ v,
+                                                       const T* __restrict__ dt, DtA dta,
+                                                       const float* __restrict__ A,
+                                                       const float* __restrict__ D,
+                                                       const float* __restrict__ Sin,
+                                                       float* __restrict__ y, int L, int H, int G,
+                                                       int N, int nc) {
+  extern __shared__ __align__(16) float sm[];
+  float* Mt = sm;                 // [Q][kQP]: M
+  float* Bs = sm + kQ * kQP;      // [Q][kSP]
+  float* Cs = Bs + kQ * kSP;      // [Q][kSP]
+  float* Ss = Cs + kQ * kSP;      // [P][kSP]
+  __shared__ float lam[64], dts[64], ex[64];
+  constexpr int NPT = P / 16;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int t0 = c * kQ, len = min(kQ, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int HP = H * P;
+  const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, bo = HP + (int64_t)g * N,
+                co = HP + (int64_t)(G + g) * N;
+  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
+  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
+  int rt[3], st[3];
+  bool on[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
+  f32x4 aG[3], aY[NPT];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) aG[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
+  const int sw = wave * 16;
+  // G on the causal tiles and C S_in^T on the wave's rows, over slices of n
+  for (int n0 = 0; n0 < N; n0 += kKS) {
+    const int nv = min(kKS, N - n0);
+    stage(Bs, v + row0 * C + bo + n0, C, kQ, len, nv);
+    stage(Cs, v + row0 * C + co + n0, C, kQ, len, nv);
+    stage(Ss, Si + n0, N, P, P, nv);
+    __syncthreads();
+    for (int kk = 0; kk < nv; kk += 4) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (on[i])
+          aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk], Bs[(st[i] * 16 + lr) * kSP + kk + lk],
+                      aG[i]);
+      const float a = Cs[(sw + lr) * kSP + kk + lk];
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) aY[pt] = mma(a, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
+    }
+    __syncthreads();
+  }
+  // M = G o E dt_s on the causal tiles (rows and columns past the chunk: 0)
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (on[i])
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
+        const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
+        Mt[t * kQP + s] = aG[i][r] * f;
+      }
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
+  __syncthreads();
+  // + M X over s <= t (the wave's rows reach s < sw + 16)
+  for (int k0 = 0; k0 < sw + 16; k0 += 4) {
+    const int s = k0 + lk;
+    const float a = Mt[(sw + lr) * kQP + k0 + lk];
+    const bool ok = s < len;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+      aY[pt] = mma(a, ok ? v[(row0 + s) * C + xo + pt * 16 + lr] : 0.f, aY[pt]);
+  }
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = sw + 4 * lk + r, p = pt * 16 + lr;
+      if (t < len) y[(row0 + t) * HP + xo + p] = aY[pt][r] + Dh * v[(row0 + t) * C + xo + p];
+    }
+}
+
+// ---------------------------------------------------------------- gated norm
+// q = y silu(z), r = (mean_group(q^2) + eps)^-1/2, out = q r w. For each row:
+//   dq = w r g - q r^3 mean_group(w g q);  dy = dq silu(z);
+//   dz = dq y silu'(z);  dw += g q r  (summed over rows).
+// dy overwrites y (each thread reads its channels before writing them). A
+// workgroup takes `rows` consecutive rows and sums its share of dw in LDS,
+// then writes it to its row of dw_part [gridDim.x][HP].
+template <class T>
+__global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __restrict__ z,
+                                                       const T* __restrict__ w,
+                                                       const T* __restrict__ g, float eps,
+                                                       T* __restrict__ dz, float* dw_part,
+                                                       int64_t nrows, int rows, int HP, int G) {
+  extern __shared__ float dwl[];  // [HP]
+  __shared__ float sq[kMaxGroups], sg[kMaxGroups];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int S = HP / G;
+  // a wave's 64 consecutive channels lie in one group: sum them in the wave
+  const bool wave_groups = S % 64 == 0;
+  for (int c = tid; c < HP; c += kThreads) dwl[c] = 0.f;
+  for (int rr = 0; rr < rows; ++rr) {
+    const int64_t row = (int64_t)blockIdx.x * rows + rr;
+    if (row >= nrows) break;
+    for (int j = tid; j < G; j += kThreads) sq[j] = sg[j] = 0.f;
+    __syncthreads();
+    for (int c0 = 0; c0 < HP; c0 += kThreads) {
+      const int c = c0 + tid;
+      float q2 = 0.f, wgq = 0.f;
+      if (c < HP) {
+        const int64_t o = row * HP + c;
+        const float zz = to_f(z[o]), q = y[o] * zz / (1.f + __expf(-zz));
+        q2 = q * q;
+        wgq = to_f(w[c]) * to_f(g[o]) * q;
+      }
+      if (wave_groups) {
+        q2 = wave_sum(q2);
+        wgq = wave_sum(wgq);
+        if (lane == 0 && c < HP) {
+          atomicAdd(&sq[c / S], q2);
+          atomicAdd(&sg[c / S], wgq);
+        }
+      } else if (c < HP) {
+        atomicAdd(&sq[c / S], q2);
+        atomicAdd(&sg[c / S], wgq);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < HP; c += kThreads) {
+      const int64_t o = row * HP + c;
+      const int j = c / S;
+      const float r = rsqrtf(sq[j] / S + eps), k3 = r * r * r * sg[j] / S;
+      const float zz = to_f(z[o]), sig = 1.f / (1.f + __expf(-zz)), s = zz * sig;
+      const float yy = y[o], q = yy * s, gg = to_f(g[o]);
+      const float dq = to_f(w[c]) * r * gg - q * k3;
+      y[o] = dq * s;
+      dz[o] = from_f<T>(dq * yy * (sig + s * (1.f - sig)));
+      dwl[c] += gg * q * r;
+    }
+    __syncthreads();
+  }
+  for (int c = tid; c < HP; c += kThreads) dw_part[(int64_t)blockIdx.x * HP + c] = dwl[c];
+}
+
+// dw[c] = sum over the parts of dw_part[.][c] (a fixed order: deterministic)
+__global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict__ part,
+                                                        float* __restrict__ out, int nparts,
+                                                        int n) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= n) return;
+  float acc = 0.f;
+  for (int i = 0; i < nparts; ++i) acc += part[(int64_t)i * n + c];
+  out[c] = acc;
+}
+
 // ---------------------------------------------------------------- dS_in part
 // Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one (chunk, head), into zb.
-template <class T>
+// Work items (16-row tile of p, up to 8 tiles of n) go round the waves;
+// operands come straight from the L2-resident rows.
+template <class T, int P>
 __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ v,
                                                       const float* __restrict__ dY,
                                                       const T* __restrict__ dt, DtA dta,
                                                       const float* __restrict__ A, float* zb,
-                                                      int L, int H, int G, int P, int N, int Q,
-                                                      int nc) {
+                                                      int L, int H, int G, int N, int nc) {
   __shared__ float lam[64], dts[64], ex[64];
+  constexpr int NPT = P / 16;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int t0 = c * Q, len = min(Q, L - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int HP = H * P, C = HP + 2 * G * N, co = HP + G * N + g * N;
+  const int HP = H * P;
+  const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, co = HP + (int64_t)(G + g) * N;
   chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
   float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  for (int i = threadIdx.x; i < P * N; i += kThreads) {
-    const int p = i / N, n = i % N;
-    float acc = 0.f;
-    for (int t = 0; t < len; ++t)
-      acc += ex[t] * dY[(row0 + t) * HP + h * P + p] * v[(row0 + t) * C + co + n];
-    out[i] = acc;
+  const int nnt = N / 16, nng = (nnt + 7) / 8;
+  for (int item = wave; item < NPT * nng; item += 4) {
+    const int pt = item % NPT, nt0 = (item / NPT) * 8, ntn = min(8, nnt - nt0);
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = zero4();
+    for (int k0 = 0; k0 < len; k0 += 4) {
+      const int t = k0 + lk;
+      const bool ok = t < len;
+      const float a = ok ? ex[t] * dY[(row0 + t) * HP + xo + pt * 16 + lr] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < ntn)
+          acc[j] = mma(a, ok ? v[(row0 + t) * C + co + (nt0 + j) * 16 + lr] : 0.f, acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < ntn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          out[(int64_t)(pt * 16 + 4 * lk + r) * N + (nt0 + j) * 16 + lr] = acc[j][r];
   }
 }
 
@@ -164,132 +330,243 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 // formed term by term, without differences of partial sums:
 //   intra-chunk:  sum_{t>=u} sum_{s<u} F[t,s] dt_s,  F = K o G o E
 //   state out:    exp(Lam_end) <dS_out, S_in> + sum_{s<u} w_s U_s
-//   inter-chunk:  sum_{t>=u} Y_t,  Y_t = dY[t] . (exp(Lam_t) C_t S_in)
-// where U_s = B_s . (X[s] dS_out).
-template <class T>
-__global__ __launch_bounds__(kThreads) void k_chunk_bwd(
+//   inter-chunk:  sum_{t>=u} Y_t,  Y_t = exp(Lam_t) dY[t] . (C_t S_in^T)
+// where U_s = X[s] . (B_s dS_out^T). Wave w owns the 16-row tile w of s
+// (dX, dB) and of t (dC, C S_in^T).
+template <class T, int P>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
     const float* __restrict__ dSo, float* __restrict__ dv, float* __restrict__ dBh,
     float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD, int L, int H, int G,
-    int P, int N, int Q, int nc) {
-  extern __shared__ float sm[];
-  const int QS = Q + 1;
-  float* Km = sm;               // [Q][QS]: K = dY X^T, then dG = K E dt_s
-  float* Gm = sm + Q * QS;      // [Q][QS]: G = C B^T, then M = G E dt_s
-  float* Fm = sm + 2 * Q * QS;  // [Q][QS]: F = K G E, then its column suffix sums
+    int N, int nc) {
+  extern __shared__ __align__(16) float sm[];
+  float* Mt = sm;                // [Q][kQP]: G, then M = G o E dt_s
+  float* Dg = sm + kQ * kQP;     // [Q][kQP]: K, then dG = K o E dt_s
+  float* SA = sm + 2 * kQ * kQP; // staging
   __shared__ float lam[64], dts[64], ex[64], wv[64], colF[64], Yo[64], U[64], dai[64], tmp[64];
   __shared__ float red[4];
+  constexpr int NPT = P / 16, KP = P / 4;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = c * Q, len = min(Q, L - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int HP = H * P, C = HP + 2 * G * N;
-  const int xo = h * P, bo = HP + g * N, co = HP + G * N + g * N;
+  const int HP = H * P;
+  const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, bo = HP + (int64_t)g * N,
+                co = HP + (int64_t)(G + g) * N;
   const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
   const int64_t sb = (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   const float* Si = Sin + sb;
   const float* dS = dSo + sb;
+  const int sw = wave * 16;
+  for (int i = tid; i < 2 * kQ * kQP; i += kThreads) sm[i] = 0.f;
   chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
   const float lamE = lam[len - 1];
-  if (tid < 64) {
-    wv[tid] = tid < len ? __expf(lamE - lam[tid]) * dts[tid] : 0.f;
-    Yo[tid] = 0.f;
-    U[tid] = 0.f;
-  }
+  if (tid < 64) wv[tid] = tid < len ? __expf(lamE - lam[tid]) * dts[tid] : 0.f;
   if (tid < 4) red[tid] = 0.f;
-  // K and G over the causal pairs
-  for (int i = tid; i < Q * Q; i += kThreads) {
-    const int t = i / Q, s = i % Q;
-    float k = 0.f, gg = 0.f;
-    if (s <= t && t < len) {
-      const float* dy = dY + (row0 + t) * HP + xo;
-      const float* xs = v + (row0 + s) * C + xo;
-      for (int p = 0; p < P; ++p) k += dy[p] * xs[p];
-      const float* ct = v + (row0 + t) * C + co;
-      const float* bs = v + (row0 + s) * C + bo;
-      for (int n = 0; n < N; ++n) gg += ct[n] * bs[n];
-    }
-    Km[t * QS + s] = k;
-    Gm[t * QS + s] = gg;
-  }
-  __syncthreads();
-  // F by columns: thread s walks t down from the chunk's end, keeping
-  // R[t,s] = sum_{t' >= t} F[t',s] in place for t > s; colF[s] = R[s,s]
-  if (tid < Q) {
-    const int s = tid;
-    float acc = 0.f;
-    for (int t = len - 1; t >= s; --t) {
-      acc += Km[t * QS + s] * Gm[t * QS + s] * __expf(lam[t] - lam[s]);
-      Fm[t * QS + s] = acc;
-    }
-    colF[s] = acc;
-  }
-  __syncthreads();
-  // dai[u] = sum_{s<u} dt_s R[u,s] (four lanes per u) and the dt_s E scaling
+
+  // (1) G = C B^T and K = dY X^T on the causal tiles, over slices of n / p
   {
-    const int u = tid >> 2, j = tid & 3;
-    float acc = 0.f;
-    if (u < len)
-      for (int s = j; s < u; s += 4) acc += dts[s] * Fm[u * QS + s];
-    acc = group_sum_last<4>(acc);
-    if (j == 0 && u < Q) dai[u] = acc;
-  }
-  for (int i = tid; i < Q * Q; i += kThreads) {
-    const int t = i / Q, s = i % Q;
-    const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
-    Km[t * QS + s] *= f;
-    Gm[t * QS + s] *= f;
+    int rt[3], st[3];
+    bool on[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
+    f32x4 aG[3], aK[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) aG[i] = aK[i] = zero4();
+    float* Cs = SA;
+    float* Bs = SA + kQ * kSP;
+    float* Ys = SA + 2 * kQ * kSP;
+    float* Xs = SA + 3 * kQ * kSP;
+    const int kmax = N > P ? N : P;
+    for (int k0 = 0; k0 < kmax; k0 += kKS) {
+      const int nvn = min(kKS, N - k0), nvp = min(kKS, P - k0);
+      if (nvn > 0) {
+        stage(Cs, v + row0 * C + co + k0, C, kQ, len, nvn);
+        stage(Bs, v + row0 * C + bo + k0, C, kQ, len, nvn);
+      }
+      if (nvp > 0) {
+        stage(Ys, dY + row0 * HP + xo + k0, HP, kQ, len, nvp);
+        stage(Xs, v + row0 * C + xo + k0, C, kQ, len, nvp);
+      }
+      __syncthreads();
+      for (int kk = 0; kk < nvn; kk += 4)
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (on[i])
+            aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk],
+                        Bs[(st[i] * 16 + lr) * kSP + kk + lk], aG[i]);
+      for (int kk = 0; kk < nvp; kk += 4)
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          if (on[i])
+            aK[i] = mma(Ys[(rt[i] * 16 + lr) * kSP + kk + lk],
+                        Xs[(st[i] * 16 + lr) * kSP + kk + lk], aK[i]);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (on[i])
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
+          Mt[t * kQP + s] = aG[i][r];
+          Dg[t * kQP + s] = aK[i][r];
+        }
   }
   __syncthreads();
-  // dX[s,p] and dD
-  float ddp = 0.f;
-  for (int i = tid; i < len * P; i += kThreads) {
-    const int s = i / P, p = i % P;
-    float acc = 0.f;
-    for (int t = s; t < len; ++t) acc += Gm[t * QS + s] * dY[(row0 + t) * HP + xo + p];
-    const float dys = dY[(row0 + s) * HP + xo + p];
-    const float* bs = v + (row0 + s) * C + bo;
-    const float* dsp = dS + (int64_t)p * N;
-    float t3 = 0.f;
-    for (int n = 0; n < N; ++n) t3 += bs[n] * dsp[n];
-    dv[(row0 + s) * C + xo + p] = acc + Dh * dys + wv[s] * t3;
-    ddp += dys * v[(row0 + s) * C + xo + p];
+
+  // (2) F by columns: thread s walks t down from the chunk's end, keeping
+  // R[t,s] = sum_{t' >= t} F[t',s] (t > s) in place; colF[s] = R[s,s]
+  {
+    float* Fm = SA;  // [Q][kQ + 1]
+    constexpr int FP = kQ + 1;
+    if (tid < kQ) {
+      const int s = tid;
+      float acc = 0.f;
+      for (int t = len - 1; t >= s; --t) {
+        acc += Dg[t * kQP + s] * Mt[t * kQP + s] * __expf(lam[t] - lam[s]);
+        Fm[t * FP + s] = acc;
+      }
+      colF[s] = acc;
+    }
+    __syncthreads();
+    // dai[u] = sum_{s<u} dt_s R[u,s] (four lanes per u), then the dt_s E scaling
+    {
+      const int u = tid >> 2, j = tid & 3;
+      float acc = 0.f;
+      if (u < len)
+        for (int s = j; s < u; s += 4) acc += dts[s] * Fm[u * FP + s];
+      acc = group_sum_last<4>(acc);
+      if (j == 0) dai[u] = acc;
+    }
+    for (int i = tid; i < kQ * kQ; i += kThreads) {
+      const int t = i / kQ, s = i % kQ;
+      const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
+      Dg[t * kQP + s] *= f;
+      Mt[t * kQP + s] *= f;
+    }
+    __syncthreads();
   }
-  // dC[t,n] (and Y_t)
-  for (int i = tid; i < len * N; i += kThreads) {
-    const int t = i / N, n = i % N;
-    float acc = 0.f;
-    for (int s = 0; s <= t; ++s) acc += Km[t * QS + s] * v[(row0 + s) * C + bo + n];
-    const float* dy = dY + (row0 + t) * HP + xo;
-    float t1 = 0.f;
-    for (int p = 0; p < P; ++p) t1 += dy[p] * Si[(int64_t)p * N + n];
-    dCh[((row0 + t) * H + h) * N + n] = acc + ex[t] * t1;
-    atomicAdd(&Yo[t], ex[t] * v[(row0 + t) * C + co + n] * t1);
+
+  // (3) dX intra: sum_{t >= s} M[t,s] dY[t,p]
+  f32x4 a1[NPT], a2[NPT], aY[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) a1[i] = a2[i] = aY[i] = zero4();
+  for (int k0 = sw; k0 < kQ; k0 += 4) {
+    const int t = k0 + lk;
+    const float a = Mt[t * kQP + sw + lr];
+    const bool ok = t < len;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+      a1[pt] = mma(a, ok ? dY[(row0 + t) * HP + xo + pt * 16 + lr] : 0.f, a1[pt]);
   }
-  // dB[s,n] (and U_s)
-  for (int i = tid; i < len * N; i += kThreads) {
-    const int s = i / N, n = i % N;
-    float acc = 0.f;
-    for (int t = s; t < len; ++t) acc += Km[t * QS + s] * v[(row0 + t) * C + co + n];
-    const float* xs = v + (row0 + s) * C + xo;
-    float t2 = 0.f;
-    for (int p = 0; p < P; ++p) t2 += xs[p] * dS[(int64_t)p * N + n];
-    dBh[((row0 + s) * H + h) * N + n] = acc + wv[s] * t2;
-    atomicAdd(&U[s], v[(row0 + s) * C + bo + n] * t2);
+
+  // (4) over slices of n: B_s dS_out^T and C_t S_in^T of the wave's rows, and
+  // the slice's tiles of dC (rows t) and dB (rows s)
+  float ya[KP], xa[KP];  // A fragments: dY and X of the wave's 16 rows
+  {
+    const int r = sw + lr;
+    const bool ok = r < len;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      ya[k] = ok ? dY[(row0 + r) * HP + xo + 4 * k + lk] : 0.f;
+      xa[k] = ok ? v[(row0 + r) * C + xo + 4 * k + lk] : 0.f;
+    }
   }
-  // <dS_out, S_in>
-  float cst = 0.f;
-  for (int i = tid; i < P * N; i += kThreads) cst += dS[i] * Si[i];
-  cst = wave_sum(cst);
-  ddp = wave_sum(ddp);
-  if (lane == 0) {
-    atomicAdd(&red[0], cst);
-    atomicAdd(&red[1], ddp);
+  float cstp = 0.f;
+  {
+    float* Bs = SA;
+    float* Cs = SA + kQ * kSP;
+    float* Ss = SA + 2 * kQ * kSP;  // [P][kSP]
+    float* Ds = Ss + P * kSP;       // [P][kSP]
+    for (int n0 = 0; n0 < N; n0 += kKS) {
+      const int nv = min(kKS, N - n0);
+      stage(Bs, v + row0 * C + bo + n0, C, kQ, len, nv);
+      stage(Cs, v + row0 * C + co + n0, C, kQ, len, nv);
+      stage(Ss, Si + n0, N, P, P, nv);
+      stage(Ds, dS + n0, N, P, P, nv);
+      __syncthreads();
+      for (int i = tid; i < P * nv; i += kThreads) {
+        const int p = i / nv, n = i % nv;
+        cstp += Ss[p * kSP + n] * Ds[p * kSP + n];
+      }
+      for (int kk = 0; kk < nv; kk += 4) {
+        const float ab = Bs[(sw + lr) * kSP + kk + lk], ac = Cs[(sw + lr) * kSP + kk + lk];
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+          a2[pt] = mma(ab, Ds[(pt * 16 + lr) * kSP + kk + lk], a2[pt]);
+          aY[pt] = mma(ac, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
+        }
+      }
+      for (int nt = 0; nt < nv / 16; ++nt) {
+        f32x4 dc = zero4(), db = zero4();
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+          dc = mma(ya[k], Ss[(4 * k + lk) * kSP + nt * 16 + lr], dc);
+          db = mma(xa[k], Ds[(4 * k + lk) * kSP + nt * 16 + lr], db);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dc[r] *= ex[sw + 4 * lk + r];
+          db[r] *= wv[sw + 4 * lk + r];
+        }
+        for (int k0 = 0; k0 < sw + 16; k0 += 4)
+          dc = mma(Dg[(sw + lr) * kQP + k0 + lk], Bs[(k0 + lk) * kSP + nt * 16 + lr], dc);
+        for (int k0 = sw; k0 < kQ; k0 += 4)
+          db = mma(Dg[(k0 + lk) * kQP + sw + lr], Cs[(k0 + lk) * kSP + nt * 16 + lr], db);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = sw + 4 * lk + r;
+          if (t < len) {
+            const int64_t o = ((row0 + t) * H + h) * N + n0 + nt * 16 + lr;
+            dCh[o] = dc[r];
+            dBh[o] = db[r];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // (5) dX, and the row sums U_s, Y_t; dD and <dS_out, S_in>
+  {
+    float up[4] = {0.f, 0.f, 0.f, 0.f}, yp[4] = {0.f, 0.f, 0.f, 0.f}, ddp = 0.f;
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = sw + 4 * lk + r, p = pt * 16 + lr;
+        if (s < len) {
+          const float xv = v[(row0 + s) * C + xo + p], dys = dY[(row0 + s) * HP + xo + p];
+          dv[(row0 + s) * C + xo + p] = a1[pt][r] + wv[s] * a2[pt][r] + Dh * dys;
+          up[r] += xv * a2[pt][r];
+          yp[r] += dys * aY[pt][r];
+          ddp += dys * xv;
+        }
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      up[r] = group_sum_last<16>(up[r]);
+      yp[r] = group_sum_last<16>(yp[r]);
+    }
+    if (lr == 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = sw + 4 * lk + r;
+        U[s] = up[r];
+        Yo[s] = ex[s] * yp[r];
+      }
+    cstp = wave_sum(cstp);
+    ddp = wave_sum(ddp);
+    if (lane == 0) {
+      atomicAdd(&red[0], cstp);
+      atomicAdd(&red[1], ddp);
+    }
   }
   __syncthreads();
   if (tid == 0 && dD) atomicAdd(dD + h, red[1]);
-  // d(a_u), d(dt_u) and dA (wave 0, one lane per position)
+  // (6) d(a_u), d(dt_u) and dA (wave 0, one lane per position)
   if (wave == 0) {
     const int u = lane;
     // sum_{t >= u} Y_t: an inclusive scan over the reversed positions
@@ -397,19 +674,29 @@ __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ 
 
 }  // namespace bwd
 
-// Workspace of the backward pass: fp32 v, y / dY, carried-in states, Lam_end,
-// dS_out, per-head dB / dC and dv, for chunk length Q.
+// Workspace of the backward pass (fp32): conv output v [T, Cch], y then dY
+// [T, H*P], carried-in states and their gradients [B, nc, H, P, N], Lam_end
+// [B, H, nc], per-head dB / dC [T, H, N], dv [T, Cch]; 64-token chunks.
 namespace {
 size_t bround(size_t b) { return (b + 255) / 256 * 256; }
+
+// LDS of the per-chunk kernels (the y recompute and the chunk gradients)
+size_t bwd_y_lds(int P) {
+  return ((size_t)bwd::kQ * bwd::kQP + 2 * bwd::kQ * bwd::kSP + (size_t)P * bwd::kSP) * 4;
 }
-// chunk length of the backward kernels (their [Q][Q+1] tiles live in LDS)
-constexpr int kBwdChunk = 64;
+size_t bwd_chunk_lds(int P) {
+  const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP, fm = (size_t)bwd::kQ * (bwd::kQ + 1),
+               stage4 = 2 * (size_t)bwd::kQ * bwd::kSP + 2 * (size_t)P * bwd::kSP;
+  return (2 * (size_t)bwd::kQ * bwd::kQP + std::max(stage1, std::max(fm, stage4))) * 4;
+}
+}  // namespace
+
 size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {
   const size_t T = (size_t)B * L, HP = (size_t)H * P, C = HP + 2 * (size_t)G * N;
-  const size_t Q = kBwdChunk, nc = (L + Q - 1) / Q;
+  const size_t nc = (L + bwd::kQ - 1) / bwd::kQ;
   const size_t st = (size_t)B * nc * H * P * N * 4;
   return bround(T * C * 4) + bround(T * HP * 4) + 2 * bround(st) + bround((size_t)B * H * nc * 4) +
-         2 * bround(T * H * N * 4) + bround(T * C * 4);
+         2 * bround(T * H * N * 4) + bround(T * C * 4) + bround((size_t)bwd::kNormBlocks * HP * 4);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
@@ -417,7 +704,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   const bool bf = a.io_bf16;
   const int B = a.B, L = a.L, H = a.H, P = a.P, G = a.G, N = a.N, W = a.W;
   const int64_t T = (int64_t)B * L, HP = (int64_t)H * P, C = HP + 2 * (int64_t)G * N;
-  const int Q = kBwdChunk, nc = (L + Q - 1) / Q;
+  const int nc = (L + kQ - 1) / kQ;
   const size_t sts = (size_t)B * nc * H * P * N * 4;
   unsigned char* w = (unsigned char*)a.ws;
   float* v = (float*)w;
@@ -435,109 +722,142 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   float* dCh = (float*)w;
   w += bround(T * H * N * 4);
   float* dv = (float*)w;
+  w += bround(T * C * 4);
+  float* dw_part = (float*)w;
   const DtA plain{H, nullptr};
+  const dim3 gc(nc, H, B), blk(kThreads);
   hipError_t e;
-#define SSD_CHECK()                         \
+#define SSD_CHECK()                          \
   if ((e = hipGetLastError()) != hipSuccess) \
     return e;
-  // recompute the forward pieces (fp32 operands)
+// one launch per head size (the kernels are specialised on P)
+#define SSD_BY_P(LAUNCH)               \
+  switch (P) {                         \
+    case 16: LAUNCH(16); break;        \
+    case 32: LAUNCH(32); break;        \
+    case 64: LAUNCH(64); break;        \
+    default: LAUNCH(128); break;       \
+  }
+  // recompute the forward: conv output, chunk states passed into carried-in
+  // states, y (all fp32)
   e = launch_conv1d(bf, B, L, (int)C, W, a.xbc, C, a.conv_w, a.conv_b, a.conv_in, v, C, true, st);
   if (e != hipSuccess) return e;
-  ScanShape s{B, L, H, P, G, N, Q, nc, plain};
+  ScanShape s{B, L, H, P, G, N, kQ, nc, plain};
   const unsigned char* vb = (const unsigned char*)v;
   e = launch_chunk_state(bf, true, true, s, v, C, a.dt, a.A, vb + HP * 4, C, states, lam_end,
                          a.status, st);
   if (e != hipSuccess) return e;
   e = launch_state_pass(s, states, lam_end, a.s_in, nullptr, a.status, st);
   if (e != hipSuccess) return e;
-  e = launch_chunk_out(bf, true, true, s, v, C, a.dt, a.A, a.D, vb + HP * 4,
-                       vb + (HP + (int64_t)G * N) * 4, C, states, y, true, a.status, st);
-  if (e != hipSuccess) return e;
+  {
+    ProfScope ps(st, KID_BWD_Y);
+    const size_t lds = bwd_y_lds(P);
+#define SSD_Y(PP)                                                                               \
+  if (bf)                                                                                       \
+    hipLaunchKernelGGL((k_bwd_y<bf16, PP>), gc, blk, lds, st, v, (const bf16*)a.dt, plain, a.A, \
+                       a.D, states, y, L, H, G, N, nc);                                         \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_bwd_y<float, PP>), gc, blk, lds, st, v, (const float*)a.dt, plain,    \
+                       a.A, a.D, states, y, L, H, G, N, nc)
+    SSD_BY_P(SSD_Y)
+#undef SSD_Y
+  }
+  SSD_CHECK();
   // zero the summed gradients
   auto zero = [&](float* p, int64_t n) {
     if (p && n > 0)
       hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 4096)),
-                         dim3(kThreads), 0, st, p, n);
+                         blk, 0, st, p, n);
   };
   zero(a.d_A, H);
   zero(a.d_D, H);
   zero(a.d_conv_w, C * W);
   zero(a.d_conv_b, C);
-  zero(a.d_norm_w, HP);
   SSD_CHECK();
-  const dim3 gr((unsigned)((T + kNormRows - 1) / kNormRows));
   {
-  ProfScope ps(st, KID_BWD_NORM);
-  if (bf)
-    hipLaunchKernelGGL(k_norm_bwd<bf16>, gr, dim3(kThreads), 0, st, y, (const bf16*)a.z,
-                       (const bf16*)a.norm_w, (const bf16*)a.d_out, a.eps, (bf16*)a.d_z,
-                       a.d_norm_w, T, (int)HP, G);
-  else
-    hipLaunchKernelGGL(k_norm_bwd<float>, gr, dim3(kThreads), 0, st, y, (const float*)a.z,
-                       (const float*)a.norm_w, (const float*)a.d_out, a.eps, (float*)a.d_z,
-                       a.d_norm_w, T, (int)HP, G);
-  }
-  SSD_CHECK();
-  const dim3 gc(nc, H, B);
-  {
-  ProfScope ps(st, KID_BWD_CHUNK_Z);
-  if (bf)
-    hipLaunchKernelGGL(k_chunk_z<bf16>, gc, dim3(kThreads), 0, st, v, y, (const bf16*)a.dt, plain,
-                       a.A, dso, L, H, G, P, N, Q, nc);
-  else
-    hipLaunchKernelGGL(k_chunk_z<float>, gc, dim3(kThreads), 0, st, v, y, (const float*)a.dt,
-                       plain, a.A, dso, L, H, G, P, N, Q, nc);
+    ProfScope ps(st, KID_BWD_NORM);
+    const int rows = (int)((T + kNormBlocks - 1) / kNormBlocks);
+    const int nb = (int)((T + rows - 1) / rows);
+    const size_t lds = (size_t)HP * 4;
+    if (bf)
+      hipLaunchKernelGGL(k_norm_bwd<bf16>, dim3(nb), blk, lds, st, y, (const bf16*)a.z,
+                         (const bf16*)a.norm_w, (const bf16*)a.d_out, a.eps, (bf16*)a.d_z,
+                         dw_part, T, rows, (int)HP, G);
+    else
+      hipLaunchKernelGGL(k_norm_bwd<float>, dim3(nb), blk, lds, st, y, (const float*)a.z,
+                         (const float*)a.norm_w, (const float*)a.d_out, a.eps, (float*)a.d_z,
+                         dw_part, T, rows, (int)HP, G);
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((HP + kThreads - 1) / kThreads)), blk, 0, st,
+                       dw_part, a.d_norm_w, nb, (int)HP);
   }
   SSD_CHECK();
   {
-  ProfScope ps(st, KID_BWD_REV_PASS);
-  hipLaunchKernelGGL(k_rev_pass, dim3((P * N + kThreads - 1) / kThreads, H, B), dim3(kThreads), 0,
-                     st, dso, lam_end, a.d_s_out, a.d_s_in, H, P * N, nc);
-  }
-  SSD_CHECK();
-  const size_t lds = 3 * (size_t)Q * (Q + 1) * 4;
-  {
-  ProfScope ps(st, KID_BWD_CHUNK);
-  if (bf)
-    hipLaunchKernelGGL(k_chunk_bwd<bf16>, gc, dim3(kThreads), lds, st, v, y, (const bf16*)a.dt,
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (bf16*)a.d_dt, a.d_A, a.d_D, L,
-                       H, G, P, N, Q, nc);
-  else
-    hipLaunchKernelGGL(k_chunk_bwd<float>, gc, dim3(kThreads), lds, st, v, y, (const float*)a.dt,
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (float*)a.d_dt, a.d_A, a.d_D,
-                       L, H, G, P, N, Q, nc);
+    ProfScope ps(st, KID_BWD_CHUNK_Z);
+#define SSD_Z(PP)                                                                                \
+  if (bf)                                                                                        \
+    hipLaunchKernelGGL((k_chunk_z<bf16, PP>), gc, blk, 0, st, v, y, (const bf16*)a.dt, plain,    \
+                       a.A, dso, L, H, G, N, nc);                                                \
+  else                                                                                           \
+    hipLaunchKernelGGL((k_chunk_z<float, PP>), gc, blk, 0, st, v, y, (const float*)a.dt, plain,  \
+                       a.A, dso, L, H, G, N, nc)
+    SSD_BY_P(SSD_Z)
+#undef SSD_Z
   }
   SSD_CHECK();
   {
-  ProfScope ps(st, KID_BWD_GROUP_SUM);
-  hipLaunchKernelGGL(k_group_sum, dim3((unsigned)((T * G * N + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, dBh, dCh, dv, T, H, G, N, (int)HP);
+    ProfScope ps(st, KID_BWD_REV_PASS);
+    hipLaunchKernelGGL(k_rev_pass, dim3((P * N + kThreads - 1) / kThreads, H, B), blk, 0, st,
+                       dso, lam_end, a.d_s_out, a.d_s_in, H, P * N, nc);
   }
   SSD_CHECK();
-  const dim3 gd((unsigned)((C + kThreads - 1) / kThreads), (L + kConvTok - 1) / kConvTok, B);
   {
-  ProfScope ps(st, KID_BWD_CONV_DU);
-  if (bf)
-    hipLaunchKernelGGL(k_conv_du<bf16>, gd, dim3(kThreads), 0, st, (const bf16*)a.xbc,
-                       (const bf16*)a.conv_in, (const bf16*)a.conv_w, (const bf16*)a.conv_b, dv,
-                       a.d_conv_w, a.d_conv_b, L, (int)C, W);
-  else
-    hipLaunchKernelGGL(k_conv_du<float>, gd, dim3(kThreads), 0, st, (const float*)a.xbc,
-                       (const float*)a.conv_in, (const float*)a.conv_w, (const float*)a.conv_b,
-                       dv, a.d_conv_w, a.d_conv_b, L, (int)C, W);
+    ProfScope ps(st, KID_BWD_CHUNK);
+    const size_t lds = bwd_chunk_lds(P);
+#define SSD_CB(PP)                                                                              \
+  if (bf)                                                                                       \
+    hipLaunchKernelGGL((k_chunk_bwd<bf16, PP>), gc, blk, lds, st, v, y, (const bf16*)a.dt,      \
+                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (bf16*)a.d_dt, a.d_A, a.d_D, \
+                       L, H, G, N, nc);                                                         \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_chunk_bwd<float, PP>), gc, blk, lds, st, v, y, (const float*)a.dt,    \
+                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (float*)a.d_dt, a.d_A,       \
+                       a.d_D, L, H, G, N, nc)
+    SSD_BY_P(SSD_CB)
+#undef SSD_CB
   }
   SSD_CHECK();
-  const dim3 gx((unsigned)((C + kThreads - 1) / kThreads), (L + W - 1 + kConvTok - 1) / kConvTok, B);
   {
-  ProfScope ps(st, KID_BWD_CONV_DX);
-  if (bf)
-    hipLaunchKernelGGL(k_conv_dx<bf16>, gx, dim3(kThreads), 0, st, dv, (const bf16*)a.conv_w,
-                       (bf16*)a.d_xbc, a.d_conv_in, L, (int)C, W);
-  else
-    hipLaunchKernelGGL(k_conv_dx<float>, gx, dim3(kThreads), 0, st, dv, (const float*)a.conv_w,
-                       (float*)a.d_xbc, a.d_conv_in, L, (int)C, W);
+    ProfScope ps(st, KID_BWD_GROUP_SUM);
+    hipLaunchKernelGGL(k_group_sum, dim3((unsigned)((T * G * N + kThreads - 1) / kThreads)), blk,
+                       0, st, dBh, dCh, dv, T, H, G, N, (int)HP);
   }
   SSD_CHECK();
+  {
+    ProfScope ps(st, KID_BWD_CONV_DU);
+    const dim3 gd((unsigned)((C + kThreads - 1) / kThreads), (L + kConvTok - 1) / kConvTok, B);
+    if (bf)
+      hipLaunchKernelGGL(k_conv_du<bf16>, gd, blk, 0, st, (const bf16*)a.xbc,
+                         (const bf16*)a.conv_in, (const bf16*)a.conv_w, (const bf16*)a.conv_b, dv,
+                         a.d_conv_w, a.d_conv_b, L, (int)C, W);
+    else
+      hipLaunchKernelGGL(k_conv_du<float>, gd, blk, 0, st, (const float*)a.xbc,
+                         (const float*)a.conv_in, (const float*)a.conv_w, (const float*)a.conv_b,
+                         dv, a.d_conv_w, a.d_conv_b, L, (int)C, W);
+  }
+  SSD_CHECK();
+  {
+    ProfScope ps(st, KID_BWD_CONV_DX);
+    const dim3 gx((unsigned)((C + kThreads - 1) / kThreads),
+                  (L + W - 1 + kConvTok - 1) / kConvTok, B);
+    if (bf)
+      hipLaunchKernelGGL(k_conv_dx<bf16>, gx, blk, 0, st, dv, (const bf16*)a.conv_w,
+                         (bf16*)a.d_xbc, a.d_conv_in, L, (int)C, W);
+    else
+      hipLaunchKernelGGL(k_conv_dx<float>, gx, blk, 0, st, dv, (const float*)a.conv_w,
+                         (float*)a.d_xbc, a.d_conv_in, L, (int)C, W);
+  }
+  SSD_CHECK();
+#undef SSD_BY_P
 #undef SSD_CHECK
   return hipSuccess;
 }

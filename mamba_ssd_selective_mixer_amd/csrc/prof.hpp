@@ -28,6 +28,7 @@ enum KernelId {
   KID_BWD_GROUP_SUM,
   KID_BWD_CONV_DU,
   KID_BWD_CONV_DX,
+  KID_BWD_Y,
   KID_COUNT
 };
 
