@@ -16,7 +16,8 @@ decode steps over a state pool in one call), the tiny-model layer prefill
 8192 tokens, each resuming from the previous piece's states, per piece and
 per chain), the decode loop (256 sequences x 64 single-token steps, 256
 heads), the tiny fp32 layer and a bf16 shape outside the fused kernels'
-envelope (both on the general kernels); under "ceilings": a streaming copy
+envelope (both on the general kernels), and the backward pass of the
+large-model layer prefill (every gradient, fp32 MFMA); under "ceilings": a streaming copy
 and an MFMA-only loop on this GPU; under "cpu_baseline": the fp64 oracle on
 the host cores.
 
@@ -39,10 +40,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0   # dense fp16 / bf16 MFMA, TFLOP/s
+MFMA_F32_PEAK_TFS = 157.3    # dense fp32 MFMA, TFLOP/s
 
 KERNEL_NAMES = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
                 "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
-                "fused_chunk_out_norm")
+                "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z", "bwd_rev_pass",
+                "bwd_chunk", "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx", "bwd_y")
 DOMINANT = "fused_chunk_out_norm"
 FUSED = ("fused_chunk_state", "fused_state_pass", "fused_chunk_out_norm")
 # Counter-measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE,
@@ -91,7 +94,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=2, help="alternating input/output buffer sets")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events")
-    ap.add_argument("--only", choices=("tiny", "chain", "decode", "general", "serving",
+    ap.add_argument("--only", choices=("tiny", "chain", "decode", "general", "serving", "backward",
                                        "unpacked"),
                     help="time only one of the secondary workloads (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -159,13 +162,17 @@ def to_dev(torch, a, dt):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda", dt)
 
 
-def kernel_times(ops, run, steps, launches_per_step=8):
+def kernel_times(ops, run, steps, launches_per_step=8, only=None):
     """{kernel: mean ms per launch} from the library's per-kernel HIP events
-    (recorded on the stream each kernel runs on) over `steps` calls of run()."""
+    (recorded on the stream each kernel runs on) over `steps` calls of run().
+    only: time just these kernels (the others launch with no events around
+    them, so the stream keeps its ordinary spacing)."""
+    ops.profile_only(only)
     ops.profile_start(launches_per_step * steps)
     for i in range(steps):
         run(i)
     ops.profile_stop()
+    ops.profile_only(None)
     out = {}
     for name in KERNEL_NAMES:
         n, t = ops.profile_read(name)
@@ -175,13 +182,15 @@ def kernel_times(ops, run, steps, launches_per_step=8):
 
 
 def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, states_out,
-                     kernel_events=True, packed=False):
+                     kernel_events=True, packed=False, breakdown=True):
     """Mean ms per prefill call over `steps` timed calls (HIP events around the
-    whole timed region), and per-kernel mean ms from a second, event-bracketed
-    pass over the same calls (the per-kernel events add gaps between
-    launches, so the step time comes from the first pass). packed: the call
-    takes the input projection's rows [z | xBC | dt_raw] with dt_bias and
-    A_log (dt and A formed in the kernels)."""
+    whole timed region), and the output kernel's mean ms over the same calls
+    (only that kernel is bracketed by the library's events, on its own
+    stream; the other launches keep their ordinary spacing). With breakdown,
+    the other kernels' mean ms from a second pass in which every launch is
+    bracketed. packed: the call takes the input projection's rows
+    [z | xBC | dt_raw] with dt_bias and A_log (dt and A formed in the
+    kernels)."""
     td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     prm = synth.packed_params(cfg) if packed else synth.layer_params(cfg)
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
@@ -224,13 +233,29 @@ def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, st
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # the output kernel (fused or general, whichever the shape runs) is
+    # bracketed by events inside the timed steps themselves
+    out_ks = [DOMINANT, "chunk_out"]
+    if kernel_events:
+        ops.profile_only(out_ks)
+        ops.profile_start(2 * steps)
     tm = Timer(torch)
     tm.start()
     for i in range(steps):
         step(i)
     ms = tm.stop_ms() / steps
     torch.cuda.synchronize()
-    kern = kernel_times(ops, step, steps) if kernel_events else {}
+    kern = {}
+    if kernel_events:
+        ops.profile_stop()
+        ops.profile_only(None)
+        for name in out_ks:
+            n, t = ops.profile_read(name)
+            if n:
+                kern[name] = t / n
+        if breakdown:
+            for k, v in kernel_times(ops, step, steps).items():
+                kern.setdefault(k, v)
     status = ops.ssd_workspace_status(ws)
     del sets, ws
     torch.cuda.empty_cache()
@@ -382,6 +407,81 @@ def run_serving(torch, ops, synth, reps, kernel_events=True):
                       f"state 128, bf16"}
 
 
+BWD_CHUNK = 64  # chunk length of the backward kernels
+
+
+def backward_flops(cfg):
+    """Algorithmic fp32 MFMA FLOPs per launch of the backward's three matrix
+    kernels (causal products counted over their lower half): the y
+    recompute (C B^T, M X, C S_in^T), the state-gradient terms (Z) and the
+    per-chunk gradients (dY X^T, C B^T, dX's two terms, dC's and dB's two
+    terms each)."""
+    Q, P, N = BWD_CHUNK, cfg.headdim, cfg.dstate
+    units = cfg.batch * cfg.nheads * -(-cfg.seqlen // Q)
+    tri = Q * Q / 2
+    return {"bwd_y": 2 * units * (tri * (N + P) + Q * N * P),
+            "bwd_chunk_z": 2 * units * Q * P * N,
+            "bwd_chunk": 2 * units * (tri * (2 * P + 3 * N) + 3 * Q * P * N)}
+
+
+def run_backward(torch, ops, synth, reps, kernel_events=True):
+    """Backward pass of the large-model layer prefill (the headline layer:
+    1 x 8192 tokens, 256 heads x 64, 8 groups, state 128, bf16 I/O): every
+    gradient (xBC, z, dt, A, D, conv weight, norm weight) for a seeded
+    upstream gradient, the forward recomputed inside the call."""
+    bf = torch.bfloat16
+    cfg = synth.CONFIGS["c2"]
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg)
+    seeds = synth.backward_seeds(cfg)
+    d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
+                    cfg.conv_width, cfg.chunk, bf)
+    args = [to_dev(torch, inp["xbc"], bf), to_dev(torch, inp["z"], bf),
+            to_dev(torch, inp["dt"], bf), to_dev(torch, prm["A"], torch.float32),
+            to_dev(torch, prm["D"], torch.float32), to_dev(torch, prm["conv_w"], bf), None,
+            to_dev(torch, seeds["norm_w"], bf), to_dev(torch, seeds["d_out"], bf)]
+    ws = ops.workspace(ops.ssd_mixer_backward_workspace_bytes(d))
+    grads = ops.ssd_mixer_backward(d, *args, eps=prm["eps"], ws=ws)
+
+    def one(_i=0):
+        ops.ssd_mixer_backward(d, *args, eps=prm["eps"], grads=grads, ws=ws)
+
+    one()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(reps):
+        one()
+    ms = tm.stop_ms() / reps
+    kern = kernel_times(ops, one, reps, launches_per_step=16) if kernel_events else {}
+    status = ops.ssd_workspace_status(ws)
+    T = cfg.batch * cfg.seqlen
+    # algorithmic bytes: xBC, z, dt and d_out read; d_xBC, d_z, d_dt written
+    nb = 2 * T * (2 * cfg.channels + 2 * cfg.hp + 2 * cfg.nheads)
+    fl = backward_flops(cfg)
+    mats = {}
+    for k, f in fl.items():
+        if k in kern:
+            tf = f / (kern[k] * 1e-3) / 1e12
+            mats[k] = {"flops_per_launch": f, "us": kern[k] * 1e3, "tflops": tf,
+                       "mfma_f32_frac": tf / MFMA_F32_PEAK_TFS}
+    del grads, ws, args
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": T / (ms * 1e-3), "ms_per_call": ms,
+            "algorithmic_bytes": nb, "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "roofline": ({"bound": "mfma", "kernel": "bwd_chunk", "dtype": "f32",
+                          "achieved": mats["bwd_chunk"]["tflops"], "peak": MFMA_F32_PEAK_TFS,
+                          "unit": "TFLOP/s", "frac": mats["bwd_chunk"]["mfma_f32_frac"]}
+                         if "bwd_chunk" in mats else None),
+            "matrix_kernels": mats,
+            "kernels_us": {k: v * 1e3 for k, v in kern.items()}, "status": status,
+            "config": "backward of the headline layer prefill: 1 x 8192 tokens, 256 heads x 64, "
+                      "8 groups, state 128, conv width 4, bf16 I/O, no conv bias, zero initial "
+                      "states; d_out ~ N(0,1), norm weight 1 + N(0,1)/4; gradients of xBC, z, dt "
+                      "(bf16) and A, D, conv weight, norm weight (fp32); fp32 MFMA, 64-token "
+                      "chunks, forward recomputed in the call"}
+
+
 def ceilings(torch):
     """A streaming 2 GiB device copy and an MFMA-only loop on this GPU."""
     from mamba_ssd_selective_mixer_amd import build as hb
@@ -505,6 +605,8 @@ def secondary(torch, ops, synth, args, which):
                                   "state 128, states ~ N(0, 0.1) updated in place"}
     if "serving" in which:
         wl["serving_mixed_batch"] = run_serving(torch, ops, synth, 5, ke)
+    if "backward" in which:
+        wl["large_layer_backward"] = run_backward(torch, ops, synth, 3, ke)
     if "unpacked" in which:
         c2 = synth.CONFIGS["c2"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
@@ -554,7 +656,8 @@ def main():
         return
     cfg = synth.CONFIGS["c2"]
     ms, kern, rc = prefill_workload(torch, ops, synth, cfg, args.steps, args.warmup, args.sets,
-                                    False, True, not args.no_kernel_events, packed=True)
+                                    False, True, not args.no_kernel_events, packed=True,
+                                    breakdown=not args.quick)
     if rc != 0:
         print(f"prefill reported status {rc}", file=sys.stderr)
         sys.exit(1)
@@ -598,7 +701,8 @@ def main():
     }
     if not args.quick:
         rec["workloads"] = secondary(torch, ops, synth, args, ("unpacked", "tiny", "chain",
-                                                               "decode", "serving", "general"))
+                                                               "decode", "serving", "general",
+                                                               "backward"))
         rec["ceilings"] = ceilings(torch)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(synth, cfg)

@@ -441,6 +441,11 @@ typedef enum {
 } ssd_kernel_id;
 int ssd_profile_start(int capacity);
 int ssd_profile_stop(void);
+/* Which kernels the timing brackets: bit k set times kernel id k (all by
+ * default); the others launch with no events around them, so the timed
+ * stream keeps its ordinary launch-to-launch spacing. Returns the previous
+ * mask. Stays in force across starts. */
+uint64_t ssd_profile_set_mask(uint64_t mask);
 int ssd_profile_read(int kernel, int64_t* launches, double* total_ms);
 const char* ssd_kernel_name(int kernel);
 

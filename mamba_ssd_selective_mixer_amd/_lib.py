@@ -31,7 +31,8 @@ EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "
            "ssd_mixer_varlen_workspace_bytes", "ssd_mixer_varlen",
            "ssd_mixer_prefill_noalloc", "ssd_mixer_backward_workspace_bytes",
            "ssd_mixer_backward", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
-           "ssd_profile_start", "ssd_profile_stop", "ssd_profile_read", "ssd_kernel_name")
+           "ssd_profile_start", "ssd_profile_stop", "ssd_profile_set_mask", "ssd_profile_read",
+           "ssd_kernel_name")
 
 
 class Dims(ctypes.Structure):
@@ -84,6 +85,7 @@ def load():
         "ssd_set_exchange_spin_limit": (i32, [i32]),
         "ssd_profile_start": (i32, [i32]),
         "ssd_profile_stop": (i32, []),
+        "ssd_profile_set_mask": (ctypes.c_uint64, [ctypes.c_uint64]),
         "ssd_profile_read": (i32, [i32, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)]),
         "ssd_kernel_name": (ctypes.c_char_p, [i32]),
     }

@@ -29,7 +29,7 @@ constexpr int kQ = 64;           // chunk length
 constexpr int kQP = kQ + 4;      // pitch of the Q x Q tiles (floats)
 constexpr int kKS = 32;          // width of a staged operand slice
 constexpr int kSP = kKS + 4;     // pitch of a staged slice
-constexpr int kNormBlocks = 512; // most norm-backward workgroups (one dw part each)
+constexpr int kNormBlocks = 1024; // most norm-backward workgroups (one dw part each)
 constexpr int kMaxGroups = 256;
 
 // MFMA 16x16x4 fp32. Lane l supplies A[row l%16][k l/16] and B[k l/16][col
@@ -48,12 +48,61 @@ __global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
 // Rows [0, rows) x columns [0, kKS) of a row-major fp32 matrix (row stride
 // rs, elements) into dst [rows][kSP]; rows >= nrows and columns >= ncols
 // (a multiple of 4) are zero.
-SSD_DEV void stage(float* dst, const float* src, int64_t rs, int rows, int nrows, int ncols) {
+SSD_DEV void stage(float* dst, const float* src, int rs, int rows, int nrows, int ncols) {
   for (int i = threadIdx.x; i < rows * (kKS / 4); i += kThreads) {
     const int r = i / (kKS / 4), c4 = (i % (kKS / 4)) * 4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < nrows && c4 < ncols) v = *reinterpret_cast<const float4*>(src + r * rs + c4);
     *reinterpret_cast<float4*>(dst + r * kSP + c4) = v;
+  }
+}
+
+// One staged slice (rows [0, ROWS) x columns [0, kKS)) held in registers
+// between its global loads and its LDS stores, so that the next slice's
+// loads are in flight while the current one is computed on.
+template <int ROWS>
+struct SliceRegs {
+  static constexpr int kItems = ROWS * (kKS / 4), kN = (kItems + kThreads - 1) / kThreads;
+  float4 v[kN];
+  SSD_DEV void load(const float* src, int rs, int nrows, int ncols) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx / (kKS / 4), c4 = (idx % (kKS / 4)) * 4;
+      v[i] = (idx < kItems && r < nrows && c4 < ncols)
+                 ? *reinterpret_cast<const float4*>(src + r * rs + c4)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  SSD_DEV void store(float* dst) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx / (kKS / 4), c4 = (idx % (kKS / 4)) * 4;
+      if (idx < kItems) *reinterpret_cast<float4*>(dst + r * kSP + c4) = v[i];
+    }
+  }
+};
+
+// Rows [0, rows) x columns [0, cols) (a multiple of 4) of a row-major fp32
+// matrix into dst [rows][pitch], scaled per row by sc[r] when sc is given;
+// rows >= nrows are zero. A pitch of 16 (mod 64) floats keeps column-wise
+// fragment reads (16 columns x 4 rows per wave) free of bank conflicts.
+SSD_DEV void stage_rows(float* dst, int pitch, const float* src, int rs, int rows, int nrows,
+                        int cols, const float* sc = nullptr) {
+  const int c4n = cols / 4;
+  for (int i = threadIdx.x; i < rows * c4n; i += kThreads) {
+    const int r = i / c4n, c4 = (i % c4n) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nrows) {
+      v = *reinterpret_cast<const float4*>(src + r * rs + c4);
+      if (sc) {
+        const float f = sc[r];
+        v.x *= f;
+        v.y *= f;
+        v.z *= f;
+        v.w *= f;
+      }
+    }
+    *reinterpret_cast<float4*>(dst + r * pitch + c4) = v;
   }
 }
 
@@ -132,12 +181,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_y(const float* __restrict__
   for (int i = 0; i < NPT; ++i) aY[i] = zero4();
   const int sw = wave * 16;
   // G on the causal tiles and C S_in^T on the wave's rows, over slices of n
+  SliceRegs<kQ> rb, rc;
+  SliceRegs<P> rs;
+  auto fetch = [&](int n0) {
+    const int nv = min(kKS, N - n0);
+    rb.load(v + row0 * C + bo + n0, (int)C, len, nv);
+    rc.load(v + row0 * C + co + n0, (int)C, len, nv);
+    rs.load(Si + n0, N, P, nv);
+  };
+  fetch(0);
   for (int n0 = 0; n0 < N; n0 += kKS) {
     const int nv = min(kKS, N - n0);
-    stage(Bs, v + row0 * C + bo + n0, C, kQ, len, nv);
-    stage(Cs, v + row0 * C + co + n0, C, kQ, len, nv);
-    stage(Ss, Si + n0, N, P, P, nv);
+    rb.store(Bs);
+    rc.store(Cs);
+    rs.store(Ss);
     __syncthreads();
+    if (n0 + kKS < N) fetch(n0 + kKS);
     for (int kk = 0; kk < nv; kk += 4) {
 #pragma unroll
       for (int i = 0; i < 3; ++i)
@@ -164,15 +223,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_y(const float* __restrict__
   for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
+  // the chunk's x rows, where B and C were staged
+  float* Xs = Bs;  // [Q][P + 16]
+  stage_rows(Xs, P + 16, v + row0 * C + xo, (int)C, kQ, len, P);
   __syncthreads();
   // + M X over s <= t (the wave's rows reach s < sw + 16)
   for (int k0 = 0; k0 < sw + 16; k0 += 4) {
-    const int s = k0 + lk;
     const float a = Mt[(sw + lr) * kQP + k0 + lk];
-    const bool ok = s < len;
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
-      aY[pt] = mma(a, ok ? v[(row0 + s) * C + xo + pt * 16 + lr] : 0.f, aY[pt]);
+      aY[pt] = mma(a, Xs[(k0 + lk) * (P + 16) + pt * 16 + lr], aY[pt]);
   }
 #pragma unroll
   for (int pt = 0; pt < NPT; ++pt)
@@ -184,91 +244,147 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_y(const float* __restrict__
 }
 
 // ---------------------------------------------------------------- gated norm
+SSD_DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+SSD_DEV float4 ld4(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+SSD_DEV void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+SSD_DEV void st4(bf16* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+SSD_DEV float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
+
 // q = y silu(z), r = (mean_group(q^2) + eps)^-1/2, out = q r w. For each row:
 //   dq = w r g - q r^3 mean_group(w g q);  dy = dq silu(z);
 //   dz = dq y silu'(z);  dw += g q r  (summed over rows).
-// dy overwrites y (each thread reads its channels before writing them). A
-// workgroup takes `rows` consecutive rows and sums its share of dw in LDS,
-// then writes it to its row of dw_part [gridDim.x][HP].
+// dy overwrites y (each thread reads its channels before writing them). Each
+// thread takes 4 consecutive channels (one norm group: groups are multiples
+// of 16 channels). A workgroup takes `rows` consecutive rows and sums its
+// share of dw in LDS, then writes it to its row of dw_part [gridDim.x][HP].
 template <class T>
 __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __restrict__ z,
                                                        const T* __restrict__ w,
                                                        const T* __restrict__ g, float eps,
                                                        T* __restrict__ dz, float* dw_part,
                                                        int64_t nrows, int rows, int HP, int G) {
-  extern __shared__ float dwl[];  // [HP]
+  extern __shared__ float4 dwl[];  // [HP / 4]
   __shared__ float sq[kMaxGroups], sg[kMaxGroups];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int S = HP / G;
-  // a wave's 64 consecutive channels lie in one group: sum them in the wave
-  const bool wave_groups = S % 64 == 0;
-  for (int c = tid; c < HP; c += kThreads) dwl[c] = 0.f;
+  const int S = HP / G, HP4 = HP / 4;
+  // a wave's 256 consecutive channels lie in one group: sum them in the wave
+  const bool wave_groups = S % 256 == 0;
+  for (int c = tid; c < HP4; c += kThreads) dwl[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int rr = 0; rr < rows; ++rr) {
     const int64_t row = (int64_t)blockIdx.x * rows + rr;
     if (row >= nrows) break;
     for (int j = tid; j < G; j += kThreads) sq[j] = sg[j] = 0.f;
     __syncthreads();
-    for (int c0 = 0; c0 < HP; c0 += kThreads) {
-      const int c = c0 + tid;
+#pragma unroll 4
+    for (int c0 = 0; c0 < HP4; c0 += kThreads) {
+      const int c4 = c0 + tid, c = 4 * c4;
       float q2 = 0.f, wgq = 0.f;
-      if (c < HP) {
+      if (c4 < HP4) {
         const int64_t o = row * HP + c;
-        const float zz = to_f(z[o]), q = y[o] * zz / (1.f + __expf(-zz));
-        q2 = q * q;
-        wgq = to_f(w[c]) * to_f(g[o]) * q;
+        const float4 zz = ld4(z + o), yy = ld4(y + o), ww = ld4(w + c), gg = ld4(g + o);
+        const float4 q = make_float4(yy.x * zz.x * frcp(1.f + __expf(-zz.x)),
+                                     yy.y * zz.y * frcp(1.f + __expf(-zz.y)),
+                                     yy.z * zz.z * frcp(1.f + __expf(-zz.z)),
+                                     yy.w * zz.w * frcp(1.f + __expf(-zz.w)));
+        q2 = sum4(make_float4(q.x * q.x, q.y * q.y, q.z * q.z, q.w * q.w));
+        wgq = sum4(make_float4(ww.x * gg.x * q.x, ww.y * gg.y * q.y, ww.z * gg.z * q.z,
+                               ww.w * gg.w * q.w));
       }
       if (wave_groups) {
         q2 = wave_sum(q2);
         wgq = wave_sum(wgq);
-        if (lane == 0 && c < HP) {
+        if (lane == 0 && c4 < HP4) {
           atomicAdd(&sq[c / S], q2);
           atomicAdd(&sg[c / S], wgq);
         }
-      } else if (c < HP) {
+      } else if (c4 < HP4) {
         atomicAdd(&sq[c / S], q2);
         atomicAdd(&sg[c / S], wgq);
       }
     }
     __syncthreads();
-    for (int c = tid; c < HP; c += kThreads) {
+#pragma unroll 4
+    for (int c4 = tid; c4 < HP4; c4 += kThreads) {
+      const int c = 4 * c4;
       const int64_t o = row * HP + c;
       const int j = c / S;
       const float r = rsqrtf(sq[j] / S + eps), k3 = r * r * r * sg[j] / S;
-      const float zz = to_f(z[o]), sig = 1.f / (1.f + __expf(-zz)), s = zz * sig;
-      const float yy = y[o], q = yy * s, gg = to_f(g[o]);
-      const float dq = to_f(w[c]) * r * gg - q * k3;
-      y[o] = dq * s;
-      dz[o] = from_f<T>(dq * yy * (sig + s * (1.f - sig)));
-      dwl[c] += gg * q * r;
+      const float4 zz = ld4(z + o), yy = ld4(y + o), ww = ld4(w + c), gg = ld4(g + o);
+      float zv[4] = {zz.x, zz.y, zz.z, zz.w}, yv[4] = {yy.x, yy.y, yy.z, yy.w};
+      float wv4[4] = {ww.x, ww.y, ww.z, ww.w}, gv[4] = {gg.x, gg.y, gg.z, gg.w};
+      float dy[4], dzv[4], dwv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sig = frcp(1.f + __expf(-zv[i])), sl = zv[i] * sig;
+        const float q = yv[i] * sl;
+        const float dq = wv4[i] * r * gv[i] - q * k3;
+        dy[i] = dq * sl;
+        dzv[i] = dq * yv[i] * (sig + sl * (1.f - sig));
+        dwv[i] = gv[i] * q * r;
+      }
+      st4(y + o, make_float4(dy[0], dy[1], dy[2], dy[3]));
+      st4(dz + o, make_float4(dzv[0], dzv[1], dzv[2], dzv[3]));
+      float4 acc = dwl[c4];
+      acc.x += dwv[0];
+      acc.y += dwv[1];
+      acc.z += dwv[2];
+      acc.w += dwv[3];
+      dwl[c4] = acc;
     }
     __syncthreads();
   }
-  for (int c = tid; c < HP; c += kThreads) dw_part[(int64_t)blockIdx.x * HP + c] = dwl[c];
+  for (int c4 = tid; c4 < HP4; c4 += kThreads)
+    st4(dw_part + (int64_t)blockIdx.x * HP + 4 * c4, dwl[c4]);
 }
 
-// dw[c] = sum over the parts of dw_part[.][c] (a fixed order: deterministic)
+// out[c] = sum over the parts of part[i * stride + c]. A workgroup takes 64
+// columns; its four waves sum the parts i = w mod 4 with four loads in
+// flight, then the four partial sums are added in a fixed order (the result
+// does not depend on timing).
 __global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict__ part,
-                                                        float* __restrict__ out, int nparts,
-                                                        int n) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
-  if (c >= n) return;
-  float acc = 0.f;
-  for (int i = 0; i < nparts; ++i) acc += part[(int64_t)i * n + c];
-  out[c] = acc;
+                                                        int64_t stride, float* __restrict__ out,
+                                                        int nparts, int n) {
+  __shared__ float red[4][64];
+  const int cl = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (c < n) {
+    int i = j;
+    for (; i + 12 < nparts; i += 16) {
+      a0 += part[(int64_t)i * stride + c];
+      a1 += part[(int64_t)(i + 4) * stride + c];
+      a2 += part[(int64_t)(i + 8) * stride + c];
+      a3 += part[(int64_t)(i + 12) * stride + c];
+    }
+    for (; i < nparts; i += 4) a0 += part[(int64_t)i * stride + c];
+  }
+  red[j][cl] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (j == 0 && c < n) out[c] = (red[0][cl] + red[1][cl]) + (red[2][cl] + red[3][cl]);
 }
 
 // ---------------------------------------------------------------- dS_in part
 // Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one (chunk, head), into zb.
-// Work items (16-row tile of p, up to 8 tiles of n) go round the waves;
-// operands come straight from the L2-resident rows.
+// The chunk's rows of exp(Lam_t) dY and of C are staged in LDS; work items
+// (16-row tile of p, up to 8 tiles of n) go round the waves.
 template <class T, int P>
 __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ v,
                                                       const float* __restrict__ dY,
                                                       const T* __restrict__ dt, DtA dta,
                                                       const float* __restrict__ A, float* zb,
                                                       int L, int H, int G, int N, int nc) {
+  extern __shared__ __align__(16) float sm[];
   __shared__ float lam[64], dts[64], ex[64];
-  constexpr int NPT = P / 16;
+  constexpr int NPT = P / 16, YP = P + 16;
+  const int CP = N + 16;
+  float* Ys = sm;            // [Q][YP]: exp(Lam_t) dY[t]
+  float* Cs = sm + kQ * YP;  // [Q][CP]
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
   const int t0 = c * kQ, len = min(kQ, L - t0);
@@ -276,21 +392,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
   const int HP = H * P;
   const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, co = HP + (int64_t)(G + g) * N;
   chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
+  stage_rows(Ys, YP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
+  stage_rows(Cs, CP, v + row0 * C + co, (int)C, kQ, len, N);
+  __syncthreads();
   float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   const int nnt = N / 16, nng = (nnt + 7) / 8;
+  const int kend = (len + 3) & ~3;
   for (int item = wave; item < NPT * nng; item += 4) {
     const int pt = item % NPT, nt0 = (item / NPT) * 8, ntn = min(8, nnt - nt0);
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = zero4();
-    for (int k0 = 0; k0 < len; k0 += 4) {
+    for (int k0 = 0; k0 < kend; k0 += 4) {
       const int t = k0 + lk;
-      const bool ok = t < len;
-      const float a = ok ? ex[t] * dY[(row0 + t) * HP + xo + pt * 16 + lr] : 0.f;
+      const float a = Ys[t * YP + pt * 16 + lr];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < ntn)
-          acc[j] = mma(a, ok ? v[(row0 + t) * C + co + (nt0 + j) * 16 + lr] : 0.f, acc[j]);
+        if (j < ntn) acc[j] = mma(a, Cs[t * CP + (nt0 + j) * 16 + lr], acc[j]);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -331,8 +449,9 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 //   intra-chunk:  sum_{t>=u} sum_{s<u} F[t,s] dt_s,  F = K o G o E
 //   state out:    exp(Lam_end) <dS_out, S_in> + sum_{s<u} w_s U_s
 //   inter-chunk:  sum_{t>=u} Y_t,  Y_t = exp(Lam_t) dY[t] . (C_t S_in^T)
-// where U_s = X[s] . (B_s dS_out^T). Wave w owns the 16-row tile w of s
-// (dX, dB) and of t (dC, C S_in^T).
+// where U_s = X[s] . (B_s dS_out^T) and Y_t = C_t . (exp(Lam_t) dY[t] S_in),
+// the latter from dC's inter-chunk part. Wave w owns the 16-row tile w of s
+// (dX, dB) and of t (dC).
 template <class T, int P>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
@@ -379,17 +498,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     float* Ys = SA + 2 * kQ * kSP;
     float* Xs = SA + 3 * kQ * kSP;
     const int kmax = N > P ? N : P;
+    SliceRegs<kQ> rc, rb, ry, rx;
+    auto fetch = [&](int k0) {
+      const int nvn = min(kKS, N - k0), nvp = min(kKS, P - k0);
+      rc.load(v + row0 * C + co + k0, (int)C, len, nvn);
+      rb.load(v + row0 * C + bo + k0, (int)C, len, nvn);
+      ry.load(dY + row0 * HP + xo + k0, HP, len, nvp);
+      rx.load(v + row0 * C + xo + k0, (int)C, len, nvp);
+    };
+    fetch(0);
     for (int k0 = 0; k0 < kmax; k0 += kKS) {
       const int nvn = min(kKS, N - k0), nvp = min(kKS, P - k0);
-      if (nvn > 0) {
-        stage(Cs, v + row0 * C + co + k0, C, kQ, len, nvn);
-        stage(Bs, v + row0 * C + bo + k0, C, kQ, len, nvn);
-      }
-      if (nvp > 0) {
-        stage(Ys, dY + row0 * HP + xo + k0, HP, kQ, len, nvp);
-        stage(Xs, v + row0 * C + xo + k0, C, kQ, len, nvp);
-      }
+      rc.store(Cs);
+      rb.store(Bs);
+      ry.store(Ys);
+      rx.store(Xs);
       __syncthreads();
+      if (k0 + kKS < kmax) fetch(k0 + kKS);
       for (int kk = 0; kk < nvn; kk += 4)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
@@ -449,21 +574,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     __syncthreads();
   }
 
-  // (3) dX intra: sum_{t >= s} M[t,s] dY[t,p]
-  f32x4 a1[NPT], a2[NPT], aY[NPT];
+  // (3) dX intra: sum_{t >= s} M[t,s] dY[t,p], the chunk's dY rows staged
+  f32x4 a1[NPT], a2[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) a1[i] = a2[i] = aY[i] = zero4();
-  for (int k0 = sw; k0 < kQ; k0 += 4) {
-    const int t = k0 + lk;
-    const float a = Mt[t * kQP + sw + lr];
-    const bool ok = t < len;
+  for (int i = 0; i < NPT; ++i) a1[i] = a2[i] = zero4();
+  {
+    constexpr int YP = P + 16;
+    float* Ys = SA;  // [Q][YP]
+    stage_rows(Ys, YP, dY + row0 * HP + xo, HP, kQ, len, P);
+    __syncthreads();
+    for (int k0 = sw; k0 < kQ; k0 += 4) {
+      const int t = k0 + lk;
+      const float a = Mt[t * kQP + sw + lr];
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-      a1[pt] = mma(a, ok ? dY[(row0 + t) * HP + xo + pt * 16 + lr] : 0.f, a1[pt]);
+      for (int pt = 0; pt < NPT; ++pt) a1[pt] = mma(a, Ys[t * YP + pt * 16 + lr], a1[pt]);
+    }
+    __syncthreads();
   }
 
-  // (4) over slices of n: B_s dS_out^T and C_t S_in^T of the wave's rows, and
-  // the slice's tiles of dC (rows t) and dB (rows s)
+  // (4) over slices of n: B_s dS_out^T of the wave's rows, and the slice's
+  // tiles of dC (rows t) and dB (rows s)
   float ya[KP], xa[KP];  // A fragments: dY and X of the wave's 16 rows
   {
     const int r = sw + lr;
@@ -475,29 +605,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     }
   }
   float cstp = 0.f;
+  float yp[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's share of Y_t, t = sw + 4 lk + r
   {
     float* Bs = SA;
     float* Cs = SA + kQ * kSP;
     float* Ss = SA + 2 * kQ * kSP;  // [P][kSP]
     float* Ds = Ss + P * kSP;       // [P][kSP]
+    SliceRegs<kQ> rb, rc;
+    SliceRegs<P> rs, rd;
+    auto fetch = [&](int n0) {
+      const int nv = min(kKS, N - n0);
+      rb.load(v + row0 * C + bo + n0, (int)C, len, nv);
+      rc.load(v + row0 * C + co + n0, (int)C, len, nv);
+      rs.load(Si + n0, N, P, nv);
+      rd.load(dS + n0, N, P, nv);
+    };
+    fetch(0);
     for (int n0 = 0; n0 < N; n0 += kKS) {
       const int nv = min(kKS, N - n0);
-      stage(Bs, v + row0 * C + bo + n0, C, kQ, len, nv);
-      stage(Cs, v + row0 * C + co + n0, C, kQ, len, nv);
-      stage(Ss, Si + n0, N, P, P, nv);
-      stage(Ds, dS + n0, N, P, P, nv);
+      rb.store(Bs);
+      rc.store(Cs);
+      rs.store(Ss);
+      rd.store(Ds);
       __syncthreads();
+      if (n0 + kKS < N) fetch(n0 + kKS);
       for (int i = tid; i < P * nv; i += kThreads) {
         const int p = i / nv, n = i % nv;
         cstp += Ss[p * kSP + n] * Ds[p * kSP + n];
       }
       for (int kk = 0; kk < nv; kk += 4) {
-        const float ab = Bs[(sw + lr) * kSP + kk + lk], ac = Cs[(sw + lr) * kSP + kk + lk];
+        const float ab = Bs[(sw + lr) * kSP + kk + lk];
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          a2[pt] = mma(ab, Ds[(pt * 16 + lr) * kSP + kk + lk], a2[pt]);
-          aY[pt] = mma(ac, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
-        }
+        for (int pt = 0; pt < NPT; ++pt) a2[pt] = mma(ab, Ds[(pt * 16 + lr) * kSP + kk + lk], a2[pt]);
       }
       for (int nt = 0; nt < nv / 16; ++nt) {
         f32x4 dc = zero4(), db = zero4();
@@ -508,8 +647,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          dc[r] *= ex[sw + 4 * lk + r];
-          db[r] *= wv[sw + 4 * lk + r];
+          const int t = sw + 4 * lk + r;
+          dc[r] *= ex[t];
+          db[r] *= wv[t];
+          // Y_t = sum_n C[t,n] (exp(Lam_t) dY[t] S_in)[n]: the inter part of dC
+          yp[r] += Cs[t * kSP + nt * 16 + lr] * dc[r];
         }
         for (int k0 = 0; k0 < sw + 16; k0 += 4)
           dc = mma(Dg[(sw + lr) * kQP + k0 + lk], Bs[(k0 + lk) * kSP + nt * 16 + lr], dc);
@@ -531,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
 
   // (5) dX, and the row sums U_s, Y_t; dD and <dS_out, S_in>
   {
-    float up[4] = {0.f, 0.f, 0.f, 0.f}, yp[4] = {0.f, 0.f, 0.f, 0.f}, ddp = 0.f;
+    float up[4] = {0.f, 0.f, 0.f, 0.f}, ddp = 0.f;
 #pragma unroll
     for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
@@ -541,7 +683,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
           const float xv = v[(row0 + s) * C + xo + p], dys = dY[(row0 + s) * HP + xo + p];
           dv[(row0 + s) * C + xo + p] = a1[pt][r] + wv[s] * a2[pt][r] + Dh * dys;
           up[r] += xv * a2[pt][r];
-          yp[r] += dys * aY[pt][r];
           ddp += dys * xv;
         }
       }
@@ -555,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
       for (int r = 0; r < 4; ++r) {
         const int s = sw + 4 * lk + r;
         U[s] = up[r];
-        Yo[s] = ex[s] * yp[r];
+        Yo[s] = yp[r];
       }
     cstp = wave_sum(cstp);
     ddp = wave_sum(ddp);
@@ -609,66 +750,87 @@ __global__ __launch_bounds__(kThreads) void k_group_sum(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- conv + SiLU
-// du = dv silu'(u) over a range of kConvTok tokens of one channel (u
-// recomputed from [conv state ; xbc]); du overwrites dv; dw, db summed.
+// du = dv silu'(u) over a range of kConvTok tokens of one channel, u
+// recomputed from the rows ext = [conv state ; xbc] through a sliding window;
+// du overwrites dv. The range's sums for the weight and bias gradients go to
+// its row of part: part[range][c * W + k] and part[range][C * W + c].
 constexpr int kConvTok = 64;
-template <class T>
+template <class T, int W>
 __global__ __launch_bounds__(kThreads) void k_conv_du(const T* __restrict__ xbc,
                                                       const T* __restrict__ cin,
                                                       const T* __restrict__ w,
                                                       const T* __restrict__ bias, float* dv,
-                                                      float* dw, float* db, int L, int C, int W) {
+                                                      float* part, int L, int C) {
   const int c = blockIdx.x * kThreads + threadIdx.x;
   const int t0 = blockIdx.y * kConvTok, b = blockIdx.z;
   if (c >= C) return;
-  float wk[4] = {0.f, 0.f, 0.f, 0.f}, dwp[4] = {0.f, 0.f, 0.f, 0.f}, dbp = 0.f;
-  for (int k = 0; k < W; ++k) wk[k] = to_f(w[(int64_t)c * W + k]);
+  float wk[W], dwp[W], win[W], dbp = 0.f;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    wk[k] = to_f(w[(int64_t)c * W + k]);
+    dwp[k] = 0.f;
+  }
   const float bc = bias ? to_f(bias[c]) : 0.f;
   // ext row e: conv state rows (e < W-1) or token e - (W-1)
   auto ext = [&](int e) -> float {
     if (e >= W - 1) return to_f(xbc[((int64_t)b * L + e - (W - 1)) * C + c]);
     return cin ? to_f(cin[((int64_t)b * (W - 1) + e) * C + c]) : 0.f;
   };
-  for (int t = t0; t < min(L, t0 + kConvTok); ++t) {
-    float e[4];
+#pragma unroll
+  for (int k = 0; k < W - 1; ++k) win[k] = ext(t0 + k);
+  const int t1 = min(L, t0 + kConvTok);
+  for (int t = t0; t < t1; ++t) {
+    win[W - 1] = ext(t + W - 1);
     float u = bc;
-    for (int k = 0; k < W; ++k) {
-      e[k] = ext(t + k);
-      u += wk[k] * e[k];
-    }
-    const float sig = 1.f / (1.f + __expf(-u));
+#pragma unroll
+    for (int k = 0; k < W; ++k) u += wk[k] * win[k];
+    const float sig = frcp(1.f + __expf(-u));
     const int64_t o = ((int64_t)b * L + t) * C + c;
     const float du = dv[o] * (sig + u * sig * (1.f - sig));
     dv[o] = du;
-    for (int k = 0; k < W; ++k) dwp[k] += du * e[k];
+#pragma unroll
+    for (int k = 0; k < W; ++k) dwp[k] += du * win[k];
     dbp += du;
+#pragma unroll
+    for (int k = 0; k < W - 1; ++k) win[k] = win[k + 1];
   }
-  for (int k = 0; k < W; ++k) atomicAdd(dw + (int64_t)c * W + k, dwp[k]);
-  if (db) atomicAdd(db + c, dbp);
+  float* pr = part + ((int64_t)b * gridDim.y + blockIdx.y) * ((int64_t)C * (W + 1));
+#pragma unroll
+  for (int k = 0; k < W; ++k) pr[(int64_t)c * W + k] = dwp[k];
+  pr[(int64_t)C * W + c] = dbp;
 }
 
 // Gradient of the conv input rows ext = [conv state ; xbc]: d_ext[e] =
-// sum_k w[k] du[e - k] over output tokens e - k in range; rows e >= W-1 go to
-// d_xbc, the first W-1 to the initial conv state's gradient (fp32).
-template <class T>
+// sum_k w[k] du[e - k] over output tokens e - k in range (a sliding window
+// over du); rows e >= W-1 go to d_xbc, the first W-1 to the initial conv
+// state's gradient (fp32).
+template <class T, int W>
 __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ du,
                                                       const T* __restrict__ w, T* __restrict__ dx,
-                                                      float* dcin, int L, int C, int W) {
+                                                      float* dcin, int L, int C) {
   const int c = blockIdx.x * kThreads + threadIdx.x;
   const int e0 = blockIdx.y * kConvTok, b = blockIdx.z;
   if (c >= C) return;
-  float wk[4] = {0.f, 0.f, 0.f, 0.f};
+  float wk[W], win[W];  // win[k] = du[e - k]
+#pragma unroll
   for (int k = 0; k < W; ++k) wk[k] = to_f(w[(int64_t)c * W + k]);
-  for (int e = e0; e < min(L + W - 1, e0 + kConvTok); ++e) {
+  auto dut = [&](int tt) -> float {
+    return (tt >= 0 && tt < L) ? du[((int64_t)b * L + tt) * C + c] : 0.f;
+  };
+#pragma unroll
+  for (int k = 1; k < W; ++k) win[k] = dut(e0 - k);
+  const int e1 = min(L + W - 1, e0 + kConvTok);
+  for (int e = e0; e < e1; ++e) {
+    win[0] = dut(e);
     float acc = 0.f;
-    for (int k = 0; k < W; ++k) {
-      const int tt = e - k;  // output token whose window puts tap k on row e
-      if (tt >= 0 && tt < L) acc += wk[k] * du[((int64_t)b * L + tt) * C + c];
-    }
+#pragma unroll
+    for (int k = 0; k < W; ++k) acc += wk[k] * win[k];
     if (e >= W - 1)
       dx[((int64_t)b * L + e - (W - 1)) * C + c] = from_f<T>(acc);
     else if (dcin)
       dcin[((int64_t)b * (W - 1) + e) * C + c] = acc;
+#pragma unroll
+    for (int k = W - 1; k > 0; --k) win[k] = win[k - 1];
   }
 }
 
@@ -680,15 +842,21 @@ __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ 
 namespace {
 size_t bround(size_t b) { return (b + 255) / 256 * 256; }
 
-// LDS of the per-chunk kernels (the y recompute and the chunk gradients)
+// LDS of the per-chunk kernels (the y recompute, the chunk gradients and
+// the state-gradient terms)
 size_t bwd_y_lds(int P) {
-  return ((size_t)bwd::kQ * bwd::kQP + 2 * bwd::kQ * bwd::kSP + (size_t)P * bwd::kSP) * 4;
+  const size_t slices = 2 * (size_t)bwd::kQ * bwd::kSP + (size_t)P * bwd::kSP,
+               xrows = (size_t)bwd::kQ * (P + 16);
+  return ((size_t)bwd::kQ * bwd::kQP + std::max(slices, xrows)) * 4;
 }
 size_t bwd_chunk_lds(int P) {
   const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP, fm = (size_t)bwd::kQ * (bwd::kQ + 1),
+               ys = (size_t)bwd::kQ * (P + 16),
                stage4 = 2 * (size_t)bwd::kQ * bwd::kSP + 2 * (size_t)P * bwd::kSP;
-  return (2 * (size_t)bwd::kQ * bwd::kQP + std::max(stage1, std::max(fm, stage4))) * 4;
+  return (2 * (size_t)bwd::kQ * bwd::kQP + std::max(std::max(stage1, fm), std::max(ys, stage4))) *
+         4;
 }
+size_t bwd_z_lds(int P, int N) { return (size_t)bwd::kQ * ((P + 16) + (N + 16)) * 4; }
 }  // namespace
 
 size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {
@@ -696,7 +864,8 @@ size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {
   const size_t nc = (L + bwd::kQ - 1) / bwd::kQ;
   const size_t st = (size_t)B * nc * H * P * N * 4;
   return bround(T * C * 4) + bround(T * HP * 4) + 2 * bround(st) + bround((size_t)B * H * nc * 4) +
-         2 * bround(T * H * N * 4) + bround(T * C * 4) + bround((size_t)bwd::kNormBlocks * HP * 4);
+         2 * bround(T * H * N * 4) + bround(T * C * 4) + bround((size_t)bwd::kNormBlocks * HP * 4) +
+         bround((size_t)B * ((L + bwd::kConvTok - 1) / bwd::kConvTok) * C * 5 * 4);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
@@ -724,6 +893,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   float* dv = (float*)w;
   w += bround(T * C * 4);
   float* dw_part = (float*)w;
+  w += bround((size_t)kNormBlocks * HP * 4);
+  float* conv_part = (float*)w;  // [B * ranges][Cch * (W + 1)]
   const DtA plain{H, nullptr};
   const dim3 gc(nc, H, B), blk(kThreads);
   hipError_t e;
@@ -771,8 +942,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   };
   zero(a.d_A, H);
   zero(a.d_D, H);
-  zero(a.d_conv_w, C * W);
-  zero(a.d_conv_b, C);
   SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_NORM);
@@ -787,18 +956,19 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(k_norm_bwd<float>, dim3(nb), blk, lds, st, y, (const float*)a.z,
                          (const float*)a.norm_w, (const float*)a.d_out, a.eps, (float*)a.d_z,
                          dw_part, T, rows, (int)HP, G);
-    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((HP + kThreads - 1) / kThreads)), blk, 0, st,
-                       dw_part, a.d_norm_w, nb, (int)HP);
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((HP + 63) / 64)), blk, 0, st, dw_part, HP,
+                       a.d_norm_w, nb, (int)HP);
   }
   SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_CHUNK_Z);
+    const size_t zl = bwd_z_lds(P, N);
 #define SSD_Z(PP)                                                                                \
   if (bf)                                                                                        \
-    hipLaunchKernelGGL((k_chunk_z<bf16, PP>), gc, blk, 0, st, v, y, (const bf16*)a.dt, plain,    \
+    hipLaunchKernelGGL((k_chunk_z<bf16, PP>), gc, blk, zl, st, v, y, (const bf16*)a.dt, plain,   \
                        a.A, dso, L, H, G, N, nc);                                                \
   else                                                                                           \
-    hipLaunchKernelGGL((k_chunk_z<float, PP>), gc, blk, 0, st, v, y, (const float*)a.dt, plain,  \
+    hipLaunchKernelGGL((k_chunk_z<float, PP>), gc, blk, zl, st, v, y, (const float*)a.dt, plain, \
                        a.A, dso, L, H, G, N, nc)
     SSD_BY_P(SSD_Z)
 #undef SSD_Z
@@ -834,27 +1004,37 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_CONV_DU);
-    const dim3 gd((unsigned)((C + kThreads - 1) / kThreads), (L + kConvTok - 1) / kConvTok, B);
-    if (bf)
-      hipLaunchKernelGGL(k_conv_du<bf16>, gd, blk, 0, st, (const bf16*)a.xbc,
-                         (const bf16*)a.conv_in, (const bf16*)a.conv_w, (const bf16*)a.conv_b, dv,
-                         a.d_conv_w, a.d_conv_b, L, (int)C, W);
-    else
-      hipLaunchKernelGGL(k_conv_du<float>, gd, blk, 0, st, (const float*)a.xbc,
-                         (const float*)a.conv_in, (const float*)a.conv_w, (const float*)a.conv_b,
-                         dv, a.d_conv_w, a.d_conv_b, L, (int)C, W);
+    const int ny = (L + kConvTok - 1) / kConvTok;
+    const dim3 gd((unsigned)((C + kThreads - 1) / kThreads), ny, B);
+#define SSD_DU(TT, WW)                                                                       \
+  hipLaunchKernelGGL((k_conv_du<TT, WW>), gd, blk, 0, st, (const TT*)a.xbc,                  \
+                     (const TT*)a.conv_in, (const TT*)a.conv_w, (const TT*)a.conv_b, dv,     \
+                     conv_part, L, (int)C)
+#define SSD_DU_W(TT) \
+  if (W == 2) SSD_DU(TT, 2); else if (W == 3) SSD_DU(TT, 3); else SSD_DU(TT, 4)
+    if (bf) { SSD_DU_W(bf16); } else { SSD_DU_W(float); }
+#undef SSD_DU_W
+#undef SSD_DU
+    const int64_t pst = C * (W + 1);
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((C * W + 63) / 64)), blk, 0, st, conv_part,
+                       pst, a.d_conv_w, B * ny, (int)(C * W));
+    if (a.d_conv_b)
+      hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((C + 63) / 64)), blk, 0, st,
+                         conv_part + C * W, pst, a.d_conv_b, B * ny, (int)C);
   }
   SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_CONV_DX);
     const dim3 gx((unsigned)((C + kThreads - 1) / kThreads),
                   (L + W - 1 + kConvTok - 1) / kConvTok, B);
-    if (bf)
-      hipLaunchKernelGGL(k_conv_dx<bf16>, gx, blk, 0, st, dv, (const bf16*)a.conv_w,
-                         (bf16*)a.d_xbc, a.d_conv_in, L, (int)C, W);
-    else
-      hipLaunchKernelGGL(k_conv_dx<float>, gx, blk, 0, st, dv, (const float*)a.conv_w,
-                         (float*)a.d_xbc, a.d_conv_in, L, (int)C, W);
+#define SSD_DX(TT, WW)                                                                         \
+  hipLaunchKernelGGL((k_conv_dx<TT, WW>), gx, blk, 0, st, dv, (const TT*)a.conv_w,             \
+                     (TT*)a.d_xbc, a.d_conv_in, L, (int)C)
+#define SSD_DX_W(TT) \
+  if (W == 2) SSD_DX(TT, 2); else if (W == 3) SSD_DX(TT, 3); else SSD_DX(TT, 4)
+    if (bf) { SSD_DX_W(bf16); } else { SSD_DX_W(float); }
+#undef SSD_DX_W
+#undef SSD_DX
   }
   SSD_CHECK();
 #undef SSD_BY_P

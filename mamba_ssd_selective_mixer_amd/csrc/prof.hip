@@ -24,6 +24,7 @@ struct Slot {
 };
 
 std::mutex g_mu;
+uint64_t g_mask = ~0ull;     // kernels timed: bit k for kernel id k
 std::vector<Slot> g_slots;   // the pool; events created once per start
 size_t g_used = 0;           // slots taken since start
 int g_open[KID_COUNT];       // slot index of the currently open bracket per kernel, or -1
@@ -51,6 +52,7 @@ void release() {
 void prof_record(hipStream_t st, int kid, bool begin) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_prof_on.load(std::memory_order_relaxed) || kid < 0 || kid >= KID_COUNT) return;
+  if (!((g_mask >> kid) & 1)) return;
   if (begin) {
     if (g_used >= g_slots.size()) {
       g_overflow = true;
@@ -122,6 +124,13 @@ int ssd_profile_read(int kernel, int64_t* launches, double* total_ms) {
   *launches = n;
   *total_ms = ms;
   return SSD_OK;
+}
+
+uint64_t ssd_profile_set_mask(uint64_t mask) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  const uint64_t old = g_mask;
+  g_mask = mask;
+  return old;
 }
 
 const char* ssd_kernel_name(int kernel) {

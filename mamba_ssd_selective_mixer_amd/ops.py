@@ -563,6 +563,12 @@ def profile_stop() -> None:
     _check(_lib.load().ssd_profile_stop(), "ssd_profile_stop")
 
 
+def profile_only(kernels=None) -> None:
+    """Time only the named kernels from now on (None: every kernel)."""
+    mask = (1 << 64) - 1 if kernels is None else sum(1 << _lib.KERNELS.index(k) for k in kernels)
+    _lib.load().ssd_profile_set_mask(mask)
+
+
 def profile_read(kernel: str) -> tuple[int, float]:
     """(timed launches, summed milliseconds) of one kernel since profile_start."""
     n = ctypes.c_int64(0)

@@ -215,6 +215,9 @@ def test_kernel_names_and_profile_arguments(lib):
     assert lib.ssd_profile_read(0, None, ctypes.byref(ms)) == -1
     assert lib.ssd_profile_read(0, ctypes.byref(n), ctypes.byref(ms)) == 0 and n.value == 0
     assert lib.ssd_profile_start(0) == -2
+    # the kernel mask: all kernels timed by default, the previous mask returned
+    assert lib.ssd_profile_set_mask(5) == 2 ** 64 - 1
+    assert lib.ssd_profile_set_mask(2 ** 64 - 1) == 5
 
 
 # Every buffer a call writes against every other buffer it touches: placed
@@ -446,8 +449,9 @@ def test_backward_refuses_before_launch(lib):
     d = dims(synth.CONFIGS["c1"])
     need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
     # workspace: the status word, fp32 conv output / its gradient, y, chunk
-    # states and their gradients (64-token chunks), per-head dB / dC, and
-    # 512 partial norm-weight gradients
+    # states and their gradients (64-token chunks), per-head dB / dC, 1024
+    # partial norm-weight gradients and the conv gradients' partial sums per
+    # 64-token range
     cfg = synth.CONFIGS["c1"]
     T, C, HP = cfg.batch * cfg.seqlen, cfg.channels, cfg.hp
     nc = -(-cfg.seqlen // 64)
@@ -455,7 +459,7 @@ def test_backward_refuses_before_launch(lib):
     r = lambda b: -(-b // 256) * 256
     assert need == (256 + 2 * r(T * C * 4) + r(T * HP * 4) + 2 * r(st)
                     + r(cfg.batch * cfg.nheads * nc * 4) + 2 * r(T * cfg.nheads * cfg.dstate * 4)
-                    + r(512 * HP * 4))
+                    + r(1024 * HP * 4) + r(cfg.batch * nc * C * 5 * 4))
     base = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
     for k in ("xbc", "z", "dt", "A", "cw", "nw", "d_out", "g_xbc", "g_z", "g_dt", "g_A", "g_cw",
               "g_nw", "ws"):

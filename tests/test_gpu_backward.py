@@ -98,6 +98,11 @@ CASES = [
     ("f32_w3", dict(batch=1, seqlen=97, conv_width=3, nheads=8, ngroups=4), {}),
     ("f32_layer_shape", dict(batch=1, seqlen=160, nheads=8, headdim=64, ngroups=2, dstate=128),
      {}),
+    # the widest head and state: head_dim 128 with state 256, and with state 16
+    ("f32_p128_n256", dict(batch=1, seqlen=100, nheads=4, headdim=128, ngroups=2, dstate=256),
+     {}),
+    ("f32_p128_n16", dict(batch=2, seqlen=70, nheads=4, headdim=128, ngroups=1, dstate=16),
+     dict(with_bias=False)),
 ]
 
 
