@@ -10,6 +10,9 @@
 // The state stream dominates: each lane owns 4 consecutive n of a row, so a
 // wave reads and writes 1 KiB contiguous per instruction; the row sums over
 // n are butterfly reductions inside aligned groups of N/4 lanes.
+// VAR: the one-token sequences of a ragged batch (continuous batching):
+// workgroup (g, j) takes the j-th listed sequence, its token row from the
+// offsets and its states from its pool slot (zeros when it starts fresh).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,17 +22,32 @@ constexpr int kDecThreads = 256;
 constexpr int kDecUnroll = 8;  // state float4 loads kept in flight per lane
 
 
-template <class T, int N, int W>
+template <class T, int N, int W, bool VAR>
 __global__ __launch_bounds__(kDecThreads) void k_decode(
     const T* __restrict__ xbc, const T* __restrict__ z, const T* __restrict__ dt,
     const float* __restrict__ A, const float* __restrict__ D, const T* __restrict__ cw,
     const T* __restrict__ cb, const T* __restrict__ nw, float eps, T* __restrict__ conv_state,
     float* __restrict__ ssm, T* __restrict__ y, int64_t xrs, int64_t zrs, DtA dta, int H, int P,
-    int G, float inv_S) {
+    int G, float inv_S, Seqs q, const int32_t* __restrict__ dec) {
   extern __shared__ __align__(16) float sm[];
-  const int g = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x;
   const int hpg = H / G, S = hpg * P;
   const int HP = H * P, GN = G * N, C = HP + 2 * GN;
+  // this workgroup's token row and states
+  int64_t row = blockIdx.y;
+  T* cst = conv_state + row * (W - 1) * C;
+  float* ssm_b = ssm + row * H * (int64_t)(P * N);
+  bool fresh = false;
+  if constexpr (VAR) {
+    if (__builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
+    const int j = blockIdx.y;
+    if (j >= dec[gridDim.y]) return;
+    const int i = dec[j], slot = q.slots[i];
+    row = q.cu[i];
+    cst = (T*)q.conv_pool + (int64_t)slot * (W - 1) * C;
+    ssm_b = q.ssm_pool + (int64_t)slot * H * (int64_t)(P * N);
+    fresh = q.has_state && !q.has_state[i];
+  }
   float* xs = sm;          // [S] post-conv x of the group's heads
   float* Bs = xs + S;      // [N]
   float* Cs = Bs + N;      // [N]
@@ -47,10 +65,17 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
     else if (o < S + N) { c0 = HP + g * N + (o - S); dst = Bs + (o - S); }
     else { c0 = HP + GN + g * N + (o - S - N); dst = Cs + (o - S - N); }
     float win[W][8];
-    T* cs = conv_state + (int64_t)b * (W - 1) * C + c0;
+    T* cs = cst + c0;
 #pragma unroll
-    for (int r = 0; r < W - 1; ++r) load8(cs + (int64_t)r * C, win[r]);
-    load8(xbc + (int64_t)b * xrs + c0, win[W - 1]);
+    for (int r = 0; r < W - 1; ++r) {
+      if (fresh) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) win[r][j] = 0.f;
+      } else {
+        load8(cs + (int64_t)r * C, win[r]);
+      }
+    }
+    load8(xbc + row * xrs + c0, win[W - 1]);
 #pragma unroll
     for (int r = 0; r < W - 1; ++r) store8(cs + (int64_t)r * C, win[r + 1]);
     float wv[W][8];
@@ -77,7 +102,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   const float4 Bv = *reinterpret_cast<const float4*>(Bs + n0);
   const float4 Cv = *reinterpret_cast<const float4*>(Cs + n0);
   const int iters = (PN + 4 * kDecThreads - 1) / (4 * kDecThreads);
-  float* sb = ssm + ((int64_t)b * H + (int64_t)g * hpg) * PN;  // the group's heads
+  float* sb = ssm_b + (int64_t)g * hpg * PN;  // the group's heads
   if (iters <= kDecUnroll) {
     f32x4 cur[kDecUnroll];
     auto load_head = [&](int hl, f32x4 (&dst)[kDecUnroll]) {
@@ -86,7 +111,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
       for (int u = 0; u < kDecUnroll; ++u) {
         const int e = 4 * tid + u * 4 * kDecThreads;
         if (u < iters && e < PN) {
-          dst[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
+          dst[u] = fresh ? zero4()
+                         : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
         }
       }
     };
@@ -95,7 +121,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
       f32x4 nxt[kDecUnroll];
       if (hl + 1 < hpg) load_head(hl + 1, nxt);
       const int h = g * hpg + hl;
-      const float dtv = dt_of(to_f(dt[(int64_t)b * dta.dts + h]), dta, h);
+      const float dtv = dt_of(to_f(dt[row * dta.dts + h]), dta, h);
       const float al = fexp(dtv * a_of(A, dta, h));
       const float Dh = D ? D[h] : 0.f;
       float* st = sb + (int64_t)hl * PN;
@@ -123,17 +149,18 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   } else {
     for (int hl = 0; hl < hpg; ++hl) {
       const int h = g * hpg + hl;
-      const float dtv = dt_of(to_f(dt[(int64_t)b * dta.dts + h]), dta, h);
+      const float dtv = dt_of(to_f(dt[row * dta.dts + h]), dta, h);
       const float al = fexp(dtv * a_of(A, dta, h));
       const float Dh = D ? D[h] : 0.f;
-      float* st = ssm + ((int64_t)b * H + h) * PN;
+      float* st = ssm_b + (int64_t)h * PN;
       for (int i0 = 0; i0 < iters; i0 += kDecUnroll) {
         f32x4 s[kDecUnroll];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
           const int e = 4 * tid + (i0 + u) * 4 * kDecThreads;
           if (i0 + u < iters && e < PN)
-            s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
+            s[u] = fresh ? zero4()
+                         : __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st + e));
         }
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
@@ -159,9 +186,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   __syncthreads();
 
   // 3. gated RMSNorm over the group's S channels (or the plain output).
-  T* yo = y + (int64_t)b * HP + (int64_t)g * S;
+  T* yo = y + row * HP + (int64_t)g * S;
   if (z) {
-    const T* zz = z + (int64_t)b * zrs + (int64_t)g * S;
+    const T* zz = z + row * zrs + (int64_t)g * S;
     float ss = 0.f;
     for (int i = tid; i < S; i += kDecThreads) {
       const float q = ys[i] * silu(to_f(zz[i]));
@@ -181,20 +208,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(
   }
 }
 
-template <class T>
+template <class T, bool VAR>
 static hipError_t decode_dispatch(int B, int H, int P, int G, int N, int W, const void* xbc,
                                   int64_t xrs, const void* z, int64_t zrs, const void* dt,
                                   const DtA& dta, const float* A, const float* D, const void* cw,
                                   const void* cb, const void* nw, float eps, void* conv_state,
-                                  float* ssm, void* y, hipStream_t st) {
+                                  float* ssm, void* y, const Seqs& q, const int32_t* dec,
+                                  hipStream_t st) {
   const int S = H / G * P;
   const size_t lds = (size_t)(2 * S + 2 * N) * sizeof(float);
   dim3 grid(G, B), block(kDecThreads);
   const float inv_S = 1.0f / (float)S;
 #define SSD_DEC(NN, WW)                                                                          \
-  hipLaunchKernelGGL((k_decode<T, NN, WW>), grid, block, lds, st, (const T*)xbc, (const T*)z,    \
-                     (const T*)dt, A, D, (const T*)cw, (const T*)cb, (const T*)nw, eps,          \
-                     (T*)conv_state, ssm, (T*)y, xrs, zrs, dta, H, P, G, inv_S)
+  hipLaunchKernelGGL((k_decode<T, NN, WW, VAR>), grid, block, lds, st, (const T*)xbc,          \
+                     (const T*)z, (const T*)dt, A, D, (const T*)cw, (const T*)cb, (const T*)nw,  \
+                     eps, (T*)conv_state, ssm, (T*)y, xrs, zrs, dta, H, P, G, inv_S, q, dec)
 #define SSD_DEC_W(NN)                     \
   switch (W) {                            \
     case 2: SSD_DEC(NN, 2); break;        \
@@ -219,10 +247,29 @@ hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
                          const void* cw, const void* cb, const void* nw, float eps,
                          void* conv_state, float* ssm_state, void* y, hipStream_t st) {
   ProfScope ps(st, KID_DECODE);
-  return io_bf16 ? decode_dispatch<bf16>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A, D, cw,
-                                         cb, nw, eps, conv_state, ssm_state, y, st)
-                 : decode_dispatch<float>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A, D, cw,
-                                          cb, nw, eps, conv_state, ssm_state, y, st);
+  const Seqs none{};
+  return io_bf16 ? decode_dispatch<bf16, false>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A,
+                                                D, cw, cb, nw, eps, conv_state, ssm_state, y,
+                                                none, nullptr, st)
+                 : decode_dispatch<float, false>(B, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta, A,
+                                                 D, cw, cb, nw, eps, conv_state, ssm_state, y,
+                                                 none, nullptr, st);
+}
+
+hipError_t launch_decode_varlen(bool io_bf16, int nseq, int H, int P, int G, int N, int W,
+                                const void* xbc, int64_t xrs, const void* z, int64_t zrs,
+                                const void* dt, const DtA& dta, const float* A, const float* D,
+                                const void* cw, const void* cb, const void* nw, float eps,
+                                const Seqs& q, const int32_t* dec, void* y, hipStream_t st) {
+  ProfScope ps(st, KID_DECODE);
+  // a workgroup per (group, listed sequence); those past the list's count
+  // return at once
+  return io_bf16 ? decode_dispatch<bf16, true>(nseq, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta,
+                                               A, D, cw, cb, nw, eps, nullptr, nullptr, y, q,
+                                               dec, st)
+                 : decode_dispatch<float, true>(nseq, H, P, G, N, W, xbc, xrs, z, zrs, dt, dta,
+                                                A, D, cw, cb, nw, eps, nullptr, nullptr, y, q,
+                                                dec, st);
 }
 
 }  // namespace ssd

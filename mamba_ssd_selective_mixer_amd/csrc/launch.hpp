@@ -105,6 +105,14 @@ size_t fast_varlen_ws_bytes(int nseq, int T, int H, int G, int num_slots);
 // most 4-head blocks per norm group the fused exchange handles
 int fast_max_norm_heads();
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st);
+// The one-token sequences of a ragged batch, one decode step each: dec lists
+// them (dec[nseq] holds their count); token rows from q.cu, states in the
+// pool slots (zeros for a fresh sequence); skipped when q.valid is not 1.
+hipError_t launch_decode_varlen(bool io_bf16, int nseq, int H, int P, int G, int N, int W,
+                                const void* xbc, int64_t xrs, const void* z, int64_t zrs,
+                                const void* dt, const DtA& dta, const float* A, const float* D,
+                                const void* cw, const void* cb, const void* nw, float eps,
+                                const Seqs& q, const int32_t* dec, void* y, hipStream_t st);
 
 }  // namespace ssd
 

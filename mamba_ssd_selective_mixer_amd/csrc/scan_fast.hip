@@ -587,7 +587,8 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     sout_p = s_out ? s_out + bh * PN : nullptr;
   } else {
     if (__builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
-    if (q.cu[b + 1] - q.cu[b] <= 0) return;  // no tokens: the slot is left as it is
+    // no tokens: the slot is left as it is; one token: the decode kernel's
+    if (q.cu[b + 1] - q.cu[b] <= 1) return;
     k0 = q.chunk_first[b];
     nc = q.chunk_first[b + 1] - q.chunk_first[b];
     float* slot = q.ssm_pool + ((int64_t)q.slots[b] * H + h) * PN;
@@ -1222,7 +1223,7 @@ bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 // chunk table and a bitmap of the pool's slots.
 struct FastLayout {
   int64_t chunks, npart;
-  size_t dS, lam, part, sync, bcv, ccv, valid, first, cseq, bitmap, total;
+  size_t dS, lam, part, sync, bcv, ccv, valid, first, cseq, bitmap, dec, total;
 };
 FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int num_slots) {
   using namespace fast;
@@ -1252,6 +1253,7 @@ FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int n
     f.first = take(((size_t)B + 1) * 4);
     f.cseq = take((size_t)f.chunks * 4);
     f.bitmap = take(((size_t)num_slots + 31) / 32 * 4);
+    f.dec = take(((size_t)B + 1) * 4);  // one-token sequences, then their count
   }
   f.total = off;
   return f;
@@ -1279,9 +1281,9 @@ constexpr int kStatusVarlen = 4;  // status bit: the ragged batch's metadata is 
 __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int nseq, int T,
     int num_slots, int32_t* chunk_first, int32_t* chunk_seq, int64_t max_chunks,
-    uint32_t* bitmap, int* valid, int* status) {
+    uint32_t* bitmap, int32_t* dec, int* valid, int* status) {
   __shared__ int bad;
-  __shared__ int csum[kTableThreads];
+  __shared__ int csum[kTableThreads], dsum[kTableThreads];
   const int tid = threadIdx.x;
   if (tid == 0) {
     bad = 0;
@@ -1294,7 +1296,7 @@ __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
   // thread tid takes sequences [i0, i1)
   const int per = (nseq + kTableThreads - 1) / kTableThreads;
   const int i0 = min(nseq, tid * per), i1 = min(nseq, i0 + per);
-  int cnt = 0, err = 0;
+  int cnt = 0, dcnt = 0, err = 0;
   if (tid == 0 && (cu[0] != 0 || cu[nseq] != T)) err = 1;
   for (int i = i0; i < i1; ++i) {
     const int len = cu[i + 1] - cu[i];
@@ -1310,29 +1312,38 @@ __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
     }
     const uint32_t bit = 1u << (sl & 31);
     if (atomicOr(bitmap + (sl >> 5), bit) & bit) err = 1;  // slot used twice
-    cnt += (len + QI - 1) / QI;
+    if (len == 1)
+      ++dcnt;  // a decode step: the decode kernel takes it, it gets no chunk
+    else
+      cnt += (len + QI - 1) / QI;
   }
   if (err) atomicOr(&bad, 1);
-  // exclusive scan of the per-thread chunk counts
+  // exclusive scans of the per-thread chunk and decode-step counts
   csum[tid] = cnt;
+  dsum[tid] = dcnt;
   __syncthreads();
   for (int d = 1; d < kTableThreads; d <<= 1) {
-    const int v = tid >= d ? csum[tid - d] : 0;
+    const int v = tid >= d ? csum[tid - d] : 0, w = tid >= d ? dsum[tid - d] : 0;
     __syncthreads();
     csum[tid] += v;
+    dsum[tid] += w;
     __syncthreads();
   }
-  int base = csum[tid] - cnt;
+  int base = csum[tid] - cnt, dbase = dsum[tid] - dcnt;
   const int total = csum[kTableThreads - 1];
   for (int i = i0; i < i1; ++i) {
     chunk_first[i] = base;
     const int len = cu[i + 1] - cu[i];
-    const int n = len > 0 ? (len + QI - 1) / QI : 0;
+    const int n = len > 1 ? (len + QI - 1) / QI : 0;
     for (int j = 0; j < n; ++j)  // bounded: garbage offsets only make the call invalid
       if (base + j >= 0 && base + j < max_chunks) chunk_seq[base + j] = i;
     base += n;
+    if (len == 1) dec[dbase++] = i;
   }
-  if (tid == 0) chunk_first[nseq] = total;
+  if (tid == 0) {
+    chunk_first[nseq] = total;
+    dec[nseq] = dsum[kTableThreads - 1];
+  }
   for (int64_t k = max(total, 0) + tid; k < max_chunks; k += kTableThreads) chunk_seq[k] = -1;
   __syncthreads();
   if (tid == 0) {
@@ -1355,7 +1366,7 @@ __global__ __launch_bounds__(256) void k_varlen_conv_state(const bf16* __restric
   const int b = blockIdx.y;
   if (cv * 8 >= C || __builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
   const int a = q.cu[b], L = q.cu[b + 1] - a;
-  if (L <= 0) return;
+  if (L <= 1) return;  // none, or a decode step (the decode kernel shifts it)
   bf16* slot = (bf16*)q.conv_pool + (int64_t)q.slots[b] * (W - 1) * C + cv * 8;
   const bool resume = !q.has_state || q.has_state[b];
 #pragma unroll
@@ -1402,7 +1413,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     q.chunk_seq = (const int32_t*)(w + f.cseq);
     hipLaunchKernelGGL(k_varlen_table, dim3(1), dim3(kTableThreads), 0, st, a.q.cu, a.q.slots,
                        a.B, a.L, a.num_slots, (int32_t*)(w + f.first), (int32_t*)(w + f.cseq),
-                       f.chunks, (uint32_t*)(w + f.bitmap), (int*)(w + f.valid), a.status);
+                       f.chunks, (uint32_t*)(w + f.bitmap), (int32_t*)(w + f.dec),
+                       (int*)(w + f.valid), a.status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1480,7 +1492,12 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     const int C = a.H * P + 2 * a.G * N;
     hipLaunchKernelGGL(k_varlen_conv_state, dim3((C / 8 + 255) / 256, a.B), dim3(256), 0, st,
                        (const bf16*)a.x, a.xs, q, C);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the one-token sequences: a decode step each, states in their slots
+    return launch_decode_varlen(true, a.B, a.H, P, a.G, N, W, a.x, a.xs, a.z, a.zs, a.dt,
+                                DtA{a.dts, a.dt_bias}, a.A, a.D, a.conv_w, a.conv_b, a.norm_w,
+                                a.eps, q, (const int32_t*)(w + f.dec), a.y, st);
   }
   if (!norm_after) return e;
   return launch_gated_norm(true, false, a.B * a.L, a.H * P, a.G, a.y, a.z, a.zs, a.norm_w, a.eps,

@@ -103,6 +103,36 @@ def test_single_sequence_matches_prefill_entry(ops):
     assert np.array_equal(host(ss)[0], gs[2]) and np.array_equal(host(cs)[0], gc[2])
 
 
+@pytest.mark.parametrize("fresh", [False, True])
+def test_one_token_sequences_match_decode_entry(ops, fresh):
+    """One-token sequences of a ragged batch are decode steps: beside a
+    prefill, they give the decode entry's output and new states bit for bit
+    (the same decode kernel, token rows and slots taken from the batch),
+    resuming from their slots or starting fresh (zero states)."""
+    import torch
+    bf = torch.bfloat16
+    cfg = synth.replace(synth.CONFIGS["c1"], chunk=128)
+    lens, slots = [1, 200, 1], [4, 0, 2]
+    has = [0 if fresh else 1, 1, 0 if fresh else 1]
+    out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, lens, slots, has, S=5)
+    T = sum(lens)
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg, batch=1, seqlen=T)
+    rows = [0, 201]  # token rows of the two one-token sequences
+    d = ops.SSDDims(2, 1, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 128, bf)
+    cs = dev(cpool[[4, 2]], bf)
+    ss = dev(spool[[4, 2]])
+    if fresh:
+        cs.zero_()
+        ss.zero_()
+    y = ops.ssd_decode_step(d, dev(inp["xbc"][0][rows], bf), dev(inp["z"][0][rows], bf),
+                            dev(inp["dt"][0][rows], bf), dev(prm["A"]), dev(prm["D"]),
+                            dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"],
+                            cs, ss)
+    assert np.array_equal(host(y), out[rows])
+    assert np.array_equal(host(cs), gc[[4, 2]]) and np.array_equal(host(ss), gs[[4, 2]])
+
+
 @pytest.mark.parametrize("lens,slots,S", [
     ([5, 3], [1, 1], 4),      # one slot used twice
     ([5, 3], [0, 4], 4),      # slot past the pool
