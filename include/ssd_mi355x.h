@@ -65,26 +65,31 @@
  * chunk in {32, 64, 128, 256}.
  *
  * Precision. State, decay exponents, sums and the norm are fp32. The dense
- * contractions of the chunked scan run on MFMA with fp32 accumulation: with
- * fp32 operands for fp32 I/O and fp16 operands for bf16 I/O (B, C, x scaled
- * by dt or the decay weights, the decay-masked C B^T and the carried-in
- * states; in the fast path, used for bf16 I/O with headdim 64, dstate 128,
- * heads per group a multiple of 4, dims->chunk >= 64 and conv width 4 when
- * the call includes the conv, also the chunk states, and D x taken from x at
- * fp16 hi + lo precision). The fp16 rounding of the carried-in states and of
- * C bounds the error of the inter-chunk term by about 2^-11 times the sum of
- * |C_n S_n| over the state, not |y|: inputs for which that sum is much larger
- * than y (a conv bias with slowly decaying heads, A of order -0.01, measured
- * at up to 8x the 2e-2 bf16 tolerance after the norm) need
- * SSD_FLAG_FP32_OPERANDS. Those fp16 intermediates (activations after SiLU,
- * C B^T, chunk states, carried-in states, the scan output before the norm)
- * must stay within fp16 range (|v| < 65504); a value beyond it becomes
- * infinite, so the output or final state is not finite and
- * ssd_workspace_status() reports SSD_ERR_NONFINITE for the call. With
- * SSD_FLAG_FP32_OPERANDS every intermediate is fp32 (no such limit). In the fast path the chunk length is an
- * internal choice (128 tokens); the result does not depend on dims->chunk
- * beyond rounding. The fast path fuses the gated norm into its chunk-output
- * kernel, also when a norm group spans several (up to 32) of that kernel's
+ * contractions of the chunked scan run on MFMA with fp32 accumulation. The
+ * general path (every shape outside the fast path, and fp32 I/O) runs
+ * 64-token chunks: its chunk states take fp32 operands for fp32 I/O and
+ * fp16 operands for bf16 I/O (x scaled by the decay weights, and B), its
+ * carried-in states are fp32 and its chunk outputs (C B^T, the masked decay
+ * matrix, C S_in, D x) take fp32 operands. The fast path (bf16 I/O with
+ * headdim 64, dstate 128, heads per group a multiple of 4, dims->chunk >= 64
+ * and conv width 4 when the call includes the conv) takes fp16 operands
+ * throughout (the chunk states and carried-in states are also stored in
+ * fp16), with D x taken from x at fp16 hi + lo precision. There the fp16
+ * rounding of the carried-in states and of C bounds the error of the
+ * inter-chunk term by about 2^-11 times the sum of |C_n S_n| over the state,
+ * not |y|: inputs for which that sum is much larger than y (a conv bias with
+ * slowly decaying heads, A of order -0.01, measured at up to 8x the 2e-2
+ * bf16 tolerance after the norm) need SSD_FLAG_FP32_OPERANDS, which sends
+ * the call to the general path with fp32 operands throughout. The fp16
+ * intermediates (activations after SiLU, C B^T, chunk states, carried-in
+ * states, the scan output before the norm) must stay within fp16 range
+ * (|v| < 65504); a value beyond it becomes infinite, so the output or final
+ * state is not finite and ssd_workspace_status() reports SSD_ERR_NONFINITE
+ * for the call. With SSD_FLAG_FP32_OPERANDS every intermediate is fp32 (no
+ * such limit). The chunk length is an internal choice (128 tokens in the
+ * fast path, 64 in the general path); the result does not depend on
+ * dims->chunk beyond rounding. The fast path fuses the gated norm into its
+ * chunk-output kernel, also when a norm group spans several (up to 32) of that kernel's
  * 4-head blocks: their per-token sums of squares are exchanged through the
  * workspace, which needs the group's blocks to run concurrently (a stream
  * with the whole GPU qualifies: 512 resident workgroups, 64 per XCD, against

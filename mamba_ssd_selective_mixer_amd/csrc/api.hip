@@ -34,7 +34,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t channels(const ssd_dims* d) {
   return (int64_t)d->nheads * d->headdim + 2 * (int64_t)d->ngroups * d->dstate;
 }
-int64_t nchunks(const ssd_dims* d) { return (d->seqlen + d->chunk - 1) / d->chunk; }
+// The general path runs 64-token chunks whatever the caller's chunk (the
+// result is the same in exact arithmetic; its output kernel is built for 64).
+constexpr int kGenChunk = 64;
+int64_t gen_chunks(const ssd_dims* d) { return (d->seqlen + kGenChunk - 1) / kGenChunk; }
 
 bool any_overlap(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || !na || !nb) return false;
@@ -128,7 +131,7 @@ bool use_fast(const ssd_dims* d, bool conv) {
 ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   ScanWs w{};
   const size_t B = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate;
-  const size_t nc = nchunks(d);
+  const size_t nc = gen_chunks(d);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -171,7 +174,7 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
              const float* s_in, float* s_out, void* y, const ScanWs& ws, hipStream_t st) {
   const bool bf = d->io_dtype == SSD_BF16;
   ssd::ScanShape s{d->batch, d->seqlen, d->nheads, d->headdim, d->ngroups,
-                   d->dstate, d->chunk, (int)nchunks(d), dta};
+                   d->dstate, kGenChunk, (int)gen_chunks(d), dta};
   const bool fo = f32op(d);
   int rc = hip_status(ssd::launch_chunk_state(bf, x_f32, fo, s, x, xs, dt, A, Bm, bs, ws.states,
                                               ws.lam_end, ws.status, st));
@@ -180,8 +183,8 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
   if (rc) return rc;
   const bool fused_norm = z != nullptr;
   void* ydst = fused_norm ? (void*)ws.y32 : y;
-  rc = hip_status(ssd::launch_chunk_out(bf, x_f32, fo, s, x, xs, dt, A, D, Bm, Cm, bs, ws.states,
-                                        ydst, fused_norm || !bf, ws.status, st));
+  rc = hip_status(ssd::launch_chunk_y(bf, x_f32, fused_norm || !bf, s, x, xs, Bm, Cm, bs, dt, A,
+                                      D, ws.states, ydst, ws.status, ssd::KID_CHUNK_OUT, st));
   if (rc) return rc;
   if (fused_norm)
     rc = hip_status(ssd::launch_gated_norm(bf, true, d->batch * d->seqlen,

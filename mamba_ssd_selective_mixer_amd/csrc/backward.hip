@@ -19,24 +19,15 @@
 // (16x16x4, fp32 accumulation) with operand slices staged in LDS; the gated
 // norm and the conv are differentiated elementwise.
 #include "common.hpp"
+#include "f32tiles.hpp"
 #include "launch.hpp"
 
 namespace ssd {
 namespace bwd {
 
-constexpr int kThreads = 256;
-constexpr int kQ = 64;           // chunk length
-constexpr int kQP = kQ + 4;      // pitch of the Q x Q tiles (floats)
-constexpr int kKS = 32;          // width of a staged operand slice
-constexpr int kSP = kKS + 4;     // pitch of a staged slice
+using namespace f32t;
 constexpr int kNormBlocks = 1024; // most norm-backward workgroups (one dw part each)
 constexpr int kMaxGroups = 256;
-
-// MFMA 16x16x4 fp32. Lane l supplies A[row l%16][k l/16] and B[k l/16][col
-// l%16]; acc[r] is C[row 4 (l/16) + r][col l%16].
-SSD_DEV f32x4 mma(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // zero n floats
 __global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
@@ -45,215 +36,7 @@ __global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
-// Rows [0, rows) x columns [0, kKS) of a row-major fp32 matrix (row stride
-// rs, elements) into dst [rows][kSP]; rows >= nrows and columns >= ncols
-// (a multiple of 4) are zero.
-SSD_DEV void stage(float* dst, const float* src, int rs, int rows, int nrows, int ncols) {
-  for (int i = threadIdx.x; i < rows * (kKS / 4); i += kThreads) {
-    const int r = i / (kKS / 4), c4 = (i % (kKS / 4)) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nrows && c4 < ncols) v = *reinterpret_cast<const float4*>(src + r * rs + c4);
-    *reinterpret_cast<float4*>(dst + r * kSP + c4) = v;
-  }
-}
-
-// One staged slice (rows [0, ROWS) x columns [0, kKS)) held in registers
-// between its global loads and its LDS stores, so that the next slice's
-// loads are in flight while the current one is computed on.
-template <int ROWS>
-struct SliceRegs {
-  static constexpr int kItems = ROWS * (kKS / 4), kN = (kItems + kThreads - 1) / kThreads;
-  float4 v[kN];
-  SSD_DEV void load(const float* src, int rs, int nrows, int ncols) {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int idx = threadIdx.x + i * kThreads, r = idx / (kKS / 4), c4 = (idx % (kKS / 4)) * 4;
-      v[i] = (idx < kItems && r < nrows && c4 < ncols)
-                 ? *reinterpret_cast<const float4*>(src + r * rs + c4)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  SSD_DEV void store(float* dst) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int idx = threadIdx.x + i * kThreads, r = idx / (kKS / 4), c4 = (idx % (kKS / 4)) * 4;
-      if (idx < kItems) *reinterpret_cast<float4*>(dst + r * kSP + c4) = v[i];
-    }
-  }
-};
-
-// Rows [0, rows) x columns [0, cols) (a multiple of 4) of a row-major fp32
-// matrix into dst [rows][pitch], scaled per row by sc[r] when sc is given;
-// rows >= nrows are zero. A pitch of 16 (mod 64) floats keeps column-wise
-// fragment reads (16 columns x 4 rows per wave) free of bank conflicts.
-SSD_DEV void stage_rows(float* dst, int pitch, const float* src, int rs, int rows, int nrows,
-                        int cols, const float* sc = nullptr) {
-  const int c4n = cols / 4;
-  for (int i = threadIdx.x; i < rows * c4n; i += kThreads) {
-    const int r = i / c4n, c4 = (i % c4n) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nrows) {
-      v = *reinterpret_cast<const float4*>(src + r * rs + c4);
-      if (sc) {
-        const float f = sc[r];
-        v.x *= f;
-        v.y *= f;
-        v.z *= f;
-        v.w *= f;
-      }
-    }
-    *reinterpret_cast<float4*>(dst + r * pitch + c4) = v;
-  }
-}
-
-// The ten causal 16x16 tiles (rt, st), st <= rt, of a 64 x 64 block spread
-// over the four waves (at most three each): whether slot i of wave w holds one.
-SSD_DEV bool causal_tile(int w, int i, int& rt, int& st) {
-  if (w == 3) {
-    rt = 3;
-    st = 3;
-    return i == 0;
-  }
-  if (w == 0) {
-    rt = i == 0 ? 0 : 1;
-    st = i == 0 ? 0 : i - 1;
-    return true;
-  }
-  rt = w + 1;
-  st = i;
-  return true;
-}
-
-// ---------------------------------------------------------------- chunk Lam
-// Lam (inclusive cumsum of dt A over the chunk, natural log units), dt and
-// exp(Lam) of the first len positions into lam / dts / ex (wave 0).
-template <class T>
-__device__ __forceinline__ void chunk_lam(const T* __restrict__ dt, const DtA& dta, int64_t row0,
-                                          int h, float Ah, int len, float* lam, float* dts,
-                                          float* ex) {
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const float d = tid < len ? dt_of(to_f(dt[(row0 + tid) * dta.dts + h]), dta, h) : 0.f;
-    const float v = wave_incl_scan(d * Ah);
-    lam[tid] = v;
-    dts[tid] = d;
-    ex[tid] = __expf(v);
-  }
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------- y recompute
-// y = M X + exp(Lam_t) C S_in^T + D X of one (chunk, head) in fp32, with
-// S_in the chunk's carried-in state (fp32). Wave w owns rows 16 w .. 16 w + 15.
-template <class T, int P>
-__global__ __launch_bounds__(kThreads, 2) void k_bwd_y(const float* __restrict__ v,
-                                                       const T* __restrict__ dt, DtA dta,
-                                                       const float* __restrict__ A,
-                                                       const float* __restrict__ D,
-                                                       const float* __restrict__ Sin,
-                                                       float* __restrict__ y, int L, int H, int G,
-                                                       int N, int nc) {
-  extern __shared__ __align__(16) float sm[];
-  float* Mt = sm;                 // [Q][kQP]: M
-  float* Bs = sm + kQ * kQP;      // [Q][kSP]
-  float* Cs = Bs + kQ * kSP;      // [Q][kSP]
-  float* Ss = Cs + kQ * kSP;      // [P][kSP]
-  __shared__ float lam[64], dts[64], ex[64];
-  constexpr int NPT = P / 16;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
-  const int t0 = c * kQ, len = min(kQ, L - t0);
-  const int64_t row0 = (int64_t)b * L + t0;
-  const int HP = H * P;
-  const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, bo = HP + (int64_t)g * N,
-                co = HP + (int64_t)(G + g) * N;
-  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
-  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
-  int rt[3], st[3];
-  bool on[3];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
-  f32x4 aG[3], aY[NPT];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) aG[i] = zero4();
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
-  const int sw = wave * 16;
-  // G on the causal tiles and C S_in^T on the wave's rows, over slices of n
-  SliceRegs<kQ> rb, rc;
-  SliceRegs<P> rs;
-  auto fetch = [&](int n0) {
-    const int nv = min(kKS, N - n0);
-    rb.load(v + row0 * C + bo + n0, (int)C, len, nv);
-    rc.load(v + row0 * C + co + n0, (int)C, len, nv);
-    rs.load(Si + n0, N, P, nv);
-  };
-  fetch(0);
-  for (int n0 = 0; n0 < N; n0 += kKS) {
-    const int nv = min(kKS, N - n0);
-    rb.store(Bs);
-    rc.store(Cs);
-    rs.store(Ss);
-    __syncthreads();
-    if (n0 + kKS < N) fetch(n0 + kKS);
-    for (int kk = 0; kk < nv; kk += 4) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        if (on[i])
-          aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk], Bs[(st[i] * 16 + lr) * kSP + kk + lk],
-                      aG[i]);
-      const float a = Cs[(sw + lr) * kSP + kk + lk];
-#pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) aY[pt] = mma(a, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
-    }
-    __syncthreads();
-  }
-  // M = G o E dt_s on the causal tiles (rows and columns past the chunk: 0)
-#pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (on[i])
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
-        const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
-        Mt[t * kQP + s] = aG[i][r] * f;
-      }
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
-  // the chunk's x rows, where B and C were staged
-  float* Xs = Bs;  // [Q][P + 16]
-  stage_rows(Xs, P + 16, v + row0 * C + xo, (int)C, kQ, len, P);
-  __syncthreads();
-  // + M X over s <= t (the wave's rows reach s < sw + 16)
-  for (int k0 = 0; k0 < sw + 16; k0 += 4) {
-    const float a = Mt[(sw + lr) * kQP + k0 + lk];
-#pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-      aY[pt] = mma(a, Xs[(k0 + lk) * (P + 16) + pt * 16 + lr], aY[pt]);
-  }
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = sw + 4 * lk + r, p = pt * 16 + lr;
-      if (t < len) y[(row0 + t) * HP + xo + p] = aY[pt][r] + Dh * v[(row0 + t) * C + xo + p];
-    }
-}
-
 // ---------------------------------------------------------------- gated norm
-SSD_DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
-SSD_DEV float4 ld4(const bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-SSD_DEV void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
-SSD_DEV void st4(bf16* p, float4 v) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-}
 SSD_DEV float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
 // q = y silu(z), r = (mean_group(q^2) + eps)^-1/2, out = q r w. For each row:
@@ -842,13 +625,8 @@ __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ 
 namespace {
 size_t bround(size_t b) { return (b + 255) / 256 * 256; }
 
-// LDS of the per-chunk kernels (the y recompute, the chunk gradients and
-// the state-gradient terms)
-size_t bwd_y_lds(int P) {
-  const size_t slices = 2 * (size_t)bwd::kQ * bwd::kSP + (size_t)P * bwd::kSP,
-               xrows = (size_t)bwd::kQ * (P + 16);
-  return ((size_t)bwd::kQ * bwd::kQP + std::max(slices, xrows)) * 4;
-}
+// LDS of the per-chunk kernels (the chunk gradients and the state-gradient
+// terms)
 size_t bwd_chunk_lds(int P) {
   const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP, fm = (size_t)bwd::kQ * (bwd::kQ + 1),
                ys = (size_t)bwd::kQ * (P + 16),
@@ -913,27 +691,16 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   // states, y (all fp32)
   e = launch_conv1d(bf, B, L, (int)C, W, a.xbc, C, a.conv_w, a.conv_b, a.conv_in, v, C, true, st);
   if (e != hipSuccess) return e;
-  ScanShape s{B, L, H, P, G, N, kQ, nc, plain};
+  ScanShape s{B, L, H, P, G, N, kQ, nc, plain};  // kQ: 64, as the output kernel needs
   const unsigned char* vb = (const unsigned char*)v;
   e = launch_chunk_state(bf, true, true, s, v, C, a.dt, a.A, vb + HP * 4, C, states, lam_end,
                          a.status, st);
   if (e != hipSuccess) return e;
   e = launch_state_pass(s, states, lam_end, a.s_in, nullptr, a.status, st);
   if (e != hipSuccess) return e;
-  {
-    ProfScope ps(st, KID_BWD_Y);
-    const size_t lds = bwd_y_lds(P);
-#define SSD_Y(PP)                                                                               \
-  if (bf)                                                                                       \
-    hipLaunchKernelGGL((k_bwd_y<bf16, PP>), gc, blk, lds, st, v, (const bf16*)a.dt, plain, a.A, \
-                       a.D, states, y, L, H, G, N, nc);                                         \
-  else                                                                                          \
-    hipLaunchKernelGGL((k_bwd_y<float, PP>), gc, blk, lds, st, v, (const float*)a.dt, plain,    \
-                       a.A, a.D, states, y, L, H, G, N, nc)
-    SSD_BY_P(SSD_Y)
-#undef SSD_Y
-  }
-  SSD_CHECK();
+  e = launch_chunk_y(bf, true, true, s, v, C, vb + HP * 4, vb + (HP + (int64_t)G * N) * 4, C, a.dt,
+                     a.A, a.D, states, y, a.status, KID_BWD_Y, st);
+  if (e != hipSuccess) return e;
   // zero the summed gradients
   auto zero = [&](float* p, int64_t n) {
     if (p && n > 0)

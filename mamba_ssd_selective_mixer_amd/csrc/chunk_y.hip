@@ -1,0 +1,168 @@
+// Chunk outputs of the chunked scan on fp32 MFMA operands, 64-token chunks
+// ("feat(model): add Nemotron-3 Nano hybrid ..." attribution commit: the SSD
+// block decomposition, diagonal blocks and off-diagonal state terms):
+//   y = M X + exp(Lam_t) C S_in^T + D X,  M = (C B^T) o exp(Lam_t - Lam_s) dt_s (s <= t)
+// per (chunk, head), with S_in the chunk's carried-in state (fp32). It is the
+// general path's output kernel (every shape, fp32 or bf16 I/O) and the
+// backward pass's recompute of y. x, B, C are read as fp32 or bf16 rows of
+// any token stride; y is written as fp32 or the I/O type.
+#include "common.hpp"
+#include "f32tiles.hpp"
+#include "launch.hpp"
+
+namespace ssd {
+namespace f32t {
+
+constexpr int kStatusNonFinite = 2;  // status bit: an output is not finite
+
+// Wave w owns rows 16 w .. 16 w + 15 of the chunk: C B^T on the ten causal
+// 16x16 tiles (three per wave at most) and C S_in^T on its rows over 32-wide
+// slices of n (the next slice's loads in flight while one is computed), M
+// into LDS, then M X over its rows from the chunk's x rows staged in LDS.
+template <class T, class TX, class TY, int P>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
+    const TX* __restrict__ x, int64_t xs, const TX* __restrict__ Bm, const TX* __restrict__ Cm,
+    int64_t bs, const T* __restrict__ dt, DtA dta, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ Sin, TY* __restrict__ y, int* status,
+    int L, int H, int G, int N, int nc) {
+  extern __shared__ __align__(16) float sm[];
+  float* Mt = sm;                 // [Q][kQP]: M
+  float* Bs = sm + kQ * kQP;      // [Q][kSP]
+  float* Cs = Bs + kQ * kSP;      // [Q][kSP]
+  float* Ss = Cs + kQ * kSP;      // [P][kSP]
+  __shared__ float lam[64], dts[64], ex[64];
+  constexpr int NPT = P / 16;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int t0 = c * kQ, len = min(kQ, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int HP = H * P;
+  const int xsi = (int)xs, bsi = (int)bs;
+  const TX* xr = x + row0 * xs + (int64_t)h * P;
+  const TX* br = Bm + row0 * bs + (int64_t)g * N;
+  const TX* cr = Cm + row0 * bs + (int64_t)g * N;
+  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
+  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
+  int rt[3], st[3];
+  bool on[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
+  f32x4 aG[3], aY[NPT];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) aG[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
+  const int sw = wave * 16;
+  SliceRegs<kQ> rb, rc;
+  SliceRegs<P> rs;
+  auto fetch = [&](int n0) {
+    const int nv = min(kKS, N - n0);
+    rb.load(br + n0, bsi, len, nv);
+    rc.load(cr + n0, bsi, len, nv);
+    rs.load(Si + n0, N, P, nv);
+  };
+  fetch(0);
+  for (int n0 = 0; n0 < N; n0 += kKS) {
+    const int nv = min(kKS, N - n0);
+    rb.store(Bs);
+    rc.store(Cs);
+    rs.store(Ss);
+    __syncthreads();
+    if (n0 + kKS < N) fetch(n0 + kKS);
+    for (int kk = 0; kk < nv; kk += 4) {
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (on[i])
+          aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk], Bs[(st[i] * 16 + lr) * kSP + kk + lk],
+                      aG[i]);
+      const float a = Cs[(sw + lr) * kSP + kk + lk];
+#pragma unroll
+      for (int pt = 0; pt < NPT; ++pt) aY[pt] = mma(a, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
+    }
+    __syncthreads();
+  }
+  // M = G o E dt_s on the causal tiles (rows and columns past the chunk: 0)
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (on[i])
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
+        const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
+        Mt[t * kQP + s] = aG[i][r] * f;
+      }
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
+  // the chunk's x rows, where B and C were staged
+  float* Xs = Bs;  // [Q][P + 16]
+  stage_rows(Xs, P + 16, xr, xsi, kQ, len, P);
+  __syncthreads();
+  // + M X over s <= t (the wave's rows reach s < sw + 16)
+  for (int k0 = 0; k0 < sw + 16; k0 += 4) {
+    const float a = Mt[(sw + lr) * kQP + k0 + lk];
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+      aY[pt] = mma(a, Xs[(k0 + lk) * (P + 16) + pt * 16 + lr], aY[pt]);
+  }
+  float chk = 0.f;  // NaN once an output is infinite or NaN
+#pragma unroll
+  for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = sw + 4 * lk + r, p = pt * 16 + lr;
+      if (t < len) {
+        const float yv = aY[pt][r] + Dh * Xs[t * (P + 16) + p];
+        chk += yv * 0.f;
+        y[(row0 + t) * HP + (int64_t)h * P + p] = from_f<TY>(yv);
+      }
+    }
+  if (status && chk != 0.f) atomicOr(status, kStatusNonFinite);
+}
+
+size_t chunk_y_lds(int P) {
+  const size_t slices = 2 * (size_t)kQ * kSP + (size_t)P * kSP, xrows = (size_t)kQ * (P + 16);
+  return ((size_t)kQ * kQP + std::max(slices, xrows)) * 4;
+}
+
+}  // namespace f32t
+
+size_t chunk_y_lds_bytes(int P) { return f32t::chunk_y_lds(P); }
+
+hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
+                          const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
+                          const void* dt, const float* A, const float* D, const float* states,
+                          void* y, int* status, int kid, hipStream_t st) {
+  using namespace f32t;
+  if (s.Q != kQ) return hipErrorInvalidValue;
+  ProfScope ps(st, kid);
+  const dim3 grid(s.nc, s.H, s.B), blk(kThreads);
+  const size_t lds = chunk_y_lds(s.P);
+#define SSD_Y(TT, TX, TY, PP)                                                                     \
+  hipLaunchKernelGGL((k_chunk_y<TT, TX, TY, PP>), grid, blk, lds, st, (const TX*)x, xs,           \
+                     (const TX*)Bm, (const TX*)Cm, bs, (const TT*)dt, s.dta, A, D, states, (TY*)y, \
+                     status, s.L, s.H, s.G, s.N, s.nc)
+#define SSD_Y_P(TT, TX, TY)                  \
+  switch (s.P) {                             \
+    case 16: SSD_Y(TT, TX, TY, 16); break;   \
+    case 32: SSD_Y(TT, TX, TY, 32); break;   \
+    case 64: SSD_Y(TT, TX, TY, 64); break;   \
+    default: SSD_Y(TT, TX, TY, 128); break;  \
+  }
+  if (!io_bf16) {
+    SSD_Y_P(float, float, float);
+  } else if (x_f32) {
+    if (y_f32) { SSD_Y_P(bf16, float, float); }
+    else { SSD_Y_P(bf16, float, bf16); }
+  } else {
+    if (y_f32) { SSD_Y_P(bf16, bf16, float); }
+    else { SSD_Y_P(bf16, bf16, bf16); }
+  }
+#undef SSD_Y_P
+#undef SSD_Y
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -34,7 +34,8 @@ hipError_t launch_decode(bool io_bf16, int B, int H, int P, int G, int N, int W,
                          const void* dt, const DtA& dta, const float* A, const float* D,
                          const void* cw, const void* cb, const void* nw, float eps,
                          void* conv_state, float* ssm_state, void* y, hipStream_t st);
-// Chunked scan, three phases: chunk states, state passing, chunk outputs.
+// Chunked scan, three phases: chunk states, state passing, chunk outputs
+// (the last in launch_chunk_y below).
 // x_f32: x, B and C are fp32 (else the I/O type); dt and y are the I/O type.
 // f32op: fp32 MFMA operands for bf16 I/O too (else fp16). status: the call's
 // status word, cleared by the chunk-state kernel; the others set bits in it.
@@ -44,11 +45,14 @@ hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanSh
                               int* status, hipStream_t st);
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
                              const float* s_in, float* s_out, int* status, hipStream_t st);
-hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
-                            const void* x, int64_t xs, const void* dt, const float* A,
-                            const float* D, const void* Bm, const void* Cm, int64_t bs,
-                            const float* states, void* y, bool y_f32, int* status,
-                            hipStream_t st);
+// Chunk outputs on fp32 MFMA operands (s.Q must be 64): y = M X + exp(Lam)
+// C S_in^T + D X. x_f32: x, B, C fp32 (else the I/O type); y_f32: y fp32
+// (else the I/O type). kid: the kernel id the timing aid records it under.
+hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
+                          const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
+                          const void* dt, const float* A, const float* D, const float* states,
+                          void* y, int* status, int kid, hipStream_t st);
+size_t chunk_y_lds_bytes(int P);
 
 }  // namespace ssd
 

@@ -182,137 +182,11 @@ __global__ __launch_bounds__(kScanThreads) void k_state_pass(float* states,
 }
 
 // ---------------------------------------------------------------------------
-// Phase 3: chunk outputs. Each wave owns 16-row tiles of the chunk: it forms
-// the causal tiles of M = (C B^T) o exp(Lam_t - Lam_s) in its LDS slab, then
-// y = M (dt x) + exp(Lam_t) C S_in^T + D x for every 16-column tile of P.
-template <class T, class TX, bool YF32, bool F32OP>
-__global__ __launch_bounds__(kScanThreads) void k_chunk_out(
-    const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, const TX* __restrict__ Bm, const TX* __restrict__ Cm, int64_t bs,
-    const float* __restrict__ states, void* __restrict__ yout, int* status, DtA dta, int L, int H,
-    int G, int P, int N, int Q, int nc) {
-  typedef OpT<T, F32OP> O;  // MFMA operand type
-  using M = Mfma<O>;
-  const int QK = Q + Pad<O>::v;
-  extern __shared__ __align__(16) unsigned char smraw[];
-  O* XdtT = reinterpret_cast<O*>(smraw);  // [P][QK]  dt_s x_s[p], k = s contiguous
-  O* Mall = XdtT + P * QK;                // [4 waves][16][QK]
-  __shared__ float lam[kScanThreads], dts[kScanThreads], wsum[4];
-
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
-  const int t0 = c * Q, len = min(Q, L - t0);
-  const int64_t row0 = (int64_t)b * L + t0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kk = M::KPL * (lane >> 4), rr = lane & 15;
-
-  chunk_cumsum<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, wsum);
-
-  const int P8 = P / 8;
-  for (int v = tid; v < Q * P8; v += kScanThreads) {
-    const int s = v / P8, p0 = (v % P8) * 8;
-    float xv[8];
-    if (s < len) {
-      load8(x + (row0 + s) * xs + (int64_t)h * P + p0, xv);
-      const float d = dts[s];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] *= d;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xv[j] = 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) XdtT[(p0 + j) * QK + s] = from_f<O>(xv[j]);
-  }
-  __syncthreads();
-
-  const float* Sin = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  const float Dh = D ? D[h] : 0.f;
-  O* Mw = Mall + wave * 16 * QK;
-  const TX* Cg = Cm + (int64_t)g * N;
-  const TX* Bg = Bm + (int64_t)g * N;
-  const int nrt = (len + 15) / 16;
-  float chk = 0.f;  // NaN once any output is infinite or NaN
-  for (int rt0 = 0; rt0 < nrt; rt0 += 4) {
-    const int rt = rt0 + wave;
-    const bool active = rt < nrt;
-    const int ns = (rt + 1) * 16;
-    const int nsr = (ns + M::KSTEP - 1) / M::KSTEP * M::KSTEP;
-    const int trow = rt * 16 + rr;  // A-operand row of this lane
-    const bool trow_ok = active && trow < len;
-    if (active) {
-      for (int st = 0; st <= rt; ++st) {
-        const int scol = st * 16 + rr;
-        const bool scol_ok = scol < len;
-        f32x4 gacc = zero4();
-        for (int k = 0; k < N; k += M::KSTEP) {
-          // a lane's k-slice past N (N = 16 under a 32-deep fp16 MFMA) is zero
-          const bool kin = k + kk < N;
-          typename M::frag fa, fb;
-          if (trow_ok && kin) fa = M::ldg(Cg + (row0 + trow) * bs + k + kk);
-          else fa = typename M::frag{};
-          if (scol_ok && kin) fb = M::ldg(Bg + (row0 + scol) * bs + k + kk);
-          else fb = typename M::frag{};
-          gacc = M::mma(fa, fb, gacc);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = rt * 16 + 4 * (lane >> 4) + r, s = st * 16 + (lane & 15);
-          float m = 0.f;
-          if (s <= t && t < len) m = gacc[r] * fexp(lam[t] - lam[s]);
-          Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<O>(m);
-        }
-      }
-      for (int s = ns + (lane & 15); s < nsr; s += 16)
-        for (int r = 0; r < 4; ++r) Mw[(4 * (lane >> 4) + r) * QK + s] = from_f<O>(0.f);
-    }
-    __syncthreads();
-    if (active) {
-      for (int pt = 0; pt < P / 16; ++pt) {
-        f32x4 acc = zero4(), acc2 = zero4();
-        const O* mp = Mw + rr * QK + kk;
-        const O* xp = XdtT + (pt * 16 + rr) * QK + kk;
-        for (int k = 0; k < nsr; k += M::KSTEP) acc = M::mma(M::ld(mp + k), M::ld(xp + k), acc);
-        const float* sp = Sin + (int64_t)(pt * 16 + rr) * N + kk;
-        for (int k = 0; k < N; k += M::KSTEP) {
-          const bool kin = k + kk < N;
-          typename M::frag fa, fs;
-          if (trow_ok && kin) fa = M::ldg(Cg + (row0 + trow) * bs + k + kk);
-          else fa = typename M::frag{};
-          if (kin) fs = M::cvt(sp + k);
-          else fs = typename M::frag{};
-          acc2 = M::mma(fa, fs, acc2);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = rt * 16 + 4 * (lane >> 4) + r, p = pt * 16 + (lane & 15);
-          if (t < len) {
-            const float xv = to_f(x[(row0 + t) * xs + (int64_t)h * P + p]);
-            const float yv = acc[r] + fexp(lam[t]) * acc2[r] + Dh * xv;
-            chk += yv * 0.f;
-            const int64_t o = (row0 + t) * (int64_t)H * P + (int64_t)h * P + p;
-            if (YF32) reinterpret_cast<float*>(yout)[o] = yv;
-            else reinterpret_cast<T*>(yout)[o] = from_f<T>(yv);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-  if (chk != 0.f) atomicOr(status, kStatusNonFinite);
-}
-
-// ---------------------------------------------------------------------------
 // op16: the MFMA operands are fp16 (else fp32)
 static size_t state_lds(bool op16, int P, int N) {
   const int KP = kStateSB + (op16 ? 8 : 4);
   return (size_t)(P + N) * KP * (op16 ? 2 : 4);
 }
-static size_t out_lds(bool op16, int P, int Q) {
-  const int QK = Q + (op16 ? 8 : 4);
-  return (size_t)(P + 4 * 16) * QK * (op16 ? 2 : 4);
-}
-
 hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
                               const void* x, int64_t xs, const void* dt, const float* A,
                               const void* Bm, int64_t bs, float* states, float* lam_end,
@@ -351,37 +225,12 @@ hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_out(bool io_bf16, bool x_f32, bool f32op, const ScanShape& s,
-                            const void* x, int64_t xs, const void* dt, const float* A,
-                            const float* D, const void* Bm, const void* Cm, int64_t bs,
-                            const float* states, void* y, bool y_f32, int* status,
-                            hipStream_t st) {
-  ProfScope ps(st, KID_CHUNK_OUT);
-  dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
-  const size_t lds = out_lds(io_bf16 && !f32op, s.P, s.Q);
-#define SSD_OUT(TT, TX, YF, F)                                                                  \
-  hipLaunchKernelGGL((k_chunk_out<TT, TX, YF, F>), grid, block, lds, st, (const TX*)x, xs,      \
-                     (const TT*)dt, A, D, (const TX*)Bm, (const TX*)Cm, bs, states, y, status,  \
-                     s.dta, s.L, s.H, s.G, s.P, s.N, s.Q, s.nc)
-#define SSD_OUT_F(TT, TX, YF) \
-  if (f32op) SSD_OUT(TT, TX, YF, true); else SSD_OUT(TT, TX, YF, false)
-  if (!io_bf16) SSD_OUT(float, float, true, true);
-  else if (x_f32) {
-    if (y_f32) { SSD_OUT_F(bf16, float, true); }
-    else { SSD_OUT_F(bf16, float, false); }
-  } else {
-    if (y_f32) { SSD_OUT_F(bf16, bf16, true); }
-    else { SSD_OUT_F(bf16, bf16, false); }
-  }
-#undef SSD_OUT_F
-#undef SSD_OUT
-  return hipGetLastError();
-}
-
-// LDS bytes the two MFMA kernels need for a shape (the host checks these
-// against the 160 KiB of one CU before launching).
+// LDS bytes the general path's two MFMA kernels need for a shape: the
+// chunk-state kernel and the fp32 output kernel (64-token chunks); the host
+// checks them against the 160 KiB of one CU before launching.
 size_t scan_lds_bytes(bool op16, int P, int N, int Q) {
-  const size_t a = state_lds(op16, P, N), b = out_lds(op16, P, Q);
+  (void)Q;  // the general path runs 64-token chunks whatever the caller's chunk
+  const size_t a = state_lds(op16, P, N), b = chunk_y_lds_bytes(P);
   return a > b ? a : b;
 }
 

@@ -68,11 +68,18 @@ def test_validate_errors(lib, kw, entry, rc):
     assert lib.ssd_validate(entry, ctypes.byref(dims(synth.CONFIGS["c1"], **kw))) == rc
 
 
-def test_fp32_envelope_limits_lds(lib):
-    d = dims(synth.CONFIGS["c0"], headdim=128, dstate=128, chunk=256)
-    assert lib.ssd_validate(1, ctypes.byref(d)) == -3
-    d = dims(synth.CONFIGS["c0"], headdim=64, dstate=128, chunk=256)
-    assert lib.ssd_validate(1, ctypes.byref(d)) == 0
+def test_envelope_fits_lds(lib):
+    """The general kernels run 64-token chunks whatever the caller's chunk, so
+    every head size, state size and chunk of the envelope fits one CU's LDS,
+    fp32 I/O and fp32 operands included (the widest: head 128, state 256)."""
+    for io in (_lib.SSD_F32, _lib.SSD_BF16):
+        for P in (16, 32, 64, 128):
+            for N in (16, 32, 64, 128, 256):
+                for Q in (32, 64, 128, 256):
+                    for flags in (0, _lib.SSD_FLAG_FP32_OPERANDS):
+                        d = dims(synth.CONFIGS["c0"], headdim=P, dstate=N, chunk=Q, io_dtype=io,
+                                 flags=flags)
+                        assert lib.ssd_validate(1, ctypes.byref(d)) == 0, (io, P, N, Q, flags)
 
 
 def test_status_strings(lib):
@@ -170,8 +177,13 @@ def test_workspace_sizes(lib):
     c1 = synth.CONFIGS["c1"]
     d = dims(c1)
     ws = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
-    nc = c1.seqlen // c1.chunk
+    nc = c1.seqlen // 128
     assert ws >= c1.batch * nc * c1.nheads * c1.headdim * c1.dstate * 2  # fp16 chunk states
+    # the general path (state 64 here): fp32 states of 64-token chunks, fp32 y
+    g = dims(c1, dstate=64)
+    wg = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(g))
+    assert wg >= (c1.batch * (c1.seqlen // 64) * c1.nheads * c1.headdim * 64 * 4
+                  + c1.batch * c1.seqlen * c1.hp * 4)
     assert lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d)) >= ws
     bad = dims(c1, headdim=48)
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(bad)) == 0
