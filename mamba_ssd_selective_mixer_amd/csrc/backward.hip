@@ -28,13 +28,7 @@ namespace bwd {
 using namespace f32t;
 constexpr int kNormBlocks = 1024; // most norm-backward workgroups (one dw part each)
 constexpr int kMaxGroups = 256;
-
-// zero n floats
-__global__ __launch_bounds__(kThreads) void k_zero(float* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * kThreads)
-    p[i] = 0.f;
-}
+constexpr int kMaxNormPieces = 64;  // 256-channel pieces of a row (H*P <= 16384)
 
 // ---------------------------------------------------------------- gated norm
 SSD_DEV float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
@@ -46,24 +40,30 @@ SSD_DEV float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 // thread takes 4 consecutive channels (one norm group: groups are multiples
 // of 16 channels). A workgroup takes `rows` consecutive rows and sums its
 // share of dw in LDS, then writes it to its row of dw_part [gridDim.x][HP].
-template <class T>
+// WG: every norm group is a whole number of 256-channel pieces (a wave's
+// channels in one iteration), so a piece's sums come from the wave
+// (deterministic DPP sums); else each 4-channel lane keeps its own. The
+// group sums then add the pieces in a fixed order (no atomics: the result
+// does not depend on timing).
+template <class T, bool WG>
 __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __restrict__ z,
                                                        const T* __restrict__ w,
                                                        const T* __restrict__ g, float eps,
                                                        T* __restrict__ dz, float* dw_part,
                                                        int64_t nrows, int rows, int HP, int G) {
-  extern __shared__ float4 dwl[];  // [HP / 4]
+  extern __shared__ float4 dwl[];  // [HP / 4], then (not WG) two [HP / 4] piece sums
   __shared__ float sq[kMaxGroups], sg[kMaxGroups];
+  __shared__ float wp2[WG ? kMaxNormPieces : 1], wpw[WG ? kMaxNormPieces : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int S = HP / G, HP4 = HP / 4;
-  // a wave's 256 consecutive channels lie in one group: sum them in the wave
-  const bool wave_groups = S % 256 == 0;
+  float* p2 = WG ? wp2 : reinterpret_cast<float*>(dwl + HP4);
+  float* pw = WG ? wpw : p2 + HP4;
+  constexpr int kUnit = WG ? 256 : 4;  // channels per piece
+  const int per = S / kUnit;
   for (int c = tid; c < HP4; c += kThreads) dwl[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int rr = 0; rr < rows; ++rr) {
     const int64_t row = (int64_t)blockIdx.x * rows + rr;
     if (row >= nrows) break;
-    for (int j = tid; j < G; j += kThreads) sq[j] = sg[j] = 0.f;
-    __syncthreads();
 #pragma unroll 4
     for (int c0 = 0; c0 < HP4; c0 += kThreads) {
       const int c4 = c0 + tid, c = 4 * c4;
@@ -79,17 +79,27 @@ __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __rest
         wgq = sum4(make_float4(ww.x * gg.x * q.x, ww.y * gg.y * q.y, ww.z * gg.z * q.z,
                                ww.w * gg.w * q.w));
       }
-      if (wave_groups) {
+      if constexpr (WG) {
         q2 = wave_sum(q2);
         wgq = wave_sum(wgq);
         if (lane == 0 && c4 < HP4) {
-          atomicAdd(&sq[c / S], q2);
-          atomicAdd(&sg[c / S], wgq);
+          p2[c4 >> 6] = q2;
+          pw[c4 >> 6] = wgq;
         }
       } else if (c4 < HP4) {
-        atomicAdd(&sq[c / S], q2);
-        atomicAdd(&sg[c / S], wgq);
+        p2[c4] = q2;
+        pw[c4] = wgq;
       }
+    }
+    __syncthreads();
+    for (int j = tid; j < G; j += kThreads) {
+      float a = 0.f, b = 0.f;
+      for (int k = 0; k < per; ++k) {
+        a += p2[j * per + k];
+        b += pw[j * per + k];
+      }
+      sq[j] = a;
+      sg[j] = b;
     }
     __syncthreads();
 #pragma unroll 4
@@ -225,7 +235,8 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 
 // ---------------------------------------------------------------- chunk grads
 // One (chunk, head, batch): dX into dv's x channels, this head's share of dB
-// and dC into dBh / dCh [T, H, N], d(dt) into ddt (io dtype), and dA, dD.
+// and dC into dBh / dCh [T, H, N], d(dt) into ddt (io dtype), and this
+// chunk's parts of dA and dD into dA / dD [B nc, H] (or dD null).
 // dt and A reach the output through Lam only (a_u = dt_u A feeds Lam_t for
 // every t >= u), so d(a_u) is the sum over t >= u of dLam_t. That sum is
 // formed term by term, without differences of partial sums:
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   float* Dg = sm + kQ * kQP;     // [Q][kQP]: K, then dG = K o E dt_s
   float* SA = sm + 2 * kQ * kQP; // staging
   __shared__ float lam[64], dts[64], ex[64], wv[64], colF[64], Yo[64], U[64], dai[64], tmp[64];
-  __shared__ float red[4];
+  __shared__ float red[4][2];  // per wave: its share of <dS_out, S_in> and of dD
   constexpr int NPT = P / 16, KP = P / 4;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
@@ -265,7 +276,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
   const float lamE = lam[len - 1];
   if (tid < 64) wv[tid] = tid < len ? __expf(lamE - lam[tid]) * dts[tid] : 0.f;
-  if (tid < 4) red[tid] = 0.f;
 
   // (1) G = C B^T and K = dY X^T on the causal tiles, over slices of n / p
   {
@@ -484,12 +494,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     cstp = wave_sum(cstp);
     ddp = wave_sum(ddp);
     if (lane == 0) {
-      atomicAdd(&red[0], cstp);
-      atomicAdd(&red[1], ddp);
+      red[wave][0] = cstp;
+      red[wave][1] = ddp;
     }
   }
   __syncthreads();
-  if (tid == 0 && dD) atomicAdd(dD + h, red[1]);
+  // this chunk's parts of dD and dA, summed over the chunks later in a fixed
+  // order: part[(b nc + c) H + h]
+  const int64_t part = ((int64_t)b * nc + c) * H + h;
+  const float cst = (red[0][0] + red[1][0]) + (red[2][0] + red[3][0]);
+  if (tid == 0 && dD) dD[part] = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
   // (6) d(a_u), d(dt_u) and dA (wave 0, one lane per position)
   if (wave == 0) {
     const int u = lane;
@@ -501,13 +515,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     __builtin_amdgcn_wave_barrier();  // tmp is written and read by one wave
     float da_dt = 0.f;
     if (u < len) {
-      const float da = dai[u] + tmp[u] + __expf(lamE) * red[0] + pw;
+      const float da = dai[u] + tmp[u] + __expf(lamE) * cst + pw;
       const float dd = colF[u] + __expf(lamE - lam[u]) * U[u] + Ah * da;
       ddt[(row0 + u) * (int64_t)H + h] = from_f<T>(dd);
       da_dt = dts[u] * da;
     }
     const float sa = wave_sum(da_dt);
-    if (lane == 0) atomicAdd(dA + h, sa);
+    if (lane == 0) dA[part] = sa;
   }
 }
 
@@ -643,7 +657,8 @@ size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {
   const size_t st = (size_t)B * nc * H * P * N * 4;
   return bround(T * C * 4) + bround(T * HP * 4) + 2 * bround(st) + bround((size_t)B * H * nc * 4) +
          2 * bround(T * H * N * 4) + bround(T * C * 4) + bround((size_t)bwd::kNormBlocks * HP * 4) +
-         bround((size_t)B * ((L + bwd::kConvTok - 1) / bwd::kConvTok) * C * 5 * 4);
+         bround((size_t)B * ((L + bwd::kConvTok - 1) / bwd::kConvTok) * C * 5 * 4) +
+         bround((size_t)2 * B * nc * H * 4);
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
@@ -673,6 +688,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   float* dw_part = (float*)w;
   w += bround((size_t)kNormBlocks * HP * 4);
   float* conv_part = (float*)w;  // [B * ranges][Cch * (W + 1)]
+  w += bround((size_t)B * ((L + kConvTok - 1) / kConvTok) * C * 5 * 4);
+  float* dA_part = (float*)w;  // [B nc, H]: each chunk's part of dA, then of dD
+  float* dD_part = dA_part + (size_t)B * nc * H;
   const DtA plain{H, nullptr};
   const dim3 gc(nc, H, B), blk(kThreads);
   hipError_t e;
@@ -701,28 +719,21 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   e = launch_chunk_y(bf, true, true, s, v, C, vb + HP * 4, vb + (HP + (int64_t)G * N) * 4, C, a.dt,
                      a.A, a.D, states, y, a.status, KID_BWD_Y, st);
   if (e != hipSuccess) return e;
-  // zero the summed gradients
-  auto zero = [&](float* p, int64_t n) {
-    if (p && n > 0)
-      hipLaunchKernelGGL(k_zero, dim3((unsigned)std::min<int64_t>((n + kThreads - 1) / kThreads, 4096)),
-                         blk, 0, st, p, n);
-  };
-  zero(a.d_A, H);
-  zero(a.d_D, H);
-  SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_NORM);
     const int rows = (int)((T + kNormBlocks - 1) / kNormBlocks);
     const int nb = (int)((T + rows - 1) / rows);
-    const size_t lds = (size_t)HP * 4;
-    if (bf)
-      hipLaunchKernelGGL(k_norm_bwd<bf16>, dim3(nb), blk, lds, st, y, (const bf16*)a.z,
-                         (const bf16*)a.norm_w, (const bf16*)a.d_out, a.eps, (bf16*)a.d_z,
-                         dw_part, T, rows, (int)HP, G);
-    else
-      hipLaunchKernelGGL(k_norm_bwd<float>, dim3(nb), blk, lds, st, y, (const float*)a.z,
-                         (const float*)a.norm_w, (const float*)a.d_out, a.eps, (float*)a.d_z,
-                         dw_part, T, rows, (int)HP, G);
+    // whole 256-channel pieces per norm group: the pieces' sums come from
+    // the waves; else each 4-channel lane's sums are kept in LDS
+    const bool wg = (HP / G) % 256 == 0;
+    const size_t lds = (size_t)HP * 4 + (wg ? 0 : (size_t)HP / 4 * 2 * 4);
+#define SSD_NORM(TT, WGV)                                                                        hipLaunchKernelGGL((k_norm_bwd<TT, WGV>), dim3(nb), blk, lds, st, y, (const TT*)a.z,                               (const TT*)a.norm_w, (const TT*)a.d_out, a.eps, (TT*)a.d_z, dw_part, T,                         rows, (int)HP, G)
+    if (bf) {
+      if (wg) SSD_NORM(bf16, true); else SSD_NORM(bf16, false);
+    } else {
+      if (wg) SSD_NORM(float, true); else SSD_NORM(float, false);
+    }
+#undef SSD_NORM
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((HP + 63) / 64)), blk, 0, st, dw_part, HP,
                        a.d_norm_w, nb, (int)HP);
   }
@@ -753,14 +764,20 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
 #define SSD_CB(PP)                                                                              \
   if (bf)                                                                                       \
     hipLaunchKernelGGL((k_chunk_bwd<bf16, PP>), gc, blk, lds, st, v, y, (const bf16*)a.dt,      \
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (bf16*)a.d_dt, a.d_A, a.d_D, \
-                       L, H, G, N, nc);                                                         \
+                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (bf16*)a.d_dt, dA_part,      \
+                       a.d_D ? dD_part : nullptr, L, H, G, N, nc);                              \
   else                                                                                          \
     hipLaunchKernelGGL((k_chunk_bwd<float, PP>), gc, blk, lds, st, v, y, (const float*)a.dt,    \
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (float*)a.d_dt, a.d_A,       \
-                       a.d_D, L, H, G, N, nc)
+                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (float*)a.d_dt, dA_part,     \
+                       a.d_D ? dD_part : nullptr, L, H, G, N, nc)
     SSD_BY_P(SSD_CB)
 #undef SSD_CB
+    // dA and dD: the chunks' parts added in a fixed order
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((H + 63) / 64)), blk, 0, st, dA_part,
+                       (int64_t)H, a.d_A, B * nc, H);
+    if (a.d_D)
+      hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((H + 63) / 64)), blk, 0, st, dD_part,
+                         (int64_t)H, a.d_D, B * nc, H);
   }
   SSD_CHECK();
   {

@@ -462,8 +462,8 @@ def test_backward_refuses_before_launch(lib):
     need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
     # workspace: the status word, fp32 conv output / its gradient, y, chunk
     # states and their gradients (64-token chunks), per-head dB / dC, 1024
-    # partial norm-weight gradients and the conv gradients' partial sums per
-    # 64-token range
+    # partial norm-weight gradients, the conv gradients' partial sums per
+    # 64-token range, and each chunk's parts of dA and dD
     cfg = synth.CONFIGS["c1"]
     T, C, HP = cfg.batch * cfg.seqlen, cfg.channels, cfg.hp
     nc = -(-cfg.seqlen // 64)
@@ -471,7 +471,8 @@ def test_backward_refuses_before_launch(lib):
     r = lambda b: -(-b // 256) * 256
     assert need == (256 + 2 * r(T * C * 4) + r(T * HP * 4) + 2 * r(st)
                     + r(cfg.batch * cfg.nheads * nc * 4) + 2 * r(T * cfg.nheads * cfg.dstate * 4)
-                    + r(1024 * HP * 4) + r(cfg.batch * nc * C * 5 * 4))
+                    + r(1024 * HP * 4) + r(cfg.batch * nc * C * 5 * 4)
+                    + r(2 * cfg.batch * nc * cfg.nheads * 4))
     base = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
     for k in ("xbc", "z", "dt", "A", "cw", "nw", "d_out", "g_xbc", "g_z", "g_dt", "g_A", "g_cw",
               "g_nw", "ws"):

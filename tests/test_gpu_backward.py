@@ -178,3 +178,49 @@ def test_backward_rejects(ops):
     with pytest.raises(ops.SSDError) as e:  # d_xbc aliasing the input
         ops.ssd_mixer_backward(d, *args, grads={"xbc": args[0]})
     assert e.value.rc == -5
+
+
+def test_backward_deterministic_and_graph_replay(ops):
+    """Every sum of the backward is taken in a fixed order (no atomics): two
+    calls give bit-identical gradients, and the call captured into a HIP graph
+    and replayed several times (the outputs and the workspace scribbled over
+    between replays, with eager work and synchronisation in between) gives
+    the same bits on every replay."""
+    import torch
+    bf = torch.bfloat16
+    cfg = synth.replace(synth.CONFIGS["c1"], batch=2, seqlen=300, nheads=8, ngroups=2)
+    prm = synth.layer_params(cfg, with_bias=True)
+    inp = synth.prefill_inputs(cfg)
+    seeds = synth.backward_seeds(cfg)
+    st = synth.initial_states(cfg)
+    d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
+                    cfg.conv_width, cfg.chunk, bf)
+    args = (dev(inp["xbc"], bf), dev(inp["z"], bf), dev(inp["dt"], bf), dev(prm["A"]),
+            dev(prm["D"]), dev(prm["conv_w"], bf), dev(prm["conv_b"], bf),
+            dev(seeds["norm_w"], bf), dev(seeds["d_out"], bf))
+    kw = dict(eps=prm["eps"], conv_state_in=dev(st["conv_state"], bf),
+              ssm_state_in=dev(st["ssm_state"]),
+              d_ssm_state_out=dev(seeds["d_ssm_state_out"]))
+    ref = {k: host(v) for k, v in ops.ssd_mixer_backward(d, *args, **kw).items()}
+    again = {k: host(v) for k, v in ops.ssd_mixer_backward(d, *args, **kw).items()}
+    for k in ref:
+        assert np.array_equal(again[k], ref[k]), f"d{k} differs between two calls"
+    ws = ops.workspace(ops.ssd_mixer_backward_workspace_bytes(d))
+    grads = ops.ssd_mixer_backward(d, *args, ws=ws, **kw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops.ssd_mixer_backward(d, *args, grads=grads, ws=ws, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.ssd_mixer_backward(d, *args, grads=grads, ws=ws, **kw)
+    for i in range(4):
+        for t in grads.values():
+            t.fill_(float("nan"))
+        ws.fill_(7)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ref:
+            assert np.array_equal(host(grads[k]), ref[k]), f"replay {i}: d{k}"
