@@ -360,7 +360,7 @@ def run_serving(torch, ops, synth, reps, kernel_events=True):
     prefills (lengths drawn from 64..1024 tokens) and 240 decode steps (one
     token each, resuming from their slots), every sequence on its own slot."""
     bf = torch.bfloat16
-    cfg = synth.replace(synth.CONFIGS["c2"], chunk=128)
+    cfg = synth.replace(synth.CONFIGS["large_layer"], chunk=128)
     r = np.random.default_rng(2024)
     lens = np.concatenate([r.integers(64, 1025, 16), np.ones(240, dtype=np.int64)])
     T, nseq, S = int(lens.sum()), len(lens), 512
@@ -430,7 +430,7 @@ def run_backward(torch, ops, synth, reps, kernel_events=True):
     gradient (xBC, z, dt, A, D, conv weight, norm weight) for a seeded
     upstream gradient, the forward recomputed inside the call."""
     bf = torch.bfloat16
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["large_layer"]
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)
     seeds = synth.backward_seeds(cfg)
@@ -572,14 +572,14 @@ def secondary(torch, ops, synth, args, which):
     wl = {}
     ke = not args.no_kernel_events
     if "tiny" in which:
-        c1 = synth.CONFIGS["c1"]
+        c1 = synth.CONFIGS["tiny_layer"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c1, max(10, args.steps), 3, 4, False,
                                         False, ke)
         wl["tiny_layer_prefill"] = dict(summarize_prefill(c1, ms, kern, False, False), status=rc,
                                         config="4 x 2048 tokens, 32 heads x 64, 8 groups, state "
                                                "128, chunk 128, bf16, no states")
     if "chain" in which:
-        c3 = synth.CONFIGS["c3"]
+        c3 = synth.CONFIGS["long_context"]
         ms, kern = run_chain(torch, ops, synth, c3, 3, ke)
         tokens = c3.seqlen * c3.pieces
         nb = prefill_bytes(c3, True, True) * c3.pieces
@@ -592,7 +592,7 @@ def secondary(torch, ops, synth, args, which):
             "config": "16 pieces of 1 x 8192 tokens, 32 heads x 64, 8 groups, state 128, "
                       "each resuming from the previous piece's conv and SSM state"}
     if "decode" in which:
-        c4 = synth.CONFIGS["c4"]
+        c4 = synth.CONFIGS["decode_loop"]
         ms, kern = run_decode(torch, ops, synth, c4, 3, ke)
         b4 = decode_bytes(c4) * c4.steps
         wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms * 1e-3),
@@ -608,7 +608,7 @@ def secondary(torch, ops, synth, args, which):
     if "backward" in which:
         wl["large_layer_backward"] = run_backward(torch, ops, synth, 3, ke)
     if "unpacked" in which:
-        c2 = synth.CONFIGS["c2"]
+        c2 = synth.CONFIGS["large_layer"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
                                         True, ke)
         wl["large_layer_prefill_unpacked"] = dict(
@@ -616,12 +616,12 @@ def secondary(torch, ops, synth, args, which):
             config="the headline layer and inputs with x | B | C, z and dt (already softplus-ed) "
                    "as separate tensors and A given")
     if "general" in which:
-        c0 = synth.CONFIGS["c0"]
+        c0 = synth.CONFIGS["tiny_fp32"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c0, 50, 5, 1, False, False, ke)
         wl["tiny_fp32_layer"] = dict(summarize_prefill(c0, ms, kern, False, False), status=rc,
                                      config="1 x 256 tokens, 4 heads x 16, 1 group, state 16, "
                                             "chunk 64, fp32 (general kernels)")
-        cg = synth.replace(synth.CONFIGS["c1"], dstate=64)
+        cg = synth.replace(synth.CONFIGS["tiny_layer"], dstate=64)
         ms, kern, rc = prefill_workload(torch, ops, synth, cg, 10, 3, 2, False, False, ke)
         wl["general_bf16_prefill"] = dict(summarize_prefill(cg, ms, kern, False, False),
                                           status=rc,
@@ -654,7 +654,7 @@ def main():
     if args.only:
         print(json.dumps(secondary(torch, ops, synth, args, (args.only,))), flush=True)
         return
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["large_layer"]
     ms, kern, rc = prefill_workload(torch, ops, synth, cfg, args.steps, args.warmup, args.sets,
                                     False, True, not args.no_kernel_events, packed=True,
                                     breakdown=not args.quick)

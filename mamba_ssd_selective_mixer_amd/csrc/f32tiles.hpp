@@ -31,18 +31,6 @@ SSD_DEV f32x4 mma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Rows [0, rows) x columns [0, kKS) of a row-major fp32 matrix (row stride
-// rs, elements) into dst [rows][kSP]; rows >= nrows and columns >= ncols
-// (a multiple of 4) are zero.
-SSD_DEV void stage(float* dst, const float* src, int rs, int rows, int nrows, int ncols) {
-  for (int i = threadIdx.x; i < rows * (kKS / 4); i += kThreads) {
-    const int r = i / (kKS / 4), c4 = (i % (kKS / 4)) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nrows && c4 < ncols) v = *reinterpret_cast<const float4*>(src + r * rs + c4);
-    *reinterpret_cast<float4*>(dst + r * kSP + c4) = v;
-  }
-}
-
 // One staged slice (rows [0, ROWS) x columns [0, kKS)) held in registers
 // between its global loads and its LDS stores, so that the next slice's
 // loads are in flight while the current one is computed on.

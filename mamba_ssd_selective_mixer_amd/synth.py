@@ -59,15 +59,15 @@ class Cfg:
 
 CONFIGS = {
     # tiny fp32 layer: batch 1, 256 tokens, 4 heads x 16, 1 group, state 16
-    "c0": Cfg("c0", 0, 1, 256, 4, 16, 1, 16, 4, 64, "f32"),
+    "tiny_fp32": Cfg("tiny_fp32", 0, 1, 256, 4, 16, 1, 16, 4, 64, "f32"),
     # tiny-model layer (32 heads x 64, 8 groups, state 128), bf16 I/O
-    "c1": Cfg("c1", 1, 4, 2048, 32, 64, 8, 128, 4, 128, "bf16"),
+    "tiny_layer": Cfg("tiny_layer", 1, 4, 2048, 32, 64, 8, 128, 4, 128, "bf16"),
     # large-model layer prefill (256 heads x 64, 8 groups, state 128)
-    "c2": Cfg("c2", 2, 1, 8192, 256, 64, 8, 128, 4, 256, "bf16"),
+    "large_layer": Cfg("large_layer", 2, 1, 8192, 256, 64, 8, 128, 4, 256, "bf16"),
     # long context: 16 pieces of 8192 tokens, each resuming from state
-    "c3": Cfg("c3", 3, 1, 8192, 32, 64, 8, 128, 4, 128, "bf16", pieces=16),
+    "long_context": Cfg("long_context", 3, 1, 8192, 32, 64, 8, 128, 4, 128, "bf16", pieces=16),
     # decode: 256 sequences x 64 single-token steps, states ~ N(0, 0.1)
-    "c4": Cfg("c4", 4, 256, 1, 256, 64, 8, 128, 4, 0, "bf16", steps=64,
+    "decode_loop": Cfg("decode_loop", 4, 256, 1, 256, 64, 8, 128, 4, 0, "bf16", steps=64,
               nonzero_init=True),
 }
 

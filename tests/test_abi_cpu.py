@@ -42,9 +42,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_validate_configs(lib):
-    for name, entry in [("c0", 4), ("c1", 4), ("c2", 4), ("c3", 4), ("c1", 1), ("c0", 0)]:
+    for name, entry in [("tiny_fp32", 4), ("tiny_layer", 4), ("large_layer", 4), ("long_context", 4), ("tiny_layer", 1), ("tiny_fp32", 0)]:
         assert lib.ssd_validate(entry, ctypes.byref(dims(synth.CONFIGS[name]))) == 0, name
-    c4 = synth.CONFIGS["c4"]
+    c4 = synth.CONFIGS["decode_loop"]
     assert lib.ssd_validate(3, ctypes.byref(dims(c4, chunk=128))) == 0
 
 
@@ -65,7 +65,7 @@ def test_validate_configs(lib):
     (dict(), 9, -3),
 ])
 def test_validate_errors(lib, kw, entry, rc):
-    assert lib.ssd_validate(entry, ctypes.byref(dims(synth.CONFIGS["c1"], **kw))) == rc
+    assert lib.ssd_validate(entry, ctypes.byref(dims(synth.CONFIGS["tiny_layer"], **kw))) == rc
 
 
 def test_envelope_fits_lds(lib):
@@ -77,7 +77,7 @@ def test_envelope_fits_lds(lib):
             for N in (16, 32, 64, 128, 256):
                 for Q in (32, 64, 128, 256):
                     for flags in (0, _lib.SSD_FLAG_FP32_OPERANDS):
-                        d = dims(synth.CONFIGS["c0"], headdim=P, dstate=N, chunk=Q, io_dtype=io,
+                        d = dims(synth.CONFIGS["tiny_fp32"], headdim=P, dstate=N, chunk=Q, io_dtype=io,
                                  flags=flags)
                         assert lib.ssd_validate(1, ctypes.byref(d)) == 0, (io, P, N, Q, flags)
 
@@ -89,7 +89,7 @@ def test_status_strings(lib):
 
 
 def test_null_and_alignment_checks_return_before_launch(lib):
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     V = ctypes.c_void_p
     # NULL required pointer
     assert lib.ssd_conv1d(ctypes.byref(d), None, 4096, V(4096), None, None, None, V(8192), 4096,
@@ -126,7 +126,7 @@ def test_prefill_decode_norm_refuse_before_launch(lib):
     documented codes, before any launch (addresses are never dereferenced)."""
     V = ctypes.c_void_p
     NULL, SHAPE, ALIAS, WORKSPACE, ALIGN = -1, -2, -5, -6, -8
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
     assert need > 0
     xbc, z, dt, A, D, cw, nw = (V(k << 36) for k in (1, 2, 3, 4, 5, 6, 7))
@@ -150,7 +150,7 @@ def test_prefill_decode_norm_refuse_before_launch(lib):
     assert prefill(ss_out=V((10 << 36) + 64)) == ALIAS   # SSM states partly overlapping
     assert prefill(ws=V((12 << 36) + 256)) == ALIAS      # workspace over the output
 
-    dd = dims(synth.CONFIGS["c4"], seqlen=1)
+    dd = dims(synth.CONFIGS["decode_loop"], seqlen=1)
     st, y = V(14 << 36), V(15 << 36)
 
     def decode(d_=dd, **kw):
@@ -159,7 +159,7 @@ def test_prefill_decode_norm_refuse_before_launch(lib):
         return lib.ssd_decode_step(ctypes.byref(d_), a["x"], a["z"], a["dt"], A, D, cw, None,
                                    a["nw"], 1e-5, a["cs"], a["ss"], a["y"], None)
 
-    assert decode(d_=dims(synth.CONFIGS["c4"], seqlen=2)) == SHAPE
+    assert decode(d_=dims(synth.CONFIGS["decode_loop"], seqlen=2)) == SHAPE
     assert decode(ss=None) == NULL
     assert decode(nw=None) == NULL
     assert decode(y=V((15 << 36) + 4)) == ALIGN
@@ -174,7 +174,7 @@ def test_prefill_decode_norm_refuse_before_launch(lib):
 
 
 def test_workspace_sizes(lib):
-    c1 = synth.CONFIGS["c1"]
+    c1 = synth.CONFIGS["tiny_layer"]
     d = dims(c1)
     ws = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
     nc = c1.seqlen // 128
@@ -194,7 +194,7 @@ def test_workspace_covers_wide_norm_groups(lib):
     the fp16 chunk increments (overwritten in place by the carried-in states),
     the convolved B and C rows the output kernel reads, and the per-row sums
     its blocks exchange."""
-    c2 = synth.CONFIGS["c2"]
+    c2 = synth.CONFIGS["large_layer"]
     d = dims(c2)
     ws = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
     nc = -(-c2.seqlen // 128)
@@ -258,7 +258,7 @@ _PREFILL_TWINS = {"cs_out": "cs_in", "ss_out": "ss_in"}
 @pytest.mark.parametrize("w,o,off", _alias_cases(_PREFILL_BUFS, _PREFILL_W, _PREFILL_TWINS))
 def test_prefill_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
     a = {k: (i + 1) << 36 for i, k in enumerate(_PREFILL_BUFS)}
     a[w] = a[o] + off
@@ -274,7 +274,7 @@ _SCAN_W = ("ss_out", "y", "ws")
 @pytest.mark.parametrize("w,o,off", _alias_cases(_SCAN_BUFS, _SCAN_W, {"ss_out": "ss_in"}))
 def test_chunk_scan_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
     a = {k: (i + 1) << 36 for i, k in enumerate(_SCAN_BUFS)}
     a[w] = a[o] + off
@@ -291,7 +291,7 @@ _DEC_W = ("cs", "ss", "y")
 @pytest.mark.parametrize("w,o,off", _alias_cases(_DEC_BUFS, _DEC_W, {}))
 def test_decode_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c4"], seqlen=1)
+    d = dims(synth.CONFIGS["decode_loop"], seqlen=1)
     a = {k: (i + 1) << 36 for i, k in enumerate(_DEC_BUFS)}
     a[w] = a[o] + off
     rc = lib.ssd_decode_step(ctypes.byref(d), *(V(a[k]) for k in _DEC_BUFS[:8]), 1e-5,
@@ -306,7 +306,7 @@ _CONV_BUFS = ("xbc", "w", "bias", "cs_in", "cs_out", "out")
                                                  {"cs_out": "cs_in"}))
 def test_conv1d_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     a = {k: (i + 1) << 36 for i, k in enumerate(_CONV_BUFS)}
     a[w] = a[o] + off
     rc = lib.ssd_conv1d(ctypes.byref(d), V(a["xbc"]), 4096, V(a["w"]), V(a["bias"]),
@@ -317,7 +317,7 @@ def test_conv1d_alias_every_pair(lib, w, o, off):
 @pytest.mark.parametrize("o", ["z", "w"])
 def test_gated_rmsnorm_alias_every_pair(lib, o):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     a = {"y": 1 << 36, "z": 2 << 36, "w": 3 << 36}
     assert lib.ssd_gated_rmsnorm(ctypes.byref(d), V(a["y"]), V(a["z"]), V(a["w"]), 1e-5,
                                  V(a[o]), None) == _ALIAS
@@ -335,7 +335,7 @@ _PK_W = ("cs_out", "ss_out", "out", "ws")
                                                  {"cs_out": "cs_in", "ss_out": "ss_in"}))
 def test_prefill_packed_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
     a = {k: (i + 1) << 36 for i, k in enumerate(_PK_BUFS)}
     a[w] = a[o] + off
@@ -350,7 +350,7 @@ def test_packed_entries_refuse_before_launch(lib):
     """Row stride narrower than [z | xBC | dt] or breaking the 16-byte rule,
     missing dt_bias / A_log / norm weight: refused before any launch."""
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
     width = 2 * 2048 + 2 * 1024 + 32
     a = [V(k << 36) for k in range(1, 14)]
@@ -367,7 +367,7 @@ def test_packed_entries_refuse_before_launch(lib):
     assert pre(a1=None) == -1                      # dt_bias
     assert pre(a2=None) == -1                      # A_log
     assert pre(a6=None) == -1                      # norm weight
-    dd = dims(synth.CONFIGS["c4"], seqlen=1)
+    dd = dims(synth.CONFIGS["decode_loop"], seqlen=1)
     wdec = 2 * 16384 + 2 * 1024 + 256
     assert lib.ssd_decode_step_packed(ctypes.byref(dd), a[0], wdec - 8, *a[1:7], 1e-5, *a[7:10],
                                       None) == -2
@@ -386,7 +386,7 @@ _VL_W = ("cpool", "spool", "out", "ws")
 @pytest.mark.parametrize("w,o,off", _alias_cases(_VL_BUFS, _VL_W, {}))
 def test_varlen_alias_every_pair(lib, w, o, off):
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"], batch=3, seqlen=500)
+    d = dims(synth.CONFIGS["tiny_layer"], batch=3, seqlen=500)
     need = lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 8)
     a = {k: (i + 1) << 36 for i, k in enumerate(_VL_BUFS)}
     a[w] = a[o] + off
@@ -400,12 +400,12 @@ def test_varlen_envelope_and_refusals(lib):
     """The batched entry runs on the fused kernels only: other shapes, flags
     or a missing pool are refused before any launch."""
     V = ctypes.c_void_p
-    d = dims(synth.CONFIGS["c1"], batch=3, seqlen=500)
+    d = dims(synth.CONFIGS["tiny_layer"], batch=3, seqlen=500)
     assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 8) > 0
     assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(d), 0) == 0
     for bad in (dict(dstate=64), dict(io_dtype=_lib.SSD_F32), dict(flags=1),
                 dict(nheads=288, ngroups=1)):  # 288 heads per norm group: beyond the fused norm
-        dd = dims(synth.CONFIGS["c1"], batch=3, seqlen=500, **bad)
+        dd = dims(synth.CONFIGS["tiny_layer"], batch=3, seqlen=500, **bad)
         assert lib.ssd_mixer_varlen_workspace_bytes(ctypes.byref(dd), 8) == 0, bad
         a = [V(k << 36) for k in range(1, 16)]
         rc = lib.ssd_mixer_varlen(ctypes.byref(dd), a[0], a[1], None, 8, *a[2:10], 1e-5, *a[10:14],
@@ -450,7 +450,7 @@ def _bwd_call(lib, d, a, need):
 
 @pytest.mark.parametrize("w,o,off", _alias_cases(_BWD_BUFS, _BWD_W, {}))
 def test_backward_alias_every_pair(lib, w, o, off):
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
     a = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
     a[w] = a[o] + off
@@ -458,13 +458,13 @@ def test_backward_alias_every_pair(lib, w, o, off):
 
 
 def test_backward_refuses_before_launch(lib):
-    d = dims(synth.CONFIGS["c1"])
+    d = dims(synth.CONFIGS["tiny_layer"])
     need = lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(d))
     # workspace: the status word, fp32 conv output / its gradient, y, chunk
     # states and their gradients (64-token chunks), per-head dB / dC, 1024
     # partial norm-weight gradients, the conv gradients' partial sums per
     # 64-token range, and each chunk's parts of dA and dD
-    cfg = synth.CONFIGS["c1"]
+    cfg = synth.CONFIGS["tiny_layer"]
     T, C, HP = cfg.batch * cfg.seqlen, cfg.channels, cfg.hp
     nc = -(-cfg.seqlen // 64)
     st = cfg.batch * nc * HP * cfg.dstate * 4

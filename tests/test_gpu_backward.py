@@ -108,13 +108,13 @@ CASES = [
 
 @pytest.mark.parametrize("name,shape,opts", CASES, ids=[c[0] for c in CASES])
 def test_backward_f32(ops, name, shape, opts):
-    cfg = synth.replace(synth.CONFIGS["c0"], **shape)
+    cfg = synth.replace(synth.CONFIGS["tiny_fp32"], **shape)
     run_case(ops, cfg, **opts)
 
 
 def test_backward_bf16_layer_shape(ops):
     """bf16 I/O at the layer's head size (64 x 128 state, 8 heads, 2 groups)."""
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=1, seqlen=160, nheads=8, ngroups=2)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=160, nheads=8, ngroups=2)
     run_case(ops, cfg)
 
 
@@ -124,7 +124,7 @@ def test_backward_state_grad_chains(ops):
     the gradient of the whole sequence (checked against the oracle on the
     joined sequence)."""
     import torch
-    cfg = synth.replace(synth.CONFIGS["c0"], batch=1, seqlen=192, nheads=4, headdim=16,
+    cfg = synth.replace(synth.CONFIGS["tiny_fp32"], batch=1, seqlen=192, nheads=4, headdim=16,
                         ngroups=2, dstate=16)
     td = torch.float32
     H, P, G, N, W = cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, cfg.conv_width
@@ -167,7 +167,7 @@ def test_backward_state_grad_chains(ops):
 
 def test_backward_rejects(ops):
     import torch
-    cfg = synth.replace(synth.CONFIGS["c0"], batch=1, seqlen=8)
+    cfg = synth.replace(synth.CONFIGS["tiny_fp32"], batch=1, seqlen=8)
     d = ops.SSDDims(1, 8, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 64,
                     torch.float32)
     t = lambda *s: torch.zeros(*s, device="cuda")
@@ -188,7 +188,7 @@ def test_backward_deterministic_and_graph_replay(ops):
     the same bits on every replay."""
     import torch
     bf = torch.bfloat16
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=2, seqlen=300, nheads=8, ngroups=2)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=2, seqlen=300, nheads=8, ngroups=2)
     prm = synth.layer_params(cfg, with_bias=True)
     inp = synth.prefill_inputs(cfg)
     seeds = synth.backward_seeds(cfg)

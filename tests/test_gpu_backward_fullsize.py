@@ -28,7 +28,7 @@ def env():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from mamba_ssd_selective_mixer_amd import ops
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["large_layer"]
     f32 = torch.float32
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)

@@ -49,7 +49,7 @@ def group_problem(cfg, g, xbc, z, dt, prm, conv_state=None, ssm_state=None):
 def test_tiny_model_layer_prefill_full(env):
     """4 x 2048 tokens, 32 heads x 64, 8 groups, state 128: every output."""
     torch, ops = env
-    cfg = synth.CONFIGS["c1"]
+    cfg = synth.CONFIGS["tiny_layer"]
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     bf = torch.bfloat16
     out = ops.ssd_mixer_prefill(dims(ops, torch, cfg), dev(inp["xbc"], bf), dev(inp["z"], bf),
@@ -65,7 +65,7 @@ def test_large_layer_prefill_full(env):
     """1 x 8192 tokens, 256 heads x 64 (32 heads per norm group), chunk 256,
     final conv and SSM state returned; groups 0 and 7 checked exactly."""
     torch, ops = env
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["large_layer"]
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     bf = torch.bfloat16
     cs = torch.empty(1, cfg.conv_width - 1, cfg.channels, dtype=bf, device="cuda")
@@ -92,7 +92,7 @@ def test_long_context_chain_full(env):
     previous piece's states, against ONE single-shot fp64 run over all the
     tokens (groups 0 and 5)."""
     torch, ops = env
-    cfg = synth.CONFIGS["c3"]
+    cfg = synth.CONFIGS["long_context"]
     prm = synth.layer_params(cfg)
     bf = torch.bfloat16
     d = dims(ops, torch, cfg)
@@ -133,7 +133,7 @@ def test_decode_loop_full(env):
     updated in place. Sequences 0, 77 and 255 are followed step by step by
     the fp64 decode."""
     torch, ops = env
-    cfg = synth.CONFIGS["c4"]
+    cfg = synth.CONFIGS["decode_loop"]
     prm = synth.layer_params(cfg)
     st = synth.initial_states(cfg)
     bf = torch.bfloat16
@@ -164,7 +164,7 @@ def test_prefill_many_sequences(env):
     blocks per group in 8 ticket partitions. Sampled sequences, outputs and
     final states, against the fp64 oracle on those sequences alone."""
     torch, ops = env
-    cfg = synth.replace(synth.CONFIGS["c2"], batch=1024, seqlen=5)
+    cfg = synth.replace(synth.CONFIGS["large_layer"], batch=1024, seqlen=5)
     assert cfg.batch * cfg.nheads // 4 > 65535
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     bf = torch.bfloat16

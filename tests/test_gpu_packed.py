@@ -73,11 +73,11 @@ def packed_case(ops, cfg, pad=8, with_state=True, pieces=None, slow=False, with_
     (dict(batch=1, seqlen=130, headdim=32, dstate=256, nheads=8, ngroups=2), 8),
 ])
 def test_prefill_packed_bf16(ops, kw, pad):
-    packed_case(ops, synth.replace(synth.CONFIGS["c1"], **kw), pad=pad)
+    packed_case(ops, synth.replace(synth.CONFIGS["tiny_layer"], **kw), pad=pad)
 
 
 def test_prefill_packed_fp32_tiny(ops):
-    packed_case(ops, synth.CONFIGS["c0"], pad=4)
+    packed_case(ops, synth.CONFIGS["tiny_fp32"], pad=4)
 
 
 @pytest.mark.parametrize("flags", [1, pytest.param(0, marks=pytest.mark.xfail(strict=True, reason=(
@@ -87,12 +87,12 @@ def test_prefill_packed_bias_slow_pieces(ops, flags):
     """Conv bias, slow decay (A_log from U(log 0.005, log 0.05)) and uneven
     pieces (one shorter than the conv window) chained through both states;
     with fp32 MFMA operands (general kernels) and on the fused path."""
-    packed_case(ops, synth.replace(synth.CONFIGS["c3"], seqlen=600), pieces=[2, 130, 257],
+    packed_case(ops, synth.replace(synth.CONFIGS["long_context"], seqlen=600), pieces=[2, 130, 257],
                 slow=True, with_bias=True, flags=flags)
 
 
-@pytest.mark.parametrize("base,kw,pad", [("c4", dict(batch=4), 8), ("c0", dict(batch=3), 4),
-                                         ("c4", dict(batch=2, nheads=32, dstate=64,
+@pytest.mark.parametrize("base,kw,pad", [("decode_loop", dict(batch=4), 8), ("tiny_fp32", dict(batch=3), 4),
+                                         ("decode_loop", dict(batch=2, nheads=32, dstate=64,
                                                      conv_width=3), 0)])
 def test_decode_packed(ops, base, kw, pad):
     cfg = synth.replace(synth.CONFIGS[base], **kw)
@@ -124,7 +124,7 @@ def test_large_layer_prefill_packed_full(ops):
     the benchmark's launch configuration; groups 0 and 7 against the oracle's
     packed prefill of that group's columns alone."""
     import torch
-    cfg = synth.CONFIGS["c2"]
+    cfg = synth.CONFIGS["large_layer"]
     prm = synth.packed_params(cfg)
     rows = synth.packed_prefill_inputs(cfg)
     bf = torch.bfloat16

@@ -34,12 +34,12 @@ def small(name, **kw):
 
 # --------------------------------------------------------------------- conv
 @pytest.mark.parametrize("name,kw,with_state,with_bias", [
-    ("c0", {}, False, False),
-    ("c0", {}, True, True),
-    ("c1", dict(batch=2, seqlen=77), True, False),
-    ("c1", dict(batch=3, seqlen=2), True, True),      # shorter than W-1
-    ("c1", dict(batch=1, seqlen=1, conv_width=2), True, False),
-    ("c2", dict(seqlen=40, conv_width=3), False, True),
+    ("tiny_fp32", {}, False, False),
+    ("tiny_fp32", {}, True, True),
+    ("tiny_layer", dict(batch=2, seqlen=77), True, False),
+    ("tiny_layer", dict(batch=3, seqlen=2), True, True),      # shorter than W-1
+    ("tiny_layer", dict(batch=1, seqlen=1, conv_width=2), True, False),
+    ("large_layer", dict(seqlen=40, conv_width=3), False, True),
 ])
 def test_conv1d(ops, name, kw, with_state, with_bias):
     import torch
@@ -58,7 +58,7 @@ def test_conv1d(ops, name, kw, with_state, with_bias):
 
 
 def test_conv1d_state_in_place(ops):
-    cfg = small("c1", batch=2, seqlen=2)
+    cfg = small("tiny_layer", batch=2, seqlen=2)
     d = make_dims(ops, cfg)
     td = torch_dtype(cfg.dtype)
     prm = synth.layer_params(cfg)
@@ -72,7 +72,7 @@ def test_conv1d_state_in_place(ops):
 
 def test_conv1d_strided_views(ops):
     import torch
-    cfg = small("c1", batch=2, seqlen=33)
+    cfg = small("tiny_layer", batch=2, seqlen=33)
     d = make_dims(ops, cfg)
     td = torch_dtype(cfg.dtype)
     prm = synth.layer_params(cfg)
@@ -132,13 +132,13 @@ def scan_case(ops, cfg, with_state, with_norm, slow=False, Q=None):
 @pytest.mark.parametrize("with_state", [False, True])
 @pytest.mark.parametrize("with_norm", [False, True])
 def test_chunk_scan_fp32_tiny(ops, with_state, with_norm):
-    scan_case(ops, synth.CONFIGS["c0"], with_state, with_norm)
+    scan_case(ops, synth.CONFIGS["tiny_fp32"], with_state, with_norm)
 
 
 @pytest.mark.parametrize("kw", [dict(batch=2, seqlen=300), dict(batch=1, seqlen=128),
                                 dict(batch=1, seqlen=1), dict(batch=2, seqlen=17)])
 def test_chunk_scan_bf16(ops, kw):
-    scan_case(ops, small("c1", **kw), True, True)
+    scan_case(ops, small("tiny_layer", **kw), True, True)
 
 
 @pytest.mark.parametrize("Q", [32, 64, 128, 256])
@@ -149,10 +149,10 @@ def test_chunk_scan_chunk_invariance(ops, Q, dstate, dtype):
     I/O with d_state 64, and fp32 I/O (1e-4) with the layer's d_state 128 and
     with 16. (bf16 I/O at head_dim 64 / d_state 128 takes the fused path,
     whose chunk length is fixed at 128 tokens.)"""
-    scan_case(ops, small("c1", batch=1, seqlen=520, dstate=dstate, dtype=dtype), True, False, Q=Q)
+    scan_case(ops, small("tiny_layer", batch=1, seqlen=520, dstate=dstate, dtype=dtype), True, False, Q=Q)
 
 
-@pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=1, seqlen=700))])
+@pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("tiny_layer", dict(batch=1, seqlen=700))])
 def test_chunk_scan_slow_decay(ops, name, kw):
     """Slow decay: the state carries signal across many chunks, so a broken
     inter-chunk state passing cannot hide behind fast forgetting."""
@@ -160,7 +160,7 @@ def test_chunk_scan_slow_decay(ops, name, kw):
 
 
 def test_chunk_scan_large_heads_group(ops):
-    scan_case(ops, small("c2", seqlen=300), True, True)
+    scan_case(ops, small("large_layer", seqlen=300), True, True)
 
 
 @pytest.mark.parametrize("Q,with_norm", [(64, True), (32, False), (128, True)])
@@ -168,7 +168,7 @@ def test_chunk_scan_bf16_small_state(ops, Q, with_norm):
     """d_state 16 with bf16 operands (generic kernels): the C.B^T and C.S_in
     contractions run 32 deep, so the k-slices past d_state must read nothing
     and count as zero."""
-    scan_case(ops, small("c1", nheads=2, ngroups=1, headdim=32, dstate=16, batch=1, seqlen=100),
+    scan_case(ops, small("tiny_layer", nheads=2, ngroups=1, headdim=32, dstate=16, batch=1, seqlen=100),
               True, with_norm, Q=Q)
 
 
@@ -177,7 +177,7 @@ def test_chunk_scan_bf16_generic_norm(ops):
     of 128 channels whose RMS is small: the norm amplifies the scan's operand
     rounding, which stays inside the tolerance with fp16 MFMA operands (bf16
     operands reached 1.7x the tolerance on this case)."""
-    scan_case(ops, small("c1", nheads=4, ngroups=2, headdim=64, dstate=16, batch=1, seqlen=257),
+    scan_case(ops, small("tiny_layer", nheads=4, ngroups=2, headdim=64, dstate=16, batch=1, seqlen=257),
               True, True, Q=128)
 
 
@@ -187,12 +187,12 @@ def test_prefill_generic_bias_normed(ops, P, N, W):
     bias shifts B and C by a shared offset whose C.B products cancel, and the
     norm amplifies what remains, so the conv output must not be rounded to
     bf16 between the conv and the scan (it reached 1.1-2.5x the tolerance)."""
-    prefill_case(ops, small("c1", nheads=64, ngroups=8, headdim=P, dstate=N, conv_width=W,
+    prefill_case(ops, small("tiny_layer", nheads=64, ngroups=8, headdim=P, dstate=N, conv_width=W,
                             batch=1, seqlen=129), with_state=False, with_bias=True)
 
 
 def test_prefill_bf16_small_state(ops):
-    prefill_case(ops, small("c1", nheads=4, ngroups=1, headdim=32, dstate=16, batch=2,
+    prefill_case(ops, small("tiny_layer", nheads=4, ngroups=1, headdim=32, dstate=16, batch=2,
                             seqlen=100), with_state=True)
 
 
@@ -202,7 +202,7 @@ def test_chunk_scan_strided_views(ops, kw):
     """x, B and C passed as strided views into one padded xBC tensor (token
     stride > row width), the way a caller hands over slices of a projection."""
     import torch
-    cfg = small("c1", **kw)
+    cfg = small("tiny_layer", **kw)
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)
@@ -225,13 +225,13 @@ def test_chunk_scan_strided_views(ops, kw):
 
 
 def test_chunk_scan_fp32_shapes(ops):
-    scan_case(ops, small("c0", nheads=8, headdim=32, ngroups=2, dstate=64, seqlen=130,
+    scan_case(ops, small("tiny_fp32", nheads=8, headdim=32, ngroups=2, dstate=64, seqlen=130,
                          batch=2), True, True)
 
 
 def test_chunk_scan_state_in_place(ops):
     import torch
-    cfg = small("c1", batch=2, seqlen=150)
+    cfg = small("tiny_layer", batch=2, seqlen=150)
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)
@@ -274,21 +274,21 @@ def decode_case(ops, cfg, steps, with_norm=True, with_bias=False):
 
 
 def test_decode_fp32_tiny(ops):
-    decode_case(ops, synth.replace(synth.CONFIGS["c0"], batch=3), steps=5)
+    decode_case(ops, synth.replace(synth.CONFIGS["tiny_fp32"], batch=3), steps=5)
 
 
 def test_decode_fp32_no_norm(ops):
-    decode_case(ops, synth.replace(synth.CONFIGS["c0"], batch=2), steps=2, with_norm=False)
+    decode_case(ops, synth.replace(synth.CONFIGS["tiny_fp32"], batch=2), steps=2, with_norm=False)
 
 
 # Decode with a conv bias: fp32 tiny shapes and bf16 shapes of the decode
 # loop's layer (256 heads in 8 groups, state 128), gate on and off.
 @pytest.mark.parametrize("base,kw,norm", [
-    ("c0", dict(batch=3), True),
-    ("c0", dict(batch=2, nheads=8, ngroups=2, headdim=32, dstate=64, conv_width=3), False),
-    ("c4", dict(batch=4), True),
-    ("c4", dict(batch=3), False),
-    ("c4", dict(batch=2, nheads=32, dstate=64, conv_width=2), True)])
+    ("tiny_fp32", dict(batch=3), True),
+    ("tiny_fp32", dict(batch=2, nheads=8, ngroups=2, headdim=32, dstate=64, conv_width=3), False),
+    ("decode_loop", dict(batch=4), True),
+    ("decode_loop", dict(batch=3), False),
+    ("decode_loop", dict(batch=2, nheads=32, dstate=64, conv_width=2), True)])
 def test_decode_conv_bias(ops, base, kw, norm):
     decode_case(ops, synth.replace(synth.CONFIGS[base], **kw), steps=4, with_norm=norm,
                 with_bias=True)
@@ -298,16 +298,16 @@ def test_decode_conv_bias(ops, base, kw, norm):
                                 dict(batch=2, nheads=16, ngroups=4, headdim=32, dstate=16,
                                      conv_width=3)])
 def test_decode_bf16(ops, kw):
-    decode_case(ops, synth.replace(synth.CONFIGS["c4"], **kw), steps=3)
+    decode_case(ops, synth.replace(synth.CONFIGS["decode_loop"], **kw), steps=3)
 
 
 # Decode shapes across the envelope (head_dim, d_state, conv width, heads per
 # group, I/O type, gate on or off), each stepped three times.
 @pytest.mark.parametrize("base,kw,norm", [
-    ("c4", dict(batch=3, nheads=8, ngroups=1, headdim=128, dstate=128, conv_width=2), True),
-    ("c4", dict(batch=5, nheads=4, ngroups=4, headdim=16, dstate=32, conv_width=3), True),
-    ("c0", dict(batch=2, nheads=8, ngroups=2, headdim=64, dstate=16), True),
-    ("c4", dict(batch=2, nheads=16, ngroups=8, headdim=32, dstate=64, conv_width=2), False)])
+    ("decode_loop", dict(batch=3, nheads=8, ngroups=1, headdim=128, dstate=128, conv_width=2), True),
+    ("decode_loop", dict(batch=5, nheads=4, ngroups=4, headdim=16, dstate=32, conv_width=3), True),
+    ("tiny_fp32", dict(batch=2, nheads=8, ngroups=2, headdim=64, dstate=16), True),
+    ("decode_loop", dict(batch=2, nheads=16, ngroups=8, headdim=32, dstate=64, conv_width=2), False)])
 def test_decode_envelope(ops, base, kw, norm):
     decode_case(ops, synth.replace(synth.CONFIGS[base], **kw), steps=3, with_norm=norm)
 
@@ -354,22 +354,22 @@ def prefill_case(ops, cfg, with_state, pieces=None, slow=False, with_bias=False,
 
 
 def test_prefill_fp32_tiny(ops):
-    prefill_case(ops, synth.CONFIGS["c0"], with_state=False)
+    prefill_case(ops, synth.CONFIGS["tiny_fp32"], with_state=False)
 
 
 def test_prefill_fp32_tiny_state_bias(ops):
-    prefill_case(ops, synth.CONFIGS["c0"], with_state=True, with_bias=True)
+    prefill_case(ops, synth.CONFIGS["tiny_fp32"], with_state=True, with_bias=True)
 
 
 def test_prefill_bf16(ops):
-    prefill_case(ops, small("c1", batch=2, seqlen=400), with_state=True)
+    prefill_case(ops, small("tiny_layer", batch=2, seqlen=400), with_state=True)
 
 
 @pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333),   # 8 heads per group
                                 dict(batch=3, seqlen=129),
                                 dict(batch=1, seqlen=5, nheads=16, ngroups=4)])
 def test_prefill_bf16_shapes(ops, kw):
-    prefill_case(ops, small("c1", **kw), with_state=True)
+    prefill_case(ops, small("tiny_layer", **kw), with_state=True)
 
 
 @pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333), dict(batch=3, seqlen=129)])
@@ -378,14 +378,14 @@ def test_prefill_bf16_conv_bias(ops, kw):
     every element of y within 2e-2 + 2e-2 |ref|. The bias shifts B and C by a
     shared offset, so C.B^T sums of O(16) partly cancel; the fp16 operands and
     the fp32 conv intermediate keep that within the tolerance."""
-    prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=False)
+    prefill_case(ops, small("tiny_layer", **kw), with_state=True, with_bias=True, with_norm=False)
 
 
 @pytest.mark.parametrize("kw", [dict(nheads=64, batch=1, seqlen=333), dict(batch=3, seqlen=129)])
 def test_prefill_bf16_conv_bias_normed(ops, kw):
     """Conv bias with the gated norm, every output element within 2e-2 (the
     fp16 MFMA operands keep the shared-offset C.B^T sums precise enough)."""
-    prefill_case(ops, small("c1", **kw), with_state=True, with_bias=True, with_norm=True)
+    prefill_case(ops, small("tiny_layer", **kw), with_state=True, with_bias=True, with_norm=True)
 
 
 FP16_ILL_CONDITIONED = pytest.mark.xfail(strict=True, reason=(
@@ -411,24 +411,24 @@ def test_prefill_bias_slow_decay(ops, kw, pieces, flags):
     default flags, every element is within 2e-2. The fused path's fp16
     operands are expected to miss the tolerance on these inputs (a documented
     limit, checked so that a change in either direction is seen)."""
-    prefill_case(ops, small("c1", **kw), with_state=True, pieces=pieces, slow=True,
+    prefill_case(ops, small("tiny_layer", **kw), with_state=True, pieces=pieces, slow=True,
                  with_bias=True, flags=flags)
 
 
-@pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=2, seqlen=300))])
+@pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("tiny_layer", dict(batch=2, seqlen=300))])
 def test_prefill_no_decay(ops, name, kw):
     """A = 0: no forgetting, the scan is a running sum over the whole
     sequence (states carried across every chunk and the initial state)."""
     prefill_case(ops, small(name, **kw), with_state=True, A=0.0)
 
 
-@pytest.mark.parametrize("name,kw", [("c0", {}), ("c1", dict(batch=2, seqlen=300))])
+@pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("tiny_layer", dict(batch=2, seqlen=300))])
 def test_prefill_memoryless(ops, name, kw):
     """A = -1e4: every decay underflows to 0, y_t = dt_t (C_t . B_t) x_t + D x_t."""
     prefill_case(ops, small(name, **kw), with_state=True, A=-1e4)
 
 
-@pytest.mark.parametrize("name,L", [("c0", 1), ("c1", 1), ("c1", 2), ("c1", 129)])
+@pytest.mark.parametrize("name,L", [("tiny_fp32", 1), ("tiny_layer", 1), ("tiny_layer", 2), ("tiny_layer", 129)])
 def test_prefill_short(ops, name, L):
     """One- and two-token calls (shorter than the conv window) and a chunk
     plus one token, resuming from nonzero conv and SSM states."""
@@ -443,7 +443,7 @@ def test_prefill_grouped_heads(ops, kw, pieces):
     C rows once for the output kernel's two 4-head blocks: several sequences
     (per-sequence row indexing), calls shorter than the conv window (conv
     state rows feed the stored C), and pieces chained through both states."""
-    prefill_case(ops, small("c1", nheads=64, **kw), with_state=True, pieces=pieces)
+    prefill_case(ops, small("tiny_layer", nheads=64, **kw), with_state=True, pieces=pieces)
 
 
 @pytest.mark.parametrize("kw", [
@@ -457,12 +457,12 @@ def test_prefill_norm_across_blocks(ops, kw):
     publishes its per-token sums of squares and gathers its partners', with
     the tickets split over 8 partitions (group count a multiple of 8) or not;
     beyond 32 blocks per group the norm runs after the scan instead."""
-    prefill_case(ops, small("c1", **kw), with_state=True)
+    prefill_case(ops, small("tiny_layer", **kw), with_state=True)
 
 
 def test_chunk_scan_norm_across_blocks(ops):
     """The same exchange in the chunk-scan entry point (no conv), one partition."""
-    scan_case(ops, small("c1", nheads=32, ngroups=1, batch=1, seqlen=300), True, True)
+    scan_case(ops, small("tiny_layer", nheads=32, ngroups=1, batch=1, seqlen=300), True, True)
 
 
 # Fast-path shapes from a seeded sweep (random.Random(7) and (11) over heads
@@ -476,7 +476,7 @@ def test_chunk_scan_norm_across_blocks(ops):
     (4, 1, 1, 128, False, False), (4, 1, 3, 300, True, False), (64, 2, 3, 128, True, False),
     (64, 8, 3, 256, True, False), (8, 2, 3, 64, True, False)])
 def test_prefill_fast_path_shapes(ops, H, G, B, L, st, bias):
-    prefill_case(ops, small("c1", nheads=H, ngroups=G, batch=B, seqlen=L), with_state=st,
+    prefill_case(ops, small("tiny_layer", nheads=H, ngroups=G, batch=B, seqlen=L), with_state=st,
                  with_bias=bias)
 
 
@@ -485,12 +485,12 @@ def test_prefill_fast_path_shapes(ops, H, G, B, L, st, bias):
 # kernel with one wave per state row.
 @pytest.mark.parametrize("P,io", [(64, "bf16"), (128, "bf16"), (32, "f32")])
 def test_prefill_dstate256(ops, P, io):
-    prefill_case(ops, small("c1", nheads=8, ngroups=2, headdim=P, dstate=256, batch=2,
+    prefill_case(ops, small("tiny_layer", nheads=8, ngroups=2, headdim=P, dstate=256, batch=2,
                             seqlen=200, dtype=io), with_state=True)
 
 
 def test_chunk_scan_dstate256_fp32(ops):
-    scan_case(ops, small("c0", nheads=4, headdim=64, ngroups=1, dstate=256, seqlen=150,
+    scan_case(ops, small("tiny_fp32", nheads=4, headdim=64, ngroups=1, dstate=256, seqlen=150,
                          batch=2), True, True)
 
 
@@ -498,22 +498,22 @@ def test_chunk_scan_dstate256_fp32(ops):
                                 dict(batch=2, nheads=4, ngroups=1, headdim=128, dstate=256,
                                      conv_width=2)])
 def test_decode_dstate256(ops, kw):
-    decode_case(ops, synth.replace(synth.CONFIGS["c4"], **kw), steps=3)
+    decode_case(ops, synth.replace(synth.CONFIGS["decode_loop"], **kw), steps=3)
 
 
 def test_prefill_generic_shapes(ops):
     """Shapes outside the fast path (d_state 64, head_dim 32) on the generic kernels."""
-    prefill_case(ops, small("c1", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
+    prefill_case(ops, small("tiny_layer", batch=2, seqlen=300, dstate=64, headdim=32), with_state=True)
 
 
 def test_prefill_pieces_uneven(ops):
     """Piecewise == single shot, including pieces shorter than W-1."""
-    prefill_case(ops, small("c3", seqlen=600), with_state=True, pieces=[1, 3, 130, 256, 257],
+    prefill_case(ops, small("long_context", seqlen=600), with_state=True, pieces=[1, 3, 130, 256, 257],
                  slow=True)
 
 
 def test_prefill_pieces_in_place(ops):
-    prefill_case(ops, small("c3", seqlen=300), with_state=True, pieces=[2, 128], inplace=True)
+    prefill_case(ops, small("long_context", seqlen=300), with_state=True, pieces=[2, 128], inplace=True)
 
 
 def test_concurrent_streams(ops):
@@ -524,7 +524,7 @@ def test_concurrent_streams(ops):
     import torch
     bf = torch.bfloat16
     cases = []
-    for cfg in (small("c1", batch=2, seqlen=300), small("c1", nheads=64, ngroups=2, batch=2,
+    for cfg in (small("tiny_layer", batch=2, seqlen=300), small("tiny_layer", nheads=64, ngroups=2, batch=2,
                                                          seqlen=300)):
         d = make_dims(ops, cfg)
         prm = synth.layer_params(cfg)
@@ -557,7 +557,7 @@ def test_graph_replay(ops, kw):
     tickets and slots, is reset by a kernel, not a memset)."""
     import torch
     bf = torch.bfloat16
-    cfg = small("c1", **kw)
+    cfg = small("tiny_layer", **kw)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg)
@@ -585,7 +585,7 @@ def test_graph_replay(ops, kw):
 
 def test_causality_gpu(ops):
     """Perturbing token t leaves every earlier output of the GPU path unchanged."""
-    cfg = small("c1", batch=1, seqlen=256)
+    cfg = small("tiny_layer", batch=1, seqlen=256)
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)
@@ -610,7 +610,7 @@ def test_determinism(ops, kw):
     the second shape normalises across 8 blocks per group, whose tickets (and
     so the order in which partners finish) change from run to run."""
     import torch
-    cfg = small("c1", **kw)
+    cfg = small("tiny_layer", **kw)
     td = torch_dtype(cfg.dtype)
     d = make_dims(ops, cfg)
     prm = synth.layer_params(cfg)

@@ -52,7 +52,7 @@ def test_exchange_timeout_is_reported(ops):
     a poll bound of 0 every wait gives up at once, the rows are NaN and the
     call reports SSD_ERR_TIMEOUT; with the bound restored the same workspace
     reports SSD_OK and the output matches the oracle."""
-    cfg = synth.replace(synth.CONFIGS["c1"], nheads=64, ngroups=8, batch=1, seqlen=300)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], nheads=64, ngroups=8, batch=1, seqlen=300)
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     prev = ops.ssd_set_exchange_spin_limit(0)
     try:
@@ -71,7 +71,7 @@ def test_exchange_timeout_is_reported(ops):
                                       (dict(batch=2, seqlen=300), 1),        # fp32 operands
                                       (dict(batch=1, seqlen=200, dstate=64), 0)])  # general
 def test_nonfinite_input_is_reported(ops, kw, flags):
-    cfg = synth.replace(synth.CONFIGS["c1"], **kw)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], **kw)
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     out, so, rc = run(ops, cfg, prm, inp, flags)
     assert rc == 0
@@ -87,7 +87,7 @@ def test_nonfinite_input_is_reported(ops, kw, flags):
 def test_fp32_operands_parity(ops, kw):
     """SSD_FLAG_FP32_OPERANDS on bf16 I/O (general kernels, fp32 MFMA
     operands): elementwise parity at the bf16 tolerance, final state too."""
-    cfg = synth.replace(synth.CONFIGS["c1"], **kw)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], **kw)
     prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
     st = synth.initial_states(cfg)["ssm_state"]
     out, so, rc = run(ops, cfg, prm, inp, flags=1, st=st)
@@ -105,7 +105,7 @@ def test_large_activations(ops):
     The fused path either stays within tolerance or reports
     SSD_ERR_NONFINITE; with SSD_FLAG_FP32_OPERANDS the call is within
     tolerance elementwise, output and final state."""
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=1, seqlen=700)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=700)
     prm = synth.layer_params(cfg, slow_decay=True)
     inp = synth.prefill_inputs(cfg)
     inp = dict(inp, xbc=inp["xbc"] * np.float32(256.0))

@@ -69,7 +69,7 @@ def test_mixed_prefill_and_decode(ops, kw):
     """Prefills of 300, 129, 64 and 2 tokens, three one-token decode steps
     and an empty sequence, on shuffled slots of a pool of 11 (two sequences
     fresh); norm within one block, across 8 blocks, and across 2 blocks."""
-    cfg = synth.replace(synth.CONFIGS["c1"], **kw)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], **kw)
     lens = [300, 1, 129, 0, 2, 1, 64, 1]
     slots = [7, 0, 3, 9, 10, 5, 1, 4]
     has = [1, 1, 0, 1, 1, 0, 1, 1]
@@ -79,7 +79,7 @@ def test_mixed_prefill_and_decode(ops, kw):
 def test_decode_only_batch(ops):
     """64 one-token sequences on a pool of 96 (a decode step of the serving
     engine through the batched entry), large-layer head count."""
-    cfg = synth.replace(synth.CONFIGS["c4"], chunk=128)
+    cfg = synth.replace(synth.CONFIGS["decode_loop"], chunk=128)
     r = np.random.default_rng(5)
     slots = r.permutation(96)[:64].tolist()
     batch_case(ops, cfg, [1] * 64, slots, None, S=96)
@@ -90,7 +90,7 @@ def test_single_sequence_matches_prefill_entry(ops):
     output and states bit for bit (same kernels, same chunks)."""
     import torch
     bf = torch.bfloat16
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=1, seqlen=700)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=700)
     out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, [700], [2], [1], S=3)
     prm = synth.layer_params(cfg)
     inp = synth.prefill_inputs(cfg, batch=1, seqlen=700)
@@ -111,7 +111,7 @@ def test_one_token_sequences_match_decode_entry(ops, fresh):
     resuming from their slots or starting fresh (zero states)."""
     import torch
     bf = torch.bfloat16
-    cfg = synth.replace(synth.CONFIGS["c1"], chunk=128)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], chunk=128)
     lens, slots = [1, 200, 1], [4, 0, 2]
     has = [0 if fresh else 1, 1, 0 if fresh else 1]
     out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, lens, slots, has, S=5)
@@ -139,7 +139,7 @@ def test_one_token_sequences_match_decode_entry(ops, fresh):
     ([5, 3], [-1, 2], 4),     # negative slot
 ])
 def test_invalid_slots_refused(ops, lens, slots, S):
-    cfg = synth.replace(synth.CONFIGS["c1"])
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"])
     out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, lens, slots, None, S=S,
                                                 check_ref=False)
     assert rc == VARLEN
@@ -151,7 +151,7 @@ def test_invalid_offsets_refused(ops):
     """cu_seqlens that do not end at the call's token count, or decrease."""
     import torch
     bf = torch.bfloat16
-    cfg = synth.CONFIGS["c1"]
+    cfg = synth.CONFIGS["tiny_layer"]
     T, S = 12, 4
     d = ops.SSDDims(2, T, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 128, bf)
     prm = synth.layer_params(cfg)

@@ -14,7 +14,7 @@ def test_round_bf16_ties_to_even():
 
 
 def test_deterministic_and_shaped():
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=2, seqlen=33)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=2, seqlen=33)
     a = synth.prefill_inputs(cfg)
     b = synth.prefill_inputs(cfg)
     for k in a:
@@ -29,17 +29,17 @@ def test_deterministic_and_shaped():
 
 
 def test_streams_differ_and_pieces_concatenate():
-    cfg = synth.replace(synth.CONFIGS["c3"], seqlen=16)
+    cfg = synth.replace(synth.CONFIGS["long_context"], seqlen=16)
     p0 = synth.prefill_inputs(cfg, piece=0)
     p1 = synth.prefill_inputs(cfg, piece=1)
     assert not np.array_equal(p0["xbc"], p1["xbc"])
-    st = synth.initial_states(synth.replace(synth.CONFIGS["c4"], batch=3))
+    st = synth.initial_states(synth.replace(synth.CONFIGS["decode_loop"], batch=3))
     assert st["conv_state"].shape == (3, 3, 18432) and st["ssm_state"].shape == (3, 256, 64, 128)
     assert abs(float(st["ssm_state"].std()) - np.sqrt(0.1)) < 0.01
 
 
 def test_distributions():
-    cfg = synth.replace(synth.CONFIGS["c1"], batch=1, seqlen=512)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=512)
     t = synth.prefill_inputs(cfg, dtype="f32")
     x, Bm, Cm = synth.split_channels(cfg, t["xbc"])
     assert abs(x.std() - 1.0) < 0.02

@@ -58,8 +58,8 @@ def both(ops, cfg):
     (dict(batch=2, seqlen=300, dstate=64), dict(batch=1, seqlen=77, dstate=64)),  # general
 ])
 def test_noalloc_matches_workspace_entry(ops, first, second):
-    both(ops, synth.replace(synth.CONFIGS["c1"], **first))
-    both(ops, synth.replace(synth.CONFIGS["c1"], **second))
+    both(ops, synth.replace(synth.CONFIGS["tiny_layer"], **first))
+    both(ops, synth.replace(synth.CONFIGS["tiny_layer"], **second))
 
 
 def test_noalloc_refuses_beyond_scratch(ops):
@@ -67,7 +67,7 @@ def test_noalloc_refuses_beyond_scratch(ops):
     than the fixed buffer: refused on the host, nothing launched."""
     import ctypes
     from mamba_ssd_selective_mixer_amd import _lib
-    c2 = synth.CONFIGS["c2"]
+    c2 = synth.CONFIGS["large_layer"]
     d = _lib.Dims(c2.batch, c2.seqlen, c2.nheads, c2.headdim, c2.ngroups, c2.dstate,
                   c2.conv_width, c2.chunk, _lib.SSD_BF16)
     lib = _lib.load()
