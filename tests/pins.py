@@ -432,8 +432,11 @@ def pin_varlen(orc):
 # finite differences of the C oracle's forward, element by element, for every
 # input and parameter (the C oracle is a different implementation, so a
 # mistake in either shows).
-def pin_backward(orc):
-    from oracle import backward as bwd
+def pin_backward(orc, bwd=None):
+    """bwd: the backward oracle module (a planted-mistake copy in the
+    mutation tests); the real one by default."""
+    if bwd is None:
+        from oracle import backward as bwd
     errs = []
     for seed, kw in [(21, dict(L=11)), (22, dict(Bn=1, L=6, H=4, G=1, P=3, N=2, W=2))]:
         k = rand_mixer(seed, **kw)

@@ -1,14 +1,17 @@
-"""Plant a plausible mistake in a copy of the C oracle and check that at
-least one pin catches it. The mistakes are planted in the oracle only, on
-the CPU; each mutated copy is compiled into a temporary directory."""
+"""Plant a plausible mistake in a copy of the C oracle (or of the backward
+oracle) and check that at least one pin catches it. The mistakes are planted
+in the oracle only, on the CPU; each mutated copy is compiled (or loaded)
+from a temporary directory."""
+import importlib.util
 import os
 
 import pytest
 
 from oracle import oracle as orc_mod
-from pins import LIMITS, PINS
+from pins import LIMITS, PINS, pin_backward
 
 SRC = os.path.join(os.path.dirname(orc_mod.__file__), "ssd_oracle.c")
+BWD_SRC = os.path.join(os.path.dirname(orc_mod.__file__), "backward.py")
 
 # name -> list of (exact text, replacement); every text must occur in the source.
 MUTATIONS = {
@@ -71,3 +74,44 @@ def test_planted_mistake_is_caught(name, tmp_path):
         if fn(orc) > LIMITS[pin]:
             caught.append(pin)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# Mistakes in the backward oracle's forward (its gradients come from
+# autograd of that forward): the backward pin compares the forward with the
+# C oracle and the gradients with central differences of the C oracle. A
+# dropped term keeps its tensor in the graph with weight zero, since autograd
+# refuses inputs that take no part in the result.
+BWD_MUTATIONS = {
+    "bwd_conv_bias_dropped": [("u = u + conv_b", "u = u + 0.0 * conv_b")],
+    "bwd_gate_without_z": [("q = y * z * torch.sigmoid(z)", "q = y * torch.sigmoid(z)")],
+    "bwd_decay_without_dt": [("torch.exp(dt[:, t] * A)", "torch.exp(A + 0.0 * dt[:, t])")],
+    "bwd_D_dropped": [("+ D[:, None] * x[:, t])", "+ 0.0 * D[:, None] * x[:, t])")],
+    "bwd_norm_sum_not_mean": [("(qg * qg).mean(-1, keepdim=True)",
+                               "(qg * qg).sum(-1, keepdim=True)")],
+    "bwd_conv_taps_reversed": [("conv_w[:, k] * ext[:, k:k + L]",
+                                "conv_w[:, W - 1 - k] * ext[:, k:k + L]")],
+    "bwd_initial_state_ignored": [("S = s_in if s_in is not None else",
+                                   "S = 0.0 * s_in if s_in is not None else")],
+    "bwd_final_state_gradient_dropped": [("loss = loss + (s_out * _t(d_s_out)).sum()",
+                                          "loss = loss")],
+}
+
+
+@pytest.fixture(scope="module")
+def c_oracle():
+    return orc_mod.Oracle()
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_planted_backward_mistake_is_caught(name, tmp_path, c_oracle):
+    src = open(BWD_SRC).read()
+    for old, new in BWD_MUTATIONS[name]:
+        assert src.count(old) >= 1, f"mutation {name}: pattern not found: {old!r}"
+        src = src.replace(old, new)
+    path = tmp_path / "bwd_mut.py"
+    path.write_text(src)
+    spec = importlib.util.spec_from_file_location("bwd_mut", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert pin_backward(c_oracle, bwd=mod) > LIMITS["backward"], (
+        f"the backward pin did not catch the planted mistake {name}")
