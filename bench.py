@@ -10,7 +10,8 @@ already resident in HBM. Two input/output buffer sets alternate across
 steps (each set, 0.85 GB, is larger than the 256 MB Infinity Cache).
 
 Also measured (reported under "workloads"): the same layer from separate
-x | B | C, z, dt tensors, a serving-style mixed batch (ragged prefills and
+x | B | C, z, dt tensors, the same layer with a conv bias (the fused kernels
+then carry the state split), a serving-style mixed batch (ragged prefills and
 decode steps over a state pool in one call), the tiny-model layer prefill
 (4 x 2048 tokens, 32 heads), the long-context chained prefill (16 pieces of
 8192 tokens, each resuming from the previous piece's states, per piece and
@@ -95,7 +96,7 @@ def parse():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-kernel HIP events")
     ap.add_argument("--only", choices=("tiny", "chain", "decode", "general", "serving", "backward",
-                                       "unpacked"),
+                                       "unpacked", "bias"),
                     help="time only one of the secondary workloads (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (for the HBM counter scale)")
@@ -182,7 +183,7 @@ def kernel_times(ops, run, steps, launches_per_step=8, only=None):
 
 
 def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, states_out,
-                     kernel_events=True, packed=False, breakdown=True):
+                     kernel_events=True, packed=False, breakdown=True, bias=False):
     """Mean ms per prefill call over `steps` timed calls (HIP events around the
     whole timed region), and the output kernel's mean ms over the same calls
     (only that kernel is bracketed by the library's events, on its own
@@ -190,9 +191,10 @@ def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, st
     the other kernels' mean ms from a second pass in which every launch is
     bracketed. packed: the call takes the input projection's rows
     [z | xBC | dt_raw] with dt_bias and A_log (dt and A formed in the
-    kernels)."""
+    kernels). bias: the conv carries a bias (drawn as in the parity tests)."""
     td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    prm = synth.packed_params(cfg) if packed else synth.layer_params(cfg)
+    prm = (synth.packed_params(cfg, with_bias=bias) if packed
+           else synth.layer_params(cfg, with_bias=bias))
     d = ops.SSDDims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate,
                     cfg.conv_width, cfg.chunk, td)
     D = to_dev(torch, prm["D"], torch.float32)
@@ -202,6 +204,7 @@ def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, st
     else:
         A = to_dev(torch, prm["A"], torch.float32)
     cw, nw = to_dev(torch, prm["conv_w"], td), to_dev(torch, prm["norm_w"], td)
+    cb = to_dev(torch, prm["conv_b"], td) if bias else None
     base = {"row": synth.packed_prefill_inputs(cfg)} if packed else synth.prefill_inputs(cfg)
     st0 = synth.initial_states(cfg) if states_in else None
     sets = []
@@ -222,11 +225,11 @@ def prefill_workload(torch, ops, synth, cfg, steps, warmup, nsets, states_in, st
     def step(i):
         s = sets[i % nsets]
         if packed:
-            ops.ssd_mixer_prefill_packed(d, s["row"], dtb, alog, D, cw, None, nw, prm["eps"],
+            ops.ssd_mixer_prefill_packed(d, s["row"], dtb, alog, D, cw, cb, nw, prm["eps"],
                                          s.get("cs_in"), s.get("cs_out"), s.get("ss_in"),
                                          s.get("ss_out"), s["out"], ws)
         else:
-            ops.ssd_mixer_prefill(d, s["xbc"], s["z"], s["dt"], A, D, cw, None, nw, prm["eps"],
+            ops.ssd_mixer_prefill(d, s["xbc"], s["z"], s["dt"], A, D, cw, cb, nw, prm["eps"],
                                   s.get("cs_in"), s.get("cs_out"), s.get("ss_in"),
                                   s.get("ss_out"), s["out"], ws)
 
@@ -615,6 +618,14 @@ def secondary(torch, ops, synth, args, which):
             summarize_prefill(c2, ms, kern, False, True), status=rc,
             config="the headline layer and inputs with x | B | C, z and dt (already softplus-ed) "
                    "as separate tensors and A given")
+    if "bias" in which:
+        c2 = synth.CONFIGS["large_layer"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
+                                        True, ke, packed=True, bias=True)
+        wl["large_layer_prefill_conv_bias"] = dict(
+            summarize_prefill(c2, ms, kern, False, True), status=rc,
+            config="the headline layer and packed rows with a conv bias ~ N(0, 0.25): the "
+                   "fused kernels carry the state split S' + a bbar^T")
     if "general" in which:
         c0 = synth.CONFIGS["tiny_fp32"]
         ms, kern, rc = prefill_workload(torch, ops, synth, c0, 50, 5, 1, False, False, ke)
@@ -700,9 +711,9 @@ def main():
         "headline": head,
     }
     if not args.quick:
-        rec["workloads"] = secondary(torch, ops, synth, args, ("unpacked", "tiny", "chain",
-                                                               "decode", "serving", "general",
-                                                               "backward"))
+        rec["workloads"] = secondary(torch, ops, synth, args, ("unpacked", "bias", "tiny",
+                                                               "chain", "decode", "serving",
+                                                               "general", "backward"))
         rec["ceilings"] = ceilings(torch)
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(synth, cfg)

@@ -74,13 +74,15 @@
  * headdim 64, dstate 128, heads per group a multiple of 4, dims->chunk >= 64
  * and conv width 4 when the call includes the conv) takes fp16 operands
  * throughout (the chunk states and carried-in states are also stored in
- * fp16), with D x taken from x at fp16 hi + lo precision. There the fp16
- * rounding of the carried-in states and of C bounds the error of the
- * inter-chunk term by about 2^-11 times the sum of |C_n S_n| over the state,
- * not |y|: inputs for which that sum is much larger than y (a conv bias with
- * slowly decaying heads, A of order -0.01, measured at up to 8x the 2e-2
- * bf16 tolerance after the norm) need SSD_FLAG_FP32_OPERANDS, which sends
- * the call to the general path with fp32 operands throughout. The fp16
+ * fp16), with D x taken from x at fp16 hi + lo precision. With a conv bias,
+ * B and C (and x) share large per-channel offsets, and the state grows along
+ * the B offset bbar, while C . bbar can nearly cancel: the fast path then
+ * carries every state as S' + a bbar^T (the same matrix, split), with the
+ * fp16 operands only for S', B - bbar and C - cbar (cbar, bbar: SiLU of the
+ * conv bias) and everything that cancels (a, C . bbar, S' . cbar) in fp32,
+ * so such inputs (slowly decaying heads, A of order -0.01) meet the 2e-2
+ * bf16 tolerance on the fast path too. SSD_FLAG_FP32_OPERANDS sends the call
+ * to the general path with fp32 operands throughout. The fp16
  * intermediates (activations after SiLU, C B^T, chunk states, carried-in
  * states, the scan output before the norm) must stay within fp16 range
  * (|v| < 65504); a value beyond it becomes infinite, so the output or final
@@ -134,13 +136,13 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 /* ssd_dims.flags. SSD_FLAG_FP32_OPERANDS: run the chunked scan's dense
  * contractions on fp32 MFMA operands for bf16 I/O as well (every
  * intermediate keeps fp32 range and precision; the general kernels are used,
- * not the fused ones). Needed when the inter-chunk term C . S_in is badly
- * conditioned: B and C sharing a large offset (a conv bias does this) over
- * slowly decaying heads make the state grow along that offset, and in some
- * rows C . S_in is a sum of large terms that nearly cancel; fp16 operands
- * resolve each term to 2^-11 of itself, and the norm divides by that row's
- * small RMS (see "Precision" above). Unknown bits are refused
- * (SSD_ERR_UNSUPPORTED). The workspace query takes the flag into account. */
+ * not the fused ones). For inputs whose offsets the fast path's state split
+ * does not see (B and C sharing a large offset that does not come from the
+ * conv bias, e.g. through ssd_chunk_scan) over slowly decaying heads, the
+ * inter-chunk term C . S_in can be a sum of large terms that nearly cancel;
+ * fp16 operands resolve each term to 2^-11 of itself (see "Precision"
+ * above). Unknown bits are refused (SSD_ERR_UNSUPPORTED). The workspace
+ * query takes the flag into account. */
 enum { SSD_FLAG_FP32_OPERANDS = 1 };
 
 typedef struct {

@@ -212,6 +212,13 @@ SSD_DEV void conv_tile(const u32x4 (&raw)[T + (CONV ? W - 1 : 0)], const ConvW<C
   }
 }
 
+// silu of the 8 bf16 conv biases of one channel vector
+SSD_DEV void bias_silu8(const u32x4 b, float (&o)[8]) {
+  unpack8(b, o);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = silu(o[j]);
+}
+
 // Load the T (+ halo) rows of one 8-channel vector: every row load is issued
 // before any is used; addresses are clamped into the sequence (the conv
 // state supplies rows before token 0 when present, else they are zeroed by
@@ -252,41 +259,104 @@ SSD_DEV void rows_mask_head(u32x4 (&raw)[T + (CONV ? W - 1 : 0)], int tseq, cons
 // src: the channel vector's element at token 0 of this batch; tseq: sequence
 // position of the first token; Lm1: last token of the sequence; ch: absolute
 // xBC channel (conv weights); cin_b: conv state of this batch or null.
+// OFS handles the shared channel offsets of B and C (see the state split
+// below), with off = silu(offb) and dw = silu(dwb) from 8 packed bf16 conv
+// biases: kOfsSub stores v - off; kOfsDot also gives, per token i, dot[i] =
+// v_i . dw on the fp32 values. The subtraction is done as the values are
+// packed (a separate pass over the tile costs registers). Rows past nvalid
+// are stored as zero and their dots are zero.
 template <bool CONV>
 using Rows8 = u32x4[8 + (CONV ? W - 1 : 0)];
-template <bool CONV, bool TRANS>
+constexpr int kOfsNone = 0, kOfsDot = 1, kOfsSub = 2;
+template <bool CONV, bool TRANS, int OFS = kOfsNone>
 SSD_DEV void conv_store(Rows8<CONV>& raw, const ConvW<CONV>& cw, int tseq, int nvalid,
                         const bf16* cin_b, f16* dst, int ld, f16* gdst = nullptr,
-                        int64_t gld = 0) {
+                        int64_t gld = 0, u32x4 offb = {}, u32x4 dwb = {},
+                        float* dot = nullptr) {
   rows_mask_head<CONV, 8>(raw, tseq, cin_b);
   float v[8][8];
   conv_tile<CONV, 8>(raw, cw, v);
-  if (nvalid < 8) {  // only the tail of a sequence
+  float off[8] = {};
+  if constexpr (OFS != kOfsNone) {
+    bias_silu8(offb, off);
+    if constexpr (OFS == kOfsDot) {
+      float dw[8];
+      bias_silu8(dwb, dw);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d = fmaf(v[i][j], dw[j], d);
+        dot[i] = i < nvalid ? d : 0.f;
+      }
+    }
+  }
+  if (nvalid < 8) {  // only the tail of a sequence (its stored rows are 0)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : 0.f;
+      for (int j = 0; j < 8; ++j) v[i][j] = i < nvalid ? v[i][j] : off[j];
   }
+  // token row i less the offsets, as fp16
+  auto row = [&](int i) {
+    return u32x4{pk(v[i][0] - off[0], v[i][1] - off[1]), pk(v[i][2] - off[2], v[i][3] - off[3]),
+                 pk(v[i][4] - off[4], v[i][5] - off[5]), pk(v[i][6] - off[6], v[i][7] - off[7])};
+  };
   if (gdst) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i < nvalid)
-        *reinterpret_cast<u32x4*>(gdst + i * gld) = u32x4{
-            pk(v[i][0], v[i][1]), pk(v[i][2], v[i][3]), pk(v[i][4], v[i][5]), pk(v[i][6], v[i][7])};
+      if (i < nvalid) *reinterpret_cast<u32x4*>(gdst + i * gld) = row(i);
   }
   if (!dst) return;
   if (TRANS) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      sts16(dst + j * ld, u32x4{pk(v[0][j], v[1][j]), pk(v[2][j], v[3][j]), pk(v[4][j], v[5][j]),
-                                pk(v[6][j], v[7][j])});
+    for (int j = 0; j < 8; ++j) {
+      const float o = off[j];
+      sts16(dst + j * ld, u32x4{pk(v[0][j] - o, v[1][j] - o), pk(v[2][j] - o, v[3][j] - o),
+                                pk(v[4][j] - o, v[5][j] - o), pk(v[6][j] - o, v[7][j] - o)});
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(dst + i * ld) = u32x4{pk(v[i][0], v[i][1]), pk(v[i][2], v[i][3]),
-                                                      pk(v[i][4], v[i][5]), pk(v[i][6], v[i][7])};
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(dst + i * ld) = row(i);
   }
 }
+// The same for 4 of the tokens, natural layout, to global memory only (rows
+// i < nvalid at gdst + i * gld): half the live tile of the 8-token form.
+// raw: the 4 (+ halo) rows of tokens tseq .. tseq + 3.
+template <bool CONV, int OFS>
+SSD_DEV void conv_store4(const u32x4* raw_p, const ConvW<CONV>& cw, int tseq, int nvalid,
+                         const bf16* cin_b, f16* gdst, int64_t gld, u32x4 offb = {},
+                         u32x4 dwb = {}, float* dot = nullptr) {
+  constexpr int R = 4 + (CONV ? W - 1 : 0);
+  u32x4 raw[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) raw[i] = raw_p[i];
+  rows_mask_head<CONV, 4>(raw, tseq, cin_b);
+  float v[4][8];
+  conv_tile<CONV, 4>(raw, cw, v);
+  float off[8] = {};
+  if constexpr (OFS != kOfsNone) {
+    bias_silu8(offb, off);
+    if constexpr (OFS == kOfsDot) {
+      float dw[8];
+      bias_silu8(dwb, dw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d = fmaf(v[i][j], dw[j], d);
+        dot[i] = i < nvalid ? d : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < nvalid)
+      *reinterpret_cast<u32x4*>(gdst + i * gld) =
+          u32x4{pk(v[i][0] - off[0], v[i][1] - off[1]), pk(v[i][2] - off[2], v[i][3] - off[3]),
+                pk(v[i][4] - off[4], v[i][5] - off[5]), pk(v[i][6] - off[6], v[i][7] - off[7])};
+}
+
 // Raw rows of one x staging item: 4 tokens (+ W-1 halo when CONV) of one
 // 8-channel vector, loaded ahead of their use.
 template <bool CONV>
@@ -334,6 +404,39 @@ SSD_DEV void x_store(XRaw<CONV>& r, const ConvW<CONV>& cw, int tseq, int nvalid,
   }
 }
 
+// ---- the state split ------------------------------------------------------
+// With a conv bias, the convolved B and C rows share per-channel offsets
+// bbar = silu(b_B) and cbar = silu(b_C), much larger than their variation,
+// and x has one too, so the state grows a large rank-one part along bbar
+// while C_t . bbar can be far smaller than |C_t| |bbar|: rounding S or C to
+// the fp16 operand precision would cost most of the bits of C_t . S. The
+// kernels therefore carry S = S' + a bbar^T (the same matrix, split):
+//   chunk state   dS' = sum_s x_s w_s (B_s - bbar)^T on the MFMA, and the
+//                 fp32 row sums da = sum_s x_s w_s (a ones-row MFMA on the
+//                 same fp16 operand);
+//   state pass    S' and a in fp32 (the carried-in state split by projecting
+//                 its rows on bbar), S'_in in fp16 plus, per row p, a_in and
+//                 sc'_in = S'_in . cbar in fp32; the final state S' + a bbar^T;
+//   output        C_t . S_in = (C_t - cbar) . S'_in + sc'_in + a_in u_t with
+//                 u_t = C_t . bbar in fp32 from the fp32 conv output, and
+//                 C_t . B_s = (C_t - cbar) . (B_s - bbar) + u_t + v_s with
+//                 v_s = cbar . (B_s - bbar).
+// Only the fp16 operands change: S', B - bbar and C - cbar are small, and
+// everything that cancels is summed in fp32. Without a bias nothing is split.
+// Per (chunk, head) the split keeps kAux x P floats: da, a_in, sc'_in.
+constexpr int kAux = 3;
+// Sums of dot[i] over the 16 lanes of a row; the lane at position cv of the
+// row keeps the sum of token cv (cv < 8).
+SSD_DEV float row_dots_pick(float (&dot)[8], int cv) {
+  float mine = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = group_sum_last<16>(dot[i]);
+    mine = cv == i ? t : mine;
+  }
+  return mine;
+}
+
 // B-channel block mapping for transposed staging: within 16 lanes, 2 channel
 // vectors x 8 token blocks, so the 16-byte LDS writes of a phase hit 16
 // distinct bank groups. Returns (cv, tbi) for block index i of a tile with
@@ -350,14 +453,18 @@ SSD_DEV void tmap(int i, int& cv, int& tbi) {
 // and store 16 bytes each (a wave's stores per row cover one whole 128-byte
 // line). B^T is staged
 // once (conv) for the group; x of one head at a time goes through two LDS
-// buffers, the rows of later heads loaded two heads ahead.
+// buffers, the rows of later heads loaded two heads ahead. With aux (a conv
+// bias: the state split) B^T is staged as B - bbar, da goes to aux and, with
+// PRE, the kept rows are B - bbar and C - cbar, with u_t per token in ug.
 template <bool CONV, bool PRE>
 __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict__ dt,
                                                const float* __restrict__ A,
                                                f16* __restrict__ states,
                                                float* __restrict__ lam_end,
                                                f16* __restrict__ bcv, f16* __restrict__ ccv,
-                                               int* status, int L, int H, int G, int nc) {
+                                               float* __restrict__ aux,
+                                               float* __restrict__ ug, int* status, int L,
+                                               int H, int G, int nc) {
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
@@ -422,6 +529,9 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   const int n0 = cv * 8, tseq = t0 + tbi * 8;
   const int nvb = min(8, max(0, len - tbi * 8));
   const int64_t grow = (row0 + tbi * 8) * s.GN + g * N + n0;  // its row in bcv / ccv
+  const bool ofs = CONV && aux;  // uniform: the state split is on
+  // conv biases of this thread's 8 B channels (zero without the split)
+  u32x4 bbr = {0u, 0u, 0u, 0u};
   {
     const int ch = s.HP + g * N + n0;
     // weights before rows (see ConvW)
@@ -434,9 +544,13 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     for (int k = 0; k < 2; ++k)
       x_load<CONV>(xr[k], xb + (hg0 + k) * P + xp0, s.xs, t0 + xtb * 4, L - 1, s,
                    (hg0 + k) * P + xp0, cin_b);
+    if constexpr (CONV) {
+      if (ofs) bbr = cwb.b;
+    }
     // with PRE, conv'd B also kept (natural layout) for the output kernel
-    conv_store<CONV, true>(rb, cwb, tseq, nvb, cin_b, BT + n0 * RS + tbi * 8, RS,
-                           PRE ? bcv + grow : nullptr, s.GN);
+    conv_store<CONV, true, CONV ? kOfsSub : kOfsNone>(rb, cwb, tseq, nvb, cin_b,
+                                                      BT + n0 * RS + tbi * 8, RS,
+                                                      PRE ? bcv + grow : nullptr, s.GN, bbr);
   }
   // with PRE, conv'd C too for the output kernel (a group spans several of
   // its 4-head blocks, each of which would otherwise redo the B and C conv):
@@ -456,11 +570,27 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
   // p-tiles 2 (w >> 1), + 1, so each row segment a wave stores is a whole
   // cache line
   const int nt0 = 4 * (wave & 1), pt0 = 2 * (wave >> 1);
+  // the split's row sums: wave w takes p-tile pt0 + (w & 1) with an A operand
+  // whose row 0 is all ones (lane rr == 0), so output row 0 is sum_s x_s w_s
+  f16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = rr == 0 ? (f16)1.0f : (f16)0.0f;
 
   x_store<CONV, false>(xr[0], cwx, t0 + xtb * 4, xnv, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
-  if constexpr (PRE)
-    conv_store<CONV, false>(rc, cwc, tseq, nvb, cin_b, nullptr, 0, ccv + grow, s.GN);
+  if constexpr (PRE) {
+    float ud[8];
+    // two halves of 4 tokens (the halo rows of the second are rows 4..)
+    constexpr int kOfsC = CONV ? kOfsDot : kOfsNone;
+    const u32x4 cbr = ofs ? cwc.b : u32x4{};
+    conv_store4<CONV, kOfsC>(rc, cwc, tseq, nvb, cin_b, ccv + grow, s.GN, cbr, bbr, ud);
+    conv_store4<CONV, kOfsC>(rc + 4, cwc, tseq + 4, nvb - 4, cin_b, ccv + grow + 4 * s.GN, s.GN,
+                             cbr, bbr, ud + 4);
+    if (ofs) {
+      const float umine = row_dots_pick(ud, cv);
+      if (cv < nvb) ug[(row0 + tbi * 8 + cv) * G + g] = umine;
+    }
+  }
   __syncthreads();
 
   // heads of the group in blocks of HB; head k = j HB + hh (even HB keeps
@@ -492,7 +622,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
       if (hh == HB - 2 && more)
         cumsum(h0 + HB, dt_of(to_f(dn0), s.dta, h0 + HB + wave),
                dt_of(to_f(dn1), s.dta, h0 + HB + wave), wnext);
-      f32x4 acc[4][2];
+      f32x4 acc[4][2], sa = zero4();
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -510,7 +640,11 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 #pragma unroll
           for (int pi = 0; pi < 2; ++pi) acc[j][pi] = mma16(bf, xf[pi], acc[j][pi]);
         }
+        if (ofs) sa = mma16(ones, (wave & 1) ? xf[1] : xf[0], sa);
       }
+      // da of rows p = (pt0 + (w & 1)) 16 + rr: output row 0 (lanes 0..15)
+      if (ofs && q4 == 0)
+        aux[(cg.kg * H + h0 + hh) * (int64_t)(kAux * P) + (pt0 + (wave & 1)) * 16 + rr] = sa[0];
       // lane: n = (nt0 + j) * 16 + r4 + r, p = (pt0 + pi) * 16 + rr
       f16* o = states + (cg.kg * H + h0 + hh) * (int64_t)(P * N);
       // lanes q4 = 2m, 2m + 1 (16 apart) trade halves (an LDS-crossbar lane
@@ -560,15 +694,24 @@ constexpr int kStatusNonFinite = 2;  // an output or the final state is not fini
 constexpr int kPassVec = 8;
 // dS and sin_h are one buffer: S_in(k) overwrites dS_k, which this thread
 // has loaded before (its own elements only), so neither pointer is restrict.
+// With aux (the state split) the carried state is S' (dS holds dS') plus a
+// bbar^T: the 16 lanes of a row p hold its 128 elements, so the row sums are
+// row-wide DPP reductions; a_in and sc'_in of chunk k go to aux beside da_k,
+// and cbar of each group to cbg (fp16).
 __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
-                                               f16* sin_h, int* sync, float* part,
+                                               f16* sin_h, float* __restrict__ aux,
+                                               f16* __restrict__ cbg,
+                                               const bf16* __restrict__ cbias, int HP, int GN,
+                                               int hpg, int* sync, float* part,
                                                int64_t npart, int* status, Seqs q, int H,
                                                int nc) {
   constexpr int PN = P * N;
   const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
   const int h = blockIdx.y, b = blockIdx.z;
+  const int p = e / N, n0 = e % N;
+  const bool ofs = aux != nullptr;
   {
     const int64_t gt = ((int64_t)(b * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
     const int64_t nt = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
@@ -602,9 +745,40 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
 #pragma unroll
     for (int j = 0; j < kPassVec; ++j) S[j] = 0.f;
   }
+  // bbar, cbar of this thread's 8 columns; a of its row (0 without the split)
+  float bbar[kPassVec] = {}, cbar[kPassVec] = {};
+  float a = 0.f;
+  if (ofs) {
+    const int g = h / hpg;
+    load8(cbias + HP + g * N + n0, bbar);
+    load8(cbias + HP + GN + g * N + n0, cbar);
+#pragma unroll
+    for (int j = 0; j < kPassVec; ++j) {
+      bbar[j] = silu(bbar[j]);
+      cbar[j] = silu(cbar[j]);
+    }
+    // cbar of the group in fp16 for the output kernel (row 0 of the group's
+    // first head; other batches write the same values)
+    if (blockIdx.x == 0 && p == 0 && h % hpg == 0)
+      *reinterpret_cast<u32x4*>(cbg + g * N + n0) =
+          u32x4{pk(cbar[0], cbar[1]), pk(cbar[2], cbar[3]), pk(cbar[4], cbar[5]),
+                pk(cbar[6], cbar[7])};
+    // carried-in state: a = (S . bbar) / |bbar|^2 per row, S' = S - a bbar^T
+    float sb = 0.f, bq = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPassVec; ++j) {
+      sb = fmaf(S[j], bbar[j], sb);
+      bq = fmaf(bbar[j], bbar[j], bq);
+    }
+    sb = group_sum_last<16>(sb);
+    bq = group_sum_last<16>(bq);
+    a = bq > 0.f ? sb / bq : 0.f;
+#pragma unroll
+    for (int j = 0; j < kPassVec; ++j) S[j] = fmaf(-a, bbar[j], S[j]);
+  }
   for (int c0 = 0; c0 < nc; c0 += kPassDepth) {
     u32x4 d[kPassDepth];
-    float al[kPassDepth];
+    float al[kPassDepth], da[kPassDepth];
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
       const int c = min(c0 + u, nc - 1);
@@ -612,6 +786,7 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
       d[u] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(dS + ((k0 + c) * H + h) * PN + e));
       al[u] = fexp2(lam_end[(k0 + c) * H + h]);  // Lam_end in log2 units
+      da[u] = ofs ? aux[((k0 + c) * H + h) * (int64_t)(kAux * P) + p] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
@@ -623,6 +798,18 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
         o.z = pk(S[4], S[5]);
         o.w = pk(S[6], S[7]);
         *reinterpret_cast<u32x4*>(sin_h + ((k0 + c) * H + h) * PN + e) = o;
+        if (ofs) {
+          float sc = 0.f;
+#pragma unroll
+          for (int j = 0; j < kPassVec; ++j) sc = fmaf(S[j], cbar[j], sc);
+          sc = group_sum_last<16>(sc);
+          if ((threadIdx.x & 15) == 0) {
+            float* ap = aux + ((k0 + c) * H + h) * (int64_t)(kAux * P);
+            ap[P + p] = a;
+            ap[2 * P + p] = sc;
+          }
+          a = al[u] * a + da[u];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           S[2 * j] = al[u] * S[2 * j] + h2f_lo(d[u][j]);
@@ -632,6 +819,10 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     }
   }
   if (sout_p) {
+    if (ofs) {
+#pragma unroll
+      for (int j = 0; j < kPassVec; ++j) S[j] = fmaf(a, bbar[j], S[j]);
+    }
     store8(sout_p + e, S);
     float chk = 0.f;  // NaN when any element is infinite or NaN
 #pragma unroll
@@ -665,7 +856,10 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
 // opposite sign, so no rounding between them), y kept as fp16 pairs -> y
 // through an LDS tile to a coalesced epilogue that gates with z
 // (prefetched), normalises each row over its 256 channels and stores
-// 16-byte vectors.
+// 16-byte vectors. With aux (the state split) B, C and S_in are the split
+// operands and u_t, v_s, a_in, sc'_in enter in fp32: u_t + v_s on the C.B^T
+// tiles before their fp16 rounding, sc'_in + a_in u_t on the inter-chunk
+// accumulators before exp(Lam_t).
 template <bool CONV, int NM, bool PREC>
 __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ dt,
                                                 const float* __restrict__ A,
@@ -673,15 +867,20 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
                                                 const f16* __restrict__ sin_h,
                                                 const f16* __restrict__ bcv,
                                                 const f16* __restrict__ ccv,
+                                                const float* __restrict__ aux,
+                                                const float* __restrict__ ug,
+                                                const f16* __restrict__ cbg,
                                                 const bf16* __restrict__ z,
                                                 const bf16* __restrict__ nw, float eps,
                                                 bf16* __restrict__ out, float* part, int* sync,
                                                 int* status, int spin_max, int L, int H, int G,
                                                 int nc) {
-  static_assert(2 * P * RS + P * NS <= 2 * QI * NS, "x tile and one head's states fit");
+  static_assert(2 * P * RS + P * NS + 2 * P * 2 <= 2 * QI * NS,
+                "x tile, one head's states and its a_in, sc'_in fit");
   static_assert(QI * OS <= 2 * QI * NS, "output tile must fit");
   __shared__ __align__(16) f16 U[2 * QI * NS];  // Bs | Cs, then x tile + states, then Ot
   __shared__ float lam[HB][QI], dts[HB][QI], csd[HB][QI];
+  __shared__ __align__(16) float uvs[2][QI];    // u_t, v_t of the split
   // conv weights ([channel][tap]) and bias of the block's HB * P x channels
   constexpr int kXW = CONV ? HB * P * W / 8 : 1, kXB = CONV ? HB * P / 8 : 1;
   __shared__ __align__(16) u32x4 XWl[kXW], XBl[kXB];
@@ -690,7 +889,10 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   f16* XT = U;                // [p][RS]: fp16(x) of the current head
   f16* XL = U + P * RS;       // [p][RS]: x - fp16(x)
   f16* Sl = U + 2 * P * RS;   // [p][NS]: S_in of the current head
+  // a_in [P] | sc'_in [P] of the current head (fp32, 16-byte aligned)
+  float* aS = reinterpret_cast<float*>(U + 2 * P * RS + P * NS);
   f16* Ot = U;                // [t][4 heads x p]: y
+  const bool ofs = CONV && aux;  // uniform: the state split is on
 
   int c, b, h0, tk = 0;
   if constexpr (NM == 2) {
@@ -773,6 +975,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   {
     const int cv = tid & 15, tbi = tid >> 4, n0 = cv * 8;
     const int tseq = t0 + tbi * 8, nv = min(8, max(0, len - tbi * 8));
+    float ud[8];  // u_t of the split, per token
     const int64_t boff = cg.tok0 * s.bs + g * N + n0;
     const int chb = s.HP + g * N + n0, chc = chb + s.GN;
     // rows of the precomputed buffers, clamped into the sequence
@@ -788,12 +991,16 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
         *reinterpret_cast<u32x4*>(dst + i * NS) = i < nv ? v[i] : u32x4{0u, 0u, 0u, 0u};
     };
     if constexpr (PREC) {
+      // rows of B - bbar and C - cbar, and u_t, from the chunk-state kernel
       u32x4 vb[8], vc[8];
       pre_rows(bcv, vb);
       pre_rows(ccv, vc);
+      float u = 0.f;
+      if (ofs && tid < QI && tid < len) u = ug[(row0 + tid) * G + g];
       x_load<CONV, PREC>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
       pre_put(vb, Bs + (tbi * 8) * NS + n0);
       pre_put(vc, Cs + (tbi * 8) * NS + n0);
+      if (ofs && tid < QI) uvs[0][tid] = u;
     } else {
       // weights before rows (see ConvW)
       ConvW<CONV> cwb, cwc;
@@ -803,13 +1010,28 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       rows_load<CONV, 8>(rb, s.b + boff, s.bs, tseq, L - 1, s, chb, cin_b);
       rows_load<CONV, 8>(rc, s.c + boff, s.bs, tseq, L - 1, s, chc, cin_b);
       x_load<CONV, PREC>(xr, xb + h0 * P + xp0, s.xs, t0 + xtb * 4, L - 1, s, h0 * P + xp0, cin_b);
-      conv_store<CONV, false>(rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS);
-      conv_store<CONV, false>(rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS);
+      // conv biases of the 8 B and C channels: the split's offsets (zero without)
+      u32x4 bbr = {0u, 0u, 0u, 0u}, cbr = {0u, 0u, 0u, 0u};
+      if constexpr (CONV) {
+        if (ofs) {
+          bbr = cwb.b;
+          cbr = cwc.b;
+        }
+      }
+      conv_store<CONV, false, CONV ? kOfsSub : kOfsNone>(
+          rb, cwb, tseq, nv, cin_b, Bs + (tbi * 8) * NS + n0, NS, nullptr, 0, bbr);
+      conv_store<CONV, false, CONV ? kOfsDot : kOfsNone>(
+          rc, cwc, tseq, nv, cin_b, Cs + (tbi * 8) * NS + n0, NS, nullptr, 0, cbr, bbr, ud);
+      if (ofs) {
+        const float um = row_dots_pick(ud, cv);
+        if (cv < 8) uvs[0][tbi * 8 + cv] = um;
+      }
     }
     if constexpr (CONV) {
       if (tid < kXW) XWl[tid] = xwp;
       else if (tid < kXW + kXB) XBl[tid - kXW] = xwp;
     }
+    if (ofs && tid < QI) uvs[1][tid] = 0.f;  // v_t: two halves are added below
   }
   // Lam (inclusive cumsum of dt A), dt, and csd[s] = exp(Lam_ref - Lam_s) dt_s
   // with Lam_ref the value at the end of s's 32-position block (<= Lam_s).
@@ -828,6 +1050,27 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     csd[wave][tc + 1] = fexp2(lref - l1) * d1;
   }
   __syncthreads();
+  if (ofs) {
+    // v_t = cbar . (B_t - bbar) from the staged fp16 rows (fp16 products are
+    // exact in the fp32 dot): waves 0, 1 take channels 0..63 and waves 2, 3
+    // channels 64..127 of token tid % 128, reading cbar at uniform addresses;
+    // the two halves meet in uvs[1] (0 + a + b is the same in either order)
+    const int sv = tid & (QI - 1), hv = wave >> 1;
+    const f16* bp = Bs + sv * NS + hv * (N / 2);
+    const f16* cp = cbg + g * N + hv * (N / 2);
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k) {
+      const f16x8 b8 = *reinterpret_cast<const f16x8*>(bp + 8 * k);
+      const f16x8 c8 = *reinterpret_cast<const f16x8*>(cp + 8 * k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        d = __builtin_amdgcn_fdot2(f16x2{b8[2 * q], b8[2 * q + 1]}, f16x2{c8[2 * q], c8[2 * q + 1]},
+                                   d, false);
+    }
+    atomicAdd(&uvs[1][sv], d);
+    __syncthreads();
+  }
 
   const int rta = wave, rtb = 7 - wave;
   // C fragments of the wave's rows (B operand: column t, k = n)
@@ -838,14 +1081,18 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
     Cfb[ks] = *reinterpret_cast<const f16x8*>(Cs + (rtb * 16 + rr) * NS + ks * 32 + kk);
   }
   // carried-in states of one head (contiguous [p][n], 16 KB): 4 x 16 bytes
-  // per thread, loaded a head ahead and staged into LDS with that head's x
+  // per thread, loaded a head ahead and staged into LDS with that head's x;
+  // with the split, threads 0..31 also carry its a_in | sc'_in (512 bytes)
   const f16* sbase = sin_h + (cg.kg * H + h0) * (int64_t)(P * N);
-  u32x4 sreg[4];
+  u32x4 sreg[4], areg = {0u, 0u, 0u, 0u};
   auto s_load = [&](int hh) {
     const f16* sp = sbase + (int64_t)hh * (P * N);
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // read once: streaming loads
       sreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sp + (tid + NT * i) * 8));
+    if (ofs && tid < 2 * P / 4)
+      areg = *reinterpret_cast<const u32x4*>(aux + (cg.kg * H + h0 + hh) * (int64_t)(kAux * P) +
+                                             P + tid * 4);
   };
   auto s_store = [&]() {
 #pragma unroll
@@ -853,8 +1100,11 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       const int idx = tid + NT * i, row = idx >> 4, v = idx & 15;  // row = p
       *reinterpret_cast<u32x4*>(Sl + row * NS + v * 8) = sreg[i];
     }
+    if (ofs && tid < 2 * P / 4) *reinterpret_cast<u32x4*>(aS + tid * 4) = areg;
   };
   s_load(0);  // in flight while the G tiles are computed
+  // u_t of the lane's tokens in the two row tiles (the split)
+  const float ua = ofs ? uvs[0][rta * 16 + rr] : 0.f, ub = ofs ? uvs[0][rtb * 16 + rr] : 0.f;
   // (B C^T) tiles j <= rt of the wave's two row tiles: lane holds C_t.B_s for
   // t = 16 rt + rr and s = 16 j + 4 q4 + r (fp16, the MFMA operand precision).
   uint2 Ga[4], Gb[8];
@@ -867,6 +1117,15 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
       const f16x8 bf = *reinterpret_cast<const f16x8*>(bp + ks * 32);
       if (j < 4 && j <= rta) ga = mma16(bf, Cfa[ks], ga);
       if (j <= rtb) gb = mma16(bf, Cfb[ks], gb);
+    }
+    if (ofs) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&uvs[1][j * 16 + r4]);
+      const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ga[r] += ua + vs[r];
+        gb[r] += ub + vs[r];
+      }
     }
     if (j < 4) Ga[j] = make_uint2(pk(ga[0], ga[1]), pk(ga[2], ga[3]));
     Gb[j] = make_uint2(pk(gb[0], gb[1]), pk(gb[2], gb[3]));
@@ -949,6 +1208,19 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
         }
       }
       {
+        if (ofs) {
+          // + sc'_in[p] + a_in[p] u_t, p = 16 pt + r4 + r
+          const float ut = ui == 0 ? ua : ub;
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            const float4 a4 = *reinterpret_cast<const float4*>(aS + pt * 16 + r4);
+            const float4 s4 = *reinterpret_cast<const float4*>(aS + P + pt * 16 + r4);
+            acc[pt][0] = fmaf(a4.x, ut, acc[pt][0] + s4.x);
+            acc[pt][1] = fmaf(a4.y, ut, acc[pt][1] + s4.y);
+            acc[pt][2] = fmaf(a4.z, ut, acc[pt][2] + s4.z);
+            acc[pt][3] = fmaf(a4.w, ut, acc[pt][3] + s4.w);
+          }
+        }
         const float et = fexp2(lt);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
@@ -1203,10 +1475,11 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
 }
 
 // Workspace: chunk-state increments, overwritten in place by the carried-in
-// states (fp16), Lam_end;
-// when a group spans several 4-head blocks, the per-row partial sums and
-// the ticket counters of the cross-block norm and, with the conv, the
-// convolved B and C rows in fp16 for the output kernel.
+// states (fp16), Lam_end; with a conv bias the state split's per-chunk rows
+// (da, a_in, sc'_in); when a group spans several 4-head blocks, the per-row
+// partial sums and the ticket counters of the cross-block norm and, with the
+// conv, the convolved B and C rows in fp16 for the output kernel (and, with
+// a bias, u_t and v_t per token and group).
 namespace {
 size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
 bool wide(int H, int G) { return H / G > fast::HB; }
@@ -1223,15 +1496,19 @@ bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 // chunk table and a bitmap of the pool's slots.
 struct FastLayout {
   int64_t chunks, npart;
-  size_t dS, lam, part, sync, bcv, ccv, valid, first, cseq, bitmap, dec, total;
+  size_t dS, lam, aux, cbg, part, sync, bcv, ccv, uv, valid, first, cseq, bitmap, dec, total;
 };
+// The split's pieces are reserved whenever the conv is on (the size query
+// does not know whether a call brings a bias); a call uses them with one.
 FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int num_slots) {
   using namespace fast;
   FastLayout f{};
   const size_t PN = P * N;
   f.chunks = varlen ? (int64_t)(L + QI - 1) / QI + B : (int64_t)B * ((L + QI - 1) / QI);
   f.npart = f.chunks * (H / HB) * QI;
-  const size_t rows = (size_t)(varlen ? L : (int64_t)B * L) * G * N * 2;
+  const size_t toks = (size_t)(varlen ? L : (int64_t)B * L);
+  const size_t rows = toks * G * N * 2;
+  const bool split = conv;
   size_t off = 0;
   auto take = [&](size_t n) {
     const size_t o = off;
@@ -1240,6 +1517,10 @@ FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int n
   };
   f.dS = take((size_t)f.chunks * H * PN * 2);
   f.lam = take((size_t)f.chunks * H * 4);
+  if (split) {
+    f.aux = take((size_t)f.chunks * H * kAux * P * 4);
+    f.cbg = take((size_t)G * N * 2);
+  }
   if (wide(H, G)) {
     f.part = take((size_t)f.npart * 4);
     f.sync = take(kParts * 4);
@@ -1247,6 +1528,7 @@ FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int n
   if (pre_c(H, G, conv)) {
     f.bcv = take(rows);
     f.ccv = take(rows);
+    if (split) f.uv = take(toks * G * 4);
   }
   if (varlen) {
     f.valid = take(4);
@@ -1385,6 +1667,7 @@ __global__ __launch_bounds__(256) void k_varlen_conv_state(const bf16* __restric
 hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   using namespace fast;
   const bool varlen = a.q.cu != nullptr;
+  const bool split = a.conv && a.conv_b;  // the state split: with a conv bias
   const FastLayout f = fast_layout(a.B, a.L, a.H, a.G, a.conv, varlen, a.num_slots);
   // dense: (chunk, ., batch) grids; ragged: (global chunk, ., 1)
   const int nc = varlen ? (int)f.chunks : (a.L + QI - 1) / QI;
@@ -1406,6 +1689,9 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   const bool prec = pre_c(a.H, a.G, a.conv);
   fast::f16* bcv = prec ? (fast::f16*)(w + f.bcv) : nullptr;
   fast::f16* ccv = prec ? (fast::f16*)(w + f.ccv) : nullptr;
+  float* aux = split ? (float*)(w + f.aux) : nullptr;
+  float* ug = split && prec ? (float*)(w + f.uv) : nullptr;
+  fast::f16* cbg = split ? (fast::f16*)(w + f.cbg) : nullptr;
   Seqs q = a.q;
   if (varlen) {
     q.valid = (const int*)(w + f.valid);
@@ -1444,21 +1730,22 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     const bf16* dt = (const bf16*)a.dt;
     if (prec)
       hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         bcv, ccv, a.status, a.L, a.H, a.G, nc);
+                         bcv, ccv, aux, ug, a.status, a.L, a.H, a.G, nc);
     else if (a.conv)
       hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, aux, nullptr, a.status, a.L, a.H, a.G, nc);
     else
       hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfScope ps(st, KID_FAST_PASS);
     hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
-                       lam_end, a.s_in, a.s_out, sinb, nm == 2 ? sync : nullptr, part,
-                       nm == 2 ? npart : 0, a.status, q, a.H, nc);
+                       lam_end, a.s_in, a.s_out, sinb, aux, cbg, (const bf16*)a.conv_b, a.H * P,
+                       a.G * N, a.H / a.G, nm == 2 ? sync : nullptr, part, nm == 2 ? npart : 0,
+                       a.status, q, a.H, nc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1467,8 +1754,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   // scan output y is written
 #define SSD_FOUT(CV, NM, PC)                                                                  \
   hipLaunchKernelGGL((k_fout<CV, NM, PC>), g1, dim3(NT), 0, st, s, (const bf16*)a.dt, a.A, a.D, \
-                     sinb, bcv, ccv, (const bf16*)a.z, (const bf16*)a.norm_w, a.eps,            \
-                     (bf16*)a.y, part, sync, a.status, a.spin_max, a.L, a.H, a.G, nc)
+                     sinb, bcv, ccv, aux, ug, cbg, (const bf16*)a.z, (const bf16*)a.norm_w,     \
+                     a.eps, (bf16*)a.y, part, sync, a.status, a.spin_max, a.L, a.H, a.G, nc)
   {
     ProfScope ps(st, KID_FAST_OUT);
     // precomputed B and C exist exactly when the conv is on and a group spans

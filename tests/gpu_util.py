@@ -34,6 +34,9 @@ def check(name: str, got, ref, tol: float):
     i = int(np.argmax(excess))
     max_abs = float(diff.max()) if diff.size else 0.0
     max_rel = float((diff / np.maximum(np.abs(ref), 1e-30)).max()) if diff.size else 0.0
+    # the margin: worst |gpu - ref| / (tol + tol |ref|), <= 1 passes (shown with -s)
+    margin = float((diff / (tol + tol * np.abs(ref))).max()) if diff.size else 0.0
+    print(f"  {name}: margin {margin:.3f}")
     assert excess.flat[i] <= 0, (
         f"{name}: |gpu-ref| beyond {tol} at flat index {i}: gpu {got.flat[i]:.6g} ref "
         f"{ref.flat[i]:.6g} (max abs {max_abs:.3e}, max rel {max_rel:.3e})")

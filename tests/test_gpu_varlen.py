@@ -25,12 +25,12 @@ def ops():
     return _ops
 
 
-def batch_case(ops, cfg, lens, slots, has, S, with_bias=False, check_ref=True):
+def batch_case(ops, cfg, lens, slots, has, S, with_bias=False, check_ref=True, slow=False):
     import torch
     bf = torch.bfloat16
     T = int(sum(lens))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    prm = synth.layer_params(cfg, with_bias=with_bias)
+    prm = synth.layer_params(cfg, slow_decay=slow, with_bias=with_bias)
     inp = synth.prefill_inputs(cfg, batch=1, seqlen=T)
     r = np.random.default_rng(cfg.index + 77)
     cpool = synth.to_io(np.sqrt(0.1) * r.standard_normal((S, cfg.conv_width - 1, cfg.channels)),
@@ -76,6 +76,20 @@ def test_mixed_prefill_and_decode(ops, kw):
     batch_case(ops, cfg, lens, slots, has, S=11)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(nheads=64)])
+def test_mixed_batch_bias_slow_decay(ops, kw):
+    """Conv bias and slow decay in a ragged batch: the chunk kernels carry
+    each sequence's state split into S' + a bbar^T (the carried-in slot
+    state split by projection), per-chunk rows in the ragged chunk table;
+    prefills of 600, 257 and 2 tokens beside decode steps and an empty
+    sequence, some slots fresh."""
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], **kw)
+    lens = [600, 1, 257, 0, 2, 1]
+    slots = [4, 0, 2, 5, 1, 3]
+    has = [1, 1, 0, 1, 1, 0]
+    batch_case(ops, cfg, lens, slots, has, S=6, with_bias=True, slow=True)
+
+
 def test_decode_only_batch(ops):
     """64 one-token sequences on a pool of 96 (a decode step of the serving
     engine through the batched entry), large-layer head count."""
@@ -85,19 +99,24 @@ def test_decode_only_batch(ops):
     batch_case(ops, cfg, [1] * 64, slots, None, S=96)
 
 
-def test_single_sequence_matches_prefill_entry(ops):
+@pytest.mark.parametrize("kw,with_bias", [(dict(), False), (dict(), True),
+                                          (dict(nheads=64), True)])
+def test_single_sequence_matches_prefill_entry(ops, kw, with_bias):
     """One sequence through the batched entry gives the dense prefill entry's
-    output and states bit for bit (same kernels, same chunks)."""
+    output and states bit for bit (same kernels, same chunks); with a conv
+    bias the state split's per-chunk rows sit at the ragged chunk indices."""
     import torch
     bf = torch.bfloat16
-    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=700)
-    out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, [700], [2], [1], S=3)
-    prm = synth.layer_params(cfg)
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=700, **kw)
+    out, gc, gs, rc, cpool, spool = batch_case(ops, cfg, [700], [2], [1], S=3,
+                                               with_bias=with_bias)
+    prm = synth.layer_params(cfg, with_bias=with_bias)
     inp = synth.prefill_inputs(cfg, batch=1, seqlen=700)
     d = ops.SSDDims(1, 700, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 128, bf)
     cs, ss = dev(cpool[2:3], bf), dev(spool[2:3])
+    cb = dev(prm["conv_b"], bf) if with_bias else None
     o = ops.ssd_mixer_prefill(d, dev(inp["xbc"], bf), dev(inp["z"], bf), dev(inp["dt"], bf),
-                              dev(prm["A"]), dev(prm["D"]), dev(prm["conv_w"], bf), None,
+                              dev(prm["A"]), dev(prm["D"]), dev(prm["conv_w"], bf), cb,
                               dev(prm["norm_w"], bf), prm["eps"], cs, cs, ss, ss)
     assert np.array_equal(host(o)[0], out)
     assert np.array_equal(host(ss)[0], gs[2]) and np.array_equal(host(cs)[0], gc[2])
