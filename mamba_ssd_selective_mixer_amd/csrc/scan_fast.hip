@@ -1479,7 +1479,7 @@ bool fast_path_ok(bool io_bf16, int P, int N, int H, int G, int Q, int W, bool c
 // (da, a_in, sc'_in); when a group spans several 4-head blocks, the per-row
 // partial sums and the ticket counters of the cross-block norm and, with the
 // conv, the convolved B and C rows in fp16 for the output kernel (and, with
-// a bias, u_t and v_t per token and group).
+// a bias, u_t per token and group).
 namespace {
 size_t ws_round(size_t b) { return (b + 255) / 256 * 256; }
 bool wide(int H, int G) { return H / G > fast::HB; }

@@ -41,6 +41,7 @@ def group_problem(cfg, g, xbc, z, dt, prm, conv_state=None, ssm_state=None):
     sub = dict(xbc=xbc[..., chans], z=None if z is None else z[..., g * S:(g + 1) * S],
                dt=dt[..., heads], A=prm["A"][heads], D=prm["D"][heads],
                conv_w=prm["conv_w"][chans], norm_w=prm["norm_w"][g * S:(g + 1) * S],
+               conv_b=None if prm["conv_b"] is None else prm["conv_b"][chans],
                conv_in=None if conv_state is None else conv_state[..., chans],
                s_in=None if ssm_state is None else ssm_state[:, heads])
     return sub, chans, heads
@@ -61,39 +62,51 @@ def test_tiny_model_layer_prefill_full(env):
     check("c1 out", host(out), ref["out"], TOLB)
 
 
-def test_large_layer_prefill_full(env):
+def cb_dev(prm, bf):
+    return None if prm["conv_b"] is None else dev(prm["conv_b"], bf)
+
+
+@pytest.mark.parametrize("bias_slow", [False, True])
+def test_large_layer_prefill_full(env, bias_slow):
     """1 x 8192 tokens, 256 heads x 64 (32 heads per norm group), chunk 256,
-    final conv and SSM state returned; groups 0 and 7 checked exactly."""
+    final conv and SSM state returned; groups 0 and 7 checked exactly. With
+    bias_slow, a conv bias and slowly decaying heads (A ~ -U(0.005, 0.05)):
+    the state grows along the B offset over thousands of tokens, the case the
+    fused kernels' state split is for."""
     torch, ops = env
     cfg = synth.CONFIGS["large_layer"]
-    prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
+    prm = synth.layer_params(cfg, slow_decay=bias_slow, with_bias=bias_slow)
+    inp = synth.prefill_inputs(cfg)
     bf = torch.bfloat16
     cs = torch.empty(1, cfg.conv_width - 1, cfg.channels, dtype=bf, device="cuda")
     ss = torch.empty(1, cfg.nheads, cfg.headdim, cfg.dstate, device="cuda")
     out = ops.ssd_mixer_prefill(dims(ops, torch, cfg), dev(inp["xbc"], bf), dev(inp["z"], bf),
                                 dev(inp["dt"], bf), dev(prm["A"]), dev(prm["D"]),
-                                dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"],
-                                None, cs, None, ss)
+                                dev(prm["conv_w"], bf), cb_dev(prm, bf),
+                                dev(prm["norm_w"], bf), prm["eps"], None, cs, None, ss)
     out_h, ss_h, cs_h = host(out), host(ss), host(cs)
     hpg = cfg.nheads // cfg.ngroups
     S = hpg * cfg.headdim
     for g in (0, 7):
         sub, chans, heads = group_problem(cfg, g, inp["xbc"], inp["z"], inp["dt"], prm)
         ref = oracle.mixer_prefill(sub["xbc"], sub["z"], sub["dt"], sub["A"], sub["D"],
-                                   sub["conv_w"], None, sub["norm_w"], prm["eps"], hpg,
+                                   sub["conv_w"], sub["conv_b"], sub["norm_w"], prm["eps"], hpg,
                                    cfg.headdim, 1, cfg.dstate)
         check(f"c2 out group {g}", out_h[..., g * S:(g + 1) * S], ref["out"], TOLB)
         check(f"c2 final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
         assert np.array_equal(cs_h[..., chans], ref["conv_out"])
 
 
-def test_long_context_chain_full(env):
+@pytest.mark.parametrize("bias_slow", [False, True])
+def test_long_context_chain_full(env, bias_slow):
     """16 pieces of 8192 tokens (131072 in all), each resuming from the
     previous piece's states, against ONE single-shot fp64 run over all the
-    tokens (groups 0 and 5)."""
+    tokens (groups 0 and 5). With bias_slow, a conv bias and slowly decaying
+    heads: every piece's carried-in state already holds the large part along
+    the B offset, which the fused kernels split off by projection."""
     torch, ops = env
     cfg = synth.CONFIGS["long_context"]
-    prm = synth.layer_params(cfg)
+    prm = synth.layer_params(cfg, slow_decay=bias_slow, with_bias=bias_slow)
     bf = torch.bfloat16
     d = dims(ops, torch, cfg)
     cs = torch.zeros(1, cfg.conv_width - 1, cfg.channels, dtype=bf, device="cuda")
@@ -106,8 +119,9 @@ def test_long_context_chain_full(env):
     for k in range(cfg.pieces):
         inp = synth.prefill_inputs(cfg, piece=k)
         out = ops.ssd_mixer_prefill(d, dev(inp["xbc"], bf), dev(inp["z"], bf), dev(inp["dt"], bf),
-                                    dev(prm["A"]), dev(prm["D"]), dev(prm["conv_w"], bf), None,
-                                    dev(prm["norm_w"], bf), prm["eps"], cs, cs, ss, ss)
+                                    dev(prm["A"]), dev(prm["D"]), dev(prm["conv_w"], bf),
+                                    cb_dev(prm, bf), dev(prm["norm_w"], bf), prm["eps"], cs, cs,
+                                    ss, ss)
         oh = host(out)
         for g in groups:
             got[g].append(oh[..., g * S:(g + 1) * S])
@@ -121,7 +135,7 @@ def test_long_context_chain_full(env):
         xbc = np.concatenate(parts[g]["xbc"], axis=1)
         ref = oracle.mixer_prefill(xbc, np.concatenate(parts[g]["z"], axis=1),
                                    np.concatenate(parts[g]["dt"], axis=1), sub["A"], sub["D"],
-                                   sub["conv_w"], None, sub["norm_w"], prm["eps"], hpg,
+                                   sub["conv_w"], sub["conv_b"], sub["norm_w"], prm["eps"], hpg,
                                    cfg.headdim, 1, cfg.dstate)
         check(f"c3 out group {g}", np.concatenate(got[g], axis=1), ref["out"], TOLB)
         check(f"c3 final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
