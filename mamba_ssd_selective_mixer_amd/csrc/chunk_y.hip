@@ -18,7 +18,10 @@ constexpr int kStatusNonFinite = 2;  // status bit: an output is not finite
 // Wave w owns rows 16 w .. 16 w + 15 of the chunk: C B^T on the ten causal
 // 16x16 tiles (three per wave at most) and C S_in^T on its rows over 32-wide
 // slices of n (the next slice's loads in flight while one is computed), M
-// into LDS, then M X over its rows from the chunk's x rows staged in LDS.
+// into LDS, then M X over its rows from the chunk's x staged transposed in
+// LDS. The contraction order is free, so within each 16-wide block of k the
+// four MFMA steps take k = 16 j + 4 (l / 16) + s (s = 0..3) for lane l: each
+// lane reads its four k values of both operands as one 16-byte LDS read.
 template <class T, class TX, class TY, int P>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
     const TX* __restrict__ x, int64_t xs, const TX* __restrict__ Bm, const TX* __restrict__ Cm,
@@ -70,15 +73,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
     rs.store(Ss);
     __syncthreads();
     if (n0 + kKS < N) fetch(n0 + kKS);
-    for (int kk = 0; kk < nv; kk += 4) {
+    // nv is a multiple of 16 (so is every supported N)
+    for (int kk = 0; kk < nv; kk += 16) {
+      const int kq = kk + 4 * lk;
 #pragma unroll
       for (int i = 0; i < 3; ++i)
-        if (on[i])
-          aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk], Bs[(st[i] * 16 + lr) * kSP + kk + lk],
-                      aG[i]);
-      const float a = Cs[(sw + lr) * kSP + kk + lk];
+        if (on[i]) {
+          const float4 a4 = ld4(Cs + (rt[i] * 16 + lr) * kSP + kq);
+          const float4 b4 = ld4(Bs + (st[i] * 16 + lr) * kSP + kq);
+          aG[i] = mma(a4.x, b4.x, aG[i]);
+          aG[i] = mma(a4.y, b4.y, aG[i]);
+          aG[i] = mma(a4.z, b4.z, aG[i]);
+          aG[i] = mma(a4.w, b4.w, aG[i]);
+        }
+      const float4 a4 = ld4(Cs + (sw + lr) * kSP + kq);
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) aY[pt] = mma(a, Ss[(pt * 16 + lr) * kSP + kk + lk], aY[pt]);
+      for (int pt = 0; pt < NPT; ++pt) {
+        const float4 b4 = ld4(Ss + (pt * 16 + lr) * kSP + kq);
+        aY[pt] = mma(a4.x, b4.x, aY[pt]);
+        aY[pt] = mma(a4.y, b4.y, aY[pt]);
+        aY[pt] = mma(a4.z, b4.z, aY[pt]);
+        aY[pt] = mma(a4.w, b4.w, aY[pt]);
+      }
     }
     __syncthreads();
   }
@@ -96,16 +112,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
   for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
-  // the chunk's x rows, where B and C were staged
-  float* Xs = Bs;  // [Q][P + 16]
-  stage_rows(Xs, P + 16, xr, xsi, kQ, len, P);
+  // the chunk's x transposed, [p][t], where B and C were staged
+  float* Xt = Bs;
+  stage_cols(Xt, kQP, xr, xsi, kQ, len, P);
   __syncthreads();
   // + M X over s <= t (the wave's rows reach s < sw + 16)
-  for (int k0 = 0; k0 < sw + 16; k0 += 4) {
-    const float a = Mt[(sw + lr) * kQP + k0 + lk];
+  for (int k0 = 0; k0 < sw + 16; k0 += 16) {
+    const int kq = k0 + 4 * lk;
+    const float4 a4 = ld4(Mt + (sw + lr) * kQP + kq);
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-      aY[pt] = mma(a, Xs[(k0 + lk) * (P + 16) + pt * 16 + lr], aY[pt]);
+    for (int pt = 0; pt < NPT; ++pt) {
+      const float4 b4 = ld4(Xt + (pt * 16 + lr) * kQP + kq);
+      aY[pt] = mma(a4.x, b4.x, aY[pt]);
+      aY[pt] = mma(a4.y, b4.y, aY[pt]);
+      aY[pt] = mma(a4.z, b4.z, aY[pt]);
+      aY[pt] = mma(a4.w, b4.w, aY[pt]);
+    }
   }
   float chk = 0.f;  // NaN once an output is infinite or NaN
 #pragma unroll
@@ -114,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
     for (int r = 0; r < 4; ++r) {
       const int t = sw + 4 * lk + r, p = pt * 16 + lr;
       if (t < len) {
-        const float yv = aY[pt][r] + Dh * Xs[t * (P + 16) + p];
+        const float yv = aY[pt][r] + Dh * Xt[p * kQP + t];
         chk += yv * 0.f;
         y[(row0 + t) * HP + (int64_t)h * P + p] = from_f<TY>(yv);
       }
@@ -123,8 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
 }
 
 size_t chunk_y_lds(int P) {
-  const size_t slices = 2 * (size_t)kQ * kSP + (size_t)P * kSP, xrows = (size_t)kQ * (P + 16);
-  return ((size_t)kQ * kQP + std::max(slices, xrows)) * 4;
+  const size_t slices = 2 * (size_t)kQ * kSP + (size_t)P * kSP, xcols = (size_t)P * kQP;
+  return ((size_t)kQ * kQP + std::max(slices, xcols)) * 4;
 }
 
 }  // namespace f32t

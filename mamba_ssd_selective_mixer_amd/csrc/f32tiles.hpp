@@ -81,6 +81,23 @@ SSD_DEV void stage_rows(float* dst, int pitch, const TX* src, int rs, int rows, 
   }
 }
 
+// The same rows transposed: dst [cols][pitch], element (r, c) at c * pitch +
+// r, so a column's consecutive rows are contiguous (k-contiguous operand
+// reads for a contraction over the rows); rows >= nrows are zero.
+template <class TX>
+SSD_DEV void stage_cols(float* dst, int pitch, const TX* src, int rs, int rows, int nrows,
+                        int cols) {
+  const int c4n = cols / 4;
+  for (int i = threadIdx.x; i < rows * c4n; i += kThreads) {
+    const int r = i % rows, c4 = (i / rows) * 4;
+    const float4 v = r < nrows ? ld4(src + r * rs + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    dst[(c4 + 0) * pitch + r] = v.x;
+    dst[(c4 + 1) * pitch + r] = v.y;
+    dst[(c4 + 2) * pitch + r] = v.z;
+    dst[(c4 + 3) * pitch + r] = v.w;
+  }
+}
+
 // The ten causal 16x16 tiles (rt, st), st <= rt, of a 64 x 64 block spread
 // over the four waves (at most three each): whether slot i of wave w holds one.
 SSD_DEV bool causal_tile(int w, int i, int& rt, int& st) {
