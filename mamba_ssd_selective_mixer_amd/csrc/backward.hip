@@ -164,8 +164,10 @@ __global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict_
 
 // ---------------------------------------------------------------- dS_in part
 // Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one (chunk, head), into zb.
-// The chunk's rows of exp(Lam_t) dY and of C are staged in LDS; work items
-// (16-row tile of p, up to 8 tiles of n) go round the waves.
+// The chunk's exp(Lam_t) dY and C are staged transposed in LDS ([p][t],
+// [n][t]), so each lane reads four consecutive t of both operands in one
+// 16-byte read (k-permuted MFMA steps, as in the chunk-output kernel); work
+// items (16-row tile of p, up to 8 tiles of n) go round the waves.
 template <class T, int P>
 __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ v,
                                                       const float* __restrict__ dY,
@@ -174,10 +176,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
                                                       int L, int H, int G, int N, int nc) {
   extern __shared__ __align__(16) float sm[];
   __shared__ float lam[64], dts[64], ex[64];
-  constexpr int NPT = P / 16, YP = P + 16;
-  const int CP = N + 16;
-  float* Ys = sm;            // [Q][YP]: exp(Lam_t) dY[t]
-  float* Cs = sm + kQ * YP;  // [Q][CP]
+  constexpr int NPT = P / 16;
+  float* Yt = sm;             // [P][kQP]: exp(Lam_t) dY[t, p]
+  float* Ct = sm + P * kQP;   // [N][kQP]: C[t, n]
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
   const int t0 = c * kQ, len = min(kQ, L - t0);
@@ -185,23 +186,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
   const int HP = H * P;
   const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, co = HP + (int64_t)(G + g) * N;
   chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
-  stage_rows(Ys, YP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
-  stage_rows(Cs, CP, v + row0 * C + co, (int)C, kQ, len, N);
+  stage_cols(Yt, kQP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
+  stage_cols(Ct, kQP, v + row0 * C + co, (int)C, kQ, len, N);
   __syncthreads();
   float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
   const int nnt = N / 16, nng = (nnt + 7) / 8;
-  const int kend = (len + 3) & ~3;
+  const int kend = (len + 15) & ~15;  // rows past len are zero
   for (int item = wave; item < NPT * nng; item += 4) {
     const int pt = item % NPT, nt0 = (item / NPT) * 8, ntn = min(8, nnt - nt0);
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = zero4();
-    for (int k0 = 0; k0 < kend; k0 += 4) {
-      const int t = k0 + lk;
-      const float a = Ys[t * YP + pt * 16 + lr];
+    for (int k0 = 0; k0 < kend; k0 += 16) {
+      const int kq = k0 + 4 * lk;
+      const float4 a4 = ld4(Yt + (pt * 16 + lr) * kQP + kq);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < ntn) acc[j] = mma(a, Cs[t * CP + (nt0 + j) * 16 + lr], acc[j]);
+        if (j < ntn) {
+          const float4 b4 = ld4(Ct + ((nt0 + j) * 16 + lr) * kQP + kq);
+          acc[j] = mma(a4.x, b4.x, acc[j]);
+          acc[j] = mma(a4.y, b4.y, acc[j]);
+          acc[j] = mma(a4.z, b4.z, acc[j]);
+          acc[j] = mma(a4.w, b4.w, acc[j]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -308,18 +315,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
       rx.store(Xs);
       __syncthreads();
       if (k0 + kKS < kmax) fetch(k0 + kKS);
-      for (int kk = 0; kk < nvn; kk += 4)
+      // k-permuted MFMA steps: a lane's four k values of both operands in
+      // one 16-byte read (nvn and nvp are multiples of 16)
+      for (int kk = 0; kk < nvn; kk += 16)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
-          if (on[i])
-            aG[i] = mma(Cs[(rt[i] * 16 + lr) * kSP + kk + lk],
-                        Bs[(st[i] * 16 + lr) * kSP + kk + lk], aG[i]);
-      for (int kk = 0; kk < nvp; kk += 4)
+          if (on[i]) {
+            const float4 a4 = ld4(Cs + (rt[i] * 16 + lr) * kSP + kk + 4 * lk);
+            const float4 b4 = ld4(Bs + (st[i] * 16 + lr) * kSP + kk + 4 * lk);
+            aG[i] = mma(a4.x, b4.x, aG[i]);
+            aG[i] = mma(a4.y, b4.y, aG[i]);
+            aG[i] = mma(a4.z, b4.z, aG[i]);
+            aG[i] = mma(a4.w, b4.w, aG[i]);
+          }
+      for (int kk = 0; kk < nvp; kk += 16)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
-          if (on[i])
-            aK[i] = mma(Ys[(rt[i] * 16 + lr) * kSP + kk + lk],
-                        Xs[(st[i] * 16 + lr) * kSP + kk + lk], aK[i]);
+          if (on[i]) {
+            const float4 a4 = ld4(Ys + (rt[i] * 16 + lr) * kSP + kk + 4 * lk);
+            const float4 b4 = ld4(Xs + (st[i] * 16 + lr) * kSP + kk + 4 * lk);
+            aK[i] = mma(a4.x, b4.x, aK[i]);
+            aK[i] = mma(a4.y, b4.y, aK[i]);
+            aK[i] = mma(a4.z, b4.z, aK[i]);
+            aK[i] = mma(a4.w, b4.w, aK[i]);
+          }
       __syncthreads();
     }
 #pragma unroll
@@ -426,10 +445,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
         const int p = i / nv, n = i % nv;
         cstp += Ss[p * kSP + n] * Ds[p * kSP + n];
       }
-      for (int kk = 0; kk < nv; kk += 4) {
-        const float ab = Bs[(sw + lr) * kSP + kk + lk];
+      for (int kk = 0; kk < nv; kk += 16) {  // k-permuted steps, nv a multiple of 16
+        const float4 a4 = ld4(Bs + (sw + lr) * kSP + kk + 4 * lk);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) a2[pt] = mma(ab, Ds[(pt * 16 + lr) * kSP + kk + lk], a2[pt]);
+        for (int pt = 0; pt < NPT; ++pt) {
+          const float4 b4 = ld4(Ds + (pt * 16 + lr) * kSP + kk + 4 * lk);
+          a2[pt] = mma(a4.x, b4.x, a2[pt]);
+          a2[pt] = mma(a4.y, b4.y, a2[pt]);
+          a2[pt] = mma(a4.z, b4.z, a2[pt]);
+          a2[pt] = mma(a4.w, b4.w, a2[pt]);
+        }
       }
       for (int nt = 0; nt < nv / 16; ++nt) {
         f32x4 dc = zero4(), db = zero4();
@@ -648,7 +673,7 @@ size_t bwd_chunk_lds(int P) {
   return (2 * (size_t)bwd::kQ * bwd::kQP + std::max(std::max(stage1, fm), std::max(ys, stage4))) *
          4;
 }
-size_t bwd_z_lds(int P, int N) { return (size_t)bwd::kQ * ((P + 16) + (N + 16)) * 4; }
+size_t bwd_z_lds(int P, int N) { return (size_t)(P + N) * bwd::kQP * 4; }
 }  // namespace
 
 size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {

@@ -83,14 +83,22 @@ SSD_DEV void stage_rows(float* dst, int pitch, const TX* src, int rs, int rows, 
 
 // The same rows transposed: dst [cols][pitch], element (r, c) at c * pitch +
 // r, so a column's consecutive rows are contiguous (k-contiguous operand
-// reads for a contraction over the rows); rows >= nrows are zero.
+// reads for a contraction over the rows); scaled per row by sc[r] when sc
+// is given; rows >= nrows are zero.
 template <class TX>
 SSD_DEV void stage_cols(float* dst, int pitch, const TX* src, int rs, int rows, int nrows,
-                        int cols) {
+                        int cols, const float* sc = nullptr) {
   const int c4n = cols / 4;
   for (int i = threadIdx.x; i < rows * c4n; i += kThreads) {
     const int r = i % rows, c4 = (i / rows) * 4;
-    const float4 v = r < nrows ? ld4(src + r * rs + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 v = r < nrows ? ld4(src + r * rs + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (sc && r < nrows) {
+      const float f = sc[r];
+      v.x *= f;
+      v.y *= f;
+      v.z *= f;
+      v.w *= f;
+    }
     dst[(c4 + 0) * pitch + r] = v.x;
     dst[(c4 + 1) * pitch + r] = v.y;
     dst[(c4 + 2) * pitch + r] = v.z;
