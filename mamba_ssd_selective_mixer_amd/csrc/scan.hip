@@ -121,7 +121,11 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
       for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<O>(bv[j]);
     }
     __syncthreads();
-    const int kk = M::KPL * (lane >> 4), rr = lane & 15;
+    // fp32 operands: k-permuted steps, the MFMA steps of a 16-wide k block
+    // taking k = 4 (l / 16) + s for lane l, so a lane's four k values of both
+    // operands are one 16-byte read (the contraction order is free)
+    constexpr bool kF32 = std::is_same<O, float>::value;
+    const int kk = (kF32 ? 4 : M::KPL) * (lane >> 4), rr = lane & 15;
 #pragma unroll
     for (int i = 0; i < kMaxTPW; ++i) {
       const int tile = wave + 4 * i;
@@ -129,9 +133,21 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
         const int tp = tile / ntn, tn = tile % ntn;
         const O* ap = XwT + (tp * 16 + rr) * KP + kk;
         const O* bp = BT + (tn * 16 + rr) * KP + kk;
+        if constexpr (kF32) {
 #pragma unroll
-        for (int k = 0; k < kStateSB; k += M::KSTEP)
-          acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
+          for (int k = 0; k < kStateSB; k += 16) {
+            const float4 a4 = *reinterpret_cast<const float4*>(ap + k);
+            const float4 b4 = *reinterpret_cast<const float4*>(bp + k);
+            acc[i] = M::mma(a4.x, b4.x, acc[i]);
+            acc[i] = M::mma(a4.y, b4.y, acc[i]);
+            acc[i] = M::mma(a4.z, b4.z, acc[i]);
+            acc[i] = M::mma(a4.w, b4.w, acc[i]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < kStateSB; k += M::KSTEP)
+            acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
+        }
       }
     }
     __syncthreads();
