@@ -575,34 +575,34 @@ def secondary(torch, ops, synth, args, which):
     wl = {}
     ke = not args.no_kernel_events
     if "tiny" in which:
-        c1 = synth.CONFIGS["tiny_layer"]
-        ms, kern, rc = prefill_workload(torch, ops, synth, c1, max(10, args.steps), 3, 4, False,
+        tiny_cfg = synth.CONFIGS["tiny_layer"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, tiny_cfg, max(10, args.steps), 3, 4, False,
                                         False, ke)
-        wl["tiny_layer_prefill"] = dict(summarize_prefill(c1, ms, kern, False, False), status=rc,
+        wl["tiny_layer_prefill"] = dict(summarize_prefill(tiny_cfg, ms, kern, False, False), status=rc,
                                         config="4 x 2048 tokens, 32 heads x 64, 8 groups, state "
                                                "128, chunk 128, bf16, no states")
     if "chain" in which:
-        c3 = synth.CONFIGS["long_context"]
-        ms, kern = run_chain(torch, ops, synth, c3, 3, ke)
-        tokens = c3.seqlen * c3.pieces
-        nb = prefill_bytes(c3, True, True) * c3.pieces
+        chain_cfg = synth.CONFIGS["long_context"]
+        ms, kern = run_chain(torch, ops, synth, chain_cfg, 3, ke)
+        tokens = chain_cfg.seqlen * chain_cfg.pieces
+        nb = prefill_bytes(chain_cfg, True, True) * chain_cfg.pieces
         wl["long_context_chain"] = {
             "tokens_per_s": tokens / (ms * 1e-3), "ms_per_chain": ms,
-            "us_per_piece": ms * 1e3 / c3.pieces,
-            "algorithmic_bytes_per_piece": nb // c3.pieces,
+            "us_per_piece": ms * 1e3 / chain_cfg.pieces,
+            "algorithmic_bytes_per_piece": nb // chain_cfg.pieces,
             "hbm_frac": nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "kernels_us": {k: v * 1e3 for k, v in kern.items()},
             "config": "16 pieces of 1 x 8192 tokens, 32 heads x 64, 8 groups, state 128, "
                       "each resuming from the previous piece's conv and SSM state"}
     if "decode" in which:
-        c4 = synth.CONFIGS["decode_loop"]
-        ms, kern = run_decode(torch, ops, synth, c4, 3, ke)
-        b4 = decode_bytes(c4) * c4.steps
-        wl["decode"] = {"tokens_per_s": c4.batch * c4.steps / (ms * 1e-3),
-                        "us_per_step": ms * 1e3 / c4.steps,
-                        "algorithmic_bytes_per_step": decode_bytes(c4),
-                        "hbm_gbs": b4 / (ms * 1e-3) / 1e9,
-                        "hbm_frac": b4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        dec_cfg = synth.CONFIGS["decode_loop"]
+        ms, kern = run_decode(torch, ops, synth, dec_cfg, 3, ke)
+        dec_bytes = decode_bytes(dec_cfg) * dec_cfg.steps
+        wl["decode"] = {"tokens_per_s": dec_cfg.batch * dec_cfg.steps / (ms * 1e-3),
+                        "us_per_step": ms * 1e3 / dec_cfg.steps,
+                        "algorithmic_bytes_per_step": decode_bytes(dec_cfg),
+                        "hbm_gbs": dec_bytes / (ms * 1e-3) / 1e9,
+                        "hbm_frac": dec_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "kernels_us": {k: v * 1e3 for k, v in kern.items()},
                         "config": "256 sequences x 64 steps, 256 heads x 64, 8 groups, "
                                   "state 128, states ~ N(0, 0.1) updated in place"}
@@ -611,25 +611,25 @@ def secondary(torch, ops, synth, args, which):
     if "backward" in which:
         wl["large_layer_backward"] = run_backward(torch, ops, synth, 3, ke)
     if "unpacked" in which:
-        c2 = synth.CONFIGS["large_layer"]
-        ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
+        large_cfg = synth.CONFIGS["large_layer"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, large_cfg, max(10, args.steps), 3, 2, False,
                                         True, ke)
         wl["large_layer_prefill_unpacked"] = dict(
-            summarize_prefill(c2, ms, kern, False, True), status=rc,
+            summarize_prefill(large_cfg, ms, kern, False, True), status=rc,
             config="the headline layer and inputs with x | B | C, z and dt (already softplus-ed) "
                    "as separate tensors and A given")
     if "bias" in which:
-        c2 = synth.CONFIGS["large_layer"]
-        ms, kern, rc = prefill_workload(torch, ops, synth, c2, max(10, args.steps), 3, 2, False,
+        large_cfg = synth.CONFIGS["large_layer"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, large_cfg, max(10, args.steps), 3, 2, False,
                                         True, ke, packed=True, bias=True)
         wl["large_layer_prefill_conv_bias"] = dict(
-            summarize_prefill(c2, ms, kern, False, True), status=rc,
+            summarize_prefill(large_cfg, ms, kern, False, True), status=rc,
             config="the headline layer and packed rows with a conv bias ~ N(0, 0.25): the "
                    "fused kernels carry the state split S' + a bbar^T")
     if "general" in which:
-        c0 = synth.CONFIGS["tiny_fp32"]
-        ms, kern, rc = prefill_workload(torch, ops, synth, c0, 50, 5, 1, False, False, ke)
-        wl["tiny_fp32_layer"] = dict(summarize_prefill(c0, ms, kern, False, False), status=rc,
+        fp32_cfg = synth.CONFIGS["tiny_fp32"]
+        ms, kern, rc = prefill_workload(torch, ops, synth, fp32_cfg, 50, 5, 1, False, False, ke)
+        wl["tiny_fp32_layer"] = dict(summarize_prefill(fp32_cfg, ms, kern, False, False), status=rc,
                                      config="1 x 256 tokens, 4 heads x 16, 1 group, state 16, "
                                             "chunk 64, fp32 (general kernels)")
         cg = synth.replace(synth.CONFIGS["tiny_layer"], dstate=64)

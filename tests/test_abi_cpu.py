@@ -44,8 +44,8 @@ def test_exports_every_declared_symbol(lib):
 def test_validate_configs(lib):
     for name, entry in [("tiny_fp32", 4), ("tiny_layer", 4), ("large_layer", 4), ("long_context", 4), ("tiny_layer", 1), ("tiny_fp32", 0)]:
         assert lib.ssd_validate(entry, ctypes.byref(dims(synth.CONFIGS[name]))) == 0, name
-    c4 = synth.CONFIGS["decode_loop"]
-    assert lib.ssd_validate(3, ctypes.byref(dims(c4, chunk=128))) == 0
+    dec = synth.CONFIGS["decode_loop"]
+    assert lib.ssd_validate(3, ctypes.byref(dims(dec, chunk=128))) == 0
 
 
 @pytest.mark.parametrize("kw,entry,rc", [
@@ -174,18 +174,18 @@ def test_prefill_decode_norm_refuse_before_launch(lib):
 
 
 def test_workspace_sizes(lib):
-    c1 = synth.CONFIGS["tiny_layer"]
-    d = dims(c1)
+    tiny = synth.CONFIGS["tiny_layer"]
+    d = dims(tiny)
     ws = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
-    nc = c1.seqlen // 128
-    assert ws >= c1.batch * nc * c1.nheads * c1.headdim * c1.dstate * 2  # fp16 chunk states
+    nc = tiny.seqlen // 128
+    assert ws >= tiny.batch * nc * tiny.nheads * tiny.headdim * tiny.dstate * 2  # fp16 chunk states
     # the general path (state 64 here): fp32 states of 64-token chunks, fp32 y
-    g = dims(c1, dstate=64)
+    g = dims(tiny, dstate=64)
     wg = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(g))
-    assert wg >= (c1.batch * (c1.seqlen // 64) * c1.nheads * c1.headdim * 64 * 4
-                  + c1.batch * c1.seqlen * c1.hp * 4)
+    assert wg >= (tiny.batch * (tiny.seqlen // 64) * tiny.nheads * tiny.headdim * 64 * 4
+                  + tiny.batch * tiny.seqlen * tiny.hp * 4)
     assert lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d)) >= ws
-    bad = dims(c1, headdim=48)
+    bad = dims(tiny, headdim=48)
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(bad)) == 0
 
 
@@ -194,13 +194,13 @@ def test_workspace_covers_wide_norm_groups(lib):
     the fp16 chunk increments (overwritten in place by the carried-in states),
     the convolved B and C rows the output kernel reads, and the per-row sums
     its blocks exchange."""
-    c2 = synth.CONFIGS["large_layer"]
-    d = dims(c2)
+    large = synth.CONFIGS["large_layer"]
+    d = dims(large)
     ws = lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d))
-    nc = -(-c2.seqlen // 128)
-    states = c2.batch * nc * c2.nheads * c2.headdim * c2.dstate * 2
-    rows = 2 * c2.batch * c2.seqlen * c2.ngroups * c2.dstate * 2
-    sums = nc * c2.batch * (c2.nheads // 4) * 128 * 4
+    nc = -(-large.seqlen // 128)
+    states = large.batch * nc * large.nheads * large.headdim * large.dstate * 2
+    rows = 2 * large.batch * large.seqlen * large.ngroups * large.dstate * 2
+    sums = nc * large.batch * (large.nheads // 4) * 128 * 4
     assert ws >= states + rows + sums
 
 

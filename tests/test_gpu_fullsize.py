@@ -59,7 +59,7 @@ def test_tiny_model_layer_prefill_full(env):
     ref = oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"], prm["conv_w"],
                                None, prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim,
                                cfg.ngroups, cfg.dstate)
-    check("c1 out", host(out), ref["out"], TOLB)
+    check("tiny layer out", host(out), ref["out"], TOLB)
 
 
 def cb_dev(prm, bf):
@@ -92,8 +92,8 @@ def test_large_layer_prefill_full(env, bias_slow):
         ref = oracle.mixer_prefill(sub["xbc"], sub["z"], sub["dt"], sub["A"], sub["D"],
                                    sub["conv_w"], sub["conv_b"], sub["norm_w"], prm["eps"], hpg,
                                    cfg.headdim, 1, cfg.dstate)
-        check(f"c2 out group {g}", out_h[..., g * S:(g + 1) * S], ref["out"], TOLB)
-        check(f"c2 final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
+        check(f"large layer out group {g}", out_h[..., g * S:(g + 1) * S], ref["out"], TOLB)
+        check(f"large layer final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
         assert np.array_equal(cs_h[..., chans], ref["conv_out"])
 
 
@@ -137,8 +137,8 @@ def test_long_context_chain_full(env, bias_slow):
                                    np.concatenate(parts[g]["dt"], axis=1), sub["A"], sub["D"],
                                    sub["conv_w"], sub["conv_b"], sub["norm_w"], prm["eps"], hpg,
                                    cfg.headdim, 1, cfg.dstate)
-        check(f"c3 out group {g}", np.concatenate(got[g], axis=1), ref["out"], TOLB)
-        check(f"c3 final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
+        check(f"chain out group {g}", np.concatenate(got[g], axis=1), ref["out"], TOLB)
+        check(f"chain final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
         assert np.array_equal(cs_h[..., chans], ref["conv_out"])
 
 
@@ -166,8 +166,8 @@ def test_decode_loop_full(env):
                                           prm["eps"], cfg.nheads, cfg.headdim, cfg.ngroups,
                                           cfg.dstate, rcs, rss)
         if k % 8 == 0 or k == cfg.steps - 1:
-            check(f"c4 out step {k}", host(y[seqs]), ro, TOLB)
-    check("c4 final SSM state", host(ss[seqs]), rss, TOLB)
+            check(f"decode out step {k}", host(y[seqs]), ro, TOLB)
+    check("decode final SSM state", host(ss[seqs]), rss, TOLB)
     assert np.array_equal(host(cs[seqs]), rcs)
 
 

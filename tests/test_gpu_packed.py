@@ -146,6 +146,6 @@ def test_large_layer_prefill_packed_full(ops):
         ref = oracle.mixer_prefill_packed(sub, prm["dt_bias"][heads], prm["A_log"][heads],
                                           prm["D"][heads], prm["conv_w"][xc], None,
                                           prm["norm_w"][zc], prm["eps"], hpg, cfg.headdim, 1, N)
-        check(f"packed c2 out group {g}", out_h[..., g * S:(g + 1) * S], ref["out"], TOL["bf16"])
-        check(f"packed c2 state group {g}", ss_h[:, heads], ref["s_out"], TOL["bf16"])
+        check(f"packed large layer out group {g}", out_h[..., g * S:(g + 1) * S], ref["out"], TOL["bf16"])
+        check(f"packed large layer state group {g}", ss_h[:, heads], ref["s_out"], TOL["bf16"])
         assert np.array_equal(cs_h[..., xc], ref["conv_out"])

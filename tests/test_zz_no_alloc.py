@@ -67,9 +67,9 @@ def test_noalloc_refuses_beyond_scratch(ops):
     than the fixed buffer: refused on the host, nothing launched."""
     import ctypes
     from mamba_ssd_selective_mixer_amd import _lib
-    c2 = synth.CONFIGS["large_layer"]
-    d = _lib.Dims(c2.batch, c2.seqlen, c2.nheads, c2.headdim, c2.ngroups, c2.dstate,
-                  c2.conv_width, c2.chunk, _lib.SSD_BF16)
+    large = synth.CONFIGS["large_layer"]
+    d = _lib.Dims(large.batch, large.seqlen, large.nheads, large.headdim, large.ngroups,
+                  large.dstate, large.conv_width, large.chunk, _lib.SSD_BF16)
     lib = _lib.load()
     assert lib.ssd_mixer_prefill_workspace_bytes(ctypes.byref(d)) > 64 << 20
     V = ctypes.c_void_p
