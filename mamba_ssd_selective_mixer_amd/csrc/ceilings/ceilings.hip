@@ -1,4 +1,4 @@
-// Machine ceilings measured on the box the benchmark runs on, so the mixer
+// Machine ceilings measured on the GPU the benchmark runs on, so the mixer
 // kernels' fractions can be read against what this GPU reaches with the
 // simplest possible kernel of each kind (a separate library: nothing of the
 // mixer path uses it).
