@@ -241,6 +241,54 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 }
 
 // ---------------------------------------------------------------- chunk grads
+constexpr int kNS = 16;        // width (in n) of the per-chunk gradient kernel's state slices
+constexpr int kBP = kNS + 4;   // pitch of such a slice stored as rows
+
+// Rows [0, ROWS) x columns [0, kNS) of a row-major fp32 matrix held in
+// registers between their global loads and their LDS stores (the next
+// slice's loads in flight while one is computed on); rows >= nrows are
+// zero. Stored as rows (element (r, c) at r pitch + c) or transposed (at
+// c pitch + r).
+template <int ROWS>
+struct NSlice {
+  static constexpr int kItems = ROWS * (kNS / 4), kN = (kItems + kThreads - 1) / kThreads;
+  float4 v[kN];
+  SSD_DEV void load(const float* src, int rs, int nrows) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx / (kNS / 4), c4 = (idx % (kNS / 4)) * 4;
+      v[i] = (idx < kItems && r < nrows) ? ld4(src + (int64_t)r * rs + c4)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  SSD_DEV void store_rows(float* dst, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx / (kNS / 4), c4 = (idx % (kNS / 4)) * 4;
+      if (idx < kItems) st4(dst + r * pitch + c4, v[i]);
+    }
+  }
+  SSD_DEV void store_cols(float* dst, int pitch) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx / (kNS / 4), c4 = (idx % (kNS / 4)) * 4;
+      if (idx < kItems) {
+        dst[(c4 + 0) * pitch + r] = v[i].x;
+        dst[(c4 + 1) * pitch + r] = v[i].y;
+        dst[(c4 + 2) * pitch + r] = v[i].z;
+        dst[(c4 + 3) * pitch + r] = v[i].w;
+      }
+    }
+  }
+};
+
+SSD_DEV f32x4 mma4(float4 a, float4 b, f32x4 c) {
+  c = mma(a.x, b.x, c);
+  c = mma(a.y, b.y, c);
+  c = mma(a.z, b.z, c);
+  return mma(a.w, b.w, c);
+}
+
 // One (chunk, head, batch): dX into dv's x channels, this head's share of dB
 // and dC into dBh / dCh [T, H, N], d(dt) into ddt (io dtype), and this
 // chunk's parts of dA and dD into dA / dD [B nc, H] (or dD null).
@@ -266,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   float* SA = sm + 2 * kQ * kQP; // staging
   __shared__ float lam[64], dts[64], ex[64], wv[64], colF[64], Yo[64], U[64], dai[64], tmp[64];
   __shared__ float red[4][2];  // per wave: its share of <dS_out, S_in> and of dD
-  constexpr int NPT = P / 16, KP = P / 4;
+  constexpr int NPT = P / 16;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
   const int t0 = c * kQ, len = min(kQ, L - t0);
@@ -353,35 +401,51 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   }
   __syncthreads();
 
-  // (2) F by columns: thread s walks t down from the chunk's end, keeping
-  // R[t,s] = sum_{t' >= t} F[t',s] (t > s) in place; colF[s] = R[s,s]
+  // (2) F by columns, R[t,s] = sum_{t' >= t} F[t',s] (s <= t < len): wave q
+  // sums its own 16 rows of t from the bottom up (lane s on column s) and
+  // keeps its column totals; R is its in-rows sum plus the totals of the
+  // later waves. K and G take their E dt_s factor in the same pass.
   {
-    float* Fm = SA;  // [Q][kQ + 1]
     constexpr int FP = kQ + 1;
-    if (tid < kQ) {
-      const int s = tid;
+    float* Fm = SA;              // [Q][FP]: sums over the wave's own rows
+    float* tot = SA + kQ * FP;   // [4][Q]: column totals of each wave's rows
+    {
+      const int s = lane;
+      const float ls = lam[s], ds = dts[s];
       float acc = 0.f;
-      for (int t = len - 1; t >= s; --t) {
-        acc += Dg[t * kQP + s] * Mt[t * kQP + s] * __expf(lam[t] - lam[s]);
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        const int t = sw + i;
+        const float e = (s <= t && t < len) ? __expf(lam[t] - ls) : 0.f;
+        const float kv = Dg[t * kQP + s], gv = Mt[t * kQP + s];
+        acc += kv * gv * e;
         Fm[t * FP + s] = acc;
+        const float f = e * ds;
+        Dg[t * kQP + s] = kv * f;
+        Mt[t * kQP + s] = gv * f;
       }
-      colF[s] = acc;
+      tot[wave * kQ + s] = acc;
     }
     __syncthreads();
-    // dai[u] = sum_{s<u} dt_s R[u,s] (four lanes per u), then the dt_s E scaling
+    // dai[u] = sum_{s<u} dt_s R[u,s] (four lanes per u; row u lies in this
+    // wave's rows) and colF[s] = R[s,s]
     {
       const int u = tid >> 2, j = tid & 3;
       float acc = 0.f;
       if (u < len)
-        for (int s = j; s < u; s += 4) acc += dts[s] * Fm[u * FP + s];
+        for (int s = j; s < u; s += 4) {
+          float r = Fm[u * FP + s];
+          for (int q = wave + 1; q < 4; ++q) r += tot[q * kQ + s];
+          acc += dts[s] * r;
+        }
       acc = group_sum_last<4>(acc);
       if (j == 0) dai[u] = acc;
     }
-    for (int i = tid; i < kQ * kQ; i += kThreads) {
-      const int t = i / kQ, s = i % kQ;
-      const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
-      Dg[t * kQP + s] *= f;
-      Mt[t * kQP + s] *= f;
+    if (wave == 0) {
+      const int s = lane;
+      float r = Fm[s * FP + s];
+      for (int q = (s >> 4) + 1; q < 4; ++q) r += tot[q * kQ + s];
+      colF[s] = r;
     }
     __syncthreads();
   }
@@ -404,85 +468,102 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     __syncthreads();
   }
 
-  // (4) over slices of n: B_s dS_out^T of the wave's rows, and the slice's
-  // tiles of dC (rows t) and dB (rows s)
-  float ya[KP], xa[KP];  // A fragments: dY and X of the wave's 16 rows
+  // (4) over 16-wide slices of n: B_s dS_out^T of the wave's rows (a2), and
+  // the slice's tiles of dC (rows t) and dB (rows s). Every product takes
+  // k-permuted steps (a lane's four k values of both operands in one 16-byte
+  // read): B and dS_out are staged both as rows (n contiguous, for a2) and
+  // transposed (k contiguous), C and S_in transposed, and dG is copied
+  // transposed into the space M held; dY and X of the wave's rows sit in
+  // registers, p = 16 j + 4 (l / 16) + (0..3) for lane l.
+  float4 ya[NPT], xa[NPT];
   {
     const int r = sw + lr;
     const bool ok = r < len;
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      ya[k] = ok ? dY[(row0 + r) * HP + xo + 4 * k + lk] : 0.f;
-      xa[k] = ok ? v[(row0 + r) * C + xo + 4 * k + lk] : 0.f;
+    for (int j = 0; j < NPT; ++j) {
+      ya[j] = ok ? ld4(dY + (row0 + r) * HP + xo + 16 * j + 4 * lk) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xa[j] = ok ? ld4(v + (row0 + r) * C + xo + 16 * j + 4 * lk) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  }
+  float* DgT = Mt;  // [Q][kQP]: dG[t, s] at s kQP + t
+  for (int i = tid; i < kQ * kQ / 4; i += kThreads) {
+    const int t = i >> 4, s4 = (i & 15) * 4;
+    const float4 d = ld4(Dg + t * kQP + s4);
+    DgT[(s4 + 0) * kQP + t] = d.x;
+    DgT[(s4 + 1) * kQP + t] = d.y;
+    DgT[(s4 + 2) * kQP + t] = d.z;
+    DgT[(s4 + 3) * kQP + t] = d.w;
   }
   float cstp = 0.f;
   float yp[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's share of Y_t, t = sw + 4 lk + r
   {
-    float* Bs = SA;
-    float* Cs = SA + kQ * kSP;
-    float* Ss = SA + 2 * kQ * kSP;  // [P][kSP]
-    float* Ds = Ss + P * kSP;       // [P][kSP]
-    SliceRegs<kQ> rb, rc;
-    SliceRegs<P> rs, rd;
+    constexpr int TP = P + 4;
+    float* Bs = SA;               // [Q][kBP]: B[s, n]
+    float* Ds = Bs + kQ * kBP;    // [P][kBP]: dS_out[p, n]
+    float* Bt = Ds + P * kBP;     // [kNS][kQP]: B[s, n] at n kQP + s
+    float* Ct = Bt + kNS * kQP;   // [kNS][kQP]: C[t, n] at n kQP + t
+    float* St = Ct + kNS * kQP;   // [kNS][TP]: S_in[p, n] at n TP + p
+    float* Dt = St + kNS * TP;    // [kNS][TP]: dS_out[p, n] at n TP + p
+    NSlice<kQ> rb, rc;
+    NSlice<P> rs, rd;
     auto fetch = [&](int n0) {
-      const int nv = min(kKS, N - n0);
-      rb.load(v + row0 * C + bo + n0, (int)C, len, nv);
-      rc.load(v + row0 * C + co + n0, (int)C, len, nv);
-      rs.load(Si + n0, N, P, nv);
-      rd.load(dS + n0, N, P, nv);
+      rb.load(v + row0 * C + bo + n0, (int)C, len);
+      rc.load(v + row0 * C + co + n0, (int)C, len);
+      rs.load(Si + n0, N, P);
+      rd.load(dS + n0, N, P);
     };
     fetch(0);
-    for (int n0 = 0; n0 < N; n0 += kKS) {
-      const int nv = min(kKS, N - n0);
-      rb.store(Bs);
-      rc.store(Cs);
-      rs.store(Ss);
-      rd.store(Ds);
+    for (int n0 = 0; n0 < N; n0 += kNS) {  // N is a multiple of 16
+      rb.store_rows(Bs, kBP);
+      rb.store_cols(Bt, kQP);
+      rc.store_cols(Ct, kQP);
+      rs.store_cols(St, TP);
+      rd.store_rows(Ds, kBP);
+      rd.store_cols(Dt, TP);
       __syncthreads();
-      if (n0 + kKS < N) fetch(n0 + kKS);
-      for (int i = tid; i < P * nv; i += kThreads) {
-        const int p = i / nv, n = i % nv;
-        cstp += Ss[p * kSP + n] * Ds[p * kSP + n];
+      if (n0 + kNS < N) fetch(n0 + kNS);
+      for (int i = tid; i < kNS * (P / 4); i += kThreads) {
+        const int n = i / (P / 4), p4 = (i % (P / 4)) * 4;
+        const float4 a = ld4(St + n * TP + p4), d = ld4(Dt + n * TP + p4);
+        cstp += (a.x * d.x + a.y * d.y) + (a.z * d.z + a.w * d.w);
       }
-      for (int kk = 0; kk < nv; kk += 16) {  // k-permuted steps, nv a multiple of 16
-        const float4 a4 = ld4(Bs + (sw + lr) * kSP + kk + 4 * lk);
+      {
+        const float4 a4 = ld4(Bs + (sw + lr) * kBP + 4 * lk);
 #pragma unroll
-        for (int pt = 0; pt < NPT; ++pt) {
-          const float4 b4 = ld4(Ds + (pt * 16 + lr) * kSP + kk + 4 * lk);
-          a2[pt] = mma(a4.x, b4.x, a2[pt]);
-          a2[pt] = mma(a4.y, b4.y, a2[pt]);
-          a2[pt] = mma(a4.z, b4.z, a2[pt]);
-          a2[pt] = mma(a4.w, b4.w, a2[pt]);
-        }
+        for (int pt = 0; pt < NPT; ++pt)
+          a2[pt] = mma4(a4, ld4(Ds + (pt * 16 + lr) * kBP + 4 * lk), a2[pt]);
       }
-      for (int nt = 0; nt < nv / 16; ++nt) {
-        f32x4 dc = zero4(), db = zero4();
+      f32x4 dc = zero4(), db = zero4();
 #pragma unroll
-        for (int k = 0; k < KP; ++k) {
-          dc = mma(ya[k], Ss[(4 * k + lk) * kSP + nt * 16 + lr], dc);
-          db = mma(xa[k], Ds[(4 * k + lk) * kSP + nt * 16 + lr], db);
-        }
+      for (int j = 0; j < NPT; ++j) {
+        dc = mma4(ya[j], ld4(St + lr * TP + 16 * j + 4 * lk), dc);
+        db = mma4(xa[j], ld4(Dt + lr * TP + 16 * j + 4 * lk), db);
+      }
+      {
+        // Y_t = sum_n C[t,n] (exp(Lam_t) dY[t] S_in)[n]: the inter part of dC
+        const float4 c4 = ld4(Ct + lr * kQP + sw + 4 * lk);
+        const float cr[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = sw + 4 * lk + r;
           dc[r] *= ex[t];
           db[r] *= wv[t];
-          // Y_t = sum_n C[t,n] (exp(Lam_t) dY[t] S_in)[n]: the inter part of dC
-          yp[r] += Cs[t * kSP + nt * 16 + lr] * dc[r];
+          yp[r] += cr[r] * dc[r];
         }
-        for (int k0 = 0; k0 < sw + 16; k0 += 4)
-          dc = mma(Dg[(sw + lr) * kQP + k0 + lk], Bs[(k0 + lk) * kSP + nt * 16 + lr], dc);
-        for (int k0 = sw; k0 < kQ; k0 += 4)
-          db = mma(Dg[(k0 + lk) * kQP + sw + lr], Cs[(k0 + lk) * kSP + nt * 16 + lr], db);
+      }
+      for (int j = 0; j <= wave; ++j)  // s < sw + 16
+        dc = mma4(ld4(Dg + (sw + lr) * kQP + 16 * j + 4 * lk), ld4(Bt + lr * kQP + 16 * j + 4 * lk),
+                  dc);
+      for (int j = wave; j < 4; ++j)  // t >= sw
+        db = mma4(ld4(DgT + (sw + lr) * kQP + 16 * j + 4 * lk),
+                  ld4(Ct + lr * kQP + 16 * j + 4 * lk), db);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = sw + 4 * lk + r;
-          if (t < len) {
-            const int64_t o = ((row0 + t) * H + h) * N + n0 + nt * 16 + lr;
-            dCh[o] = dc[r];
-            dBh[o] = db[r];
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int t = sw + 4 * lk + r;
+        if (t < len) {
+          const int64_t o = ((row0 + t) * H + h) * N + n0 + lr;
+          dCh[o] = dc[r];
+          dBh[o] = db[r];
         }
       }
       __syncthreads();
@@ -667,9 +748,11 @@ size_t bround(size_t b) { return (b + 255) / 256 * 256; }
 // LDS of the per-chunk kernels (the chunk gradients and the state-gradient
 // terms)
 size_t bwd_chunk_lds(int P) {
-  const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP, fm = (size_t)bwd::kQ * (bwd::kQ + 1),
+  const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP,
+               fm = (size_t)bwd::kQ * (bwd::kQ + 1) + 4 * (size_t)bwd::kQ,
                ys = (size_t)bwd::kQ * (P + 16),
-               stage4 = 2 * (size_t)bwd::kQ * bwd::kSP + 2 * (size_t)P * bwd::kSP;
+               stage4 = (size_t)(bwd::kQ + P) * bwd::kBP + 2 * (size_t)bwd::kNS * bwd::kQP +
+                        2 * (size_t)bwd::kNS * (P + 4);
   return (2 * (size_t)bwd::kQ * bwd::kQP + std::max(std::max(stage1, fm), std::max(ys, stage4))) *
          4;
 }
