@@ -46,7 +46,8 @@ MFMA_F32_PEAK_TFS = 157.3    # dense fp32 MFMA, TFLOP/s
 KERNEL_NAMES = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
                 "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
                 "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z", "bwd_rev_pass",
-                "bwd_chunk", "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx", "bwd_y")
+                "bwd_chunk", "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx", "bwd_y",
+                "chunk_cb")
 DOMINANT = "fused_chunk_out_norm"
 FUSED = ("fused_chunk_state", "fused_state_pass", "fused_chunk_out_norm")
 # Counter-measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE,
@@ -414,17 +415,19 @@ BWD_CHUNK = 64  # chunk length of the backward kernels
 
 
 def backward_flops(cfg):
-    """Algorithmic fp32 MFMA FLOPs per launch of the backward's three matrix
-    kernels (causal products counted over their lower half): the y
-    recompute (C B^T, M X, C S_in^T), the state-gradient terms (Z) and the
-    per-chunk gradients (dY X^T, C B^T, dX's two terms, dC's and dB's two
-    terms each)."""
+    """Algorithmic fp32 MFMA FLOPs per launch of the backward's matrix
+    kernels (causal products counted over their lower half): C B^T once per
+    chunk and group, the y recompute (M X, C S_in^T), the state-gradient
+    terms (Z) and the per-chunk gradients (dY X^T, dX's two terms, dC's and
+    dB's two terms each)."""
     Q, P, N = BWD_CHUNK, cfg.headdim, cfg.dstate
-    units = cfg.batch * cfg.nheads * -(-cfg.seqlen // Q)
+    nc = -(-cfg.seqlen // Q)
+    units = cfg.batch * cfg.nheads * nc
     tri = Q * Q / 2
-    return {"bwd_y": 2 * units * (tri * (N + P) + Q * N * P),
+    return {"chunk_cb": 2 * cfg.batch * cfg.ngroups * nc * tri * N,
+            "bwd_y": 2 * units * (tri * P + Q * N * P),
             "bwd_chunk_z": 2 * units * Q * P * N,
-            "bwd_chunk": 2 * units * (tri * (2 * P + 3 * N) + 3 * Q * P * N)}
+            "bwd_chunk": 2 * units * (tri * (2 * P + 2 * N) + 3 * Q * P * N)}
 
 
 def run_backward(torch, ops, synth, reps, kernel_events=True):
@@ -456,7 +459,7 @@ def run_backward(torch, ops, synth, reps, kernel_events=True):
     for _ in range(reps):
         one()
     ms = tm.stop_ms() / reps
-    kern = kernel_times(ops, one, reps, launches_per_step=16) if kernel_events else {}
+    kern = kernel_times(ops, one, reps, launches_per_step=20) if kernel_events else {}
     status = ops.ssd_workspace_status(ws)
     T = cfg.batch * cfg.seqlen
     # algorithmic bytes: xBC, z, dt and d_out read; d_xBC, d_z, d_dt written

@@ -444,7 +444,9 @@ typedef enum {
   SSD_K_BWD_CONV_DU = 15,    /* backward: SiLU + conv weight gradient */
   SSD_K_BWD_CONV_DX = 16,    /* backward: conv input gradient         */
   SSD_K_BWD_Y = 17,          /* backward: scan output recomputed      */
-  SSD_K_COUNT = 18
+  SSD_K_CHUNK_CB = 18,       /* generic path and backward: C B^T per
+                                chunk and group                       */
+  SSD_K_COUNT = 19
 } ssd_kernel_id;
 int ssd_profile_start(int capacity);
 int ssd_profile_stop(void);

@@ -15,7 +15,7 @@ SSD_F32, SSD_BF16 = 0, 1
 KERNELS = ("conv1d_silu", "conv_state", "gated_rmsnorm", "decode_step", "chunk_state",
            "state_pass", "chunk_out", "fused_chunk_state", "fused_state_pass",
            "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z", "bwd_rev_pass", "bwd_chunk",
-           "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx", "bwd_y")
+           "bwd_group_sum", "bwd_conv_du", "bwd_conv_dx", "bwd_y", "chunk_cb")
 ENTRY = {"conv1d": 0, "chunk_scan": 1, "gated_rmsnorm": 2, "decode_step": 3, "mixer_prefill": 4}
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_DTYPE", -5: "SSD_ERR_ALIAS", -6: "SSD_ERR_WORKSPACE", -7: "SSD_ERR_HIP",

@@ -117,6 +117,7 @@ struct ScanWs {
   float* states;
   float* lam_end;
   float* y32;
+  float* cb;  // each chunk's C B^T per group
   unsigned char* conv;
   void* fastws;
   size_t total;
@@ -140,13 +141,14 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
   };
   w.fast = use_fast(d, conv);
   const size_t o_status = take(4);  // the call's status word (ssd_workspace_status)
-  size_t o_states = 0, o_lam = 0, o_y = 0, o_conv = 0, o_fast = 0;
+  size_t o_states = 0, o_lam = 0, o_y = 0, o_cb = 0, o_conv = 0, o_fast = 0;
   if (w.fast) {
     o_fast = take(ssd::fast_ws_bytes(d->batch, d->seqlen, d->nheads, d->ngroups, conv));
   } else {
     o_states = take(B * nc * H * P * N * 4);
     o_lam = take(B * H * nc * 4);
     o_y = take(B * L * H * P * 4);
+    o_cb = take(ssd::chunk_cb_bytes((int)B, (int)nc, d->ngroups));
     if (conv) o_conv = take(B * L * (size_t)channels(d) * 4);  // fp32 conv output
   }
   w.total = off;
@@ -159,6 +161,7 @@ ScanWs carve(const ssd_dims* d, void* base, bool conv) {
       w.states = (float*)(p + o_states);
       w.lam_end = (float*)(p + o_lam);
       w.y32 = (float*)(p + o_y);
+      w.cb = (float*)(p + o_cb);
       w.conv = conv ? p + o_conv : nullptr;
     }
   }
@@ -183,8 +186,9 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
   if (rc) return rc;
   const bool fused_norm = z != nullptr;
   void* ydst = fused_norm ? (void*)ws.y32 : y;
-  rc = hip_status(ssd::launch_chunk_y(bf, x_f32, fused_norm || !bf, s, x, xs, Bm, Cm, bs, dt, A,
-                                      D, ws.states, ydst, ws.status, ssd::KID_CHUNK_OUT, st));
+  rc = hip_status(ssd::launch_chunk_y(bf, x_f32, fused_norm || !bf, s, x, xs, Bm, Cm, bs, ws.cb,
+                                      dt, A, D, ws.states, ydst, ws.status, ssd::KID_CHUNK_OUT,
+                                      st));
   if (rc) return rc;
   if (fused_norm)
     rc = hip_status(ssd::launch_gated_norm(bf, true, d->batch * d->seqlen,

@@ -305,7 +305,8 @@ template <class T, int P>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
-    const float* __restrict__ dSo, float* __restrict__ dv, float* __restrict__ dBh,
+    const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
+    float* __restrict__ dBh,
     float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD, int L, int H, int G,
     int N, int nc) {
   extern __shared__ __align__(16) float sm[];
@@ -332,70 +333,50 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   const float lamE = lam[len - 1];
   if (tid < 64) wv[tid] = tid < len ? __expf(lamE - lam[tid]) * dts[tid] : 0.f;
 
-  // (1) G = C B^T and K = dY X^T on the causal tiles, over slices of n / p
+  // (1) K = dY X^T on the causal tiles over slices of p; G from the group's
+  // C B^T (computed once per chunk and group)
   {
     int rt[3], st[3];
     bool on[3];
+    f32x4 aK[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
-    f32x4 aG[3], aK[3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) aG[i] = aK[i] = zero4();
-    float* Cs = SA;
-    float* Bs = SA + kQ * kSP;
-    float* Ys = SA + 2 * kQ * kSP;
-    float* Xs = SA + 3 * kQ * kSP;
-    const int kmax = N > P ? N : P;
-    SliceRegs<kQ> rc, rb, ry, rx;
+    for (int i = 0; i < 3; ++i) {
+      on[i] = causal_tile(wave, i, rt[i], st[i]);
+      aK[i] = zero4();
+    }
+    float* Ys = SA;
+    float* Xs = SA + kQ * kSP;
+    SliceRegs<kQ> ry, rx;
     auto fetch = [&](int k0) {
-      const int nvn = min(kKS, N - k0), nvp = min(kKS, P - k0);
-      rc.load(v + row0 * C + co + k0, (int)C, len, nvn);
-      rb.load(v + row0 * C + bo + k0, (int)C, len, nvn);
+      const int nvp = min(kKS, P - k0);
       ry.load(dY + row0 * HP + xo + k0, HP, len, nvp);
       rx.load(v + row0 * C + xo + k0, (int)C, len, nvp);
     };
     fetch(0);
-    for (int k0 = 0; k0 < kmax; k0 += kKS) {
-      const int nvn = min(kKS, N - k0), nvp = min(kKS, P - k0);
-      rc.store(Cs);
-      rb.store(Bs);
+    for (int k0 = 0; k0 < P; k0 += kKS) {
+      const int nvp = min(kKS, P - k0);
       ry.store(Ys);
       rx.store(Xs);
       __syncthreads();
-      if (k0 + kKS < kmax) fetch(k0 + kKS);
+      if (k0 + kKS < P) fetch(k0 + kKS);
       // k-permuted MFMA steps: a lane's four k values of both operands in
-      // one 16-byte read (nvn and nvp are multiples of 16)
-      for (int kk = 0; kk < nvn; kk += 16)
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-          if (on[i]) {
-            const float4 a4 = ld4(Cs + (rt[i] * 16 + lr) * kSP + kk + 4 * lk);
-            const float4 b4 = ld4(Bs + (st[i] * 16 + lr) * kSP + kk + 4 * lk);
-            aG[i] = mma(a4.x, b4.x, aG[i]);
-            aG[i] = mma(a4.y, b4.y, aG[i]);
-            aG[i] = mma(a4.z, b4.z, aG[i]);
-            aG[i] = mma(a4.w, b4.w, aG[i]);
-          }
+      // one 16-byte read (nvp is a multiple of 16)
       for (int kk = 0; kk < nvp; kk += 16)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
-          if (on[i]) {
-            const float4 a4 = ld4(Ys + (rt[i] * 16 + lr) * kSP + kk + 4 * lk);
-            const float4 b4 = ld4(Xs + (st[i] * 16 + lr) * kSP + kk + 4 * lk);
-            aK[i] = mma(a4.x, b4.x, aK[i]);
-            aK[i] = mma(a4.y, b4.y, aK[i]);
-            aK[i] = mma(a4.z, b4.z, aK[i]);
-            aK[i] = mma(a4.w, b4.w, aK[i]);
-          }
+          if (on[i])
+            aK[i] = mma4(ld4(Ys + (rt[i] * 16 + lr) * kSP + kk + 4 * lk),
+                         ld4(Xs + (st[i] * 16 + lr) * kSP + kk + 4 * lk), aK[i]);
       __syncthreads();
     }
+    const float* cbk = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
 #pragma unroll
     for (int i = 0; i < 3; ++i)
       if (on[i])
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
-          Mt[t * kQP + s] = aG[i][r];
+          Mt[t * kQP + s] = cbk[t * kQ + s];
           Dg[t * kQP + s] = aK[i][r];
         }
   }
@@ -748,7 +729,7 @@ size_t bround(size_t b) { return (b + 255) / 256 * 256; }
 // LDS of the per-chunk kernels (the chunk gradients and the state-gradient
 // terms)
 size_t bwd_chunk_lds(int P) {
-  const size_t stage1 = 4 * (size_t)bwd::kQ * bwd::kSP,
+  const size_t stage1 = 2 * (size_t)bwd::kQ * bwd::kSP,
                fm = (size_t)bwd::kQ * (bwd::kQ + 1) + 4 * (size_t)bwd::kQ,
                ys = (size_t)bwd::kQ * (P + 16),
                stage4 = (size_t)(bwd::kQ + P) * bwd::kBP + 2 * (size_t)bwd::kNS * bwd::kQP +
@@ -766,7 +747,7 @@ size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N) {
   return bround(T * C * 4) + bround(T * HP * 4) + 2 * bround(st) + bround((size_t)B * H * nc * 4) +
          2 * bround(T * H * N * 4) + bround(T * C * 4) + bround((size_t)bwd::kNormBlocks * HP * 4) +
          bround((size_t)B * ((L + bwd::kConvTok - 1) / bwd::kConvTok) * C * 5 * 4) +
-         bround((size_t)2 * B * nc * H * 4);
+         bround((size_t)2 * B * nc * H * 4) + bround(chunk_cb_bytes(B, (int)nc, G));
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
@@ -799,6 +780,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   w += bround((size_t)B * ((L + kConvTok - 1) / kConvTok) * C * 5 * 4);
   float* dA_part = (float*)w;  // [B nc, H]: each chunk's part of dA, then of dD
   float* dD_part = dA_part + (size_t)B * nc * H;
+  w += bround((size_t)2 * B * nc * H * 4);
+  float* cb = (float*)w;  // [B nc G][Q][Q]: each chunk's C B^T per group
   const DtA plain{H, nullptr};
   const dim3 gc(nc, H, B), blk(kThreads);
   hipError_t e;
@@ -824,8 +807,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = launch_state_pass(s, states, lam_end, a.s_in, nullptr, a.status, st);
   if (e != hipSuccess) return e;
-  e = launch_chunk_y(bf, true, true, s, v, C, vb + HP * 4, vb + (HP + (int64_t)G * N) * 4, C, a.dt,
-                     a.A, a.D, states, y, a.status, KID_BWD_Y, st);
+  e = launch_chunk_y(bf, true, true, s, v, C, vb + HP * 4, vb + (HP + (int64_t)G * N) * 4, C, cb,
+                     a.dt, a.A, a.D, states, y, a.status, KID_BWD_Y, st);
   if (e != hipSuccess) return e;
   {
     ProfScope ps(st, KID_BWD_NORM);
@@ -872,11 +855,11 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
 #define SSD_CB(PP)                                                                              \
   if (bf)                                                                                       \
     hipLaunchKernelGGL((k_chunk_bwd<bf16, PP>), gc, blk, lds, st, v, y, (const bf16*)a.dt,      \
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (bf16*)a.d_dt, dA_part,      \
+                       plain, a.A, a.D, states, dso, cb, dv, dBh, dCh, (bf16*)a.d_dt, dA_part,  \
                        a.d_D ? dD_part : nullptr, L, H, G, N, nc);                              \
   else                                                                                          \
     hipLaunchKernelGGL((k_chunk_bwd<float, PP>), gc, blk, lds, st, v, y, (const float*)a.dt,    \
-                       plain, a.A, a.D, states, dso, dv, dBh, dCh, (float*)a.d_dt, dA_part,     \
+                       plain, a.A, a.D, states, dso, cb, dv, dBh, dCh, (float*)a.d_dt, dA_part, \
                        a.d_D ? dD_part : nullptr, L, H, G, N, nc)
     SSD_BY_P(SSD_CB)
 #undef SSD_CB

@@ -2,8 +2,10 @@
 // ("feat(model): add Nemotron-3 Nano hybrid ..." attribution commit: the SSD
 // block decomposition, diagonal blocks and off-diagonal state terms):
 //   y = M X + exp(Lam_t) C S_in^T + D X,  M = (C B^T) o exp(Lam_t - Lam_s) dt_s (s <= t)
-// per (chunk, head), with S_in the chunk's carried-in state (fp32). It is the
-// general path's output kernel (every shape, fp32 or bf16 I/O) and the
+// per (chunk, head), with S_in the chunk's carried-in state (fp32). C B^T
+// depends on the group only, so it is formed once per chunk and group (a
+// kernel of its own) and read by every head of the group. These are the
+// general path's output kernels (every shape, fp32 or bf16 I/O) and the
 // backward pass's recompute of y. x, B, C are read as fp32 or bf16 rows of
 // any token stride; y is written as fp32 or the I/O type.
 #include "common.hpp"
@@ -15,66 +17,52 @@ namespace f32t {
 
 constexpr int kStatusNonFinite = 2;  // status bit: an output is not finite
 
-// Wave w owns rows 16 w .. 16 w + 15 of the chunk: C B^T on the ten causal
-// 16x16 tiles (three per wave at most) and C S_in^T on its rows over 32-wide
-// slices of n (the next slice's loads in flight while one is computed), M
-// into LDS, then M X over its rows from the chunk's x staged transposed in
-// LDS. The contraction order is free, so within each 16-wide block of k the
-// four MFMA steps take k = 16 j + 4 (l / 16) + s (s = 0..3) for lane l: each
-// lane reads its four k values of both operands as one 16-byte LDS read.
-template <class T, class TX, class TY, int P>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
-    const TX* __restrict__ x, int64_t xs, const TX* __restrict__ Bm, const TX* __restrict__ Cm,
-    int64_t bs, const T* __restrict__ dt, DtA dta, const float* __restrict__ A,
-    const float* __restrict__ D, const float* __restrict__ Sin, TY* __restrict__ y, int* status,
-    int L, int H, int G, int N, int nc) {
+// G = C B^T of one chunk and group on the ten causal 16x16 tiles (three per
+// wave at most), shared by every head of the group: cb [B][nc][G][Q][Q],
+// element (t, s) at t Q + s; rows past the chunk's end are zero and the
+// tiles above the diagonal are not written. B and C go through LDS in
+// 32-wide slices of n (the next slice's loads in flight while one is
+// computed). The contraction order is free, so within each 16-wide block
+// of k the four MFMA steps take k = 16 j + 4 (l / 16) + s (s = 0..3) for
+// lane l: each lane reads its four k values of both operands as one
+// 16-byte LDS read.
+template <class TX>
+__global__ __launch_bounds__(kThreads) void k_chunk_cb(const TX* __restrict__ Bm,
+                                                       const TX* __restrict__ Cm, int64_t bs,
+                                                       float* __restrict__ cb, int L, int G,
+                                                       int N, int nc) {
   extern __shared__ __align__(16) float sm[];
-  float* Mt = sm;                 // [Q][kQP]: M
-  float* Bs = sm + kQ * kQP;      // [Q][kSP]
-  float* Cs = Bs + kQ * kSP;      // [Q][kSP]
-  float* Ss = Cs + kQ * kSP;      // [P][kSP]
-  __shared__ float lam[64], dts[64], ex[64];
-  constexpr int NPT = P / 16;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  float* Bs = sm;              // [Q][kSP]
+  float* Cs = sm + kQ * kSP;   // [Q][kSP]
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 15, lk = lane >> 4;
   const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int HP = H * P;
-  const int xsi = (int)xs, bsi = (int)bs;
-  const TX* xr = x + row0 * xs + (int64_t)h * P;
+  const int bsi = (int)bs;
   const TX* br = Bm + row0 * bs + (int64_t)g * N;
   const TX* cr = Cm + row0 * bs + (int64_t)g * N;
-  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
-  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
   int rt[3], st[3];
   bool on[3];
+  f32x4 aG[3];
 #pragma unroll
-  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
-  f32x4 aG[3], aY[NPT];
-#pragma unroll
-  for (int i = 0; i < 3; ++i) aG[i] = zero4();
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
-  const int sw = wave * 16;
+  for (int i = 0; i < 3; ++i) {
+    on[i] = causal_tile(wave, i, rt[i], st[i]);
+    aG[i] = zero4();
+  }
   SliceRegs<kQ> rb, rc;
-  SliceRegs<P> rs;
   auto fetch = [&](int n0) {
     const int nv = min(kKS, N - n0);
     rb.load(br + n0, bsi, len, nv);
     rc.load(cr + n0, bsi, len, nv);
-    rs.load(Si + n0, N, P, nv);
   };
   fetch(0);
   for (int n0 = 0; n0 < N; n0 += kKS) {
     const int nv = min(kKS, N - n0);
     rb.store(Bs);
     rc.store(Cs);
-    rs.store(Ss);
     __syncthreads();
     if (n0 + kKS < N) fetch(n0 + kKS);
-    // nv is a multiple of 16 (so is every supported N)
-    for (int kk = 0; kk < nv; kk += 16) {
+    for (int kk = 0; kk < nv; kk += 16) {  // nv is a multiple of 16 (so is every supported N)
       const int kq = kk + 4 * lk;
 #pragma unroll
       for (int i = 0; i < 3; ++i)
@@ -86,6 +74,76 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
           aG[i] = mma(a4.z, b4.z, aG[i]);
           aG[i] = mma(a4.w, b4.w, aG[i]);
         }
+    }
+    __syncthreads();
+  }
+  float* o = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (on[i])
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[(rt[i] * 16 + 4 * lk + r) * kQ + st[i] * 16 + lr] = aG[i][r];
+}
+
+// Wave w owns rows 16 w .. 16 w + 15 of the chunk: its causal tiles of G
+// (from the group's C B^T), C S_in^T on its rows over 32-wide slices of n
+// (the next slice's loads in flight while one is computed), M into LDS,
+// then M X over its rows from the chunk's x staged transposed in LDS; the
+// k-permuted MFMA steps as in k_chunk_cb.
+template <class T, class TX, class TY, int P>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
+    const TX* __restrict__ x, int64_t xs, const TX* __restrict__ Cm, int64_t bs,
+    const float* __restrict__ cb, const T* __restrict__ dt, DtA dta, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ Sin, TY* __restrict__ y, int* status,
+    int L, int H, int G, int N, int nc) {
+  extern __shared__ __align__(16) float sm[];
+  float* Mt = sm;                 // [Q][kQP]: M
+  float* Cs = sm + kQ * kQP;      // [Q][kSP]
+  float* Ss = Cs + kQ * kSP;      // [P][kSP]
+  __shared__ float lam[64], dts[64], ex[64];
+  constexpr int NPT = P / 16;
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int t0 = c * kQ, len = min(kQ, L - t0);
+  const int64_t row0 = (int64_t)b * L + t0;
+  const int HP = H * P;
+  const int xsi = (int)xs, bsi = (int)bs;
+  const TX* xr = x + row0 * xs + (int64_t)h * P;
+  const TX* cr = Cm + row0 * bs + (int64_t)g * N;
+  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
+  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
+  int rt[3], st[3];
+  bool on[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
+  f32x4 aG[3], aY[NPT];
+  const float* cbk = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    if (on[i])
+#pragma unroll
+      for (int r = 0; r < 4; ++r) aG[i][r] = cbk[(rt[i] * 16 + 4 * lk + r) * kQ + st[i] * 16 + lr];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
+  const int sw = wave * 16;
+  SliceRegs<kQ> rc;
+  SliceRegs<P> rs;
+  auto fetch = [&](int n0) {
+    const int nv = min(kKS, N - n0);
+    rc.load(cr + n0, bsi, len, nv);
+    rs.load(Si + n0, N, P, nv);
+  };
+  fetch(0);
+  for (int n0 = 0; n0 < N; n0 += kKS) {
+    const int nv = min(kKS, N - n0);
+    rc.store(Cs);
+    rs.store(Ss);
+    __syncthreads();
+    if (n0 + kKS < N) fetch(n0 + kKS);
+    // nv is a multiple of 16 (so is every supported N)
+    for (int kk = 0; kk < nv; kk += 16) {
+      const int kq = kk + 4 * lk;
       const float4 a4 = ld4(Cs + (sw + lr) * kSP + kq);
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
@@ -112,8 +170,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
   for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
-  // the chunk's x transposed, [p][t], where B and C were staged
-  float* Xt = Bs;
+  // the chunk's x transposed, [p][t], where C and S_in were staged
+  float* Xt = Cs;
   stage_cols(Xt, kQP, xr, xsi, kQ, len, P);
   __syncthreads();
   // + M X over s <= t (the wave's rows reach s < sw + 16)
@@ -145,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
 }
 
 size_t chunk_y_lds(int P) {
-  const size_t slices = 2 * (size_t)kQ * kSP + (size_t)P * kSP, xcols = (size_t)P * kQP;
+  const size_t slices = (size_t)(kQ + P) * kSP, xcols = (size_t)P * kQP;
   return ((size_t)kQ * kQP + std::max(slices, xcols)) * 4;
 }
 
@@ -153,19 +211,41 @@ size_t chunk_y_lds(int P) {
 
 size_t chunk_y_lds_bytes(int P) { return f32t::chunk_y_lds(P); }
 
-hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
-                          const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
-                          const void* dt, const float* A, const float* D, const float* states,
-                          void* y, int* status, int kid, hipStream_t st) {
+size_t chunk_cb_bytes(int B, int nc, int G) {
+  return (size_t)B * nc * G * f32t::kQ * f32t::kQ * 4;
+}
+
+hipError_t launch_chunk_cb(bool x_bf16, const ScanShape& s, const void* Bm, const void* Cm,
+                           int64_t bs, float* cb, hipStream_t st) {
   using namespace f32t;
   if (s.Q != kQ) return hipErrorInvalidValue;
+  ProfScope ps(st, KID_CHUNK_CB);
+  const dim3 grid(s.nc, s.G, s.B), blk(kThreads);
+  const size_t lds = 2 * (size_t)kQ * kSP * 4;
+  if (x_bf16)
+    hipLaunchKernelGGL((k_chunk_cb<bf16>), grid, blk, lds, st, (const bf16*)Bm, (const bf16*)Cm, bs,
+                       cb, s.L, s.G, s.N, s.nc);
+  else
+    hipLaunchKernelGGL((k_chunk_cb<float>), grid, blk, lds, st, (const float*)Bm,
+                       (const float*)Cm, bs, cb, s.L, s.G, s.N, s.nc);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
+                          const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
+                          float* cb, const void* dt, const float* A, const float* D,
+                          const float* states, void* y, int* status, int kid, hipStream_t st) {
+  using namespace f32t;
+  if (s.Q != kQ) return hipErrorInvalidValue;
+  hipError_t e = launch_chunk_cb(io_bf16 && !x_f32, s, Bm, Cm, bs, cb, st);
+  if (e != hipSuccess) return e;
   ProfScope ps(st, kid);
   const dim3 grid(s.nc, s.H, s.B), blk(kThreads);
   const size_t lds = chunk_y_lds(s.P);
-#define SSD_Y(TT, TX, TY, PP)                                                                     \
-  hipLaunchKernelGGL((k_chunk_y<TT, TX, TY, PP>), grid, blk, lds, st, (const TX*)x, xs,           \
-                     (const TX*)Bm, (const TX*)Cm, bs, (const TT*)dt, s.dta, A, D, states, (TY*)y, \
-                     status, s.L, s.H, s.G, s.N, s.nc)
+#define SSD_Y(TT, TX, TY, PP)                                                                   \
+  hipLaunchKernelGGL((k_chunk_y<TT, TX, TY, PP>), grid, blk, lds, st, (const TX*)x, xs,         \
+                     (const TX*)Cm, bs, cb, (const TT*)dt, s.dta, A, D, states, (TY*)y, status, \
+                     s.L, s.H, s.G, s.N, s.nc)
 #define SSD_Y_P(TT, TX, TY)                  \
   switch (s.P) {                             \
     case 16: SSD_Y(TT, TX, TY, 16); break;   \

@@ -47,11 +47,19 @@ hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam
                              const float* s_in, float* s_out, int* status, hipStream_t st);
 // Chunk outputs on fp32 MFMA operands (s.Q must be 64): y = M X + exp(Lam)
 // C S_in^T + D X. x_f32: x, B, C fp32 (else the I/O type); y_f32: y fp32
-// (else the I/O type). kid: the kernel id the timing aid records it under.
+// (else the I/O type). cb: chunk_cb_bytes of workspace, filled first with
+// each chunk's C B^T per group (launch_chunk_cb). kid: the kernel id the
+// timing aid records the output kernel under.
 hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
                           const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
-                          const void* dt, const float* A, const float* D, const float* states,
-                          void* y, int* status, int kid, hipStream_t st);
+                          float* cb, const void* dt, const float* A, const float* D,
+                          const float* states, void* y, int* status, int kid, hipStream_t st);
+// C B^T of each 64-token chunk and group on the causal 16x16 tiles into cb
+// [B][nc][G][64][64] (fp32; element (t, s) at t 64 + s). x_bf16: B and C
+// are bf16 (else fp32).
+hipError_t launch_chunk_cb(bool x_bf16, const ScanShape& s, const void* Bm, const void* Cm,
+                           int64_t bs, float* cb, hipStream_t st);
+size_t chunk_cb_bytes(int B, int nc, int G);
 size_t chunk_y_lds_bytes(int P);
 
 }  // namespace ssd

@@ -35,7 +35,7 @@ const char* kNames[KID_COUNT] = {
     "chunk_state",      "state_pass",       "chunk_out",     "fused_chunk_state",
     "fused_state_pass", "fused_chunk_out_norm", "bwd_gated_norm", "bwd_chunk_z",
     "bwd_rev_pass",     "bwd_chunk",        "bwd_group_sum", "bwd_conv_du",
-    "bwd_conv_dx",      "bwd_y",
+    "bwd_conv_dx",      "bwd_y",            "chunk_cb",
 };
 
 void release() {

@@ -29,6 +29,7 @@ enum KernelId {
   KID_BWD_CONV_DU,
   KID_BWD_CONV_DX,
   KID_BWD_Y,
+  KID_CHUNK_CB,
   KID_COUNT
 };
 

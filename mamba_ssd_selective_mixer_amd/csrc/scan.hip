@@ -91,10 +91,12 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
 #pragma unroll
   for (int i = 0; i < kMaxTPW; ++i) acc[i] = zero4();
 
+  // staged transposed ([p][s], [n][s]) with one token per lane, so a wave's
+  // LDS stores hit consecutive addresses
   const int P8 = P / 8, N8 = N / 8;
   for (int s0 = 0; s0 < len; s0 += kStateSB) {
     for (int v = tid; v < kStateSB * P8; v += kScanThreads) {
-      const int s = v / P8, p0 = (v % P8) * 8;
+      const int s = v % kStateSB, p0 = (v / kStateSB) * 8;
       float xv[8];
       if (s0 + s < len) {
         load8(x + (row0 + s0 + s) * xs + (int64_t)h * P + p0, xv);
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
       for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<O>(xv[j]);
     }
     for (int v = tid; v < kStateSB * N8; v += kScanThreads) {
-      const int s = v / N8, n0 = (v % N8) * 8;
+      const int s = v % kStateSB, n0 = (v / kStateSB) * 8;
       float bv[8];
       if (s0 + s < len) {
         load8(Bm + (row0 + s0 + s) * bs + (int64_t)g * N + n0, bv);

@@ -463,7 +463,8 @@ def test_backward_refuses_before_launch(lib):
     # workspace: the status word, fp32 conv output / its gradient, y, chunk
     # states and their gradients (64-token chunks), per-head dB / dC, 1024
     # partial norm-weight gradients, the conv gradients' partial sums per
-    # 64-token range, and each chunk's parts of dA and dD
+    # 64-token range, each chunk's parts of dA and dD, and each chunk's
+    # C B^T per group (64 x 64 fp32)
     cfg = synth.CONFIGS["tiny_layer"]
     T, C, HP = cfg.batch * cfg.seqlen, cfg.channels, cfg.hp
     nc = -(-cfg.seqlen // 64)
@@ -472,7 +473,8 @@ def test_backward_refuses_before_launch(lib):
     assert need == (256 + 2 * r(T * C * 4) + r(T * HP * 4) + 2 * r(st)
                     + r(cfg.batch * cfg.nheads * nc * 4) + 2 * r(T * cfg.nheads * cfg.dstate * 4)
                     + r(1024 * HP * 4) + r(cfg.batch * nc * C * 5 * 4)
-                    + r(2 * cfg.batch * nc * cfg.nheads * 4))
+                    + r(2 * cfg.batch * nc * cfg.nheads * 4)
+                    + r(cfg.batch * nc * cfg.ngroups * 64 * 64 * 4))
     base = {k: (i + 1) << 36 for i, k in enumerate(_BWD_BUFS)}
     for k in ("xbc", "z", "dt", "A", "cw", "nw", "d_out", "g_xbc", "g_z", "g_dt", "g_A", "g_cw",
               "g_nw", "ws"):
