@@ -665,8 +665,9 @@ int ssd_mixer_varlen(const ssd_dims* d, const int32_t* cu_seqlens, const int32_t
   return hip_status(ssd::launch_fast_scan(a, (hipStream_t)stream));
 }
 
-// The backward kernels' own limits: a norm row spreads over the 256 threads
-// of a workgroup at most 64 channels each; norm groups fit a 256-entry table.
+// The backward kernels' own limits: a norm row spreads over one workgroup,
+// at most 64 channels on each of 256 threads (16 on each of 1024 when the row
+// is held in registers); norm groups fit a 256-entry table.
 constexpr int kBwdMaxHP = 256 * 64, kBwdMaxGroups = 256;
 
 size_t ssd_mixer_backward_workspace_bytes(const ssd_dims* d) {

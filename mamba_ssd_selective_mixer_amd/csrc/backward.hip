@@ -40,26 +40,22 @@ SSD_DEV float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 // thread takes 4 consecutive channels (one norm group: groups are multiples
 // of 16 channels). A workgroup takes `rows` consecutive rows and sums its
 // share of dw in LDS, then writes it to its row of dw_part [gridDim.x][HP].
-// WG: every norm group is a whole number of 256-channel pieces (a wave's
-// channels in one iteration), so a piece's sums come from the wave
-// (deterministic DPP sums); else each 4-channel lane keeps its own. The
-// group sums then add the pieces in a fixed order (no atomics: the result
-// does not depend on timing).
-template <class T, bool WG>
+// Each 4-channel lane keeps its row sums in LDS; the group sums then add
+// them in a fixed order (no atomics: the result does not depend on timing).
+// Norm groups of whole 256-channel pieces take k_norm_bwd_wide instead.
+template <class T>
 __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __restrict__ z,
                                                        const T* __restrict__ w,
                                                        const T* __restrict__ g, float eps,
                                                        T* __restrict__ dz, float* dw_part,
                                                        int64_t nrows, int rows, int HP, int G) {
-  extern __shared__ float4 dwl[];  // [HP / 4], then (not WG) two [HP / 4] piece sums
+  extern __shared__ float4 dwl[];  // [HP / 4], then two [HP / 4] lane sums
   __shared__ float sq[kMaxGroups], sg[kMaxGroups];
-  __shared__ float wp2[WG ? kMaxNormPieces : 1], wpw[WG ? kMaxNormPieces : 1];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int S = HP / G, HP4 = HP / 4;
-  float* p2 = WG ? wp2 : reinterpret_cast<float*>(dwl + HP4);
-  float* pw = WG ? wpw : p2 + HP4;
-  constexpr int kUnit = WG ? 256 : 4;  // channels per piece
-  const int per = S / kUnit;
+  float* p2 = reinterpret_cast<float*>(dwl + HP4);
+  float* pw = p2 + HP4;
+  const int per = S / 4;
   for (int c = tid; c < HP4; c += kThreads) dwl[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int rr = 0; rr < rows; ++rr) {
     const int64_t row = (int64_t)blockIdx.x * rows + rr;
@@ -79,14 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __rest
         wgq = sum4(make_float4(ww.x * gg.x * q.x, ww.y * gg.y * q.y, ww.z * gg.z * q.z,
                                ww.w * gg.w * q.w));
       }
-      if constexpr (WG) {
-        q2 = wave_sum(q2);
-        wgq = wave_sum(wgq);
-        if (lane == 0 && c4 < HP4) {
-          p2[c4 >> 6] = q2;
-          pw[c4 >> 6] = wgq;
-        }
-      } else if (c4 < HP4) {
+      if (c4 < HP4) {
         p2[c4] = q2;
         pw[c4] = wgq;
       }
@@ -134,6 +123,143 @@ __global__ __launch_bounds__(kThreads) void k_norm_bwd(float* y, const T* __rest
   }
   for (int c4 = tid; c4 < HP4; c4 += kThreads)
     st4(dw_part + (int64_t)blockIdx.x * HP + 4 * c4, dwl[c4]);
+}
+
+// The same for bf16 I/O and norm groups of whole 256-channel pieces, with
+// each row read once: a 1024-thread workgroup holds a row's channels in
+// registers (up to four 4-channel units per thread, z and g as raw bf16;
+// unit c4 = tid + 1024 k, so piece k * 16 + wave is one wave's 64 lanes),
+// loads the next row meanwhile, and sums its share of dw in LDS (each
+// thread its own units). A piece's sums come from its wave (deterministic
+// DPP sums) and the group sums add the pieces in a fixed order.
+constexpr int kNormWideThreads = 1024;
+constexpr int kNormWideBlocks = 256;
+SSD_DEV float4 bf4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__global__ __launch_bounds__(kNormWideThreads) void k_norm_bwd_wide(
+    float* y, const bf16* __restrict__ z, const bf16* __restrict__ w, const bf16* __restrict__ g,
+    float eps, bf16* __restrict__ dz, float* dw_part, int64_t nrows, int rows, int HP, int G) {
+  constexpr int KU = kMaxNormPieces * 64 / kNormWideThreads;
+  extern __shared__ float4 dwl[];  // [HP / 4]
+  __shared__ float p2[kMaxNormPieces], pw[kMaxNormPieces], sq[kMaxGroups], sg[kMaxGroups];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = HP / G, HP4 = HP / 4, per = S / 256;
+  bool on[KU];
+  uint2 wr[KU];
+#pragma unroll
+  for (int k = 0; k < KU; ++k) {
+    const int c4 = tid + kNormWideThreads * k;
+    on[k] = c4 < HP4;
+    wr[k] = on[k] ? *reinterpret_cast<const uint2*>(w + 4 * c4) : make_uint2(0u, 0u);
+    if (on[k]) dwl[c4] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * rows;
+  const int nr = (int)min((int64_t)rows, nrows - r0);
+  float4 yn[KU];
+  uint2 zn[KU], gn[KU];
+#pragma unroll
+  for (int k = 0; k < KU; ++k) {
+    yn[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    zn[k] = gn[k] = make_uint2(0u, 0u);
+  }
+  auto fetch = [&](int64_t row) {
+#pragma unroll
+    for (int k = 0; k < KU; ++k)
+      if (on[k]) {
+        const int64_t o = row * HP + 4 * (tid + kNormWideThreads * k);
+        yn[k] = ld4(y + o);
+        zn[k] = *reinterpret_cast<const uint2*>(z + o);
+        gn[k] = *reinterpret_cast<const uint2*>(g + o);
+      }
+  };
+  if (nr > 0) fetch(r0);
+  for (int rr = 0; rr < nr; ++rr) {
+    const int64_t row = r0 + rr;
+    float4 yy[KU];
+    uint2 zr[KU], gr[KU];
+#pragma unroll
+    for (int k = 0; k < KU; ++k) {
+      yy[k] = yn[k];
+      zr[k] = zn[k];
+      gr[k] = gn[k];
+    }
+    if (rr + 1 < nr) fetch(row + 1);
+#pragma unroll
+    for (int k = 0; k < KU; ++k) {
+      const float4 zz = bf4(zr[k]), gg = bf4(gr[k]), wv = bf4(wr[k]);
+      const float4 qk = make_float4(yy[k].x * zz.x * frcp(1.f + __expf(-zz.x)),
+                                    yy[k].y * zz.y * frcp(1.f + __expf(-zz.y)),
+                                    yy[k].z * zz.z * frcp(1.f + __expf(-zz.z)),
+                                    yy[k].w * zz.w * frcp(1.f + __expf(-zz.w)));
+      // on[k] is uniform over a wave (HP / 4 is a multiple of 64 here)
+      const float q2 = wave_sum(sum4(make_float4(qk.x * qk.x, qk.y * qk.y, qk.z * qk.z,
+                                                 qk.w * qk.w)));
+      const float wgq = wave_sum(sum4(make_float4(wv.x * gg.x * qk.x, wv.y * gg.y * qk.y,
+                                                  wv.z * gg.z * qk.z, wv.w * gg.w * qk.w)));
+      if (lane == 0 && on[k]) {
+        p2[k * (kNormWideThreads / 64) + wave] = q2;
+        pw[k * (kNormWideThreads / 64) + wave] = wgq;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float a = 0.f, b = 0.f;
+      for (int k = 0; k < per; ++k) {
+        a += p2[tid * per + k];
+        b += pw[tid * per + k];
+      }
+      sq[tid] = a;
+      sg[tid] = b;
+    }
+    __syncthreads();
+    // the row's values are taken up again from their raw registers (the
+    // empty asm hides them from the compiler, which would otherwise keep
+    // every value derived in the first pass alive across the barriers)
+#pragma unroll
+    for (int k = 0; k < KU; ++k)
+      asm volatile(""
+                   : "+v"(yy[k].x), "+v"(yy[k].y), "+v"(yy[k].z), "+v"(yy[k].w), "+v"(zr[k].x),
+                     "+v"(zr[k].y), "+v"(gr[k].x), "+v"(gr[k].y), "+v"(wr[k].x), "+v"(wr[k].y));
+#pragma unroll
+    for (int k = 0; k < KU; ++k)
+      if (on[k]) {
+        const int c = 4 * (tid + kNormWideThreads * k);
+        const int64_t o = row * HP + c;
+        const int j = c / S;
+        const float r = rsqrtf(sq[j] / S + eps), k3 = r * r * r * sg[j] / S;
+        const float4 zz = bf4(zr[k]), gg = bf4(gr[k]), wv = bf4(wr[k]);
+        const float zv[4] = {zz.x, zz.y, zz.z, zz.w};
+        const float yv[4] = {yy[k].x, yy[k].y, yy[k].z, yy[k].w};
+        const float wq[4] = {wv.x, wv.y, wv.z, wv.w};
+        const float gv[4] = {gg.x, gg.y, gg.z, gg.w};
+        float dy[4], dzv[4], dwv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sig = frcp(1.f + __expf(-zv[i])), sl = zv[i] * sig;
+          const float qq = yv[i] * sl;
+          const float dq = wq[i] * r * gv[i] - qq * k3;
+          dy[i] = dq * sl;
+          dzv[i] = dq * yv[i] * (sig + sl * (1.f - sig));
+          dwv[i] = gv[i] * qq * r;
+        }
+        st4(y + o, make_float4(dy[0], dy[1], dy[2], dy[3]));
+        st4(dz + o, make_float4(dzv[0], dzv[1], dzv[2], dzv[3]));
+        float4 acc = dwl[c / 4];
+        acc.x += dwv[0];
+        acc.y += dwv[1];
+        acc.z += dwv[2];
+        acc.w += dwv[3];
+        dwl[c / 4] = acc;
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < KU; ++k)
+    if (on[k]) {
+      const int c4 = tid + kNormWideThreads * k;
+      st4(dw_part + (int64_t)blockIdx.x * HP + 4 * c4, dwl[c4]);
+    }
 }
 
 // out[c] = sum over the parts of part[i * stride + c]. A workgroup takes 64
@@ -812,18 +938,26 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps(st, KID_BWD_NORM);
-    const int rows = (int)((T + kNormBlocks - 1) / kNormBlocks);
+    // bf16 I/O with whole 256-channel pieces per norm group: the pieces'
+    // sums come from the waves, and a row fits one 1024-thread workgroup's
+    // registers; else each 4-channel lane's sums are kept in LDS
+    const bool wide = bf && (HP / G) % 256 == 0;
+    const int nblk = wide ? kNormWideBlocks : kNormBlocks;
+    const int rows = (int)((T + nblk - 1) / nblk);
     const int nb = (int)((T + rows - 1) / rows);
-    // whole 256-channel pieces per norm group: the pieces' sums come from
-    // the waves; else each 4-channel lane's sums are kept in LDS
-    const bool wg = (HP / G) % 256 == 0;
-    const size_t lds = (size_t)HP * 4 + (wg ? 0 : (size_t)HP / 4 * 2 * 4);
-#define SSD_NORM(TT, WGV)                                                                        hipLaunchKernelGGL((k_norm_bwd<TT, WGV>), dim3(nb), blk, lds, st, y, (const TT*)a.z,                               (const TT*)a.norm_w, (const TT*)a.d_out, a.eps, (TT*)a.d_z, dw_part, T,                         rows, (int)HP, G)
-    if (bf) {
-      if (wg) SSD_NORM(bf16, true); else SSD_NORM(bf16, false);
-    } else {
-      if (wg) SSD_NORM(float, true); else SSD_NORM(float, false);
-    }
+    const size_t lds = (size_t)HP * 4 + (size_t)HP / 4 * 2 * 4;  // k_norm_bwd: dw, lane sums
+#define SSD_NORM(TT)                                                                             \
+  hipLaunchKernelGGL((k_norm_bwd<TT>), dim3(nb), blk, lds, st, y, (const TT*)a.z,                \
+                     (const TT*)a.norm_w, (const TT*)a.d_out, a.eps, (TT*)a.d_z, dw_part, T,    \
+                     rows, (int)HP, G)
+    if (wide)
+      hipLaunchKernelGGL(k_norm_bwd_wide, dim3(nb), dim3(kNormWideThreads), (size_t)HP * 4, st, y,
+                         (const bf16*)a.z, (const bf16*)a.norm_w, (const bf16*)a.d_out, a.eps,
+                         (bf16*)a.d_z, dw_part, T, rows, (int)HP, G);
+    else if (bf)
+      SSD_NORM(bf16);
+    else
+      SSD_NORM(float);
 #undef SSD_NORM
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((HP + 63) / 64)), blk, 0, st, dw_part, HP,
                        a.d_norm_w, nb, (int)HP);
