@@ -557,7 +557,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     __syncthreads();
   }
 
-  // (3) dX intra: sum_{t >= s} M[t,s] dY[t,p], the chunk's dY rows staged
+  // (3) dX intra: sum_{t >= s} M[t,s] dY[t,p], the chunk's dY rows staged.
+  // dX's two products are formed transposed (rows p, columns s), so lane l
+  // holds p = 16 pt + 4 (l / 16) + (0..3) of token s = sw + l % 16: the same
+  // elements as its dY and X fragments below.
   f32x4 a1[NPT], a2[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i) a1[i] = a2[i] = zero4();
@@ -568,14 +571,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     __syncthreads();
     for (int k0 = sw; k0 < kQ; k0 += 4) {
       const int t = k0 + lk;
-      const float a = Mt[t * kQP + sw + lr];
+      const float m = Mt[t * kQP + sw + lr];
 #pragma unroll
-      for (int pt = 0; pt < NPT; ++pt) a1[pt] = mma(a, Ys[t * YP + pt * 16 + lr], a1[pt]);
+      for (int pt = 0; pt < NPT; ++pt) a1[pt] = mma(Ys[t * YP + pt * 16 + lr], m, a1[pt]);
     }
     __syncthreads();
   }
 
-  // (4) over 16-wide slices of n: B_s dS_out^T of the wave's rows (a2), and
+  // (4) over 16-wide slices of n: B_s dS_out^T of the wave's tokens (a2), and
   // the slice's tiles of dC (rows t) and dB (rows s). Every product takes
   // k-permuted steps (a lane's four k values of both operands in one 16-byte
   // read): B and dS_out are staged both as rows (n contiguous, for a2) and
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
         const float4 a4 = ld4(Bs + (sw + lr) * kBP + 4 * lk);
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt)
-          a2[pt] = mma4(a4, ld4(Ds + (pt * 16 + lr) * kBP + 4 * lk), a2[pt]);
+          a2[pt] = mma4(ld4(Ds + (pt * 16 + lr) * kBP + 4 * lk), a4, a2[pt]);
       }
       f32x4 dc = zero4(), db = zero4();
 #pragma unroll
@@ -677,33 +680,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     }
   }
 
-  // (5) dX, and the row sums U_s, Y_t; dD and <dS_out, S_in>
+  // (5) dX, and the row sums U_s, Y_t; dD and <dS_out, S_in>. Lane l holds
+  // four consecutive p of token s = sw + l % 16 in a1, a2, ya and xa.
   {
-    float up[4] = {0.f, 0.f, 0.f, 0.f}, ddp = 0.f;
+    const int s = sw + lr;
+    float up = 0.f, ddp = 0.f;
+    if (s < len) {
+      const float ws = wv[s];
 #pragma unroll
-    for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = sw + 4 * lk + r, p = pt * 16 + lr;
-        if (s < len) {
-          const float xv = v[(row0 + s) * C + xo + p], dys = dY[(row0 + s) * HP + xo + p];
-          dv[(row0 + s) * C + xo + p] = a1[pt][r] + wv[s] * a2[pt][r] + Dh * dys;
-          up[r] += xv * a2[pt][r];
-          ddp += dys * xv;
-        }
+      for (int pt = 0; pt < NPT; ++pt) {
+        const float4 xv = xa[pt], dys = ya[pt];
+        st4(dv + (row0 + s) * C + xo + 16 * pt + 4 * lk,
+            make_float4(a1[pt][0] + ws * a2[pt][0] + Dh * dys.x,
+                        a1[pt][1] + ws * a2[pt][1] + Dh * dys.y,
+                        a1[pt][2] + ws * a2[pt][2] + Dh * dys.z,
+                        a1[pt][3] + ws * a2[pt][3] + Dh * dys.w));
+        up += (xv.x * a2[pt][0] + xv.y * a2[pt][1]) + (xv.z * a2[pt][2] + xv.w * a2[pt][3]);
+        ddp += (dys.x * xv.x + dys.y * xv.y) + (dys.z * xv.z + dys.w * xv.w);
       }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      up[r] = group_sum_last<16>(up[r]);
-      yp[r] = group_sum_last<16>(yp[r]);
     }
+    // U_s: the lanes l, l + 16, l + 32, l + 48 hold the parts of token s
+    up += __shfl_xor(up, 16);
+    up += __shfl_xor(up, 32);
+    if (lk == 0) U[s] = up;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yp[r] = group_sum_last<16>(yp[r]);
     if (lr == 0)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = sw + 4 * lk + r;
-        U[s] = up[r];
-        Yo[s] = yp[r];
-      }
+      for (int r = 0; r < 4; ++r) Yo[sw + 4 * lk + r] = yp[r];
     cstp = wave_sum(cstp);
     ddp = wave_sum(ddp);
     if (lane == 0) {
