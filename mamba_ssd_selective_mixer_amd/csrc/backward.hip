@@ -764,85 +764,107 @@ __global__ __launch_bounds__(kThreads) void k_group_sum(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- conv + SiLU
-// du = dv silu'(u) over a range of kConvTok tokens of one channel, u
+// du = dv silu'(u) over a range of kConvTok tokens of four channels, u
 // recomputed from the rows ext = [conv state ; xbc] through a sliding window;
 // du overwrites dv. The range's sums for the weight and bias gradients go to
-// its row of part: part[range][c * W + k] and part[range][C * W + c].
+// its row of part: part[range][c * W + k] and part[range][C * W + c]. Each
+// thread takes 4 consecutive channels (C is a multiple of 16), so its loads
+// and stores are 16-byte (fp32) or 8-byte (bf16) vectors.
 constexpr int kConvTok = 64;
+SSD_DEV float4 f4mul(float4 a, float4 b) { return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w); }
+SSD_DEV float4 f4fma(float4 a, float4 b, float4 c) {
+  return make_float4(a.x * b.x + c.x, a.y * b.y + c.y, a.z * b.z + c.z, a.w * b.w + c.w);
+}
 template <class T, int W>
 __global__ __launch_bounds__(kThreads) void k_conv_du(const T* __restrict__ xbc,
                                                       const T* __restrict__ cin,
                                                       const T* __restrict__ w,
                                                       const T* __restrict__ bias, float* dv,
                                                       float* part, int L, int C) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int c = (blockIdx.x * kThreads + threadIdx.x) * 4;
   const int t0 = blockIdx.y * kConvTok, b = blockIdx.z;
   if (c >= C) return;
-  float wk[W], dwp[W], win[W], dbp = 0.f;
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 wk[W], dwp[W], win[W], dbp = z4;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
-    wk[k] = to_f(w[(int64_t)c * W + k]);
-    dwp[k] = 0.f;
+    wk[k] = make_float4(to_f(w[(int64_t)c * W + k]), to_f(w[(int64_t)(c + 1) * W + k]),
+                        to_f(w[(int64_t)(c + 2) * W + k]), to_f(w[(int64_t)(c + 3) * W + k]));
+    dwp[k] = z4;
   }
-  const float bc = bias ? to_f(bias[c]) : 0.f;
+  const float4 bc = bias ? ld4(bias + c) : z4;
   // ext row e: conv state rows (e < W-1) or token e - (W-1)
-  auto ext = [&](int e) -> float {
-    if (e >= W - 1) return to_f(xbc[((int64_t)b * L + e - (W - 1)) * C + c]);
-    return cin ? to_f(cin[((int64_t)b * (W - 1) + e) * C + c]) : 0.f;
+  auto ext = [&](int e) -> float4 {
+    if (e >= W - 1) return ld4(xbc + ((int64_t)b * L + e - (W - 1)) * C + c);
+    return cin ? ld4(cin + ((int64_t)b * (W - 1) + e) * C + c) : z4;
   };
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) win[k] = ext(t0 + k);
   const int t1 = min(L, t0 + kConvTok);
   for (int t = t0; t < t1; ++t) {
     win[W - 1] = ext(t + W - 1);
-    float u = bc;
+    float4 u = bc;
 #pragma unroll
-    for (int k = 0; k < W; ++k) u += wk[k] * win[k];
-    const float sig = frcp(1.f + __expf(-u));
+    for (int k = 0; k < W; ++k) u = f4fma(wk[k], win[k], u);
+    const float uv[4] = {u.x, u.y, u.z, u.w};
+    float g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sig = frcp(1.f + __expf(-uv[i]));
+      g[i] = sig + uv[i] * sig * (1.f - sig);
+    }
     const int64_t o = ((int64_t)b * L + t) * C + c;
-    const float du = dv[o] * (sig + u * sig * (1.f - sig));
-    dv[o] = du;
+    const float4 du = f4mul(ld4(dv + o), make_float4(g[0], g[1], g[2], g[3]));
+    st4(dv + o, du);
 #pragma unroll
-    for (int k = 0; k < W; ++k) dwp[k] += du * win[k];
-    dbp += du;
+    for (int k = 0; k < W; ++k) dwp[k] = f4fma(du, win[k], dwp[k]);
+    dbp = make_float4(dbp.x + du.x, dbp.y + du.y, dbp.z + du.z, dbp.w + du.w);
 #pragma unroll
     for (int k = 0; k < W - 1; ++k) win[k] = win[k + 1];
   }
   float* pr = part + ((int64_t)b * gridDim.y + blockIdx.y) * ((int64_t)C * (W + 1));
 #pragma unroll
-  for (int k = 0; k < W; ++k) pr[(int64_t)c * W + k] = dwp[k];
-  pr[(int64_t)C * W + c] = dbp;
+  for (int k = 0; k < W; ++k) {
+    pr[(int64_t)c * W + k] = dwp[k].x;
+    pr[(int64_t)(c + 1) * W + k] = dwp[k].y;
+    pr[(int64_t)(c + 2) * W + k] = dwp[k].z;
+    pr[(int64_t)(c + 3) * W + k] = dwp[k].w;
+  }
+  st4(pr + (int64_t)C * W + c, dbp);
 }
 
 // Gradient of the conv input rows ext = [conv state ; xbc]: d_ext[e] =
 // sum_k w[k] du[e - k] over output tokens e - k in range (a sliding window
 // over du); rows e >= W-1 go to d_xbc, the first W-1 to the initial conv
-// state's gradient (fp32).
+// state's gradient (fp32). Four consecutive channels per thread.
 template <class T, int W>
 __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ du,
                                                       const T* __restrict__ w, T* __restrict__ dx,
                                                       float* dcin, int L, int C) {
-  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const int c = (blockIdx.x * kThreads + threadIdx.x) * 4;
   const int e0 = blockIdx.y * kConvTok, b = blockIdx.z;
   if (c >= C) return;
-  float wk[W], win[W];  // win[k] = du[e - k]
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 wk[W], win[W];  // win[k] = du[e - k]
 #pragma unroll
-  for (int k = 0; k < W; ++k) wk[k] = to_f(w[(int64_t)c * W + k]);
-  auto dut = [&](int tt) -> float {
-    return (tt >= 0 && tt < L) ? du[((int64_t)b * L + tt) * C + c] : 0.f;
+  for (int k = 0; k < W; ++k)
+    wk[k] = make_float4(to_f(w[(int64_t)c * W + k]), to_f(w[(int64_t)(c + 1) * W + k]),
+                        to_f(w[(int64_t)(c + 2) * W + k]), to_f(w[(int64_t)(c + 3) * W + k]));
+  auto dut = [&](int tt) -> float4 {
+    return (tt >= 0 && tt < L) ? ld4(du + ((int64_t)b * L + tt) * C + c) : z4;
   };
 #pragma unroll
   for (int k = 1; k < W; ++k) win[k] = dut(e0 - k);
   const int e1 = min(L + W - 1, e0 + kConvTok);
   for (int e = e0; e < e1; ++e) {
     win[0] = dut(e);
-    float acc = 0.f;
+    float4 acc = z4;
 #pragma unroll
-    for (int k = 0; k < W; ++k) acc += wk[k] * win[k];
+    for (int k = 0; k < W; ++k) acc = f4fma(wk[k], win[k], acc);
     if (e >= W - 1)
-      dx[((int64_t)b * L + e - (W - 1)) * C + c] = from_f<T>(acc);
+      st4(dx + ((int64_t)b * L + e - (W - 1)) * C + c, acc);
     else if (dcin)
-      dcin[((int64_t)b * (W - 1) + e) * C + c] = acc;
+      st4(dcin + ((int64_t)b * (W - 1) + e) * C + c, acc);
 #pragma unroll
     for (int k = W - 1; k > 0; --k) win[k] = win[k - 1];
   }
@@ -1018,7 +1040,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   {
     ProfScope ps(st, KID_BWD_CONV_DU);
     const int ny = (L + kConvTok - 1) / kConvTok;
-    const dim3 gd((unsigned)((C + kThreads - 1) / kThreads), ny, B);
+    const dim3 gd((unsigned)((C / 4 + kThreads - 1) / kThreads), ny, B);
 #define SSD_DU(TT, WW)                                                                       \
   hipLaunchKernelGGL((k_conv_du<TT, WW>), gd, blk, 0, st, (const TT*)a.xbc,                  \
                      (const TT*)a.conv_in, (const TT*)a.conv_w, (const TT*)a.conv_b, dv,     \
@@ -1038,7 +1060,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   SSD_CHECK();
   {
     ProfScope ps(st, KID_BWD_CONV_DX);
-    const dim3 gx((unsigned)((C + kThreads - 1) / kThreads),
+    const dim3 gx((unsigned)((C / 4 + kThreads - 1) / kThreads),
                   (L + W - 1 + kConvTok - 1) / kConvTok, B);
 #define SSD_DX(TT, WW)                                                                         \
   hipLaunchKernelGGL((k_conv_dx<TT, WW>), gx, blk, 0, st, dv, (const TT*)a.conv_w,             \
