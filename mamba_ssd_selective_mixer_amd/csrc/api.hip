@@ -23,6 +23,7 @@ bool f32op(const ssd_dims* d) { return (d->flags & SSD_FLAG_FP32_OPERANDS) != 0;
 
 // bound on the polls of the fast path's cross-block norm exchange
 std::atomic<int> g_spin_limit{1 << 20};
+std::atomic<int> g_bwd_heads{0};  // backward per-chunk workgroup heads; 0: from the shape
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool is_one_of(int v, std::initializer_list<int> set) {
   for (int s : set)
@@ -768,6 +769,7 @@ int ssd_mixer_backward(const ssd_dims* d, const void* xbc, const void* z, const 
   a.d_conv_in = d_conv_state_in;
   a.d_s_in = d_ssm_state_in;
   a.status = (int*)workspace;
+  a.chunk_heads = g_bwd_heads.load(std::memory_order_relaxed);
   a.ws = (unsigned char*)workspace + round_up(4, kWsAlign);
   return hip_status(ssd::launch_backward(a, (hipStream_t)stream));
 }
@@ -789,6 +791,11 @@ int ssd_workspace_status(const void* workspace, void* stream) {
 int ssd_set_exchange_spin_limit(int polls) {
   if (polls < 0) return SSD_ERR_SHAPE;
   return g_spin_limit.exchange(polls);
+}
+
+int ssd_set_backward_chunk_heads(int heads) {
+  if (heads < 0 || heads > 32 || (heads & (heads - 1))) return SSD_ERR_SHAPE;
+  return g_bwd_heads.exchange(heads);
 }
 
 }  // extern "C"

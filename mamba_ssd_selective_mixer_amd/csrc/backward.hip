@@ -368,6 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 
 // ---------------------------------------------------------------- chunk grads
 constexpr int kNS = 16;        // width (in n) of the per-chunk gradient kernel's state slices
+constexpr int kChunkHeads = 32; // most heads of one group per per-chunk gradient workgroup
 constexpr int kBP = kNS + 4;   // pitch of such a slice stored as rows
 
 // Rows [0, ROWS) x columns [0, kNS) of a row-major fp32 matrix held in
@@ -416,8 +417,10 @@ SSD_DEV f32x4 mma4(float4 a, float4 b, f32x4 c) {
 }
 
 // One (chunk, head, batch): dX into dv's x channels, this head's share of dB
-// and dC into dBh / dCh [T, H, N], d(dt) into ddt (io dtype), and this
-// chunk's parts of dA and dD into dA / dD [B nc, H] (or dD null).
+// and dC into its workgroup's rows of dBh / dCh [T, H / hpb, N] (written by
+// the workgroup's first head, added to by the others), d(dt) into ddt (io
+// dtype), and this chunk's parts of dA and dD into dA / dD [B nc, H] (or dD
+// null).
 // dt and A reach the output through Lam only (a_u = dt_u A feeds Lam_t for
 // every t >= u), so d(a_u) is the sum over t >= u of dLam_t. That sum is
 // formed term by term, without differences of partial sums:
@@ -428,13 +431,12 @@ SSD_DEV f32x4 mma4(float4 a, float4 b, f32x4 c) {
 // the latter from dC's inter-chunk part. Wave w owns the 16-row tile w of s
 // (dX, dB) and of t (dC).
 template <class T, int P>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
+__device__ __forceinline__ void chunk_bwd_head(
     const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
     const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
-    float* __restrict__ dBh,
-    float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD, int L, int H, int G,
-    int N, int nc) {
+    float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
+    int L, int H, int G, int N, int nc, int h, int hpb) {
   extern __shared__ __align__(16) float sm[];
   float* Mt = sm;                // [Q][kQP]: G, then M = G o E dt_s
   float* Dg = sm + kQ * kQP;     // [Q][kQP]: K, then dG = K o E dt_s
@@ -442,11 +444,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   __shared__ float lam[64], dts[64], ex[64], wv[64], colF[64], Yo[64], U[64], dai[64], tmp[64];
   __shared__ float red[4][2];  // per wave: its share of <dS_out, S_in> and of dD
   constexpr int NPT = P / 16;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int c = blockIdx.x, b = blockIdx.z, g = h / (H / G);
+  // the thread index is hidden from the compiler per head, so the many
+  // lane-dependent addresses are formed inside the head instead of being
+  // hoisted out of the workgroup's head loop and held in registers across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
   const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int HP = H * P;
+  const int HP = H * P, Hs = H / hpb;
+  const bool first = h % hpb == 0;  // the block's first head writes its dB / dC rows
   const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, bo = HP + (int64_t)g * N,
                 co = HP + (int64_t)(G + g) * N;
   const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
@@ -632,6 +640,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
       rd.store_cols(Dt, TP);
       __syncthreads();
       if (n0 + kNS < N) fetch(n0 + kNS);
+      // the workgroup's earlier heads' sums of this slice's dC / dB rows
+      // (written by this lane), loaded while the slice is computed
+      float pc[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+      if (!first)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = sw + 4 * lk + r;
+          if (t < len) {
+            const int64_t o = ((row0 + t) * Hs + h / hpb) * N + n0 + lr;
+            pc[r] = dCh[o];
+            pb[r] = dBh[o];
+          }
+        }
       for (int i = tid; i < kNS * (P / 4); i += kThreads) {
         const int n = i / (P / 4), p4 = (i % (P / 4)) * 4;
         const float4 a = ld4(St + n * TP + p4), d = ld4(Dt + n * TP + p4);
@@ -671,9 +692,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
       for (int r = 0; r < 4; ++r) {
         const int t = sw + 4 * lk + r;
         if (t < len) {
-          const int64_t o = ((row0 + t) * H + h) * N + n0 + lr;
-          dCh[o] = dc[r];
-          dBh[o] = db[r];
+          const int64_t o = ((row0 + t) * Hs + h / hpb) * N + n0 + lr;
+          dCh[o] = pc[r] + dc[r];
+          dBh[o] = pb[r] + db[r];
         }
       }
       __syncthreads();
@@ -742,19 +763,42 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
   }
 }
 
+// hpb heads of one group per workgroup, one after the other (MULTI; else
+// hpb = 1): their dB and dC rows are summed in place (rows [T, H / hpb, N]).
+template <class T, int P, bool MULTI>
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
+    const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
+    const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
+    const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
+    float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
+    int L, int H, int G, int N, int nc, int hpb) {
+  if constexpr (!MULTI) {
+    chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
+                         N, nc, blockIdx.y, 1);
+  } else {
+#pragma unroll 1
+    for (int j = 0; j < hpb; ++j) {
+      chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
+                           N, nc, blockIdx.y * hpb + j, hpb);
+      __syncthreads();  // LDS is reused by the next head
+    }
+  }
+}
+
 // ---------------------------------------------------------------- group sums
-// dv's B and C channels = the sums of dBh / dCh over the heads of each group.
+// dv's B and C channels = the sums of dBh / dCh over the rows of each group
+// (Hs / G rows per group, each already the sum of a workgroup's heads).
 __global__ __launch_bounds__(kThreads) void k_group_sum(const float* __restrict__ dBh,
                                                         const float* __restrict__ dCh,
-                                                        float* dv, int64_t T, int H, int G,
+                                                        float* dv, int64_t T, int Hs, int G,
                                                         int N, int HP) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= T * G * N) return;
   const int64_t t = i / (G * N);
-  const int gn = (int)(i % (G * N)), g = gn / N, n = gn % N, hpg = H / G;
+  const int gn = (int)(i % (G * N)), g = gn / N, n = gn % N, spg = Hs / G;
   float sb = 0.f, sc = 0.f;
-  for (int k = 0; k < hpg; ++k) {
-    const int64_t o = (t * H + g * hpg + k) * N + n;
+  for (int k = 0; k < spg; ++k) {
+    const int64_t o = (t * Hs + g * spg + k) * N + n;
     sb += dBh[o];
     sc += dCh[o];
   }
@@ -1009,20 +1053,40 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
                        dso, lam_end, a.d_s_out, a.d_s_in, H, P * N, nc);
   }
   SSD_CHECK();
+  // heads per workgroup of the per-chunk kernel (their dB / dC rows summed in
+  // place): the most, up to kChunkHeads, that divide the heads of a group and
+  // leave at least 1024 workgroups; one for head size 128, whose registers
+  // do not hold the head loop
+  int hpb = P == 128 ? 1 : kChunkHeads;
+  while (hpb > 1 && ((H / G) % hpb || (int64_t)B * nc * (H / hpb) < 1024)) hpb /= 2;
+  if (a.chunk_heads > 0 && a.chunk_heads <= kChunkHeads && P != 128 && (H / G) % a.chunk_heads == 0)
+    hpb = a.chunk_heads;  // a diagnostic setting, where the shape allows it
   {
     ProfScope ps(st, KID_BWD_CHUNK);
     const size_t lds = bwd_chunk_lds(P);
-#define SSD_CB(PP)                                                                              \
-  if (bf)                                                                                       \
-    hipLaunchKernelGGL((k_chunk_bwd<bf16, PP>), gc, blk, lds, st, v, y, (const bf16*)a.dt,      \
-                       plain, a.A, a.D, states, dso, cb, dv, dBh, dCh, (bf16*)a.d_dt, dA_part,  \
-                       a.d_D ? dD_part : nullptr, L, H, G, N, nc);                              \
-  else                                                                                          \
-    hipLaunchKernelGGL((k_chunk_bwd<float, PP>), gc, blk, lds, st, v, y, (const float*)a.dt,    \
-                       plain, a.A, a.D, states, dso, cb, dv, dBh, dCh, (float*)a.d_dt, dA_part, \
-                       a.d_D ? dD_part : nullptr, L, H, G, N, nc)
+    const dim3 gh(nc, H / hpb, B);
+#define SSD_CB_M(TT, PP, MM)                                                                    \
+  hipLaunchKernelGGL((k_chunk_bwd<TT, PP, MM>), gh, blk, lds, st, v, y, (const TT*)a.dt, plain, \
+                     a.A, a.D, states, dso, cb, dv, dBh, dCh, (TT*)a.d_dt, dA_part,             \
+                     a.d_D ? dD_part : nullptr, L, H, G, N, nc, hpb)
+#define SSD_CB_T(TT, PP)             \
+  {                                  \
+    if (PP == 128 || hpb == 1)       \
+      SSD_CB_M(TT, PP, false);       \
+    else                             \
+      SSD_CB_M(TT, PP, PP != 128);   \
+  }
+#define SSD_CB(PP)      \
+  {                     \
+    if (bf)             \
+      SSD_CB_T(bf16, PP) \
+    else                \
+      SSD_CB_T(float, PP) \
+  }
     SSD_BY_P(SSD_CB)
 #undef SSD_CB
+#undef SSD_CB_T
+#undef SSD_CB_M
     // dA and dD: the chunks' parts added in a fixed order
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((H + 63) / 64)), blk, 0, st, dA_part,
                        (int64_t)H, a.d_A, B * nc, H);
@@ -1034,7 +1098,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   {
     ProfScope ps(st, KID_BWD_GROUP_SUM);
     hipLaunchKernelGGL(k_group_sum, dim3((unsigned)((T * G * N + kThreads - 1) / kThreads)), blk,
-                       0, st, dBh, dCh, dv, T, H, G, N, (int)HP);
+                       0, st, dBh, dCh, dv, T, H / hpb, G, N, (int)HP);
   }
   SSD_CHECK();
   {

@@ -553,6 +553,15 @@ def ssd_set_exchange_spin_limit(polls: int) -> int:
     return rc
 
 
+def ssd_set_backward_chunk_heads(heads: int) -> int:
+    """Diagnostic: heads per workgroup of the backward's per-chunk gradient
+    kernel (0: chosen from the shape); returns the previous setting."""
+    rc = int(_lib.load().ssd_set_backward_chunk_heads(int(heads)))
+    if rc < 0:
+        raise SSDError(rc, "ssd_set_backward_chunk_heads")
+    return rc
+
+
 def profile_start(capacity: int) -> None:
     """Time every kernel launch of the library with a pair of HIP events on
     the launch stream, for the next `capacity` launches."""

@@ -490,3 +490,17 @@ def test_backward_refuses_before_launch(lib):
     assert lib.ssd_mixer_backward_workspace_bytes(ctypes.byref(wide)) == 0
     assert _bwd_call(lib, wide, base, need) == -3
     assert _bwd_call(lib, dims(cfg, flags=4), base, need) == -3
+
+
+def test_backward_chunk_heads_setting(lib):
+    """The per-chunk workgroup heads diagnostic takes 0 or a power of two up
+    to 32, returns the previous setting, and refuses anything else."""
+    prev = lib.ssd_set_backward_chunk_heads(4)
+    try:
+        assert prev == 0
+        for bad in (-1, 3, 6, 64):
+            assert lib.ssd_set_backward_chunk_heads(bad) == -2, bad
+        assert lib.ssd_set_backward_chunk_heads(32) == 4
+        assert lib.ssd_set_backward_chunk_heads(1) == 32
+    finally:
+        lib.ssd_set_backward_chunk_heads(0)

@@ -118,6 +118,32 @@ def test_backward_bf16_layer_shape(ops):
     run_case(ops, cfg)
 
 
+HEADS_CASES = [
+    # bf16 I/O at the layer's head size, 4 heads per group: 2 and 4 per workgroup
+    ("bf16_layer_h2", "tiny_layer", dict(batch=1, seqlen=160, nheads=8, ngroups=2), 2),
+    ("bf16_layer_h4", "tiny_layer", dict(batch=1, seqlen=160, nheads=8, ngroups=2), 4),
+    # fp32, head sizes 16 and 32, 2 heads per group, ragged tails
+    ("f32_p16_h2", "tiny_fp32", dict(batch=2, seqlen=150, nheads=4, headdim=16, ngroups=2,
+                                     dstate=16), 2),
+    ("f32_p32_h2", "tiny_fp32", dict(batch=1, seqlen=200, nheads=4, headdim=32, ngroups=2,
+                                     dstate=64), 2),
+]
+
+
+@pytest.mark.parametrize("name,base,shape,heads", HEADS_CASES, ids=[c[0] for c in HEADS_CASES])
+def test_backward_heads_per_workgroup(ops, name, base, shape, heads):
+    """Several heads of a group per workgroup of the per-chunk gradient kernel,
+    one after the other, their dB and dC rows summed in place (the large
+    layer takes 32; small shapes keep one unless the diagnostic asks): every
+    gradient against the oracle."""
+    cfg = synth.replace(synth.CONFIGS[base], **shape)
+    prev = ops.ssd_set_backward_chunk_heads(heads)
+    try:
+        run_case(ops, cfg)
+    finally:
+        ops.ssd_set_backward_chunk_heads(prev)
+
+
 def test_backward_state_grad_chains(ops):
     """The initial-state gradient of a two-piece prefill chains: feeding the
     second piece's d_ssm_state_in as the first piece's d_ssm_state_out gives
