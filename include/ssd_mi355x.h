@@ -413,14 +413,17 @@ int ssd_set_exchange_spin_limit(int polls);
 
 /*
  * Diagnostic: the number of heads of one group that each workgroup of the
- * backward's per-chunk gradient kernel takes, one after the other, summing
- * their dB and dC rows in place (0, the default: the most, up to 32, that
- * divide the heads per group and leave at least 1024 workgroups; one for
- * head size 128). A setting of 1, 2, 4, 8, 16 or 32 is used by later
+ * backward's per-chunk kernels takes, one after the other: the gradient
+ * kernel sums their dB and dC rows in place, the state-gradient-term kernel
+ * stages the chunk's C once for them. 0, the default: chosen from the shape
+ * (the most, up to 32 and 8, that divide the heads per group and leave at
+ * least 1024 and 2048 workgroups; one in the gradient kernel for head size
+ * 128). A setting of 1, 2, 4, 8, 16 or 32 is used by later
  * ssd_mixer_backward calls, process wide, wherever it divides the heads per
- * group and the head size is below 128 (else the default applies); it
- * changes the order in which dB and dC are summed, nothing else. Returns the
- * previous setting, or SSD_ERR_SHAPE for any other value.
+ * group (and, in the gradient kernel, the head size is below 128; else the
+ * default applies); it changes the order in which dB and dC are summed,
+ * nothing else. Returns the previous setting, or SSD_ERR_SHAPE for any
+ * other value.
  */
 int ssd_set_backward_chunk_heads(int heads);
 

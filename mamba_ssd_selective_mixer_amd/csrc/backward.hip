@@ -289,9 +289,10 @@ __global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- dS_in part
-// Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one (chunk, head), into zb.
-// The chunk's exp(Lam_t) dY and C are staged transposed in LDS ([p][t],
-// [n][t]), so each lane reads four consecutive t of both operands in one
+// Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one chunk for hpb heads of one
+// group, one after the other, into zb. The chunk's C (shared by the heads)
+// and each head's exp(Lam_t) dY are staged transposed in LDS ([n][t],
+// [p][t]), so each lane reads four consecutive t of both operands in one
 // 16-byte read (k-permuted MFMA steps, as in the chunk-output kernel); work
 // items (16-row tile of p, up to 8 tiles of n) go round the waves.
 template <class T, int P>
@@ -299,49 +300,60 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
                                                       const float* __restrict__ dY,
                                                       const T* __restrict__ dt, DtA dta,
                                                       const float* __restrict__ A, float* zb,
-                                                      int L, int H, int G, int N, int nc) {
+                                                      int L, int H, int G, int N, int nc,
+                                                      int hpb) {
   extern __shared__ __align__(16) float sm[];
   __shared__ float lam[64], dts[64], ex[64];
   constexpr int NPT = P / 16;
   float* Yt = sm;             // [P][kQP]: exp(Lam_t) dY[t, p]
   float* Ct = sm + P * kQP;   // [N][kQP]: C[t, n]
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int c = blockIdx.x, b = blockIdx.z, g = blockIdx.y * hpb / (H / G);
   const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   const int HP = H * P;
-  const int64_t C = HP + 2 * (int64_t)G * N, xo = (int64_t)h * P, co = HP + (int64_t)(G + g) * N;
-  chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
-  stage_cols(Yt, kQP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
+  const int64_t C = HP + 2 * (int64_t)G * N, co = HP + (int64_t)(G + g) * N;
   stage_cols(Ct, kQP, v + row0 * C + co, (int)C, kQ, len, N);
-  __syncthreads();
-  float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  const int nnt = N / 16, nng = (nnt + 7) / 8;
-  const int kend = (len + 15) & ~15;  // rows past len are zero
-  for (int item = wave; item < NPT * nng; item += 4) {
-    const int pt = item % NPT, nt0 = (item / NPT) * 8, ntn = min(8, nnt - nt0);
-    f32x4 acc[8];
+#pragma unroll 1
+  for (int hj = 0; hj < hpb; ++hj) {
+    const int h = blockIdx.y * hpb + hj;
+    // the thread index is hidden per head, so lane-dependent addresses are not
+    // hoisted out of the head loop and held in registers across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+    const int64_t xo = (int64_t)h * P;
+    chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
+    stage_cols(Yt, kQP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
+    __syncthreads();
+    float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    const int nnt = N / 16, nng = (nnt + 7) / 8;
+    const int kend = (len + 15) & ~15;  // rows past len are zero
+    for (int item = wave; item < NPT * nng; item += 4) {
+      const int pt = item % NPT, nt0 = (item / NPT) * 8, ntn = min(8, nnt - nt0);
+      f32x4 acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = zero4();
-    for (int k0 = 0; k0 < kend; k0 += 16) {
-      const int kq = k0 + 4 * lk;
-      const float4 a4 = ld4(Yt + (pt * 16 + lr) * kQP + kq);
+      for (int j = 0; j < 8; ++j) acc[j] = zero4();
+      for (int k0 = 0; k0 < kend; k0 += 16) {
+        const int kq = k0 + 4 * lk;
+        const float4 a4 = ld4(Yt + (pt * 16 + lr) * kQP + kq);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < ntn) {
+            const float4 b4 = ld4(Ct + ((nt0 + j) * 16 + lr) * kQP + kq);
+            acc[j] = mma(a4.x, b4.x, acc[j]);
+            acc[j] = mma(a4.y, b4.y, acc[j]);
+            acc[j] = mma(a4.z, b4.z, acc[j]);
+            acc[j] = mma(a4.w, b4.w, acc[j]);
+          }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (j < ntn) {
-          const float4 b4 = ld4(Ct + ((nt0 + j) * 16 + lr) * kQP + kq);
-          acc[j] = mma(a4.x, b4.x, acc[j]);
-          acc[j] = mma(a4.y, b4.y, acc[j]);
-          acc[j] = mma(a4.z, b4.z, acc[j]);
-          acc[j] = mma(a4.w, b4.w, acc[j]);
-        }
+        if (j < ntn)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            out[(int64_t)(pt * 16 + 4 * lk + r) * N + (nt0 + j) * 16 + lr] = acc[j][r];
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < ntn)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out[(int64_t)(pt * 16 + 4 * lk + r) * N + (nt0 + j) * 16 + lr] = acc[j][r];
+    __syncthreads();  // Yt, lam and ex are restaged for the next head
   }
 }
 
@@ -369,6 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_rev_pass(float* buf, const float* 
 // ---------------------------------------------------------------- chunk grads
 constexpr int kNS = 16;        // width (in n) of the per-chunk gradient kernel's state slices
 constexpr int kChunkHeads = 32; // most heads of one group per per-chunk gradient workgroup
+constexpr int kZHeads = 8;      // most heads of one group per state-gradient-term workgroup
 constexpr int kBP = kNS + 4;   // pitch of such a slice stored as rows
 
 // Rows [0, ROWS) x columns [0, kNS) of a row-major fp32 matrix held in
@@ -1036,13 +1049,19 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t st) {
   {
     ProfScope ps(st, KID_BWD_CHUNK_Z);
     const size_t zl = bwd_z_lds(P, N);
+    // heads per workgroup (one C staging for all of them): the most, up to
+    // kZHeads, that divide the heads of a group and leave 2048 workgroups
+    int zh = kZHeads;
+    while (zh > 1 && ((H / G) % zh || (int64_t)B * nc * (H / zh) < 2048)) zh /= 2;
+    if (a.chunk_heads > 0 && (H / G) % a.chunk_heads == 0) zh = a.chunk_heads;  // diagnostic
+    const dim3 gz(nc, H / zh, B);
 #define SSD_Z(PP)                                                                                \
   if (bf)                                                                                        \
-    hipLaunchKernelGGL((k_chunk_z<bf16, PP>), gc, blk, zl, st, v, y, (const bf16*)a.dt, plain,   \
-                       a.A, dso, L, H, G, N, nc);                                                \
+    hipLaunchKernelGGL((k_chunk_z<bf16, PP>), gz, blk, zl, st, v, y, (const bf16*)a.dt, plain,   \
+                       a.A, dso, L, H, G, N, nc, zh);                                            \
   else                                                                                           \
-    hipLaunchKernelGGL((k_chunk_z<float, PP>), gc, blk, zl, st, v, y, (const float*)a.dt, plain, \
-                       a.A, dso, L, H, G, N, nc)
+    hipLaunchKernelGGL((k_chunk_z<float, PP>), gz, blk, zl, st, v, y, (const float*)a.dt, plain, \
+                       a.A, dso, L, H, G, N, nc, zh)
     SSD_BY_P(SSD_Z)
 #undef SSD_Z
   }

@@ -160,7 +160,7 @@ struct BackwardArgs {
   float* d_s_in;        // [B, H, P, N] or null
   void* ws;             // backward_ws_bytes(...) bytes, 256-byte aligned
   int* status;          // the call's status word
-  int chunk_heads;      // heads per per-chunk gradient workgroup; 0: chosen from the shape
+  int chunk_heads;      // heads per workgroup of the per-chunk kernels; 0: chosen from the shape
 };
 size_t backward_ws_bytes(int B, int L, int H, int P, int G, int N);
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t st);

@@ -554,8 +554,8 @@ def ssd_set_exchange_spin_limit(polls: int) -> int:
 
 
 def ssd_set_backward_chunk_heads(heads: int) -> int:
-    """Diagnostic: heads per workgroup of the backward's per-chunk gradient
-    kernel (0: chosen from the shape); returns the previous setting."""
+    """Diagnostic: heads per workgroup of the backward's per-chunk kernels
+    (0: chosen from the shape); returns the previous setting."""
     rc = int(_lib.load().ssd_set_backward_chunk_heads(int(heads)))
     if rc < 0:
         raise SSDError(rc, "ssd_set_backward_chunk_heads")

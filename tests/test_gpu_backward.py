@@ -132,9 +132,10 @@ HEADS_CASES = [
 
 @pytest.mark.parametrize("name,base,shape,heads", HEADS_CASES, ids=[c[0] for c in HEADS_CASES])
 def test_backward_heads_per_workgroup(ops, name, base, shape, heads):
-    """Several heads of a group per workgroup of the per-chunk gradient kernel,
-    one after the other, their dB and dC rows summed in place (the large
-    layer takes 32; small shapes keep one unless the diagnostic asks): every
+    """Several heads of a group per workgroup of the per-chunk kernels, one
+    after the other: the gradient kernel sums their dB and dC rows in place,
+    the state-gradient-term kernel stages C once for them (the large layer
+    takes 32 and 8; small shapes keep one unless the diagnostic asks): every
     gradient against the oracle."""
     cfg = synth.replace(synth.CONFIGS[base], **shape)
     prev = ops.ssd_set_backward_chunk_heads(heads)
