@@ -25,6 +25,7 @@ namespace ssd {
 
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kStateSB = 64;       // tokens staged per block in the chunk-state kernel
+constexpr int kStateHeads = 8;     // most heads of one group per chunk-state workgroup
 
 template <class T> struct Pad { static constexpr int v = 8; };     // fp16 operands: 16 bytes per LDS row
 template <> struct Pad<float> { static constexpr int v = 4; };
@@ -54,7 +55,9 @@ __device__ __forceinline__ void chunk_cumsum(const T* __restrict__ dt, const DtA
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: chunk states dS_k = (w x)^T B per (chunk, head, batch).
+// Phase 1: chunk states dS_k = (w x)^T B per (chunk, head, batch), for hpb
+// heads of one group per workgroup, one after the other (a chunk of one
+// 64-token slab stages B once for all of them).
 // T: I/O type (dt); TX: element type of x and B (T, or fp32 when they come
 // from the conv's internal fp32 copy). MAXT: most 16x16 output tiles per wave
 // (P N / 1024 rounded up to 16 or 32; d_state 256 with head_dim 128 needs 32).
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
     const TX* __restrict__ x, int64_t xs, const T* __restrict__ dt, const float* __restrict__ A,
     const TX* __restrict__ Bm, int64_t bs, float* __restrict__ states,
     float* __restrict__ lam_end, int* status, DtA dta, int L, int H, int G, int P, int N, int Q,
-    int nc) {
+    int nc, int hpb) {
   typedef OpT<T, F32OP> O;  // MFMA operand type
   using M = Mfma<O>;
   constexpr int KP = kStateSB + Pad<O>::v;
@@ -72,103 +75,113 @@ __global__ __launch_bounds__(kScanThreads) void k_chunk_state(
   O* BT = XwT + P * KP;                  // [N][KP]  B_s[n]
   __shared__ float lam[kScanThreads], dts[kScanThreads], wgt[kScanThreads], wsum[4];
 
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / (H / G);
+  const int c = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y * hpb / (H / G);
   const int t0 = c * Q, len = min(Q, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // this call's status word starts clear (later kernels only set bits)
   if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *status = 0;
+#pragma unroll 1
+  for (int hj = 0; hj < hpb; ++hj) {
+    const int h = blockIdx.y * hpb + hj;
+    // the thread index is hidden per head, so lane-dependent addresses are not
+    // hoisted out of the head loop and held in registers across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
 
-  chunk_cumsum<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, wsum);
-  const float lamE = lam[len - 1];
-  wgt[tid] = tid < len ? fexp(lamE - lam[tid]) * dts[tid] : 0.f;
-  __syncthreads();
-
-  const int ntn = N / 16, tiles = (P / 16) * ntn;
-  constexpr int kMaxTPW = MAXT;
-  f32x4 acc[kMaxTPW];
-#pragma unroll
-  for (int i = 0; i < kMaxTPW; ++i) acc[i] = zero4();
-
-  // staged transposed ([p][s], [n][s]) with one token per lane, so a wave's
-  // LDS stores hit consecutive addresses
-  const int P8 = P / 8, N8 = N / 8;
-  for (int s0 = 0; s0 < len; s0 += kStateSB) {
-    for (int v = tid; v < kStateSB * P8; v += kScanThreads) {
-      const int s = v % kStateSB, p0 = (v / kStateSB) * 8;
-      float xv[8];
-      if (s0 + s < len) {
-        load8(x + (row0 + s0 + s) * xs + (int64_t)h * P + p0, xv);
-        const float ww = wgt[s0 + s];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] *= ww;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<O>(xv[j]);
-    }
-    for (int v = tid; v < kStateSB * N8; v += kScanThreads) {
-      const int s = v % kStateSB, n0 = (v / kStateSB) * 8;
-      float bv[8];
-      if (s0 + s < len) {
-        load8(Bm + (row0 + s0 + s) * bs + (int64_t)g * N + n0, bv);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<O>(bv[j]);
-    }
+    chunk_cumsum<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, wsum);
+    const float lamE = lam[len - 1];
+    wgt[tid] = tid < len ? fexp(lamE - lam[tid]) * dts[tid] : 0.f;
     __syncthreads();
-    // fp32 operands: k-permuted steps, the MFMA steps of a 16-wide k block
-    // taking k = 4 (l / 16) + s for lane l, so a lane's four k values of both
-    // operands are one 16-byte read (the contraction order is free)
-    constexpr bool kF32 = std::is_same<O, float>::value;
-    const int kk = (kF32 ? 4 : M::KPL) * (lane >> 4), rr = lane & 15;
+
+    const int ntn = N / 16, tiles = (P / 16) * ntn;
+    constexpr int kMaxTPW = MAXT;
+    f32x4 acc[kMaxTPW];
+#pragma unroll
+    for (int i = 0; i < kMaxTPW; ++i) acc[i] = zero4();
+
+    // staged transposed ([p][s], [n][s]) with one token per lane, so a wave's
+    // LDS stores hit consecutive addresses
+    const int P8 = P / 8, N8 = N / 8;
+    for (int s0 = 0; s0 < len; s0 += kStateSB) {
+      for (int v = tid; v < kStateSB * P8; v += kScanThreads) {
+        const int s = v % kStateSB, p0 = (v / kStateSB) * 8;
+        float xv[8];
+        if (s0 + s < len) {
+          load8(x + (row0 + s0 + s) * xs + (int64_t)h * P + p0, xv);
+          const float ww = wgt[s0 + s];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[j] *= ww;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) XwT[(p0 + j) * KP + s] = from_f<O>(xv[j]);
+      }
+      // B is the group's: staged once when the chunk is one slab
+      if (hj == 0 || len > kStateSB)
+        for (int v = tid; v < kStateSB * N8; v += kScanThreads) {
+          const int s = v % kStateSB, n0 = (v / kStateSB) * 8;
+          float bv[8];
+          if (s0 + s < len) {
+            load8(Bm + (row0 + s0 + s) * bs + (int64_t)g * N + n0, bv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bv[j] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) BT[(n0 + j) * KP + s] = from_f<O>(bv[j]);
+        }
+      __syncthreads();
+      // fp32 operands: k-permuted steps, the MFMA steps of a 16-wide k block
+      // taking k = 4 (l / 16) + s for lane l, so a lane's four k values of both
+      // operands are one 16-byte read (the contraction order is free)
+      constexpr bool kF32 = std::is_same<O, float>::value;
+      const int kk = (kF32 ? 4 : M::KPL) * (lane >> 4), rr = lane & 15;
+#pragma unroll
+      for (int i = 0; i < kMaxTPW; ++i) {
+        const int tile = wave + 4 * i;
+        if (tile < tiles) {
+          const int tp = tile / ntn, tn = tile % ntn;
+          const O* ap = XwT + (tp * 16 + rr) * KP + kk;
+          const O* bp = BT + (tn * 16 + rr) * KP + kk;
+          if constexpr (kF32) {
+#pragma unroll
+            for (int k = 0; k < kStateSB; k += 16) {
+              const float4 a4 = *reinterpret_cast<const float4*>(ap + k);
+              const float4 b4 = *reinterpret_cast<const float4*>(bp + k);
+              acc[i] = M::mma(a4.x, b4.x, acc[i]);
+              acc[i] = M::mma(a4.y, b4.y, acc[i]);
+              acc[i] = M::mma(a4.z, b4.z, acc[i]);
+              acc[i] = M::mma(a4.w, b4.w, acc[i]);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < kStateSB; k += M::KSTEP)
+              acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
 #pragma unroll
     for (int i = 0; i < kMaxTPW; ++i) {
       const int tile = wave + 4 * i;
       if (tile < tiles) {
         const int tp = tile / ntn, tn = tile % ntn;
-        const O* ap = XwT + (tp * 16 + rr) * KP + kk;
-        const O* bp = BT + (tn * 16 + rr) * KP + kk;
-        if constexpr (kF32) {
 #pragma unroll
-          for (int k = 0; k < kStateSB; k += 16) {
-            const float4 a4 = *reinterpret_cast<const float4*>(ap + k);
-            const float4 b4 = *reinterpret_cast<const float4*>(bp + k);
-            acc[i] = M::mma(a4.x, b4.x, acc[i]);
-            acc[i] = M::mma(a4.y, b4.y, acc[i]);
-            acc[i] = M::mma(a4.z, b4.z, acc[i]);
-            acc[i] = M::mma(a4.w, b4.w, acc[i]);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < kStateSB; k += M::KSTEP)
-            acc[i] = M::mma(M::ld(ap + k), M::ld(bp + k), acc[i]);
+        for (int r = 0; r < 4; ++r) {
+          const int p = tp * 16 + 4 * (lane >> 4) + r, n = tn * 16 + (lane & 15);
+          out[(int64_t)p * N + n] = acc[i][r];
         }
       }
     }
-    __syncthreads();
+    if (tid == 0) lam_end[((int64_t)b * H + h) * nc + c] = lamE;
   }
-
-  float* out = states + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-#pragma unroll
-  for (int i = 0; i < kMaxTPW; ++i) {
-    const int tile = wave + 4 * i;
-    if (tile < tiles) {
-      const int tp = tile / ntn, tn = tile % ntn;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = tp * 16 + 4 * (lane >> 4) + r, n = tn * 16 + (lane & 15);
-        out[(int64_t)p * N + n] = acc[i][r];
-      }
-    }
-  }
-  if (tid == 0) lam_end[((int64_t)b * H + h) * nc + c] = lamE;
 }
 
 // ---------------------------------------------------------------------------
@@ -210,13 +223,17 @@ hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanSh
                               const void* Bm, int64_t bs, float* states, float* lam_end,
                               int* status, hipStream_t st) {
   ProfScope ps(st, KID_CHUNK_STATE);
-  dim3 grid(s.nc, s.H, s.B), block(kScanThreads);
+  // heads per workgroup: the most, up to kStateHeads, that divide the heads
+  // of a group and leave 2048 workgroups (one slab per chunk: B staged once)
+  int hpb = s.Q <= kStateSB ? kStateHeads : 1;
+  while (hpb > 1 && ((s.H / s.G) % hpb || (int64_t)s.B * s.nc * (s.H / hpb) < 2048)) hpb /= 2;
+  dim3 grid(s.nc, s.H / hpb, s.B), block(kScanThreads);
   const size_t lds = state_lds(io_bf16 && !f32op, s.P, s.N);
   const bool t32 = s.P * s.N > 16 * 1024;  // tiles per wave beyond 16
 #define SSD_STATE_T(TT, TX, F, T)                                                              \
   hipLaunchKernelGGL((k_chunk_state<TT, TX, F, T>), grid, block, lds, st, (const TX*)x, xs,     \
                      (const TT*)dt, A, (const TX*)Bm, bs, states, lam_end, status, s.dta, s.L,  \
-                     s.H, s.G, s.P, s.N, s.Q, s.nc)
+                     s.H, s.G, s.P, s.N, s.Q, s.nc, hpb)
 #define SSD_STATE(TT, TX, F) \
   if (t32) SSD_STATE_T(TT, TX, F, 32); else SSD_STATE_T(TT, TX, F, 16)
   if (!io_bf16) {

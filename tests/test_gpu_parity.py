@@ -224,6 +224,17 @@ def test_chunk_scan_strided_views(ops, kw):
     check("final state (strided)", host(so), rs, TOL[cfg.dtype])
 
 
+@pytest.mark.parametrize("kw", [
+    dict(dtype="f32", nheads=64, headdim=16, ngroups=4, dstate=16),   # 16 heads per group
+    dict(dtype="bf16", nheads=64, headdim=32, ngroups=8, dstate=64),  # fp16 operands
+])
+def test_chunk_scan_state_heads_per_workgroup(ops, kw):
+    """Long enough (2 x 2048 tokens, 64 heads) that the chunk-state kernel
+    takes two heads of a group per workgroup, staging the chunk's B once for
+    both."""
+    scan_case(ops, small("tiny_layer", batch=2, seqlen=2048, **kw), True, True)
+
+
 def test_chunk_scan_fp32_shapes(ops):
     scan_case(ops, small("tiny_fp32", nheads=8, headdim=32, ngroups=2, dstate=64, seqlen=130,
                          batch=2), True, True)
