@@ -931,7 +931,9 @@ __global__ __launch_bounds__(kThreads) void k_conv_dx(const float* __restrict__ 
 
 // Workspace of the backward pass (fp32): conv output v [T, Cch], y then dY
 // [T, H*P], carried-in states and their gradients [B, nc, H, P, N], Lam_end
-// [B, H, nc], per-head dB / dC [T, H, N], dv [T, Cch]; 64-token chunks.
+// [B, H, nc], dB / dC rows per per-chunk workgroup [T, H / hpb, N] (sized
+// for hpb = 1), dv [T, Cch], the partial sums, and each chunk's C B^T per
+// group [B, nc, G, Q, Q]; 64-token chunks.
 namespace {
 size_t bround(size_t b) { return (b + 255) / 256 * 256; }
 
