@@ -14,6 +14,7 @@
 namespace ssd {
 
 constexpr int kConvTT = 32;   // tokens per thread
+constexpr int kConvAhead = 4; // input rows loaded ahead of their use
 constexpr int kConvThreads = 256;
 
 // TO: output element type (the I/O type, or fp32 for the scan's internal copy)
@@ -48,8 +49,9 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d(
     }
   }
   const int tend = min(L, t0 + kConvTT);
-  for (int t = t0; t < tend; ++t) {
-    load8(xbc + ((int64_t)b * L + t) * xs + c0, win[W - 1]);
+  // one output row from win[] (its newest row in win[W-1]), then the window
+  // slides by one
+  auto step = [&](int t) {
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -63,6 +65,24 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d(
     for (int r = 0; r < W - 1; ++r)
 #pragma unroll
       for (int j = 0; j < 8; ++j) win[r][j] = win[r + 1][j];
+  };
+  // kConvAhead rows are loaded before any of them is used, so a short run
+  // does not wait one memory latency per token
+  int t = t0;
+  for (; t + kConvAhead <= tend; t += kConvAhead) {
+    float rows[kConvAhead][8];
+#pragma unroll
+    for (int q = 0; q < kConvAhead; ++q) load8(xbc + ((int64_t)b * L + t + q) * xs + c0, rows[q]);
+#pragma unroll
+    for (int q = 0; q < kConvAhead; ++q) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) win[W - 1][j] = rows[q][j];
+      step(t + q);
+    }
+  }
+  for (; t < tend; ++t) {
+    load8(xbc + ((int64_t)b * L + t) * xs + c0, win[W - 1]);
+    step(t);
   }
 }
 
