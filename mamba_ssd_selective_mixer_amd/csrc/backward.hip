@@ -289,12 +289,43 @@ __global__ __launch_bounds__(kThreads) void k_sum_parts(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- dS_in part
+// Rows [0, 64) x columns [0, COLS) of a row-major fp32 matrix held in
+// registers (rows >= nrows zero), then stored transposed and scaled per row
+// (element (r, c) at c * pitch + r, times sc[r]), with stage_cols' mapping.
+template <int COLS>
+struct ColRegs {
+  static constexpr int kItems = kQ * (COLS / 4), kN = (kItems + kThreads - 1) / kThreads;
+  float4 v[kN];
+  SSD_DEV void load(const float* src, int rs, int nrows) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx % kQ, c4 = (idx / kQ) * 4;
+      v[i] = (idx < kItems && r < nrows) ? ld4(src + (int64_t)r * rs + c4)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  SSD_DEV void store_cols(float* dst, int pitch, const float* sc) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      const int idx = threadIdx.x + i * kThreads, r = idx % kQ, c4 = (idx / kQ) * 4;
+      if (idx < kItems) {
+        const float f = sc[r];
+        dst[(c4 + 0) * pitch + r] = v[i].x * f;
+        dst[(c4 + 1) * pitch + r] = v[i].y * f;
+        dst[(c4 + 2) * pitch + r] = v[i].z * f;
+        dst[(c4 + 3) * pitch + r] = v[i].w * f;
+      }
+    }
+  }
+};
+
 // Z[p,n] = sum_t exp(Lam_t) dY[t,p] C[t,n] of one chunk for hpb heads of one
 // group, one after the other, into zb. The chunk's C (shared by the heads)
 // and each head's exp(Lam_t) dY are staged transposed in LDS ([n][t],
 // [p][t]), so each lane reads four consecutive t of both operands in one
 // 16-byte read (k-permuted MFMA steps, as in the chunk-output kernel); work
-// items (16-row tile of p, up to 8 tiles of n) go round the waves.
+// items (16-row tile of p, up to 8 tiles of n) go round the waves. The next
+// head's dY rows are loaded into registers while a head is computed.
 template <class T, int P>
 __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ v,
                                                       const float* __restrict__ dY,
@@ -313,6 +344,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
   const int HP = H * P;
   const int64_t C = HP + 2 * (int64_t)G * N, co = HP + (int64_t)(G + g) * N;
   stage_cols(Ct, kQP, v + row0 * C + co, (int)C, kQ, len, N);
+  ColRegs<P> yr;
+  yr.load(dY + row0 * HP + (int64_t)blockIdx.y * hpb * P, HP, len);
 #pragma unroll 1
   for (int hj = 0; hj < hpb; ++hj) {
     const int h = blockIdx.y * hpb + hj;
@@ -321,10 +354,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_z(const float* __restrict__ 
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
-    const int64_t xo = (int64_t)h * P;
     chunk_lam<T>(dt, dta, row0, h, a_of(A, dta, h), len, lam, dts, ex);
-    stage_cols(Yt, kQP, dY + row0 * HP + xo, HP, kQ, len, P, ex);
+    yr.store_cols(Yt, kQP, ex);
     __syncthreads();
+    if (hj + 1 < hpb) yr.load(dY + row0 * HP + (int64_t)(h + 1) * P, HP, len);
     float* out = zb + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
     const int nnt = N / 16, nng = (nnt + 7) / 8;
     const int kend = (len + 15) & ~15;  // rows past len are zero
