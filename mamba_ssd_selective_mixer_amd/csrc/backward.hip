@@ -482,7 +482,8 @@ __device__ __forceinline__ void chunk_bwd_head(
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
     const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
     float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
-    int L, int H, int G, int N, int nc, int h, int hpb) {
+    int L, int H, int G, int N, int nc, int h, int hpb, SliceRegs<kQ>& ry, SliceRegs<kQ>& rx,
+    bool fetched) {
   extern __shared__ __align__(16) float sm[];
   float* Mt = sm;                // [Q][kQP]: G, then M = G o E dt_s
   float* Dg = sm + kQ * kQP;     // [Q][kQP]: K, then dG = K o E dt_s
@@ -526,13 +527,12 @@ __device__ __forceinline__ void chunk_bwd_head(
     }
     float* Ys = SA;
     float* Xs = SA + kQ * kSP;
-    SliceRegs<kQ> ry, rx;
     auto fetch = [&](int k0) {
       const int nvp = min(kKS, P - k0);
       ry.load(dY + row0 * HP + xo + k0, HP, len, nvp);
       rx.load(v + row0 * C + xo + k0, (int)C, len, nvp);
     };
-    fetch(0);
+    if (!fetched) fetch(0);  // else the previous head loaded the first slice
     for (int k0 = 0; k0 < P; k0 += kKS) {
       const int nvp = min(kKS, P - k0);
       ry.store(Ys);
@@ -747,6 +747,14 @@ __device__ __forceinline__ void chunk_bwd_head(
     }
   }
 
+  // the next head of the workgroup: its first slice of dY and X, loaded
+  // while this head finishes
+  if (h % hpb + 1 < hpb) {
+    const int nvp = min(kKS, P);
+    ry.load(dY + row0 * HP + xo + P, HP, len, nvp);
+    rx.load(v + row0 * C + xo + P, (int)C, len, nvp);
+  }
+
   // (5) dX, and the row sums U_s, Y_t; dD and <dS_out, S_in>. Lane l holds
   // four consecutive p of token s = sw + l % 16 in a1, a2, ya and xa.
   {
@@ -818,14 +826,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
     float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
     int L, int H, int G, int N, int nc, int hpb) {
+  SliceRegs<kQ> ry, rx;  // the first dY / X slice of a head's K product
   if constexpr (!MULTI) {
     chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
-                         N, nc, blockIdx.y, 1);
+                         N, nc, blockIdx.y, 1, ry, rx, false);
   } else {
 #pragma unroll 1
     for (int j = 0; j < hpb; ++j) {
       chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
-                           N, nc, blockIdx.y * hpb + j, hpb);
+                           N, nc, blockIdx.y * hpb + j, hpb, ry, rx, j > 0);
       __syncthreads();  // LDS is reused by the next head
     }
   }
