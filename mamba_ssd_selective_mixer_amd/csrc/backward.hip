@@ -480,10 +480,10 @@ template <class T, int P>
 __device__ __forceinline__ void chunk_bwd_head(
     const float* __restrict__ v, const float* __restrict__ dY, const T* __restrict__ dt, DtA dta,
     const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ Sin,
-    const float* __restrict__ dSo, const float* __restrict__ cb, float* __restrict__ dv,
+    const float* __restrict__ dSo, float* __restrict__ dv,
     float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
     int L, int H, int G, int N, int nc, int h, int hpb, SliceRegs<kQ>& ry, SliceRegs<kQ>& rx,
-    bool fetched) {
+    bool fetched, const f32x4 (&gt)[3]) {
   extern __shared__ __align__(16) float sm[];
   float* Mt = sm;                // [Q][kQP]: G, then M = G o E dt_s
   float* Dg = sm + kQ * kQP;     // [Q][kQP]: K, then dG = K o E dt_s
@@ -514,8 +514,8 @@ __device__ __forceinline__ void chunk_bwd_head(
   const float lamE = lam[len - 1];
   if (tid < 64) wv[tid] = tid < len ? __expf(lamE - lam[tid]) * dts[tid] : 0.f;
 
-  // (1) K = dY X^T on the causal tiles over slices of p; G from the group's
-  // C B^T (computed once per chunk and group)
+  // (1) K = dY X^T on the causal tiles over slices of p; G (gt) from the
+  // group's C B^T, computed once per chunk and group
   {
     int rt[3], st[3];
     bool on[3];
@@ -549,14 +549,13 @@ __device__ __forceinline__ void chunk_bwd_head(
                          ld4(Xs + (st[i] * 16 + lr) * kSP + kk + 4 * lk), aK[i]);
       __syncthreads();
     }
-    const float* cbk = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
 #pragma unroll
     for (int i = 0; i < 3; ++i)
       if (on[i])
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
-          Mt[t * kQP + s] = cbk[t * kQ + s];
+          Mt[t * kQP + s] = gt[i][r];
           Dg[t * kQP + s] = aK[i][r];
         }
   }
@@ -827,14 +826,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_bwd(
     float* __restrict__ dBh, float* __restrict__ dCh, T* __restrict__ ddt, float* dA, float* dD,
     int L, int H, int G, int N, int nc, int hpb) {
   SliceRegs<kQ> ry, rx;  // the first dY / X slice of a head's K product
+  // this wave's causal tiles of the group's C B^T, the same for every head
+  // of the workgroup (element (t, s) at t Q + s)
+  f32x4 gt[3];
+  {
+    const int lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+    const int g = blockIdx.y * hpb / (H / G);
+    const float* cbk = cb + (((int64_t)blockIdx.z * nc + blockIdx.x) * G + g) * (kQ * kQ);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      int rt, st;
+      const bool on = causal_tile(threadIdx.x >> 6, i, rt, st);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        gt[i][r] = on ? cbk[(rt * 16 + 4 * lk + r) * kQ + st * 16 + lr] : 0.f;
+    }
+  }
   if constexpr (!MULTI) {
-    chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
-                         N, nc, blockIdx.y, 1, ry, rx, false);
+    chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, dv, dBh, dCh, ddt, dA, dD, L, H, G, N,
+                         nc, blockIdx.y, 1, ry, rx, false, gt);
   } else {
 #pragma unroll 1
     for (int j = 0; j < hpb; ++j) {
-      chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, cb, dv, dBh, dCh, ddt, dA, dD, L, H, G,
-                           N, nc, blockIdx.y * hpb + j, hpb, ry, rx, j > 0);
+      chunk_bwd_head<T, P>(v, dY, dt, dta, A, D, Sin, dSo, dv, dBh, dCh, ddt, dA, dD, L, H, G, N,
+                           nc, blockIdx.y * hpb + j, hpb, ry, rx, j > 0, gt);
       __syncthreads();  // LDS is reused by the next head
     }
   }
