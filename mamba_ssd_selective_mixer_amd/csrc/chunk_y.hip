@@ -16,6 +16,7 @@ namespace ssd {
 namespace f32t {
 
 constexpr int kStatusNonFinite = 2;  // status bit: an output is not finite
+constexpr int kYHeads = 8;           // most heads of one group per output workgroup
 
 // G = C B^T of one chunk and group on the ten causal 16x16 tiles (three per
 // wave at most), shared by every head of the group: cb [B][nc][G][Q][Q],
@@ -89,117 +90,131 @@ __global__ __launch_bounds__(kThreads) void k_chunk_cb(const TX* __restrict__ Bm
 // (from the group's C B^T), C S_in^T on its rows over 32-wide slices of n
 // (the next slice's loads in flight while one is computed), M into LDS,
 // then M X over its rows from the chunk's x staged transposed in LDS; the
-// k-permuted MFMA steps as in k_chunk_cb.
+// k-permuted MFMA steps as in k_chunk_cb. A workgroup takes hpb heads of
+// one group, one after the other; the G tiles are read once for all.
 template <class T, class TX, class TY, int P>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_y(
     const TX* __restrict__ x, int64_t xs, const TX* __restrict__ Cm, int64_t bs,
     const float* __restrict__ cb, const T* __restrict__ dt, DtA dta, const float* __restrict__ A,
     const float* __restrict__ D, const float* __restrict__ Sin, TY* __restrict__ y, int* status,
-    int L, int H, int G, int N, int nc) {
+    int L, int H, int G, int N, int nc, int hpb) {
   extern __shared__ __align__(16) float sm[];
   float* Mt = sm;                 // [Q][kQP]: M
   float* Cs = sm + kQ * kQP;      // [Q][kSP]
   float* Ss = Cs + kQ * kSP;      // [P][kSP]
   __shared__ float lam[64], dts[64], ex[64];
   constexpr int NPT = P / 16;
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+  const int c = blockIdx.x, b = blockIdx.z, g = blockIdx.y * hpb / (H / G);
   const int t0 = c * kQ, len = min(kQ, L - t0);
   const int64_t row0 = (int64_t)b * L + t0;
   const int HP = H * P;
   const int xsi = (int)xs, bsi = (int)bs;
-  const TX* xr = x + row0 * xs + (int64_t)h * P;
   const TX* cr = Cm + row0 * bs + (int64_t)g * N;
-  const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
-  const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
-  chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
   int rt[3], st[3];
   bool on[3];
+  f32x4 aG[3];
+  {
+    const int lane = threadIdx.x & 63, lr = lane & 15, lk = lane >> 4;
+    const float* cbk = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) on[i] = causal_tile(wave, i, rt[i], st[i]);
-  f32x4 aG[3], aY[NPT];
-  const float* cbk = cb + (((int64_t)b * nc + c) * G + g) * (kQ * kQ);
+    for (int i = 0; i < 3; ++i) {
+      on[i] = causal_tile(threadIdx.x >> 6, i, rt[i], st[i]);
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (on[i])
+      for (int r = 0; r < 4; ++r)
+        aG[i][r] = on[i] ? cbk[(rt[i] * 16 + 4 * lk + r) * kQ + st[i] * 16 + lr] : 0.f;
+    }
+  }
+#pragma unroll 1
+  for (int hj = 0; hj < hpb; ++hj) {
+    const int h = blockIdx.y * hpb + hj;
+    // the thread index is hidden per head, so lane-dependent addresses are
+    // not hoisted out of the head loop and held in registers across it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+    const TX* xr = x + row0 * xs + (int64_t)h * P;
+    const float Ah = a_of(A, dta, h), Dh = D ? D[h] : 0.f;
+    const float* Si = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N;
+    chunk_lam<T>(dt, dta, row0, h, Ah, len, lam, dts, ex);
+    f32x4 aY[NPT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) aG[i][r] = cbk[(rt[i] * 16 + 4 * lk + r) * kQ + st[i] * 16 + lr];
+    for (int i = 0; i < NPT; ++i) aY[i] = zero4();
+    const int sw = wave * 16;
+    SliceRegs<kQ> rc;
+    SliceRegs<P> rs;
+    auto fetch = [&](int n0) {
+      const int nv = min(kKS, N - n0);
+      rc.load(cr + n0, bsi, len, nv);
+      rs.load(Si + n0, N, P, nv);
+    };
+    fetch(0);
+    for (int n0 = 0; n0 < N; n0 += kKS) {
+      const int nv = min(kKS, N - n0);
+      rc.store(Cs);
+      rs.store(Ss);
+      __syncthreads();
+      if (n0 + kKS < N) fetch(n0 + kKS);
+      // nv is a multiple of 16 (so is every supported N)
+      for (int kk = 0; kk < nv; kk += 16) {
+        const int kq = kk + 4 * lk;
+        const float4 a4 = ld4(Cs + (sw + lr) * kSP + kq);
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) aY[i] = zero4();
-  const int sw = wave * 16;
-  SliceRegs<kQ> rc;
-  SliceRegs<P> rs;
-  auto fetch = [&](int n0) {
-    const int nv = min(kKS, N - n0);
-    rc.load(cr + n0, bsi, len, nv);
-    rs.load(Si + n0, N, P, nv);
-  };
-  fetch(0);
-  for (int n0 = 0; n0 < N; n0 += kKS) {
-    const int nv = min(kKS, N - n0);
-    rc.store(Cs);
-    rs.store(Ss);
+        for (int pt = 0; pt < NPT; ++pt) {
+          const float4 b4 = ld4(Ss + (pt * 16 + lr) * kSP + kq);
+          aY[pt] = mma(a4.x, b4.x, aY[pt]);
+          aY[pt] = mma(a4.y, b4.y, aY[pt]);
+          aY[pt] = mma(a4.z, b4.z, aY[pt]);
+          aY[pt] = mma(a4.w, b4.w, aY[pt]);
+        }
+      }
+      __syncthreads();
+    }
+    // M = G o E dt_s on the causal tiles (rows and columns past the chunk: 0)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (on[i])
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
+          const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
+          Mt[t * kQP + s] = aG[i][r] * f;
+        }
+#pragma unroll
+    for (int pt = 0; pt < NPT; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
+    // the chunk's x transposed, [p][t], where C and S_in were staged
+    float* Xt = Cs;
+    stage_cols(Xt, kQP, xr, xsi, kQ, len, P);
     __syncthreads();
-    if (n0 + kKS < N) fetch(n0 + kKS);
-    // nv is a multiple of 16 (so is every supported N)
-    for (int kk = 0; kk < nv; kk += 16) {
-      const int kq = kk + 4 * lk;
-      const float4 a4 = ld4(Cs + (sw + lr) * kSP + kq);
+    // + M X over s <= t (the wave's rows reach s < sw + 16)
+    for (int k0 = 0; k0 < sw + 16; k0 += 16) {
+      const int kq = k0 + 4 * lk;
+      const float4 a4 = ld4(Mt + (sw + lr) * kQP + kq);
 #pragma unroll
       for (int pt = 0; pt < NPT; ++pt) {
-        const float4 b4 = ld4(Ss + (pt * 16 + lr) * kSP + kq);
+        const float4 b4 = ld4(Xt + (pt * 16 + lr) * kQP + kq);
         aY[pt] = mma(a4.x, b4.x, aY[pt]);
         aY[pt] = mma(a4.y, b4.y, aY[pt]);
         aY[pt] = mma(a4.z, b4.z, aY[pt]);
         aY[pt] = mma(a4.w, b4.w, aY[pt]);
       }
     }
-    __syncthreads();
-  }
-  // M = G o E dt_s on the causal tiles (rows and columns past the chunk: 0)
+    float chk = 0.f;  // NaN once an output is infinite or NaN
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
-    if (on[i])
+    for (int pt = 0; pt < NPT; ++pt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = rt[i] * 16 + 4 * lk + r, s = st[i] * 16 + lr;
-        const float f = (s <= t && t < len) ? __expf(lam[t] - lam[s]) * dts[s] : 0.f;
-        Mt[t * kQP + s] = aG[i][r] * f;
+        const int t = sw + 4 * lk + r, p = pt * 16 + lr;
+        if (t < len) {
+          const float yv = aY[pt][r] + Dh * Xt[p * kQP + t];
+          chk += yv * 0.f;
+          y[(row0 + t) * HP + (int64_t)h * P + p] = from_f<TY>(yv);
+        }
       }
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) aY[pt][r] *= ex[sw + 4 * lk + r];
-  // the chunk's x transposed, [p][t], where C and S_in were staged
-  float* Xt = Cs;
-  stage_cols(Xt, kQP, xr, xsi, kQ, len, P);
-  __syncthreads();
-  // + M X over s <= t (the wave's rows reach s < sw + 16)
-  for (int k0 = 0; k0 < sw + 16; k0 += 16) {
-    const int kq = k0 + 4 * lk;
-    const float4 a4 = ld4(Mt + (sw + lr) * kQP + kq);
-#pragma unroll
-    for (int pt = 0; pt < NPT; ++pt) {
-      const float4 b4 = ld4(Xt + (pt * 16 + lr) * kQP + kq);
-      aY[pt] = mma(a4.x, b4.x, aY[pt]);
-      aY[pt] = mma(a4.y, b4.y, aY[pt]);
-      aY[pt] = mma(a4.z, b4.z, aY[pt]);
-      aY[pt] = mma(a4.w, b4.w, aY[pt]);
-    }
+    if (status && chk != 0.f) atomicOr(status, kStatusNonFinite);
+    __syncthreads();  // LDS and lam are reused by the next head
   }
-  float chk = 0.f;  // NaN once an output is infinite or NaN
-#pragma unroll
-  for (int pt = 0; pt < NPT; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = sw + 4 * lk + r, p = pt * 16 + lr;
-      if (t < len) {
-        const float yv = aY[pt][r] + Dh * Xt[p * kQP + t];
-        chk += yv * 0.f;
-        y[(row0 + t) * HP + (int64_t)h * P + p] = from_f<TY>(yv);
-      }
-    }
-  if (status && chk != 0.f) atomicOr(status, kStatusNonFinite);
 }
 
 size_t chunk_y_lds(int P) {
@@ -240,12 +255,17 @@ hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape&
   hipError_t e = launch_chunk_cb(io_bf16 && !x_f32, s, Bm, Cm, bs, cb, st);
   if (e != hipSuccess) return e;
   ProfScope ps(st, kid);
-  const dim3 grid(s.nc, s.H, s.B), blk(kThreads);
+  // heads per workgroup (the group's C B^T tiles read once for them): the
+  // most, up to kYHeads, that divide the heads of a group and leave 2048
+  // workgroups
+  int hpb = kYHeads;
+  while (hpb > 1 && ((s.H / s.G) % hpb || (int64_t)s.B * s.nc * (s.H / hpb) < 2048)) hpb /= 2;
+  const dim3 grid(s.nc, s.H / hpb, s.B), blk(kThreads);
   const size_t lds = chunk_y_lds(s.P);
 #define SSD_Y(TT, TX, TY, PP)                                                                   \
   hipLaunchKernelGGL((k_chunk_y<TT, TX, TY, PP>), grid, blk, lds, st, (const TX*)x, xs,         \
                      (const TX*)Cm, bs, cb, (const TT*)dt, s.dta, A, D, states, (TY*)y, status, \
-                     s.L, s.H, s.G, s.N, s.nc)
+                     s.L, s.H, s.G, s.N, s.nc, hpb)
 #define SSD_Y_P(TT, TX, TY)                  \
   switch (s.P) {                             \
     case 16: SSD_Y(TT, TX, TY, 16); break;   \
