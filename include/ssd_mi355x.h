@@ -428,6 +428,20 @@ int ssd_set_exchange_spin_limit(int polls);
 int ssd_set_backward_chunk_heads(int heads);
 
 /*
+ * Diagnostic: where the general kernels (every shape outside the fused
+ * path) apply the grouped gated RMSNorm ("feat(model): Nemotron-H hybrid
+ * ... on the CPU", section "2. feat(model)": GatedRMSNorm after the scan).
+ * 0, the default: inside the chunk-output kernel when a norm group (1, 2,
+ * 4 or 8 heads, at most 256 channels) fits one workgroup and the call has
+ * at least 512 (chunk, group) workgroups, else y goes to the workspace and
+ * a separate norm kernel follows; 1: inside the output kernel wherever the
+ * group fits; 2: always the separate kernel. Either way the same values
+ * are computed (the sums run in another order). Process wide, for later
+ * calls. Returns the previous mode, or SSD_ERR_SHAPE for any other value.
+ */
+int ssd_set_output_norm_fusion(int mode);
+
+/*
  * Per-kernel timing of the library's own launches, a measurement aid (the
  * timing is read on the stream each kernel runs on, so it needs no access
  * to the caller's streams). ssd_profile_start(capacity) creates `capacity`

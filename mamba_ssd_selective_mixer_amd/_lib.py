@@ -31,7 +31,7 @@ EXPORTS = ("ssd_conv_channels", "ssd_ssm_state_bytes", "ssd_conv_state_bytes", "
            "ssd_mixer_varlen_workspace_bytes", "ssd_mixer_varlen",
            "ssd_mixer_prefill_noalloc", "ssd_mixer_backward_workspace_bytes",
            "ssd_mixer_backward", "ssd_workspace_status", "ssd_set_exchange_spin_limit",
-           "ssd_set_backward_chunk_heads",
+           "ssd_set_backward_chunk_heads", "ssd_set_output_norm_fusion",
            "ssd_profile_start", "ssd_profile_stop", "ssd_profile_set_mask", "ssd_profile_read",
            "ssd_kernel_name")
 
@@ -85,6 +85,7 @@ def load():
         "ssd_workspace_status": (i32, [vp, vp]),
         "ssd_set_exchange_spin_limit": (i32, [i32]),
         "ssd_set_backward_chunk_heads": (i32, [i32]),
+        "ssd_set_output_norm_fusion": (i32, [i32]),
         "ssd_profile_start": (i32, [i32]),
         "ssd_profile_stop": (i32, []),
         "ssd_profile_set_mask": (ctypes.c_uint64, [ctypes.c_uint64]),

@@ -24,6 +24,12 @@ bool f32op(const ssd_dims* d) { return (d->flags & SSD_FLAG_FP32_OPERANDS) != 0;
 // bound on the polls of the fast path's cross-block norm exchange
 std::atomic<int> g_spin_limit{1 << 20};
 std::atomic<int> g_bwd_heads{0};  // backward per-chunk workgroup heads; 0: from the shape
+// general path's norm: 0 fused into the output kernel from the shape, 1
+// fused wherever a norm group fits one workgroup, 2 never (y, then the norm)
+std::atomic<int> g_norm_fuse{0};
+// fewest (chunk, group) workgroups for which the shape-chosen fusion pays:
+// fewer leave the chip idle while each workgroup walks its group's heads
+constexpr int64_t kNormFuseBlocks = 512;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool is_one_of(int v, std::initializer_list<int> set) {
   for (int s : set)
@@ -185,6 +191,16 @@ int run_scan(const ssd_dims* d, const void* x, int64_t xs, const void* dt, const
   if (rc) return rc;
   rc = hip_status(ssd::launch_state_pass(s, ws.states, ws.lam_end, s_in, s_out, ws.status, st));
   if (rc) return rc;
+  const int fuse = g_norm_fuse.load(std::memory_order_relaxed);
+  const int64_t blocks = (int64_t)d->batch * s.nc * d->ngroups;
+  if (z && ssd::chunk_y_fuses_norm(d->nheads, d->ngroups, d->headdim) &&
+      (fuse == 1 || (fuse == 0 && blocks >= kNormFuseBlocks))) {
+    // one workgroup holds a whole norm group: the norm runs in the output kernel
+    const ssd::YNorm nm{z, zs, norm_w, eps};
+    return hip_status(ssd::launch_chunk_y(bf, x_f32, !bf, s, x, xs, Bm, Cm, bs, ws.cb, dt, A, D,
+                                          ws.states, y, ws.status, ssd::KID_CHUNK_OUT, st,
+                                          &nm));
+  }
   const bool fused_norm = z != nullptr;
   void* ydst = fused_norm ? (void*)ws.y32 : y;
   rc = hip_status(ssd::launch_chunk_y(bf, x_f32, fused_norm || !bf, s, x, xs, Bm, Cm, bs, ws.cb,
@@ -796,6 +812,11 @@ int ssd_set_exchange_spin_limit(int polls) {
 int ssd_set_backward_chunk_heads(int heads) {
   if (heads < 0 || heads > 32 || (heads & (heads - 1))) return SSD_ERR_SHAPE;
   return g_bwd_heads.exchange(heads);
+}
+
+int ssd_set_output_norm_fusion(int mode) {
+  if (mode < 0 || mode > 2) return SSD_ERR_SHAPE;
+  return g_norm_fuse.exchange(mode);
 }
 
 }  // extern "C"

@@ -45,15 +45,29 @@ hipError_t launch_chunk_state(bool io_bf16, bool x_f32, bool f32op, const ScanSh
                               int* status, hipStream_t st);
 hipError_t launch_state_pass(const ScanShape& s, float* states, const float* lam_end,
                              const float* s_in, float* s_out, int* status, hipStream_t st);
+// The grouped gated RMSNorm fused into the chunk-output kernel: z (I/O
+// type, token stride zs), the norm weight w [H P] (I/O type) and eps.
+struct YNorm {
+  const void* z;
+  int64_t zs;
+  const void* w;
+  float eps;
+};
+// Whether the output kernel can fuse the norm: a norm group of 1, 2, 4 or
+// 8 heads and at most 256 channels (one workgroup holds it in registers).
+bool chunk_y_fuses_norm(int H, int G, int P);
 // Chunk outputs on fp32 MFMA operands (s.Q must be 64): y = M X + exp(Lam)
 // C S_in^T + D X. x_f32: x, B, C fp32 (else the I/O type); y_f32: y fp32
 // (else the I/O type). cb: chunk_cb_bytes of workspace, filled first with
 // each chunk's C B^T per group (launch_chunk_cb). kid: the kernel id the
-// timing aid records the output kernel under.
+// timing aid records the output kernel under. norm: when given (and
+// chunk_y_fuses_norm holds), y is the normalised output in the I/O type
+// (y_f32 must then say whether the I/O type is fp32).
 hipError_t launch_chunk_y(bool io_bf16, bool x_f32, bool y_f32, const ScanShape& s,
                           const void* x, int64_t xs, const void* Bm, const void* Cm, int64_t bs,
                           float* cb, const void* dt, const float* A, const float* D,
-                          const float* states, void* y, int* status, int kid, hipStream_t st);
+                          const float* states, void* y, int* status, int kid, hipStream_t st,
+                          const YNorm* norm = nullptr);
 // C B^T of each 64-token chunk and group on the causal 16x16 tiles into cb
 // [B][nc][G][64][64] (fp32; element (t, s) at t 64 + s). x_bf16: B and C
 // are bf16 (else fp32).

@@ -562,6 +562,16 @@ def ssd_set_backward_chunk_heads(heads: int) -> int:
     return rc
 
 
+def ssd_set_output_norm_fusion(mode: int) -> int:
+    """Diagnostic: the general kernels' gated norm inside the output kernel
+    (0: chosen from the shape, 1: wherever the group fits, 2: never);
+    returns the previous mode."""
+    rc = int(_lib.load().ssd_set_output_norm_fusion(int(mode)))
+    if rc < 0:
+        raise SSDError(rc, "ssd_set_output_norm_fusion")
+    return rc
+
+
 def profile_start(capacity: int) -> None:
     """Time every kernel launch of the library with a pair of HIP events on
     the launch stream, for the next `capacity` launches."""

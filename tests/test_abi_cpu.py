@@ -492,6 +492,20 @@ def test_backward_refuses_before_launch(lib):
     assert _bwd_call(lib, dims(cfg, flags=4), base, need) == -3
 
 
+def test_output_norm_fusion_setting(lib):
+    """The general path's norm-fusion diagnostic takes 0, 1 or 2, returns
+    the previous mode, and refuses anything else."""
+    prev = lib.ssd_set_output_norm_fusion(1)
+    try:
+        assert prev == 0
+        for bad in (-1, 3, 100):
+            assert lib.ssd_set_output_norm_fusion(bad) == -2, bad
+        assert lib.ssd_set_output_norm_fusion(2) == 1
+        assert lib.ssd_set_output_norm_fusion(0) == 2
+    finally:
+        lib.ssd_set_output_norm_fusion(0)
+
+
 def test_backward_chunk_heads_setting(lib):
     """The per-chunk workgroup heads diagnostic takes 0 or a power of two up
     to 32, returns the previous setting, and refuses anything else."""

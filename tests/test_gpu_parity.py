@@ -191,6 +191,35 @@ def test_prefill_generic_bias_normed(ops, P, N, W):
                             batch=1, seqlen=129), with_state=False, with_bias=True)
 
 
+_NORM_FUSE = [
+    ("tiny_fp32", dict(batch=2, seqlen=200), "scan"),            # 4 heads x 16: one 64-channel piece
+    ("tiny_layer", dict(nheads=2, ngroups=1, headdim=32, dstate=16, batch=1, seqlen=100), "scan"),
+    ("tiny_layer", dict(nheads=4, ngroups=2, headdim=64, dstate=16, batch=1, seqlen=257), "scan"),
+    ("tiny_layer", dict(dstate=64, batch=2, seqlen=200), "prefill"),            # 4 x 64: two pieces
+    ("tiny_layer", dict(nheads=4, ngroups=2, headdim=128, dstate=64, batch=1, seqlen=150), "prefill"),
+    ("tiny_layer", dict(nheads=8, ngroups=8, headdim=64, dstate=32, batch=1, seqlen=77), "prefill"),
+    ("tiny_fp32", dict(nheads=16, ngroups=2, headdim=32, dstate=32, batch=1, seqlen=130), "prefill"),
+]
+
+
+@pytest.mark.parametrize("name,kw,entry", _NORM_FUSE)
+@pytest.mark.parametrize("mode", [1, 2])
+def test_general_norm_fusion(ops, name, kw, entry, mode):
+    """General kernels with the gated norm inside the chunk-output kernel
+    (mode 1: wherever the group fits; here 1, 2, 4 and 8 heads per group,
+    64 to 256 channels, one and two LDS pieces) and after it (mode 2), both
+    against the oracle, with states and ragged chunk tails."""
+    prev = ops.ssd_set_output_norm_fusion(mode)
+    try:
+        cfg = small(name, **kw)
+        if entry == "scan":
+            scan_case(ops, cfg, True, True)
+        else:
+            prefill_case(ops, cfg, with_state=True)
+    finally:
+        ops.ssd_set_output_norm_fusion(prev)
+
+
 def test_prefill_bf16_small_state(ops):
     prefill_case(ops, small("tiny_layer", nheads=4, ngroups=1, headdim=32, dstate=16, batch=2,
                             seqlen=100), with_state=True)
