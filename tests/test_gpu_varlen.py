@@ -188,3 +188,63 @@ def test_invalid_offsets_refused(ops):
         assert ops.ssd_workspace_status(ws) == VARLEN, cu
         assert float(out.float().sub(7.0).abs().max()) == 0.0
         assert float(gs.abs().max()) == 0.0 and float(gc.float().abs().max()) == 0.0
+
+
+def test_graph_replay_and_stream_order(ops):
+    """A ragged batch (prefills and one-token decode steps) captured into a
+    HIP graph replays to the eager result bit for bit on every replay, with
+    the pools restored and the workspace scribbled over by eager work
+    between replays (the chunk table, decode list and norm tickets are
+    rebuilt by kernels, not memsets); and work the caller enqueues after the
+    call on its stream sees every output and state (read back without any
+    device-wide sync)."""
+    import torch
+    bf = torch.bfloat16
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], nheads=64, chunk=128)
+    lens, slots = [1, 300, 1, 1, 129, 1], [6, 0, 2, 5, 3, 1]
+    T = int(sum(lens))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    prm = synth.layer_params(cfg)
+    inp = synth.prefill_inputs(cfg, batch=1, seqlen=T)
+    r = np.random.default_rng(3)
+    S = 7
+    cpool = dev(synth.to_io(np.sqrt(0.1) * r.standard_normal((S, 3, cfg.channels)), "bf16"), bf)
+    spool = dev((np.sqrt(0.1) * r.standard_normal((S, cfg.nheads, cfg.headdim, cfg.dstate))
+                 ).astype(np.float32))
+    d = ops.SSDDims(len(lens), T, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, 4, 128, bf)
+    args = (dev(inp["xbc"][0], bf), dev(inp["z"][0], bf), dev(inp["dt"][0], bf), dev(prm["A"]),
+            dev(prm["D"]), dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf))
+    ws = ops.workspace(ops.ssd_mixer_varlen_workspace_bytes(d, S))
+    out = torch.empty(T, cfg.hp, dtype=bf, device="cuda")
+    gc, gs = cpool.clone(), spool.clone()
+
+    def call():
+        ops.ssd_mixer_varlen(d, cu, sl, *args, gc, gs, eps=prm["eps"], out=out, ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+        # stream order: copies enqueued after the call on the same stream
+        ref = (out.clone(), gc.clone(), gs.clone())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = tuple(host(t) for t in ref)
+    assert np.array_equal(host(out), ref[0]) and np.array_equal(host(gs), ref[2])
+    gc.copy_(cpool)
+    gs.copy_(spool)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        gc.copy_(cpool)
+        gs.copy_(spool)
+        out.fill_(float("nan"))
+        ws.fill_(7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), ref[0]), f"replay {i}: out"
+        assert np.array_equal(host(gc), ref[1]), f"replay {i}: conv pool"
+        assert np.array_equal(host(gs), ref[2]), f"replay {i}: ssm pool"
