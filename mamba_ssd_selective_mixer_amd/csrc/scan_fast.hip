@@ -116,15 +116,19 @@ SSD_DEV void sts16(f16* p, const u32x4 v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(v[0], v[1]);
   *reinterpret_cast<uint2*>(p + 4) = make_uint2(v[2], v[3]);
 }
-SSD_DEV void load8h(const f16* p, float (&v)[8]) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p);
-  const uint2 b = *reinterpret_cast<const uint2*>(p + 4);
-  const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+// 8 fp16 (four pairs) to fp32
+SSD_DEV void unpack8h(const u32x4 u, float (&v)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = h2f_lo(w[i]);
     v[2 * i + 1] = h2f_hi(w[i]);
   }
+}
+SSD_DEV void load8h(const f16* p, float (&v)[8]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  const uint2 b = *reinterpret_cast<const uint2*>(p + 4);
+  unpack8h(u32x4{a.x, a.y, b.x, b.y}, v);
 }
 // An empty asm that takes the values in registers: the computation of x
 // cannot be sunk past this point.
@@ -1337,26 +1341,27 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
   __syncthreads();
 
   if constexpr (NM == 2) {
-    // q = y silu(z) goes back into Ot (fp16) and each row's sum of q^2 over
-    // this block's 256 channels is published at device scope
+    // q = y silu(z) is kept in registers as fp16 pairs (the y registers are
+    // free by now) and each row's sum of q^2 over this block's 256 channels
+    // is published at device scope
     const int nb = H / G / HB, grp = tk / nb;
     float* inv_s = &csd[0][0];  // per-row sums, then 1 / rms (csd is free by now)
+    u32x4 qk[EPI][2];
 #pragma unroll
     for (int e = 0; e < EPI; ++e) {
       const int t = et0 + 16 * e;
       float ss = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        f16* op = Ot + t * OS + hf * 128 + ev8 * 8;
         float yv[8], zv[8];
-        load8h(op, yv);
+        load8h(Ot + t * OS + hf * 128 + ev8 * 8, yv);
         unpack8(zr[2 * e + hf], zv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           yv[j] *= silu(zv[j]);
           ss += yv[j] * yv[j];
         }
-        sts16(op, u32x4{pk(yv[0], yv[1]), pk(yv[2], yv[3]), pk(yv[4], yv[5]), pk(yv[6], yv[7])});
+        qk[e][hf] = u32x4{pk(yv[0], yv[1]), pk(yv[2], yv[3]), pk(yv[4], yv[5]), pk(yv[6], yv[7])};
       }
       ss = group_sum_last<16>(ss);
       if (ev8 == 0) inv_s[t] = ss;
@@ -1402,7 +1407,7 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           float yv[8];
-          load8h(Ot + t * OS + hf * 128 + ev8 * 8, yv);
+          unpack8h(qk[e][hf], yv);
 #pragma unroll
           for (int j = 0; j < 8; ++j) yv[j] *= wv8[hf][j] * inv;
           // streaming store: the normalised output is final
