@@ -683,24 +683,60 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 
 // ---------------------------------------------------------------- phase 2
 // S_in(0) = initial state (or 0); S_in(k+1) = exp(Lam_end,k) S_in(k) + dS_k.
-// One thread carries 8 consecutive (p, n) elements of one (batch, head) in
-// fp32 through all chunks, reading dS_k 8 chunks ahead. It also resets the
+// One thread carries V consecutive (p, n) elements of one (batch, head) in
+// fp32 through all chunks, reading dS_k 64 / V chunks ahead (256 bytes of
+// loads in flight per thread). V = 8 (16-byte accesses) when that gives the
+// grid two workgroups per CU; calls with few heads and sequences (one long
+// sequence of the tiny layer: 128 workgroups at V = 8) take V = 4 or 2, so
+// more lanes stream the buffer, each with a deeper look-ahead along its
+// chain of chunks. It also resets the
 // state of the output kernel's cross-block norm (this launch always precedes
 // that one on the stream): the kParts ticket counters to 0 and the npart
 // per-row partial-sum slots to kUnset.
 constexpr int kParts = 8;          // ticket partitions: block index mod 8, one per XCD
 constexpr float kUnset = -1.0f;    // an unwritten slot: never a sum of squares (nor NaN)
-constexpr int kPassDepth = 8;
 // bits of the call's status word (first word of the workspace)
 constexpr int kStatusTimeout = 1;    // a cross-block norm wait gave up
 constexpr int kStatusNonFinite = 2;  // an output or the final state is not finite
-constexpr int kPassVec = 8;
+// V fp16 of one thread: one load or store of 2 V bytes
+template <int V> struct PassVec;
+template <> struct PassVec<8> { typedef u32x4 T; };
+template <> struct PassVec<4> { typedef uint32_t T __attribute__((ext_vector_type(2))); };
+template <> struct PassVec<2> { typedef uint32_t T; };
+template <int V>
+SSD_DEV uint32_t pass_word(const typename PassVec<V>::T& v, int i) {
+  if constexpr (V == 2) return v;
+  else return v[i];
+}
+template <int V>
+SSD_DEV void pass_ldf(const float* p, float (&v)[V]) {
+  if constexpr (V == 8) {
+    load8(p, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; j += 2) {
+      const float2 f = *reinterpret_cast<const float2*>(p + j);
+      v[j] = f.x;
+      v[j + 1] = f.y;
+    }
+  }
+}
+template <int V>
+SSD_DEV void pass_stf(float* p, const float (&v)[V]) {
+  if constexpr (V == 8) {
+    store8(p, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; j += 2) *reinterpret_cast<float2*>(p + j) = make_float2(v[j], v[j + 1]);
+  }
+}
 // dS and sin_h are one buffer: S_in(k) overwrites dS_k, which this thread
 // has loaded before (its own elements only), so neither pointer is restrict.
 // With aux (the state split) the carried state is S' (dS holds dS') plus a
-// bbar^T: the 16 lanes of a row p hold its 128 elements, so the row sums are
-// row-wide DPP reductions; a_in and sc'_in of chunk k go to aux beside da_k,
-// and cbar of each group to cbg (fp16).
+// bbar^T: the 16 lanes of a row p hold its 128 elements (V = 8 only), so
+// the row sums are row-wide DPP reductions; a_in and sc'_in of chunk k go to
+// aux beside da_k, and cbar of each group to cbg (fp16).
+template <int V>
 __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
                                                const float* __restrict__ lam_end,
                                                const float* s_in, float* s_out,
@@ -711,10 +747,12 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
                                                int64_t npart, int* status, Seqs q, int H,
                                                int nc) {
   constexpr int PN = P * N;
-  const int e = (blockIdx.x * 256 + threadIdx.x) * kPassVec;
+  typedef typename PassVec<V>::T VT;
+  constexpr int kPassDepth = 64 / V;  // chunks of loads in flight
+  const int e = (blockIdx.x * 256 + threadIdx.x) * V;
   const int h = blockIdx.y, b = blockIdx.z;
   const int p = e / N, n0 = e % N;
-  const bool ofs = aux != nullptr;
+  const bool ofs = V == 8 && aux != nullptr;  // the launcher takes V = 8 with the split
   {
     const int64_t gt = ((int64_t)(b * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
     const int64_t nt = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
@@ -741,22 +779,22 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     sin_p = !q.has_state || q.has_state[b] ? slot : nullptr;
     sout_p = slot;
   }
-  float S[kPassVec];
+  float S[V];
   if (sin_p) {
-    load8(sin_p + e, S);
+    pass_ldf<V>(sin_p + e, S);
   } else {
 #pragma unroll
-    for (int j = 0; j < kPassVec; ++j) S[j] = 0.f;
+    for (int j = 0; j < V; ++j) S[j] = 0.f;
   }
   // bbar, cbar of this thread's 8 columns; a of its row (0 without the split)
-  float bbar[kPassVec] = {}, cbar[kPassVec] = {};
+  float bbar[8] = {}, cbar[8] = {};
   float a = 0.f;
-  if (ofs) {
+  if constexpr (V == 8) if (ofs) {
     const int g = h / hpg;
     load8(cbias + HP + g * N + n0, bbar);
     load8(cbias + HP + GN + g * N + n0, cbar);
 #pragma unroll
-    for (int j = 0; j < kPassVec; ++j) {
+    for (int j = 0; j < 8; ++j) {
       bbar[j] = silu(bbar[j]);
       cbar[j] = silu(cbar[j]);
     }
@@ -769,7 +807,7 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     // carried-in state: a = (S . bbar) / |bbar|^2 per row, S' = S - a bbar^T
     float sb = 0.f, bq = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPassVec; ++j) {
+    for (int j = 0; j < 8; ++j) {
       sb = fmaf(S[j], bbar[j], sb);
       bq = fmaf(bbar[j], bbar[j], bq);
     }
@@ -777,17 +815,17 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     bq = group_sum_last<16>(bq);
     a = bq > 0.f ? sb / bq : 0.f;
 #pragma unroll
-    for (int j = 0; j < kPassVec; ++j) S[j] = fmaf(-a, bbar[j], S[j]);
+    for (int j = 0; j < 8; ++j) S[j] = fmaf(-a, bbar[j], S[j]);
   }
   for (int c0 = 0; c0 < nc; c0 += kPassDepth) {
-    u32x4 d[kPassDepth];
+    VT d[kPassDepth];
     float al[kPassDepth], da[kPassDepth];
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
       const int c = min(c0 + u, nc - 1);
       // each increment is read once: a streaming load
       d[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(dS + ((k0 + c) * H + h) * PN + e));
+          reinterpret_cast<const VT*>(dS + ((k0 + c) * H + h) * PN + e));
       al[u] = fexp2(lam_end[(k0 + c) * H + h]);  // Lam_end in log2 units
       da[u] = ofs ? aux[((k0 + c) * H + h) * (int64_t)(kAux * P) + p] : 0.f;
     }
@@ -795,16 +833,18 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     for (int u = 0; u < kPassDepth; ++u) {
       const int c = c0 + u;
       if (c < nc) {
-        u32x4 o;
-        o.x = pk(S[0], S[1]);
-        o.y = pk(S[2], S[3]);
-        o.z = pk(S[4], S[5]);
-        o.w = pk(S[6], S[7]);
-        *reinterpret_cast<u32x4*>(sin_h + ((k0 + c) * H + h) * PN + e) = o;
-        if (ofs) {
+        VT o;
+        if constexpr (V == 2) {
+          o = pk(S[0], S[1]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < V / 2; ++j) o[j] = pk(S[2 * j], S[2 * j + 1]);
+        }
+        *reinterpret_cast<VT*>(sin_h + ((k0 + c) * H + h) * PN + e) = o;
+        if constexpr (V == 8) if (ofs) {
           float sc = 0.f;
 #pragma unroll
-          for (int j = 0; j < kPassVec; ++j) sc = fmaf(S[j], cbar[j], sc);
+          for (int j = 0; j < 8; ++j) sc = fmaf(S[j], cbar[j], sc);
           sc = group_sum_last<16>(sc);
           if ((threadIdx.x & 15) == 0) {
             float* ap = aux + ((k0 + c) * H + h) * (int64_t)(kAux * P);
@@ -814,22 +854,23 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
           a = al[u] * a + da[u];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          S[2 * j] = al[u] * S[2 * j] + h2f_lo(d[u][j]);
-          S[2 * j + 1] = al[u] * S[2 * j + 1] + h2f_hi(d[u][j]);
+        for (int j = 0; j < V / 2; ++j) {
+          const uint32_t w = pass_word<V>(d[u], j);
+          S[2 * j] = al[u] * S[2 * j] + h2f_lo(w);
+          S[2 * j + 1] = al[u] * S[2 * j + 1] + h2f_hi(w);
         }
       }
     }
   }
   if (sout_p) {
-    if (ofs) {
+    if constexpr (V == 8) if (ofs) {
 #pragma unroll
-      for (int j = 0; j < kPassVec; ++j) S[j] = fmaf(a, bbar[j], S[j]);
+      for (int j = 0; j < 8; ++j) S[j] = fmaf(a, bbar[j], S[j]);
     }
-    store8(sout_p + e, S);
+    pass_stf<V>(sout_p + e, S);
     float chk = 0.f;  // NaN when any element is infinite or NaN
 #pragma unroll
-    for (int j = 0; j < kPassVec; ++j) chk += S[j] * 0.f;
+    for (int j = 0; j < V; ++j) chk += S[j] * 0.f;
     if (chk != 0.f) atomicOr(status, kStatusNonFinite);
   }
 }
@@ -1743,10 +1784,21 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps(st, KID_FAST_PASS);
-    hipLaunchKernelGGL(k_fpass, dim3(PN / (256 * kPassVec), a.H, a.B), dim3(256), 0, st, dS,
-                       lam_end, a.s_in, a.s_out, sinb, aux, cbg, (const bf16*)a.conv_b, a.H * P,
-                       a.G * N, a.H / a.G, nm == 2 ? sync : nullptr, part, nm == 2 ? npart : 0,
-                       a.status, q, a.H, nc);
+    // 8 elements per thread unless that leaves fewer than two workgroups
+    // per CU (the split always takes 8)
+    const int64_t heads = (int64_t)a.H * a.B;
+    const int pv = split || heads * (PN / (256 * 8)) >= 512 ? 8
+                   : heads * (PN / (256 * 4)) >= 512        ? 4
+                                                            : 2;
+#define SSD_FPASS(V)                                                                           \
+  hipLaunchKernelGGL(k_fpass<V>, dim3(PN / (256 * V), a.H, a.B), dim3(256), 0, st, dS, lam_end, \
+                     a.s_in, a.s_out, sinb, aux, cbg, (const bf16*)a.conv_b, a.H * P, a.G * N,  \
+                     a.H / a.G, nm == 2 ? sync : nullptr, part, nm == 2 ? npart : 0, a.status, q, \
+                     a.H, nc)
+    if (pv == 8) SSD_FPASS(8);
+    else if (pv == 4) SSD_FPASS(4);
+    else SSD_FPASS(2);
+#undef SSD_FPASS
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
