@@ -97,6 +97,38 @@ def test_large_layer_prefill_full(env, bias_slow):
         assert np.array_equal(cs_h[..., chans], ref["conv_out"])
 
 
+def test_one_long_sequence_full(env):
+    """One sequence of 32768 tokens in a single call (tiny-layer heads,
+    slowly decaying, from a nonzero state): 256 chunks per head walked by the
+    state pass with its narrowest vectors and deepest look-ahead (2 elements,
+    32 chunks in flight, as a call this size runs it); groups 0 and 7
+    against one fp64 run, outputs and final states."""
+    torch, ops = env
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], batch=1, seqlen=32768)
+    prm = synth.layer_params(cfg, slow_decay=True)
+    inp = synth.prefill_inputs(cfg)
+    st = synth.initial_states(cfg)
+    bf = torch.bfloat16
+    cs = dev(st["conv_state"], bf)
+    ss = dev(st["ssm_state"])
+    out = ops.ssd_mixer_prefill(dims(ops, torch, cfg), dev(inp["xbc"], bf), dev(inp["z"], bf),
+                                dev(inp["dt"], bf), dev(prm["A"]), dev(prm["D"]),
+                                dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"],
+                                cs, cs, ss, ss)
+    oh, ss_h, cs_h = host(out), host(ss), host(cs)
+    S = cfg.nheads // cfg.ngroups * cfg.headdim
+    for g in (0, 7):
+        sub, chans, heads = group_problem(cfg, g, inp["xbc"], inp["z"], inp["dt"], prm,
+                                          st["conv_state"], st["ssm_state"])
+        ref = oracle.mixer_prefill(sub["xbc"], sub["z"], sub["dt"], sub["A"], sub["D"],
+                                   sub["conv_w"], None, sub["norm_w"], prm["eps"],
+                                   cfg.nheads // cfg.ngroups, cfg.headdim, 1, cfg.dstate,
+                                   conv_in=sub["conv_in"], s_in=sub["s_in"])
+        check(f"long sequence out group {g}", oh[..., g * S:(g + 1) * S], ref["out"], TOLB)
+        check(f"long sequence final state group {g}", ss_h[:, heads], ref["s_out"], TOLB)
+        assert np.array_equal(cs_h[..., chans], ref["conv_out"])
+
+
 @pytest.mark.parametrize("bias_slow", [False, True])
 def test_long_context_chain_full(env, bias_slow):
     """16 pieces of 8192 tokens (131072 in all), each resuming from the
