@@ -74,7 +74,8 @@
  * headdim 64, dstate 128, heads per group a multiple of 4, dims->chunk >= 64
  * and conv width 4 when the call includes the conv) takes fp16 operands
  * throughout (the chunk states and carried-in states are also stored in
- * fp16), with D x taken from x at fp16 hi + lo precision. With a conv bias,
+ * fp16), with D x taken from the fp16 x operand against D at fp16 hi + lo
+ * precision. With a conv bias,
  * B and C (and x) share large per-channel offsets, and the state grows along
  * the B offset bbar, while C . bbar can nearly cancel: the fast path then
  * carries every state as S' + a bbar^T (the same matrix, split), with the
@@ -98,7 +99,11 @@
  * at most 31 waiting per XCD). A wait that cannot complete writes NaN rows
  * after a bounded time instead of hanging and records SSD_ERR_TIMEOUT for
  * ssd_workspace_status(). Wider norm groups are normalised
- * by a separate pass over the scan output.
+ * by a separate pass over the scan output. The general path fuses the norm
+ * into its chunk-output kernel when a norm group (1, 2, 4 or 8 heads, at
+ * most 256 channels) fits one workgroup and the call is large enough to fill
+ * the GPU that way (ssd_set_output_norm_fusion), else it writes the scan
+ * output to the workspace and a separate pass normalises it.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
