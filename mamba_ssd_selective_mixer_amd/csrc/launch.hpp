@@ -90,6 +90,7 @@ struct Seqs {
   const int32_t* slots;        // [nseq] state slot of each sequence
   const uint8_t* has_state;    // [nseq] resume from the slot (else zeros), or null: all
   const int* valid;            // 1 when the call's metadata passed the device checks
+  const int32_t* nchunks;      // [1] chunks the table holds (chunk_first[nseq])
   void* conv_pool;             // [slots, W-1, Cch] io dtype
   float* ssm_pool;             // [slots, H, P, N] fp32
 };

@@ -940,6 +940,20 @@ __global__ __launch_bounds__(NT, 2) void k_fout(Src s, const bf16* __restrict__ 
 
   int c, b, h0, tk = 0;
   if constexpr (NM == 2) {
+    // A ragged batch's grid covers the padded chunk table. Workgroups past
+    // the chunks the table holds (or all, for a refused table) leave here,
+    // before taking a ticket, when every ticket partition keeps whole norm
+    // groups: the first nact H/HB workgroups by index then hold exactly the
+    // tickets of the table's groups. Otherwise they take one and leave below.
+    if (s.q.cu) {
+      const int nparts0 = (gridDim.x * gridDim.z * G) % kParts == 0 ? kParts : 1;
+      const int nact = __builtin_amdgcn_readfirstlane(*s.q.valid) == 1
+                           ? __builtin_amdgcn_readfirstlane(*s.q.nchunks)
+                           : 0;
+      const int64_t lin =
+          ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+      if (((int64_t)nact * G) % nparts0 == 0 && lin >= (int64_t)nact * (H / HB)) return;
+    }
     // the tile comes from a ticket taken in arrival order. Blocks whose index
     // is v mod kParts (those one XCD receives) take tickets from counter v
     // and serve the norm groups that are v mod kParts, so the blocks of a
@@ -1738,6 +1752,7 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   if (varlen) {
     q.valid = (const int*)(w + f.valid);
     q.chunk_first = (const int32_t*)(w + f.first);
+    q.nchunks = q.chunk_first + a.B;
     q.chunk_seq = (const int32_t*)(w + f.cseq);
     hipLaunchKernelGGL(k_varlen_table, dim3(1), dim3(kTableThreads), 0, st, a.q.cu, a.q.slots,
                        a.B, a.L, a.num_slots, (int32_t*)(w + f.first), (int32_t*)(w + f.cseq),
