@@ -91,6 +91,8 @@ struct Seqs {
   const uint8_t* has_state;    // [nseq] resume from the slot (else zeros), or null: all
   const int* valid;            // 1 when the call's metadata passed the device checks
   const int32_t* nchunks;      // [1] chunks the table holds (chunk_first[nseq])
+  const int32_t* pre;          // sequences with two or more tokens, in order
+  const int32_t* npre;         // [1] their count
   void* conv_pool;             // [slots, W-1, Cch] io dtype
   float* ssm_pool;             // [slots, H, P, N] fp32
 };

@@ -750,18 +750,30 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
   typedef typename PassVec<V>::T VT;
   constexpr int kPassDepth = 64 / V;  // chunks of loads in flight
   const int e = (blockIdx.x * 256 + threadIdx.x) * V;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.y;
   const int p = e / N, n0 = e % N;
   const bool ofs = V == 8 && aux != nullptr;  // the launcher takes V = 8 with the split
   {
-    const int64_t gt = ((int64_t)(b * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+    const int64_t gt =
+        ((int64_t)(blockIdx.z * H + h) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
     const int64_t nt = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
     if (sync && gt < kParts) sync[gt] = 0;
     for (int64_t i = gt; i < npart; i += nt) part[i] = kUnset;
   }
+  // Dense batch: sequence blockIdx.z. Ragged batch: the entries blockIdx.z,
+  // blockIdx.z + gridDim.z, ... of the table's list of sequences with two or
+  // more tokens (a sequence with none keeps its slot, one token is the decode
+  // kernel's), so the grid need not span every sequence of the batch.
+  const int nz = !q.cu ? (int)blockIdx.z + 1
+                 : __builtin_amdgcn_readfirstlane(*q.valid) == 1
+                     ? __builtin_amdgcn_readfirstlane(*q.npre)
+                     : 0;
+  for (int zi = blockIdx.z; zi < nz; zi += gridDim.z) {
+  const int b = !q.cu ? zi : __builtin_amdgcn_readfirstlane(q.pre[zi]);
   // the chunks of sequence b (global chunk k0 onwards) and where its state
   // comes from and goes to
   int64_t k0;
+  int ncs = nc;
   const float* sin_p;
   float* sout_p;
   if (!q.cu) {
@@ -770,11 +782,8 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     sin_p = s_in ? s_in + bh * PN : nullptr;
     sout_p = s_out ? s_out + bh * PN : nullptr;
   } else {
-    if (__builtin_amdgcn_readfirstlane(*q.valid) != 1) return;
-    // no tokens: the slot is left as it is; one token: the decode kernel's
-    if (q.cu[b + 1] - q.cu[b] <= 1) return;
     k0 = q.chunk_first[b];
-    nc = q.chunk_first[b + 1] - q.chunk_first[b];
+    ncs = q.chunk_first[b + 1] - q.chunk_first[b];
     float* slot = q.ssm_pool + ((int64_t)q.slots[b] * H + h) * PN;
     sin_p = !q.has_state || q.has_state[b] ? slot : nullptr;
     sout_p = slot;
@@ -817,12 +826,12 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
 #pragma unroll
     for (int j = 0; j < 8; ++j) S[j] = fmaf(-a, bbar[j], S[j]);
   }
-  for (int c0 = 0; c0 < nc; c0 += kPassDepth) {
+  for (int c0 = 0; c0 < ncs; c0 += kPassDepth) {
     VT d[kPassDepth];
     float al[kPassDepth], da[kPassDepth];
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
-      const int c = min(c0 + u, nc - 1);
+      const int c = min(c0 + u, ncs - 1);
       // each increment is read once: a streaming load
       d[u] = __builtin_nontemporal_load(
           reinterpret_cast<const VT*>(dS + ((k0 + c) * H + h) * PN + e));
@@ -832,7 +841,7 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
 #pragma unroll
     for (int u = 0; u < kPassDepth; ++u) {
       const int c = c0 + u;
-      if (c < nc) {
+      if (c < ncs) {
         VT o;
         if constexpr (V == 2) {
           o = pk(S[0], S[1]);
@@ -873,6 +882,7 @@ __global__ __launch_bounds__(256) void k_fpass(const f16* dS,
     for (int j = 0; j < V; ++j) chk += S[j] * 0.f;
     if (chk != 0.f) atomicOr(status, kStatusNonFinite);
   }
+  }  // sequences
 }
 
 // ---------------------------------------------------------------- phase 3
@@ -1552,7 +1562,7 @@ bool pre_c(int H, int G, bool conv) { return conv && wide(H, G); }
 // chunk table and a bitmap of the pool's slots.
 struct FastLayout {
   int64_t chunks, npart;
-  size_t dS, lam, aux, cbg, part, sync, bcv, ccv, uv, valid, first, cseq, bitmap, dec, total;
+  size_t dS, lam, aux, cbg, part, sync, bcv, ccv, uv, valid, first, cseq, bitmap, dec, pre, total;
 };
 // The split's pieces are reserved whenever the conv is on (the size query
 // does not know whether a call brings a bias); a call uses them with one.
@@ -1592,6 +1602,7 @@ FastLayout fast_layout(int B, int L, int H, int G, bool conv, bool varlen, int n
     f.cseq = take((size_t)f.chunks * 4);
     f.bitmap = take(((size_t)num_slots + 31) / 32 * 4);
     f.dec = take(((size_t)B + 1) * 4);  // one-token sequences, then their count
+    f.pre = take(((size_t)B + 1) * 4);  // sequences of two or more tokens, then their count
   }
   f.total = off;
   return f;
@@ -1619,9 +1630,9 @@ constexpr int kStatusVarlen = 4;  // status bit: the ragged batch's metadata is 
 __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, int nseq, int T,
     int num_slots, int32_t* chunk_first, int32_t* chunk_seq, int64_t max_chunks,
-    uint32_t* bitmap, int32_t* dec, int* valid, int* status) {
+    uint32_t* bitmap, int32_t* dec, int32_t* pre, int* valid, int* status) {
   __shared__ int bad;
-  __shared__ int csum[kTableThreads], dsum[kTableThreads];
+  __shared__ int csum[kTableThreads], dsum[kTableThreads], psum[kTableThreads];
   const int tid = threadIdx.x;
   if (tid == 0) {
     bad = 0;
@@ -1634,7 +1645,7 @@ __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
   // thread tid takes sequences [i0, i1)
   const int per = (nseq + kTableThreads - 1) / kTableThreads;
   const int i0 = min(nseq, tid * per), i1 = min(nseq, i0 + per);
-  int cnt = 0, dcnt = 0, err = 0;
+  int cnt = 0, dcnt = 0, pcnt = 0, err = 0;
   if (tid == 0 && (cu[0] != 0 || cu[nseq] != T)) err = 1;
   for (int i = i0; i < i1; ++i) {
     const int len = cu[i + 1] - cu[i];
@@ -1650,24 +1661,29 @@ __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
     }
     const uint32_t bit = 1u << (sl & 31);
     if (atomicOr(bitmap + (sl >> 5), bit) & bit) err = 1;  // slot used twice
-    if (len == 1)
+    if (len == 1) {
       ++dcnt;  // a decode step: the decode kernel takes it, it gets no chunk
-    else
+    } else {
       cnt += (len + QI - 1) / QI;
+      ++pcnt;
+    }
   }
   if (err) atomicOr(&bad, 1);
-  // exclusive scans of the per-thread chunk and decode-step counts
+  // exclusive scans of the per-thread chunk, decode-step and prefill counts
   csum[tid] = cnt;
   dsum[tid] = dcnt;
+  psum[tid] = pcnt;
   __syncthreads();
   for (int d = 1; d < kTableThreads; d <<= 1) {
-    const int v = tid >= d ? csum[tid - d] : 0, w = tid >= d ? dsum[tid - d] : 0;
+    const int v = tid >= d ? csum[tid - d] : 0, w = tid >= d ? dsum[tid - d] : 0,
+              u = tid >= d ? psum[tid - d] : 0;
     __syncthreads();
     csum[tid] += v;
     dsum[tid] += w;
+    psum[tid] += u;
     __syncthreads();
   }
-  int base = csum[tid] - cnt, dbase = dsum[tid] - dcnt;
+  int base = csum[tid] - cnt, dbase = dsum[tid] - dcnt, pbase = psum[tid] - pcnt;
   const int total = csum[kTableThreads - 1];
   for (int i = i0; i < i1; ++i) {
     chunk_first[i] = base;
@@ -1677,10 +1693,12 @@ __global__ __launch_bounds__(kTableThreads) void k_varlen_table(
       if (base + j >= 0 && base + j < max_chunks) chunk_seq[base + j] = i;
     base += n;
     if (len == 1) dec[dbase++] = i;
+    else if (len > 1) pre[pbase++] = i;
   }
   if (tid == 0) {
     chunk_first[nseq] = total;
     dec[nseq] = dsum[kTableThreads - 1];
+    pre[nseq] = psum[kTableThreads - 1];
   }
   for (int64_t k = max(total, 0) + tid; k < max_chunks; k += kTableThreads) chunk_seq[k] = -1;
   __syncthreads();
@@ -1753,10 +1771,13 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     q.valid = (const int*)(w + f.valid);
     q.chunk_first = (const int32_t*)(w + f.first);
     q.nchunks = q.chunk_first + a.B;
+    q.pre = (const int32_t*)(w + f.pre);
+    q.npre = q.pre + a.B;
     q.chunk_seq = (const int32_t*)(w + f.cseq);
     hipLaunchKernelGGL(k_varlen_table, dim3(1), dim3(kTableThreads), 0, st, a.q.cu, a.q.slots,
                        a.B, a.L, a.num_slots, (int32_t*)(w + f.first), (int32_t*)(w + f.cseq),
                        f.chunks, (uint32_t*)(w + f.bitmap), (int32_t*)(w + f.dec),
+                       (int32_t*)(w + f.pre),
                        (int*)(w + f.valid), a.status);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1801,12 +1822,17 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     ProfScope ps(st, KID_FAST_PASS);
     // 8 elements per thread unless that leaves fewer than two workgroups
     // per CU (the split always takes 8)
-    const int64_t heads = (int64_t)a.H * a.B;
+    // a ragged batch's workgroups walk the list of its prefills, gridDim.z
+    // apart: enough z slices for 2048 workgroups at 8 elements per thread
+    const int64_t per_z = (int64_t)a.H * (PN / (256 * 8));
+    const int zdim =
+        !varlen ? a.B : (int)std::min<int64_t>(a.B, std::max<int64_t>(1, (2048 + per_z - 1) / per_z));
+    const int64_t heads = (int64_t)a.H * zdim;
     const int pv = split || heads * (PN / (256 * 8)) >= 512 ? 8
                    : heads * (PN / (256 * 4)) >= 512        ? 4
                                                             : 2;
 #define SSD_FPASS(V)                                                                           \
-  hipLaunchKernelGGL(k_fpass<V>, dim3(PN / (256 * V), a.H, a.B), dim3(256), 0, st, dS, lam_end, \
+  hipLaunchKernelGGL(k_fpass<V>, dim3(PN / (256 * V), a.H, zdim), dim3(256), 0, st, dS, lam_end, \
                      a.s_in, a.s_out, sinb, aux, cbg, (const bf16*)a.conv_b, a.H * P, a.G * N,  \
                      a.H / a.G, nm == 2 ? sync : nullptr, part, nm == 2 ? npart : 0, a.status, q, \
                      a.H, nc)
