@@ -467,11 +467,15 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
                                                f16* __restrict__ bcv, f16* __restrict__ ccv,
                                                float* __restrict__ aux,
                                                float* __restrict__ ug, int* status, int L,
-                                               int H, int G, int nc) {
+                                               int H, int G, int nc, int hs) {
   __shared__ __align__(16) f16 BT[N * RS];      // [n][s]
   __shared__ __align__(16) f16 XB[2 * P * RS];  // two [p][s] buffers of x_s w_s
   __shared__ float wv[2][HB][QI];               // w_s of the current / next head block
-  const int hpg = H / G, g = blockIdx.y, hg0 = g * hpg;
+  // hs workgroups share a (chunk, group), each walking hpg of its heads; the
+  // first also keeps the convolved B and C rows for the output kernel
+  const int g = blockIdx.y / hs, part = blockIdx.y % hs;
+  const int hpg = H / G / hs, hg0 = g * (H / G) + part * hpg;
+  const bool keep = PRE && part == 0;
   ChunkGeo cg;
   if (!chunk_geo(s, blockIdx.x, blockIdx.z, L, nc, cg)) return;
   L = cg.L;
@@ -553,14 +557,14 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
     // with PRE, conv'd B also kept (natural layout) for the output kernel
     conv_store<CONV, true, CONV ? kOfsSub : kOfsNone>(rb, cwb, tseq, nvb, cin_b,
                                                       BT + n0 * RS + tbi * 8, RS,
-                                                      PRE ? bcv + grow : nullptr, s.GN, bbr);
+                                                      keep ? bcv + grow : nullptr, s.GN, bbr);
   }
   // with PRE, conv'd C too for the output kernel (a group spans several of
   // its 4-head blocks, each of which would otherwise redo the B and C conv):
   // rows fetched now, converted after head 0 is staged
   Rows8<CONV> rc;
   ConvW<CONV> cwc;
-  if constexpr (PRE) {
+  if constexpr (PRE) if (keep) {
     const int ch = s.HP + s.GN + g * N + n0;
     convw_load<CONV>(cwc, s, ch);
     rows_load<CONV, 8>(rc, s.c + cg.tok0 * s.bs + g * N + n0, s.bs, tseq, L - 1, s, ch,
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 
   x_store<CONV, false>(xr[0], cwx, t0 + xtb * 4, xnv, cin_b, &wv[0][0][xtb * 4],
                        XB + xp0 * RS + xtb * 4, nullptr, RS);
-  if constexpr (PRE) {
+  if constexpr (PRE) if (keep) {
     float ud[8];
     // two halves of 4 tokens (the halo rows of the second are rows 4..)
     constexpr int kOfsC = CONV ? kOfsDot : kOfsNone;
@@ -1804,17 +1808,22 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   {
     // one workgroup per (chunk, group, batch): B staged once for the group
     ProfScope ps(st, KID_FAST_STATE);
-    const dim3 g0(nc, a.G, gz);
+    // a ragged batch splits each (chunk, group)'s heads over two workgroups
+    // when they come in blocks of 8: its chunk count is known only on the
+    // device, and one workgroup per (chunk, group) left the serving batch's
+    // 552 of them a second, nearly empty round of a 512-workgroup machine
+    const int hs = varlen && (a.H / a.G) % (2 * HB) == 0 ? 2 : 1;
+    const dim3 g0(nc, a.G * hs, gz);
     const bf16* dt = (const bf16*)a.dt;
     if (prec)
       hipLaunchKernelGGL((k_fstate<true, true>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         bcv, ccv, aux, ug, a.status, a.L, a.H, a.G, nc);
+                         bcv, ccv, aux, ug, a.status, a.L, a.H, a.G, nc, hs);
     else if (a.conv)
       hipLaunchKernelGGL((k_fstate<true, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, aux, nullptr, a.status, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, aux, nullptr, a.status, a.L, a.H, a.G, nc, hs);
     else
       hipLaunchKernelGGL((k_fstate<false, false>), g0, dim3(NT), 0, st, s, dt, a.A, dS, lam_end,
-                         nullptr, nullptr, nullptr, nullptr, a.status, a.L, a.H, a.G, nc);
+                         nullptr, nullptr, nullptr, nullptr, a.status, a.L, a.H, a.G, nc, hs);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
