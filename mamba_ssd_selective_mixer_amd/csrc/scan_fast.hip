@@ -690,7 +690,7 @@ __global__ __launch_bounds__(NT, 2) void k_fstate(Src s, const bf16* __restrict_
 // One thread carries V consecutive (p, n) elements of one (batch, head) in
 // fp32 through all chunks, reading dS_k 64 / V chunks ahead (256 bytes of
 // loads in flight per thread). V = 8 (16-byte accesses) when that gives the
-// grid two workgroups per CU; calls with few heads and sequences (one long
+// grid four workgroups per CU; calls with few heads and sequences (one long
 // sequence of the tiny layer: 128 workgroups at V = 8) take V = 4 or 2, so
 // more lanes stream the buffer, each with a deeper look-ahead along its
 // chain of chunks. It also resets the
@@ -1829,7 +1829,7 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     ProfScope ps(st, KID_FAST_PASS);
-    // 8 elements per thread unless that leaves fewer than two workgroups
+    // 8 elements per thread unless that leaves fewer than four workgroups
     // per CU (the split always takes 8)
     // a ragged batch's workgroups walk the list of its prefills, gridDim.z
     // apart: enough z slices for 2048 workgroups at 8 elements per thread
@@ -1837,8 +1837,8 @@ hipError_t launch_fast_scan(const FastScanArgs& a, hipStream_t st) {
     const int zdim =
         !varlen ? a.B : (int)std::min<int64_t>(a.B, std::max<int64_t>(1, (2048 + per_z - 1) / per_z));
     const int64_t heads = (int64_t)a.H * zdim;
-    const int pv = split || heads * (PN / (256 * 8)) >= 512 ? 8
-                   : heads * (PN / (256 * 4)) >= 512        ? 4
+    const int pv = split || heads * (PN / (256 * 8)) >= 1024 ? 8
+                   : heads * (PN / (256 * 4)) >= 1024       ? 4
                                                             : 2;
 #define SSD_FPASS(V)                                                                           \
   hipLaunchKernelGGL(k_fpass<V>, dim3(PN / (256 * V), a.H, zdim), dim3(256), 0, st, dS, lam_end, \
