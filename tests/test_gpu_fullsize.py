@@ -97,6 +97,31 @@ def test_large_layer_prefill_full(env, bias_slow):
         assert np.array_equal(cs_h[..., chans], ref["conv_out"])
 
 
+def test_general_layer_prefill_full(env):
+    """4 x 2048 tokens, 32 heads x 64, 8 groups, state 64 (outside the fused
+    kernels' envelope), with states in and out: every output and final state.
+    At this size the general output kernel applies the gated norm itself
+    (1024 (chunk, group) workgroups), as the benchmark runs it."""
+    torch, ops = env
+    cfg = synth.replace(synth.CONFIGS["tiny_layer"], dstate=64)
+    prm, inp = synth.layer_params(cfg), synth.prefill_inputs(cfg)
+    st = synth.initial_states(cfg)
+    bf = torch.bfloat16
+    cs_in, ss_in = dev(st["conv_state"], bf), dev(st["ssm_state"])
+    cs_out, ss_out = torch.empty_like(cs_in), torch.empty_like(ss_in)
+    out = ops.ssd_mixer_prefill(dims(ops, torch, cfg), dev(inp["xbc"], bf), dev(inp["z"], bf),
+                                dev(inp["dt"], bf), dev(prm["A"]), dev(prm["D"]),
+                                dev(prm["conv_w"], bf), None, dev(prm["norm_w"], bf), prm["eps"],
+                                cs_in, cs_out, ss_in, ss_out)
+    ref = oracle.mixer_prefill(inp["xbc"], inp["z"], inp["dt"], prm["A"], prm["D"], prm["conv_w"],
+                               None, prm["norm_w"], prm["eps"], cfg.nheads, cfg.headdim,
+                               cfg.ngroups, cfg.dstate, conv_in=st["conv_state"],
+                               s_in=st["ssm_state"])
+    check("general layer out", host(out), ref["out"], TOLB)
+    check("general layer final state", host(ss_out), ref["s_out"], TOLB)
+    assert np.array_equal(host(cs_out), ref["conv_out"])
+
+
 def test_one_long_sequence_full(env):
     """One sequence of 32768 tokens in a single call (tiny-layer heads,
     slowly decaying, from a nonzero state): 256 chunks per head walked by the
